@@ -1,0 +1,173 @@
+"""ctypes wrapper of the plain-C fp64 oracle (``tree_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Builds ``libtree_oracle.so`` with gcc on first use; the functions
+take and return numpy arrays.  Nothing here is shared with the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+ORC_BAD_TREE = 0x1
+ORC_OVERFLOW = 0x2
+ORC_BAD_LEN = 0x4
+ORC_BAD_PATH = 0x8
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tree_oracle.c")
+_LIB = os.path.join(_HERE, "libtree_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle (plain C, -O2, no fast-math so sums keep their written order)."""
+    tmp = out + f".tmp{os.getpid()}"
+    subprocess.check_call(["gcc", "-std=c11", "-O2", "-Wall", "-shared", "-fPIC", "-pthread",
+                           src, "-o", tmp, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the oracle library, building it if it is missing or older than its source."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+            _lib = _declare(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    P = ctypes.c_void_p
+    i = ctypes.c_int
+    lib.oracle_tree_paths.argtypes = [P, i, P, P]
+    lib.oracle_tree_paths.restype = i
+    lib.oracle_build_mask.argtypes = [P, i, i, P, P]
+    lib.oracle_build_mask.restype = None
+    lib.oracle_attention.argtypes = [i, P, P, P, P, P, P, P, i, i, i, i, i, i, ctypes.c_double,
+                                     P, ctypes.c_long, P, P, i]
+    lib.oracle_attention.restype = i
+    lib.oracle_accept.argtypes = [P, P, P, i, i, P, P, P]
+    lib.oracle_accept.restype = None
+    lib.oracle_compact.argtypes = [i, P, P, P, P, P, P, P, P, i, i, i, i, i, P]
+    lib.oracle_compact.restype = None
+    return lib
+
+
+def _p(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _i32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _elem_bits(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 32
+    if a.dtype == np.uint16:
+        return 16
+    raise TypeError(f"oracle takes float32 or bfloat16 bits (uint16), got {a.dtype}")
+
+
+def tree_paths(parent, lib=None) -> tuple[list[list[int]], int]:
+    """Paths root..i of one tree and its status bits."""
+    lib = lib or load()
+    parent = _i32(parent)
+    T = parent.shape[0]
+    paths = np.empty((T, T), np.int32)
+    plen = np.empty(T, np.int32)
+    st = lib.oracle_tree_paths(_p(parent), T, _p(paths), _p(plen))
+    return [list(map(int, paths[i, : plen[i]])) for i in range(T)], int(st)
+
+
+def build_mask(parent, lib=None) -> tuple[np.ndarray, np.ndarray]:
+    """anc_mask [B,T,W] uint64 and status [B] int32 for a [B,T] parent array."""
+    lib = lib or load()
+    parent = _i32(parent)
+    B, T = parent.shape
+    W = (T + 63) // 64
+    anc = np.empty((B, T, W), np.uint64)
+    status = np.empty(B, np.int32)
+    lib.oracle_build_mask(_p(parent), B, T, _p(anc), _p(status))
+    return anc, status
+
+
+def attention(q, k_cache, v_cache, cache_len, k_tree, v_tree, parent, scale=None, rows=None,
+              n_threads=None, lib=None) -> tuple[np.ndarray, np.ndarray]:
+    """fp64 tree attention.  ``rows`` is an optional [n,3] array of (b, h, i); then the result
+    is [n, D] and [n]; otherwise [B,T,Hq,D] and [B,T,Hq]."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q)
+    bits = _elem_bits(q)
+    k_cache, v_cache, k_tree, v_tree = (np.ascontiguousarray(x, dtype=q.dtype)
+                                        for x in (k_cache, v_cache, k_tree, v_tree))
+    cache_len = _i32(cache_len)
+    parent = _i32(parent)
+    B, T, Hq, D = q.shape
+    Hkv = k_tree.shape[2]
+    Lmax = k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if n_threads is None:
+        n_threads = len(os.sched_getaffinity(0))
+    if rows is not None:
+        rows = _i32(rows).reshape(-1, 3)
+        n = rows.shape[0]
+        out = np.empty((n, D), np.float64)
+        lse = np.empty(n, np.float64)
+    else:
+        n = B * T * Hq
+        out = np.empty((B, T, Hq, D), np.float64)
+        lse = np.empty((B, T, Hq), np.float64)
+    rc = lib.oracle_attention(bits, _p(q), _p(k_cache), _p(v_cache), _p(cache_len), _p(k_tree),
+                              _p(v_tree), _p(parent), B, T, Hq, Hkv, D, Lmax, float(scale),
+                              _p(rows), n, _p(out), _p(lse), int(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_attention rejected its arguments")
+    return out, lse
+
+
+def accept(parent, draft, target, lib=None) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """accept_path [B,T] (-1 padded), accept_len [B], bonus_tok [B]."""
+    lib = lib or load()
+    parent, draft, target = _i32(parent), _i32(draft), _i32(target)
+    B, T = parent.shape
+    path = np.empty((B, T), np.int32)
+    n = np.empty(B, np.int32)
+    bonus = np.empty(B, np.int32)
+    lib.oracle_accept(_p(parent), _p(draft), _p(target), B, T, _p(path), _p(n), _p(bonus))
+    return path, n, bonus
+
+
+def compact(k_cache, v_cache, cache_len, k_tree, v_tree, accept_path, accept_len, status=None,
+            lib=None):
+    """In-place compaction of host copies; returns (cache_len_out, status)."""
+    lib = lib or load()
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    assert k_cache.dtype == v_cache.dtype == k_tree.dtype == v_tree.dtype
+    B, Hkv, Lmax, D = k_cache.shape
+    T = k_tree.shape[1]
+    k_tree = np.ascontiguousarray(k_tree)
+    v_tree = np.ascontiguousarray(v_tree)
+    cache_len = _i32(cache_len)
+    accept_path, accept_len = _i32(accept_path), _i32(accept_len)
+    out_len = np.empty(B, np.int32)
+    st = np.zeros(B, np.int32) if status is None else status
+    lib.oracle_compact(k_cache.dtype.itemsize, _p(k_cache), _p(v_cache), _p(cache_len),
+                       _p(out_len), _p(k_tree), _p(v_tree), _p(accept_path), _p(accept_len),
+                       B, T, Hkv, D, Lmax, _p(st))
+    return out_len, st

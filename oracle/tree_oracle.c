@@ -1,0 +1,337 @@
+/*
+ * CPU oracle for tree-attention verification of a speculative draft tree.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or load this file:
+ * only the tests, the smoke check and the benchmark's CPU-baseline leg use it.  It shares no
+ * code, header, table or helper with the HIP library.
+ *
+ * Everything is written as the plain definition, in fp64, with no blocking or fusion:
+ *
+ *   path(i)        root..i, found by following parent pointers until -1 and reversing
+ *                  (lesty.tech "EAGLE-2 vs. Medusa", section 5, tree-attention mask code).
+ *   mask row i     bit j set iff j lies on path(i): a node sees itself and its ancestors only,
+ *                  never a sibling branch (same section; rainlin.net "EAGLE 系列", section 4,
+ *                  where "good" sees exactly [It, is, a, good]).
+ *   attention      for query head h of node i: ordinary softmax attention of q[b,i,h] over the
+ *                  sequence prefix rows 0..L_b-1 followed by the K/V rows of path(i).  This is
+ *                  the causal attention of the last position of prefix ++ path(i); a tree pass
+ *                  equals verifying every root-to-node path on its own (rainlin.net section 4),
+ *                  so no mask is needed.  Query head h reads KV head h / (Hq / Hkv).
+ *   acceptance     greedy: a drafted token is accepted iff it equals the target model's choice
+ *                  at its parent (lesty.tech section 4); a node is accepted iff every node on its
+ *                  path is; the single longest accepted path is kept (lesty.tech section 8;
+ *                  rainlin.net section 3.2).  Ties at equal depth go to the smallest index.
+ *   compaction     the accepted path's K/V rows are appended to the cache after the prefix, in
+ *                  path order, and nothing else is written (lesty.tech section 8).
+ *
+ * Floating inputs are either float32 (elem_bits = 32) or raw bfloat16 bit patterns
+ * (elem_bits = 16), which are widened exactly.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_BAD_TREE 0x1
+#define ORC_OVERFLOW 0x2
+#define ORC_BAD_LEN 0x4
+#define ORC_BAD_PATH 0x8
+
+/* ------------------------------------------------------------------------------------------ */
+/* tree paths                                                                                  */
+/* ------------------------------------------------------------------------------------------ */
+
+/* A tree is valid iff node 0 is the only root and every other node's parent comes before it
+ * (the flattened level order of the worked tree). */
+static int tree_is_valid(const int32_t* parent, int T) {
+  if (T < 1 || parent[0] != -1) return 0;
+  for (int i = 1; i < T; ++i)
+    if (parent[i] < 0 || parent[i] >= i) return 0;
+  return 1;
+}
+
+/* Writes path(i) = [root, ..., parent(i), i] to out and returns its length.  For an invalid
+ * tree every node's path is just the node itself. */
+static int node_path(const int32_t* parent, int T, int valid, int i, int32_t* out) {
+  (void)T;
+  if (!valid) {
+    out[0] = i;
+    return 1;
+  }
+  int n = 0;
+  for (int cur = i; cur != -1; cur = parent[cur]) out[n++] = cur;
+  for (int a = 0, z = n - 1; a < z; ++a, --z) {
+    int32_t t = out[a];
+    out[a] = out[z];
+    out[z] = t;
+  }
+  return n;
+}
+
+/* paths[i*T + k] = k-th node of path(i) (-1 past its length), plen[i] = its length.
+ * Returns the status bits of the tree. */
+int oracle_tree_paths(const int32_t* parent, int T, int32_t* paths, int32_t* plen) {
+  int valid = tree_is_valid(parent, T);
+  for (int i = 0; i < T; ++i) {
+    for (int k = 0; k < T; ++k) paths[(size_t)i * T + k] = -1;
+    plen[i] = node_path(parent, T, valid, i, paths + (size_t)i * T);
+  }
+  return valid ? 0 : ORC_BAD_TREE;
+}
+
+/* anc[b,i,w]: bit (j % 64) of word j / 64 is set iff node j is on path(i). */
+void oracle_build_mask(const int32_t* parent, int B, int T, uint64_t* anc, int32_t* status) {
+  int W = (T + 63) / 64;
+  int32_t* path = (int32_t*)malloc(sizeof(int32_t) * (size_t)T);
+  for (int b = 0; b < B; ++b) {
+    const int32_t* pb = parent + (size_t)b * T;
+    int valid = tree_is_valid(pb, T);
+    status[b] = valid ? 0 : ORC_BAD_TREE;
+    for (int i = 0; i < T; ++i) {
+      uint64_t* row = anc + ((size_t)b * T + i) * W;
+      for (int w = 0; w < W; ++w) row[w] = 0;
+      int n = node_path(pb, T, valid, i, path);
+      for (int k = 0; k < n; ++k) row[path[k] / 64] |= (uint64_t)1 << (path[k] % 64);
+    }
+  }
+  free(path);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* attention                                                                                   */
+/* ------------------------------------------------------------------------------------------ */
+
+static double load_elem(const void* base, size_t idx, int elem_bits) {
+  if (elem_bits == 32) return (double)((const float*)base)[idx];
+  uint32_t u = (uint32_t)((const uint16_t*)base)[idx] << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+typedef struct {
+  int elem_bits;
+  const void *q, *k_cache, *v_cache, *k_tree, *v_tree;
+  const int32_t *cache_len, *parent;
+  int B, T, Hq, Hkv, D, Lmax;
+  double scale;
+  const int32_t* rows; /* [n_rows*3] of (b, h, i), or NULL for every (b, i, h) in out's order */
+  long n_rows;
+  double *out, *lse;
+  long next; /* work counter, protected by mu */
+  pthread_mutex_t mu;
+} attn_job;
+
+/* One output row: softmax(scale * q . k_j) weighted sum of v_j over the prefix then path(i). */
+static void attention_row(const attn_job* J, int b, int h, int i, double* o, double* lse_out,
+                          double* s, int32_t* path) {
+  const int D = J->D, G = J->Hq / J->Hkv, kvh = h / G;
+  const int32_t* pb = J->parent + (size_t)b * J->T;
+  int valid = tree_is_valid(pb, J->T);
+  int npath = node_path(pb, J->T, valid, i, path);
+  int L = J->cache_len[b];
+  if (L < 0) L = 0;
+  if (L > J->Lmax) L = J->Lmax;
+  int nkeys = L + npath;
+  size_t qoff = (((size_t)b * J->T + i) * J->Hq + h) * D;
+
+  /* key j < L: prefix row j; key L + k: tree row path[k] */
+  for (int j = 0; j < nkeys; ++j) {
+    const void* kb;
+    size_t koff;
+    if (j < L) {
+      kb = J->k_cache;
+      koff = (((size_t)b * J->Hkv + kvh) * J->Lmax + j) * D;
+    } else {
+      kb = J->k_tree;
+      koff = (((size_t)b * J->T + path[j - L]) * J->Hkv + kvh) * D;
+    }
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d)
+      dot += load_elem(J->q, qoff + d, J->elem_bits) * load_elem(kb, koff + d, J->elem_bits);
+    s[j] = J->scale * dot;
+  }
+  double m = -INFINITY;
+  for (int j = 0; j < nkeys; ++j)
+    if (s[j] > m) m = s[j];
+  double den = 0.0;
+  for (int j = 0; j < nkeys; ++j) {
+    s[j] = exp(s[j] - m);
+    den += s[j];
+  }
+  for (int d = 0; d < D; ++d) o[d] = 0.0;
+  for (int j = 0; j < nkeys; ++j) {
+    const void* vb;
+    size_t voff;
+    if (j < L) {
+      vb = J->v_cache;
+      voff = (((size_t)b * J->Hkv + kvh) * J->Lmax + j) * D;
+    } else {
+      vb = J->v_tree;
+      voff = (((size_t)b * J->T + path[j - L]) * J->Hkv + kvh) * D;
+    }
+    for (int d = 0; d < D; ++d) o[d] += s[j] * load_elem(vb, voff + d, J->elem_bits);
+  }
+  for (int d = 0; d < D; ++d) o[d] /= den;
+  *lse_out = m + log(den);
+}
+
+static void* attention_worker(void* arg) {
+  attn_job* J = (attn_job*)arg;
+  double* s = (double*)malloc(sizeof(double) * ((size_t)J->Lmax + J->T));
+  int32_t* path = (int32_t*)malloc(sizeof(int32_t) * (size_t)J->T);
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    long r = J->next++;
+    pthread_mutex_unlock(&J->mu);
+    if (r >= J->n_rows) break;
+    int b, h, i;
+    if (J->rows) {
+      b = J->rows[3 * r];
+      h = J->rows[3 * r + 1];
+      i = J->rows[3 * r + 2];
+    } else { /* out is [B, T, Hq, D] */
+      h = (int)(r % J->Hq);
+      i = (int)((r / J->Hq) % J->T);
+      b = (int)(r / ((long)J->Hq * J->T));
+    }
+    attention_row(J, b, h, i, J->out + (size_t)r * J->D, J->lse + r, s, path);
+  }
+  free(s);
+  free(path);
+  return NULL;
+}
+
+/* Tree attention of the selected rows (or of every row when rows == NULL, then out is
+ * [B,T,Hq,D] and lse [B,T,Hq]).  Returns 0, or -1 on bad arguments. */
+int oracle_attention(int elem_bits, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* cache_len, const void* k_tree, const void* v_tree,
+                     const int32_t* parent, int B, int T, int Hq, int Hkv, int D, int Lmax,
+                     double scale, const int32_t* rows, long n_rows, double* out, double* lse,
+                     int n_threads) {
+  if ((elem_bits != 32 && elem_bits != 16) || B < 1 || T < 1 || Hkv < 1 ||
+      Hq % Hkv != 0 || D < 1 || Lmax < 0)
+    return -1;
+  attn_job J;
+  J.elem_bits = elem_bits;
+  J.q = q;
+  J.k_cache = k_cache;
+  J.v_cache = v_cache;
+  J.k_tree = k_tree;
+  J.v_tree = v_tree;
+  J.cache_len = cache_len;
+  J.parent = parent;
+  J.B = B;
+  J.T = T;
+  J.Hq = Hq;
+  J.Hkv = Hkv;
+  J.D = D;
+  J.Lmax = Lmax;
+  J.scale = scale;
+  J.rows = rows;
+  J.n_rows = rows ? n_rows : (long)B * T * Hq;
+  J.out = out;
+  J.lse = lse;
+  J.next = 0;
+  pthread_mutex_init(&J.mu, NULL);
+  if (n_threads < 1) n_threads = 1;
+  if (n_threads > 256) n_threads = 256;
+  pthread_t th[256];
+  for (int t = 0; t < n_threads; ++t) pthread_create(&th[t], NULL, attention_worker, &J);
+  for (int t = 0; t < n_threads; ++t) pthread_join(th[t], NULL);
+  pthread_mutex_destroy(&J.mu);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* acceptance walk                                                                             */
+/* ------------------------------------------------------------------------------------------ */
+
+/* accept_path[b, :len] = path of the deepest accepted node (smallest index among equals),
+ * -1 after it; accept_len[b] = its length (the root counts); bonus_tok[b] = target at it. */
+void oracle_accept(const int32_t* parent, const int32_t* draft, const int32_t* target, int B,
+                   int T, int32_t* accept_path, int32_t* accept_len, int32_t* bonus_tok) {
+  char* acc = (char*)malloc((size_t)T);
+  int32_t* depth = (int32_t*)malloc(sizeof(int32_t) * (size_t)T);
+  for (int b = 0; b < B; ++b) {
+    const int32_t* pb = parent + (size_t)b * T;
+    const int32_t* db = draft + (size_t)b * T;
+    const int32_t* tb = target + (size_t)b * T;
+    int valid = tree_is_valid(pb, T);
+    /* the root is the token the target model itself chose last step: always accepted */
+    acc[0] = 1;
+    depth[0] = 0;
+    for (int c = 1; c < T; ++c) {
+      if (!valid) {
+        acc[c] = 0;
+        depth[c] = 0;
+        continue;
+      }
+      int p = pb[c]; /* p < c, so acc[p] and depth[p] are already known */
+      acc[c] = acc[p] && db[c] == tb[p];
+      depth[c] = depth[p] + 1;
+    }
+    int best = 0;
+    for (int c = 1; c < T; ++c)
+      if (acc[c] && depth[c] > depth[best]) best = c;
+    int32_t* out = accept_path + (size_t)b * T;
+    for (int k = 0; k < T; ++k) out[k] = -1;
+    accept_len[b] = node_path(pb, T, valid, best, out);
+    bonus_tok[b] = tb[best];
+  }
+  free(acc);
+  free(depth);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* compaction                                                                                  */
+/* ------------------------------------------------------------------------------------------ */
+
+/* For each sequence b with L = cache_len[b] and n = accept_len[b]: cache rows L..L+n-1 of every
+ * KV head receive tree rows accept_path[b, 0..n-1]; cache_len_out[b] = L + n.  Invalid lengths
+ * or path entries, or L + n > Lmax, set status bits and commit nothing (cache_len_out[b] = L).
+ * All source rows are read into a temporary before any row is written, so tree rows that live
+ * inside the cache are handled too.  status bits are OR-ed in. */
+void oracle_compact(int elem_bytes, void* k_cache, void* v_cache, const int32_t* cache_len,
+                    int32_t* cache_len_out, const void* k_tree, const void* v_tree,
+                    const int32_t* accept_path, const int32_t* accept_len, int B, int T, int Hkv,
+                    int D, int Lmax, int32_t* status) {
+  size_t row = (size_t)D * elem_bytes;
+  unsigned char* tmp = (unsigned char*)malloc(row * 2 * (size_t)T * Hkv);
+  for (int b = 0; b < B; ++b) {
+    int L = cache_len[b];
+    int n = accept_len[b];
+    int bits = 0;
+    if (L < 0 || L > Lmax) bits |= ORC_BAD_LEN;
+    if (n < 0 || n > T) {
+      bits |= ORC_BAD_PATH;
+    } else {
+      for (int k = 0; k < n; ++k) {
+        int j = accept_path[(size_t)b * T + k];
+        if (j < 0 || j >= T) bits |= ORC_BAD_PATH;
+      }
+    }
+    if (!bits && (long)L + n > Lmax) bits |= ORC_OVERFLOW;
+    status[b] |= bits;
+    if (bits) {
+      cache_len_out[b] = L;
+      continue;
+    }
+    for (int h = 0; h < Hkv; ++h)
+      for (int k = 0; k < n; ++k) {
+        int j = accept_path[(size_t)b * T + k];
+        size_t src = (((size_t)b * T + j) * Hkv + h) * row;
+        memcpy(tmp + ((size_t)(h * n + k) * 2 + 0) * row, (const unsigned char*)k_tree + src, row);
+        memcpy(tmp + ((size_t)(h * n + k) * 2 + 1) * row, (const unsigned char*)v_tree + src, row);
+      }
+    for (int h = 0; h < Hkv; ++h)
+      for (int k = 0; k < n; ++k) {
+        size_t dst = (((size_t)b * Hkv + h) * Lmax + L + k) * row;
+        memcpy((unsigned char*)k_cache + dst, tmp + ((size_t)(h * n + k) * 2 + 0) * row, row);
+        memcpy((unsigned char*)v_cache + dst, tmp + ((size_t)(h * n + k) * 2 + 1) * row, row);
+      }
+    cache_len_out[b] = L + n;
+  }
+  free(tmp);
+}

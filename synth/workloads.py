@@ -1,0 +1,349 @@
+"""Seeded synthetic workloads shaped like the pages' verification workloads.
+
+None of the pages' datasets (MT-bench, ShareGPT, HumanEval) nor any model
+weights are available, and the verification path needs neither: it only needs
+a draft tree, per-node draft and target tokens, a KV prefix and the q/k/v of
+the tree tokens.  Everything here is drawn from ``numpy.random.default_rng``
+seeded with ``SeedSequence([workload_id, b, stream, extra])`` where ``stream``
+is 0 for the tree and tokens, 1 for q, 2 for k/v and 3 for the prefix length,
+so every sequence of a batch is reproducible on its own.
+
+Trees for the larger workloads follow the EAGLE-2 dynamic draft tree
+(rainlin.net "EAGLE 系列", section 7: expand the top nodes of the deepest
+layer by path-product confidence, then rerank all candidates and keep the
+best, which stays a connected tree because a child's value never exceeds its
+parent's).  Target tokens follow the calibration observation of section 6
+(draft confidence approximates acceptance rate): the target picks a child of
+an expanded node with probability equal to that child's confidence.
+
+The worked 8-node tree It/is/has/a/the/to/good/be (rainlin.net section 4) is
+``worked_tree_parent()``.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+# Stream ids of the per-sequence seed sequences.
+STREAM_TREE, STREAM_Q, STREAM_KV, STREAM_LEN = 0, 1, 2, 3
+
+BF16_NAN_BITS = np.uint16(0x7FC0)
+LLAMA3_VOCAB = 128256  # any vocabulary at least as large as the branch width works
+
+
+@dataclasses.dataclass(frozen=True)
+class WorkloadSpec:
+    """Shape and tree recipe of one synthetic workload."""
+
+    wid: int                 # numeric id, first element of every seed sequence
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    L_lo: int                # prefix length ~ U{L_lo..L_hi}; L_lo == L_hi means fixed
+    L_hi: int
+    T: int
+    dtype: str               # "f32" or "bf16"
+    tree: str                # "worked" or "eagle2"
+    depth_max: int = 0
+    topk: int = 0
+    branch: int = 0
+    vocab: int = LLAMA3_VOCAB
+    desc: str = ""
+
+
+WORKLOADS: dict[str, WorkloadSpec] = {
+    s.name: s
+    for s in [
+        WorkloadSpec(1, "worked_tree_fp32", B=1, Hq=2, Hkv=1, D=64, L_lo=16, L_hi=16, T=8,
+                     dtype="f32", tree="worked", vocab=1000,
+                     desc="worked 8-node tree It/is/has/a/the/to/good/be, prefix 16, 2 query heads on 1 KV "
+                          "head, head_dim 64, fp32"),
+        WorkloadSpec(2, "llama8b_b1_L4096_T60", B=1, Hq=32, Hkv=8, D=128, L_lo=4096, L_hi=4096, T=60,
+                     dtype="bf16", tree="eagle2", depth_max=6, topk=10, branch=10,
+                     desc="Llama-3-8B-like layer: batch 1, 32/8 heads, head_dim 128, prefix 4096, 60-node "
+                          "EAGLE-2 tree (depth<=6, top-10 expand, 10 children), bf16"),
+        WorkloadSpec(3, "batch32_L512-4096_T60", B=32, Hq=32, Hkv=8, D=128, L_lo=512, L_hi=4096, T=60,
+                     dtype="bf16", tree="eagle2", depth_max=6, topk=10, branch=10,
+                     desc="continuous batch: 32 sequences, prefix U[512,4096], 32/8 heads, head_dim 128, "
+                          "60-node EAGLE-2 tree per sequence, bf16"),
+        WorkloadSpec(4, "llama70b_b8_L32768_T64", B=8, Hq=64, Hkv=8, D=128, L_lo=32768, L_hi=32768, T=64,
+                     dtype="bf16", tree="eagle2", depth_max=8, topk=10, branch=10,
+                     desc="70B-like layer, long context: batch 8, 64/8 heads, head_dim 128, prefix 32768, "
+                          "64-node EAGLE-2 tree (depth<=8), bf16"),
+        WorkloadSpec(5, "wide_b64_L1024-8192_T128", B=64, Hq=32, Hkv=8, D=128, L_lo=1024, L_hi=8192,
+                     T=128, dtype="bf16", tree="eagle2", depth_max=10, topk=16, branch=16,
+                     desc="wide-tree stress: batch 64, prefix U[1024,8192], 32/8 heads, head_dim 128, "
+                          "128-node tree (depth<=10, 16-way expansion), bf16"),
+    ]
+}
+
+
+def _rng(wid: int, b: int, stream: int, extra: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([wid, b, stream, extra]))
+
+
+# ----------------------------------------------------------------------------------------------
+# bf16 storage helpers (input encoding only)
+# ----------------------------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); return the raw bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_NAN_BITS
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ----------------------------------------------------------------------------------------------
+# trees and tokens
+# ----------------------------------------------------------------------------------------------
+def worked_tree_parent() -> np.ndarray:
+    """Parent array of the worked tree It/is/has/a/the/to/good/be in its flattened level order."""
+    return np.array([-1, 0, 0, 1, 1, 2, 3, 5], dtype=np.int32)
+
+
+def random_parent(rng: np.random.Generator, T: int, kind: str = "random") -> np.ndarray:
+    """A valid level-ordered tree (parent[0] = -1, 0 <= parent[i] < i) of the given kind."""
+    p = np.empty(T, dtype=np.int32)
+    p[0] = -1
+    if T == 1:
+        return p
+    if kind == "chain":
+        p[1:] = np.arange(T - 1, dtype=np.int32)
+    elif kind == "star":
+        p[1:] = 0
+    elif kind == "random":
+        for i in range(1, T):
+            p[i] = rng.integers(0, i)
+    elif kind == "deep":  # mostly chain-like with occasional branches
+        for i in range(1, T):
+            p[i] = i - 1 if rng.random() < 0.8 else rng.integers(0, i)
+    else:
+        raise ValueError(kind)
+    return p
+
+
+def _children(parent: np.ndarray) -> list[list[int]]:
+    kids: list[list[int]] = [[] for _ in range(len(parent))]
+    for i in range(1, len(parent)):
+        kids[int(parent[i])].append(i)
+    return kids
+
+
+def _worked_tree_tokens(rng: np.random.Generator, vocab: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Tokens for the worked tree: draft uniform in [0, vocab); a node with children gets, with
+    probability 0.7, the token of one child picked uniformly, otherwise a uniform token that no
+    child carries; a leaf gets a uniform token."""
+    parent = worked_tree_parent()
+    T = len(parent)
+    draft = rng.integers(0, vocab, size=T).astype(np.int32)
+    target = np.empty(T, dtype=np.int32)
+    kids = _children(parent)
+    for u in range(T):
+        if kids[u] and rng.random() < 0.7:
+            target[u] = draft[kids[u][int(rng.integers(0, len(kids[u])))]]
+        else:
+            child_toks = {int(draft[c]) for c in kids[u]}
+            while True:
+                tok = int(rng.integers(0, vocab))
+                if tok not in child_toks:
+                    break
+            target[u] = tok
+    return parent, draft, target
+
+
+def eagle2_tree(rng: np.random.Generator, T: int, depth_max: int, topk: int, branch: int,
+                vocab: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """EAGLE-2-style dynamic draft tree with calibrated synthetic targets.
+
+    Expansion: at each level take the ``topk`` nodes of the deepest layer with the largest
+    path-product value (ties: earlier-created node first) and give each ``branch`` children
+    whose confidences are the softmax of ``branch`` N(0, variance 2) logits and whose tokens are
+    distinct.  A child's value is its parent's value times its confidence.
+    Rerank: keep the ``T`` nodes of largest value (ties: shallower, then earlier).  Because every
+    confidence is below one, a parent always outranks its children, so the kept set is a tree.
+    Flattening: order by (depth, flattened index of the parent, confidence rank among siblings).
+    Targets: an expanded node's target is the token of one of its children (kept or not) drawn
+    with probability equal to the child's confidence; an unexpanded node gets a uniform token.
+    """
+    depth = [0]
+    par = [-1]
+    value = [1.0]
+    token = [int(rng.integers(0, vocab))]
+    rank = [0]
+    expanded: dict[int, tuple[list[int], np.ndarray]] = {}
+    frontier = [0]
+    for _level in range(1, depth_max + 1):
+        chosen = sorted(frontier, key=lambda n: (-value[n], n))[:topk]
+        new_frontier: list[int] = []
+        for u in chosen:
+            logits = rng.normal(0.0, math.sqrt(2.0), size=branch)
+            e = np.exp(logits - logits.max())
+            conf = e / e.sum()
+            toks = rng.choice(vocab, size=branch, replace=False)
+            order = np.argsort(-conf, kind="stable")
+            kid_ids = []
+            for r, ci in enumerate(order):
+                nid = len(depth)
+                depth.append(depth[u] + 1)
+                par.append(u)
+                value.append(value[u] * float(conf[ci]))
+                token.append(int(toks[ci]))
+                rank.append(r)
+                kid_ids.append(nid)
+                new_frontier.append(nid)
+            expanded[u] = (kid_ids, conf[order])
+        frontier = new_frontier
+    n_all = len(depth)
+    if T > n_all:
+        raise ValueError(f"tree budget {T} exceeds {n_all} candidates")
+    keep = sorted(range(n_all), key=lambda n: (-value[n], depth[n], n))[:T]
+    keep_set = set(keep)
+    for n in keep:
+        if par[n] >= 0 and par[n] not in keep_set:
+            raise AssertionError("reranked set is not ancestor-closed")
+    flat_of: dict[int, int] = {}
+    order_nodes = sorted(keep, key=lambda n: (depth[n], -1 if par[n] < 0 else 0, n))
+    # assign flattened indices level by level so the parent's flattened index is known
+    by_depth: dict[int, list[int]] = {}
+    for n in order_nodes:
+        by_depth.setdefault(depth[n], []).append(n)
+    flat: list[int] = []
+    for d in sorted(by_depth):
+        level_nodes = sorted(by_depth[d], key=lambda n: (-1 if par[n] < 0 else flat_of[par[n]], rank[n]))
+        for n in level_nodes:
+            flat_of[n] = len(flat)
+            flat.append(n)
+    parent = np.array([-1 if par[n] < 0 else flat_of[par[n]] for n in flat], dtype=np.int32)
+    draft = np.array([token[n] for n in flat], dtype=np.int32)
+    target = np.empty(T, dtype=np.int32)
+    for i, n in enumerate(flat):
+        if n in expanded:
+            kid_ids, conf = expanded[n]
+            pick = int(rng.choice(len(kid_ids), p=conf / conf.sum()))
+            target[i] = token[kid_ids[pick]]
+        else:
+            target[i] = int(rng.integers(0, vocab))
+    return parent, draft, target
+
+
+# ----------------------------------------------------------------------------------------------
+# whole workloads
+# ----------------------------------------------------------------------------------------------
+@dataclasses.dataclass
+class Workload:
+    """Host arrays of one verification step.  Floating tensors are float32 arrays for
+    ``dtype == "f32"`` and raw bfloat16 bit patterns (uint16) for ``dtype == "bf16"``."""
+
+    spec: WorkloadSpec
+    B: int
+    T: int
+    Hq: int
+    Hkv: int
+    D: int
+    Lmax: int
+    dtype: str
+    parent: np.ndarray       # [B,T] int32
+    draft: np.ndarray        # [B,T] int32
+    target: np.ndarray       # [B,T] int32
+    cache_len: np.ndarray    # [B] int32
+    q: np.ndarray            # [B,T,Hq,D]
+    k_cache: np.ndarray      # [B,Hkv,Lmax,D]; rows >= cache_len[b] are NaN
+    v_cache: np.ndarray
+    k_tree: np.ndarray       # [B,T,Hkv,D]
+    v_tree: np.ndarray
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def kv_prefix_bytes(self) -> int:
+        elem = 4 if self.dtype == "f32" else 2
+        return int(self.cache_len.astype(np.int64).sum()) * self.Hkv * self.D * 2 * elem
+
+
+def _normal(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return x if dtype == "f32" else f32_to_bf16_bits(x)
+
+
+def make_workload(spec: WorkloadSpec | str, extra_seed: int = 0, B: int | None = None,
+                  T: int | None = None, L: tuple[int, int] | None = None,
+                  Hq: int | None = None, Hkv: int | None = None, D: int | None = None,
+                  dtype: str | None = None, parent_kind: str | None = None,
+                  lmax_pad: int = 64, with_kv: bool = True) -> Workload:
+    """Draw one workload.  Keyword overrides shrink or reshape a spec for tests (the tree
+    recipe of the spec is kept unless ``parent_kind`` asks for a random shape instead)."""
+    if isinstance(spec, str):
+        spec = WORKLOADS[spec]
+    B = spec.B if B is None else B
+    T = spec.T if T is None else T
+    Hq = spec.Hq if Hq is None else Hq
+    Hkv = spec.Hkv if Hkv is None else Hkv
+    D = spec.D if D is None else D
+    dtype = spec.dtype if dtype is None else dtype
+    L_lo, L_hi = (spec.L_lo, spec.L_hi) if L is None else L
+    wid = spec.wid
+
+    parent = np.empty((B, T), np.int32)
+    draft = np.empty((B, T), np.int32)
+    target = np.empty((B, T), np.int32)
+    cache_len = np.empty(B, np.int32)
+    for b in range(B):
+        rt = _rng(wid, b, STREAM_TREE, extra_seed)
+        if parent_kind is not None:
+            p = random_parent(rt, T, parent_kind)
+            small_vocab = 4  # small vocabulary: matches and duplicate siblings are frequent
+            parent[b] = p
+            draft[b] = rt.integers(0, small_vocab, size=T)
+            target[b] = rt.integers(0, small_vocab, size=T)
+        elif spec.tree == "worked":
+            if T != 8:
+                raise ValueError("the worked tree has 8 nodes")
+            parent[b], draft[b], target[b] = _worked_tree_tokens(rt, spec.vocab)
+        else:
+            parent[b], draft[b], target[b] = eagle2_tree(rt, T, spec.depth_max, spec.topk,
+                                                         spec.branch, spec.vocab)
+        rl = _rng(wid, b, STREAM_LEN, extra_seed)
+        cache_len[b] = L_lo if L_lo == L_hi else int(rl.integers(L_lo, L_hi + 1))
+
+    Lmax = int(cache_len.max()) + T
+    Lmax = ((Lmax + lmax_pad - 1) // lmax_pad) * lmax_pad
+
+    store = np.float32 if dtype == "f32" else np.uint16
+    nan = np.float32(np.nan) if dtype == "f32" else BF16_NAN_BITS
+    q = np.empty((B, T, Hq, D), store)
+    if with_kv:
+        k_cache = np.full((B, Hkv, Lmax, D), nan, store)
+        v_cache = np.full((B, Hkv, Lmax, D), nan, store)
+    else:
+        k_cache = v_cache = np.empty((0,), store)
+    k_tree = np.empty((B, T, Hkv, D), store)
+    v_tree = np.empty((B, T, Hkv, D), store)
+    for b in range(B):
+        q[b] = _normal(_rng(wid, b, STREAM_Q, extra_seed), (T, Hq, D), dtype)
+        rkv = _rng(wid, b, STREAM_KV, extra_seed)
+        Lb = int(cache_len[b])
+        if with_kv:
+            k_cache[b, :, :Lb] = _normal(rkv, (Hkv, Lb, D), dtype)
+            v_cache[b, :, :Lb] = _normal(rkv, (Hkv, Lb, D), dtype)
+        k_tree[b] = _normal(rkv, (T, Hkv, D), dtype)
+        v_tree[b] = _normal(rkv, (T, Hkv, D), dtype)
+    return Workload(spec=spec, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, Lmax=Lmax, dtype=dtype,
+                    parent=parent, draft=draft, target=target, cache_len=cache_len, q=q,
+                    k_cache=k_cache, v_cache=v_cache, k_tree=k_tree, v_tree=v_tree)

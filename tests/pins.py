@@ -1,0 +1,510 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function takes a loaded oracle library and raises ``AssertionError`` when the
+oracle disagrees with something the pages or the mathematics fix:
+
+* the worked tree and its printed mask row (tests/golden/worked_tree.txt);
+* an independent closure formulation of "self plus ancestors" (boolean reachability through
+  repeated parent steps) on every tree of up to 6 nodes and on random trees of up to 128;
+* closed forms of attention (K = 0 with one-hot V rows; scale 0 gives the mean of the visible
+  rows), textbook causal attention from ``torch.nn.functional.scaled_dot_product_attention`` on
+  chain trees and single-node trees, and an explicit dense-mask softmax on random trees;
+* hand-derived acceptance cases (tests/golden/accept_hand_cases.txt), the chain extremes and a
+  brute-force enumeration of root-to-node paths;
+* compaction against direct row selection, including tree rows that live inside the cache.
+
+``test_oracle_pins.py`` runs every pin against the oracle; ``test_oracle_mutants.py`` runs them
+against deliberately broken copies of the oracle source to show that each plausible mistake is
+caught by at least one pin.
+"""
+from __future__ import annotations
+
+import itertools
+import os
+
+import numpy as np
+
+from oracle import oracle as O
+from synth import f32_to_bf16_bits, random_parent, worked_tree_parent
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------------------------------------
+# helpers (independent formulations)
+# ----------------------------------------------------------------------------------------------
+def closure_mask(parent: np.ndarray) -> np.ndarray:
+    """Dense bool [T,T]: reach[i, j] iff j == i or j is reached from i by parent steps.
+    Computed as the fixed point of R <- R | (R @ A) with A[i, parent(i)] = 1."""
+    T = len(parent)
+    A = np.zeros((T, T), dtype=np.int64)
+    for i in range(T):
+        if parent[i] >= 0:
+            A[i, parent[i]] = 1
+    R = np.eye(T, dtype=np.int64)
+    while True:
+        Rn = ((R + R @ A) > 0).astype(np.int64)
+        if (Rn == R).all():
+            return R.astype(bool)
+        R = Rn
+
+
+def bits_to_dense(anc_row: np.ndarray, T: int) -> np.ndarray:
+    out = np.zeros(T, bool)
+    for j in range(T):
+        out[j] = (int(anc_row[j // 64]) >> (j % 64)) & 1
+    return out
+
+
+def read_worked_tree():
+    rows = []
+    tokens = None
+    with open(os.path.join(GOLDEN, "worked_tree.txt"), encoding="utf-8") as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("tokens"):
+                tokens = line.split()[1:]
+                continue
+            idx, tok, par, vis, src = line.split()
+            rows.append((int(idx), tok, int(par), vis.split(","), src))
+    return tokens, rows
+
+
+def read_accept_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "accept_hand_cases.txt"), encoding="utf-8") as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, rest = line.split(":", 1)
+            draft, target, path, bonus = (x.strip() for x in rest.split("|"))
+            cases.append((name, draft.split(), target.split(), [int(x) for x in path.split(",")],
+                          bonus))
+    return cases
+
+
+def dense_tree_attention(q, k_cache, v_cache, cache_len, k_tree, v_tree, parent, scale):
+    """Explicit masked softmax over [prefix ++ all T tree rows] with the closure mask; KV heads
+    repeated G times (numpy, float64)."""
+    q, k_cache, v_cache, k_tree, v_tree = (np.asarray(x, np.float64)
+                                           for x in (q, k_cache, v_cache, k_tree, v_tree))
+    B, T, Hq, D = q.shape
+    Hkv = k_tree.shape[2]
+    G = Hq // Hkv
+    out = np.zeros((B, T, Hq, D))
+    lse = np.zeros((B, T, Hq))
+    for b in range(B):
+        L = int(cache_len[b])
+        keys = np.concatenate([k_cache[b, :, :L, :], k_tree[b].transpose(1, 0, 2)], axis=1)
+        vals = np.concatenate([v_cache[b, :, :L, :], v_tree[b].transpose(1, 0, 2)], axis=1)
+        keys = np.repeat(keys, G, axis=0)  # [Hq, L+T, D]
+        vals = np.repeat(vals, G, axis=0)
+        vis = np.concatenate([np.ones((T, L), bool), closure_mask(parent[b])], axis=1)  # [T, L+T]
+        s = np.einsum("thd,hkd->thk", q[b], keys) * scale
+        s = np.where(vis[:, None, :], s, -np.inf)
+        m = s.max(axis=-1, keepdims=True)
+        w = np.exp(s - m)
+        den = w.sum(axis=-1, keepdims=True)
+        out[b] = np.einsum("thk,hkd->thd", w, vals) / den
+        lse[b] = (m + np.log(den))[..., 0]
+    return out, lse
+
+
+def _rand(rng, shape, dtype):
+    x = rng.standard_normal(size=shape).astype(np.float32)
+    return x if dtype == "f32" else f32_to_bf16_bits(x)
+
+
+def _as_f64(x, dtype):
+    if dtype == "f32":
+        return x.astype(np.float64)
+    return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def small_case(rng, B=2, T=7, Hq=4, Hkv=2, D=16, Ls=(5, 9), dtype="f32", kind="random"):
+    parent = np.stack([random_parent(rng, T, kind) for _ in range(B)])
+    cache_len = np.array([Ls[b % len(Ls)] for b in range(B)], np.int32)
+    Lmax = int(cache_len.max()) + T + 3
+    nan = np.float32(np.nan) if dtype == "f32" else np.uint16(0x7FC0)
+    store = np.float32 if dtype == "f32" else np.uint16
+    k_cache = np.full((B, Hkv, Lmax, D), nan, store)
+    v_cache = np.full((B, Hkv, Lmax, D), nan, store)
+    for b in range(B):
+        L = int(cache_len[b])
+        k_cache[b, :, :L] = _rand(rng, (Hkv, L, D), dtype)
+        v_cache[b, :, :L] = _rand(rng, (Hkv, L, D), dtype)
+    q = _rand(rng, (B, T, Hq, D), dtype)
+    k_tree = _rand(rng, (B, T, Hkv, D), dtype)
+    v_tree = _rand(rng, (B, T, Hkv, D), dtype)
+    return dict(q=q, k_cache=k_cache, v_cache=v_cache, cache_len=cache_len, k_tree=k_tree,
+                v_tree=v_tree, parent=parent)
+
+
+# ----------------------------------------------------------------------------------------------
+# mask pins
+# ----------------------------------------------------------------------------------------------
+def pin_worked_tree_mask(lib):
+    tokens, rows = read_worked_tree()
+    parent = np.array([r[2] for r in rows], np.int32)
+    assert (parent == worked_tree_parent()).all()
+    anc, st = O.build_mask(parent[None], lib=lib)
+    assert st[0] == 0
+    for idx, tok, _par, vis, src in rows:
+        got = [tokens[j] for j in range(len(tokens)) if bits_to_dense(anc[0, idx], 8)[j]]
+        assert got == vis, (tok, got, vis, src)
+    # the printed row: "good" sees exactly It, is, a, good -> bits 0, 1, 3, 6
+    assert int(anc[0, 6, 0]) == 0b01001011
+
+
+def pin_mask_closure_bruteforce(lib):
+    for T in range(1, 7):
+        for choice in itertools.product(*[range(i) for i in range(1, T)]):
+            parent = np.array([-1, *choice], np.int32)
+            anc, st = O.build_mask(parent[None], lib=lib)
+            assert st[0] == 0
+            R = closure_mask(parent)
+            for i in range(T):
+                assert (bits_to_dense(anc[0, i], T) == R[i]).all(), (parent, i)
+
+
+def pin_mask_closure_random(lib):
+    rng = np.random.default_rng(11)
+    for T in (1, 2, 63, 64, 65, 100, 127, 128):
+        for kind in ("random", "chain", "star", "deep"):
+            parent = random_parent(rng, T, kind)
+            anc, st = O.build_mask(parent[None], lib=lib)
+            assert st[0] == 0
+            assert anc.shape == (1, T, (T + 63) // 64)
+            R = closure_mask(parent)
+            for i in range(T):
+                assert (bits_to_dense(anc[0, i], T) == R[i]).all(), (kind, T, i)
+            # no bit at or beyond T
+            for i in range(T):
+                for w in range(anc.shape[2]):
+                    hi = T - 64 * w
+                    if hi < 64:
+                        assert int(anc[0, i, w]) >> max(hi, 0) == 0
+
+
+def pin_mask_invalid_trees(lib):
+    bad = [[0, 0, 1], [-1, 1, 0], [-1, 0, 3], [-1, -1, 0], [-1, 0, 2]]
+    for p in bad:
+        parent = np.array(p, np.int32)
+        anc, st = O.build_mask(parent[None], lib=lib)
+        assert st[0] == O.ORC_BAD_TREE, p
+        for i in range(len(p)):
+            assert int(anc[0, i, 0]) == 1 << i, p
+
+
+# ----------------------------------------------------------------------------------------------
+# attention pins
+# ----------------------------------------------------------------------------------------------
+def pin_visibility_probe(lib):
+    """K = 0, V rows one-hot: every visible key gets weight 1 / (#visible); the worked tree's
+    "good" row (prefix 16) is 1/20 on columns 0..15 and 16 + {0, 1, 3, 6}."""
+    parent = worked_tree_parent()
+    T, L, D, Hq, Hkv = 8, 16, 64, 2, 1
+    Lmax = L + T
+    k_cache = np.zeros((1, Hkv, Lmax, D), np.float32)
+    v_cache = np.zeros((1, Hkv, Lmax, D), np.float32)
+    k_cache[0, 0, L:] = np.nan  # rows past the prefix must never be read
+    v_cache[0, 0, L:] = np.nan
+    for j in range(L):
+        v_cache[0, 0, j, j] = 1.0
+    k_tree = np.zeros((1, T, Hkv, D), np.float32)
+    v_tree = np.zeros((1, T, Hkv, D), np.float32)
+    for t in range(T):
+        v_tree[0, t, 0, L + t] = 1.0
+    q = np.random.default_rng(3).standard_normal((1, T, Hq, D)).astype(np.float32)
+    out, lse = O.attention(q, k_cache, v_cache, np.array([L], np.int32), k_tree, v_tree,
+                           parent[None], lib=lib)
+    R = closure_mask(parent)
+    for i in range(T):
+        n_vis = L + int(R[i].sum())
+        want = np.zeros(D)
+        want[:L] = 1.0 / n_vis
+        want[L + np.nonzero(R[i])[0]] = 1.0 / n_vis
+        for h in range(Hq):
+            assert np.abs(out[0, i, h] - want).max() < 1e-15, (i, h)
+            assert abs(lse[0, i, h] - np.log(n_vis)) < 1e-14
+    good = out[0, 6, 0]
+    assert np.allclose(good[[0, 15, 16, 17, 19, 22]], 1 / 20) and good[[18, 20, 21, 23]].max() == 0
+
+
+def pin_scale_zero_is_mean(lib):
+    rng = np.random.default_rng(5)
+    c = small_case(rng, B=2, T=6, Hq=4, Hkv=2, D=8)
+    out, lse = O.attention(**c, scale=0.0, lib=lib)
+    R = [closure_mask(c["parent"][b]) for b in range(2)]
+    for b in range(2):
+        L = int(c["cache_len"][b])
+        for i in range(6):
+            for h in range(4):
+                kvh = h // 2
+                rows = [c["v_cache"][b, kvh, j] for j in range(L)]
+                rows += [c["v_tree"][b, j, kvh] for j in np.nonzero(R[b][i])[0]]
+                want = np.mean(np.array(rows, np.float64), axis=0)
+                assert np.abs(out[b, i, h] - want).max() < 1e-12
+                assert abs(lse[b, i, h] - np.log(len(rows))) < 1e-12
+
+
+def _sdpa_chain(q, k_cache, v_cache, L, k_tree, v_tree, scale):
+    """Chain tree (node t's path is 0..t) as textbook causal attention of the last T positions
+    of prefix ++ chain, via torch's CPU scaled_dot_product_attention with an explicit mask."""
+    import torch
+
+    T, Hq, D = q.shape
+    Hkv = k_tree.shape[1]
+    G = Hq // Hkv
+    K = np.concatenate([k_cache[:, :L, :], k_tree.transpose(1, 0, 2)], axis=1)  # [Hkv, L+T, D]
+    V = np.concatenate([v_cache[:, :L, :], v_tree.transpose(1, 0, 2)], axis=1)
+    Kt = torch.from_numpy(K).repeat_interleave(G, dim=0)
+    Vt = torch.from_numpy(V).repeat_interleave(G, dim=0)
+    Qt = torch.from_numpy(q.transpose(1, 0, 2).copy())  # [Hq, T, D]
+    # query t sits at absolute position L + t and sees keys 0 .. L + t
+    allowed = torch.arange(L + T)[None, :] <= (L + torch.arange(T))[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(Qt, Kt, Vt, attn_mask=allowed,
+                                                         scale=scale)
+    s = (Qt @ Kt.transpose(-1, -2)) * scale
+    s = s.masked_fill(~allowed, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return o.numpy().transpose(1, 0, 2), lse.numpy().T
+
+
+def pin_chain_matches_causal_sdpa(lib):
+    rng = np.random.default_rng(7)
+    for dtype in ("f32", "bf16"):
+        for (L, T, Hq, Hkv, D) in [(16, 8, 2, 1, 64), (33, 5, 4, 2, 32), (0, 4, 3, 3, 8)]:
+            c = small_case(rng, B=1, T=T, Hq=Hq, Hkv=Hkv, D=D, Ls=(L,), dtype=dtype, kind="chain")
+            out, lse = O.attention(**c, lib=lib)
+            f = lambda x: _as_f64(x, dtype)  # noqa: E731
+            want, want_lse = _sdpa_chain(f(c["q"][0]), f(c["k_cache"][0]), f(c["v_cache"][0]), L,
+                                         f(c["k_tree"][0]), f(c["v_tree"][0]), 1 / np.sqrt(D))
+            assert np.abs(out[0] - want).max() < 1e-12, (dtype, L, T)
+            assert np.abs(lse[0] - want_lse).max() < 1e-12
+
+
+def pin_single_node_is_decode(lib):
+    """T = 1: ordinary decode attention of one query over prefix ++ itself."""
+    import torch
+
+    rng = np.random.default_rng(9)
+    for L in (0, 1, 50):
+        c = small_case(rng, B=1, T=1, Hq=4, Hkv=1, D=16, Ls=(L,))
+        out, lse = O.attention(**c, lib=lib)
+        K = np.concatenate([c["k_cache"][0, 0, :L], c["k_tree"][0, :, 0]], axis=0).astype(np.float64)
+        V = np.concatenate([c["v_cache"][0, 0, :L], c["v_tree"][0, :, 0]], axis=0).astype(np.float64)
+        Q = c["q"][0, 0].astype(np.float64)  # [Hq, D]
+        o = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q)[:, None, :], torch.from_numpy(K)[None].expand(4, -1, -1),
+            torch.from_numpy(V)[None].expand(4, -1, -1), scale=0.25)
+        assert np.abs(out[0, 0] - o.numpy()[:, 0, :]).max() < 1e-12
+
+
+def pin_dense_mask_bruteforce(lib):
+    rng = np.random.default_rng(13)
+    for kind in ("random", "star", "deep"):
+        for dtype in ("f32", "bf16"):
+            c = small_case(rng, B=3, T=9, Hq=6, Hkv=2, D=12, Ls=(0, 4, 11), dtype=dtype, kind=kind)
+            out, lse = O.attention(**c, lib=lib)
+            f = {k: (_as_f64(v, dtype) if k in ("q", "k_cache", "v_cache", "k_tree", "v_tree")
+                     else v) for k, v in c.items()}
+            want, want_lse = dense_tree_attention(**f, scale=1 / np.sqrt(12))
+            assert np.abs(out - want).max() < 1e-12, (kind, dtype)
+            assert np.abs(lse - want_lse).max() < 1e-12
+
+
+def pin_per_path_invariant(lib):
+    """A tree pass equals verifying each root-to-node path on its own."""
+    rng = np.random.default_rng(17)
+    c = small_case(rng, B=1, T=10, Hq=4, Hkv=2, D=16, Ls=(12,), kind="random")
+    out, lse = O.attention(**c, lib=lib)
+    paths, st = O.tree_paths(c["parent"][0], lib=lib)
+    assert st == 0
+    for i in range(10):
+        p = paths[i]
+        n = len(p)
+        sub = dict(q=c["q"][:, p], k_cache=c["k_cache"], v_cache=c["v_cache"],
+                   cache_len=c["cache_len"], k_tree=c["k_tree"][:, p], v_tree=c["v_tree"][:, p],
+                   parent=np.arange(-1, n - 1, dtype=np.int32)[None])
+        o2, l2 = O.attention(**sub, lib=lib)
+        assert np.abs(o2[0, n - 1] - out[0, i]).max() < 1e-13
+        assert np.abs(l2[0, n - 1] - lse[0, i]).max() < 1e-13
+
+
+def pin_selected_rows_match_full(lib):
+    rng = np.random.default_rng(19)
+    c = small_case(rng, B=2, T=5, Hq=4, Hkv=2, D=8, Ls=(3, 7))
+    out, lse = O.attention(**c, lib=lib)
+    rows = np.array([[1, 3, 4], [0, 0, 0], [1, 1, 2]], np.int32)
+    o2, l2 = O.attention(**c, rows=rows, lib=lib)
+    for r, (b, h, i) in enumerate(rows):
+        assert (o2[r] == out[b, i, h]).all() and l2[r] == lse[b, i, h]
+
+
+# ----------------------------------------------------------------------------------------------
+# acceptance pins
+# ----------------------------------------------------------------------------------------------
+def pin_accept_hand_cases(lib):
+    parent = worked_tree_parent()
+    for name, draft, target, want_path, want_bonus in read_accept_cases():
+        names = sorted(set(draft) | set(target))
+        ids = {n: k for k, n in enumerate(names)}
+        d = np.array([[ids[x] for x in draft]], np.int32)
+        t = np.array([[ids[x] for x in target]], np.int32)
+        path, n, bonus = O.accept(parent[None], d, t, lib=lib)
+        assert list(path[0, : n[0]]) == want_path, name
+        assert (path[0, n[0]:] == -1).all(), name
+        assert bonus[0] == ids[want_bonus], name
+
+
+def pin_accept_chain_extremes(lib):
+    T = 9
+    parent = np.arange(-1, T - 1, dtype=np.int32)[None]
+    draft = np.arange(100, 100 + T, dtype=np.int32)[None]
+    target = np.roll(draft, -1, axis=1)
+    target[0, -1] = 7
+    path, n, bonus = O.accept(parent, draft, target, lib=lib)
+    assert n[0] == T and list(path[0]) == list(range(T)) and bonus[0] == 7
+    path, n, bonus = O.accept(parent, draft, np.full_like(draft, 5), lib=lib)
+    assert n[0] == 1 and path[0, 0] == 0 and (path[0, 1:] == -1).all() and bonus[0] == 5
+
+
+def _brute_accept(parent, draft, target):
+    T = len(parent)
+    kids = [[] for _ in range(T)]
+    for i in range(1, T):
+        kids[parent[i]].append(i)
+    best = [0]
+
+    def dfs(path):
+        nonlocal best
+        if len(path) > len(best) or (len(path) == len(best) and path[-1] < best[-1]):
+            best = list(path)
+        for c in kids[path[-1]]:
+            if draft[c] == target[path[-1]]:
+                dfs(path + [c])
+
+    dfs([0])
+    return best, int(target[best[-1]])
+
+
+def pin_accept_bruteforce(lib):
+    rng = np.random.default_rng(23)
+    for trial in range(300):
+        T = int(rng.integers(1, 14))
+        parent = random_parent(rng, T, ["random", "star", "chain", "deep"][trial % 4])
+        vocab = int(rng.integers(1, 4))
+        draft = rng.integers(0, vocab, T).astype(np.int32)
+        target = rng.integers(0, vocab, T).astype(np.int32)
+        path, n, bonus = O.accept(parent[None], draft[None], target[None], lib=lib)
+        want, wb = _brute_accept(parent, draft, target)
+        assert list(path[0, : n[0]]) == want, (parent, draft, target)
+        assert bonus[0] == wb
+
+
+# ----------------------------------------------------------------------------------------------
+# compaction pins
+# ----------------------------------------------------------------------------------------------
+def pin_compact_hand_case(lib):
+    """Prefix 16, accepted path [0, 1, 3, 6]: cache rows 16..19 <- tree rows 0, 1, 3, 6."""
+    D, T, L, Lmax = 4, 8, 16, 32
+    k_cache = np.full((1, 1, Lmax, D), -1.0, np.float32)
+    v_cache = np.full((1, 1, Lmax, D), -2.0, np.float32)
+    k_tree = np.arange(T * D, dtype=np.float32).reshape(1, T, 1, D)
+    v_tree = -k_tree
+    path = np.array([[0, 1, 3, 6, -1, -1, -1, -1]], np.int32)
+    out_len, st = O.compact(k_cache, v_cache, np.array([L], np.int32), k_tree, v_tree, path,
+                            np.array([4], np.int32), lib=lib)
+    assert out_len[0] == 20 and st[0] == 0
+    for r, j in zip(range(16, 20), [0, 1, 3, 6]):
+        assert (k_cache[0, 0, r] == k_tree[0, j, 0]).all() and (v_cache[0, 0, r] == v_tree[0, j, 0]).all()
+    assert (k_cache[0, 0, :16] == -1).all() and (k_cache[0, 0, 20:] == -1).all()
+    assert (v_cache[0, 0, 20:] == -2).all()
+
+
+def pin_compact_alias(lib):
+    """Tree rows stored in the cache itself at rows 16..23: the same result as from a copy."""
+    D, T, L, Lmax = 4, 8, 16, 32
+    base = np.random.default_rng(29).standard_normal((1, 1, Lmax, D)).astype(np.float32)
+    k_cache = base.copy()
+    v_cache = -base.copy()
+    k_tree_copy = k_cache[0, 0, L:L + T].reshape(1, T, 1, D).copy()
+    v_tree_copy = v_cache[0, 0, L:L + T].reshape(1, T, 1, D).copy()
+    k_view = k_cache[0, 0, L:L + T].reshape(1, T, 1, D)
+    v_view = v_cache[0, 0, L:L + T].reshape(1, T, 1, D)
+    assert np.shares_memory(k_view, k_cache)
+    path = np.array([[0, 1, 3, 6, -1, -1, -1, -1]], np.int32)
+    out_len, st = O.compact(k_cache, v_cache, np.array([L], np.int32), k_view, v_view, path,
+                            np.array([4], np.int32), lib=lib)
+    assert out_len[0] == 20
+    for r, j in enumerate([0, 1, 3, 6]):
+        assert (k_cache[0, 0, L + r] == k_tree_copy[0, j, 0]).all()
+        assert (v_cache[0, 0, L + r] == v_tree_copy[0, j, 0]).all()
+    assert (k_cache[0, 0, :L] == base[0, 0, :L]).all()
+    assert (k_cache[0, 0, L + 4:] == base[0, 0, L + 4:]).all()
+
+
+def pin_compact_random(lib):
+    rng = np.random.default_rng(31)
+    B, T, Hkv, D = 5, 9, 3, 8
+    cache_len = np.array([0, 3, 10, 20, 17], np.int32)
+    Lmax = 26
+    k_cache = rng.standard_normal((B, Hkv, Lmax, D)).astype(np.float32)
+    v_cache = rng.standard_normal((B, Hkv, Lmax, D)).astype(np.float32)
+    k_tree = rng.standard_normal((B, T, Hkv, D)).astype(np.float32)
+    v_tree = rng.standard_normal((B, T, Hkv, D)).astype(np.float32)
+    paths = np.full((B, T), -1, np.int32)
+    lens = np.array([9, 2, 1, 7, 5], np.int32)  # sequence 3: 20 + 7 > 26 overflows
+    for b in range(B):
+        chosen = np.sort(rng.choice(T, size=lens[b], replace=False))
+        chosen[0] = 0
+        paths[b, : lens[b]] = np.sort(chosen)
+    k0, v0 = k_cache.copy(), v_cache.copy()
+    out_len, st = O.compact(k_cache, v_cache, cache_len, k_tree, v_tree, paths, lens, lib=lib)
+    for b in range(B):
+        L, n = int(cache_len[b]), int(lens[b])
+        if L + n > Lmax:
+            assert st[b] == O.ORC_OVERFLOW and out_len[b] == L
+            assert (k_cache[b] == k0[b]).all() and (v_cache[b] == v0[b]).all()
+            continue
+        assert st[b] == 0 and out_len[b] == L + n
+        want_k, want_v = k0[b].copy(), v0[b].copy()
+        want_k[:, L:L + n] = k_tree[b, paths[b, :n]].transpose(1, 0, 2)
+        want_v[:, L:L + n] = v_tree[b, paths[b, :n]].transpose(1, 0, 2)
+        assert (k_cache[b] == want_k).all() and (v_cache[b] == want_v).all()
+    # malformed lengths and path entries commit nothing
+    k1 = k_cache.copy()
+    st = np.zeros(B, np.int32)
+    bad_len = np.array([-1, 3, 10, 20, 99], np.int32)
+    bad_paths = paths.copy()
+    bad_paths[1, 0] = T
+    out_len, st = O.compact(k_cache, v_cache, bad_len, k_tree, v_tree, bad_paths,
+                            np.array([1, 2, T + 1, 0, 1], np.int32), st, lib=lib)
+    assert list(st) == [O.ORC_BAD_LEN, O.ORC_BAD_PATH, O.ORC_BAD_PATH, 0, O.ORC_BAD_LEN]
+    assert (k_cache[[0, 1, 2, 4]] == k1[[0, 1, 2, 4]]).all()
+    assert out_len[3] == 20
+
+
+ALL_PINS = [
+    pin_worked_tree_mask,
+    pin_mask_closure_bruteforce,
+    pin_mask_closure_random,
+    pin_mask_invalid_trees,
+    pin_visibility_probe,
+    pin_scale_zero_is_mean,
+    pin_chain_matches_causal_sdpa,
+    pin_single_node_is_decode,
+    pin_dense_mask_bruteforce,
+    pin_per_path_invariant,
+    pin_selected_rows_match_full,
+    pin_accept_hand_cases,
+    pin_accept_chain_extremes,
+    pin_accept_bruteforce,
+    pin_compact_hand_case,
+    pin_compact_alias,
+    pin_compact_random,
+]

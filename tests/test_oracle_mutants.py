@@ -1,0 +1,82 @@
+"""Plausible mistakes planted in copies of the oracle source must each fail at least one pin.
+
+The oracle itself is never modified: each case copies ``oracle/tree_oracle.c``, replaces one
+snippet, compiles the copy into a temporary library and runs every pin against it.  CPU only.
+"""
+import os
+
+import pytest
+
+import pins
+from oracle import oracle as O
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
+                   "tree_oracle.c")
+
+MUTANTS = {
+    # a node does not see itself
+    "path_without_self": ("for (int cur = i; cur != -1; cur = parent[cur]) out[n++] = cur;",
+                          "for (int cur = (i ? parent[i] : i); cur != -1; cur = parent[cur]) "
+                          "out[n++] = cur;"),
+    # path kept in walk order (node first) instead of root first
+    "path_not_reversed": ("for (int a = 0, z = n - 1; a < z; ++a, --z) {",
+                          "for (int a = 0, z = -1; a < z; ++a, --z) {"),
+    # mask bits numbered from the top of the word
+    "mask_bit_order": ("row[path[k] / 64] |= (uint64_t)1 << (path[k] % 64);",
+                       "row[path[k] / 64] |= (uint64_t)1 << (63 - path[k] % 64);"),
+    # one prefix row dropped
+    "prefix_off_by_one": ("int nkeys = L + npath;", "int nkeys = (L > 0 ? L - 1 : 0) + npath;"),
+    # query heads mapped round-robin instead of in contiguous groups
+    "gqa_round_robin": ("kvh = h / G;", "kvh = h % J->Hkv;"),
+    # scale ignored
+    "no_scale": ("s[j] = J->scale * dot;", "s[j] = dot;"),
+    # tree keys taken by position instead of by path node
+    "tree_row_by_position": ("koff = (((size_t)b * J->T + path[j - L]) * J->Hkv + kvh) * D;",
+                             "koff = (((size_t)b * J->T + (j - L)) * J->Hkv + kvh) * D;"),
+    # values read from the key tensor for the tree part
+    "tree_values_from_keys": ("vb = J->v_tree;", "vb = J->k_tree;"),
+    # log-sum-exp without the running maximum
+    "lse_without_max": ("*lse_out = m + log(den);", "*lse_out = log(den);"),
+    # a draft compared with the target at its own position instead of its parent's
+    "accept_own_target": ("acc[c] = acc[p] && db[c] == tb[p];", "acc[c] = acc[p] && db[c] == tb[c];"),
+    # acceptance ignores whether the ancestors were accepted
+    "accept_ignores_ancestors": ("acc[c] = acc[p] && db[c] == tb[p];", "acc[c] = db[c] == tb[p];"),
+    # equal depth resolved towards the largest index
+    "accept_tie_largest": ("if (acc[c] && depth[c] > depth[best]) best = c;",
+                           "if (acc[c] && depth[c] >= depth[best]) best = c;"),
+    # first accepted child rather than the longest path
+    "accept_first_match": ("if (acc[c] && depth[c] > depth[best]) best = c;",
+                           "if (acc[c] && depth[c] == depth[best] + 1 && pb[c] == best) best = c;"),
+    # bonus token taken at the parent of the last kept node
+    "bonus_at_parent": ("bonus_tok[b] = tb[best];", "bonus_tok[b] = tb[best ? pb[best] : 0];"),
+    # compaction writes one row too far
+    "compact_shifted": ("size_t dst = (((size_t)b * Hkv + h) * Lmax + L + k) * row;",
+                        "size_t dst = (((size_t)b * Hkv + h) * Lmax + L + k + (k > 0)) * row;"),
+    # compaction length excludes the root
+    "compact_len": ("cache_len_out[b] = L + n;", "cache_len_out[b] = L + n - 1;"),
+    # overflow check off by one
+    "compact_overflow": ("if (!bits && (long)L + n > Lmax) bits |= ORC_OVERFLOW;",
+                         "if (!bits && (long)L + n > Lmax + 1) bits |= ORC_OVERFLOW;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC, encoding="utf-8").read()
+    assert src.count(old) == 1, f"mutation site of {name} not found once in the oracle source"
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new), encoding="utf-8")
+    so = O.build(str(mutant_src), str(tmp_path / "libmutant.so"))
+    lib = O.load(so)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            caught.append(pin.__name__)
+            break
+        except Exception as e:  # a crash or bad value in the mutant also counts as caught
+            caught.append(f"{pin.__name__}:{type(e).__name__}")
+            break
+    assert caught, f"mutant {name} passed every pin"
