@@ -1,0 +1,160 @@
+/*
+ * tree_verify.h — C ABI of libtreeverify.so: the verification step of tree speculative decoding
+ * on an AMD Instinct MI355X (gfx950).
+ *
+ * One verification step, as described on lesty.tech "EAGLE-2 vs. Medusa" (sections 4, 5, 8) and
+ * rainlin.net "大模型投机解码（二）：EAGLE 系列" (sections 3.2, 4, 7):
+ *   1. tree_build_mask      per-node ancestor bitmask of the flattened draft tree;
+ *   2. tree_verify_attn     every tree node attends to its sequence's KV prefix plus only its
+ *                           own root-to-node path;
+ *   3. tree_accept          greedy acceptance, keep the single longest accepted path;
+ *   4. kv_compact_accepted  append the accepted nodes' K/V to the cache, drop the rest.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers, except where a parameter says otherwise.  The caller
+ *     owns every buffer; the library never allocates, frees, copies to the host or
+ *     synchronizes.  Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     outputs are valid once that stream reaches the end of the call's work.
+ *   - Tensors are dense, row-major, in the shapes given in brackets.  One floating dtype per
+ *     call (tv_dtype): fp32, or bfloat16 stored as 16-bit words.
+ *   - The tree is flattened in level order with a single root at index 0 and parent[i] < i for
+ *     i > 0 (the worked tree It/is/has/a/the/to/good/be flattens to
+ *     [It, is, has, a, the, to, good, be] with parent = [-1,0,0,1,1,2,3,5]).
+ *   - Ancestor masks are W = ceil(T/64) 64-bit words per node; bit (j % 64) of word (j / 64)
+ *     refers to node j.
+ *   - Limits: 1 <= T <= 128, D in {64, 128}, Hq % Hkv == 0, B >= 1, Lmax >= 0.
+ *   - Return value: TV_OK, or a negative tv_status.  Host-checkable problems (null pointers,
+ *     shapes, limits, dtype, workspace size) are reported before anything is launched.  A
+ *     launch failure is reported as TV_ERR_HIP.  Problems in the data itself are found on the
+ *     device and reported as bits in a caller-owned int32 status[B] array; they never cause an
+ *     out-of-bounds access.
+ */
+#ifndef TREE_VERIFY_H
+#define TREE_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TV_OK = 0,
+  TV_ERR_INVALID_ARG = -1, /* null pointer, bad shape or limit */
+  TV_ERR_UNSUPPORTED = -2, /* dtype or head_dim outside what the kernels are built for */
+  TV_ERR_WORKSPACE = -3,   /* workspace missing or smaller than tree_verify_attn_workspace_size */
+  TV_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} tv_status;
+
+typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
+
+/* Device status bits (per sequence b). */
+#define TV_BAD_TREE 0x1 /* parent[0] != -1, or parent[i] < 0 or >= i for some i > 0 */
+#define TV_OVERFLOW 0x2 /* cache_len[b] + accept_len[b] > Lmax: nothing committed */
+#define TV_BAD_LEN 0x4  /* cache_len[b] < 0 or > Lmax */
+#define TV_BAD_PATH 0x8 /* accept_len[b] outside [0, T] or an accepted index outside [0, T) */
+
+/* Human-readable name of a tv_status return value or of a single status bit. */
+const char* tv_status_string(int code);
+
+/*
+ * tree_build_mask — ancestor bitmask of every node.
+ * Defined by the tree-attention mask of lesty.tech section 5 (mask[i, j] is set iff j is i or
+ * an ancestor of i, found by following parent pointers) and the worked example of rainlin.net
+ * section 4 ("good" sees exactly [It, is, a, good]).
+ *
+ *   parent    [B,T]    int32, -1 at the root
+ *   anc_mask  [B,T,W]  uint64 out: bit j of row i set iff j is on the root-to-i path
+ *   status    [B]      int32 out: WRITTEN (not OR-ed) with TV_BAD_TREE or 0.  For a bad tree
+ *                      every row of that sequence is written with only its own bit set.
+ */
+int tree_build_mask(const int32_t* parent, int B, int T, uint64_t* anc_mask, int32_t* status,
+                    void* stream);
+
+/*
+ * Bytes of workspace tree_verify_attn needs for these shapes and this split setting (0 when
+ * the prefix is not split).  Deterministic for the same arguments on the same device.
+ */
+size_t tree_verify_attn_workspace_size(int B, int T, int Hq, int Hkv, int D, int Lmax, int dtype,
+                                       int split_keys);
+
+/*
+ * tree_verify_attn — tree attention over the KV prefix plus each node's ancestors.
+ * A tree node attends to every prefix row of its sequence and, among the tree's own rows, only
+ * to the nodes on its root-to-node path; siblings are invisible (lesty.tech section 5; the
+ * path-by-path equivalence of rainlin.net section 4).  Query head h reads KV head
+ * h / (Hq / Hkv).  Scores are scale * q.k; softmax over the visible keys; output = weighted sum
+ * of the visible V rows.
+ *
+ *   q          [B,T,Hq,D]      dtype   queries of the tree tokens
+ *   k_cache    [B,Hkv,Lmax,D]  dtype   prefix keys; rows 0..cache_len[b]-1 are read, no others
+ *   v_cache    [B,Hkv,Lmax,D]  dtype   prefix values, same rows
+ *   cache_len  [B]             int32   prefix length L_b (clamped into [0, Lmax]; an
+ *                                      out-of-range value sets TV_BAD_LEN in status)
+ *   k_tree     [B,T,Hkv,D]     dtype   keys of the tree tokens
+ *   v_tree     [B,T,Hkv,D]     dtype   values of the tree tokens
+ *   anc_mask   [B,T,W]         uint64  from tree_build_mask (bit 0 must be set in every row)
+ *   out        [B,T,Hq,D]      dtype   out: attention output (bf16 rounded to nearest even)
+ *   lse        [B,T,Hq]        fp32    out, optional (NULL): natural-log sum of exp of scores
+ *   status     [B]             int32   optional (NULL): TV_BAD_LEN is OR-ed in
+ *   scale      <= 0 selects 1/sqrt(D)
+ *   split_keys prefix keys per split-K chunk (rounded up to a multiple of 64); 0 = automatic.
+ *              Results agree across split settings to rounding.
+ *   workspace  device buffer of at least tree_verify_attn_workspace_size(...) bytes (may be
+ *              NULL when that size is 0); holds per-split partial results, no state across
+ *              calls.
+ */
+int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* cache_len, const void* k_tree, const void* v_tree,
+                     const uint64_t* anc_mask, void* out, float* lse, int32_t* status, int B,
+                     int T, int Hq, int Hkv, int D, int Lmax, int dtype, float scale,
+                     int split_keys, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tree_accept — greedy acceptance and the single longest accepted path.
+ * A drafted token is accepted iff it equals the target model's greedy choice at its parent
+ * (lesty.tech section 4); a node is accepted iff every node on its root path is; the root (the
+ * token the target emitted last step) is always accepted.  The deepest accepted node is kept,
+ * ties going to the smallest flattened index (lesty.tech section 8: only the single longest
+ * accepted path is retained; rainlin.net section 3.2: the longest valid branch is accepted).
+ *
+ *   anc_mask     [B,T,W]  uint64  from tree_build_mask
+ *   draft_tok    [B,T]    int32   drafted token of each node (entry 0 is not checked)
+ *   target_tok   [B,T]    int32   target model's greedy token at each node
+ *   accept_path  [B,T]    int32   out: accepted node indices root first, -1 after accept_len
+ *   accept_len   [B]      int32   out: nodes kept, counting the root (>= 1)
+ *   bonus_tok    [B]      int32   out: target_tok at the last kept node
+ */
+int tree_accept(const uint64_t* anc_mask, const int32_t* draft_tok, const int32_t* target_tok,
+                int B, int T, int32_t* accept_path, int32_t* accept_len, int32_t* bonus_tok,
+                void* stream);
+
+/*
+ * kv_compact_accepted — commit the accepted path's K/V to the cache.
+ * The tree's K/V rows were written to scratch during the verification pass; the surviving
+ * path's rows enter the cache and the rejected ones are dropped (lesty.tech section 8).  For
+ * every KV head, cache rows L_b .. L_b + accept_len[b] - 1 receive tree rows accept_path[b, 0..]
+ * in path order; no other cache row is written; cache_len_out[b] = L_b + accept_len[b].
+ *
+ *   k_cache, v_cache  [B,Hkv,Lmax,D]  dtype  in/out
+ *   cache_len         [B]             int32  L_b
+ *   cache_len_out     [B]             int32  out; may be the same pointer as cache_len (it must
+ *                                            then be exactly equal, not partly overlapping)
+ *   k_tree, v_tree    [B,T,Hkv,D]     dtype  may live inside the cache: every accepted row of a
+ *                                            (sequence, KV head) is read before any is written
+ *   accept_path [B,T], accept_len [B]  int32  from tree_accept
+ *   status            [B]             int32  optional (NULL): TV_BAD_LEN, TV_BAD_PATH or
+ *                                            TV_OVERFLOW OR-ed in; such a sequence commits
+ *                                            nothing and gets cache_len_out[b] = cache_len[b]
+ */
+int kv_compact_accepted(void* k_cache, void* v_cache, const int32_t* cache_len,
+                        int32_t* cache_len_out, const void* k_tree, const void* v_tree,
+                        const int32_t* accept_path, const int32_t* accept_len, int B, int T,
+                        int Hkv, int D, int Lmax, int dtype, int32_t* status, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TREE_VERIFY_H */

@@ -1,0 +1,116 @@
+"""Helpers shared by the GPU tests: upload synthetic workloads, run the HIP path through the C
+ABI binding, run the CPU oracle on the same host bytes, compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import oracle as O
+
+# Tolerances.  Attention outputs: max-abs error 1e-5 for fp32 inputs and 2e-2 for bf16 inputs
+# with fp32 accumulation.  lse carries no bf16 rounding of P (the row sums are accumulated from
+# the fp32 probabilities), so it is held to 1e-3 for bf16 inputs and 1e-5 for fp32.
+TOL_OUT = {"f32": 1e-5, "bf16": 2e-2}
+TOL_LSE = {"f32": 1e-5, "bf16": 1e-3}
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray, dtype: str | None = None) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:  # bfloat16 bit patterns
+        return torch.from_numpy(a.view(np.int16)).to(dev()).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev())
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def as_f64(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def upload(w) -> dict:
+    return dict(parent=to_dev(w.parent), draft=to_dev(w.draft), target=to_dev(w.target),
+                cache_len=to_dev(w.cache_len), q=to_dev(w.q), k_cache=to_dev(w.k_cache),
+                v_cache=to_dev(w.v_cache), k_tree=to_dev(w.k_tree), v_tree=to_dev(w.v_tree))
+
+
+def run_step(g: dict, split_keys: int = 0, tv=None):
+    """mask -> attention -> acceptance -> compaction on the device; host copies of results."""
+    import tree_attention_verification_attn_amd as tvmod
+
+    tv = tv or tvmod
+    anc, status = tv.tree_build_mask(g["parent"])
+    out, lse = tv.tree_verify_attn(g["q"], g["k_cache"], g["v_cache"], g["cache_len"],
+                                   g["k_tree"], g["v_tree"], anc, status=status,
+                                   split_keys=split_keys)
+    path, alen, bonus = tv.tree_accept(anc, g["draft"], g["target"])
+    new_len = tv.kv_compact_accepted(g["k_cache"], g["v_cache"], g["cache_len"], g["k_tree"],
+                                     g["v_tree"], path, alen, status=status)
+    torch.cuda.synchronize()
+    return dict(anc=to_host(anc).view(np.uint64), status=to_host(status), out=to_host(out),
+                lse=to_host(lse), path=to_host(path), alen=to_host(alen), bonus=to_host(bonus),
+                new_len=to_host(new_len), k_cache=to_host(g["k_cache"]),
+                v_cache=to_host(g["v_cache"]))
+
+
+def sample_rows(w, n_random: int, seed: int = 0) -> np.ndarray:
+    """(b, h, i) rows: corners of every axis plus uniform random ones."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b in {0, w.B - 1}:
+        for h in {0, w.Hq - 1, w.G - 1, w.G % w.Hq}:
+            for i in {0, w.T - 1, w.T // 2}:
+                rows.add((b, h, i))
+    while len(rows) < n_random + 24:
+        rows.add((int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.T))))
+    return np.array(sorted(rows), np.int32)
+
+
+def check_step(w, res: dict, rows: np.ndarray | None = None, label: str = "") -> dict:
+    """Compare a device step with the oracle.  Integer results and the cache bytes must match
+    exactly; attention within the dtype's tolerance (all rows, or the sampled ones)."""
+    o_anc, o_st = O.build_mask(w.parent)
+    assert np.array_equal(res["anc"], o_anc), f"{label}: ancestor mask differs"
+    o_path, o_len, o_bonus = O.accept(w.parent, w.draft, w.target)
+    assert np.array_equal(res["path"], o_path), f"{label}: accept_path differs"
+    assert np.array_equal(res["alen"], o_len), f"{label}: accept_len differs"
+    assert np.array_equal(res["bonus"], o_bonus), f"{label}: bonus_tok differs"
+
+    kc, vc = w.k_cache.copy(), w.v_cache.copy()
+    o_st2 = o_st.copy()
+    L_clamped = np.clip(w.cache_len, 0, w.Lmax).astype(np.int32)
+    o_new_len, o_st2 = O.compact(kc, vc, w.cache_len, w.k_tree, w.v_tree, o_path, o_len, o_st2)
+    bad_len = (w.cache_len < 0) | (w.cache_len > w.Lmax)
+    o_st2 = o_st2 | np.where(bad_len, O.ORC_BAD_LEN, 0).astype(np.int32)
+    assert np.array_equal(res["new_len"], o_new_len), f"{label}: cache_len_out differs"
+    assert np.array_equal(res["status"], o_st2), f"{label}: status {res['status']} vs {o_st2}"
+    bits = np.uint32 if kc.dtype == np.float32 else np.uint16
+    assert np.array_equal(res["k_cache"].view(bits), kc.view(bits)), f"{label}: K cache differs"
+    assert np.array_equal(res["v_cache"].view(bits), vc.view(bits)), f"{label}: V cache differs"
+
+    out = as_f64(res["out"])
+    if rows is None:
+        o_out, o_lse = O.attention(w.q, w.k_cache, w.v_cache, L_clamped, w.k_tree, w.v_tree,
+                                   w.parent)
+        got, got_lse = out, res["lse"].astype(np.float64)
+    else:
+        o_out, o_lse = O.attention(w.q, w.k_cache, w.v_cache, L_clamped, w.k_tree, w.v_tree,
+                                   w.parent, rows=rows)
+        got = out[rows[:, 0], rows[:, 2], rows[:, 1]]
+        got_lse = res["lse"][rows[:, 0], rows[:, 2], rows[:, 1]].astype(np.float64)
+    err = float(np.abs(got - o_out).max())
+    lerr = float(np.abs(got_lse - o_lse).max())
+    assert np.isfinite(got).all(), f"{label}: non-finite attention output"
+    assert err <= TOL_OUT[w.dtype], f"{label}: attention max-abs error {err}"
+    assert lerr <= TOL_LSE[w.dtype], f"{label}: lse max-abs error {lerr}"
+    return dict(err=err, lse_err=lerr)

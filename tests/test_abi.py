@@ -1,0 +1,158 @@
+"""The C ABI of libtreeverify.so without a GPU: it loads, exports every function declared in
+include/tree_verify.h, and reports host-checkable argument errors before launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tree_verify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import tree_attention_verification_attn_amd as tv
+    from tree_attention_verification_attn_amd import build
+
+    if not os.path.exists(build.LIB):
+        build.build_library()
+    return tv.load_library()
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?([a-z_][a-z_0-9]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for fn in ("tree_build_mask", "tree_verify_attn", "tree_verify_attn_workspace_size",
+               "tree_accept", "kv_compact_accepted", "tv_status_string"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_function(lib):
+    from tree_attention_verification_attn_amd import build
+
+    out = subprocess.run(["nm", "-D", "--defined-only", build.LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for fn in declared_functions():
+        assert fn in exported, fn
+        assert hasattr(lib, fn)
+
+
+def test_header_compiles_as_c():
+    src = '#include "tree_verify.h"\nint main(void){return TV_OK + TV_F32 + TV_BAD_TREE * 0;}\n'
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-x", "c", "-I",
+                    os.path.join(ROOT, "include"), "-", "-o", "/dev/null"], input=src, text=True,
+                   check=True)
+
+
+def test_status_strings(lib):
+    import tree_attention_verification_attn_amd as tv
+
+    for code in (tv.TV_OK, tv.TV_ERR_INVALID_ARG, tv.TV_ERR_UNSUPPORTED, tv.TV_ERR_WORKSPACE,
+                 tv.TV_ERR_HIP, tv.TV_BAD_TREE, tv.TV_OVERFLOW, tv.TV_BAD_LEN, tv.TV_BAD_PATH):
+        assert lib.tv_status_string(code)
+    assert b"unknown" in lib.tv_status_string(12345)
+
+
+# A fake non-null pointer: every call below must be rejected before it is dereferenced.
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def test_build_mask_argument_errors(lib):
+    assert lib.tree_build_mask(None, 1, 8, FAKE, FAKE, None) == -1
+    assert lib.tree_build_mask(FAKE, 1, 8, None, FAKE, None) == -1
+    assert lib.tree_build_mask(FAKE, 1, 8, FAKE, None, None) == -1
+    assert lib.tree_build_mask(FAKE, 0, 8, FAKE, FAKE, None) == -1
+    assert lib.tree_build_mask(FAKE, 1, 0, FAKE, FAKE, None) == -1
+    assert lib.tree_build_mask(FAKE, 1, 129, FAKE, FAKE, None) == -1
+
+
+def _attn(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, cl=FAKE, kt=FAKE, vt=FAKE, anc=FAKE, out=FAKE, lse=None,
+             st=None, B=1, T=8, Hq=2, Hkv=1, D=64, Lmax=16, dt=0, scale=0.0, split=0, ws=None,
+             wsb=0)
+    a.update(kw)
+    return lib.tree_verify_attn(a["q"], a["kc"], a["vc"], a["cl"], a["kt"], a["vt"], a["anc"],
+                                a["out"], a["lse"], a["st"], a["B"], a["T"], a["Hq"], a["Hkv"],
+                                a["D"], a["Lmax"], a["dt"], a["scale"], a["split"], a["ws"],
+                                a["wsb"], None)
+
+
+def test_attention_argument_errors(lib):
+    for name in ("q", "kc", "vc", "cl", "kt", "vt", "anc", "out"):
+        assert _attn(lib, **{name: None}) == -1, name
+    assert _attn(lib, B=0) == -1
+    assert _attn(lib, T=0) == -1
+    assert _attn(lib, T=129) == -1
+    assert _attn(lib, Hq=3, Hkv=2) == -1
+    assert _attn(lib, Hkv=0) == -1
+    assert _attn(lib, Lmax=-1) == -1
+    assert _attn(lib, split=-64) == -1
+    assert _attn(lib, D=96) == -2
+    assert _attn(lib, dt=7) == -2
+    # split-K over a long prefix needs a workspace
+    need = lib.tree_verify_attn_workspace_size(1, 8, 2, 1, 64, 4096, 0, 256)
+    assert need > 0
+    assert _attn(lib, Lmax=4096, split=256) == -3
+    assert _attn(lib, Lmax=4096, split=256, ws=FAKE, wsb=need - 1) == -3
+
+
+def test_workspace_size_rules(lib):
+    ws = lib.tree_verify_attn_workspace_size
+    # one chunk covers the prefix: no workspace
+    assert ws(1, 8, 2, 1, 64, 16, 0, 1024) == 0
+    # S chunks of 256 keys over 4096 keys, one 256-row block: S * 256 rows * (D + 2) floats
+    assert ws(1, 8, 2, 1, 64, 4096, 0, 256) == 16 * 256 * 66 * 4
+    # bad arguments report 0
+    assert ws(1, 8, 3, 2, 64, 4096, 0, 0) == 0
+    assert ws(1, 8, 2, 1, 80, 4096, 0, 0) == 0
+
+
+def test_accept_argument_errors(lib):
+    assert lib.tree_accept(None, FAKE, FAKE, 1, 8, FAKE, FAKE, FAKE, None) == -1
+    assert lib.tree_accept(FAKE, FAKE, FAKE, 1, 8, FAKE, None, FAKE, None) == -1
+    assert lib.tree_accept(FAKE, FAKE, FAKE, 1, 129, FAKE, FAKE, FAKE, None) == -1
+    assert lib.tree_accept(FAKE, FAKE, FAKE, 0, 8, FAKE, FAKE, FAKE, None) == -1
+
+
+def test_compact_argument_errors(lib):
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 1, 64, 32, 0, None, None]
+    for i in range(8):
+        bad = list(args)
+        bad[i] = None
+        assert lib.kv_compact_accepted(*bad) == -1, i
+    bad = list(args)
+    bad[11] = 80  # head_dim
+    assert lib.kv_compact_accepted(*bad) == -2
+    bad = list(args)
+    bad[13] = 3  # dtype
+    assert lib.kv_compact_accepted(*bad) == -2
+    bad = list(args)
+    bad[12] = -1  # Lmax
+    assert lib.kv_compact_accepted(*bad) == -1
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    import tree_attention_verification_attn_amd as tv
+
+    with pytest.raises(ValueError):
+        tv.tree_build_mask(torch.zeros((1, 8), dtype=torch.int32))
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "tree_attention_verification_attn_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "oracle" not in text.lower(), f

@@ -1,0 +1,28 @@
+"""Tree-attention verification of speculative draft trees on AMD Instinct MI355X (gfx950).
+
+The computation lives in libtreeverify.so (hand-written HIP kernels behind the C ABI in
+include/tree_verify.h); this package only builds and binds it.
+"""
+from .binding import (  # noqa: F401
+    EXPORTS,
+    TV_BAD_LEN,
+    TV_BAD_PATH,
+    TV_BAD_TREE,
+    TV_BF16,
+    TV_ERR_HIP,
+    TV_ERR_INVALID_ARG,
+    TV_ERR_UNSUPPORTED,
+    TV_ERR_WORKSPACE,
+    TV_F32,
+    TV_OK,
+    TV_OVERFLOW,
+    TreeVerifyError,
+    kv_compact_accepted,
+    lib_path,
+    load_library,
+    status_string,
+    tree_accept,
+    tree_build_mask,
+    tree_verify_attn,
+    tree_verify_attn_workspace_size,
+)

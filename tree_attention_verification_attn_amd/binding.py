@@ -1,0 +1,228 @@
+"""Thin Python binding of libtreeverify.so (the C ABI in include/tree_verify.h).
+
+Argument marshalling only: torch tensors supply device memory and the current HIP stream; every
+step of the computation runs in the library's HIP kernels.  Output tensors that the caller does
+not pass are allocated here with torch.  Loading fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from . import build as _build
+
+TV_OK, TV_ERR_INVALID_ARG, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_HIP = 0, -1, -2, -3, -4
+TV_F32, TV_BF16 = 0, 1
+TV_BAD_TREE, TV_OVERFLOW, TV_BAD_LEN, TV_BAD_PATH = 0x1, 0x2, 0x4, 0x8
+
+EXPORTS = ("tv_status_string", "tree_build_mask", "tree_verify_attn_workspace_size",
+           "tree_verify_attn", "tree_accept", "kv_compact_accepted")
+
+
+class TreeVerifyError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} ({code})")
+        self.code = code
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libtreeverify.so (no build here: run __graft_entry__.build() or build.py first)."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or _build.LIB
+        if not os.path.exists(p):
+            raise ImportError(f"libtreeverify.so not found at {p}; build it with "
+                              "`python -m tree_attention_verification_attn_amd.build`")
+        lib = ctypes.CDLL(p)
+        _declare(lib)
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def _declare(lib: ctypes.CDLL) -> None:
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.tv_status_string.argtypes = [I]
+    lib.tv_status_string.restype = ctypes.c_char_p
+    lib.tree_build_mask.argtypes = [P, I, I, P, P, P]
+    lib.tree_build_mask.restype = I
+    lib.tree_verify_attn_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+    lib.tree_verify_attn_workspace_size.restype = ctypes.c_size_t
+    lib.tree_verify_attn.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, P,
+                                     ctypes.c_size_t, P]
+    lib.tree_verify_attn.restype = I
+    lib.tree_accept.argtypes = [P, P, P, I, I, P, P, P, P]
+    lib.tree_accept.restype = I
+    lib.kv_compact_accepted.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, P]
+    lib.kv_compact_accepted.restype = I
+
+
+def status_string(code: int) -> str:
+    return load_library().tv_status_string(int(code)).decode()
+
+
+def _check(fn: str, code: int) -> None:
+    if code != TV_OK:
+        raise TreeVerifyError(fn, code, status_string(code))
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TV_F32
+    if t.dtype == torch.bfloat16:
+        return TV_BF16
+    raise TypeError(f"tree verification takes float32 or bfloat16 tensors, got {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+def tree_build_mask(parent: torch.Tensor, anc_mask: torch.Tensor | None = None,
+                    status: torch.Tensor | None = None, stream=None):
+    """parent [B,T] int32 -> (anc_mask [B,T,W] uint64 as int64 storage, status [B] int32)."""
+    _need(parent, "parent", torch.int32, 2)
+    B, T = parent.shape
+    W = (T + 63) // 64
+    if anc_mask is None:
+        anc_mask = torch.empty((B, T, W), dtype=torch.int64, device=parent.device)
+    if status is None:
+        status = torch.empty((B,), dtype=torch.int32, device=parent.device)
+    _need(anc_mask, "anc_mask", torch.int64, 3)
+    _need(status, "status", torch.int32, 1)
+    _check("tree_build_mask", load_library().tree_build_mask(
+        _ptr(parent), B, T, _ptr(anc_mask), _ptr(status), _stream(stream)))
+    return anc_mask, status
+
+
+def tree_verify_attn_workspace_size(B: int, T: int, Hq: int, Hkv: int, D: int, Lmax: int,
+                                    dtype: torch.dtype, split_keys: int = 0) -> int:
+    code = TV_BF16 if dtype == torch.bfloat16 else TV_F32
+    return int(load_library().tree_verify_attn_workspace_size(B, T, Hq, Hkv, D, Lmax, code,
+                                                              split_keys))
+
+
+def tree_verify_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, anc_mask, out=None,
+                     lse=None, status=None, scale: float = 0.0, split_keys: int = 0,
+                     workspace: torch.Tensor | None = None, with_lse: bool = True, stream=None):
+    """Tree attention.  Returns (out [B,T,Hq,D], lse [B,T,Hq] float32 or None)."""
+    _need(q, "q", None, 4)
+    B, T, Hq, D = q.shape
+    dt = _dtype_code(q)
+    _need(k_cache, "k_cache", q.dtype, 4)
+    _need(v_cache, "v_cache", q.dtype, 4)
+    _need(k_tree, "k_tree", q.dtype, 4)
+    _need(v_tree, "v_tree", q.dtype, 4)
+    _need(cache_len, "cache_len", torch.int32, 1)
+    _need(anc_mask, "anc_mask", torch.int64, 3)
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if (tuple(k_cache.shape) != (B, Hkv, Lmax, D) or tuple(v_cache.shape) != tuple(k_cache.shape)
+            or tuple(k_tree.shape) != (B, T, Hkv, D) or tuple(v_tree.shape) != (B, T, Hkv, D)
+            or tuple(cache_len.shape) != (B,) or tuple(anc_mask.shape) != (B, T, (T + 63) // 64)):
+        raise ValueError("inconsistent tree_verify_attn shapes")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, 4)
+    if lse is None and with_lse:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    ws_bytes = tree_verify_attn_workspace_size(B, T, Hq, Hkv, D, Lmax, q.dtype, split_keys)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("tree_verify_attn", load_library().tree_verify_attn(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(k_tree), _ptr(v_tree),
+        _ptr(anc_mask), _ptr(out), _ptr(lse), _ptr(status), B, T, Hq, Hkv, D, Lmax, dt,
+        float(scale), int(split_keys), _ptr(workspace), ws_have, _stream(stream)))
+    return out, lse
+
+
+def tree_accept(anc_mask, draft_tok, target_tok, accept_path=None, accept_len=None,
+                bonus_tok=None, stream=None):
+    """Greedy longest accepted path -> (accept_path [B,T], accept_len [B], bonus_tok [B])."""
+    _need(anc_mask, "anc_mask", torch.int64, 3)
+    _need(draft_tok, "draft_tok", torch.int32, 2)
+    _need(target_tok, "target_tok", torch.int32, 2)
+    B, T = draft_tok.shape
+    if tuple(target_tok.shape) != (B, T) or tuple(anc_mask.shape) != (B, T, (T + 63) // 64):
+        raise ValueError("inconsistent tree_accept shapes")
+    dev = draft_tok.device
+    accept_path = torch.empty((B, T), dtype=torch.int32, device=dev) if accept_path is None else accept_path
+    accept_len = torch.empty((B,), dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    bonus_tok = torch.empty((B,), dtype=torch.int32, device=dev) if bonus_tok is None else bonus_tok
+    _need(accept_path, "accept_path", torch.int32, 2)
+    _need(accept_len, "accept_len", torch.int32, 1)
+    _need(bonus_tok, "bonus_tok", torch.int32, 1)
+    _check("tree_accept", load_library().tree_accept(
+        _ptr(anc_mask), _ptr(draft_tok), _ptr(target_tok), B, T, _ptr(accept_path),
+        _ptr(accept_len), _ptr(bonus_tok), _stream(stream)))
+    return accept_path, accept_len, bonus_tok
+
+
+def kv_compact_accepted(k_cache, v_cache, cache_len, k_tree, v_tree, accept_path, accept_len,
+                        cache_len_out=None, status=None, stream=None):
+    """Append the accepted rows to the caches in place -> cache_len_out [B] int32."""
+    _need(k_cache, "k_cache", None, 4)
+    B, Hkv, Lmax, D = k_cache.shape
+    dt = _dtype_code(k_cache)
+    _need(v_cache, "v_cache", k_cache.dtype, 4)
+    _need(cache_len, "cache_len", torch.int32, 1)
+    _need(accept_path, "accept_path", torch.int32, 2)
+    _need(accept_len, "accept_len", torch.int32, 1)
+    T = accept_path.shape[1]
+    dense = (T * Hkv * D, Hkv * D, D, 1)
+    for name, t in (("k_tree", k_tree), ("v_tree", v_tree)):
+        # may be a view into the cache itself (tree rows written in place during verification)
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != k_cache.dtype:
+            raise ValueError(f"{name} must be a device tensor of the cache dtype")
+        if tuple(t.shape) != (B, T, Hkv, D):
+            raise ValueError(f"{name} must be [B,T,Hkv,D]")
+        if any(sz > 1 and st != want for sz, st, want in zip(t.shape, t.stride(), dense)):
+            raise ValueError(f"{name} must be laid out as a dense [B,T,Hkv,D] tensor")
+    if tuple(v_cache.shape) != (B, Hkv, Lmax, D) or tuple(accept_len.shape) != (B,):
+        raise ValueError("inconsistent kv_compact_accepted shapes")
+    if cache_len_out is None:
+        cache_len_out = torch.empty_like(cache_len)
+    _need(cache_len_out, "cache_len_out", torch.int32, 1)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    _check("kv_compact_accepted", load_library().kv_compact_accepted(
+        _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(cache_len_out), _ptr(k_tree),
+        _ptr(v_tree), _ptr(accept_path), _ptr(accept_len), B, T, Hkv, D, Lmax, dt,
+        _ptr(status), _stream(stream)))
+    return cache_len_out

@@ -1,0 +1,629 @@
+// tree_verify_attn: tree attention of a flattened draft tree over its sequence's KV prefix.
+//
+// Work decomposition (one KV head at a time, GQA-grouped):
+//   * The G*T query rows of one (sequence b, KV head) are ordered r = t*G + g (node t, query
+//     head kvh*G + g).  A workgroup owns 256 of them: 4 wavefronts x 64 rows.  Every prefix key
+//     is visible to every row, so the K/V rows streamed through LDS are shared by all 256 rows.
+//   * The prefix is cut into equal chunks of `chunk` keys (split-K).  Chunk s of sequence b is
+//     processed by its own workgroup; chunk 0 also processes the T tree keys, which are masked
+//     per row by the ancestor bitmask.  Partial results (unnormalised O, running max m, sum l)
+//     are merged by attn_combine; a sequence with a single non-empty chunk is written directly.
+//   * Per 64-key tile: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, Q
+//     held in registers as the B operand), masking, online softmax in the log2 domain, then
+//     O^T += V^T P^T (V^T fragments from LDS with the gfx950 transpose read, P taken straight
+//     from the S^T accumulators).  In the transposed form a lane holds one query row in both
+//     the score and the output accumulators, so the softmax statistics never leave the lane
+//     pair (l, l^32).
+//   * Online softmax with lazy rescaling: the running max is raised only when a row's max grows
+//     by more than 2^8, so P <= 256 and O is rescaled rarely.
+//   * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same structure.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <type_traits>
+
+#include "tv_internal.h"
+
+namespace tv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int kWaves = 4;
+constexpr int kRows = 256;         // query rows per workgroup
+constexpr int kKT = 64;            // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units a row's max may outgrow the running max
+
+struct AttnArgs {
+  const char* q;
+  const char* kc;
+  const char* vc;
+  const int32_t* cache_len;
+  const char* kt;
+  const char* vt;
+  const uint64_t* anc;
+  char* out;
+  float* lse;
+  int32_t* status;
+  float* part_o;   // [slot][kRows*D] in register order
+  float* part_ml;  // [slot][kRows][2]
+  int B, T, Hq, Hkv, G, Lmax, W, GT, RB, S, chunk;
+  float c;         // scale * log2(e)
+};
+
+template <typename E, int D>
+struct Layout {
+  static constexpr bool kBF16 = std::is_same<E, __bf16>::value;
+  static constexpr int kElem = sizeof(E);
+  static constexpr int kRowBytes = D * kElem;
+  static constexpr int kCPR = kRowBytes / 16;  // 16-byte chunks per row
+  // Padded LDS rows.  K rows are read 16 consecutive keys at a time (stride = 4 banks mod 64);
+  // V rows are read by the transpose loads as 4 keys x 64 bytes (stride = 16 banks mod 64).
+  // Both patterns, and the 16-byte row writes, are free of LDS bank conflicts, and every
+  // fragment address is one per-lane base plus a compile-time offset.
+  static constexpr int kPitchK = kRowBytes + 16;
+  static constexpr int kPitchV = kBF16 ? kRowBytes + 64 : kRowBytes + 16;
+  static constexpr int kTileK = kKT * kPitchK;
+  static constexpr int kTileV = kKT * kPitchV;
+  static constexpr int kStage = kTileK + kTileV;
+  static constexpr int kLoads = kKT * kCPR / 256;  // chunks per thread per tile
+  static constexpr int kDB = D / 32;               // 32-wide d blocks
+};
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of lane l ^ 32.
+__device__ inline float partner(float x) {
+  const int lane = __lane_id();
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Logical work item -> hardware workgroup id.  Workgroups are dealt to the 8 XCDs round-robin;
+// this gives every XCD a contiguous range of logical items, so items that read the same K/V
+// chunk (consecutive row blocks) or the same Q rows (consecutive splits) share an L2.
+__device__ inline int xcd_remap(int bid, int n) {
+  const int per = n / 8, rem = n % 8;
+  const int xcd = bid % 8, slot = bid / 8;
+  return xcd * per + min(xcd, rem) + slot;
+}
+
+template <typename E, int D, bool kSplit>
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void attn_main(AttnArgs a) {
+  using Lay = Layout<E, D>;
+  constexpr bool kBF16 = Lay::kBF16;
+  constexpr int kDB = Lay::kDB;
+  // Marks the kernel as using accumulation registers, so the MFMA accumulators are allocated
+  // there (AGPR form) instead of competing with the softmax values for arch VGPRs.
+  asm volatile("" ::: "a0");
+  __shared__ __attribute__((aligned(16))) char smem[2 * Lay::kStage];
+
+  const int n_items = a.B * a.Hkv * a.S * a.RB;
+  const int item = xcd_remap(blockIdx.x, n_items);
+  const int rb = item % a.RB;
+  const int s = (item / a.RB) % a.S;
+  const int kvh = (item / (a.RB * a.S)) % a.Hkv;
+  const int b = item / (a.RB * a.S * a.Hkv);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, h = lane >> 5;
+
+  const int L_raw = a.cache_len[b];
+  const int L = min(max(L_raw, 0), a.Lmax);
+  if (a.status && (L_raw < 0 || L_raw > a.Lmax) && kvh == 0 && s == 0 && rb == 0 && tid == 0)
+    atomicOr(a.status + b, TV_BAD_LEN);
+  const int n_split = max(1, ceil_div(L, a.chunk));
+  if (s >= n_split) return;  // empty chunk: nothing to merge
+  const bool direct = !kSplit || n_split == 1;
+
+  const int k0 = s * a.chunk, k1 = min(k0 + a.chunk, L);
+  const int n_prefix_tiles = k1 > k0 ? (k1 - k0 + kKT - 1) / kKT : 0;
+  const int n_tree_tiles = s == 0 ? (a.T + kKT - 1) / kKT : 0;
+  const int n_tiles = n_tree_tiles + n_prefix_tiles;
+
+  // ---- rows of this lane: r = rb*256 + wave*64 + nb*32 + n ---------------------------------
+  int row_t[2], row_head[2];
+  bool row_ok[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int r = rb * kRows + wave * 64 + nb * 32 + n;
+    row_ok[nb] = r < a.GT;
+    row_t[nb] = row_ok[nb] ? r / a.G : 0;
+    row_head[nb] = kvh * a.G + (row_ok[nb] ? r % a.G : 0);
+  }
+
+  // ---- Q fragments (B operand): row n, d = ks*K + [group of lane] --------------------------
+  constexpr int kKS = kBF16 ? D / 16 : D / 2;
+  using QFrag = typename std::conditional<kBF16, bf16x8, float>::type;
+  QFrag qf[2][kKS];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    // padding rows load a real row (row_t = 0): finite values, outputs never written
+    const E* qrow = reinterpret_cast<const E*>(a.q) +
+                    (((size_t)b * a.T + row_t[nb]) * a.Hq + row_head[nb]) * D;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      if constexpr (kBF16) {
+        qf[nb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + 8 * h);
+      } else {
+        qf[nb][ks] = qrow[ks * 2 + h];
+      }
+    }
+  }
+  // ancestor mask words of the lane's rows (padding rows see only the root)
+  uint64_t mk[2][2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    mk[nb][0] = 1;
+    mk[nb][1] = 0;
+    if (row_ok[nb] && n_tree_tiles) {
+      const uint64_t* mrow = a.anc + ((size_t)b * a.T + row_t[nb]) * a.W;
+      mk[nb][0] = mrow[0];
+      mk[nb][1] = a.W > 1 ? mrow[1] : 0;
+    }
+  }
+
+  // ---- tile staging ------------------------------------------------------------------------
+  const size_t kv_head_base = (((size_t)b * a.Hkv + kvh) * a.Lmax) * Lay::kRowBytes;
+  const size_t tree_base = (size_t)b * a.T * a.Hkv * Lay::kRowBytes + (size_t)kvh * Lay::kRowBytes;
+  const size_t tree_stride = (size_t)a.Hkv * Lay::kRowBytes;
+  u32x4 rk[Lay::kLoads], rv[Lay::kLoads];
+
+  auto tile_keys = [&](int tile, int& base, int& end, bool& is_tree) {
+    is_tree = tile < n_tree_tiles;
+    if (is_tree) {
+      base = tile * kKT;
+      end = a.T;
+    } else {
+      base = k0 + (tile - n_tree_tiles) * kKT;
+      end = k1;
+    }
+  };
+  // Keys past the end of the tile's range load the last valid row instead: their scores are
+  // masked to -inf, so P = 0 and a finite row contributes exactly nothing, and no cache row at
+  // or past cache_len is ever read.
+  auto load_tile = [&](int tile) {
+    int base, end;
+    bool is_tree;
+    tile_keys(tile, base, end, is_tree);
+    const char* kb = is_tree ? a.kt : a.kc;
+    const char* vb = is_tree ? a.vt : a.vc;
+    const size_t rbase = is_tree ? tree_base : kv_head_base;
+    const size_t rstride = is_tree ? tree_stride : (size_t)Lay::kRowBytes;
+#pragma unroll
+    for (int p = 0; p < Lay::kLoads; ++p) {
+      const int qd = tid + 256 * p;
+      const int row = qd / Lay::kCPR, ch = qd % Lay::kCPR;
+      const int key = min(base + row, end - 1);
+      const size_t off = rbase + (size_t)key * rstride;
+      rk[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + off) + ch);
+      rv[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + off) + ch);
+    }
+  };
+  auto store_tile = [&](int buf) {
+    char* kl = smem + buf * Lay::kStage;
+    char* vl = kl + Lay::kTileK;
+#pragma unroll
+    for (int p = 0; p < Lay::kLoads; ++p) {
+      const int qd = tid + 256 * p;
+      const int row = qd / Lay::kCPR, ch = qd % Lay::kCPR;
+      *reinterpret_cast<u32x4*>(kl + row * Lay::kPitchK + ch * 16) = rk[p];
+      *reinterpret_cast<u32x4*>(vl + row * Lay::kPitchV + ch * 16) = rv[p];
+    }
+  };
+
+  // ---- accumulators ------------------------------------------------------------------------
+  f32x16 oacc[kDB][2];
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) oacc[db][nb] = f32x16{};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+
+  if (n_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int buf = tile & 1;
+    if (tile + 1 < n_tiles) load_tile(tile + 1);
+    const char* kl = smem + buf * Lay::kStage;
+    const char* vl = kl + Lay::kTileK;
+    int base, end;
+    bool is_tree;
+    tile_keys(tile, base, end, is_tree);
+    const bool need_mask = is_tree || base + kKT > end;
+    // a tree tile covers nodes 64*tile .. 64*tile+63: one mask word per row
+    uint64_t mword[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) mword[nb] = !is_tree ? ~0ull : (tile == 0 ? mk[nb][0] : mk[nb][1]);
+
+    // The 64-key tile is consumed as two 32-key blocks kb; each runs QK, softmax and PV.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // ---- S^T = K Q^T for keys kb*32 .. kb*32+31 ------------------------------------------
+      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        if constexpr (kBF16) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+              kl + (kb * 32 + n) * Lay::kPitchK + (2 * ks + h) * 16);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nb][ks], sacc[nb], 0, 0, 0);
+        } else {
+          const float kf = *reinterpret_cast<const float*>(
+              kl + (kb * 32 + n) * Lay::kPitchK + (2 * ks + h) * 4);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf, qf[nb][ks], sacc[nb], 0, 0, 0);
+        }
+      }
+
+      // ---- mask: element r is key base + kb*32 + 8*(r/4) + 4*h + r%4 ------------------------
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const bool vis = base + kk < end && ((mword[nb] >> kk) & 1);
+            sacc[nb][r] = vis ? sacc[nb][r] : -INFINITY;
+          }
+        }
+      }
+
+      // ---- online softmax (log2 domain) ----------------------------------------------------
+      bool need_rescale = false;
+      float m_new[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
+        mx = fmaxf(mx, partner(mx));
+        m_new[nb] = fmaxf(m_run[nb], mx * a.c);
+        need_rescale |= m_new[nb] > m_run[nb] + kRescaleSlack;
+      }
+      if (__ballot(need_rescale)) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          float alpha = 1.f;
+          if (m_new[nb] > m_run[nb] + kRescaleSlack) {
+            alpha = fast_exp2(m_run[nb] - m_new[nb]);  // 0 on the first block
+            m_run[nb] = m_new[nb];
+          }
+          l_run[nb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) oacc[db][nb] *= alpha;
+        }
+      }
+      using PFrag = typename std::conditional<kBF16, bf16x8, float>::type;
+      PFrag pf[2][kBF16 ? 2 : 16];  // [nb][16-key step] (bf16) or [nb][element] (fp32)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float mb = m_run[nb] == -INFINITY ? 0.f : m_run[nb];
+        float p[16];
+        float lsum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p[r] = fast_exp2(__builtin_fmaf(sacc[nb][r], a.c, -mb));
+          lsum += p[r];
+        }
+        l_run[nb] += lsum;
+        if constexpr (kBF16) {
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * st + 2 * e], p[8 * st + 2 * e + 1]);
+            pf[nb][st] = __builtin_bit_cast(bf16x8, w);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pf[nb][r] = p[r];
+        }
+      }
+
+      // ---- O^T += V^T P^T ------------------------------------------------------------------
+      if constexpr (kBF16) {
+        // 16-key step st covers keys kb*32 + 16st + {4h..4h+3} (elements 0-3) and
+        // kb*32 + 16st + 8 + {4h..4h+3} (elements 4-7); a transpose read gives lane i of each
+        // 16-lane group 4 consecutive keys at d = D0 + i.
+        const int tr_key = 4 * h + ((lane & 15) >> 2);
+        const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) {
+            const int o0 = (kb * 32 + 16 * st + tr_key) * Lay::kPitchV + (db * 32 + tr_d) * 2;
+            const int o1 = o0 + 8 * Lay::kPitchV;
+            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vl + o0));
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vl + o1));
+            const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+              oacc[db][nb] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb][st], oacc[db][nb], 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const int key = kb * 32 + 8 * (u >> 2) + 4 * h + (u & 3);
+#pragma unroll
+          for (int db = 0; db < kDB; ++db) {
+            const float vf =
+                *reinterpret_cast<const float*>(vl + key * Lay::kPitchV + (db * 32 + n) * 4);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+              oacc[db][nb] =
+                  __builtin_amdgcn_mfma_f32_32x32x2f32(vf, pf[nb][u], oacc[db][nb], 0, 0, 0);
+          }
+        }
+      }
+    }
+
+    if (tile + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----------------------------------------------------------------------------
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) l_run[nb] += partner(l_run[nb]);
+
+  if (direct) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      if (!row_ok[nb]) continue;
+      const float inv = 1.f / l_run[nb];
+      const size_t orow = ((size_t)b * a.T + row_t[nb]) * a.Hq + row_head[nb];
+      E* o = reinterpret_cast<E*>(a.out) + orow * D;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d = db * 32 + 8 * j + 4 * h;
+          const f32x16& acc = oacc[db][nb];
+          if constexpr (kBF16) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[4 * j] * inv, acc[4 * j + 1] * inv);
+            w.y = pack_bf16x2(acc[4 * j + 2] * inv, acc[4 * j + 3] * inv);
+            *reinterpret_cast<uint2*>(o + d) = w;
+          } else {
+            *reinterpret_cast<float4*>(o + d) =
+                float4{acc[4 * j] * inv, acc[4 * j + 1] * inv, acc[4 * j + 2] * inv,
+                       acc[4 * j + 3] * inv};
+          }
+        }
+      if (a.lse && h == 0) a.lse[orow] = (m_run[nb] + __log2f(l_run[nb])) * kLn2;
+    }
+  } else {
+    const size_t slot = (((size_t)b * a.Hkv + kvh) * a.RB + rb) * a.S + s;
+    float4* po = reinterpret_cast<float4*>(a.part_o + slot * (size_t)kRows * D);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x16& acc = oacc[db][nb];
+          po[((((wave * 2 + nb) * kDB + db) * 4 + j) << 6) + lane] =
+              float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+        }
+    if (h == 0) {
+      float2* pml = reinterpret_cast<float2*>(a.part_ml + slot * (size_t)kRows * 2);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) pml[wave * 64 + nb * 32 + n] = float2{m_run[nb], l_run[nb]};
+    }
+  }
+}
+
+// Merge the per-chunk partials of sequences with more than one non-empty chunk:
+//   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  lse = (M + log2 den) ln 2.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+  constexpr int kDB = D / 32;
+  const int item = blockIdx.x;  // (b, kvh, rb)
+  const int rb = item % a.RB;
+  const int kvh = (item / a.RB) % a.Hkv;
+  const int b = item / (a.RB * a.Hkv);
+  const int L = min(max(a.cache_len[b], 0), a.Lmax);
+  const int n_split = max(1, ceil_div(L, a.chunk));
+  if (n_split == 1) return;  // written directly by attn_main
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 31, h = lane >> 5;
+  const size_t slot0 = (((size_t)b * a.Hkv + kvh) * a.RB + rb) * a.S;
+  const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
+  const float4* po = reinterpret_cast<const float4*>(a.part_o);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int rloc = wave * 64 + nb * 32 + n;
+    const int r = rb * kRows + rloc;
+    if (r >= a.GT) continue;
+    float M = -INFINITY;
+    for (int s = 0; s < n_split; ++s) M = fmaxf(M, pml[(slot0 + s) * kRows + rloc].x);
+    float den = 0.f;
+    for (int s = 0; s < n_split; ++s) {
+      const float2 ml = pml[(slot0 + s) * kRows + rloc];
+      den += fast_exp2(ml.x - M) * ml.y;
+    }
+    const float inv = 1.f / den;
+    float4 acc[kDB][4];
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[db][j] = float4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n_split; ++s) {
+      const float w = fast_exp2(pml[(slot0 + s) * kRows + rloc].x - M) * inv;
+      const float4* ps = po + (slot0 + s) * (size_t)kRows * D / 4;
+#pragma unroll
+      for (int db = 0; db < kDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 v = ps[((((wave * 2 + nb) * kDB + db) * 4 + j) << 6) + lane];
+          acc[db][j].x += w * v.x;
+          acc[db][j].y += w * v.y;
+          acc[db][j].z += w * v.z;
+          acc[db][j].w += w * v.w;
+        }
+    }
+    const int t = r / a.G, head = kvh * a.G + r % a.G;
+    const size_t orow = ((size_t)b * a.T + t) * a.Hq + head;
+    E* o = reinterpret_cast<E*>(a.out) + orow * D;
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = db * 32 + 8 * j + 4 * h;
+        if constexpr (std::is_same<E, __bf16>::value) {
+          uint2 w;
+          w.x = pack_bf16x2(acc[db][j].x, acc[db][j].y);
+          w.y = pack_bf16x2(acc[db][j].z, acc[db][j].w);
+          *reinterpret_cast<uint2*>(o + d) = w;
+        } else {
+          *reinterpret_cast<float4*>(o + d) = acc[db][j];
+        }
+      }
+    if (a.lse && h == 0) a.lse[orow] = (M + __log2f(den)) * kLn2;
+  }
+}
+
+struct Plan {
+  int RB, S, chunk;
+  size_t ws_bytes;
+};
+
+Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int split_keys) {
+  Plan p;
+  const int G = Hq / Hkv;
+  p.RB = ceil_div(G * T, kRows);
+  const int Lc = Lmax > 0 ? Lmax : 1;
+  int chunk;
+  if (split_keys > 0) {
+    chunk = ceil_div(split_keys, kKT) * kKT;
+  } else {
+    // Enough workgroups for two rounds over the compute units, but chunks of >= 256 keys.
+    const long long units = (long long)B * Hkv * p.RB;
+    const long long want = 2LL * device_cu_count();
+    int S = (int)std::min<long long>(std::max<long long>(1, ceil_div_ll(want, units)),
+                                     std::max(1, ceil_div(Lc, 256)));
+    chunk = ceil_div(ceil_div(Lc, S), kKT) * kKT;
+  }
+  p.chunk = chunk;
+  p.S = std::max(1, ceil_div(Lc, chunk));
+  p.ws_bytes = p.S > 1 ? (size_t)B * Hkv * p.RB * p.S * kRows * (D + 2) * sizeof(float) : 0;
+  return p;
+}
+
+template <typename E, int D>
+int launch(const AttnArgs& a, hipStream_t stream) {
+  const int n_items = a.B * a.Hkv * a.S * a.RB;
+  if (a.S > 1) {
+    hipLaunchKernelGGL((attn_main<E, D, true>), dim3(n_items), dim3(256), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+    hipLaunchKernelGGL((attn_combine<E, D>), dim3(a.B * a.Hkv * a.RB), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((attn_main<E, D, false>), dim3(n_items), dim3(256), 0, stream, a);
+  }
+  return launch_status();
+}
+
+}  // namespace
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cu <= 0)
+      cu = 256;
+    cached[dev] = cu;
+  }
+  return cached[dev];
+}
+
+}  // namespace tv
+
+using namespace tv;
+
+static bool attn_shapes_ok(int B, int T, int Hq, int Hkv, int Lmax) {
+  return B >= 1 && T >= 1 && T <= kMaxT && Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 && Lmax >= 0 &&
+         (long long)B * Hkv * 64 * ceil_div(Hq / Hkv * T, kRows) < (1LL << 31);
+}
+
+extern "C" size_t tree_verify_attn_workspace_size(int B, int T, int Hq, int Hkv, int D, int Lmax,
+                                                  int dtype, int split_keys) {
+  if (!attn_shapes_ok(B, T, Hq, Hkv, Lmax) || (D != 64 && D != 128) ||
+      (dtype != TV_F32 && dtype != TV_BF16))
+    return 0;
+  return make_plan(B, T, Hq, Hkv, D, Lmax, split_keys).ws_bytes;
+}
+
+extern "C" int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* cache_len, const void* k_tree, const void* v_tree,
+                                const uint64_t* anc_mask, void* out, float* lse, int32_t* status,
+                                int B, int T, int Hq, int Hkv, int D, int Lmax, int dtype,
+                                float scale, int split_keys, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !cache_len || !k_tree || !v_tree || !anc_mask || !out ||
+      !attn_shapes_ok(B, T, Hq, Hkv, Lmax) || split_keys < 0)
+    return TV_ERR_INVALID_ARG;
+  if ((dtype != TV_F32 && dtype != TV_BF16) || (D != 64 && D != 128)) return TV_ERR_UNSUPPORTED;
+  const Plan p = make_plan(B, T, Hq, Hkv, D, Lmax, split_keys);
+  if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return TV_ERR_WORKSPACE;
+  if ((long long)B * Hkv * p.RB * p.S >= (1LL << 31)) return TV_ERR_INVALID_ARG;
+
+  AttnArgs a;
+  a.q = (const char*)q;
+  a.kc = (const char*)k_cache;
+  a.vc = (const char*)v_cache;
+  a.cache_len = cache_len;
+  a.kt = (const char*)k_tree;
+  a.vt = (const char*)v_tree;
+  a.anc = anc_mask;
+  a.out = (char*)out;
+  a.lse = lse;
+  a.status = status;
+  a.B = B;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.Lmax = Lmax;
+  a.W = ceil_div(T, 64);
+  a.GT = a.G * T;
+  a.RB = p.RB;
+  a.S = p.S;
+  a.chunk = p.chunk;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
+  a.c = sc * kLog2e;
+  float* ws = (float*)workspace;
+  a.part_o = ws;
+  a.part_ml = p.ws_bytes ? ws + (size_t)B * Hkv * p.RB * p.S * kRows * D : nullptr;
+
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == TV_BF16) return D == 128 ? launch<__bf16, 128>(a, st) : launch<__bf16, 64>(a, st);
+  return D == 128 ? launch<float, 128>(a, st) : launch<float, 64>(a, st);
+}
