@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""Benchmark of the tree-verification step on one MI355X.
+
+One step = tree_build_mask + tree_verify_attn + tree_accept + kv_compact_accepted (one layer)
+over one batch of the chosen synthetic workload, all on one stream with the inputs resident in
+HBM.  Copies of the input set are rotated so the bytes touched per sweep exceed twice the
+256 MB Infinity Cache.  Prints one JSON line:
+
+  value            KV-prefix bytes of the step / step time (GB/s), i.e. the prefix K/V read rate
+                   of the whole verification step
+  attn_kv_gbps     the same bytes / tree_verify_attn time alone
+  tree_tokens_per_s, accepted_tokens_per_s   B*T and sum(accept_len) per second of step time
+  roofline         the attention main kernel against MI355X's HBM (8 TB/s) or bf16 MFMA peak
+  cpu_baseline     the CPU oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from synth import WORKLOADS, make_workload  # noqa: E402
+
+DEFAULT_WORKLOAD = "llama8b_b1_L4096_T60"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+MALL_BYTES = 256 << 20
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_main_hbm_counters.json")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    p.add_argument("--split-keys", type=int, default=0, help="prefix keys per split (0 = auto)")
+    p.add_argument("--rotate", type=int, default=0, help="input copies to rotate (0 = auto)")
+    p.add_argument("--mode", choices=("graph", "eager"), default="graph",
+                   help="replay each step as a captured HIP graph, or launch eagerly")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tree_attention_verification_attn_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+class StepSet:
+    """Device buffers of one copy of the workload, plus pre-marshalled C-ABI argument tuples."""
+
+    def __init__(self, tv, torch, w, base=None, split_keys=0, workspace=None):
+        dev = torch.device("cuda:0")
+
+        def up(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        if base is None:
+            t = dict(parent=up(w.parent), draft=up(w.draft), target=up(w.target),
+                     cache_len=up(w.cache_len), q=up(w.q), k_cache=up(w.k_cache),
+                     v_cache=up(w.v_cache), k_tree=up(w.k_tree), v_tree=up(w.v_tree))
+        else:
+            t = {k: v.clone() for k, v in base.t.items()}
+        B, T, Hq, D = w.B, w.T, w.Hq, w.D
+        W = (T + 63) // 64
+        t["anc"] = torch.empty((B, T, W), dtype=torch.int64, device=dev)
+        t["status"] = torch.zeros((B,), dtype=torch.int32, device=dev)
+        t["out"] = torch.empty_like(t["q"])
+        t["lse"] = torch.empty((B, T, Hq), dtype=torch.float32, device=dev)
+        t["path"] = torch.empty((B, T), dtype=torch.int32, device=dev)
+        t["alen"] = torch.empty((B,), dtype=torch.int32, device=dev)
+        t["bonus"] = torch.empty((B,), dtype=torch.int32, device=dev)
+        t["cache_len_out"] = torch.empty((B,), dtype=torch.int32, device=dev)
+        self.t = t
+        P = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
+        dt = tv.TV_BF16 if w.dtype == "bf16" else tv.TV_F32
+        ws_bytes = 0 if workspace is None else workspace.numel()
+        ws_ptr = None if workspace is None else P(workspace)
+        self.lib = tv.load_library()
+        self.mask_args = (P(t["parent"]), B, T, P(t["anc"]), P(t["status"]))
+        self.attn_args = (P(t["q"]), P(t["k_cache"]), P(t["v_cache"]), P(t["cache_len"]),
+                          P(t["k_tree"]), P(t["v_tree"]), P(t["anc"]), P(t["out"]), P(t["lse"]),
+                          P(t["status"]), B, T, Hq, w.Hkv, D, w.Lmax, dt, ctypes.c_float(0.0),
+                          split_keys, ws_ptr, ctypes.c_size_t(ws_bytes))
+        self.accept_args = (P(t["anc"]), P(t["draft"]), P(t["target"]), B, T, P(t["path"]),
+                            P(t["alen"]), P(t["bonus"]))
+        self.compact_args = (P(t["k_cache"]), P(t["v_cache"]), P(t["cache_len"]),
+                             P(t["cache_len_out"]), P(t["k_tree"]), P(t["v_tree"]), P(t["path"]),
+                             P(t["alen"]), B, T, w.Hkv, D, w.Lmax, dt, P(t["status"]))
+
+    def mask(self, stream):
+        rc = self.lib.tree_build_mask(*self.mask_args, stream)
+        assert rc == 0, rc
+
+    def attn(self, stream):
+        rc = self.lib.tree_verify_attn(*self.attn_args, stream)
+        assert rc == 0, rc
+
+    def accept(self, stream):
+        rc = self.lib.tree_accept(*self.accept_args, stream)
+        assert rc == 0, rc
+
+    def compact(self, stream):
+        rc = self.lib.kv_compact_accepted(*self.compact_args, stream)
+        assert rc == 0, rc
+
+    def step(self, stream):
+        self.mask(stream)
+        self.attn(stream)
+        self.accept(stream)
+        self.compact(stream)
+
+
+def cpu_baseline(w, kv_bytes: int, target_s: float) -> dict:
+    """The oracle (never tuned) on a bounded random sample of attention rows."""
+    from oracle import oracle as O
+
+    cores = len(os.sched_getaffinity(0))
+    total = w.B * w.T * w.Hq
+    rng = np.random.default_rng(0)
+
+    def rows_of(n):
+        idx = rng.choice(total, size=n, replace=False)
+        b = idx // (w.T * w.Hq)
+        i = (idx // w.Hq) % w.T
+        h = idx % w.Hq
+        return np.stack([b, h, i], axis=1).astype(np.int32)
+
+    L = np.clip(w.cache_len, 0, w.Lmax).astype(np.int32)
+    n0 = min(total, cores)
+    t0 = time.perf_counter()
+    O.attention(w.q, w.k_cache, w.v_cache, L, w.k_tree, w.v_tree, w.parent, rows=rows_of(n0),
+                n_threads=cores)
+    dt0 = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(total, max(n0, n0 * target_s / dt0)))
+    rows = rows_of(n)
+    t0 = time.perf_counter()
+    O.attention(w.q, w.k_cache, w.v_cache, L, w.k_tree, w.v_tree, w.parent, rows=rows,
+                n_threads=cores)
+    dt = time.perf_counter() - t0
+    frac = n / total
+    full_s = dt / frac
+    return {
+        "value": kv_bytes / full_s / 1e9,
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{n} of {total} (b, query head, node) attention rows drawn uniformly "
+                   f"(seed 0), fp64, {dt:.1f} s wall; rate = KV-prefix bytes of the whole step "
+                   f"x {frac:.4f} / wall time; mask, acceptance and compaction excluded"),
+        "est_step_s": full_s,
+        "tree_tokens_per_s": w.B * w.T / full_s,
+    }
+
+
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the verification step has no multi-GPU path in "
+              "this build (sequences and KV heads would shard with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+    import torch
+
+    import tree_attention_verification_attn_amd as tv
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    tv.load_library()
+    torch.cuda.set_device(0)
+
+    print(f"[bench] generating workload {args.workload}", file=sys.stderr, flush=True)
+    w = make_workload(args.workload)
+    kv_bytes = w.kv_prefix_bytes()
+    L = np.clip(w.cache_len, 0, w.Lmax).astype(np.int64)
+    flops = 4 * int(L.sum()) * w.Hq * w.T * w.D  # QK^T and PV over the prefix
+    elem = 2 if w.dtype == "bf16" else 4
+    set_bytes = (w.k_cache.nbytes + w.v_cache.nbytes + w.q.nbytes * 2 + w.k_tree.nbytes * 2)
+    n_sets = args.rotate or max(1, math.ceil(2 * MALL_BYTES / max(kv_bytes, 1)))
+    free, total_mem = torch.cuda.mem_get_info()
+    n_sets = max(1, min(n_sets, int(0.5 * free / set_bytes)))
+
+    ws_bytes = tv.tree_verify_attn_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.Lmax,
+                                                  torch.bfloat16 if w.dtype == "bf16"
+                                                  else torch.float32, args.split_keys)
+    workspace = torch.zeros((max(ws_bytes, 1),), dtype=torch.uint8, device="cuda") if ws_bytes else None
+    print(f"[bench] uploading {n_sets} input sets ({set_bytes / 2**20:.1f} MiB each), "
+          f"workspace {ws_bytes / 2**20:.1f} MiB", file=sys.stderr, flush=True)
+    sets = [StepSet(tv, torch, w, split_keys=args.split_keys, workspace=workspace)]
+    for _ in range(n_sets - 1):
+        sets.append(StepSet(tv, torch, w, base=sets[0], split_keys=args.split_keys,
+                            workspace=workspace))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    graphs = None
+    if args.mode == "graph":
+        graphs = []
+        with torch.cuda.stream(stream):
+            for s in sets:  # one eager step first so any lazy initialisation is outside capture
+                s.step(sptr)
+        stream.synchronize()
+        for s in sets:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                s.step(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run_steps(k, offset=0):
+        for i in range(k):
+            j = (offset + i) % n_sets
+            if graphs is not None:
+                graphs[j].replay()
+            else:
+                sets[j].step(sptr)
+
+    with torch.cuda.stream(stream):
+        run_steps(args.warmup)
+        stream.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        e0.record(stream)
+        run_steps(args.steps, offset=args.warmup)
+        e1.record(stream)
+        e1.synchronize()
+        t_wall = time.perf_counter() - t_wall
+        torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    t_step = ms_per_step * 1e-3
+
+    # ---- per-call durations: a separate eager pass with events between the calls -------------
+    n_prof = min(args.steps, 200)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_prof)]
+    for row in ev:  # torch creates the underlying events on first record
+        for e in row:
+            e.record(stream)
+    stream.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(n_prof):
+            s = sets[i % n_sets]
+            ei = ev[i]
+            tv.profile_attn_main(ei[2], ei[3])
+            ei[0].record(stream)
+            s.mask(sptr)
+            ei[1].record(stream)
+            s.attn(sptr)
+            ei[4].record(stream)
+            s.accept(sptr)
+            ei[5].record(stream)
+            s.compact(sptr)
+        tv.profile_attn_main(None, None)
+        end = torch.cuda.Event(enable_timing=True)
+        end.record(stream)
+        end.synchronize()
+
+    def avg(a, b):
+        return float(np.mean([ev[i][a].elapsed_time(ev[i][b]) for i in range(n_prof)])) * 1e-3
+
+    t_mask, t_attn, t_main, t_accept = avg(0, 1), avg(1, 4), avg(2, 3), avg(4, 5)
+    t_compact = float(np.mean([ev[i][5].elapsed_time(ev[i + 1][0]) for i in range(n_prof - 1)]
+                              + [ev[-1][5].elapsed_time(end)])) * 1e-3
+
+    alen = sets[0].t["alen"].cpu().numpy()
+    status = sets[0].t["status"].cpu().numpy()
+    if (status & ~0).any():
+        print(f"[bench] warning: device status bits set: {np.unique(status)}", file=sys.stderr)
+
+    # ---- roofline of the dominant kernel ------------------------------------------------------
+    intensity = flops / kv_bytes
+    peak_tf = MFMA_PEAK_TFLOPS[w.dtype]
+    ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
+    traffic = None
+    if os.path.exists(COUNTERS_FILE):
+        with open(COUNTERS_FILE, encoding="utf-8") as f:
+            cnt = json.load(f)
+        rec = cnt.get(args.workload)
+        if rec and rec.get("kernel_source_hash") == kernel_source_hash():
+            traffic = rec.get("hbm_bytes_per_launch")
+    if intensity < ridge:
+        roof = {"bound": "hbm", "achieved": kv_bytes / t_main / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / t_main / 1e12, "peak": peak_tf,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    roof["kernel"] = "attn_main"
+    roof["kernel_us"] = t_main * 1e6
+    roof["algorithmic_bytes"] = kv_bytes
+    roof["algorithmic_flops"] = flops
+
+    value = kv_bytes / t_step / 1e9
+    result = {
+        "metric": "tree-verify attn KV-read GB/s (% HBM peak) + verified tree tokens/sec",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "desc": w.spec.desc, "B": w.B, "T": w.T,
+                   "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "prefix_tokens": int(L.sum()),
+                   "Lmax": w.Lmax, "layers": 1, "mode": args.mode, "rotated_sets": n_sets,
+                   "split_keys": args.split_keys},
+        "hbm_frac": value / HBM_PEAK_GBS,
+        "attn_kv_gbps": kv_bytes / t_attn / 1e9,
+        "attn_hbm_frac": kv_bytes / t_attn / 1e9 / HBM_PEAK_GBS,
+        "attn_mfma_frac": flops / t_attn / 1e12 / peak_tf,
+        "tree_tokens_per_s": w.B * w.T / t_step,
+        "accepted_tokens_per_s": float(alen.sum()) / t_step,
+        "step_breakdown_us": {"tree_build_mask": t_mask * 1e6, "tree_verify_attn": t_attn * 1e6,
+                              "attn_main": t_main * 1e6, "tree_accept": t_accept * 1e6,
+                              "kv_compact_accepted": t_compact * 1e6},
+        "wall_s_timed": t_wall,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, kv_bytes, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

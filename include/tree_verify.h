@@ -112,6 +112,16 @@ int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                      int split_keys, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * tv_profile_attn_main — profiling hook for the attention main kernel.
+ * While set, every tree_verify_attn call records `ev_before` (a hipEvent_t) on its stream just
+ * before launching its main kernel and `ev_after` just after it, i.e. before the split-K merge,
+ * so the main kernel's duration can be read with hipEventElapsedTime.  Pass NULL, NULL to turn
+ * it off.  Process-wide setting, not synchronised: set it while no other thread calls
+ * tree_verify_attn.  Returns TV_ERR_INVALID_ARG if exactly one event is NULL.
+ */
+int tv_profile_attn_main(void* ev_before, void* ev_after);
+
+/*
  * tree_accept — greedy acceptance and the single longest accepted path.
  * A drafted token is accepted iff it equals the target model's greedy choice at its parent
  * (lesty.tech section 4); a node is accepted iff every node on its root path is; the root (the

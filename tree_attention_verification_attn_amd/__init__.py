@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     kv_compact_accepted,
     lib_path,
     load_library,
+    profile_attn_main,
     status_string,
     tree_accept,
     tree_build_mask,

@@ -19,7 +19,7 @@ TV_F32, TV_BF16 = 0, 1
 TV_BAD_TREE, TV_OVERFLOW, TV_BAD_LEN, TV_BAD_PATH = 0x1, 0x2, 0x4, 0x8
 
 EXPORTS = ("tv_status_string", "tree_build_mask", "tree_verify_attn_workspace_size",
-           "tree_verify_attn", "tree_accept", "kv_compact_accepted")
+           "tree_verify_attn", "tree_accept", "kv_compact_accepted", "tv_profile_attn_main")
 
 
 class TreeVerifyError(RuntimeError):
@@ -68,6 +68,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_accept.restype = I
     lib.kv_compact_accepted.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, P]
     lib.kv_compact_accepted.restype = I
+    lib.tv_profile_attn_main.argtypes = [P, P]
+    lib.tv_profile_attn_main.restype = I
 
 
 def status_string(code: int) -> str:
@@ -108,6 +110,13 @@ def _need(t: torch.Tensor, name: str, dtype=None, ndim=None) -> None:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dimensions, got {t.dim()}")
+
+
+def profile_attn_main(before: torch.cuda.Event | None, after: torch.cuda.Event | None) -> None:
+    """Record `before`/`after` around every later tree_verify_attn main kernel (None, None: off).
+    The events must have been recorded once (torch creates them lazily)."""
+    ptr = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)  # noqa: E731
+    _check("tv_profile_attn_main", load_library().tv_profile_attn_main(ptr(before), ptr(after)))
 
 
 def tree_build_mask(parent: torch.Tensor, anc_mask: torch.Tensor | None = None,

@@ -2,18 +2,20 @@
 //
 // Work decomposition (one KV head at a time, GQA-grouped):
 //   * The G*T query rows of one (sequence b, KV head) are ordered r = t*G + g (node t, query
-//     head kvh*G + g).  A workgroup owns 256 of them: 4 wavefronts x 64 rows.  Every prefix key
-//     is visible to every row, so the K/V rows streamed through LDS are shared by all 256 rows.
+//     head kvh*G + g).  A workgroup owns 128 of them: 4 wavefronts x 32 rows.  Every prefix key
+//     is visible to every row, so a K/V tile staged in LDS serves all 128 rows.  Two workgroups
+//     share a compute unit (two wavefronts per SIMD), so one wavefront's softmax overlaps the
+//     other's matrix instructions.
 //   * The prefix is cut into equal chunks of `chunk` keys (split-K).  Chunk s of sequence b is
 //     processed by its own workgroup; chunk 0 also processes the T tree keys, which are masked
 //     per row by the ancestor bitmask.  Partial results (unnormalised O, running max m, sum l)
 //     are merged by attn_combine; a sequence with a single non-empty chunk is written directly.
-//   * Per 64-key tile: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS as the A operand, Q
-//     held in registers as the B operand), masking, online softmax in the log2 domain, then
-//     O^T += V^T P^T (V^T fragments from LDS with the gfx950 transpose read, P taken straight
-//     from the S^T accumulators).  In the transposed form a lane holds one query row in both
-//     the score and the output accumulators, so the softmax statistics never leave the lane
-//     pair (l, l^32).
+//   * Per 64-key tile, in two 32-key blocks: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS
+//     as the A operand, Q held in registers as the B operand), masking, online softmax in the
+//     log2 domain, then O^T += V^T P^T (V^T fragments from LDS with the gfx950 transpose read,
+//     P taken straight from the S^T accumulators).  In this transposed form a lane holds one
+//     query row in both the score and the output accumulators, so the softmax statistics never
+//     leave the lane pair (l, l^32).
 //   * Online softmax with lazy rescaling: the running max is raised only when a row's max grows
 //     by more than 2^8, so P <= 256 and O is rescaled rarely.
 //   * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same structure.
@@ -36,8 +38,8 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kWaves = 4;
-constexpr int kRows = 256;         // query rows per workgroup
-constexpr int kKT = 64;            // keys per tile
+constexpr int kRows = 32 * kWaves;  // query rows per workgroup
+constexpr int kKT = 64;             // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units a row's max may outgrow the running max
@@ -74,8 +76,9 @@ struct Layout {
   static constexpr int kTileK = kKT * kPitchK;
   static constexpr int kTileV = kKT * kPitchV;
   static constexpr int kStage = kTileK + kTileV;
-  static constexpr int kLoads = kKT * kCPR / 256;  // chunks per thread per tile
-  static constexpr int kDB = D / 32;               // 32-wide d blocks
+  static constexpr int kLoads = kKT * kCPR / (64 * kWaves);  // chunks per thread per tile
+  static constexpr int kDB = D / 32;                         // 32-wide d blocks
+  static constexpr int kKS = kBF16 ? D / 16 : D / 2;         // MFMA k-steps over D
 };
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -103,14 +106,12 @@ __device__ inline int xcd_remap(int bid, int n) {
 }
 
 template <typename E, int D, bool kSplit>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
 void attn_main(AttnArgs a) {
   using Lay = Layout<E, D>;
   constexpr bool kBF16 = Lay::kBF16;
   constexpr int kDB = Lay::kDB;
-  // Marks the kernel as using accumulation registers, so the MFMA accumulators are allocated
-  // there (AGPR form) instead of competing with the softmax values for arch VGPRs.
-  asm volatile("" ::: "a0");
+  constexpr int kKS = Lay::kKS;
   __shared__ __attribute__((aligned(16))) char smem[2 * Lay::kStage];
 
   const int n_items = a.B * a.Hkv * a.S * a.RB;
@@ -136,46 +137,33 @@ void attn_main(AttnArgs a) {
   const int n_tree_tiles = s == 0 ? (a.T + kKT - 1) / kKT : 0;
   const int n_tiles = n_tree_tiles + n_prefix_tiles;
 
-  // ---- rows of this lane: r = rb*256 + wave*64 + nb*32 + n ---------------------------------
-  int row_t[2], row_head[2];
-  bool row_ok[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int r = rb * kRows + wave * 64 + nb * 32 + n;
-    row_ok[nb] = r < a.GT;
-    row_t[nb] = row_ok[nb] ? r / a.G : 0;
-    row_head[nb] = kvh * a.G + (row_ok[nb] ? r % a.G : 0);
-  }
+  // ---- the lane's query row: r = rb*128 + wave*32 + n -------------------------------------
+  const int r = rb * kRows + wave * 32 + n;
+  const bool row_ok = r < a.GT;
+  const int row_t = row_ok ? r / a.G : 0;  // padding rows load a real row; never written
+  const int row_head = kvh * a.G + (row_ok ? r % a.G : 0);
 
-  // ---- Q fragments (B operand): row n, d = ks*K + [group of lane] --------------------------
-  constexpr int kKS = kBF16 ? D / 16 : D / 2;
+  // ---- Q fragments (B operand): row n, d = 16*ks + 8*h .. +7 (bf16) or 2*ks + h (fp32) -----
   using QFrag = typename std::conditional<kBF16, bf16x8, float>::type;
-  QFrag qf[2][kKS];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    // padding rows load a real row (row_t = 0): finite values, outputs never written
+  QFrag qf[kKS];
+  {
     const E* qrow = reinterpret_cast<const E*>(a.q) +
-                    (((size_t)b * a.T + row_t[nb]) * a.Hq + row_head[nb]) * D;
+                    (((size_t)b * a.T + row_t) * a.Hq + row_head) * D;
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       if constexpr (kBF16) {
-        qf[nb][ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + 8 * h);
+        qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + 8 * h);
       } else {
-        qf[nb][ks] = qrow[ks * 2 + h];
+        qf[ks] = qrow[ks * 2 + h];
       }
     }
   }
-  // ancestor mask words of the lane's rows (padding rows see only the root)
-  uint64_t mk[2][2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    mk[nb][0] = 1;
-    mk[nb][1] = 0;
-    if (row_ok[nb] && n_tree_tiles) {
-      const uint64_t* mrow = a.anc + ((size_t)b * a.T + row_t[nb]) * a.W;
-      mk[nb][0] = mrow[0];
-      mk[nb][1] = a.W > 1 ? mrow[1] : 0;
-    }
+  // ancestor mask words of the lane's row (padding rows see only the root)
+  uint64_t mk0 = 1, mk1 = 0;
+  if (row_ok && n_tree_tiles) {
+    const uint64_t* mrow = a.anc + ((size_t)b * a.T + row_t) * a.W;
+    mk0 = mrow[0];
+    mk1 = a.W > 1 ? mrow[1] : 0;
   }
 
   // ---- tile staging ------------------------------------------------------------------------
@@ -228,19 +216,23 @@ void attn_main(AttnArgs a) {
   };
 
   // ---- accumulators ------------------------------------------------------------------------
-  f32x16 oacc[kDB][2];
+  f32x16 oacc[kDB];
 #pragma unroll
-  for (int db = 0; db < kDB; ++db)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) oacc[db][nb] = f32x16{};
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+  for (int db = 0; db < kDB; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
 
   if (n_tiles > 0) {
     load_tile(0);
     store_tile(0);
   }
   __syncthreads();
+
+  // per-lane LDS fragment bases (bytes)
+  const int k_frag = n * Lay::kPitchK + h * (kBF16 ? 16 : 4);
+  const int v_frag = kBF16 ? (4 * h + ((lane & 15) >> 2)) * Lay::kPitchV +
+                                 (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2
+                           : (4 * h) * Lay::kPitchV + n * 4;
 
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int buf = tile & 1;
@@ -252,132 +244,91 @@ void attn_main(AttnArgs a) {
     tile_keys(tile, base, end, is_tree);
     const bool need_mask = is_tree || base + kKT > end;
     // a tree tile covers nodes 64*tile .. 64*tile+63: one mask word per row
-    uint64_t mword[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) mword[nb] = !is_tree ? ~0ull : (tile == 0 ? mk[nb][0] : mk[nb][1]);
+    const uint64_t mword = !is_tree ? ~0ull : (tile == 0 ? mk0 : mk1);
 
-    // The 64-key tile is consumed as two 32-key blocks kb; each runs QK, softmax and PV.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // ---- S^T = K Q^T for keys kb*32 .. kb*32+31 ------------------------------------------
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+      f32x16 sacc = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
         if constexpr (kBF16) {
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-              kl + (kb * 32 + n) * Lay::kPitchK + (2 * ks + h) * 16);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[nb][ks], sacc[nb], 0, 0, 0);
+              kl + k_frag + kb * 32 * Lay::kPitchK + ks * 32);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
         } else {
           const float kf = *reinterpret_cast<const float*>(
-              kl + (kb * 32 + n) * Lay::kPitchK + (2 * ks + h) * 4);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb)
-            sacc[nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(kf, qf[nb][ks], sacc[nb], 0, 0, 0);
+              kl + k_frag + kb * 32 * Lay::kPitchK + ks * 8);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf, qf[ks], sacc, 0, 0, 0);
         }
       }
 
-      // ---- mask: element r is key base + kb*32 + 8*(r/4) + 4*h + r%4 ------------------------
+      // ---- mask: element e is key base + kb*32 + 8*(e/4) + 4*h + e%4 ------------------------
       if (need_mask) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const bool vis = base + kk < end && ((mword[nb] >> kk) & 1);
-            sacc[nb][r] = vis ? sacc[nb][r] : -INFINITY;
-          }
+        for (int e = 0; e < 16; ++e) {
+          const int kk = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+          const bool vis = base + kk < end && ((mword >> kk) & 1);
+          sacc[e] = vis ? sacc[e] : -INFINITY;
         }
       }
 
       // ---- online softmax (log2 domain) ----------------------------------------------------
-      bool need_rescale = false;
-      float m_new[2];
+      float mx = sacc[0];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float mx = -INFINITY;
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
+      mx = fmaxf(mx, partner(mx));
+      const float m_new = fmaxf(m_run, mx * a.c);
+      const bool grow = m_new > m_run + kRescaleSlack;
+      if (__ballot(grow)) {
+        float alpha = 1.f;
+        if (grow) {
+          alpha = fast_exp2(m_run - m_new);  // 0 on the first block
+          m_run = m_new;
+        }
+        l_run *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nb][r]);
-        mx = fmaxf(mx, partner(mx));
-        m_new[nb] = fmaxf(m_run[nb], mx * a.c);
-        need_rescale |= m_new[nb] > m_run[nb] + kRescaleSlack;
+        for (int db = 0; db < kDB; ++db) oacc[db] *= alpha;
       }
-      if (__ballot(need_rescale)) {
+      const float mb = m_run == -INFINITY ? 0.f : m_run;
+      float p[16];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          float alpha = 1.f;
-          if (m_new[nb] > m_run[nb] + kRescaleSlack) {
-            alpha = fast_exp2(m_run[nb] - m_new[nb]);  // 0 on the first block
-            m_run[nb] = m_new[nb];
-          }
-          l_run[nb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < kDB; ++db) oacc[db][nb] *= alpha;
-        }
-      }
-      using PFrag = typename std::conditional<kBF16, bf16x8, float>::type;
-      PFrag pf[2][kBF16 ? 2 : 16];  // [nb][16-key step] (bf16) or [nb][element] (fp32)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const float mb = m_run[nb] == -INFINITY ? 0.f : m_run[nb];
-        float p[16];
-        float lsum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p[r] = fast_exp2(__builtin_fmaf(sacc[nb][r], a.c, -mb));
-          lsum += p[r];
-        }
-        l_run[nb] += lsum;
-        if constexpr (kBF16) {
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * st + 2 * e], p[8 * st + 2 * e + 1]);
-            pf[nb][st] = __builtin_bit_cast(bf16x8, w);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) pf[nb][r] = p[r];
-        }
+      for (int e = 0; e < 16; ++e) {
+        p[e] = fast_exp2(__builtin_fmaf(sacc[e], a.c, -mb));
+        l_run += p[e];
       }
 
       // ---- O^T += V^T P^T ------------------------------------------------------------------
       if constexpr (kBF16) {
-        // 16-key step st covers keys kb*32 + 16st + {4h..4h+3} (elements 0-3) and
-        // kb*32 + 16st + 8 + {4h..4h+3} (elements 4-7); a transpose read gives lane i of each
-        // 16-lane group 4 consecutive keys at d = D0 + i.
-        const int tr_key = 4 * h + ((lane & 15) >> 2);
-        const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        // 16-key step st: keys kb*32 + 16st + {4h..4h+3} (elements 0-3) and kb*32 + 16st + 8 +
+        // {4h..4h+3} (elements 4-7); a transpose read gives lane i of each 16-lane group four
+        // consecutive keys at d = D0 + i.
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * st + 2 * e], p[8 * st + 2 * e + 1]);
+          const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
           for (int db = 0; db < kDB; ++db) {
-            const int o0 = (kb * 32 + 16 * st + tr_key) * Lay::kPitchV + (db * 32 + tr_d) * 2;
-            const int o1 = o0 + 8 * Lay::kPitchV;
+            const int o0 = v_frag + (kb * 32 + 16 * st) * Lay::kPitchV + db * 64;
             const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vl + o0));
-            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vl + o1));
+            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vl + o0 + 8 * Lay::kPitchV));
             const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, v);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-              oacc[db][nb] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb][st], oacc[db][nb], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pf,
+                                                              oacc[db], 0, 0, 0);
           }
         }
       } else {
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int key = kb * 32 + 8 * (u >> 2) + 4 * h + (u & 3);
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb * 32 + 8 * (e >> 2) + (e & 3);  // + 4h folded into v_frag
 #pragma unroll
           for (int db = 0; db < kDB; ++db) {
             const float vf =
-                *reinterpret_cast<const float*>(vl + key * Lay::kPitchV + (db * 32 + n) * 4);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-              oacc[db][nb] =
-                  __builtin_amdgcn_mfma_f32_32x32x2f32(vf, pf[nb][u], oacc[db][nb], 0, 0, 0);
+                *reinterpret_cast<const float*>(vl + v_frag + key * Lay::kPitchV + db * 128);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf, p[e], oacc[db], 0, 0, 0);
           }
         }
       }
@@ -388,22 +339,19 @@ void attn_main(AttnArgs a) {
   }
 
   // ---- epilogue ----------------------------------------------------------------------------
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) l_run[nb] += partner(l_run[nb]);
+  l_run += partner(l_run);
 
   if (direct) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      if (!row_ok[nb]) continue;
-      const float inv = 1.f / l_run[nb];
-      const size_t orow = ((size_t)b * a.T + row_t[nb]) * a.Hq + row_head[nb];
+    if (row_ok) {
+      const float inv = 1.f / l_run;
+      const size_t orow = ((size_t)b * a.T + row_t) * a.Hq + row_head;
       E* o = reinterpret_cast<E*>(a.out) + orow * D;
 #pragma unroll
       for (int db = 0; db < kDB; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int d = db * 32 + 8 * j + 4 * h;
-          const f32x16& acc = oacc[db][nb];
+          const f32x16& acc = oacc[db];
           if constexpr (kBF16) {
             uint2 w;
             w.x = pack_bf16x2(acc[4 * j] * inv, acc[4 * j + 1] * inv);
@@ -415,97 +363,93 @@ void attn_main(AttnArgs a) {
                        acc[4 * j + 3] * inv};
           }
         }
-      if (a.lse && h == 0) a.lse[orow] = (m_run[nb] + __log2f(l_run[nb])) * kLn2;
+      if (a.lse && h == 0) a.lse[orow] = (m_run + __log2f(l_run)) * kLn2;
     }
   } else {
     const size_t slot = (((size_t)b * a.Hkv + kvh) * a.RB + rb) * a.S + s;
     float4* po = reinterpret_cast<float4*>(a.part_o + slot * (size_t)kRows * D);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int db = 0; db < kDB; ++db)
 #pragma unroll
-      for (int db = 0; db < kDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x16& acc = oacc[db][nb];
-          po[((((wave * 2 + nb) * kDB + db) * 4 + j) << 6) + lane] =
-              float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
-        }
+      for (int j = 0; j < 4; ++j) {
+        const f32x16& acc = oacc[db];
+        po[(((wave * kDB + db) * 4 + j) << 6) + lane] =
+            float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+      }
     if (h == 0) {
       float2* pml = reinterpret_cast<float2*>(a.part_ml + slot * (size_t)kRows * 2);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) pml[wave * 64 + nb * 32 + n] = float2{m_run[nb], l_run[nb]};
+      pml[wave * 32 + n] = float2{m_run, l_run};
     }
   }
 }
 
 // Merge the per-chunk partials of sequences with more than one non-empty chunk:
 //   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  lse = (M + log2 den) ln 2.
+// One wavefront per 32 rows of a row block.
 template <typename E, int D>
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+__global__ __launch_bounds__(64) void attn_combine(AttnArgs a) {
   constexpr int kDB = D / 32;
-  const int item = blockIdx.x;  // (b, kvh, rb)
+  const int wave = blockIdx.x % kWaves;
+  const int item = blockIdx.x / kWaves;  // (b, kvh, rb)
   const int rb = item % a.RB;
   const int kvh = (item / a.RB) % a.Hkv;
   const int b = item / (a.RB * a.Hkv);
   const int L = min(max(a.cache_len[b], 0), a.Lmax);
   const int n_split = max(1, ceil_div(L, a.chunk));
   if (n_split == 1) return;  // written directly by attn_main
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lane = threadIdx.x;
   const int n = lane & 31, h = lane >> 5;
+  const int rloc = wave * 32 + n;
+  const int r = rb * kRows + rloc;
+  if (r >= a.GT) return;
   const size_t slot0 = (((size_t)b * a.Hkv + kvh) * a.RB + rb) * a.S;
   const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
   const float4* po = reinterpret_cast<const float4*>(a.part_o);
+
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pml[(slot0 + s) * kRows + rloc].x);
+  float den = 0.f;
+  float4 acc[kDB][4];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int rloc = wave * 64 + nb * 32 + n;
-    const int r = rb * kRows + rloc;
-    if (r >= a.GT) continue;
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s) M = fmaxf(M, pml[(slot0 + s) * kRows + rloc].x);
-    float den = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-      const float2 ml = pml[(slot0 + s) * kRows + rloc];
-      den += fast_exp2(ml.x - M) * ml.y;
-    }
-    const float inv = 1.f / den;
-    float4 acc[kDB][4];
+  for (int db = 0; db < kDB; ++db)
 #pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[db][j] = float4{0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n_split; ++s) {
-      const float w = fast_exp2(pml[(slot0 + s) * kRows + rloc].x - M) * inv;
-      const float4* ps = po + (slot0 + s) * (size_t)kRows * D / 4;
-#pragma unroll
-      for (int db = 0; db < kDB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 v = ps[((((wave * 2 + nb) * kDB + db) * 4 + j) << 6) + lane];
-          acc[db][j].x += w * v.x;
-          acc[db][j].y += w * v.y;
-          acc[db][j].z += w * v.z;
-          acc[db][j].w += w * v.w;
-        }
-    }
-    const int t = r / a.G, head = kvh * a.G + r % a.G;
-    const size_t orow = ((size_t)b * a.T + t) * a.Hq + head;
-    E* o = reinterpret_cast<E*>(a.out) + orow * D;
+    for (int j = 0; j < 4; ++j) acc[db][j] = float4{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < n_split; ++s) {
+    const float2 ml = pml[(slot0 + s) * kRows + rloc];
+    const float w = fast_exp2(ml.x - M);
+    den += w * ml.y;
+    const float4* ps = po + (slot0 + s) * (size_t)kRows * D / 4;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d = db * 32 + 8 * j + 4 * h;
-        if constexpr (std::is_same<E, __bf16>::value) {
-          uint2 w;
-          w.x = pack_bf16x2(acc[db][j].x, acc[db][j].y);
-          w.y = pack_bf16x2(acc[db][j].z, acc[db][j].w);
-          *reinterpret_cast<uint2*>(o + d) = w;
-        } else {
-          *reinterpret_cast<float4*>(o + d) = acc[db][j];
-        }
+        const float4 v = ps[(((wave * kDB + db) * 4 + j) << 6) + lane];
+        acc[db][j].x += w * v.x;
+        acc[db][j].y += w * v.y;
+        acc[db][j].z += w * v.z;
+        acc[db][j].w += w * v.w;
       }
-    if (a.lse && h == 0) a.lse[orow] = (M + __log2f(den)) * kLn2;
   }
+  const float inv = 1.f / den;
+  const int t = r / a.G, head = kvh * a.G + r % a.G;
+  const size_t orow = ((size_t)b * a.T + t) * a.Hq + head;
+  E* o = reinterpret_cast<E*>(a.out) + orow * D;
+#pragma unroll
+  for (int db = 0; db < kDB; ++db)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = db * 32 + 8 * j + 4 * h;
+      const float4 v = acc[db][j];
+      if constexpr (std::is_same<E, __bf16>::value) {
+        uint2 w;
+        w.x = pack_bf16x2(v.x * inv, v.y * inv);
+        w.y = pack_bf16x2(v.z * inv, v.w * inv);
+        *reinterpret_cast<uint2*>(o + d) = w;
+      } else {
+        *reinterpret_cast<float4*>(o + d) = float4{v.x * inv, v.y * inv, v.z * inv, v.w * inv};
+      }
+    }
+  if (a.lse && h == 0) a.lse[orow] = (M + __log2f(den)) * kLn2;
 }
 
 struct Plan {
@@ -522,9 +466,10 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int split_keys) {
   if (split_keys > 0) {
     chunk = ceil_div(split_keys, kKT) * kKT;
   } else {
-    // Enough workgroups for two rounds over the compute units, but chunks of >= 256 keys.
+    // Two workgroups fit on a compute unit: aim for two rounds of those, with chunks of at
+    // least 256 keys.
     const long long units = (long long)B * Hkv * p.RB;
-    const long long want = 2LL * device_cu_count();
+    const long long want = 4LL * device_cu_count();
     int S = (int)std::min<long long>(std::max<long long>(1, ceil_div_ll(want, units)),
                                      std::max(1, ceil_div(Lc, 256)));
     chunk = ceil_div(ceil_div(Lc, S), kKT) * kKT;
@@ -535,16 +480,22 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int split_keys) {
   return p;
 }
 
+// Profiling events recorded around the main kernel (tv_profile_attn_main).
+hipEvent_t g_prof_before = nullptr, g_prof_after = nullptr;
+
 template <typename E, int D>
 int launch(const AttnArgs& a, hipStream_t stream) {
   const int n_items = a.B * a.Hkv * a.S * a.RB;
-  if (a.S > 1) {
+  if (g_prof_before && hipEventRecord(g_prof_before, stream) != hipSuccess) return TV_ERR_HIP;
+  if (a.S > 1)
     hipLaunchKernelGGL((attn_main<E, D, true>), dim3(n_items), dim3(256), 0, stream, a);
-    if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
-    hipLaunchKernelGGL((attn_combine<E, D>), dim3(a.B * a.Hkv * a.RB), dim3(256), 0, stream, a);
-  } else {
+  else
     hipLaunchKernelGGL((attn_main<E, D, false>), dim3(n_items), dim3(256), 0, stream, a);
-  }
+  if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
+  if (g_prof_after && hipEventRecord(g_prof_after, stream) != hipSuccess) return TV_ERR_HIP;
+  if (a.S > 1)
+    hipLaunchKernelGGL((attn_combine<E, D>), dim3(a.B * a.Hkv * a.RB * kWaves), dim3(64), 0,
+                       stream, a);
   return launch_status();
 }
 
@@ -571,6 +522,13 @@ using namespace tv;
 static bool attn_shapes_ok(int B, int T, int Hq, int Hkv, int Lmax) {
   return B >= 1 && T >= 1 && T <= kMaxT && Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0 && Lmax >= 0 &&
          (long long)B * Hkv * 64 * ceil_div(Hq / Hkv * T, kRows) < (1LL << 31);
+}
+
+extern "C" int tv_profile_attn_main(void* ev_before, void* ev_after) {
+  if ((ev_before == nullptr) != (ev_after == nullptr)) return TV_ERR_INVALID_ARG;
+  g_prof_before = (hipEvent_t)ev_before;
+  g_prof_after = (hipEvent_t)ev_after;
+  return TV_OK;
 }
 
 extern "C" size_t tree_verify_attn_workspace_size(int B, int T, int Hq, int Hkv, int D, int Lmax,
