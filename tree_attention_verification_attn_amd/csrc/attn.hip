@@ -2,10 +2,13 @@
 //
 // Work decomposition (one KV head at a time, GQA-grouped):
 //   * The G*T query rows of one (sequence b, KV head) are ordered r = t*G + g (node t, query
-//     head kvh*G + g).  A workgroup owns 128 of them: 4 wavefronts x 32 rows.  Every prefix key
-//     is visible to every row, so a K/V tile staged in LDS serves all 128 rows.  Two workgroups
-//     share a compute unit (two wavefronts per SIMD), so one wavefront's softmax overlaps the
-//     other's matrix instructions.
+//     head kvh*G + g).  A workgroup owns 256 of them: 8 wavefronts x 32 rows, two wavefronts per
+//     SIMD, so one wavefront's softmax overlaps the other's matrix instructions.  Every prefix
+//     key is visible to every row, so a K/V tile staged in LDS serves all 256 rows.
+//   * K/V tiles of 64 keys move HBM -> LDS by direct-to-LDS loads (global_load_lds_dwordx4)
+//     through a ring of LDS stages, three tiles ahead of the one being computed; no registers
+//     hold staged data.  Each wavefront waits only for its own loads of the tile it needs, then
+//     one barrier per tile publishes the tile and frees the oldest stage.
 //   * The prefix is cut into equal chunks of `chunk` keys (split-K).  Chunk s of sequence b is
 //     processed by its own workgroup; chunk 0 also processes the T tree keys, which are masked
 //     per row by the ancestor bitmask.  Partial results (unnormalised O, running max m, sum l)
@@ -16,6 +19,9 @@
 //     P taken straight from the S^T accumulators).  In this transposed form a lane holds one
 //     query row in both the score and the output accumulators, so the softmax statistics never
 //     leave the lane pair (l, l^32).
+//   * LDS rows are unpadded; 16-byte chunks are XOR-swizzled by row so the K reads (16 keys x
+//     one chunk), the transposed V reads (4 keys x 4 chunks per 16 lanes) and the 1 KB
+//     direct-load writes are all free of bank conflicts.
 //   * Online softmax with lazy rescaling: the running max is raised only when a row's max grows
 //     by more than 2^8, so P <= 256 and O is rescaled rarely.
 //   * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same structure.
@@ -34,10 +40,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // query rows per workgroup
 constexpr int kKT = 64;             // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
@@ -65,20 +71,22 @@ template <typename E, int D>
 struct Layout {
   static constexpr bool kBF16 = std::is_same<E, __bf16>::value;
   static constexpr int kElem = sizeof(E);
-  static constexpr int kRowBytes = D * kElem;
-  static constexpr int kCPR = kRowBytes / 16;  // 16-byte chunks per row
-  // Padded LDS rows.  K rows are read 16 consecutive keys at a time (stride = 4 banks mod 64);
-  // V rows are read by the transpose loads as 4 keys x 64 bytes (stride = 16 banks mod 64).
-  // Both patterns, and the 16-byte row writes, are free of LDS bank conflicts, and every
-  // fragment address is one per-lane base plus a compile-time offset.
-  static constexpr int kPitchK = kRowBytes + 16;
-  static constexpr int kPitchV = kBF16 ? kRowBytes + 64 : kRowBytes + 16;
-  static constexpr int kTileK = kKT * kPitchK;
-  static constexpr int kTileV = kKT * kPitchV;
-  static constexpr int kStage = kTileK + kTileV;
-  static constexpr int kLoads = kKT * kCPR / (64 * kWaves);  // chunks per thread per tile
-  static constexpr int kDB = D / 32;                         // 32-wide d blocks
-  static constexpr int kKS = kBF16 ? D / 16 : D / 2;         // MFMA k-steps over D
+  static constexpr int kRowBytes = D * kElem;          // 128, 256 or 512
+  static constexpr int kCPR = kRowBytes / 16;          // 16-byte chunks per row
+  static constexpr int kTile = kKT * kRowBytes;        // bytes of one K (or V) tile
+  static constexpr int kStage = 2 * kTile;             // K tile then V tile
+  static constexpr int kStages = kStage <= 32768 ? 4 : 2;
+  static constexpr int kAhead = kStages - 1;           // tiles in flight beyond the current one
+  static constexpr int kRowsPerDma = 1024 / kRowBytes; // rows one wavefront-wide load fills
+  static constexpr int kDmaPerWave = kTile / 1024 / kWaves;  // per K (or V) tile
+  static constexpr int kDB = D / 32;                   // 32-wide d blocks
+  static constexpr int kKS = kBF16 ? D / 16 : D / 2;   // MFMA k-steps over D
+
+  // XOR applied to the chunk index of tile row `row` (depends on row mod 16 only).
+  __device__ static inline int swz(int row) {
+    return kCPR == 8 ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3))
+                     : (((row & 3) << 2) | ((row >> 2) & 3));
+  }
 };
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -96,6 +104,30 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// One wavefront-wide direct-to-LDS load: lane l's 16 bytes at sbase + voff land at LDS address
+// lds + 16*l.  Issued from inline assembly so that the compiler does not order LDS reads behind
+// every in-flight tile; the kernel waits for these loads itself (vm_wait) before its barriers.
+// M0 carries the LDS address and is restored afterwards.
+__device__ inline void lds_dma16(uint32_t lds, const void* sbase, uint32_t voff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(sbase)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(n) (n <= 63), other counters untouched.
+template <int N>
+__device__ inline void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Logical work item -> hardware workgroup id.  Workgroups are dealt to the 8 XCDs round-robin;
 // this gives every XCD a contiguous range of logical items, so items that read the same K/V
 // chunk (consecutive row blocks) or the same Q rows (consecutive splits) share an L2.
@@ -106,13 +138,17 @@ __device__ inline int xcd_remap(int bid, int n) {
 }
 
 template <typename E, int D, bool kSplit>
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(2, 2)))
 void attn_main(AttnArgs a) {
   using Lay = Layout<E, D>;
   constexpr bool kBF16 = Lay::kBF16;
   constexpr int kDB = Lay::kDB;
   constexpr int kKS = Lay::kKS;
-  __shared__ __attribute__((aligned(16))) char smem[2 * Lay::kStage];
+  constexpr int kRB = Lay::kRowBytes;
+  constexpr int kNS = Lay::kStages;
+  constexpr int kDPW = Lay::kDmaPerWave;
+  __shared__ __attribute__((aligned(1024))) char smem[kNS * Lay::kStage];
 
   const int n_items = a.B * a.Hkv * a.S * a.RB;
   const int item = xcd_remap(blockIdx.x, n_items);
@@ -121,7 +157,8 @@ void attn_main(AttnArgs a) {
   const int kvh = (item / (a.RB * a.S)) % a.Hkv;
   const int b = item / (a.RB * a.S * a.Hkv);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
 
   const int L_raw = a.cache_len[b];
@@ -137,7 +174,7 @@ void attn_main(AttnArgs a) {
   const int n_tree_tiles = s == 0 ? (a.T + kKT - 1) / kKT : 0;
   const int n_tiles = n_tree_tiles + n_prefix_tiles;
 
-  // ---- the lane's query row: r = rb*128 + wave*32 + n -------------------------------------
+  // ---- the lane's query row: r = rb*256 + wave*32 + n -------------------------------------
   const int r = rb * kRows + wave * 32 + n;
   const bool row_ok = r < a.GT;
   const int row_t = row_ok ? r / a.G : 0;  // padding rows load a real row; never written
@@ -166,54 +203,66 @@ void attn_main(AttnArgs a) {
     mk1 = a.W > 1 ? mrow[1] : 0;
   }
 
-  // ---- tile staging ------------------------------------------------------------------------
-  const size_t kv_head_base = (((size_t)b * a.Hkv + kvh) * a.Lmax) * Lay::kRowBytes;
-  const size_t tree_base = (size_t)b * a.T * a.Hkv * Lay::kRowBytes + (size_t)kvh * Lay::kRowBytes;
-  const size_t tree_stride = (size_t)a.Hkv * Lay::kRowBytes;
-  u32x4 rk[Lay::kLoads], rv[Lay::kLoads];
+  // ---- direct-to-LDS tile loads ------------------------------------------------------------
+  // Wavefront w fills K rows [w*kDPW*kRowsPerDma, ...) of a tile, and the same V rows; lane l
+  // writes chunk slot l % kCPR of row l / kCPR, which holds logical chunk slot ^ swz(row).
+  const char* kc_head = a.kc + (((size_t)b * a.Hkv + kvh) * a.Lmax) * kRB;
+  const char* vc_head = a.vc + (((size_t)b * a.Hkv + kvh) * a.Lmax) * kRB;
+  const char* kt_head = a.kt + ((size_t)b * a.T * a.Hkv + kvh) * kRB;
+  const char* vt_head = a.vt + ((size_t)b * a.T * a.Hkv + kvh) * kRB;
+  const uint32_t tree_stride = (uint32_t)a.Hkv * kRB;
+  int dma_row[kDPW];
+  uint32_t dma_chunk[kDPW];
+#pragma unroll
+  for (int i = 0; i < kDPW; ++i) {
+    dma_row[i] = (wave * kDPW + i) * Lay::kRowsPerDma + lane / Lay::kCPR;
+    dma_chunk[i] = (uint32_t)(((lane % Lay::kCPR) ^ Lay::swz(dma_row[i])) << 4);
+  }
+  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
 
-  auto tile_keys = [&](int tile, int& base, int& end, bool& is_tree) {
-    is_tree = tile < n_tree_tiles;
-    if (is_tree) {
-      base = tile * kKT;
-      end = a.T;
+  auto issue_tile = [&](int tile) {
+    const int stage = tile % kNS;
+    const uint32_t kl = smem_base + stage * Lay::kStage + wave * kDPW * 1024;
+    const uint32_t vl = kl + Lay::kTile;
+    if (tile < n_tree_tiles) {
+      const int base = tile * kKT;
+#pragma unroll
+      for (int i = 0; i < kDPW; ++i) {
+        // keys past the tree load the last node's row: masked to -inf, they add exactly 0
+        const uint32_t off = (uint32_t)min(base + dma_row[i], a.T - 1) * tree_stride + dma_chunk[i];
+        lds_dma16(kl + i * 1024, kt_head, off);
+        lds_dma16(vl + i * 1024, vt_head, off);
+      }
     } else {
-      base = k0 + (tile - n_tree_tiles) * kKT;
-      end = k1;
-    }
-  };
-  // Keys past the end of the tile's range load the last valid row instead: their scores are
-  // masked to -inf, so P = 0 and a finite row contributes exactly nothing, and no cache row at
-  // or past cache_len is ever read.
-  auto load_tile = [&](int tile) {
-    int base, end;
-    bool is_tree;
-    tile_keys(tile, base, end, is_tree);
-    const char* kb = is_tree ? a.kt : a.kc;
-    const char* vb = is_tree ? a.vt : a.vc;
-    const size_t rbase = is_tree ? tree_base : kv_head_base;
-    const size_t rstride = is_tree ? tree_stride : (size_t)Lay::kRowBytes;
+      const int base = k0 + (tile - n_tree_tiles) * kKT;
 #pragma unroll
-    for (int p = 0; p < Lay::kLoads; ++p) {
-      const int qd = tid + 256 * p;
-      const int row = qd / Lay::kCPR, ch = qd % Lay::kCPR;
-      const int key = min(base + row, end - 1);
-      const size_t off = rbase + (size_t)key * rstride;
-      rk[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + off) + ch);
-      rv[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + off) + ch);
+      for (int i = 0; i < kDPW; ++i) {
+        // keys past the chunk load its last row (never a row at or past cache_len)
+        const uint32_t off = (uint32_t)min(base + dma_row[i], k1 - 1) * kRB + dma_chunk[i];
+        lds_dma16(kl + i * 1024, kc_head, off);
+        lds_dma16(vl + i * 1024, vc_head, off);
+      }
     }
   };
-  auto store_tile = [&](int buf) {
-    char* kl = smem + buf * Lay::kStage;
-    char* vl = kl + Lay::kTileK;
+
+  // ---- per-lane LDS fragment offsets (bytes within a K or V tile) --------------------------
+  uint32_t koff[kBF16 ? kKS : 1];
+  uint32_t voff[kBF16 ? 2 * kDB : 1];
+  if constexpr (kBF16) {
 #pragma unroll
-    for (int p = 0; p < Lay::kLoads; ++p) {
-      const int qd = tid + 256 * p;
-      const int row = qd / Lay::kCPR, ch = qd % Lay::kCPR;
-      *reinterpret_cast<u32x4*>(kl + row * Lay::kPitchK + ch * 16) = rk[p];
-      *reinterpret_cast<u32x4*>(vl + row * Lay::kPitchV + ch * 16) = rv[p];
-    }
-  };
+    for (int ks = 0; ks < kKS; ++ks)
+      koff[ks] = n * kRB + ((((2 * ks + h) ^ Lay::swz(n))) << 4);
+    const int tr_key = 4 * h + ((lane & 15) >> 2);             // key within an 8-key half
+    const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // d within a 32-wide block
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec)
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) {
+        const int row = 8 * sec + tr_key;
+        voff[sec * kDB + db] =
+            row * kRB + (((4 * db + (tr_d >> 3)) ^ Lay::swz(row)) << 4) + (tr_d & 7) * 2;
+      }
+  }
 
   // ---- accumulators ------------------------------------------------------------------------
   f32x16 oacc[kDB];
@@ -222,26 +271,42 @@ void attn_main(AttnArgs a) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  // per-lane LDS fragment bases (bytes)
-  const int k_frag = n * Lay::kPitchK + h * (kBF16 ? 16 : 4);
-  const int v_frag = kBF16 ? (4 * h + ((lane & 15) >> 2)) * Lay::kPitchV +
-                                 (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2
-                           : (4 * h) * Lay::kPitchV + n * 4;
+  // Q and mask loads complete before the tile loads start, so later waits count tiles only.
+  vm_wait<0>();
+#pragma unroll
+  for (int t = 0; t < Lay::kAhead; ++t)
+    if (t < n_tiles) issue_tile(t);
 
   for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < n_tiles) load_tile(tile + 1);
-    const char* kl = smem + buf * Lay::kStage;
-    const char* vl = kl + Lay::kTileK;
+    // wait for this wavefront's loads of `tile`; newer tiles may stay in flight
+    const int newer = min(Lay::kAhead - 1, n_tiles - 1 - tile);
+    if constexpr (Lay::kAhead >= 3) {
+      if (newer >= 2) vm_wait<4 * kDPW>();
+      else if (newer == 1) vm_wait<2 * kDPW>();
+      else vm_wait<0>();
+    } else if constexpr (Lay::kAhead == 2) {
+      if (newer >= 1) vm_wait<2 * kDPW>();
+      else vm_wait<0>();
+    } else {
+      vm_wait<0>();
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): earlier LDS reads are done
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // tile is in LDS for every wavefront; oldest stage is free
+    asm volatile("" ::: "memory");
+    if (tile + Lay::kAhead < n_tiles) issue_tile(tile + Lay::kAhead);
+
+    const char* kl = smem + (tile % kNS) * Lay::kStage;
+    const char* vl = kl + Lay::kTile;
     int base, end;
-    bool is_tree;
-    tile_keys(tile, base, end, is_tree);
+    bool is_tree = tile < n_tree_tiles;
+    if (is_tree) {
+      base = tile * kKT;
+      end = a.T;
+    } else {
+      base = k0 + (tile - n_tree_tiles) * kKT;
+      end = k1;
+    }
     const bool need_mask = is_tree || base + kKT > end;
     // a tree tile covers nodes 64*tile .. 64*tile+63: one mask word per row
     const uint64_t mword = !is_tree ? ~0ull : (tile == 0 ? mk0 : mk1);
@@ -253,12 +318,14 @@ void attn_main(AttnArgs a) {
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) {
         if constexpr (kBF16) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-              kl + k_frag + kb * 32 * Lay::kPitchK + ks * 32);
+          const bf16x8 kf =
+              *reinterpret_cast<const bf16x8*>(kl + koff[ks] + kb * 32 * kRB);
           sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
         } else {
+          const int key = kb * 32 + n;
+          const int d = 2 * ks + h;
           const float kf = *reinterpret_cast<const float*>(
-              kl + k_frag + kb * 32 * Lay::kPitchK + ks * 8);
+              kl + key * kRB + ((((d >> 2) ^ Lay::swz(key))) << 4) + (d & 3) * 4);
           sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf, qf[ks], sacc, 0, 0, 0);
         }
       }
@@ -309,12 +376,13 @@ void attn_main(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * st + 2 * e], p[8 * st + 2 * e + 1]);
           const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
+          const int rows = (kb * 32 + 16 * st) * kRB;
 #pragma unroll
           for (int db = 0; db < kDB; ++db) {
-            const int o0 = v_frag + (kb * 32 + 16 * st) * Lay::kPitchV + db * 64;
-            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vl + o0));
+            const i16x4 v0 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vl + rows + voff[db]));
             const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(vl + o0 + 8 * Lay::kPitchV));
+                (lds_i16x4*)(vl + rows + voff[kDB + db]));
             const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pf,
                                                               oacc[db], 0, 0, 0);
@@ -323,19 +391,17 @@ void attn_main(AttnArgs a) {
       } else {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = kb * 32 + 8 * (e >> 2) + (e & 3);  // + 4h folded into v_frag
+          const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
 #pragma unroll
           for (int db = 0; db < kDB; ++db) {
-            const float vf =
-                *reinterpret_cast<const float*>(vl + v_frag + key * Lay::kPitchV + db * 128);
+            const int d = db * 32 + n;
+            const float vf = *reinterpret_cast<const float*>(
+                vl + key * kRB + ((((d >> 2) ^ Lay::swz(key))) << 4) + (d & 3) * 4);
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf, p[e], oacc[db], 0, 0, 0);
           }
         }
       }
     }
-
-    if (tile + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue ----------------------------------------------------------------------------
@@ -385,7 +451,7 @@ void attn_main(AttnArgs a) {
 
 // Merge the per-chunk partials of sequences with more than one non-empty chunk:
 //   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  lse = (M + log2 den) ln 2.
-// One wavefront per 32 rows of a row block.
+// One wavefront per 32 rows of a row block; the loads of four chunks are in flight together.
 template <typename E, int D>
 __global__ __launch_bounds__(64) void attn_combine(AttnArgs a) {
   constexpr int kDB = D / 32;
@@ -414,20 +480,25 @@ __global__ __launch_bounds__(64) void attn_combine(AttnArgs a) {
   for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[db][j] = float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int s = 0; s < n_split; ++s) {
     const float2 ml = pml[(slot0 + s) * kRows + rloc];
+    const float4* ps = po + (slot0 + s) * (size_t)kRows * D / 4;
+    float4 v[kDB][4];
+#pragma unroll
+    for (int db = 0; db < kDB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[db][j] = ps[(((wave * kDB + db) * 4 + j) << 6) + lane];
     const float w = fast_exp2(ml.x - M);
     den += w * ml.y;
-    const float4* ps = po + (slot0 + s) * (size_t)kRows * D / 4;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4 v = ps[(((wave * kDB + db) * 4 + j) << 6) + lane];
-        acc[db][j].x += w * v.x;
-        acc[db][j].y += w * v.y;
-        acc[db][j].z += w * v.z;
-        acc[db][j].w += w * v.w;
+        acc[db][j].x += w * v[db][j].x;
+        acc[db][j].y += w * v[db][j].y;
+        acc[db][j].z += w * v[db][j].z;
+        acc[db][j].w += w * v[db][j].w;
       }
   }
   const float inv = 1.f / den;
@@ -466,10 +537,9 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int split_keys) {
   if (split_keys > 0) {
     chunk = ceil_div(split_keys, kKT) * kKT;
   } else {
-    // Two workgroups fit on a compute unit: aim for two rounds of those, with chunks of at
-    // least 256 keys.
+    // One workgroup per compute unit: aim for two rounds, with chunks of at least 256 keys.
     const long long units = (long long)B * Hkv * p.RB;
-    const long long want = 4LL * device_cu_count();
+    const long long want = 2LL * device_cu_count();
     int S = (int)std::min<long long>(std::max<long long>(1, ceil_div_ll(want, units)),
                                      std::max(1, ceil_div(Lc, 256)));
     chunk = ceil_div(ceil_div(Lc, S), kKT) * kKT;
@@ -488,9 +558,9 @@ int launch(const AttnArgs& a, hipStream_t stream) {
   const int n_items = a.B * a.Hkv * a.S * a.RB;
   if (g_prof_before && hipEventRecord(g_prof_before, stream) != hipSuccess) return TV_ERR_HIP;
   if (a.S > 1)
-    hipLaunchKernelGGL((attn_main<E, D, true>), dim3(n_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_main<E, D, true>), dim3(n_items), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((attn_main<E, D, false>), dim3(n_items), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_main<E, D, false>), dim3(n_items), dim3(kThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (g_prof_after && hipEventRecord(g_prof_after, stream) != hipSuccess) return TV_ERR_HIP;
   if (a.S > 1)
