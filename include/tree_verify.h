@@ -99,8 +99,9 @@ size_t tree_verify_attn_workspace_size(int B, int T, int Hq, int Hkv, int D, int
  *   lse        [B,T,Hq]        fp32    out, optional (NULL): natural-log sum of exp of scores
  *   status     [B]             int32   optional (NULL): TV_BAD_LEN is OR-ed in
  *   scale      <= 0 selects 1/sqrt(D)
- *   split_keys prefix keys per split-K chunk (rounded up to a multiple of 64); 0 = automatic.
- *              Results agree across split settings to rounding.
+ *   split_keys keys per split-K chunk, rounded up to a multiple of 64; a sequence's keys are
+ *              counted as its tree tiles (ceil(T/64) tiles of 64) followed by its prefix.
+ *              0 = automatic.  Results agree across split settings to rounding.
  *   workspace  device buffer of at least tree_verify_attn_workspace_size(...) bytes (may be
  *              NULL when that size is 0); holds per-split partial results, no state across
  *              calls.

@@ -9,10 +9,11 @@
 //     through a ring of LDS stages, three tiles ahead of the one being computed; no registers
 //     hold staged data.  Each wavefront waits only for its own loads of the tile it needs, then
 //     one barrier per tile publishes the tile and frees the oldest stage.
-//   * The prefix is cut into equal chunks of `chunk` keys (split-K).  Chunk s of sequence b is
-//     processed by its own workgroup; chunk 0 also processes the T tree keys, which are masked
-//     per row by the ancestor bitmask.  Partial results (unnormalised O, running max m, sum l)
-//     are merged by attn_combine; a sequence with a single non-empty chunk is written directly.
+//   * A sequence's keys form 64-key tiles: its tree tiles (masked per row by the ancestor
+//     bitmask), then its prefix tiles.  They are cut into equal chunks of `chunk_tiles` tiles
+//     (split-K), each processed by its own workgroup.  Partial results (unnormalised O, running
+//     max m, sum l) are merged by attn_combine; a sequence with a single chunk is written
+//     directly.
 //   * Per 64-key tile, in two 32-key blocks: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS
 //     as the A operand, Q held in registers as the B operand), masking, online softmax in the
 //     log2 domain, then O^T += V^T P^T (V^T fragments from LDS with the gfx950 transpose read,
@@ -63,7 +64,7 @@ struct AttnArgs {
   int32_t* status;
   float* part_o;   // [slot][kRows*D] in register order
   float* part_ml;  // [slot][kRows][2]
-  int B, T, Hq, Hkv, G, Lmax, W, GT, RB, S, chunk;
+  int B, T, Hq, Hkv, G, Lmax, W, GT, RB, S, chunk_tiles;
   float c;         // scale * log2(e)
 };
 
@@ -165,13 +166,19 @@ void attn_main(AttnArgs a) {
   const int L = min(max(L_raw, 0), a.Lmax);
   if (a.status && (L_raw < 0 || L_raw > a.Lmax) && kvh == 0 && s == 0 && rb == 0 && tid == 0)
     atomicOr(a.status + b, TV_BAD_LEN);
-  const int n_split = max(1, ceil_div(L, a.chunk));
+  // Chunks are cut from the sequence's tiles in the order tree tiles, then prefix tiles, so
+  // the chunk that carries the tree does no more work than the others.
+  const int tree_tiles = ceil_div(a.T, kKT);
+  const int all_tiles = tree_tiles + ceil_div(L, kKT);
+  const int n_split = ceil_div(all_tiles, a.chunk_tiles);
   if (s >= n_split) return;  // empty chunk: nothing to merge
   const bool direct = !kSplit || n_split == 1;
 
-  const int k0 = s * a.chunk, k1 = min(k0 + a.chunk, L);
-  const int n_prefix_tiles = k1 > k0 ? (k1 - k0 + kKT - 1) / kKT : 0;
-  const int n_tree_tiles = s == 0 ? (a.T + kKT - 1) / kKT : 0;
+  const int v0 = s * a.chunk_tiles, v1 = min(v0 + a.chunk_tiles, all_tiles);
+  const int n_tree_tiles = max(0, min(v1, tree_tiles) - v0);
+  const int k0 = max(v0 - tree_tiles, 0) * kKT;
+  const int k1 = min(max(v1 - tree_tiles, 0) * kKT, L);
+  const int n_prefix_tiles = k1 > k0 ? ceil_div(k1 - k0, kKT) : 0;
   const int n_tiles = n_tree_tiles + n_prefix_tiles;
 
   // ---- the lane's query row: r = rb*256 + wave*32 + n -------------------------------------
@@ -179,6 +186,55 @@ void attn_main(AttnArgs a) {
   const bool row_ok = r < a.GT;
   const int row_t = row_ok ? r / a.G : 0;  // padding rows load a real row; never written
   const int row_head = kvh * a.G + (row_ok ? r % a.G : 0);
+
+  // ---- direct-to-LDS tile loads ------------------------------------------------------------
+  // Wavefront w fills K rows [w*kDPW*kRowsPerDma, ...) of a tile, and the same V rows; lane l
+  // writes chunk slot l % kCPR of row l / kCPR, which holds logical chunk slot ^ swz(row).
+  const char* kc_head = a.kc + (((size_t)b * a.Hkv + kvh) * a.Lmax) * kRB;
+  const char* vc_head = a.vc + (((size_t)b * a.Hkv + kvh) * a.Lmax) * kRB;
+  const char* kt_head = a.kt + ((size_t)b * a.T * a.Hkv + kvh) * kRB;
+  const char* vt_head = a.vt + ((size_t)b * a.T * a.Hkv + kvh) * kRB;
+  const uint32_t tree_stride = (uint32_t)a.Hkv * kRB;
+  int dma_row[kDPW];
+  uint32_t dma_chunk[kDPW];
+#pragma unroll
+  for (int i = 0; i < kDPW; ++i) {
+    dma_row[i] = (wave * kDPW + i) * Lay::kRowsPerDma + lane / Lay::kCPR;
+    dma_chunk[i] = (uint32_t)(((lane % Lay::kCPR) ^ Lay::swz(dma_row[i])) << 4);
+  }
+  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
+
+  auto issue_tile = [&](int tile) {
+    const int stage = tile % kNS;
+    const uint32_t kl = smem_base + stage * Lay::kStage + wave * kDPW * 1024;
+    const uint32_t vl = kl + Lay::kTile;
+    if (tile < n_tree_tiles) {
+      const int base = (v0 + tile) * kKT;
+#pragma unroll
+      for (int i = 0; i < kDPW; ++i) {
+        // keys past the tree load the last node's row: masked to -inf, they add exactly 0
+        const uint32_t off = (uint32_t)min(base + dma_row[i], a.T - 1) * tree_stride + dma_chunk[i];
+        lds_dma16(kl + i * 1024, kt_head, off);
+        lds_dma16(vl + i * 1024, vt_head, off);
+      }
+    } else {
+      const int base = k0 + (tile - n_tree_tiles) * kKT;
+#pragma unroll
+      for (int i = 0; i < kDPW; ++i) {
+        // keys past the chunk load its last row (never a row at or past cache_len)
+        const uint32_t off = (uint32_t)min(base + dma_row[i], k1 - 1) * kRB + dma_chunk[i];
+        lds_dma16(kl + i * 1024, kc_head, off);
+        lds_dma16(vl + i * 1024, vc_head, off);
+      }
+    }
+  };
+
+  // The first tiles' loads go out before the Q loads so the two latencies overlap; both are
+  // complete before the tile loop (vm_wait<0> below), so no compiler-tracked load is pending
+  // inside the loop and the loop's own waits count tile loads only.
+#pragma unroll
+  for (int t = 0; t < Lay::kAhead; ++t)
+    if (t < n_tiles) issue_tile(t);
 
   // ---- Q fragments (B operand): row n, d = 16*ks + 8*h .. +7 (bf16) or 2*ks + h (fp32) -----
   using QFrag = typename std::conditional<kBF16, bf16x8, float>::type;
@@ -203,48 +259,6 @@ void attn_main(AttnArgs a) {
     mk1 = a.W > 1 ? mrow[1] : 0;
   }
 
-  // ---- direct-to-LDS tile loads ------------------------------------------------------------
-  // Wavefront w fills K rows [w*kDPW*kRowsPerDma, ...) of a tile, and the same V rows; lane l
-  // writes chunk slot l % kCPR of row l / kCPR, which holds logical chunk slot ^ swz(row).
-  const char* kc_head = a.kc + (((size_t)b * a.Hkv + kvh) * a.Lmax) * kRB;
-  const char* vc_head = a.vc + (((size_t)b * a.Hkv + kvh) * a.Lmax) * kRB;
-  const char* kt_head = a.kt + ((size_t)b * a.T * a.Hkv + kvh) * kRB;
-  const char* vt_head = a.vt + ((size_t)b * a.T * a.Hkv + kvh) * kRB;
-  const uint32_t tree_stride = (uint32_t)a.Hkv * kRB;
-  int dma_row[kDPW];
-  uint32_t dma_chunk[kDPW];
-#pragma unroll
-  for (int i = 0; i < kDPW; ++i) {
-    dma_row[i] = (wave * kDPW + i) * Lay::kRowsPerDma + lane / Lay::kCPR;
-    dma_chunk[i] = (uint32_t)(((lane % Lay::kCPR) ^ Lay::swz(dma_row[i])) << 4);
-  }
-  const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
-
-  auto issue_tile = [&](int tile) {
-    const int stage = tile % kNS;
-    const uint32_t kl = smem_base + stage * Lay::kStage + wave * kDPW * 1024;
-    const uint32_t vl = kl + Lay::kTile;
-    if (tile < n_tree_tiles) {
-      const int base = tile * kKT;
-#pragma unroll
-      for (int i = 0; i < kDPW; ++i) {
-        // keys past the tree load the last node's row: masked to -inf, they add exactly 0
-        const uint32_t off = (uint32_t)min(base + dma_row[i], a.T - 1) * tree_stride + dma_chunk[i];
-        lds_dma16(kl + i * 1024, kt_head, off);
-        lds_dma16(vl + i * 1024, vt_head, off);
-      }
-    } else {
-      const int base = k0 + (tile - n_tree_tiles) * kKT;
-#pragma unroll
-      for (int i = 0; i < kDPW; ++i) {
-        // keys past the chunk load its last row (never a row at or past cache_len)
-        const uint32_t off = (uint32_t)min(base + dma_row[i], k1 - 1) * kRB + dma_chunk[i];
-        lds_dma16(kl + i * 1024, kc_head, off);
-        lds_dma16(vl + i * 1024, vc_head, off);
-      }
-    }
-  };
-
   // ---- per-lane LDS fragment offsets (bytes within a K or V tile) --------------------------
   uint32_t koff[kBF16 ? kKS : 1];
   uint32_t voff[kBF16 ? 2 * kDB : 1];
@@ -264,6 +278,8 @@ void attn_main(AttnArgs a) {
       }
   }
 
+  vm_wait<0>();
+
   // ---- accumulators ------------------------------------------------------------------------
   f32x16 oacc[kDB];
 #pragma unroll
@@ -271,11 +287,6 @@ void attn_main(AttnArgs a) {
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  // Q and mask loads complete before the tile loads start, so later waits count tiles only.
-  vm_wait<0>();
-#pragma unroll
-  for (int t = 0; t < Lay::kAhead; ++t)
-    if (t < n_tiles) issue_tile(t);
 
   for (int tile = 0; tile < n_tiles; ++tile) {
     // wait for this wavefront's loads of `tile`; newer tiles may stay in flight
@@ -301,7 +312,7 @@ void attn_main(AttnArgs a) {
     int base, end;
     bool is_tree = tile < n_tree_tiles;
     if (is_tree) {
-      base = tile * kKT;
+      base = (v0 + tile) * kKT;
       end = a.T;
     } else {
       base = k0 + (tile - n_tree_tiles) * kKT;
@@ -309,7 +320,7 @@ void attn_main(AttnArgs a) {
     }
     const bool need_mask = is_tree || base + kKT > end;
     // a tree tile covers nodes 64*tile .. 64*tile+63: one mask word per row
-    const uint64_t mword = !is_tree ? ~0ull : (tile == 0 ? mk0 : mk1);
+    const uint64_t mword = !is_tree ? ~0ull : (base == 0 ? mk0 : mk1);
 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -431,7 +442,7 @@ void attn_main(AttnArgs a) {
         }
       if (a.lse && h == 0) a.lse[orow] = (m_run + __log2f(l_run)) * kLn2;
     }
-  } else {
+  } else if (row_ok) {  // padding rows are never merged
     const size_t slot = (((size_t)b * a.Hkv + kvh) * a.RB + rb) * a.S + s;
     float4* po = reinterpret_cast<float4*>(a.part_o + slot * (size_t)kRows * D);
 #pragma unroll
@@ -451,17 +462,18 @@ void attn_main(AttnArgs a) {
 
 // Merge the per-chunk partials of sequences with more than one non-empty chunk:
 //   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  lse = (M + log2 den) ln 2.
-// One wavefront per 32 rows of a row block; the loads of four chunks are in flight together.
+// One wavefront per (32 rows, 32-wide d block); the loads of four chunks are in flight together.
 template <typename E, int D>
 __global__ __launch_bounds__(64) void attn_combine(AttnArgs a) {
   constexpr int kDB = D / 32;
-  const int wave = blockIdx.x % kWaves;
-  const int item = blockIdx.x / kWaves;  // (b, kvh, rb)
+  const int db = blockIdx.x % kDB;
+  const int wave = (blockIdx.x / kDB) % kWaves;
+  const int item = blockIdx.x / (kDB * kWaves);  // (b, kvh, rb)
   const int rb = item % a.RB;
   const int kvh = (item / a.RB) % a.Hkv;
   const int b = item / (a.RB * a.Hkv);
   const int L = min(max(a.cache_len[b], 0), a.Lmax);
-  const int n_split = max(1, ceil_div(L, a.chunk));
+  const int n_split = ceil_div(ceil_div(a.T, kKT) + ceil_div(L, kKT), a.chunk_tiles);
   if (n_split == 1) return;  // written directly by attn_main
   const int lane = threadIdx.x;
   const int n = lane & 31, h = lane >> 5;
@@ -475,56 +487,48 @@ __global__ __launch_bounds__(64) void attn_combine(AttnArgs a) {
   float M = -INFINITY;
   for (int s = 0; s < n_split; ++s) M = fmaxf(M, pml[(slot0 + s) * kRows + rloc].x);
   float den = 0.f;
-  float4 acc[kDB][4];
+  float4 acc[4];
 #pragma unroll
-  for (int db = 0; db < kDB; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[db][j] = float4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; ++j) acc[j] = float4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
   for (int s = 0; s < n_split; ++s) {
     const float2 ml = pml[(slot0 + s) * kRows + rloc];
     const float4* ps = po + (slot0 + s) * (size_t)kRows * D / 4;
-    float4 v[kDB][4];
+    float4 v[4];
 #pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[db][j] = ps[(((wave * kDB + db) * 4 + j) << 6) + lane];
+    for (int j = 0; j < 4; ++j) v[j] = ps[(((wave * kDB + db) * 4 + j) << 6) + lane];
     const float w = fast_exp2(ml.x - M);
     den += w * ml.y;
 #pragma unroll
-    for (int db = 0; db < kDB; ++db)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[db][j].x += w * v[db][j].x;
-        acc[db][j].y += w * v[db][j].y;
-        acc[db][j].z += w * v[db][j].z;
-        acc[db][j].w += w * v[db][j].w;
-      }
+    for (int j = 0; j < 4; ++j) {
+      acc[j].x += w * v[j].x;
+      acc[j].y += w * v[j].y;
+      acc[j].z += w * v[j].z;
+      acc[j].w += w * v[j].w;
+    }
   }
   const float inv = 1.f / den;
   const int t = r / a.G, head = kvh * a.G + r % a.G;
   const size_t orow = ((size_t)b * a.T + t) * a.Hq + head;
   E* o = reinterpret_cast<E*>(a.out) + orow * D;
 #pragma unroll
-  for (int db = 0; db < kDB; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = db * 32 + 8 * j + 4 * h;
-      const float4 v = acc[db][j];
-      if constexpr (std::is_same<E, __bf16>::value) {
-        uint2 w;
-        w.x = pack_bf16x2(v.x * inv, v.y * inv);
-        w.y = pack_bf16x2(v.z * inv, v.w * inv);
-        *reinterpret_cast<uint2*>(o + d) = w;
-      } else {
-        *reinterpret_cast<float4*>(o + d) = float4{v.x * inv, v.y * inv, v.z * inv, v.w * inv};
-      }
+  for (int j = 0; j < 4; ++j) {
+    const int d = db * 32 + 8 * j + 4 * h;
+    const float4 v = acc[j];
+    if constexpr (std::is_same<E, __bf16>::value) {
+      uint2 w;
+      w.x = pack_bf16x2(v.x * inv, v.y * inv);
+      w.y = pack_bf16x2(v.z * inv, v.w * inv);
+      *reinterpret_cast<uint2*>(o + d) = w;
+    } else {
+      *reinterpret_cast<float4*>(o + d) = float4{v.x * inv, v.y * inv, v.z * inv, v.w * inv};
     }
-  if (a.lse && h == 0) a.lse[orow] = (M + __log2f(den)) * kLn2;
+  }
+  if (a.lse && h == 0 && db == 0) a.lse[orow] = (M + __log2f(den)) * kLn2;
 }
 
 struct Plan {
-  int RB, S, chunk;
+  int RB, S, chunk_tiles;
   size_t ws_bytes;
 };
 
@@ -532,20 +536,21 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int split_keys) {
   Plan p;
   const int G = Hq / Hkv;
   p.RB = ceil_div(G * T, kRows);
-  const int Lc = Lmax > 0 ? Lmax : 1;
-  int chunk;
+  // tiles of the longest sequence: its tree tiles, then its prefix tiles
+  const int tiles = ceil_div(T, kKT) + ceil_div(Lmax, kKT);
+  int chunk_tiles;
   if (split_keys > 0) {
-    chunk = ceil_div(split_keys, kKT) * kKT;
+    chunk_tiles = ceil_div(split_keys, kKT);
   } else {
-    // One workgroup per compute unit: aim for two rounds, with chunks of at least 256 keys.
+    // One workgroup per compute unit: aim for two rounds, with chunks of at least 4 tiles.
     const long long units = (long long)B * Hkv * p.RB;
     const long long want = 2LL * device_cu_count();
-    int S = (int)std::min<long long>(std::max<long long>(1, ceil_div_ll(want, units)),
-                                     std::max(1, ceil_div(Lc, 256)));
-    chunk = ceil_div(ceil_div(Lc, S), kKT) * kKT;
+    const int S = (int)std::min<long long>(std::max<long long>(1, ceil_div_ll(want, units)),
+                                           std::max(1, ceil_div(tiles, 4)));
+    chunk_tiles = ceil_div(tiles, S);
   }
-  p.chunk = chunk;
-  p.S = std::max(1, ceil_div(Lc, chunk));
+  p.chunk_tiles = chunk_tiles;
+  p.S = ceil_div(tiles, chunk_tiles);
   p.ws_bytes = p.S > 1 ? (size_t)B * Hkv * p.RB * p.S * kRows * (D + 2) * sizeof(float) : 0;
   return p;
 }
@@ -564,8 +569,8 @@ int launch(const AttnArgs& a, hipStream_t stream) {
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (g_prof_after && hipEventRecord(g_prof_after, stream) != hipSuccess) return TV_ERR_HIP;
   if (a.S > 1)
-    hipLaunchKernelGGL((attn_combine<E, D>), dim3(a.B * a.Hkv * a.RB * kWaves), dim3(64), 0,
-                       stream, a);
+    hipLaunchKernelGGL((attn_combine<E, D>), dim3(a.B * a.Hkv * a.RB * kWaves * (D / 32)),
+                       dim3(64), 0, stream, a);
   return launch_status();
 }
 
@@ -644,7 +649,7 @@ extern "C" int tree_verify_attn(const void* q, const void* k_cache, const void* 
   a.GT = a.G * T;
   a.RB = p.RB;
   a.S = p.S;
-  a.chunk = p.chunk;
+  a.chunk_tiles = p.chunk_tiles;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
   a.c = sc * kLog2e;
   float* ws = (float*)workspace;
