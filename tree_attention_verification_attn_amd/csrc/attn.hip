@@ -6,26 +6,31 @@
 //     SIMD, so one wavefront's softmax overlaps the other's matrix instructions.  Every prefix
 //     key is visible to every row, so a K/V tile staged in LDS serves all 256 rows.
 //   * K/V tiles of 64 keys move HBM -> LDS by direct-to-LDS loads (global_load_lds_dwordx4)
-//     through a ring of LDS stages, three tiles ahead of the one being computed; no registers
-//     hold staged data.  Each wavefront waits only for its own loads of the tile it needs, then
-//     one barrier per tile publishes the tile and frees the oldest stage.
+//     through a ring of four LDS stages; no registers hold staged data.  Each wavefront waits
+//     only for its own loads of the tile it needs, then one barrier per tile publishes the tile
+//     and frees a stage for the next load.
 //   * A sequence's keys form 64-key tiles: its tree tiles (masked per row by the ancestor
 //     bitmask), then its prefix tiles.  They are cut into equal chunks of `chunk_tiles` tiles
 //     (split-K), each processed by its own workgroup.  Partial results (unnormalised O, running
 //     max m, sum l) are merged by attn_combine; a sequence with a single chunk is written
 //     directly.
-//   * Per 64-key tile, in two 32-key blocks: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from LDS
-//     as the A operand, Q held in registers as the B operand), masking, online softmax in the
-//     log2 domain, then O^T += V^T P^T (V^T fragments from LDS with the gfx950 transpose read,
-//     P taken straight from the S^T accumulators).  In this transposed form a lane holds one
-//     query row in both the score and the output accumulators, so the softmax statistics never
-//     leave the lane pair (l, l^32).
+//   * A tile is two 32-key blocks.  Per block: S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (K from
+//     LDS as the A operand, Q held in registers as the B operand), masking, online softmax in
+//     the log2 domain, then O^T += V^T P^T (V^T fragments from LDS with the gfx950 transpose
+//     read, P taken straight from the S^T accumulators).  In this transposed form a lane holds
+//     one query row in both the score and the output accumulators, so the softmax statistics
+//     never leave the lane pair (l, l^32).
+//   * The blocks run as a two-deep software pipeline: while the softmax of block j runs on the
+//     vector ALU, the matrix core computes S of block j+1 and O of block j-1, within one
+//     wavefront and across the two wavefronts of each SIMD.  The pipeline runs across tile
+//     barriers, so the tile of block j-1 is still read after the barrier of the next tile.
 //   * LDS rows are unpadded; 16-byte chunks are XOR-swizzled by row so the K reads (16 keys x
 //     one chunk), the transposed V reads (4 keys x 4 chunks per 16 lanes) and the 1 KB
 //     direct-load writes are all free of bank conflicts.
-//   * Online softmax with lazy rescaling: the running max is raised only when a row's max grows
-//     by more than 2^8, so P <= 256 and O is rescaled rarely.
-//   * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same structure.
+//   * Online softmax with lazy rescaling: p = 2^(S c - m) against the running max m, accepted
+//     as long as no lane's block sum exceeds 1024; only then is the block max taken, m raised
+//     and O rescaled.
+//   * fp32 inputs use v_mfma_f32_32x32x2_f32 and run the blocks one after the other.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -49,7 +54,7 @@ constexpr int kRows = 32 * kWaves;  // query rows per workgroup
 constexpr int kKT = 64;             // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleSlack = 8.0f;  // log2 units a row's max may outgrow the running max
+constexpr float kSumLimit = 1024.f;  // a lane's block sum above this forces a rescale
 
 struct AttnArgs {
   const char* q;
@@ -77,7 +82,11 @@ struct Layout {
   static constexpr int kTile = kKT * kRowBytes;        // bytes of one K (or V) tile
   static constexpr int kStage = 2 * kTile;             // K tile then V tile
   static constexpr int kStages = kStage <= 32768 ? 4 : 2;
-  static constexpr int kAhead = kStages - 1;           // tiles in flight beyond the current one
+  // bf16 pipelines blocks across tile barriers: four stages hold the tile read for S, the tile
+  // read for O and two in flight.  fp32 (the small exact path) runs its blocks one after the
+  // other, with every stage but the current one in flight.
+  static constexpr bool kCrossTile = kBF16;
+  static constexpr int kAhead = kCrossTile ? kStages - 2 : kStages - 1;
   static constexpr int kRowsPerDma = 1024 / kRowBytes; // rows one wavefront-wide load fills
   static constexpr int kDmaPerWave = kTile / 1024 / kWaves;  // per K (or V) tile
   static constexpr int kDB = D / 32;                   // 32-wide d blocks
@@ -138,6 +147,18 @@ __device__ inline int xcd_remap(int bid, int n) {
   return xcd * per + min(xcd, rem) + slot;
 }
 
+// Score block j = 32 keys: tile j/2, half j%2.  P of a block: bf16 operands or fp32 values.
+template <bool kBF16>
+struct PBlock;
+template <>
+struct PBlock<true> {
+  bf16x8 v[2];  // 16-key steps st = 0, 1
+};
+template <>
+struct PBlock<false> {
+  float v[16];  // element e of the S^T accumulator
+};
+
 template <typename E, int D, bool kSplit>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2)))
@@ -179,7 +200,7 @@ void attn_main(AttnArgs a) {
   const int k0 = max(v0 - tree_tiles, 0) * kKT;
   const int k1 = min(max(v1 - tree_tiles, 0) * kKT, L);
   const int n_prefix_tiles = k1 > k0 ? ceil_div(k1 - k0, kKT) : 0;
-  const int n_tiles = n_tree_tiles + n_prefix_tiles;
+  const int n_tiles = n_tree_tiles + n_prefix_tiles;  // >= 1 for every non-empty chunk
 
   // ---- the lane's query row: r = rb*256 + wave*32 + n -------------------------------------
   const int r = rb * kRows + wave * 32 + n;
@@ -229,9 +250,9 @@ void attn_main(AttnArgs a) {
     }
   };
 
-  // The first tiles' loads go out before the Q loads so the two latencies overlap; both are
-  // complete before the tile loop (vm_wait<0> below), so no compiler-tracked load is pending
-  // inside the loop and the loop's own waits count tile loads only.
+  // The first tiles go out before the Q loads so the two latencies overlap; they are complete
+  // before the block pipeline starts (vm_wait<0> below), so no compiler-tracked load is pending
+  // inside it and its own waits count tile loads only.
 #pragma unroll
   for (int t = 0; t < Lay::kAhead; ++t)
     if (t < n_tiles) issue_tile(t);
@@ -280,137 +301,253 @@ void attn_main(AttnArgs a) {
 
   vm_wait<0>();
 
-  // ---- accumulators ------------------------------------------------------------------------
+  // ---- accumulators and running statistics -------------------------------------------------
   f32x16 oacc[kDB];
 #pragma unroll
   for (int db = 0; db < kDB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY;  // running max of S*c (log2 domain) over the row
+  float l_run = 0.f;        // the lane's part of the row sum of 2^(S*c - m_run)
+  float alpha = 1.f;        // O rescale factor decided by the latest softmax
+  bool rescale_o = false;
 
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    // wait for this wavefront's loads of `tile`; newer tiles may stay in flight
-    const int newer = min(Lay::kAhead - 1, n_tiles - 1 - tile);
-    if constexpr (Lay::kAhead >= 3) {
-      if (newer >= 2) vm_wait<4 * kDPW>();
-      else if (newer == 1) vm_wait<2 * kDPW>();
-      else vm_wait<0>();
-    } else if constexpr (Lay::kAhead == 2) {
-      if (newer >= 1) vm_wait<2 * kDPW>();
-      else vm_wait<0>();
-    } else {
-      vm_wait<0>();
-    }
+  // Barrier of tile t: every wavefront's loads of tile t have landed, and every wavefront is
+  // done with the tile whose stage tile t + kAhead takes (across tiles, tile t-2, whose last
+  // reader is the O^T step of block 2t-3; one block after another, tile t-1), so that tile is
+  // loaded now.
+  auto barrier_tile = [&](int t) {
+    // newer tiles may stay in flight
+    const int newer = min(Lay::kAhead - 1, n_tiles - 1 - t);
+    if (Lay::kAhead >= 3 && newer >= 2) vm_wait<(Lay::kAhead >= 3 ? 4 * kDPW : 0)>();
+    else if (Lay::kAhead >= 2 && newer == 1) vm_wait<(Lay::kAhead >= 2 ? 2 * kDPW : 0)>();
+    else vm_wait<0>();
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): earlier LDS reads are done
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // tile is in LDS for every wavefront; oldest stage is free
+    __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (tile + Lay::kAhead < n_tiles) issue_tile(tile + Lay::kAhead);
+    if (t + Lay::kAhead < n_tiles) issue_tile(t + Lay::kAhead);
+  };
 
-    const char* kl = smem + (tile % kNS) * Lay::kStage;
-    const char* vl = kl + Lay::kTile;
-    int base, end;
-    bool is_tree = tile < n_tree_tiles;
-    if (is_tree) {
-      base = (v0 + tile) * kKT;
-      end = a.T;
+  // LDS offsets of the lane's fragments in the tile whose K (V) is being read.
+  uint32_t kaddr[kBF16 ? kKS : 1], vaddr[kBF16 ? 2 * kDB : 1];
+  auto set_k = [&](int tile) {
+    if constexpr (kBF16) {
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) kaddr[ks] = koff[ks] + (tile % kNS) * Lay::kStage;
     } else {
-      base = k0 + (tile - n_tree_tiles) * kKT;
-      end = k1;
+      kaddr[0] = (tile % kNS) * Lay::kStage;
     }
-    const bool need_mask = is_tree || base + kKT > end;
-    // a tree tile covers nodes 64*tile .. 64*tile+63: one mask word per row
-    const uint64_t mword = !is_tree ? ~0ull : (base == 0 ? mk0 : mk1);
+  };
+  auto set_v = [&](int tile) {
+    if constexpr (kBF16) {
+#pragma unroll
+      for (int i = 0; i < 2 * kDB; ++i)
+        vaddr[i] = voff[i] + (tile % kNS) * Lay::kStage + Lay::kTile;
+    } else {
+      vaddr[0] = (tile % kNS) * Lay::kStage + Lay::kTile;
+    }
+  };
 
+  // S^T = K Q^T for block j (its tile set by set_k)
+  auto qk = [&](int j, f32x16& S) {
+    const int kb = j & 1;
+    S = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // ---- S^T = K Q^T for keys kb*32 .. kb*32+31 ------------------------------------------
-      f32x16 sacc = f32x16{};
+    for (int ks = 0; ks < kKS; ++ks) {
+      if constexpr (kBF16) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(smem + kaddr[ks] + kb * 32 * kRB);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S, 0, 0, 0);
+      } else {
+        const int key = kb * 32 + n;
+        const int d = 2 * ks + h;
+        const float kf = *reinterpret_cast<const float*>(
+            smem + kaddr[0] + key * kRB + ((((d >> 2) ^ Lay::swz(key))) << 4) + (d & 3) * 4);
+        S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf, qf[ks], S, 0, 0, 0);
+      }
+    }
+  };
+
+  // O^T += V^T P^T for block j (its tile set by set_v)
+  auto pv = [&](int j, const PBlock<kBF16>& P) {
+    const int kb = j & 1;
+    if constexpr (kBF16) {
+      // 16-key step st: keys kb*32 + 16st + {4h..4h+3} (elements 0-3) and kb*32 + 16st + 8 +
+      // {4h..4h+3} (elements 4-7); a transpose read gives lane i of each 16-lane group four
+      // consecutive keys at d = D0 + i.
 #pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        if constexpr (kBF16) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(kl + koff[ks] + kb * 32 * kRB);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc, 0, 0, 0);
-        } else {
-          const int key = kb * 32 + n;
-          const int d = 2 * ks + h;
-          const float kf = *reinterpret_cast<const float*>(
-              kl + key * kRB + ((((d >> 2) ^ Lay::swz(key))) << 4) + (d & 3) * 4);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x2f32(kf, qf[ks], sacc, 0, 0, 0);
+      for (int st = 0; st < 2; ++st) {
+        const char* vl = smem + (kb * 32 + 16 * st) * kRB;
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const i16x4 x0 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vl + vaddr[db]));
+          const i16x4 x1 =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vl + vaddr[kDB + db]));
+          const i16x8 v = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v),
+                                                            P.v[st], oacc[db], 0, 0, 0);
         }
       }
-
-      // ---- mask: element e is key base + kb*32 + 8*(e/4) + 4*h + e%4 ------------------------
-      if (need_mask) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int kk = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-          const bool vis = base + kk < end && ((mword >> kk) & 1);
-          sacc[e] = vis ? sacc[e] : -INFINITY;
-        }
-      }
-
-      // ---- online softmax (log2 domain) ----------------------------------------------------
-      float mx = sacc[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, sacc[e]);
-      mx = fmaxf(mx, partner(mx));
-      const float m_new = fmaxf(m_run, mx * a.c);
-      const bool grow = m_new > m_run + kRescaleSlack;
-      if (__ballot(grow)) {
-        float alpha = 1.f;
-        if (grow) {
-          alpha = fast_exp2(m_run - m_new);  // 0 on the first block
-          m_run = m_new;
-        }
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < kDB; ++db) oacc[db] *= alpha;
-      }
-      const float mb = m_run == -INFINITY ? 0.f : m_run;
-      float p[16];
+    } else {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        p[e] = fast_exp2(__builtin_fmaf(sacc[e], a.c, -mb));
-        l_run += p[e];
+        const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+#pragma unroll
+        for (int db = 0; db < kDB; ++db) {
+          const int d = db * 32 + n;
+          const float vf = *reinterpret_cast<const float*>(
+              smem + vaddr[0] + key * kRB + ((((d >> 2) ^ Lay::swz(key))) << 4) + (d & 3) * 4);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf, P.v[e], oacc[db], 0, 0, 0);
+        }
       }
+    }
+  };
 
-      // ---- O^T += V^T P^T ------------------------------------------------------------------
-      if constexpr (kBF16) {
-        // 16-key step st: keys kb*32 + 16st + {4h..4h+3} (elements 0-3) and kb*32 + 16st + 8 +
-        // {4h..4h+3} (elements 4-7); a transpose read gives lane i of each 16-lane group four
-        // consecutive keys at d = D0 + i.
+  // Mask block j's scores where needed: tree keys by the row's ancestor bits, keys at or past
+  // the end of the tree or of the chunk.  Element e is key kb*32 + 8*(e/4) + 4*h + e%4 of the
+  // tile; a tree tile covers nodes 64*tile .. 64*tile+63, so one mask word per row.
+  auto mask_block = [&](int j, f32x16& S) {
+    const int tile = j >> 1, kb = j & 1;
+    const bool is_tree = tile < n_tree_tiles;
+    const int base = is_tree ? (v0 + tile) * kKT : k0 + (tile - n_tree_tiles) * kKT;
+    const int lim = (is_tree ? a.T : k1) - base - kb * 32;  // keys of this block that exist
+    if (!is_tree && lim >= 32) return;
+    const uint32_t lenbits = lim >= 32 ? 0xffffffffu : (lim <= 0 ? 0u : (1u << lim) - 1u);
+    const uint64_t mw = !is_tree ? ~0ull : (base == 0 ? mk0 : mk1);
+    const uint32_t bits = (((uint32_t)(mw >> (32 * kb))) & lenbits) >> (4 * h);
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          uint32_t w[4];
+    for (int e = 0; e < 16; ++e) {
+      const int keep = -(int)((bits >> (8 * (e >> 2) + (e & 3))) & 1u);  // all ones or zero
+      S[e] = __int_as_float((__float_as_int(S[e]) & keep) | (__float_as_int(-INFINITY) & ~keep));
+    }
+  };
+
+  // p = 2^(S*c - m_run), packed as the P operand; returns the lane's sum of the p it packed.
+  auto exp_pack = [&](const f32x16& S, float mb, PBlock<kBF16>& P) -> float {
+    float sum = 0.f;
+    if constexpr (kBF16) {
+      // the row sum adds the fp32 values; only the O^T operand is rounded to bf16
+      float p[16];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * st + 2 * e], p[8 * st + 2 * e + 1]);
-          const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
-          const int rows = (kb * 32 + 16 * st) * kRB;
+      for (int e = 0; e < 16; ++e) p[e] = fast_exp2(__builtin_fmaf(S[e], a.c, -mb));
 #pragma unroll
-          for (int db = 0; db < kDB; ++db) {
-            const i16x4 v0 =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vl + rows + voff[db]));
-            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(vl + rows + voff[kDB + db]));
-            const i16x8 v = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pf,
-                                                              oacc[db], 0, 0, 0);
-          }
-        }
-      } else {
+      for (int st = 0; st < 2; ++st) {
+        uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(p[8 * st + 2 * e], p[8 * st + 2 * e + 1]);
+        P.v[st] = __builtin_bit_cast(bf16x8, w);
+      }
+      sum = p[0];
 #pragma unroll
-          for (int db = 0; db < kDB; ++db) {
-            const int d = db * 32 + n;
-            const float vf = *reinterpret_cast<const float*>(
-                vl + key * kRB + ((((d >> 2) ^ Lay::swz(key))) << 4) + (d & 3) * 4);
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf, p[e], oacc[db], 0, 0, 0);
-          }
-        }
+      for (int e = 1; e < 16; ++e) sum += p[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        P.v[e] = fast_exp2(__builtin_fmaf(S[e], a.c, -mb));
+        sum += P.v[e];
+      }
+    }
+    return sum;
+  };
+
+  // Online softmax of one block with lazy rescaling.  The fast path keeps m_run: a lane whose
+  // block sum is at most kSumLimit has every p in range (p <= sum), and the block is taken as
+  // is.  Otherwise (a score outgrew m_run, or m_run is unset) the wavefront takes the
+  // slow path: exact row max over the block, new m_run, alpha = 2^(m_old - m_new), p again.
+  auto softmax = [&](const f32x16& S, PBlock<kBF16>& P) {
+    float bsum = exp_pack(S, m_run, P);
+    rescale_o = __ballot(!(bsum <= kSumLimit)) != 0;  // also catches inf and NaN
+    if (rescale_o) {
+      float mx = S[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[e]);
+      mx = fmaxf(mx, partner(mx));
+      const float m_new = fmaxf(m_run, mx * a.c);
+      alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);  // 0 while m_run is unset
+      m_run = m_new;
+      bsum = exp_pack(S, m_new == -INFINITY ? 0.f : m_new, P);
+      l_run = __builtin_fmaf(l_run, alpha, bsum);
+    } else {
+      l_run += bsum;
+    }
+  };
+
+  auto rescale = [&]() {
+    if (rescale_o) {
+#pragma unroll
+      for (int db = 0; db < kDB; ++db) oacc[db] *= alpha;
+    }
+  };
+
+  // Keeps the softmax of a region inside it: without a use here the compiler sinks the
+  // exponentials and sums to their next uses, out of reach of the region's matrix work.
+  auto end_region = [&](const PBlock<kBF16>& P) {
+    if constexpr (kBF16) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) asm volatile("" ::"v"(P.v[st]));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) asm volatile("" ::"v"(P.v[e]));
+    }
+    asm volatile("" ::"v"(l_run));
+  };
+
+  // ---- block pipeline ----------------------------------------------------------------------
+  // Region R(j) issues the S^T product of block j+1, the O^T product of block j-1 and the
+  // softmax of block j, in one basic block, so that the matrix work of one block and the vector
+  // work of another interleave in the wavefront's instruction stream.  Between regions: the
+  // mask of block j+1 and the O rescale decided by block j.  Even blocks' S and P live in
+  // Se / Pe, odd blocks' in So / Po.
+  f32x16 Se, So;
+  PBlock<kBF16> Pe, Po;
+  if constexpr (Lay::kCrossTile) {
+    barrier_tile(0);
+    set_k(0);
+    qk(0, Se);
+    mask_block(0, Se);
+    // R(0)
+    qk(1, So);
+    softmax(Se, Pe);
+    end_region(Pe);
+    mask_block(1, So);
+    rescale();
+    for (int t = 1; t < n_tiles; ++t) {
+      barrier_tile(t);
+      // R(2t-1): S of block 2t, O of block 2t-2, softmax of block 2t-1
+      set_k(t);
+      set_v(t - 1);
+      qk(2 * t, Se);
+      pv(2 * t - 2, Pe);
+      softmax(So, Po);
+      end_region(Po);
+      mask_block(2 * t, Se);
+      rescale();
+      // R(2t): S of block 2t+1, O of block 2t-1, softmax of block 2t
+      qk(2 * t + 1, So);
+      pv(2 * t - 1, Po);
+      softmax(Se, Pe);
+      end_region(Pe);
+      mask_block(2 * t + 1, So);
+      rescale();
+    }
+    // R(2n-1): O of block 2n-2, softmax of block 2n-1; then O of block 2n-1
+    set_v(n_tiles - 1);
+    pv(2 * n_tiles - 2, Pe);
+    softmax(So, Po);
+    end_region(Po);
+    rescale();
+    pv(2 * n_tiles - 1, Po);
+  } else {
+    for (int t = 0; t < n_tiles; ++t) {
+      barrier_tile(t);
+      set_k(t);
+      set_v(t);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        qk(2 * t + kb, Se);
+        mask_block(2 * t + kb, Se);
+        softmax(Se, Pe);
+        rescale();
+        pv(2 * t + kb, Pe);
       }
     }
   }
