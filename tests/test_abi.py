@@ -110,10 +110,11 @@ def test_workspace_size_rules(lib):
     # one chunk covers the prefix: no workspace
     assert ws(1, 8, 2, 1, 64, 16, 0, 1024) == 0
     # 1 tree tile + 64 prefix tiles in chunks of 4 tiles -> 17 chunks, one 256-row block:
-    # S * 256 rows * (D + 2) floats
-    assert ws(1, 8, 2, 1, 64, 4096, 0, 256) == 17 * 256 * 66 * 4
-    # G*T = 8*60 = 480 rows -> 2 row blocks of 256; 65 tiles in chunks of 32 -> 3 chunks
-    assert ws(2, 60, 64, 8, 128, 4096, 1, 2048) == 2 * 8 * 2 * 3 * 256 * 130 * 4
+    # S * 256 rows * (D fp32 partial O + 2 fp32 statistics)
+    assert ws(1, 8, 2, 1, 64, 4096, 0, 256) == 17 * 256 * (64 * 4 + 8)
+    # G*T = 8*60 = 480 rows -> 2 row blocks of 256; 65 tiles in chunks of 32 -> 3 chunks;
+    # bf16 inputs keep the partial O in bf16
+    assert ws(2, 60, 64, 8, 128, 4096, 1, 2048) == 2 * 8 * 2 * 3 * 256 * (128 * 2 + 8)
     # bad arguments report 0
     assert ws(1, 8, 3, 2, 64, 4096, 0, 0) == 0
     assert ws(1, 8, 2, 1, 80, 4096, 0, 0) == 0

@@ -67,8 +67,8 @@ struct AttnArgs {
   char* out;
   float* lse;
   int32_t* status;
-  float* part_o;   // [slot][kRows*D] in register order
-  float* part_ml;  // [slot][kRows][2]
+  char* part_o;    // [slot][kRows*D] elements of the input type, in register order
+  float* part_ml;  // [slot][kRows][2]: running max m and sum l per row
   int B, T, Hq, Hkv, G, Lmax, W, GT, RB, S, chunk_tiles;
   float c;         // scale * log2(e)
 };
@@ -580,15 +580,24 @@ void attn_main(AttnArgs a) {
       if (a.lse && h == 0) a.lse[orow] = (m_run + __log2f(l_run)) * kLn2;
     }
   } else if (row_ok) {  // padding rows are never merged
+    // unnormalised O in the input type (bf16 partials carry the rounding the output gets
+    // anyway), four consecutive d per lane and group: group index ((wave*kDB + db)*4 + j)*64 + lane
     const size_t slot = (((size_t)b * a.Hkv + kvh) * a.RB + rb) * a.S + s;
-    float4* po = reinterpret_cast<float4*>(a.part_o + slot * (size_t)kRows * D);
+    using PO = typename std::conditional<kBF16, uint2, float4>::type;
+    PO* po = reinterpret_cast<PO*>(a.part_o + slot * (size_t)kRows * D * sizeof(E));
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x16& acc = oacc[db];
-        po[(((wave * kDB + db) * 4 + j) << 6) + lane] =
-            float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+        if constexpr (kBF16) {
+          po[(((wave * kDB + db) * 4 + j) << 6) + lane] =
+              uint2{pack_bf16x2(acc[4 * j], acc[4 * j + 1]),
+                    pack_bf16x2(acc[4 * j + 2], acc[4 * j + 3])};
+        } else {
+          po[(((wave * kDB + db) * 4 + j) << 6) + lane] =
+              float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]};
+        }
       }
     if (h == 0) {
       float2* pml = reinterpret_cast<float2*>(a.part_ml + slot * (size_t)kRows * 2);
@@ -599,69 +608,88 @@ void attn_main(AttnArgs a) {
 
 // Merge the per-chunk partials of sequences with more than one non-empty chunk:
 //   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  lse = (M + log2 den) ln 2.
-// One wavefront per (32 rows, 32-wide d block); the loads of four chunks are in flight together.
+// One thread per group of four consecutive d of one row (the partials' register order), so a
+// row block of 256 rows is D / 4 workgroups' work.  Chunks are taken eight at a time with all
+// their loads in flight, and M is raised per batch (online, as in the main kernel).  Workgroups
+// are dealt to XCDs in the same (b, kvh) order as attn_main's, so a merge reads partials from
+// the L2 they were written to.
 template <typename E, int D>
-__global__ __launch_bounds__(64) void attn_combine(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+  constexpr bool kBF16 = std::is_same<E, __bf16>::value;
   constexpr int kDB = D / 32;
-  const int db = blockIdx.x % kDB;
-  const int wave = (blockIdx.x / kDB) % kWaves;
-  const int item = blockIdx.x / (kDB * kWaves);  // (b, kvh, rb)
+  constexpr int kWGs = kRows * D / 4 / 256;  // workgroups per (b, kvh, rb)
+  constexpr int kBatch = 8;
+  const int c = xcd_remap(blockIdx.x, a.B * a.Hkv * a.RB * kWGs);
+  const int item = c / kWGs;  // (b, kvh, rb)
+  const int g = (c % kWGs) * 256 + threadIdx.x;
   const int rb = item % a.RB;
   const int kvh = (item / a.RB) % a.Hkv;
   const int b = item / (a.RB * a.Hkv);
   const int L = min(max(a.cache_len[b], 0), a.Lmax);
   const int n_split = ceil_div(ceil_div(a.T, kKT) + ceil_div(L, kKT), a.chunk_tiles);
   if (n_split == 1) return;  // written directly by attn_main
-  const int lane = threadIdx.x;
-  const int n = lane & 31, h = lane >> 5;
-  const int rloc = wave * 32 + n;
+  // g = ((wave*kDB + db)*4 + j)*64 + lane  ->  row wave*32 + lane%32, d = db*32 + 8j + 4*(lane/32)
+  const int lane = g & 63, j = (g >> 6) & 3, db = (g >> 8) % kDB, wave = (g >> 8) / kDB;
+  const int rloc = wave * 32 + (lane & 31);
   const int r = rb * kRows + rloc;
   if (r >= a.GT) return;
+  const int d = db * 32 + 8 * j + 4 * (lane >> 5);
   const size_t slot0 = (((size_t)b * a.Hkv + kvh) * a.RB + rb) * a.S;
-  const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
-  const float4* po = reinterpret_cast<const float4*>(a.part_o);
+  const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + slot0 * kRows + rloc;
 
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pml[(slot0 + s) * kRows + rloc].x);
-  float den = 0.f;
-  float4 acc[4];
+  float M = -INFINITY, den = 0.f;
+  float4 acc = float4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < n_split; s0 += kBatch) {
+    float2 ml[kBatch];
+    float4 v[kBatch];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = float4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = 0; s < n_split; ++s) {
-    const float2 ml = pml[(slot0 + s) * kRows + rloc];
-    const float4* ps = po + (slot0 + s) * (size_t)kRows * D / 4;
-    float4 v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = ps[(((wave * kDB + db) * 4 + j) << 6) + lane];
-    const float w = fast_exp2(ml.x - M);
-    den += w * ml.y;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[j].x += w * v[j].x;
-      acc[j].y += w * v[j].y;
-      acc[j].z += w * v[j].z;
-      acc[j].w += w * v[j].w;
+    for (int u = 0; u < kBatch; ++u) {
+      // past the last chunk: load the last one again (no branch, so all loads stay in flight)
+      // and give it weight 0
+      const int s = min(s0 + u, n_split - 1);
+      ml[u] = pml[(size_t)s * kRows];
+      if (s0 + u >= n_split) ml[u].x = -INFINITY;
+      const size_t gi = (slot0 + s) * (kRows * D / 4) + g;
+      if constexpr (kBF16) {
+        const uint2 w = reinterpret_cast<const uint2*>(a.part_o)[gi];
+        v[u] = float4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                      __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+      } else {
+        v[u] = reinterpret_cast<const float4*>(a.part_o)[gi];
+      }
     }
+    // every non-empty chunk has a finite m (each row sees a key in it), so Mb is finite
+    float Mb = M;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) Mb = fmaxf(Mb, ml[u].x);
+    const float sc = fast_exp2(M - Mb);  // 0 on the first batch
+    den *= sc;
+    acc.x *= sc;
+    acc.y *= sc;
+    acc.z *= sc;
+    acc.w *= sc;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = fast_exp2(ml[u].x - Mb);
+      den += w * ml[u].y;
+      acc.x += w * v[u].x;
+      acc.y += w * v[u].y;
+      acc.z += w * v[u].z;
+      acc.w += w * v[u].w;
+    }
+    M = Mb;
   }
   const float inv = 1.f / den;
   const int t = r / a.G, head = kvh * a.G + r % a.G;
   const size_t orow = ((size_t)b * a.T + t) * a.Hq + head;
   E* o = reinterpret_cast<E*>(a.out) + orow * D;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int d = db * 32 + 8 * j + 4 * h;
-    const float4 v = acc[j];
-    if constexpr (std::is_same<E, __bf16>::value) {
-      uint2 w;
-      w.x = pack_bf16x2(v.x * inv, v.y * inv);
-      w.y = pack_bf16x2(v.z * inv, v.w * inv);
-      *reinterpret_cast<uint2*>(o + d) = w;
-    } else {
-      *reinterpret_cast<float4*>(o + d) = float4{v.x * inv, v.y * inv, v.z * inv, v.w * inv};
-    }
+  if constexpr (kBF16) {
+    *reinterpret_cast<uint2*>(o + d) =
+        uint2{pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv)};
+  } else {
+    *reinterpret_cast<float4*>(o + d) = float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
   }
-  if (a.lse && h == 0 && db == 0) a.lse[orow] = (M + __log2f(den)) * kLn2;
+  if (a.lse && d == 0) a.lse[orow] = (M + __log2f(den)) * kLn2;
 }
 
 struct Plan {
@@ -669,7 +697,7 @@ struct Plan {
   size_t ws_bytes;
 };
 
-Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int split_keys) {
+Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int elem_bytes, int split_keys) {
   Plan p;
   const int G = Hq / Hkv;
   p.RB = ceil_div(G * T, kRows);
@@ -688,7 +716,8 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int split_keys) {
   }
   p.chunk_tiles = chunk_tiles;
   p.S = ceil_div(tiles, chunk_tiles);
-  p.ws_bytes = p.S > 1 ? (size_t)B * Hkv * p.RB * p.S * kRows * (D + 2) * sizeof(float) : 0;
+  // per slot: kRows x D partial O in the input type, then kRows x (m, l) in fp32
+  p.ws_bytes = p.S > 1 ? (size_t)B * Hkv * p.RB * p.S * kRows * ((size_t)D * elem_bytes + 8) : 0;
   return p;
 }
 
@@ -706,8 +735,8 @@ int launch(const AttnArgs& a, hipStream_t stream) {
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (g_prof_after && hipEventRecord(g_prof_after, stream) != hipSuccess) return TV_ERR_HIP;
   if (a.S > 1)
-    hipLaunchKernelGGL((attn_combine<E, D>), dim3(a.B * a.Hkv * a.RB * kWaves * (D / 32)),
-                       dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((attn_combine<E, D>), dim3(a.B * a.Hkv * a.RB * (kRows * D / 4 / 256)),
+                       dim3(256), 0, stream, a);
   return launch_status();
 }
 
@@ -748,7 +777,7 @@ extern "C" size_t tree_verify_attn_workspace_size(int B, int T, int Hq, int Hkv,
   if (!attn_shapes_ok(B, T, Hq, Hkv, Lmax) || (D != 64 && D != 128) ||
       (dtype != TV_F32 && dtype != TV_BF16))
     return 0;
-  return make_plan(B, T, Hq, Hkv, D, Lmax, split_keys).ws_bytes;
+  return make_plan(B, T, Hq, Hkv, D, Lmax, dtype == TV_BF16 ? 2 : 4, split_keys).ws_bytes;
 }
 
 extern "C" int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
@@ -761,7 +790,7 @@ extern "C" int tree_verify_attn(const void* q, const void* k_cache, const void* 
       !attn_shapes_ok(B, T, Hq, Hkv, Lmax) || split_keys < 0)
     return TV_ERR_INVALID_ARG;
   if ((dtype != TV_F32 && dtype != TV_BF16) || (D != 64 && D != 128)) return TV_ERR_UNSUPPORTED;
-  const Plan p = make_plan(B, T, Hq, Hkv, D, Lmax, split_keys);
+  const Plan p = make_plan(B, T, Hq, Hkv, D, Lmax, dtype == TV_BF16 ? 2 : 4, split_keys);
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return TV_ERR_WORKSPACE;
   if ((long long)B * Hkv * p.RB * p.S >= (1LL << 31)) return TV_ERR_INVALID_ARG;
 
@@ -789,9 +818,11 @@ extern "C" int tree_verify_attn(const void* q, const void* k_cache, const void* 
   a.chunk_tiles = p.chunk_tiles;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
   a.c = sc * kLog2e;
-  float* ws = (float*)workspace;
+  char* ws = (char*)workspace;
   a.part_o = ws;
-  a.part_ml = p.ws_bytes ? ws + (size_t)B * Hkv * p.RB * p.S * kRows * D : nullptr;
+  a.part_ml = p.ws_bytes ? (float*)(ws + (size_t)B * Hkv * p.RB * p.S * kRows * D *
+                                              (dtype == TV_BF16 ? 2 : 4))
+                         : nullptr;
 
   hipStream_t st = (hipStream_t)stream;
   if (dtype == TV_BF16) return D == 128 ? launch<__bf16, 128>(a, st) : launch<__bf16, 64>(a, st);

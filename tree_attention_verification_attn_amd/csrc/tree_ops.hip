@@ -104,6 +104,15 @@ __device__ inline int wave_max(int v) {
   return v;
 }
 
+__device__ inline uint64_t shfl64(uint64_t v, int src) {
+  const int lo = __shfl((int)(uint32_t)v, src, 64);
+  const int hi = __shfl((int)(uint32_t)(v >> 32), src, 64);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// All global loads (mask rows, draft and target tokens of the lane's two nodes) are issued
+// together; the parent's target token and the winner's mask row then come from other lanes by
+// shuffles, so the kernel makes one round trip to memory before its writes.
 __global__ __launch_bounds__(64) void accept_kernel(const uint64_t* __restrict__ anc,
                                                     const int32_t* __restrict__ draft,
                                                     const int32_t* __restrict__ target, int T,
@@ -116,22 +125,33 @@ __global__ __launch_bounds__(64) void accept_kernel(const uint64_t* __restrict__
   low_bits(T, in_lo, in_hi);
 
   uint64_t a0[2], a1[2];
-  bool ok[2];
+  int dr[2], tg[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int c = lane + 64 * k;
     a0[k] = a1[k] = 0;
-    ok[k] = false;
+    dr[k] = tg[k] = 0;
     if (c < T) {
       const uint64_t* row = anc + (base + c) * W;
       a0[k] = row[0] & in_lo;
       a1[k] = (W == 2 ? row[1] : 0) & in_hi;
-      uint64_t blo, bhi;  // strictly below c
-      low_bits(c, blo, bhi);
-      const uint64_t m0 = a0[k] & blo, m1 = a1[k] & bhi;
-      const int p = m1 ? 64 + 63 - __clzll(m1) : (m0 ? 63 - __clzll(m0) : -1);
-      ok[k] = (c == 0) || (p >= 0 && draft[base + c] == target[base + p]);
+      dr[k] = draft[base + c];
+      tg[k] = target[base + c];
     }
+  }
+  bool ok[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    uint64_t blo, bhi;  // strictly below c
+    low_bits(c, blo, bhi);
+    const uint64_t m0 = a0[k] & blo, m1 = a1[k] & bhi;
+    const int p = m1 ? 64 + 63 - __clzll(m1) : (m0 ? 63 - __clzll(m0) : -1);
+    // target token of node p, held by lane p % 64 in slot p / 64 (every lane takes part)
+    const int pp = max(p, 0);
+    const int t0 = __shfl(tg[0], pp & 63, 64), t1 = __shfl(tg[1], pp & 63, 64);
+    const int tp = pp >= 64 ? t1 : t0;
+    ok[k] = c < T && ((c == 0) || (p >= 0 && dr[k] == tp));
   }
   const uint64_t ok_lo = __ballot(ok[0]);
   const uint64_t ok_hi = __ballot(ok[1]);
@@ -148,8 +168,12 @@ __global__ __launch_bounds__(64) void accept_kernel(const uint64_t* __restrict__
   key = wave_max(key);
   const int best = key >= 0 ? 255 - (key & 255) : 0;
 
-  const uint64_t* brow = anc + (base + best) * W;
-  const uint64_t b0 = brow[0] & in_lo, b1 = (W == 2 ? brow[1] : 0) & in_hi;
+  // the winner's mask row and target token, from lane best % 64, slot best / 64
+  const int src = best & 63;
+  const bool hi_slot = best >= 64;
+  const uint64_t b0 = hi_slot ? shfl64(a0[1], src) : shfl64(a0[0], src);
+  const uint64_t b1 = hi_slot ? shfl64(a1[1], src) : shfl64(a1[0], src);
+  const int bonus = hi_slot ? __shfl(tg[1], src, 64) : __shfl(tg[0], src, 64);
   const int n = __popcll(b0) + __popcll(b1);
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -166,7 +190,7 @@ __global__ __launch_bounds__(64) void accept_kernel(const uint64_t* __restrict__
   }
   if (lane == 0) {
     accept_len[b] = n;
-    bonus_tok[b] = target[base + best];
+    bonus_tok[b] = bonus;
   }
 }
 
@@ -182,20 +206,21 @@ __global__ __launch_bounds__(256) void compact_kernel(
     int heads_per_wg, int stage_rows, int32_t* status) {
   extern __shared__ uint4 stage[];
   __shared__ int s_bits;
+  __shared__ int s_path[kMaxT];
   const int b = blockIdx.x, hg = blockIdx.y, tid = threadIdx.x;
+  // the whole path row is read with the lengths (one round trip), then checked from LDS
   const int L = cache_len[b];
   const int n = alen[b];
+  if (tid < T) s_path[tid] = path[(size_t)b * T + tid];
   if (tid == 0) s_bits = 0;
   __syncthreads();
   int bits = 0;
   if (L < 0 || L > Lmax) bits |= TV_BAD_LEN;
   if (n < 0 || n > T) {
     bits |= TV_BAD_PATH;
-  } else {
-    for (int i = tid; i < n; i += 256) {
-      const int j = path[(size_t)b * T + i];
-      if (j < 0 || j >= T) atomicOr(&s_bits, TV_BAD_PATH);
-    }
+  } else if (tid < n) {
+    const int j = s_path[tid];
+    if (j < 0 || j >= T) atomicOr(&s_bits, TV_BAD_PATH);
   }
   __syncthreads();
   bits |= s_bits;
@@ -219,7 +244,7 @@ __global__ __launch_bounds__(256) void compact_kernel(
       const int i = r % n;
       r /= n;
       const int kv = r & 1, head = h + (r >> 1);
-      const int j = path[(size_t)b * T + i];
+      const int j = s_path[i];
       const char* src = (kv ? vt : kt) + (((size_t)b * T + j) * Hkv + head) * row_bytes;
       stage[q] = reinterpret_cast<const uint4*>(src)[chunk];
     }
