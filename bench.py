@@ -48,6 +48,9 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     p.add_argument("--split-keys", type=int, default=0, help="prefix keys per split (0 = auto)")
+    p.add_argument("--api", choices=("fused", "separate"), default="fused",
+                   help="time the step through tree_verify_step (three launches) or through the "
+                        "four separate entry points; the other is timed too and reported")
     p.add_argument("--rotate", type=int, default=0, help="input copies to rotate (0 = auto)")
     p.add_argument("--mode", choices=("graph", "eager"), default="graph",
                    help="replay each step as a captured HIP graph, or launch eagerly")
@@ -183,6 +186,13 @@ class StepSet:
         self.compact_args = (P(t["k_cache"]), P(t["v_cache"]), P(t["cache_len"]),
                              P(t["cache_len_out"]), P(t["k_tree"]), P(t["v_tree"]), P(t["path"]),
                              P(t["alen"]), B, T, w.Hkv, D, w.Lmax, dt, P(t["status"]))
+        self.step_args = (P(t["parent"]), P(t["draft"]), P(t["target"]), P(t["q"]),
+                          P(t["k_cache"]), P(t["v_cache"]), P(t["cache_len"]),
+                          P(t["cache_len_out"]), P(t["k_tree"]), P(t["v_tree"]), P(t["anc"]),
+                          P(t["out"]), P(t["lse"]), P(t["path"]), P(t["alen"]), P(t["bonus"]),
+                          P(t["status"]), B, T, Hq, w.Hkv, D, w.Lmax, dt, ctypes.c_float(0.0),
+                          split_keys, ws_ptr, ctypes.c_size_t(ws_bytes))
+        self.api = "fused"
 
     def mask(self, stream):
         rc = self.lib.tree_build_mask(*self.mask_args, stream)
@@ -200,7 +210,14 @@ class StepSet:
         rc = self.lib.kv_compact_accepted(*self.compact_args, stream)
         assert rc == 0, rc
 
+    def fused(self, stream):
+        rc = self.lib.tree_verify_step(*self.step_args, stream)
+        assert rc == 0, rc
+
     def step(self, stream):
+        if self.api == "fused":
+            self.fused(stream)
+            return
         self.mask(stream)
         self.attn(stream)
         self.accept(stream)
@@ -300,41 +317,50 @@ def main() -> int:
 
     stream = torch.cuda.Stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
-    graphs = None
-    if args.mode == "graph":
-        graphs = []
-        with torch.cuda.stream(stream):
-            for s in sets:  # one eager step first so any lazy initialisation is outside capture
-                s.step(sptr)
-        stream.synchronize()
+
+    def time_api(api):
+        """W untimed steps, then exactly K timed steps through `api`; (ms per step, wall s)."""
         for s in sets:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                s.step(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-            graphs.append(g)
-        torch.cuda.synchronize()
+            s.api = api
+        graphs = None
+        if args.mode == "graph":
+            graphs = []
+            with torch.cuda.stream(stream):
+                for s in sets:  # one eager step first so lazy initialisation is outside capture
+                    s.step(sptr)
+            stream.synchronize()
+            for s in sets:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    s.step(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+                graphs.append(g)
+            torch.cuda.synchronize()
 
-    def run_steps(k, offset=0):
-        for i in range(k):
-            j = (offset + i) % n_sets
-            if graphs is not None:
-                graphs[j].replay()
-            else:
-                sets[j].step(sptr)
+        def run_steps(k, offset=0):
+            for i in range(k):
+                j = (offset + i) % n_sets
+                if graphs is not None:
+                    graphs[j].replay()
+                else:
+                    sets[j].step(sptr)
 
-    with torch.cuda.stream(stream):
-        run_steps(args.warmup)
-        stream.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter()
-        e0.record(stream)
-        run_steps(args.steps, offset=args.warmup)
-        e1.record(stream)
-        e1.synchronize()
-        t_wall = time.perf_counter() - t_wall
-        torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+        with torch.cuda.stream(stream):
+            run_steps(args.warmup)
+            stream.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t_wall = time.perf_counter()
+            e0.record(stream)
+            run_steps(args.steps, offset=args.warmup)
+            e1.record(stream)
+            e1.synchronize()
+            t_wall = time.perf_counter() - t_wall
+            torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps, t_wall
+
+    other = "separate" if args.api == "fused" else "fused"
+    ms_other, _ = time_api(other)
+    ms_per_step, t_wall = time_api(args.api)
     t_step = ms_per_step * 1e-3
 
     # ---- per-call durations: a separate eager pass with events between the calls -------------
@@ -415,7 +441,8 @@ def main() -> int:
         "config": {"workload": args.workload, "desc": w.spec.desc, "B": w.B, "T": w.T,
                    "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "prefix_tokens": int(L.sum()),
                    "Lmax": w.Lmax, "layers": 1, "mode": args.mode, "rotated_sets": n_sets,
-                   "split_keys": args.split_keys},
+                   "split_keys": args.split_keys, "step_api": args.api},
+        "ms_per_step_by_api": {args.api: ms_per_step, other: ms_other},
         "hbm_frac": value / HBM_PEAK_GBS,
         "attn_kv_gbps": kv_bytes / t_attn / 1e9,
         "attn_hbm_frac": kv_bytes / t_attn / 1e9 / HBM_PEAK_GBS,

@@ -164,6 +164,32 @@ int kv_compact_accepted(void* k_cache, void* v_cache, const int32_t* cache_len,
                         const int32_t* accept_path, const int32_t* accept_len, int B, int T,
                         int Hkv, int D, int Lmax, int dtype, int32_t* status, void* stream);
 
+/*
+ * tree_verify_step — one whole verification step: tree_build_mask, tree_verify_attn,
+ * tree_accept and kv_compact_accepted, in that order and with the same results and status
+ * bits, fused into three kernel launches (ancestor masks; the attention main kernel; the
+ * split-K merge together with the acceptance walk and the compaction).  The step is the one
+ * the pages describe: attention of the flattened tree (lesty.tech section 5), greedy
+ * acceptance of the longest path (section 4; rainlin.net section 3.2), commit of its K/V
+ * (lesty.tech section 8).
+ *
+ * Arguments are those of the four calls: parent, draft_tok, target_tok as for tree_build_mask
+ * and tree_accept; q, k_cache, v_cache, cache_len, k_tree, v_tree, out, lse, scale,
+ * split_keys, workspace as for tree_verify_attn (the same workspace size); anc_mask is an
+ * output here; accept_path, accept_len, bonus_tok as for tree_accept; cache_len_out as for
+ * kv_compact_accepted (it may be the same pointer as cache_len, not partly overlapping).
+ * status [B] is required; it is written by the mask stage and OR-ed by the others.  When
+ * k_tree or v_tree overlaps a cache buffer, the step runs the four calls one after the other,
+ * so that rows are staged as kv_compact_accepted does.
+ */
+int tree_verify_step(const int32_t* parent, const int32_t* draft_tok, const int32_t* target_tok,
+                     const void* q, void* k_cache, void* v_cache, const int32_t* cache_len,
+                     int32_t* cache_len_out, const void* k_tree, const void* v_tree,
+                     uint64_t* anc_mask, void* out, float* lse, int32_t* accept_path,
+                     int32_t* accept_len, int32_t* bonus_tok, int32_t* status, int B, int T,
+                     int Hq, int Hkv, int D, int Lmax, int dtype, float scale, int split_keys,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

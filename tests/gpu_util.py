@@ -63,6 +63,23 @@ def run_step(g: dict, split_keys: int = 0, tv=None):
                 v_cache=to_host(g["v_cache"]))
 
 
+def run_step_fused(g: dict, split_keys: int = 0, in_place_len: bool = False, tv=None):
+    """The same step through the fused entry point tree_verify_step."""
+    import tree_attention_verification_attn_amd as tvmod
+
+    tv = tv or tvmod
+    r = tv.tree_verify_step(g["parent"], g["draft"], g["target"], g["q"], g["k_cache"],
+                            g["v_cache"], g["cache_len"], g["k_tree"], g["v_tree"],
+                            cache_len_out=g["cache_len"] if in_place_len else None,
+                            split_keys=split_keys)
+    torch.cuda.synchronize()
+    return dict(anc=to_host(r["anc_mask"]).view(np.uint64), status=to_host(r["status"]),
+                out=to_host(r["out"]), lse=to_host(r["lse"]), path=to_host(r["accept_path"]),
+                alen=to_host(r["accept_len"]), bonus=to_host(r["bonus_tok"]),
+                new_len=to_host(r["cache_len_out"]), k_cache=to_host(g["k_cache"]),
+                v_cache=to_host(g["v_cache"]))
+
+
 def sample_rows(w, n_random: int, seed: int = 0) -> np.ndarray:
     """(b, h, i) rows: corners of every axis plus uniform random ones."""
     rng = np.random.default_rng(seed)

@@ -110,14 +110,38 @@ def test_workspace_size_rules(lib):
     # one chunk covers the prefix: no workspace
     assert ws(1, 8, 2, 1, 64, 16, 0, 1024) == 0
     # 1 tree tile + 64 prefix tiles in chunks of 4 tiles -> 17 chunks, one 256-row block:
-    # S * 256 rows * (D fp32 partial O + 2 fp32 statistics)
-    assert ws(1, 8, 2, 1, 64, 4096, 0, 256) == 17 * 256 * (64 * 4 + 8)
+    # S * 256 rows * (D fp32 partial O + 2 fp32 statistics), then one int32 chunk count per
+    # sequence
+    assert ws(1, 8, 2, 1, 64, 4096, 0, 256) == 17 * 256 * (64 * 4 + 8) + 1 * 4
     # G*T = 8*60 = 480 rows -> 2 row blocks of 256; 65 tiles in chunks of 32 -> 3 chunks;
     # bf16 inputs keep the partial O in bf16
-    assert ws(2, 60, 64, 8, 128, 4096, 1, 2048) == 2 * 8 * 2 * 3 * 256 * (128 * 2 + 8)
+    assert ws(2, 60, 64, 8, 128, 4096, 1, 2048) == 2 * 8 * 2 * 3 * 256 * (128 * 2 + 8) + 2 * 4
     # bad arguments report 0
     assert ws(1, 8, 3, 2, 64, 4096, 0, 0) == 0
     assert ws(1, 8, 2, 1, 80, 4096, 0, 0) == 0
+
+
+def test_step_argument_errors(lib):
+    # 17 device pointers, then B, T, Hq, Hkv, D, Lmax, dtype, scale, split_keys, ws, ws_bytes,
+    # stream
+    base = [FAKE] * 17 + [1, 8, 2, 1, 64, 16, 0, 0.0, 0, None, 0, None]
+    for i in list(range(12)) + list(range(13, 17)):  # every pointer but lse is required
+        bad = list(base)
+        bad[i] = None
+        assert lib.tree_verify_step(*bad) == -1, i
+    bad = list(base)
+    bad[12] = None  # lse is optional
+    bad[17] = 0     # B = 0 -> rejected before any launch
+    assert lib.tree_verify_step(*bad) == -1
+    bad = list(base)
+    bad[21] = 96    # head_dim
+    assert lib.tree_verify_step(*bad) == -2
+    # partly overlapping cache_len / cache_len_out
+    bad = list(base)
+    bad[6] = ctypes.c_void_p(0x2000)
+    bad[7] = ctypes.c_void_p(0x2002)
+    bad[17] = 4
+    assert lib.tree_verify_step(*bad) == -1
 
 
 def test_accept_argument_errors(lib):

@@ -26,4 +26,5 @@ from .binding import (  # noqa: F401
     tree_build_mask,
     tree_verify_attn,
     tree_verify_attn_workspace_size,
+    tree_verify_step,
 )

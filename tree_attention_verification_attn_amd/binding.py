@@ -19,7 +19,8 @@ TV_F32, TV_BF16 = 0, 1
 TV_BAD_TREE, TV_OVERFLOW, TV_BAD_LEN, TV_BAD_PATH = 0x1, 0x2, 0x4, 0x8
 
 EXPORTS = ("tv_status_string", "tree_build_mask", "tree_verify_attn_workspace_size",
-           "tree_verify_attn", "tree_accept", "kv_compact_accepted", "tv_profile_attn_main")
+           "tree_verify_attn", "tree_accept", "kv_compact_accepted", "tv_profile_attn_main",
+           "tree_verify_step")
 
 
 class TreeVerifyError(RuntimeError):
@@ -70,6 +71,9 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.kv_compact_accepted.restype = I
     lib.tv_profile_attn_main.argtypes = [P, P]
     lib.tv_profile_attn_main.restype = I
+    lib.tree_verify_step.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                     I, I, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
+    lib.tree_verify_step.restype = I
 
 
 def status_string(code: int) -> str:
@@ -235,3 +239,63 @@ def kv_compact_accepted(k_cache, v_cache, cache_len, k_tree, v_tree, accept_path
         _ptr(v_tree), _ptr(accept_path), _ptr(accept_len), B, T, Hkv, D, Lmax, dt,
         _ptr(status), _stream(stream)))
     return cache_len_out
+
+
+def tree_verify_step(parent, draft_tok, target_tok, q, k_cache, v_cache, cache_len, k_tree,
+                     v_tree, cache_len_out=None, out=None, lse=None, anc_mask=None,
+                     accept_path=None, accept_len=None, bonus_tok=None, status=None,
+                     scale: float = 0.0, split_keys: int = 0,
+                     workspace: torch.Tensor | None = None, with_lse: bool = True, stream=None):
+    """One fused verification step (masks, attention, acceptance, compaction in place).
+
+    Returns a dict with anc_mask, out, lse, accept_path, accept_len, bonus_tok, cache_len_out
+    and status."""
+    _need(parent, "parent", torch.int32, 2)
+    _need(draft_tok, "draft_tok", torch.int32, 2)
+    _need(target_tok, "target_tok", torch.int32, 2)
+    _need(q, "q", None, 4)
+    B, T, Hq, D = q.shape
+    dt = _dtype_code(q)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_tree", k_tree),
+                    ("v_tree", v_tree)):
+        _need(t, name, q.dtype, 4)
+    _need(cache_len, "cache_len", torch.int32, 1)
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    W = (T + 63) // 64
+    if (tuple(k_cache.shape) != (B, Hkv, Lmax, D) or tuple(v_cache.shape) != tuple(k_cache.shape)
+            or tuple(k_tree.shape) != (B, T, Hkv, D) or tuple(v_tree.shape) != (B, T, Hkv, D)
+            or tuple(cache_len.shape) != (B,) or tuple(parent.shape) != (B, T)
+            or tuple(draft_tok.shape) != (B, T) or tuple(target_tok.shape) != (B, T)):
+        raise ValueError("inconsistent tree_verify_step shapes")
+    dev = q.device
+    new = lambda shape, dtype: torch.empty(shape, dtype=dtype, device=dev)  # noqa: E731
+    anc_mask = new((B, T, W), torch.int64) if anc_mask is None else anc_mask
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and with_lse:
+        lse = new((B, T, Hq), torch.float32)
+    accept_path = new((B, T), torch.int32) if accept_path is None else accept_path
+    accept_len = new((B,), torch.int32) if accept_len is None else accept_len
+    bonus_tok = new((B,), torch.int32) if bonus_tok is None else bonus_tok
+    cache_len_out = torch.empty_like(cache_len) if cache_len_out is None else cache_len_out
+    status = new((B,), torch.int32) if status is None else status
+    _need(anc_mask, "anc_mask", torch.int64, 3)
+    _need(out, "out", q.dtype, 4)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+    for name, t in (("accept_len", accept_len), ("bonus_tok", bonus_tok),
+                    ("cache_len_out", cache_len_out), ("status", status)):
+        _need(t, name, torch.int32, 1)
+    _need(accept_path, "accept_path", torch.int32, 2)
+    ws_bytes = tree_verify_attn_workspace_size(B, T, Hq, Hkv, D, Lmax, q.dtype, split_keys)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("tree_verify_step", load_library().tree_verify_step(
+        _ptr(parent), _ptr(draft_tok), _ptr(target_tok), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+        _ptr(cache_len), _ptr(cache_len_out), _ptr(k_tree), _ptr(v_tree), _ptr(anc_mask),
+        _ptr(out), _ptr(lse), _ptr(accept_path), _ptr(accept_len), _ptr(bonus_tok),
+        _ptr(status), B, T, Hq, Hkv, D, Lmax, dt, float(scale), int(split_keys),
+        _ptr(workspace), ws_have, _stream(stream)))
+    return dict(anc_mask=anc_mask, out=out, lse=lse, accept_path=accept_path,
+                accept_len=accept_len, bonus_tok=bonus_tok, cache_len_out=cache_len_out,
+                status=status)

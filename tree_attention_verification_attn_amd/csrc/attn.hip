@@ -37,7 +37,7 @@
 #include <cmath>
 #include <type_traits>
 
-#include "tv_internal.h"
+#include "tree_device.h"
 
 namespace tv {
 namespace {
@@ -69,6 +69,7 @@ struct AttnArgs {
   int32_t* status;
   char* part_o;    // [slot][kRows*D] elements of the input type, in register order
   float* part_ml;  // [slot][kRows][2]: running max m and sum l per row
+  int32_t* nsplit; // [B] non-empty chunks of each sequence, for the merge
   int B, T, Hq, Hkv, G, Lmax, W, GT, RB, S, chunk_tiles;
   float c;         // scale * log2(e)
 };
@@ -192,6 +193,7 @@ void attn_main(AttnArgs a) {
   const int tree_tiles = ceil_div(a.T, kKT);
   const int all_tiles = tree_tiles + ceil_div(L, kKT);
   const int n_split = ceil_div(all_tiles, a.chunk_tiles);
+  if (kSplit && kvh == 0 && s == 0 && rb == 0 && tid == 0) a.nsplit[b] = n_split;
   if (s >= n_split) return;  // empty chunk: nothing to merge
   const bool direct = !kSplit || n_split == 1;
 
@@ -614,20 +616,26 @@ void attn_main(AttnArgs a) {
 // are dealt to XCDs in the same (b, kvh) order as attn_main's, so a merge reads partials from
 // the L2 they were written to.
 template <typename E, int D>
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+constexpr int combine_wgs_per_item() {
+  return kRows * D / 4 / 256;  // workgroups of 256 threads per (b, kvh, rb)
+}
+
+// Logical merge workgroup c (of B * Hkv * RB * combine_wgs_per_item), 256 threads.  The chunk
+// count comes from the workspace (written by attn_main), not from cache_len, which a fused
+// compaction may be updating at the same time.
+template <typename E, int D>
+__device__ void combine_group(const AttnArgs& a, int c) {
   constexpr bool kBF16 = std::is_same<E, __bf16>::value;
   constexpr int kDB = D / 32;
-  constexpr int kWGs = kRows * D / 4 / 256;  // workgroups per (b, kvh, rb)
+  constexpr int kWGs = combine_wgs_per_item<E, D>();
   constexpr int kBatch = 8;
-  const int c = xcd_remap(blockIdx.x, a.B * a.Hkv * a.RB * kWGs);
   const int item = c / kWGs;  // (b, kvh, rb)
   const int g = (c % kWGs) * 256 + threadIdx.x;
   const int rb = item % a.RB;
   const int kvh = (item / a.RB) % a.Hkv;
   const int b = item / (a.RB * a.Hkv);
-  const int L = min(max(a.cache_len[b], 0), a.Lmax);
-  const int n_split = ceil_div(ceil_div(a.T, kKT) + ceil_div(L, kKT), a.chunk_tiles);
-  if (n_split == 1) return;  // written directly by attn_main
+  const int n_split = a.nsplit[b];
+  if (n_split <= 1) return;  // written directly by attn_main
   // g = ((wave*kDB + db)*4 + j)*64 + lane  ->  row wave*32 + lane%32, d = db*32 + 8j + 4*(lane/32)
   const int lane = g & 63, j = (g >> 6) & 3, db = (g >> 8) % kDB, wave = (g >> 8) / kDB;
   const int rloc = wave * 32 + (lane & 31);
@@ -692,6 +700,71 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   if (a.lse && d == 0) a.lse[orow] = (M + __log2f(den)) * kLn2;
 }
 
+template <typename E, int D>
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+  combine_group<E, D>(a, xcd_remap(blockIdx.x, a.B * a.Hkv * a.RB * combine_wgs_per_item<E, D>()));
+}
+
+// ---- fused tail of a verification step -----------------------------------------------------
+// Workgroups [0, n_comb) merge split-K partials (as attn_combine); workgroup n_comb + b runs
+// the acceptance walk of sequence b on its first wavefront, then all four wavefronts copy the
+// accepted K/V rows of every KV head into the cache.  Used only when the tree K/V does not
+// overlap the cache, so rows are copied directly, without staging.
+struct TailArgs {
+  const uint64_t* anc;
+  const int32_t* draft;
+  const int32_t* target;
+  int32_t* accept_path;
+  int32_t* accept_len;
+  int32_t* bonus_tok;
+  char* kc;  // writable views of the caches
+  char* vc;
+  int32_t* cache_len_out;
+  int32_t* status;
+  int n_comb, W, row_bytes;
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void step_tail(AttnArgs a, TailArgs t) {
+  if ((int)blockIdx.x < t.n_comb) {
+    combine_group<E, D>(a, xcd_remap(blockIdx.x, t.n_comb));
+    return;
+  }
+  __shared__ int s_path[kMaxT];
+  __shared__ int s_n;
+  const int b = blockIdx.x - t.n_comb, tid = threadIdx.x;
+  const int L = a.cache_len[b];  // read before this workgroup writes cache_len_out[b]
+  if (tid < 64) {
+    const int n = accept_walk(b, a.T, t.W, t.anc, t.draft, t.target, t.accept_path, t.accept_len,
+                              t.bonus_tok, s_path);
+    if (tid == 0) s_n = n;
+  }
+  __syncthreads();
+  const int n = s_n;  // in [1, T]; the path's entries are valid node indices
+  int bits = 0;
+  if (L < 0 || L > a.Lmax) bits |= TV_BAD_LEN;
+  else if ((long long)L + n > a.Lmax) bits |= TV_OVERFLOW;
+  if (!bits) {
+    const int cpr = t.row_bytes / 16;
+    const int total = a.Hkv * 2 * n * cpr;
+    for (int q = tid; q < total; q += 256) {
+      const int chunk = q % cpr;
+      int r = q / cpr;
+      const int i = r % n;
+      r /= n;
+      const int kv = r & 1, head = r >> 1;
+      const int j = s_path[i];
+      const char* src = (kv ? a.vt : a.kt) + (((size_t)b * a.T + j) * a.Hkv + head) * t.row_bytes;
+      char* dst = (kv ? t.vc : t.kc) + (((size_t)b * a.Hkv + head) * a.Lmax + L + i) * t.row_bytes;
+      reinterpret_cast<uint4*>(dst)[chunk] = reinterpret_cast<const uint4*>(src)[chunk];
+    }
+  }
+  if (tid == 0) {
+    if (bits && t.status) atomicOr(t.status + b, bits);
+    t.cache_len_out[b] = bits ? L : L + n;
+  }
+}
+
 struct Plan {
   int RB, S, chunk_tiles;
   size_t ws_bytes;
@@ -716,8 +789,11 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int elem_bytes, i
   }
   p.chunk_tiles = chunk_tiles;
   p.S = ceil_div(tiles, chunk_tiles);
-  // per slot: kRows x D partial O in the input type, then kRows x (m, l) in fp32
-  p.ws_bytes = p.S > 1 ? (size_t)B * Hkv * p.RB * p.S * kRows * ((size_t)D * elem_bytes + 8) : 0;
+  // per slot: kRows x D partial O in the input type, then kRows x (m, l) in fp32; then the
+  // chunk count of every sequence
+  p.ws_bytes = p.S > 1 ? (size_t)B * Hkv * p.RB * p.S * kRows * ((size_t)D * elem_bytes + 8) +
+                             (size_t)B * sizeof(int32_t)
+                       : 0;
   return p;
 }
 
@@ -725,7 +801,7 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int elem_bytes, i
 hipEvent_t g_prof_before = nullptr, g_prof_after = nullptr;
 
 template <typename E, int D>
-int launch(const AttnArgs& a, hipStream_t stream) {
+int launch_main(const AttnArgs& a, hipStream_t stream) {
   const int n_items = a.B * a.Hkv * a.S * a.RB;
   if (g_prof_before && hipEventRecord(g_prof_before, stream) != hipSuccess) return TV_ERR_HIP;
   if (a.S > 1)
@@ -734,9 +810,26 @@ int launch(const AttnArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((attn_main<E, D, false>), dim3(n_items), dim3(kThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
   if (g_prof_after && hipEventRecord(g_prof_after, stream) != hipSuccess) return TV_ERR_HIP;
+  return TV_OK;
+}
+
+template <typename E, int D>
+int launch_attn(const AttnArgs& a, hipStream_t stream) {
+  const int rc = launch_main<E, D>(a, stream);
+  if (rc != TV_OK) return rc;
   if (a.S > 1)
-    hipLaunchKernelGGL((attn_combine<E, D>), dim3(a.B * a.Hkv * a.RB * (kRows * D / 4 / 256)),
-                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_combine<E, D>),
+                       dim3(a.B * a.Hkv * a.RB * combine_wgs_per_item<E, D>()), dim3(256), 0,
+                       stream, a);
+  return launch_status();
+}
+
+template <typename E, int D>
+int launch_step(const AttnArgs& a, TailArgs t, hipStream_t stream) {
+  const int rc = launch_main<E, D>(a, stream);
+  if (rc != TV_OK) return rc;
+  t.n_comb = a.S > 1 ? a.B * a.Hkv * a.RB * combine_wgs_per_item<E, D>() : 0;
+  hipLaunchKernelGGL((step_tail<E, D>), dim3(t.n_comb + a.B), dim3(256), 0, stream, a, t);
   return launch_status();
 }
 
@@ -780,21 +873,21 @@ extern "C" size_t tree_verify_attn_workspace_size(int B, int T, int Hq, int Hkv,
   return make_plan(B, T, Hq, Hkv, D, Lmax, dtype == TV_BF16 ? 2 : 4, split_keys).ws_bytes;
 }
 
-extern "C" int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
-                                const int32_t* cache_len, const void* k_tree, const void* v_tree,
-                                const uint64_t* anc_mask, void* out, float* lse, int32_t* status,
-                                int B, int T, int Hq, int Hkv, int D, int Lmax, int dtype,
-                                float scale, int split_keys, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+// Checks the attention arguments and fills `a`; returns TV_OK or the error to report.
+static int prepare_attn(AttnArgs& a, Plan& p, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* cache_len, const void* k_tree,
+                        const void* v_tree, const uint64_t* anc_mask, void* out, float* lse,
+                        int32_t* status, int B, int T, int Hq, int Hkv, int D, int Lmax,
+                        int dtype, float scale, int split_keys, void* workspace,
+                        size_t workspace_bytes) {
   if (!q || !k_cache || !v_cache || !cache_len || !k_tree || !v_tree || !anc_mask || !out ||
       !attn_shapes_ok(B, T, Hq, Hkv, Lmax) || split_keys < 0)
     return TV_ERR_INVALID_ARG;
   if ((dtype != TV_F32 && dtype != TV_BF16) || (D != 64 && D != 128)) return TV_ERR_UNSUPPORTED;
-  const Plan p = make_plan(B, T, Hq, Hkv, D, Lmax, dtype == TV_BF16 ? 2 : 4, split_keys);
+  p = make_plan(B, T, Hq, Hkv, D, Lmax, dtype == TV_BF16 ? 2 : 4, split_keys);
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return TV_ERR_WORKSPACE;
   if ((long long)B * Hkv * p.RB * p.S >= (1LL << 31)) return TV_ERR_INVALID_ARG;
 
-  AttnArgs a;
   a.q = (const char*)q;
   a.kc = (const char*)k_cache;
   a.vc = (const char*)v_cache;
@@ -818,13 +911,99 @@ extern "C" int tree_verify_attn(const void* q, const void* k_cache, const void* 
   a.chunk_tiles = p.chunk_tiles;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
   a.c = sc * kLog2e;
+  const int elem = dtype == TV_BF16 ? 2 : 4;
   char* ws = (char*)workspace;
+  const size_t slots = (size_t)B * Hkv * p.RB * p.S;
   a.part_o = ws;
-  a.part_ml = p.ws_bytes ? (float*)(ws + (size_t)B * Hkv * p.RB * p.S * kRows * D *
-                                              (dtype == TV_BF16 ? 2 : 4))
-                         : nullptr;
+  a.part_ml = p.ws_bytes ? (float*)(ws + slots * kRows * D * elem) : nullptr;
+  a.nsplit = p.ws_bytes ? (int32_t*)(ws + slots * kRows * ((size_t)D * elem + 8)) : nullptr;
+  return TV_OK;
+}
 
+extern "C" int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* cache_len, const void* k_tree, const void* v_tree,
+                                const uint64_t* anc_mask, void* out, float* lse, int32_t* status,
+                                int B, int T, int Hq, int Hkv, int D, int Lmax, int dtype,
+                                float scale, int split_keys, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  AttnArgs a;
+  Plan p;
+  const int rc = prepare_attn(a, p, q, k_cache, v_cache, cache_len, k_tree, v_tree, anc_mask,
+                              out, lse, status, B, T, Hq, Hkv, D, Lmax, dtype, scale, split_keys,
+                              workspace, workspace_bytes);
+  if (rc != TV_OK) return rc;
   hipStream_t st = (hipStream_t)stream;
-  if (dtype == TV_BF16) return D == 128 ? launch<__bf16, 128>(a, st) : launch<__bf16, 64>(a, st);
-  return D == 128 ? launch<float, 128>(a, st) : launch<float, 64>(a, st);
+  if (dtype == TV_BF16)
+    return D == 128 ? launch_attn<__bf16, 128>(a, st) : launch_attn<__bf16, 64>(a, st);
+  return D == 128 ? launch_attn<float, 128>(a, st) : launch_attn<float, 64>(a, st);
+}
+
+// True when byte ranges [a, a + na) and [b, b + nb) intersect.
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+extern "C" int tree_verify_step(const int32_t* parent, const int32_t* draft_tok,
+                                const int32_t* target_tok, const void* q, void* k_cache,
+                                void* v_cache, const int32_t* cache_len, int32_t* cache_len_out,
+                                const void* k_tree, const void* v_tree, uint64_t* anc_mask,
+                                void* out, float* lse, int32_t* accept_path, int32_t* accept_len,
+                                int32_t* bonus_tok, int32_t* status, int B, int T, int Hq,
+                                int Hkv, int D, int Lmax, int dtype, float scale,
+                                int split_keys, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (!parent || !draft_tok || !target_tok || !cache_len_out || !accept_path || !accept_len ||
+      !bonus_tok || !status)
+    return TV_ERR_INVALID_ARG;
+  AttnArgs a;
+  Plan p;
+  int rc = prepare_attn(a, p, q, k_cache, v_cache, cache_len, k_tree, v_tree, anc_mask, out, lse,
+                        status, B, T, Hq, Hkv, D, Lmax, dtype, scale, split_keys, workspace,
+                        workspace_bytes);
+  if (rc != TV_OK) return rc;
+  if (cache_len_out != cache_len &&
+      overlaps(cache_len_out, (size_t)B * 4, cache_len, (size_t)B * 4))
+    return TV_ERR_INVALID_ARG;
+  // 1. ancestor masks (writes status)
+  rc = tree_build_mask(parent, B, T, anc_mask, status, stream);
+  if (rc != TV_OK) return rc;
+  const size_t elem = dtype == TV_BF16 ? 2 : 4;
+  const size_t cache_bytes = (size_t)B * Hkv * Lmax * D * elem;
+  const size_t tree_bytes = (size_t)B * T * Hkv * D * elem;
+  if (overlaps(k_tree, tree_bytes, k_cache, cache_bytes) ||
+      overlaps(k_tree, tree_bytes, v_cache, cache_bytes) ||
+      overlaps(v_tree, tree_bytes, k_cache, cache_bytes) ||
+      overlaps(v_tree, tree_bytes, v_cache, cache_bytes)) {
+    // Tree rows inside the cache: the compaction must stage rows (kv_compact_accepted).
+    rc = tree_verify_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, anc_mask, out, lse,
+                          status, B, T, Hq, Hkv, D, Lmax, dtype, scale, split_keys, workspace,
+                          workspace_bytes, stream);
+    if (rc != TV_OK) return rc;
+    rc = tree_accept(anc_mask, draft_tok, target_tok, B, T, accept_path, accept_len, bonus_tok,
+                     stream);
+    if (rc != TV_OK) return rc;
+    return kv_compact_accepted(k_cache, v_cache, cache_len, cache_len_out, k_tree, v_tree,
+                               accept_path, accept_len, B, T, Hkv, D, Lmax, dtype, status,
+                               stream);
+  }
+  // 2. attention main kernel, 3. merge + acceptance + compaction
+  TailArgs t;
+  t.anc = anc_mask;
+  t.draft = draft_tok;
+  t.target = target_tok;
+  t.accept_path = accept_path;
+  t.accept_len = accept_len;
+  t.bonus_tok = bonus_tok;
+  t.kc = (char*)k_cache;
+  t.vc = (char*)v_cache;
+  t.cache_len_out = cache_len_out;
+  t.status = status;
+  t.n_comb = 0;
+  t.W = ceil_div(T, 64);
+  t.row_bytes = D * (int)elem;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == TV_BF16)
+    return D == 128 ? launch_step<__bf16, 128>(a, t, st) : launch_step<__bf16, 64>(a, t, st);
+  return D == 128 ? launch_step<float, 128>(a, t, st) : launch_step<float, 64>(a, t, st);
 }

@@ -1,0 +1,123 @@
+// Device code shared by the acceptance kernel and the fused verification-step tail: the
+// greedy acceptance walk over one sequence's tree, run by one wavefront.  Not part of the ABI.
+#pragma once
+
+#include "tv_internal.h"
+
+namespace tv {
+
+__device__ inline uint64_t bit64(int j) { return (uint64_t)1 << (j & 63); }
+
+// Bits [0, n) of a two-word mask (n in [0, 128]).
+__device__ inline void low_bits(int n, uint64_t& lo, uint64_t& hi) {
+  lo = n >= 64 ? ~0ull : (n <= 0 ? 0ull : bit64(n) - 1);
+  hi = n >= 128 ? ~0ull : (n <= 64 ? 0ull : bit64(n - 64) - 1);
+}
+
+__device__ inline int wave_max(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+__device__ inline uint64_t shfl64(uint64_t v, int src) {
+  const int lo = __shfl((int)(uint32_t)v, src, 64);
+  const int hi = __shfl((int)(uint32_t)(v >> 32), src, 64);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Acceptance walk of sequence b by the calling wavefront (all 64 lanes, lane = threadIdx % 64):
+// ok[c] = (c is the root) or draft[c] == target[parent(c)], with parent(c) the highest set bit
+// of anc[c] below c.  A node is accepted iff its whole mask lies inside the ok ballot.  The
+// deepest accepted node wins (popcount of its mask), ties to the smaller index.  Writes
+// accept_path / accept_len / bonus_tok of b; if s_path is not null the path (root first) also
+// goes there.  Returns accept_len.
+//
+// All global loads (mask rows, draft and target tokens of the lane's two nodes) are issued
+// together; the parent's target token and the winner's mask row then come from other lanes by
+// shuffles, so the walk makes one round trip to memory before its writes.
+__device__ inline int accept_walk(int b, int T, int W, const uint64_t* __restrict__ anc,
+                                  const int32_t* __restrict__ draft,
+                                  const int32_t* __restrict__ target,
+                                  int32_t* __restrict__ accept_path,
+                                  int32_t* __restrict__ accept_len,
+                                  int32_t* __restrict__ bonus_tok, int* s_path) {
+  const int lane = threadIdx.x & 63;
+  const size_t base = (size_t)b * T;
+  uint64_t in_lo, in_hi;  // bits of real nodes: garbage above T is ignored
+  low_bits(T, in_lo, in_hi);
+
+  uint64_t a0[2], a1[2];
+  int dr[2], tg[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    a0[k] = a1[k] = 0;
+    dr[k] = tg[k] = 0;
+    if (c < T) {
+      const uint64_t* row = anc + (base + c) * W;
+      a0[k] = row[0] & in_lo;
+      a1[k] = (W == 2 ? row[1] : 0) & in_hi;
+      dr[k] = draft[base + c];
+      tg[k] = target[base + c];
+    }
+  }
+  bool ok[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    uint64_t blo, bhi;  // strictly below c
+    low_bits(c, blo, bhi);
+    const uint64_t m0 = a0[k] & blo, m1 = a1[k] & bhi;
+    const int p = m1 ? 64 + 63 - __clzll(m1) : (m0 ? 63 - __clzll(m0) : -1);
+    // target token of node p, held by lane p % 64 in slot p / 64 (every lane takes part)
+    const int pp = max(p, 0);
+    const int t0 = __shfl(tg[0], pp & 63, 64), t1 = __shfl(tg[1], pp & 63, 64);
+    const int tp = pp >= 64 ? t1 : t0;
+    ok[k] = c < T && ((c == 0) || (p >= 0 && dr[k] == tp));
+  }
+  const uint64_t ok_lo = __ballot(ok[0]);
+  const uint64_t ok_hi = __ballot(ok[1]);
+
+  int key = -1;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    if (c < T && (a0[k] & ~ok_lo) == 0 && (a1[k] & ~ok_hi) == 0) {
+      const int depth = __popcll(a0[k]) + __popcll(a1[k]);
+      key = max(key, (depth << 8) | (255 - c));
+    }
+  }
+  key = wave_max(key);
+  const int best = key >= 0 ? 255 - (key & 255) : 0;
+
+  // the winner's mask row and target token, from lane best % 64, slot best / 64
+  const int src = best & 63;
+  const bool hi_slot = best >= 64;
+  const uint64_t b0 = hi_slot ? shfl64(a0[1], src) : shfl64(a0[0], src);
+  const uint64_t b1 = hi_slot ? shfl64(a1[1], src) : shfl64(a1[0], src);
+  const int bonus = hi_slot ? __shfl(tg[1], src, 64) : __shfl(tg[0], src, 64);
+  const int n = __popcll(b0) + __popcll(b1);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    if (c < T) {
+      const bool on_path = k == 0 ? ((b0 >> c) & 1) : ((b1 >> (c - 64)) & 1);
+      if (on_path) {
+        uint64_t blo, bhi;
+        low_bits(c, blo, bhi);
+        const int pos = __popcll(b0 & blo) + __popcll(b1 & bhi);
+        accept_path[base + pos] = c;
+        if (s_path) s_path[pos] = c;
+      }
+      if (c >= n) accept_path[base + c] = -1;
+    }
+  }
+  if (lane == 0) {
+    accept_len[b] = n;
+    bonus_tok[b] = bonus;
+  }
+  return n;
+}
+
+}  // namespace tv
