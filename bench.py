@@ -48,6 +48,10 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=40)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     p.add_argument("--split-keys", type=int, default=0, help="prefix keys per split (0 = auto)")
+    p.add_argument("--graph-steps", type=int, default=0,
+                   help="consecutive steps captured in one HIP graph, cycling the input sets "
+                        "as the layers of a model would (0 = auto: the smallest multiple of the "
+                        "set count that is >= 8)")
     p.add_argument("--api", choices=("fused", "separate"), default="fused",
                    help="time the step through tree_verify_step (three launches) or through the "
                         "four separate entry points; the other is timed too and reported")
@@ -318,31 +322,45 @@ def main() -> int:
     stream = torch.cuda.Stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
 
+    graph_steps = args.graph_steps or n_sets * math.ceil(8 / n_sets)
+
     def time_api(api):
-        """W untimed steps, then exactly K timed steps through `api`; (ms per step, wall s)."""
+        """W untimed steps, then exactly K timed steps through `api`; (ms per step, wall s).
+
+        In graph mode a graph holds `graph_steps` consecutive steps on input sets 0, 1, ...
+        (cycling); a run of k steps replays whole graphs, then one graph of the remainder."""
         for s in sets:
             s.api = api
-        graphs = None
+        graphs = {}
+
+        def graph_of(n):
+            if n not in graphs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                    for i in range(n):
+                        sets[i % n_sets].step(cs)
+                graphs[n] = g
+            return graphs[n]
+
         if args.mode == "graph":
-            graphs = []
             with torch.cuda.stream(stream):
                 for s in sets:  # one eager step first so lazy initialisation is outside capture
                     s.step(sptr)
             stream.synchronize()
-            for s in sets:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    s.step(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-                graphs.append(g)
+            for n in {graph_steps, args.warmup % graph_steps, args.steps % graph_steps} - {0}:
+                graph_of(n)
             torch.cuda.synchronize()
 
-        def run_steps(k, offset=0):
-            for i in range(k):
-                j = (offset + i) % n_sets
-                if graphs is not None:
-                    graphs[j].replay()
-                else:
-                    sets[j].step(sptr)
+        def run_steps(k):
+            if args.mode == "graph":
+                for _ in range(k // graph_steps):
+                    graphs[graph_steps].replay()
+                if k % graph_steps:
+                    graphs[k % graph_steps].replay()
+            else:
+                for i in range(k):
+                    sets[i % n_sets].step(sptr)
 
         with torch.cuda.stream(stream):
             run_steps(args.warmup)
@@ -351,7 +369,7 @@ def main() -> int:
             torch.cuda.synchronize()
             t_wall = time.perf_counter()
             e0.record(stream)
-            run_steps(args.steps, offset=args.warmup)
+            run_steps(args.steps)
             e1.record(stream)
             e1.synchronize()
             t_wall = time.perf_counter() - t_wall
@@ -364,12 +382,17 @@ def main() -> int:
     t_step = ms_per_step * 1e-3
 
     # ---- per-call durations: a separate eager pass with events between the calls -------------
+    # Events between eager calls include launch latency; the main kernel's own duration comes
+    # from the library's profiling hook, whose events take that kernel's start and end
+    # timestamps (hipExtLaunchKernel).
     n_prof = min(args.steps, 200)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_prof)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_prof)]
     for row in ev:  # torch creates the underlying events on first record
         for e in row:
             e.record(stream)
     stream.synchronize()
+    for s in sets:
+        s.api = "separate"
     with torch.cuda.stream(stream):
         for i in range(n_prof):
             s = sets[i % n_sets]
@@ -383,17 +406,36 @@ def main() -> int:
             s.accept(sptr)
             ei[5].record(stream)
             s.compact(sptr)
+            ei[6].record(stream)
         tv.profile_attn_main(None, None)
-        end = torch.cuda.Event(enable_timing=True)
-        end.record(stream)
-        end.synchronize()
+        stream.synchronize()
 
     def avg(a, b):
         return float(np.mean([ev[i][a].elapsed_time(ev[i][b]) for i in range(n_prof)])) * 1e-3
 
-    t_mask, t_attn, t_main, t_accept = avg(0, 1), avg(1, 4), avg(2, 3), avg(4, 5)
-    t_compact = float(np.mean([ev[i][5].elapsed_time(ev[i + 1][0]) for i in range(n_prof - 1)]
-                              + [ev[-1][5].elapsed_time(end)])) * 1e-3
+    t_mask, t_attn, t_main, t_accept, t_compact = avg(0, 1), avg(1, 4), avg(2, 3), avg(4, 5), avg(5, 6)
+
+    # the same for the fused step: its main kernel (which also builds the masks) and the whole
+    # call (main kernel, then merge + acceptance + compaction)
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_prof)]
+    for row in evf:
+        for e in row:
+            e.record(stream)
+    stream.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(n_prof):
+            s = sets[i % n_sets]
+            ei = evf[i]
+            tv.profile_attn_main(ei[1], ei[2])
+            ei[0].record(stream)
+            s.fused(sptr)
+            ei[3].record(stream)
+        tv.profile_attn_main(None, None)
+        stream.synchronize()
+    t_main_fused = float(np.mean([evf[i][1].elapsed_time(evf[i][2]) for i in range(n_prof)])) * 1e-3
+    t_fused_call = float(np.mean([evf[i][0].elapsed_time(evf[i][3]) for i in range(n_prof)])) * 1e-3
+    if args.api == "fused":
+        t_main = t_main_fused
 
     alen = sets[0].t["alen"].cpu().numpy()
     status = sets[0].t["status"].cpu().numpy()
@@ -419,7 +461,8 @@ def main() -> int:
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
-    roof["kernel"] = "attn_main"
+    roof["kernel"] = ("attn_main (tree_verify_step's instantiation, which also builds the masks)"
+                      if args.api == "fused" else "attn_main")
     roof["kernel_us"] = t_main * 1e6
     roof["algorithmic_bytes"] = kv_bytes
     roof["algorithmic_flops"] = flops
@@ -441,7 +484,8 @@ def main() -> int:
         "config": {"workload": args.workload, "desc": w.spec.desc, "B": w.B, "T": w.T,
                    "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "prefix_tokens": int(L.sum()),
                    "Lmax": w.Lmax, "layers": 1, "mode": args.mode, "rotated_sets": n_sets,
-                   "split_keys": args.split_keys, "step_api": args.api},
+                   "split_keys": args.split_keys, "step_api": args.api,
+                   "graph_steps": graph_steps if args.mode == "graph" else None},
         "ms_per_step_by_api": {args.api: ms_per_step, other: ms_other},
         "hbm_frac": value / HBM_PEAK_GBS,
         "attn_kv_gbps": kv_bytes / t_attn / 1e9,
@@ -450,8 +494,10 @@ def main() -> int:
         "tree_tokens_per_s": w.B * w.T / t_step,
         "accepted_tokens_per_s": float(alen.sum()) / t_step,
         "step_breakdown_us": {"tree_build_mask": t_mask * 1e6, "tree_verify_attn": t_attn * 1e6,
-                              "attn_main": t_main * 1e6, "tree_accept": t_accept * 1e6,
+                              "attn_main": avg(2, 3) * 1e6, "tree_accept": t_accept * 1e6,
                               "kv_compact_accepted": t_compact * 1e6},
+        "fused_step_breakdown_us": {"tree_verify_step": t_fused_call * 1e6,
+                                    "attn_main_with_masks": t_main_fused * 1e6},
         "wall_s_timed": t_wall,
         "roofline": roof,
     }

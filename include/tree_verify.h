@@ -114,11 +114,12 @@ int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
 
 /*
  * tv_profile_attn_main — profiling hook for the attention main kernel.
- * While set, every tree_verify_attn call records `ev_before` (a hipEvent_t) on its stream just
- * before launching its main kernel and `ev_after` just after it, i.e. before the split-K merge,
- * so the main kernel's duration can be read with hipEventElapsedTime.  Pass NULL, NULL to turn
- * it off.  Process-wide setting, not synchronised: set it while no other thread calls
- * tree_verify_attn.  Returns TV_ERR_INVALID_ARG if exactly one event is NULL.
+ * While set, every tree_verify_attn and tree_verify_step call launches its main kernel with
+ * hipExtLaunchKernel so that `ev_before` and `ev_after` (hipEvent_t) take that kernel's own
+ * start and end timestamps; hipEventElapsedTime then gives the main kernel's duration alone
+ * (not the split-K merge, not the launch).  Pass NULL, NULL to turn it off.  Process-wide
+ * setting, not synchronised: set it while no other thread calls either function.  Returns
+ * TV_ERR_INVALID_ARG if exactly one event is NULL.
  */
 int tv_profile_attn_main(void* ev_before, void* ev_after);
 

@@ -31,6 +31,7 @@
 //     as long as no lane's block sum exceeds 1024; only then is the block max taken, m raised
 //     and O rescaled.
 //   * fp32 inputs use v_mfma_f32_32x32x2_f32 and run the blocks one after the other.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -63,7 +64,8 @@ struct AttnArgs {
   const int32_t* cache_len;
   const char* kt;
   const char* vt;
-  const uint64_t* anc;
+  const uint64_t* anc;      // ancestor masks, or (masks built in the kernel) their output
+  const int32_t* parent;    // parent array when the kernel builds the masks itself
   char* out;
   float* lse;
   int32_t* status;
@@ -160,7 +162,88 @@ struct PBlock<false> {
   float v[16];  // element e of the S^T accumulator
 };
 
-template <typename E, int D, bool kSplit>
+// Ancestor masks of sequence b built by wavefront 0 from the parent array (pointer jumping over
+// wavefront shuffles): node c = lane + 64*k lives in lane c % 64, slot k.  Each node keeps the
+// set of its ancestors closer than 2^r and a pointer to the ancestor at distance 2^r; one round
+// merges the pointed-to node's set and doubles the pointer, every lane reading the others' old
+// values.  A tree that is not level-ordered with one root gets only each node's own bit (as
+// tree_build_mask).  par[k] is parent[b, lane + 64*k].  Writes the masks to s_anc (and to
+// anc_out when not null); returns whether the tree was bad.
+__device__ inline bool build_masks_wave(const int (&par)[2], int b, int T,
+                                        uint64_t (*s_anc)[2], uint64_t* anc_out) {
+  const int lane = threadIdx.x & 63;
+  const int W = T > 64 ? 2 : 1;
+  uint64_t lo[2], hi[2];
+  int ptr[2];
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    lo[k] = hi[k] = 0;
+    ptr[k] = -1;
+    if (c < T) {
+      const int p = par[k];
+      const bool ok = c == 0 ? p == -1 : (p >= 0 && p < c);
+      bad |= !ok;
+      ptr[k] = (c > 0 && ok) ? p : -1;
+      lo[k] = k == 0 ? bit64(c) : 0;
+      hi[k] = k == 1 ? bit64(c) : 0;
+    }
+  }
+  bad = __ballot(bad) != 0;
+  for (int span = 1; span < T; span <<= 1) {
+    uint64_t nlo[2], nhi[2];
+    int nptr[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      // every lane takes part in every shuffle; the result is kept only where ptr >= 0
+      const int src = max(ptr[k], 0);
+      const int sl = src & 63;
+      const bool s1 = src >= 64;
+      const uint64_t l0 = shfl64(lo[0], sl);
+      const int p0 = __shfl(ptr[0], sl, 64);
+      uint64_t plo = l0, phi = 0;
+      int pp = p0;
+      if (W == 2) {
+        const uint64_t l1 = shfl64(lo[1], sl), h0 = shfl64(hi[0], sl), h1 = shfl64(hi[1], sl);
+        const int p1 = __shfl(ptr[1], sl, 64);
+        plo = s1 ? l1 : l0;
+        phi = s1 ? h1 : h0;
+        pp = s1 ? p1 : p0;
+      }
+      const bool follow = ptr[k] >= 0;
+      nlo[k] = follow ? (lo[k] | plo) : lo[k];
+      nhi[k] = follow ? (hi[k] | phi) : hi[k];
+      nptr[k] = follow ? pp : ptr[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      lo[k] = nlo[k];
+      hi[k] = nhi[k];
+      ptr[k] = nptr[k];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    if (c < T) {
+      if (bad) {
+        lo[k] = k == 0 ? bit64(c) : 0;
+        hi[k] = k == 1 ? bit64(c) : 0;
+      }
+      s_anc[c][0] = lo[k];
+      s_anc[c][1] = hi[k];
+      if (anc_out) {
+        uint64_t* row = anc_out + ((size_t)b * T + c) * W;
+        row[0] = lo[k];
+        if (W == 2) row[1] = hi[k];
+      }
+    }
+  }
+  return bad;
+}
+
+template <typename E, int D, bool kSplit, bool kMasks>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2)))
 void attn_main(AttnArgs a) {
@@ -186,7 +269,9 @@ void attn_main(AttnArgs a) {
 
   const int L_raw = a.cache_len[b];
   const int L = min(max(L_raw, 0), a.Lmax);
-  if (a.status && (L_raw < 0 || L_raw > a.Lmax) && kvh == 0 && s == 0 && rb == 0 && tid == 0)
+  // one workgroup per sequence reports its status (and, building masks, writes them)
+  const bool writer = kvh == 0 && s == 0 && rb == 0;
+  if (!kMasks && a.status && (L_raw < 0 || L_raw > a.Lmax) && writer && tid == 0)
     atomicOr(a.status + b, TV_BAD_LEN);
   // Chunks are cut from the sequence's tiles in the order tree tiles, then prefix tiles, so
   // the chunk that carries the tree does no more work than the others.
@@ -276,10 +361,21 @@ void attn_main(AttnArgs a) {
   }
   // ancestor mask words of the lane's row (padding rows see only the root)
   uint64_t mk0 = 1, mk1 = 0;
-  if (row_ok && n_tree_tiles) {
+  if (!kMasks && row_ok && n_tree_tiles) {
     const uint64_t* mrow = a.anc + ((size_t)b * a.T + row_t) * a.W;
     mk0 = mrow[0];
     mk1 = a.W > 1 ? mrow[1] : 0;
+  }
+  // Masks built here: wavefront 0 of every workgroup that reads tree keys, and of the
+  // sequence's writer, runs the pointer jumping once its tile loads have landed; the other
+  // wavefronts read their rows' masks after the first tile barrier.
+  __shared__ uint64_t s_anc[kMasks ? kMaxT : 1][2];
+  const bool need_masks = kMasks && (n_tree_tiles > 0 || writer);
+  int par[2] = {-1, -1};
+  if (need_masks && wave == 0) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (lane + 64 * k < a.T) par[k] = a.parent[(size_t)b * a.T + lane + 64 * k];
   }
 
   // ---- per-lane LDS fragment offsets (bytes within a K or V tile) --------------------------
@@ -302,6 +398,14 @@ void attn_main(AttnArgs a) {
   }
 
   vm_wait<0>();
+  if constexpr (kMasks) {
+    if (need_masks && wave == 0) {
+      const bool bad = build_masks_wave(par, b, a.T, s_anc,
+                                        writer ? const_cast<uint64_t*>(a.anc) : nullptr);
+      if (writer && lane == 0 && a.status)
+        a.status[b] = (bad ? TV_BAD_TREE : 0) | ((L_raw < 0 || L_raw > a.Lmax) ? TV_BAD_LEN : 0);
+    }
+  }
 
   // ---- accumulators and running statistics -------------------------------------------------
   f32x16 oacc[kDB];
@@ -501,8 +605,17 @@ void attn_main(AttnArgs a) {
   // Se / Pe, odd blocks' in So / Po.
   f32x16 Se, So;
   PBlock<kBF16> Pe, Po;
+  auto masks_from_lds = [&]() {
+    if constexpr (kMasks) {
+      if (row_ok && n_tree_tiles) {
+        mk0 = s_anc[row_t][0];
+        mk1 = s_anc[row_t][1];
+      }
+    }
+  };
   if constexpr (Lay::kCrossTile) {
     barrier_tile(0);
+    masks_from_lds();
     set_k(0);
     qk(0, Se);
     mask_block(0, Se);
@@ -541,6 +654,7 @@ void attn_main(AttnArgs a) {
   } else {
     for (int t = 0; t < n_tiles; ++t) {
       barrier_tile(t);
+      if (t == 0) masks_from_lds();
       set_k(t);
       set_v(t);
 #pragma unroll
@@ -800,17 +914,18 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int elem_bytes, i
 // Profiling events recorded around the main kernel (tv_profile_attn_main).
 hipEvent_t g_prof_before = nullptr, g_prof_after = nullptr;
 
-template <typename E, int D>
+template <typename E, int D, bool kMasks = false>
 int launch_main(const AttnArgs& a, hipStream_t stream) {
   const int n_items = a.B * a.Hkv * a.S * a.RB;
-  if (g_prof_before && hipEventRecord(g_prof_before, stream) != hipSuccess) return TV_ERR_HIP;
-  if (a.S > 1)
-    hipLaunchKernelGGL((attn_main<E, D, true>), dim3(n_items), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_main<E, D, false>), dim3(n_items), dim3(kThreads), 0, stream, a);
-  if (hipGetLastError() != hipSuccess) return TV_ERR_HIP;
-  if (g_prof_after && hipEventRecord(g_prof_after, stream) != hipSuccess) return TV_ERR_HIP;
-  return TV_OK;
+  auto kernel = a.S > 1 ? attn_main<E, D, true, kMasks> : attn_main<E, D, false, kMasks>;
+  if (g_prof_before) {
+    // the events take the kernel's own start and end timestamps
+    hipExtLaunchKernelGGL(kernel, dim3(n_items), dim3(kThreads), 0, stream, g_prof_before,
+                          g_prof_after, 0, a);
+  } else {
+    hipLaunchKernelGGL(kernel, dim3(n_items), dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
 template <typename E, int D>
@@ -826,7 +941,7 @@ int launch_attn(const AttnArgs& a, hipStream_t stream) {
 
 template <typename E, int D>
 int launch_step(const AttnArgs& a, TailArgs t, hipStream_t stream) {
-  const int rc = launch_main<E, D>(a, stream);
+  const int rc = launch_main<E, D, true>(a, stream);
   if (rc != TV_OK) return rc;
   t.n_comb = a.S > 1 ? a.B * a.Hkv * a.RB * combine_wgs_per_item<E, D>() : 0;
   hipLaunchKernelGGL((step_tail<E, D>), dim3(t.n_comb + a.B), dim3(256), 0, stream, a, t);
@@ -895,6 +1010,7 @@ static int prepare_attn(AttnArgs& a, Plan& p, const void* q, const void* k_cache
   a.kt = (const char*)k_tree;
   a.vt = (const char*)v_tree;
   a.anc = anc_mask;
+  a.parent = nullptr;
   a.out = (char*)out;
   a.lse = lse;
   a.status = status;
@@ -965,9 +1081,6 @@ extern "C" int tree_verify_step(const int32_t* parent, const int32_t* draft_tok,
   if (cache_len_out != cache_len &&
       overlaps(cache_len_out, (size_t)B * 4, cache_len, (size_t)B * 4))
     return TV_ERR_INVALID_ARG;
-  // 1. ancestor masks (writes status)
-  rc = tree_build_mask(parent, B, T, anc_mask, status, stream);
-  if (rc != TV_OK) return rc;
   const size_t elem = dtype == TV_BF16 ? 2 : 4;
   const size_t cache_bytes = (size_t)B * Hkv * Lmax * D * elem;
   const size_t tree_bytes = (size_t)B * T * Hkv * D * elem;
@@ -976,6 +1089,8 @@ extern "C" int tree_verify_step(const int32_t* parent, const int32_t* draft_tok,
       overlaps(v_tree, tree_bytes, k_cache, cache_bytes) ||
       overlaps(v_tree, tree_bytes, v_cache, cache_bytes)) {
     // Tree rows inside the cache: the compaction must stage rows (kv_compact_accepted).
+    rc = tree_build_mask(parent, B, T, anc_mask, status, stream);
+    if (rc != TV_OK) return rc;
     rc = tree_verify_attn(q, k_cache, v_cache, cache_len, k_tree, v_tree, anc_mask, out, lse,
                           status, B, T, Hq, Hkv, D, Lmax, dtype, scale, split_keys, workspace,
                           workspace_bytes, stream);
@@ -987,7 +1102,8 @@ extern "C" int tree_verify_step(const int32_t* parent, const int32_t* draft_tok,
                                accept_path, accept_len, B, T, Hkv, D, Lmax, dtype, status,
                                stream);
   }
-  // 2. attention main kernel, 3. merge + acceptance + compaction
+  // attention main kernel (building the ancestor masks), then merge + acceptance + compaction
+  a.parent = parent;
   TailArgs t;
   t.anc = anc_mask;
   t.draft = draft_tok;
