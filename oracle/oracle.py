@@ -57,6 +57,10 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_tree_paths.restype = i
     lib.oracle_build_mask.argtypes = [P, i, i, P, P]
     lib.oracle_build_mask.restype = None
+    lib.oracle_paged_gather.argtypes = [i, P, P, i, P, i, i, P, P, i, i, i, i, i, P, P, P, P]
+    lib.oracle_paged_gather.restype = i
+    lib.oracle_commit_paged.argtypes = [P, i, P, P, P, P, P, i, i, i, P, P, P]
+    lib.oracle_commit_paged.restype = None
     lib.oracle_attention.argtypes = [i, P, P, P, P, P, P, P, i, i, i, i, i, i, ctypes.c_double,
                                      P, ctypes.c_long, P, P, i]
     lib.oracle_attention.restype = i
@@ -171,3 +175,62 @@ def compact(k_cache, v_cache, cache_len, k_tree, v_tree, accept_path, accept_len
                        _p(out_len), _p(k_tree), _p(v_tree), _p(accept_path), _p(accept_len),
                        B, T, Hkv, D, Lmax, _p(st))
     return out_len, st
+
+
+def paged_gather(k_pool, v_pool, table, page_size, cache_len, tree_slot, Lmax, fill=np.nan,
+                 lib=None):
+    """Dense copies (k_cache, v_cache [B,Hkv,Lmax,D], k_tree, v_tree [B,T,Hkv,D]) of the rows a
+    paged cache names; cache rows past each prefix hold ``fill`` (bf16 pools: the NaN pattern)."""
+    lib = lib or load()
+    k_pool = np.ascontiguousarray(k_pool)
+    v_pool = np.ascontiguousarray(v_pool, dtype=k_pool.dtype)
+    table, cache_len, tree_slot = _i32(table), _i32(cache_len), _i32(tree_slot)
+    num_slots, Hkv, D = k_pool.shape
+    B, max_pages = table.shape
+    T = tree_slot.shape[1]
+    if k_pool.dtype == np.uint16:
+        nan = np.uint16(0x7FC0)
+        k_cache = np.full((B, Hkv, Lmax, D), nan, np.uint16)
+    else:
+        k_cache = np.full((B, Hkv, Lmax, D), fill, k_pool.dtype)
+    v_cache = k_cache.copy()
+    k_tree = np.empty((B, T, Hkv, D), k_pool.dtype)
+    v_tree = np.empty_like(k_tree)
+    rc = lib.oracle_paged_gather(k_pool.dtype.itemsize, _p(k_pool), _p(v_pool), num_slots,
+                                 _p(table), max_pages, int(page_size), _p(cache_len),
+                                 _p(tree_slot), B, T, Hkv, D, int(Lmax), _p(k_cache), _p(v_cache),
+                                 _p(k_tree), _p(v_tree))
+    if rc != 0:
+        raise ValueError("a table entry or tree slot names a slot outside the pool")
+    return k_cache, v_cache, k_tree, v_tree
+
+
+def paged_attention(q, k_pool, v_pool, table, page_size, cache_len, tree_slot, parent,
+                    scale=None, rows=None, n_threads=None, lib=None):
+    """Tree attention over a paged cache: attention over the rows the table names."""
+    cache_len = _i32(cache_len)
+    Lmax = max(1, int(cache_len.max(initial=0)))
+    kc, vc, kt, vt = paged_gather(k_pool, v_pool, table, page_size, cache_len, tree_slot, Lmax,
+                                  lib=lib)
+    return attention(q, kc, vc, cache_len, kt, vt, parent, scale=scale, rows=rows,
+                     n_threads=n_threads, lib=lib)
+
+
+def commit_paged(table, cache_len, tree_slot, accept_path, accept_len, num_slots, free_slots,
+                 free_top, status=None, lib=None):
+    """Pointer-swap commit on host copies (pages of one token): updates ``table``,
+    ``free_slots`` and returns (cache_len_out, free_top, status)."""
+    lib = lib or load()
+    assert table.dtype == np.int32 and table.flags.c_contiguous
+    assert free_slots.dtype == np.int32 and free_slots.flags.c_contiguous
+    B, max_pages = table.shape
+    tree_slot, cache_len = _i32(tree_slot), _i32(cache_len)
+    accept_path, accept_len = _i32(accept_path), _i32(accept_len)
+    T = tree_slot.shape[1]
+    out_len = np.empty(B, np.int32)
+    top = np.array([free_top], np.int32)
+    st = np.zeros(B, np.int32) if status is None else status
+    lib.oracle_commit_paged(_p(table), max_pages, _p(cache_len), _p(out_len), _p(tree_slot),
+                            _p(accept_path), _p(accept_len), B, T, int(num_slots),
+                            _p(free_slots), _p(top), _p(st))
+    return out_len, int(top[0]), st

@@ -23,6 +23,14 @@
  *                  rainlin.net section 3.2).  Ties at equal depth go to the smallest index.
  *   compaction     the accepted path's K/V rows are appended to the cache after the prefix, in
  *                  path order, and nothing else is written (lesty.tech section 8).
+ *   paged KV       (lesty.tech section 8, PagedAttention blocks) the K/V rows live in a pool of
+ *                  token slots [num_slots, Hkv, D]; logical position p of sequence b is slot
+ *                  table[b][p / P] * P + p % P for pages of P tokens, and tree node j is slot
+ *                  tree_slot[b][j].  Attention over a paged cache is attention over the rows
+ *                  the table names: oracle_paged_gather copies them into the dense layout.
+ *                  Committing the accepted path by pointer swap makes the table's entries for
+ *                  positions L_b .. L_b+n-1 name the accepted nodes' slots, in path order, and
+ *                  returns the rejected nodes' slots to a free list; no row is copied.
  *
  * Floating inputs are either float32 (elem_bits = 32) or raw bfloat16 bit patterns
  * (elem_bits = 16), which are widened exactly.
@@ -334,4 +342,97 @@ void oracle_compact(int elem_bytes, void* k_cache, void* v_cache, const int32_t*
     cache_len_out[b] = L + n;
   }
   free(tmp);
+}
+
+
+/* ---- paged KV ------------------------------------------------------------------------------ */
+
+/* Dense copies of the rows a paged cache names: k_cache/v_cache [B,Hkv,Lmax,D] receive rows
+ * 0..L_b-1 of every sequence (other rows untouched), k_tree/v_tree [B,T,Hkv,D] the tree nodes'
+ * rows.  Returns 0, or -1 if an entry names a slot outside the pool (nothing is read there). */
+int oracle_paged_gather(int elem_bytes, const void* k_pool, const void* v_pool, int num_slots,
+                        const int32_t* table, int max_pages, int page_size,
+                        const int32_t* cache_len, const int32_t* tree_slot, int B, int T,
+                        int Hkv, int D, int Lmax, void* k_cache, void* v_cache, void* k_tree,
+                        void* v_tree) {
+  size_t row = (size_t)D * elem_bytes;
+  int rc = 0;
+  for (int b = 0; b < B; ++b) {
+    int L = cache_len[b];
+    for (int p = 0; p < L && p < Lmax; ++p) {
+      int page = table[(size_t)b * max_pages + p / page_size];
+      long slot = (long)page * page_size + p % page_size;
+      if (page < 0 || slot >= num_slots) {
+        rc = -1;
+        continue;
+      }
+      for (int h = 0; h < Hkv; ++h) {
+        size_t src = ((size_t)slot * Hkv + h) * row;
+        size_t dst = (((size_t)b * Hkv + h) * Lmax + p) * row;
+        memcpy((unsigned char*)k_cache + dst, (const unsigned char*)k_pool + src, row);
+        memcpy((unsigned char*)v_cache + dst, (const unsigned char*)v_pool + src, row);
+      }
+    }
+    for (int j = 0; j < T; ++j) {
+      int slot = tree_slot[(size_t)b * T + j];
+      if (slot < 0 || slot >= num_slots) {
+        rc = -1;
+        continue;
+      }
+      for (int h = 0; h < Hkv; ++h) {
+        size_t src = ((size_t)slot * Hkv + h) * row;
+        size_t dst = (((size_t)b * T + j) * Hkv + h) * row;
+        memcpy((unsigned char*)k_tree + dst, (const unsigned char*)k_pool + src, row);
+        memcpy((unsigned char*)v_tree + dst, (const unsigned char*)v_pool + src, row);
+      }
+    }
+  }
+  return rc;
+}
+
+/* Commit of the accepted path by pointer swap, pages of one token.  For every sequence, in
+ * order: the length, path and slots are checked (a failing sequence commits nothing and keeps
+ * its length, as oracle_compact); then table[b][L + k] = tree_slot[b][path[k]] for k < n, and
+ * the slots of the nodes not on the path are appended to free_slots in node order at
+ * *free_top, which advances by their number (entries at or past num_slots are not written). */
+void oracle_commit_paged(int32_t* table, int max_pages, const int32_t* cache_len,
+                         int32_t* cache_len_out, const int32_t* tree_slot,
+                         const int32_t* accept_path, const int32_t* accept_len, int B, int T,
+                         int num_slots, int32_t* free_slots, int32_t* free_top, int32_t* status) {
+  unsigned char* on_path = (unsigned char*)malloc((size_t)T);
+  for (int b = 0; b < B; ++b) {
+    int L = cache_len[b];
+    int n = accept_len[b];
+    int bits = 0;
+    if (L < 0 || L > max_pages) bits |= ORC_BAD_LEN;
+    memset(on_path, 0, (size_t)T);
+    if (n < 0 || n > T) {
+      bits |= ORC_BAD_PATH;
+    } else {
+      for (int k = 0; k < n; ++k) {
+        int j = accept_path[(size_t)b * T + k];
+        if (j < 0 || j >= T || on_path[j]) bits |= ORC_BAD_PATH;
+        else on_path[j] = 1;
+      }
+    }
+    for (int j = 0; j < T; ++j) {
+      int slot = tree_slot[(size_t)b * T + j];
+      if (slot < 0 || slot >= num_slots) bits |= ORC_BAD_PATH;
+    }
+    if (!bits && (long)L + n > max_pages) bits |= ORC_OVERFLOW;
+    status[b] |= bits;
+    if (bits) {
+      cache_len_out[b] = L;
+      continue;
+    }
+    for (int k = 0; k < n; ++k)
+      table[(size_t)b * max_pages + L + k] = tree_slot[(size_t)b * T + accept_path[(size_t)b * T + k]];
+    for (int j = 0; j < T; ++j) {
+      if (on_path[j]) continue;
+      int at = (*free_top)++;
+      if (at < num_slots) free_slots[at] = tree_slot[(size_t)b * T + j];
+    }
+    cache_len_out[b] = L + n;
+  }
+  free(on_path);
 }

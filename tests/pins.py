@@ -489,6 +489,152 @@ def pin_compact_random(lib):
     assert out_len[3] == 20
 
 
+# ---- paged KV ("EAGLE-2 vs. Medusa" section 8) --------------------------------------------------
+def _paged_from_dense(rng, k_cache, v_cache, cache_len, P, shuffle):
+    """Pool + table holding the dense cache's rows 0..L_b-1 (pages of P tokens), built by plain
+    numpy indexing; pages are placed in shuffled physical order when ``shuffle``."""
+    B, Hkv, Lmax, D = k_cache.shape
+    n_pages = [(-(-int(L) // P)) for L in cache_len]
+    total = sum(n_pages)
+    phys = rng.permutation(total) if shuffle else np.arange(total)
+    max_pages = max(1, max(n_pages))
+    table = np.full((B, max_pages), -1, np.int32)
+    k_pool = np.zeros((total * P + 3, Hkv, D), k_cache.dtype)
+    v_pool = np.zeros_like(k_pool)
+    nxt = 0
+    for b in range(B):
+        for j in range(n_pages[b]):
+            pg = int(phys[nxt])
+            nxt += 1
+            table[b, j] = pg
+            for o in range(P):
+                pos = j * P + o
+                if pos < cache_len[b]:
+                    k_pool[pg * P + o] = k_cache[b, :, pos]
+                    v_pool[pg * P + o] = v_cache[b, :, pos]
+    return k_pool, v_pool, table
+
+
+def _with_tree_slots(rng, k_pool, v_pool, k_tree, v_tree):
+    """Append the tree rows to the pool at shuffled slots; returns the pool and tree_slot."""
+    B, T, Hkv, D = k_tree.shape
+    base = k_pool.shape[0]
+    order = rng.permutation(B * T)
+    tree_slot = (base + order).reshape(B, T).astype(np.int32)
+    kp = np.concatenate([k_pool, np.zeros((B * T, Hkv, D), k_pool.dtype)])
+    vp = np.concatenate([v_pool, np.zeros((B * T, Hkv, D), v_pool.dtype)])
+    for b in range(B):
+        for j in range(T):
+            kp[tree_slot[b, j]] = k_tree[b, j]
+            vp[tree_slot[b, j]] = v_tree[b, j]
+    return kp, vp, tree_slot
+
+
+def pin_paged_gather_and_attention(lib):
+    """Attention through a block table (any page size, pages in any physical order) equals the
+    pinned dense attention on the same rows, bit for bit."""
+    rng = np.random.default_rng(41)
+    for P, shuffle, dtype in [(1, True, "f32"), (4, False, "f32"), (16, True, "bf16"),
+                              (3, True, "f32")]:
+        case = small_case(rng, B=3, T=9, Hq=4, Hkv=2, D=16, Ls=(0, 37), dtype=dtype)
+        q, kc, vc, L, kt, vt, parent = (case[k] for k in
+                                        ("q", "k_cache", "v_cache", "cache_len", "k_tree",
+                                         "v_tree", "parent"))
+        k_pool, v_pool, table = _paged_from_dense(rng, kc, vc, L, P, shuffle)
+        k_pool, v_pool, tree_slot = _with_tree_slots(rng, k_pool, v_pool, kt, vt)
+        gk, gv, gkt, gvt = O.paged_gather(k_pool, v_pool, table, P, L, tree_slot, kc.shape[2],
+                                          lib=lib)
+        for b in range(kc.shape[0]):
+            n = int(L[b])
+            assert (gk[b, :, :n] == kc[b, :, :n]).all() and (gv[b, :, :n] == vc[b, :, :n]).all()
+        assert (gkt == kt).all() and (gvt == vt).all()
+        o1, l1 = O.attention(q, kc, vc, L, kt, vt, parent, lib=lib)
+        o2, l2 = O.paged_attention(q, k_pool, v_pool, table, P, L, tree_slot, parent, lib=lib)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), (P, shuffle, dtype)
+    # an entry outside the pool is refused, not read
+    bad = table.copy()
+    bad[0, 0] = k_pool.shape[0]
+    try:
+        O.paged_gather(k_pool, v_pool, bad, P, np.maximum(L, 1), tree_slot, 64, lib=lib)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("out-of-pool page accepted")
+
+
+def pin_commit_paged_hand_case(lib):
+    """Worked tree, path [0, 2, 5] after a 3-token prefix, one-token pages."""
+    table = np.full((1, 12), -1, np.int32)
+    table[0, :3] = [40, 41, 42]
+    tree_slot = np.array([[50, 51, 52, 53, 54, 55, 56, 57]], np.int32)
+    path = np.array([[0, 2, 5, -1, -1, -1, -1, -1]], np.int32)
+    free = np.full(64, -7, np.int32)
+    out_len, top, st = O.commit_paged(table, np.array([3], np.int32), tree_slot, path,
+                                      np.array([3], np.int32), 60, free, 10, lib=lib)
+    assert list(table[0]) == [40, 41, 42, 50, 52, 55] + [-1] * 6
+    assert out_len[0] == 6 and top == 15 and st[0] == 0
+    assert list(free[10:15]) == [51, 53, 54, 56, 57] and (free[:10] == -7).all()
+
+
+def pin_commit_paged_matches_copy(lib):
+    """After a pointer-swap commit, the rows the table names for positions 0..L+n-1 are exactly
+    the cache the pinned copying compaction produces; the free list receives exactly the
+    rejected nodes' slots; bad sequences commit nothing."""
+    rng = np.random.default_rng(43)
+    B, T, Hkv, D = 6, 9, 2, 8
+    case = small_case(rng, B=B, T=T, Hq=2, Hkv=Hkv, D=D, Ls=(0, 20))
+    kc, vc, L, kt, vt = (case[k] for k in ("k_cache", "v_cache", "cache_len", "k_tree", "v_tree"))
+    k_pool, v_pool, table = _paged_from_dense(rng, kc, vc, L, 1, True)
+    k_pool, v_pool, tree_slot = _with_tree_slots(rng, k_pool, v_pool, kt, vt)
+    num_slots = k_pool.shape[0]
+    max_pages = 26
+    tbl = np.full((B, max_pages), -1, np.int32)
+    tbl[:, :table.shape[1]] = table
+    paths = np.full((B, T), -1, np.int32)
+    lens = np.array([1, 4, 9, 2, 7, 3], np.int32)
+    for b in range(B):
+        chosen = np.sort(rng.choice(np.arange(1, T), size=lens[b] - 1, replace=False))
+        paths[b, :lens[b]] = np.concatenate([[0], chosen])
+    L = L.copy()
+    L[4] = 20  # 20 + 7 = 27 > 26: overflow by one row
+    free = np.full(num_slots + 8, -1, np.int32)
+    t0 = tbl.copy()
+    out_len, top, st = O.commit_paged(tbl, L, tree_slot, paths, lens, num_slots, free, 0, lib=lib)
+    # the copying compaction on the dense view of the same data
+    Lmax = max_pages
+    dk = np.zeros((B, Hkv, Lmax, D), kc.dtype)
+    dv = np.zeros_like(dk)
+    for b in range(B):
+        for p in range(min(int(L[b]), kc.shape[2])):
+            dk[b, :, p] = kc[b, :, p]
+            dv[b, :, p] = vc[b, :, p]
+    want_len, want_st = O.compact(dk, dv, L, kt, vt, paths, lens, lib=lib)
+    assert np.array_equal(out_len, want_len) and np.array_equal(st, want_st)
+    rejected = []
+    for b in range(B):
+        if st[b]:
+            assert (tbl[b] == t0[b]).all()
+            continue
+        for p in range(int(out_len[b])):
+            if p < L[b]:
+                continue
+            slot = tbl[b, p]
+            assert (k_pool[slot] == dk[b, :, p]).all() and (v_pool[slot] == dv[b, :, p]).all()
+        rejected += [int(tree_slot[b, j]) for j in range(T) if j not in set(paths[b, :lens[b]])]
+    assert top == len(rejected) and sorted(free[:top]) == sorted(rejected)
+    # malformed paths, lengths and slots commit nothing
+    tbl2 = t0.copy()
+    dup = paths.copy()
+    dup[1, 2] = dup[1, 1]
+    slots = tree_slot.copy()
+    slots[2, 5] = num_slots
+    out_len, top2, st = O.commit_paged(tbl2, np.array([-1, 3, 3, 3, 3, 27], np.int32), slots,
+                                       dup, lens, num_slots, free, 5, lib=lib)
+    assert list(st[:3]) == [O.ORC_BAD_LEN, O.ORC_BAD_PATH, O.ORC_BAD_PATH]
+    assert st[5] == O.ORC_BAD_LEN
+    assert (tbl2[[0, 1, 2, 5]] == t0[[0, 1, 2, 5]]).all()
+
+
 ALL_PINS = [
     pin_worked_tree_mask,
     pin_mask_closure_bruteforce,
@@ -507,4 +653,7 @@ ALL_PINS = [
     pin_compact_hand_case,
     pin_compact_alias,
     pin_compact_random,
+    pin_paged_gather_and_attention,
+    pin_commit_paged_hand_case,
+    pin_commit_paged_matches_copy,
 ]

@@ -53,10 +53,31 @@ MUTANTS = {
     "compact_shifted": ("size_t dst = (((size_t)b * Hkv + h) * Lmax + L + k) * row;",
                         "size_t dst = (((size_t)b * Hkv + h) * Lmax + L + k + (k > 0)) * row;"),
     # compaction length excludes the root
-    "compact_len": ("cache_len_out[b] = L + n;", "cache_len_out[b] = L + n - 1;"),
+    "compact_len": ("cache_len_out[b] = L + n;\n  }\n  free(tmp);",
+                    "cache_len_out[b] = L + n - 1;\n  }\n  free(tmp);"),
+    # pointer-swap commit length excludes the root
+    "commit_len": ("cache_len_out[b] = L + n;\n  }\n  free(on_path);",
+                   "cache_len_out[b] = L + n - 1;\n  }\n  free(on_path);"),
     # overflow check off by one
     "compact_overflow": ("if (!bits && (long)L + n > Lmax) bits |= ORC_OVERFLOW;",
                          "if (!bits && (long)L + n > Lmax + 1) bits |= ORC_OVERFLOW;"),
+    # paged gather ignores the offset within a page
+    "paged_no_offset": ("long slot = (long)page * page_size + p % page_size;",
+                        "long slot = (long)page * page_size;"),
+    # paged gather indexes the table by position instead of by page
+    "paged_table_by_position": ("int page = table[(size_t)b * max_pages + p / page_size];",
+                                "int page = table[(size_t)b * max_pages + p % max_pages];"),
+    # tree rows read at the node's index instead of its slot
+    "paged_tree_by_index": ("int slot = tree_slot[(size_t)b * T + j];\n      if (slot < 0 || slot >= num_slots) {\n        rc = -1;",
+                            "int slot = j;\n      if (slot < 0 || slot >= num_slots) {\n        rc = -1;"),
+    # commit adopts the slots in node order rather than path order (same set)
+    "commit_node_order": ("table[(size_t)b * max_pages + L + k] = tree_slot[(size_t)b * T + accept_path[(size_t)b * T + k]];",
+                          "table[(size_t)b * max_pages + L + k] = tree_slot[(size_t)b * T + accept_path[(size_t)b * T + (n - 1 - k)]];"),
+    # accepted nodes' slots also returned to the free list
+    "commit_frees_accepted": ("      if (on_path[j]) continue;\n", ""),
+    # commit overflow check off by one
+    "commit_overflow": ("if (!bits && (long)L + n > max_pages) bits |= ORC_OVERFLOW;",
+                        "if (!bits && (long)L + n > max_pages + 1) bits |= ORC_OVERFLOW;"),
 }
 
 
