@@ -54,6 +54,7 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_OVERFLOW 0x2 /* cache_len[b] + accept_len[b] > Lmax: nothing committed */
 #define TV_BAD_LEN 0x4  /* cache_len[b] < 0 or > Lmax */
 #define TV_BAD_PATH 0x8 /* accept_len[b] outside [0, T] or an accepted index outside [0, T) */
+#define TV_BAD_PAGE 0x10 /* paged K/V: a block-table entry or tree slot outside the pool */
 
 /* Human-readable name of a tv_status return value or of a single status bit. */
 const char* tv_status_string(int code);
@@ -164,6 +165,62 @@ int kv_compact_accepted(void* k_cache, void* v_cache, const int32_t* cache_len,
                         int32_t* cache_len_out, const void* k_tree, const void* v_tree,
                         const int32_t* accept_path, const int32_t* accept_len, int B, int T,
                         int Hkv, int D, int Lmax, int dtype, int32_t* status, void* stream);
+
+/*
+ * tree_verify_attn_paged — tree_verify_attn over a paged KV cache.
+ * The K/V rows live in a pool of token slots, as in the PagedAttention scheme of lesty.tech
+ * section 8: speculative tree nodes are written into reserved scratch slots of the pool and the
+ * sequence's prefix is reached through a block table.  Results equal tree_verify_attn on the
+ * dense cache those rows form.
+ *
+ *   k_pool, v_pool [num_slots,Hkv,D]  dtype   slot s holds one token's rows for every KV head
+ *   block_table    [B,max_pages]      int32   page of each group of page_size positions:
+ *                                             position p of sequence b is slot
+ *                                             block_table[b][p / page_size] * page_size +
+ *                                             p % page_size
+ *   page_size      power of two >= 1
+ *   cache_len      [B]                int32   L_b, clamped into [0, max_pages * page_size]
+ *                                             (TV_BAD_LEN otherwise)
+ *   tree_slot      [B,T]              int32   slot of each tree node's K/V rows
+ *   other arguments as for tree_verify_attn, with Lmax = max_pages * page_size for the
+ *   workspace size (tree_verify_attn_workspace_size).  A table entry or tree slot outside the
+ *   pool is never read through: it is clamped into the pool and TV_BAD_PAGE is OR-ed into
+ *   status[b].
+ */
+int tree_verify_attn_paged(const void* q, const void* k_pool, const void* v_pool, int num_slots,
+                           const int32_t* block_table, int max_pages, int page_size,
+                           const int32_t* cache_len, const int32_t* tree_slot,
+                           const uint64_t* anc_mask, void* out, float* lse, int32_t* status,
+                           int B, int T, int Hq, int Hkv, int D, int dtype, float scale,
+                           int split_keys, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kv_commit_paged — commit the accepted path by pointer swap (lesty.tech section 8): the block
+ * table's entries for positions L_b .. L_b + accept_len[b] - 1 take the accepted nodes' slots,
+ * in path order, and the slots of the tree's rejected nodes are returned to the free list by
+ * one atomic increment of free_top; no K/V row is copied.  Pages hold one token (page_size must
+ * be 1: accepted nodes are scattered over the tree's slots, so only token-sized pages can adopt
+ * them exactly; kv_compact_accepted is the copying commit).
+ *
+ *   block_table [B,max_pages]  int32  in/out
+ *   cache_len, cache_len_out   as for kv_compact_accepted (may be the same pointer)
+ *   tree_slot [B,T], accept_path [B,T], accept_len [B]  int32
+ *   free_slots  [num_slots]    int32  out: rejected slots are written at free_top, free_top+1, ..
+ *                                     in node order per sequence (the order between sequences
+ *                                     follows the atomics); entries at or past num_slots are not
+ *                                     written
+ *   free_top    [1]            int32  in/out: advanced by the number of rejected nodes
+ *   status      [B]            int32  optional (NULL): TV_BAD_LEN (cache_len outside
+ *                                     [0, max_pages]), TV_BAD_PATH (bad accept_len, an accepted
+ *                                     index outside [0, T) or repeated, a tree slot outside the
+ *                                     pool) or TV_OVERFLOW (L_b + accept_len[b] > max_pages)
+ *                                     OR-ed in; such a sequence commits nothing, frees nothing
+ *                                     and keeps cache_len_out[b] = cache_len[b]
+ */
+int kv_commit_paged(int32_t* block_table, int max_pages, int page_size, const int32_t* cache_len,
+                    int32_t* cache_len_out, const int32_t* tree_slot, const int32_t* accept_path,
+                    const int32_t* accept_len, int32_t* free_slots, int32_t* free_top,
+                    int num_slots, int B, int T, int32_t* status, void* stream);
 
 /*
  * tree_verify_step — one whole verification step: tree_build_mask, tree_verify_attn,

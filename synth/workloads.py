@@ -347,3 +347,55 @@ def make_workload(spec: WorkloadSpec | str, extra_seed: int = 0, B: int | None =
     return Workload(spec=spec, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, Lmax=Lmax, dtype=dtype,
                     parent=parent, draft=draft, target=target, cache_len=cache_len, q=q,
                     k_cache=k_cache, v_cache=v_cache, k_tree=k_tree, v_tree=v_tree)
+
+
+@dataclasses.dataclass
+class PagedLayout:
+    """A workload's K/V placed in a pool of token slots, for the paged entry points.
+
+    k_pool / v_pool [num_slots, Hkv, D]; block_table [B, max_pages] names each sequence's pages
+    (page_size positions each, physical pages in shuffled order, -1 past the prefix);
+    tree_slot [B, T] names each tree node's slot (shuffled, after the prefix pages); the last
+    ``spare`` slots are unused (room the free list can hand out)."""
+    page_size: int
+    k_pool: np.ndarray
+    v_pool: np.ndarray
+    block_table: np.ndarray
+    tree_slot: np.ndarray
+    num_slots: int
+    max_pages: int
+
+
+def make_paged(w: "Workload", page_size: int, seed: int = 0, headroom: int | None = None,
+               spare: int = 0) -> PagedLayout:
+    """Place w's prefix rows and tree rows into a pool.  Pure data placement: slot and page
+    numbers come from a seeded permutation; no value is computed.  ``headroom`` positions past
+    each prefix get table room (default T, enough to commit a whole path)."""
+    rng = np.random.default_rng(np.random.SeedSequence([w.spec.wid, 7, seed]))
+    P = int(page_size)
+    B, T, Hkv, D = w.B, w.T, w.Hkv, w.D
+    L = np.clip(w.cache_len, 0, w.Lmax).astype(np.int64)
+    headroom = T if headroom is None else headroom
+    n_pages = [int(-(-int(x) // P)) for x in L]
+    total_pages = sum(n_pages)
+    max_pages = max(1, max(-(-(int(x) + headroom) // P) for x in L))
+    phys = rng.permutation(total_pages)
+    num_slots = total_pages * P + B * T + spare
+    k_pool = np.zeros((num_slots, Hkv, D), w.k_cache.dtype)
+    v_pool = np.zeros_like(k_pool)
+    table = np.full((B, max_pages), -1, np.int32)
+    nxt = 0
+    for b in range(B):
+        pages = phys[nxt:nxt + n_pages[b]]
+        nxt += n_pages[b]
+        table[b, :n_pages[b]] = pages
+        if n_pages[b] == 0:
+            continue
+        pos = np.arange(int(L[b]))
+        slots = pages[pos // P] * P + pos % P
+        k_pool[slots] = w.k_cache[b, :, :L[b]].transpose(1, 0, 2)
+        v_pool[slots] = w.v_cache[b, :, :L[b]].transpose(1, 0, 2)
+    tree_slot = (total_pages * P + rng.permutation(B * T)).reshape(B, T).astype(np.int32)
+    k_pool[tree_slot.reshape(-1)] = w.k_tree.reshape(B * T, Hkv, D)
+    v_pool[tree_slot.reshape(-1)] = w.v_tree.reshape(B * T, Hkv, D)
+    return PagedLayout(P, k_pool, v_pool, table, tree_slot, num_slots, max_pages)

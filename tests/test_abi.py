@@ -57,7 +57,8 @@ def test_status_strings(lib):
     import tree_attention_verification_attn_amd as tv
 
     for code in (tv.TV_OK, tv.TV_ERR_INVALID_ARG, tv.TV_ERR_UNSUPPORTED, tv.TV_ERR_WORKSPACE,
-                 tv.TV_ERR_HIP, tv.TV_BAD_TREE, tv.TV_OVERFLOW, tv.TV_BAD_LEN, tv.TV_BAD_PATH):
+                 tv.TV_ERR_HIP, tv.TV_BAD_TREE, tv.TV_OVERFLOW, tv.TV_BAD_LEN, tv.TV_BAD_PATH,
+                 tv.TV_BAD_PAGE):
         assert lib.tv_status_string(code)
     assert b"unknown" in lib.tv_status_string(12345)
 
@@ -142,6 +143,31 @@ def test_step_argument_errors(lib):
     bad[7] = ctypes.c_void_p(0x2002)
     bad[17] = 4
     assert lib.tree_verify_step(*bad) == -1
+
+
+def test_paged_argument_errors(lib):
+    def attn(**kw):
+        a = dict(q=FAKE, kp=FAKE, vp=FAKE, ns=100, tb=FAKE, mp=4, P=16, cl=FAKE, ts=FAKE, anc=FAKE,
+                 out=FAKE, B=1, T=8, Hq=2, Hkv=1, D=64, dt=0)
+        a.update(kw)
+        return lib.tree_verify_attn_paged(a["q"], a["kp"], a["vp"], a["ns"], a["tb"], a["mp"],
+                                          a["P"], a["cl"], a["ts"], a["anc"], a["out"], None,
+                                          None, a["B"], a["T"], a["Hq"], a["Hkv"], a["D"],
+                                          a["dt"], 0.0, 0, None, 0, None)
+    for name in ("q", "kp", "vp", "tb", "cl", "ts", "anc", "out"):
+        assert attn(**{name: None}) == -1, name
+    assert attn(P=0) == -1 and attn(P=12) == -1  # page size: a power of two
+    assert attn(ns=0) == -1 and attn(mp=0) == -1
+    assert attn(D=96) == -2
+    assert attn(mp=1 << 20, P=1 << 12) == -1  # table reach beyond 2^30 positions
+    commit = [FAKE, 8, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 100, 1, 8, None, None]
+    for i in (0, 3, 4, 5, 6, 7, 8, 9):
+        bad = list(commit)
+        bad[i] = None
+        assert lib.kv_commit_paged(*bad) == -1, i
+    bad = list(commit)
+    bad[2] = 16  # pointer swap needs one-token pages
+    assert lib.kv_commit_paged(*bad) == -2
 
 
 def test_accept_argument_errors(lib):

@@ -6,6 +6,7 @@ include/tree_verify.h); this package only builds and binds it.
 from .binding import (  # noqa: F401
     EXPORTS,
     TV_BAD_LEN,
+    TV_BAD_PAGE,
     TV_BAD_PATH,
     TV_BAD_TREE,
     TV_BF16,
@@ -17,6 +18,7 @@ from .binding import (  # noqa: F401
     TV_OK,
     TV_OVERFLOW,
     TreeVerifyError,
+    kv_commit_paged,
     kv_compact_accepted,
     lib_path,
     load_library,
@@ -25,6 +27,7 @@ from .binding import (  # noqa: F401
     tree_accept,
     tree_build_mask,
     tree_verify_attn,
+    tree_verify_attn_paged,
     tree_verify_attn_workspace_size,
     tree_verify_step,
 )

@@ -16,11 +16,11 @@ from . import build as _build
 
 TV_OK, TV_ERR_INVALID_ARG, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_HIP = 0, -1, -2, -3, -4
 TV_F32, TV_BF16 = 0, 1
-TV_BAD_TREE, TV_OVERFLOW, TV_BAD_LEN, TV_BAD_PATH = 0x1, 0x2, 0x4, 0x8
+TV_BAD_TREE, TV_OVERFLOW, TV_BAD_LEN, TV_BAD_PATH, TV_BAD_PAGE = 0x1, 0x2, 0x4, 0x8, 0x10
 
 EXPORTS = ("tv_status_string", "tree_build_mask", "tree_verify_attn_workspace_size",
            "tree_verify_attn", "tree_accept", "kv_compact_accepted", "tv_profile_attn_main",
-           "tree_verify_step")
+           "tree_verify_step", "tree_verify_attn_paged", "kv_commit_paged")
 
 
 class TreeVerifyError(RuntimeError):
@@ -74,6 +74,11 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_verify_step.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                      I, I, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
     lib.tree_verify_step.restype = I
+    lib.tree_verify_attn_paged.argtypes = [P, P, P, I, P, I, I, P, P, P, P, P, P,
+                                           I, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
+    lib.tree_verify_attn_paged.restype = I
+    lib.kv_commit_paged.argtypes = [P, I, I, P, P, P, P, P, P, P, I, I, I, P, P]
+    lib.kv_commit_paged.restype = I
 
 
 def status_string(code: int) -> str:
@@ -299,3 +304,71 @@ def tree_verify_step(parent, draft_tok, target_tok, q, k_cache, v_cache, cache_l
     return dict(anc_mask=anc_mask, out=out, lse=lse, accept_path=accept_path,
                 accept_len=accept_len, bonus_tok=bonus_tok, cache_len_out=cache_len_out,
                 status=status)
+
+
+def tree_verify_attn_paged(q, k_pool, v_pool, block_table, page_size: int, cache_len, tree_slot,
+                           anc_mask, out=None, lse=None, status=None, scale: float = 0.0,
+                           split_keys: int = 0, workspace: torch.Tensor | None = None,
+                           with_lse: bool = True, stream=None):
+    """Tree attention over a paged cache (pool [num_slots,Hkv,D], block table [B,max_pages])."""
+    _need(q, "q", None, 4)
+    B, T, Hq, D = q.shape
+    dt = _dtype_code(q)
+    _need(k_pool, "k_pool", q.dtype, 3)
+    _need(v_pool, "v_pool", q.dtype, 3)
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(cache_len, "cache_len", torch.int32, 1)
+    _need(tree_slot, "tree_slot", torch.int32, 2)
+    _need(anc_mask, "anc_mask", torch.int64, 3)
+    num_slots, Hkv = k_pool.shape[0], k_pool.shape[1]
+    max_pages = block_table.shape[1]
+    if (tuple(k_pool.shape) != (num_slots, Hkv, D) or tuple(v_pool.shape) != tuple(k_pool.shape)
+            or block_table.shape[0] != B or tuple(tree_slot.shape) != (B, T)
+            or tuple(cache_len.shape) != (B,) or tuple(anc_mask.shape) != (B, T, (T + 63) // 64)):
+        raise ValueError("inconsistent tree_verify_attn_paged shapes")
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", q.dtype, 4)
+    if lse is None and with_lse:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    ws_bytes = tree_verify_attn_workspace_size(B, T, Hq, Hkv, D, max_pages * page_size, q.dtype,
+                                               split_keys)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=q.device)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("tree_verify_attn_paged", load_library().tree_verify_attn_paged(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), num_slots, _ptr(block_table), max_pages,
+        int(page_size), _ptr(cache_len), _ptr(tree_slot), _ptr(anc_mask), _ptr(out), _ptr(lse),
+        _ptr(status), B, T, Hq, Hkv, D, dt, float(scale), int(split_keys), _ptr(workspace),
+        ws_have, _stream(stream)))
+    return out, lse
+
+
+def kv_commit_paged(block_table, cache_len, tree_slot, accept_path, accept_len, free_slots,
+                    free_top, num_slots: int, page_size: int = 1, cache_len_out=None,
+                    status=None, stream=None):
+    """Pointer-swap commit (one-token pages); updates block_table, free_slots, free_top in place
+    and returns cache_len_out [B] int32."""
+    for name, t, nd in (("block_table", block_table, 2), ("cache_len", cache_len, 1),
+                        ("tree_slot", tree_slot, 2), ("accept_path", accept_path, 2),
+                        ("accept_len", accept_len, 1), ("free_slots", free_slots, 1),
+                        ("free_top", free_top, 1)):
+        _need(t, name, torch.int32, nd)
+    B, max_pages = block_table.shape
+    T = tree_slot.shape[1]
+    if (tuple(cache_len.shape) != (B,) or tuple(tree_slot.shape) != (B, T)
+            or tuple(accept_path.shape) != (B, T) or tuple(accept_len.shape) != (B,)
+            or free_slots.numel() < num_slots or free_top.numel() != 1):
+        raise ValueError("inconsistent kv_commit_paged shapes")
+    cache_len_out = torch.empty_like(cache_len) if cache_len_out is None else cache_len_out
+    _need(cache_len_out, "cache_len_out", torch.int32, 1)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    _check("kv_commit_paged", load_library().kv_commit_paged(
+        _ptr(block_table), max_pages, int(page_size), _ptr(cache_len), _ptr(cache_len_out),
+        _ptr(tree_slot), _ptr(accept_path), _ptr(accept_len), _ptr(free_slots), _ptr(free_top),
+        int(num_slots), B, T, _ptr(status), _stream(stream)))
+    return cache_len_out

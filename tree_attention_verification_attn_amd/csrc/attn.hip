@@ -72,6 +72,11 @@ struct AttnArgs {
   char* part_o;    // [slot][kRows*D] elements of the input type, in register order
   float* part_ml;  // [slot][kRows][2]: running max m and sum l per row
   int32_t* nsplit; // [B] non-empty chunks of each sequence, for the merge
+  // paged K/V: kc / vc are pools [num_slots, Hkv, D]; position p of sequence b lives in slot
+  // table[b][p >> log2P] * P + (p & (P-1)), tree node j in slot tree_slot[b][j]
+  const int32_t* table;
+  const int32_t* tree_slot;
+  int max_pages, log2P, num_slots;
   int B, T, Hq, Hkv, G, Lmax, W, GT, RB, S, chunk_tiles;
   float c;         // scale * log2(e)
 };
@@ -133,6 +138,25 @@ __device__ inline void lds_dma16(uint32_t lds, const void* sbase, uint32_t voff)
       : "s"(lds), "v"(voff), "s"(sbase)
       : "memory");
 }
+
+// The same load from a 64-bit address in a VGPR pair (paged K/V: rows anywhere in a pool).
+__device__ inline void lds_dma16_addr(uint32_t lds, const void* addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(addr)
+      : "memory");
+}
+
+// Read-only int32 tables read with wavefront-uniform indices: through the constant address
+// space they become scalar loads, which count on lgkmcnt and leave the vmcnt of the tile loads
+// alone.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
 
 // s_waitcnt vmcnt(n) (n <= 63), other counters untouched.
 template <int N>
@@ -243,7 +267,7 @@ __device__ inline bool build_masks_wave(const int (&par)[2], int b, int T,
   return bad;
 }
 
-template <typename E, int D, bool kSplit, bool kMasks>
+template <typename E, int D, bool kSplit, bool kMasks, bool kPaged>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2)))
 void attn_main(AttnArgs a) {
@@ -312,10 +336,59 @@ void attn_main(AttnArgs a) {
   }
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
 
+  // Paged K/V: the rows of one direct-load instruction are kRowsPerDma consecutive keys (one
+  // per group of kCPR lanes); their slots are read with scalar loads (uniform per group) and
+  // each lane keeps its group's.  Entries outside the pool are clamped into it and reported.
+  bool bad_slot = false;
+  auto check_slot = [&](long long slot) -> int {
+    const bool out = slot < 0 || slot >= a.num_slots;
+    bad_slot = bad_slot || out;
+    return out ? (slot < 0 ? 0 : a.num_slots - 1) : (int)slot;
+  };
+  auto issue_tile_paged = [&](int tile, uint32_t kl, uint32_t vl) {
+    const size_t hstride = (size_t)a.Hkv * kRB;  // bytes per pool slot
+    const char* kpool = a.kc + (size_t)kvh * kRB;
+    const char* vpool = a.vc + (size_t)kvh * kRB;
+    const int grp = lane / Lay::kCPR;
+#pragma unroll
+    for (int i = 0; i < kDPW; ++i) {
+      const int r0 = (wave * kDPW + i) * Lay::kRowsPerDma;  // first key row of the instruction
+      int mine = 0;
+      if (tile < n_tree_tiles) {
+        const_i32* ts = (const_i32*)a.tree_slot + (size_t)b * a.T;
+        const int base = (v0 + tile) * kKT + r0;
+#pragma unroll
+        for (int j = 0; j < Lay::kRowsPerDma; ++j) {
+          const int slot = check_slot(ts[min(base + j, a.T - 1)]);
+          mine = grp == j ? slot : mine;
+        }
+      } else {
+        const_i32* tb = (const_i32*)a.table + (size_t)b * a.max_pages;
+        const int base = k0 + (tile - n_tree_tiles) * kKT + r0;
+        const int pmask = (1 << a.log2P) - 1;
+#pragma unroll
+        for (int j = 0; j < Lay::kRowsPerDma; ++j) {
+          const int pos = min(base + j, k1 - 1);
+          const int page = tb[pos >> a.log2P];
+          const int slot =
+              check_slot(page < 0 ? -1LL : (long long)page * (pmask + 1) + (pos & pmask));
+          mine = grp == j ? slot : mine;
+        }
+      }
+      const size_t off = (size_t)mine * hstride + dma_chunk[i];
+      lds_dma16_addr(kl + i * 1024, kpool + off);
+      lds_dma16_addr(vl + i * 1024, vpool + off);
+    }
+  };
+
   auto issue_tile = [&](int tile) {
     const int stage = tile % kNS;
     const uint32_t kl = smem_base + stage * Lay::kStage + wave * kDPW * 1024;
     const uint32_t vl = kl + Lay::kTile;
+    if constexpr (kPaged) {
+      issue_tile_paged(tile, kl, vl);
+      return;
+    }
     if (tile < n_tree_tiles) {
       const int base = (v0 + tile) * kKT;
 #pragma unroll
@@ -669,6 +742,7 @@ void attn_main(AttnArgs a) {
   }
 
   // ---- epilogue ----------------------------------------------------------------------------
+  if (kPaged && bad_slot && tid == 64 * wave && a.status) atomicOr(a.status + b, TV_BAD_PAGE);
   l_run += partner(l_run);
 
   if (direct) {
@@ -914,10 +988,11 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int elem_bytes, i
 // Profiling events recorded around the main kernel (tv_profile_attn_main).
 hipEvent_t g_prof_before = nullptr, g_prof_after = nullptr;
 
-template <typename E, int D, bool kMasks = false>
+template <typename E, int D, bool kMasks = false, bool kPaged = false>
 int launch_main(const AttnArgs& a, hipStream_t stream) {
   const int n_items = a.B * a.Hkv * a.S * a.RB;
-  auto kernel = a.S > 1 ? attn_main<E, D, true, kMasks> : attn_main<E, D, false, kMasks>;
+  auto kernel = a.S > 1 ? attn_main<E, D, true, kMasks, kPaged>
+                        : attn_main<E, D, false, kMasks, kPaged>;
   if (g_prof_before) {
     // the events take the kernel's own start and end timestamps
     hipExtLaunchKernelGGL(kernel, dim3(n_items), dim3(kThreads), 0, stream, g_prof_before,
@@ -928,9 +1003,9 @@ int launch_main(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
-template <typename E, int D>
+template <typename E, int D, bool kPaged = false>
 int launch_attn(const AttnArgs& a, hipStream_t stream) {
-  const int rc = launch_main<E, D>(a, stream);
+  const int rc = launch_main<E, D, false, kPaged>(a, stream);
   if (rc != TV_OK) return rc;
   if (a.S > 1)
     hipLaunchKernelGGL((attn_combine<E, D>),
@@ -1011,6 +1086,11 @@ static int prepare_attn(AttnArgs& a, Plan& p, const void* q, const void* k_cache
   a.vt = (const char*)v_tree;
   a.anc = anc_mask;
   a.parent = nullptr;
+  a.table = nullptr;
+  a.tree_slot = nullptr;
+  a.max_pages = 0;
+  a.log2P = 0;
+  a.num_slots = 0;
   a.out = (char*)out;
   a.lse = lse;
   a.status = status;
@@ -1052,6 +1132,36 @@ extern "C" int tree_verify_attn(const void* q, const void* k_cache, const void* 
   if (dtype == TV_BF16)
     return D == 128 ? launch_attn<__bf16, 128>(a, st) : launch_attn<__bf16, 64>(a, st);
   return D == 128 ? launch_attn<float, 128>(a, st) : launch_attn<float, 64>(a, st);
+}
+
+extern "C" int tree_verify_attn_paged(const void* q, const void* k_pool, const void* v_pool,
+                                      int num_slots, const int32_t* block_table, int max_pages,
+                                      int page_size, const int32_t* cache_len,
+                                      const int32_t* tree_slot, const uint64_t* anc_mask,
+                                      void* out, float* lse, int32_t* status, int B, int T,
+                                      int Hq, int Hkv, int D, int dtype, float scale,
+                                      int split_keys, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!block_table || !tree_slot || num_slots < 1 || max_pages < 1 || page_size < 1 ||
+      (page_size & (page_size - 1)) || (long long)max_pages * page_size >= (1LL << 30))
+    return TV_ERR_INVALID_ARG;
+  AttnArgs a;
+  Plan p;
+  const int cap = max_pages * page_size;  // positions the table can name
+  // the dense argument checks, with the pools standing in for the caches and the tree K/V
+  const int rc = prepare_attn(a, p, q, k_pool, v_pool, cache_len, k_pool, v_pool, anc_mask, out,
+                              lse, status, B, T, Hq, Hkv, D, cap, dtype, scale, split_keys,
+                              workspace, workspace_bytes);
+  if (rc != TV_OK) return rc;
+  a.table = block_table;
+  a.tree_slot = tree_slot;
+  a.max_pages = max_pages;
+  a.log2P = 31 - __builtin_clz((unsigned)page_size);
+  a.num_slots = num_slots;
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == TV_BF16)
+    return D == 128 ? launch_attn<__bf16, 128, true>(a, st) : launch_attn<__bf16, 64, true>(a, st);
+  return D == 128 ? launch_attn<float, 128, true>(a, st) : launch_attn<float, 64, true>(a, st);
 }
 
 // True when byte ranges [a, a + na) and [b, b + nb) intersect.
