@@ -55,6 +55,13 @@ def parse_args():
     p.add_argument("--api", choices=("fused", "separate"), default="fused",
                    help="time the step through tree_verify_step (three launches) or through the "
                         "four separate entry points; the other is timed too and reported")
+    p.add_argument("--kv", choices=("dense", "paged"), default="dense",
+                   help="dense caches, or a paged pool read through a block table with the path "
+                        "committed by pointer swap (page size 1; kv_compact_accepted's copy is "
+                        "timed beside it)")
+    p.add_argument("--page-size", type=int, default=1,
+                   help="tokens per page for --kv paged (the commit needs 1; larger pages time "
+                        "mask + attention + acceptance)")
     p.add_argument("--rotate", type=int, default=0, help="input copies to rotate (0 = auto)")
     p.add_argument("--mode", choices=("graph", "eager"), default="graph",
                    help="replay each step as a captured HIP graph, or launch eagerly")
@@ -149,7 +156,7 @@ def kernel_source_hash() -> str:
 class StepSet:
     """Device buffers of one copy of the workload, plus pre-marshalled C-ABI argument tuples."""
 
-    def __init__(self, tv, torch, w, base=None, split_keys=0, workspace=None):
+    def __init__(self, tv, torch, w, base=None, split_keys=0, workspace=None, paged=None):
         dev = torch.device("cuda:0")
 
         def up(a):
@@ -197,6 +204,33 @@ class StepSet:
                           P(t["status"]), B, T, Hq, w.Hkv, D, w.Lmax, dt, ctypes.c_float(0.0),
                           split_keys, ws_ptr, ctypes.c_size_t(ws_bytes))
         self.api = "fused"
+        self.paged = paged
+        if paged is not None:  # the same rows in a pool of token slots (synth.make_paged)
+            if base is None:
+                t["k_pool"], t["v_pool"] = up(paged.k_pool), up(paged.v_pool)
+                t["table"], t["tree_slot"] = up(paged.block_table), up(paged.tree_slot)
+            t["free"] = torch.full((paged.num_slots,), -1, dtype=torch.int32, device=dev)
+            t["free_top"] = torch.zeros((1,), dtype=torch.int32, device=dev)
+            mp = paged.block_table.shape[1]
+            self.attn_paged_args = (P(t["q"]), P(t["k_pool"]), P(t["v_pool"]), paged.num_slots,
+                                    P(t["table"]), mp, paged.page_size, P(t["cache_len"]),
+                                    P(t["tree_slot"]), P(t["anc"]), P(t["out"]), P(t["lse"]),
+                                    P(t["status"]), B, T, Hq, w.Hkv, D, dt, ctypes.c_float(0.0),
+                                    split_keys, ws_ptr, ctypes.c_size_t(ws_bytes))
+            self.commit_args = (P(t["table"]), mp, paged.page_size, P(t["cache_len"]),
+                                P(t["cache_len_out"]), P(t["tree_slot"]), P(t["path"]),
+                                P(t["alen"]), P(t["free"]), P(t["free_top"]), paged.num_slots,
+                                B, T, P(t["status"]))
+            self.api = "paged"
+
+    def attn_paged(self, stream):
+        rc = self.lib.tree_verify_attn_paged(*self.attn_paged_args, stream)
+        assert rc == 0, rc
+
+    def commit(self, stream):
+        if self.paged.page_size == 1:
+            rc = self.lib.kv_commit_paged(*self.commit_args, stream)
+            assert rc == 0, rc
 
     def mask(self, stream):
         rc = self.lib.tree_build_mask(*self.mask_args, stream)
@@ -221,6 +255,12 @@ class StepSet:
     def step(self, stream):
         if self.api == "fused":
             self.fused(stream)
+            return
+        if self.api == "paged":
+            self.mask(stream)
+            self.attn_paged(stream)
+            self.accept(stream)
+            self.commit(stream)
             return
         self.mask(stream)
         self.attn(stream)
@@ -303,6 +343,8 @@ def main() -> int:
     flops = 4 * int(L.sum()) * w.Hq * w.T * w.D  # QK^T and PV over the prefix
     elem = 2 if w.dtype == "bf16" else 4
     set_bytes = (w.k_cache.nbytes + w.v_cache.nbytes + w.q.nbytes * 2 + w.k_tree.nbytes * 2)
+    if args.kv == "paged":
+        set_bytes *= 2  # the pool holds the same rows again
     n_sets = args.rotate or max(1, math.ceil(2 * MALL_BYTES / max(kv_bytes, 1)))
     free, total_mem = torch.cuda.mem_get_info()
     n_sets = max(1, min(n_sets, int(0.5 * free / set_bytes)))
@@ -310,13 +352,23 @@ def main() -> int:
     ws_bytes = tv.tree_verify_attn_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.Lmax,
                                                   torch.bfloat16 if w.dtype == "bf16"
                                                   else torch.float32, args.split_keys)
+    paged = None
+    if args.kv == "paged":
+        from synth import make_paged
+
+        paged = make_paged(w, args.page_size, seed=0)
+        cap = paged.block_table.shape[1] * paged.page_size
+        ws_bytes = max(ws_bytes, tv.tree_verify_attn_workspace_size(
+            w.B, w.T, w.Hq, w.Hkv, w.D, cap,
+            torch.bfloat16 if w.dtype == "bf16" else torch.float32, args.split_keys))
+        args.api = "paged"
     workspace = torch.zeros((max(ws_bytes, 1),), dtype=torch.uint8, device="cuda") if ws_bytes else None
     print(f"[bench] uploading {n_sets} input sets ({set_bytes / 2**20:.1f} MiB each), "
           f"workspace {ws_bytes / 2**20:.1f} MiB", file=sys.stderr, flush=True)
-    sets = [StepSet(tv, torch, w, split_keys=args.split_keys, workspace=workspace)]
+    sets = [StepSet(tv, torch, w, split_keys=args.split_keys, workspace=workspace, paged=paged)]
     for _ in range(n_sets - 1):
         sets.append(StepSet(tv, torch, w, base=sets[0], split_keys=args.split_keys,
-                            workspace=workspace))
+                            workspace=workspace, paged=paged))
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
@@ -376,8 +428,8 @@ def main() -> int:
             torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps, t_wall
 
-    other = "separate" if args.api == "fused" else "fused"
-    ms_other, _ = time_api(other)
+    other = {"fused": "separate", "separate": "fused", "paged": None}[args.api]
+    ms_other = time_api(other)[0] if other else None
     ms_per_step, t_wall = time_api(args.api)
     t_step = ms_per_step * 1e-3
 
@@ -437,6 +489,46 @@ def main() -> int:
     if args.api == "fused":
         t_main = t_main_fused
 
+    # paged K/V: the same calls with the attention reading the pool through the block table and
+    # the commit by pointer swap; the dense pass above timed the copying commit on the same path
+    paged_breakdown = None
+    if args.kv == "paged":
+        evp = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n_prof)]
+        for row in evp:
+            for e in row:
+                e.record(stream)
+        stream.synchronize()
+        with torch.cuda.stream(stream):
+            for i in range(n_prof):
+                s = sets[i % n_sets]
+                ei = evp[i]
+                tv.profile_attn_main(ei[2], ei[3])
+                ei[0].record(stream)
+                s.mask(sptr)
+                ei[1].record(stream)
+                s.attn_paged(sptr)
+                ei[4].record(stream)
+                s.accept(sptr)
+                ei[5].record(stream)
+                s.commit(sptr)
+                ei[6].record(stream)
+            tv.profile_attn_main(None, None)
+            stream.synchronize()
+
+        def pavg(a, b):
+            return float(np.mean([evp[i][a].elapsed_time(evp[i][b]) for i in range(n_prof)])) * 1e-3
+
+        t_main = pavg(2, 3)
+        paged_breakdown = {
+            "page_size": paged.page_size, "num_slots": paged.num_slots,
+            "max_pages": int(paged.block_table.shape[1]),
+            "tree_verify_attn_paged_us": pavg(1, 4) * 1e6, "attn_main_paged_us": t_main * 1e6,
+            "kv_commit_paged_us": pavg(5, 6) * 1e6 if paged.page_size == 1 else None,
+            "kv_compact_accepted_copy_us": t_compact * 1e6,
+            "note": ("per-call times from events between eager calls (launch latency included); "
+                     "attn_main_paged_us from the kernel's own timestamps"),
+        }
+
     alen = sets[0].t["alen"].cpu().numpy()
     status = sets[0].t["status"].cpu().numpy()
     if (status & ~0).any():
@@ -461,8 +553,10 @@ def main() -> int:
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
-    roof["kernel"] = ("attn_main (tree_verify_step's instantiation, which also builds the masks)"
-                      if args.api == "fused" else "attn_main")
+    roof["kernel"] = {"fused": "attn_main (tree_verify_step's instantiation, which also builds "
+                               "the masks)",
+                      "separate": "attn_main",
+                      "paged": "attn_main (tree_verify_attn_paged's instantiation)"}[args.api]
     roof["kernel_us"] = t_main * 1e6
     roof["algorithmic_bytes"] = kv_bytes
     roof["algorithmic_flops"] = flops
@@ -484,9 +578,11 @@ def main() -> int:
         "config": {"workload": args.workload, "desc": w.spec.desc, "B": w.B, "T": w.T,
                    "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "prefix_tokens": int(L.sum()),
                    "Lmax": w.Lmax, "layers": 1, "mode": args.mode, "rotated_sets": n_sets,
-                   "split_keys": args.split_keys, "step_api": args.api,
+                   "split_keys": args.split_keys, "step_api": args.api, "kv": args.kv,
                    "graph_steps": graph_steps if args.mode == "graph" else None},
-        "ms_per_step_by_api": {args.api: ms_per_step, other: ms_other},
+        "ms_per_step_by_api": ({args.api: ms_per_step, other: ms_other} if other
+                               else {args.api: ms_per_step}),
+        "paged": paged_breakdown,
         "hbm_frac": value / HBM_PEAK_GBS,
         "attn_kv_gbps": kv_bytes / t_attn / 1e9,
         "attn_hbm_frac": kv_bytes / t_attn / 1e9 / HBM_PEAK_GBS,

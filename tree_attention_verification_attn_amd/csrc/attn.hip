@@ -153,10 +153,19 @@ __device__ inline void lds_dma16_addr(uint32_t lds, const void* addr) {
       : "memory");
 }
 
-// Read-only int32 tables read with wavefront-uniform indices: through the constant address
-// space they become scalar loads, which count on lgkmcnt and leave the vmcnt of the tile loads
-// alone.
-typedef const __attribute__((address_space(4))) int32_t const_i32;
+// One wavefront-wide 4-byte direct-to-LDS load: lane l's dword at `addr` lands at lds + 4*l.
+__device__ inline void lds_dma4_addr(uint32_t lds, const void* addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(addr)
+      : "memory");
+}
 
 // s_waitcnt vmcnt(n) (n <= 63), other counters untouched.
 template <int N>
@@ -336,56 +345,69 @@ void attn_main(AttnArgs a) {
   }
   const uint32_t smem_base = (uint32_t)(uintptr_t)smem;
 
-  // Paged K/V: the rows of one direct-load instruction are kRowsPerDma consecutive keys (one
-  // per group of kCPR lanes); their slots are read with scalar loads (uniform per group) and
-  // each lane keeps its group's.  Entries outside the pool are clamped into it and reported.
+  // Paged K/V: the rows of one direct-load instruction are kRowsPerDma consecutive keys, one
+  // per group of kCPR lanes.  Each lane's table entry (the page of its prefix key, or the slot
+  // of its tree node) is itself brought in by a 4-byte direct-to-LDS load into a small per-
+  // wavefront area, ahead of the tile: the entry loads join the tile loads in the one in-order
+  // vmcnt stream, so the waits below stay exact and no scalar load shares lgkmcnt with the LDS
+  // fragment reads.  At issue each lane reads its entry back and forms the slot.  Entries
+  // outside the pool are clamped into it and reported.
+  __shared__ __attribute__((aligned(256))) int32_t s_ent[kPaged ? 2 * kWaves * kDPW * 64 : 1];
   bool bad_slot = false;
-  auto check_slot = [&](long long slot) -> int {
-    const bool out = slot < 0 || slot >= a.num_slots;
-    bad_slot = bad_slot || out;
-    return out ? (slot < 0 ? 0 : a.num_slots - 1) : (int)slot;
+  // key position (prefix tiles) or node (tree tiles) of this lane's row in instruction i
+  auto row_key = [&](int tile, int i) __attribute__((always_inline)) -> int {
+    const int r = (wave * kDPW + i) * Lay::kRowsPerDma + lane / Lay::kCPR;
+    return tile < n_tree_tiles ? min((v0 + tile) * kKT + r, a.T - 1)
+                               : min(k0 + (tile - n_tree_tiles) * kKT + r, k1 - 1);
   };
-  auto issue_tile_paged = [&](int tile, uint32_t kl, uint32_t vl) {
+  auto ent_lds = [&](int tile, int i) __attribute__((always_inline)) -> uint32_t {
+    return (uint32_t)(uintptr_t)s_ent + ((((tile & 1) * kWaves + wave) * kDPW + i) * 64) * 4;
+  };
+  auto load_entries = [&](int tile) __attribute__((always_inline)) {  // kDPW loads
+    if constexpr (kPaged) {
+#pragma unroll
+      for (int i = 0; i < kDPW; ++i) {
+        const int key = row_key(tile, i);
+        const int32_t* src = tile < n_tree_tiles
+                                 ? a.tree_slot + (size_t)b * a.T + key
+                                 : a.table + (size_t)b * a.max_pages + (key >> a.log2P);
+        lds_dma4_addr(ent_lds(tile, i), src);
+      }
+    }
+  };
+  // the tile's entries have landed (the caller waited for them)
+  auto issue_tile_paged = [&](int tile, uint32_t kl, uint32_t vl) __attribute__((always_inline)) {
     const size_t hstride = (size_t)a.Hkv * kRB;  // bytes per pool slot
     const char* kpool = a.kc + (size_t)kvh * kRB;
     const char* vpool = a.vc + (size_t)kvh * kRB;
-    const int grp = lane / Lay::kCPR;
+    const int pmask = (1 << a.log2P) - 1;
 #pragma unroll
     for (int i = 0; i < kDPW; ++i) {
-      const int r0 = (wave * kDPW + i) * Lay::kRowsPerDma;  // first key row of the instruction
-      int mine = 0;
-      if (tile < n_tree_tiles) {
-        const_i32* ts = (const_i32*)a.tree_slot + (size_t)b * a.T;
-        const int base = (v0 + tile) * kKT + r0;
-#pragma unroll
-        for (int j = 0; j < Lay::kRowsPerDma; ++j) {
-          const int slot = check_slot(ts[min(base + j, a.T - 1)]);
-          mine = grp == j ? slot : mine;
-        }
-      } else {
-        const_i32* tb = (const_i32*)a.table + (size_t)b * a.max_pages;
-        const int base = k0 + (tile - n_tree_tiles) * kKT + r0;
-        const int pmask = (1 << a.log2P) - 1;
-#pragma unroll
-        for (int j = 0; j < Lay::kRowsPerDma; ++j) {
-          const int pos = min(base + j, k1 - 1);
-          const int page = tb[pos >> a.log2P];
-          const int slot =
-              check_slot(page < 0 ? -1LL : (long long)page * (pmask + 1) + (pos & pmask));
-          mine = grp == j ? slot : mine;
-        }
-      }
+      const int e = *(const int32_t*)((const char*)s_ent + (ent_lds(tile, i) -
+                                                            (uint32_t)(uintptr_t)s_ent) + 4 * lane);
+      const long long slot =
+          tile < n_tree_tiles
+              ? (long long)e
+              : (e < 0 ? -1LL : (long long)e * (pmask + 1) + (row_key(tile, i) & pmask));
+      const bool out = slot < 0 || slot >= a.num_slots;
+      bad_slot = bad_slot || out;
+      const int mine = out ? (slot < 0 ? 0 : a.num_slots - 1) : (int)slot;
       const size_t off = (size_t)mine * hstride + dma_chunk[i];
       lds_dma16_addr(kl + i * 1024, kpool + off);
       lds_dma16_addr(vl + i * 1024, vpool + off);
     }
   };
 
-  auto issue_tile = [&](int tile) {
+  auto issue_tile = [&](int tile) __attribute__((always_inline)) {
     const int stage = tile % kNS;
     const uint32_t kl = smem_base + stage * Lay::kStage + wave * kDPW * 1024;
     const uint32_t vl = kl + Lay::kTile;
     if constexpr (kPaged) {
+      if constexpr (!Lay::kCrossTile) {
+        // fp32 (the small exact path): entries fetched at issue, waiting for everything
+        load_entries(tile);
+        vm_wait<0>();
+      }
       issue_tile_paged(tile, kl, vl);
       return;
     }
@@ -413,9 +435,19 @@ void attn_main(AttnArgs a) {
   // The first tiles go out before the Q loads so the two latencies overlap; they are complete
   // before the block pipeline starts (vm_wait<0> below), so no compiler-tracked load is pending
   // inside it and its own waits count tile loads only.
+  if constexpr (kPaged && Lay::kCrossTile) {
+    // entries of tiles 0 and 1, then their data; the entries of tile 2 follow (the pipeline
+    // below keeps the entries of tile t+2 ahead of the data of tile t+1)
+    load_entries(0);
+    if (n_tiles > 1) load_entries(1);
+    vm_wait<0>();
+  }
 #pragma unroll
   for (int t = 0; t < Lay::kAhead; ++t)
     if (t < n_tiles) issue_tile(t);
+  if constexpr (kPaged && Lay::kCrossTile) {
+    if (n_tiles > 2) load_entries(2);
+  }
 
   // ---- Q fragments (B operand): row n, d = 16*ks + 8*h .. +7 (bf16) or 2*ks + h (fp32) -----
   using QFrag = typename std::conditional<kBF16, bf16x8, float>::type;
@@ -493,7 +525,28 @@ void attn_main(AttnArgs a) {
   // done with the tile whose stage tile t + kAhead takes (across tiles, tile t-2, whose last
   // reader is the O^T step of block 2t-3; one block after another, tile t-1), so that tile is
   // loaded now.
-  auto barrier_tile = [&](int t) {
+  auto barrier_tile = [&](int t) __attribute__((always_inline)) {
+    if constexpr (kPaged && Lay::kCrossTile) {
+      // Issue order per barrier t: entries of tile t+3, then data of tile t+2.  Loads newer
+      // than tile t's data: entries of t+2 and data of t+1 (issued at barrier t-1).
+      constexpr int En = kDPW, Dd = 2 * kDPW;
+      if (t + 2 < n_tiles) vm_wait<En + Dd>();
+      else if (t + 1 < n_tiles) vm_wait<Dd>();
+      else vm_wait<0>();
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 3 < n_tiles) load_entries(t + 3);
+      if (t + 2 < n_tiles) {
+        // entries of t+2 have landed once only data of t+1 and entries of t+3 may remain
+        if (t + 3 < n_tiles) vm_wait<Dd + En>();
+        else vm_wait<Dd>();
+        asm volatile("" ::: "memory");
+        issue_tile(t + 2);
+      }
+      return;
+    }
     // newer tiles may stay in flight
     const int newer = min(Lay::kAhead - 1, n_tiles - 1 - t);
     if (Lay::kAhead >= 3 && newer >= 2) vm_wait<(Lay::kAhead >= 3 ? 4 * kDPW : 0)>();
@@ -508,7 +561,7 @@ void attn_main(AttnArgs a) {
 
   // LDS offsets of the lane's fragments in the tile whose K (V) is being read.
   uint32_t kaddr[kBF16 ? kKS : 1], vaddr[kBF16 ? 2 * kDB : 1];
-  auto set_k = [&](int tile) {
+  auto set_k = [&](int tile) __attribute__((always_inline)) {
     if constexpr (kBF16) {
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks) kaddr[ks] = koff[ks] + (tile % kNS) * Lay::kStage;
@@ -516,7 +569,7 @@ void attn_main(AttnArgs a) {
       kaddr[0] = (tile % kNS) * Lay::kStage;
     }
   };
-  auto set_v = [&](int tile) {
+  auto set_v = [&](int tile) __attribute__((always_inline)) {
     if constexpr (kBF16) {
 #pragma unroll
       for (int i = 0; i < 2 * kDB; ++i)
@@ -527,7 +580,7 @@ void attn_main(AttnArgs a) {
   };
 
   // S^T = K Q^T for block j (its tile set by set_k)
-  auto qk = [&](int j, f32x16& S) {
+  auto qk = [&](int j, f32x16& S) __attribute__((always_inline)) {
     const int kb = j & 1;
     S = f32x16{};
 #pragma unroll
@@ -546,7 +599,7 @@ void attn_main(AttnArgs a) {
   };
 
   // O^T += V^T P^T for block j (its tile set by set_v)
-  auto pv = [&](int j, const PBlock<kBF16>& P) {
+  auto pv = [&](int j, const PBlock<kBF16>& P) __attribute__((always_inline)) {
     const int kb = j & 1;
     if constexpr (kBF16) {
       // 16-key step st: keys kb*32 + 16st + {4h..4h+3} (elements 0-3) and kb*32 + 16st + 8 +
@@ -584,7 +637,7 @@ void attn_main(AttnArgs a) {
   // Mask block j's scores where needed: tree keys by the row's ancestor bits, keys at or past
   // the end of the tree or of the chunk.  Element e is key kb*32 + 8*(e/4) + 4*h + e%4 of the
   // tile; a tree tile covers nodes 64*tile .. 64*tile+63, so one mask word per row.
-  auto mask_block = [&](int j, f32x16& S) {
+  auto mask_block = [&](int j, f32x16& S) __attribute__((always_inline)) {
     const int tile = j >> 1, kb = j & 1;
     const bool is_tree = tile < n_tree_tiles;
     const int base = is_tree ? (v0 + tile) * kKT : k0 + (tile - n_tree_tiles) * kKT;
@@ -601,7 +654,7 @@ void attn_main(AttnArgs a) {
   };
 
   // p = 2^(S*c - m_run), packed as the P operand; returns the lane's sum of the p it packed.
-  auto exp_pack = [&](const f32x16& S, float mb, PBlock<kBF16>& P) -> float {
+  auto exp_pack = [&](const f32x16& S, float mb, PBlock<kBF16>& P) __attribute__((always_inline)) -> float {
     float sum = 0.f;
     if constexpr (kBF16) {
       // the row sum adds the fp32 values; only the O^T operand is rounded to bf16
@@ -632,7 +685,7 @@ void attn_main(AttnArgs a) {
   // block sum is at most kSumLimit has every p in range (p <= sum), and the block is taken as
   // is.  Otherwise (a score outgrew m_run, or m_run is unset) the wavefront takes the
   // slow path: exact row max over the block, new m_run, alpha = 2^(m_old - m_new), p again.
-  auto softmax = [&](const f32x16& S, PBlock<kBF16>& P) {
+  auto softmax = [&](const f32x16& S, PBlock<kBF16>& P) __attribute__((always_inline)) {
     float bsum = exp_pack(S, m_run, P);
     rescale_o = __ballot(!(bsum <= kSumLimit)) != 0;  // also catches inf and NaN
     if (rescale_o) {
@@ -650,7 +703,7 @@ void attn_main(AttnArgs a) {
     }
   };
 
-  auto rescale = [&]() {
+  auto rescale = [&]() __attribute__((always_inline)) {
     if (rescale_o) {
 #pragma unroll
       for (int db = 0; db < kDB; ++db) oacc[db] *= alpha;
@@ -659,7 +712,7 @@ void attn_main(AttnArgs a) {
 
   // Keeps the softmax of a region inside it: without a use here the compiler sinks the
   // exponentials and sums to their next uses, out of reach of the region's matrix work.
-  auto end_region = [&](const PBlock<kBF16>& P) {
+  auto end_region = [&](const PBlock<kBF16>& P) __attribute__((always_inline)) {
     if constexpr (kBF16) {
 #pragma unroll
       for (int st = 0; st < 2; ++st) asm volatile("" ::"v"(P.v[st]));
@@ -678,7 +731,7 @@ void attn_main(AttnArgs a) {
   // Se / Pe, odd blocks' in So / Po.
   f32x16 Se, So;
   PBlock<kBF16> Pe, Po;
-  auto masks_from_lds = [&]() {
+  auto masks_from_lds = [&]() __attribute__((always_inline)) {
     if constexpr (kMasks) {
       if (row_ok && n_tree_tiles) {
         mk0 = s_anc[row_t][0];
@@ -742,7 +795,7 @@ void attn_main(AttnArgs a) {
   }
 
   // ---- epilogue ----------------------------------------------------------------------------
-  if (kPaged && bad_slot && tid == 64 * wave && a.status) atomicOr(a.status + b, TV_BAD_PAGE);
+  if (kPaged && __ballot(bad_slot) && lane == 0 && a.status) atomicOr(a.status + b, TV_BAD_PAGE);
   l_run += partner(l_run);
 
   if (direct) {
