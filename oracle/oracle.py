@@ -16,6 +16,7 @@ ORC_BAD_TREE = 0x1
 ORC_OVERFLOW = 0x2
 ORC_BAD_LEN = 0x4
 ORC_BAD_PATH = 0x8
+ORC_BAD_TOKEN = 0x20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tree_oracle.c")
@@ -68,6 +69,8 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_accept.restype = None
     lib.oracle_compact.argtypes = [i, P, P, P, P, P, P, P, P, i, i, i, i, i, P]
     lib.oracle_compact.restype = None
+    lib.oracle_accept_stochastic.argtypes = [P, P, P, P, P, P, i, i, i, i, P, P, P, P]
+    lib.oracle_accept_stochastic.restype = None
     return lib
 
 
@@ -234,3 +237,26 @@ def commit_paged(table, cache_len, tree_slot, accept_path, accept_len, num_slots
                             _p(accept_path), _p(accept_len), B, T, int(num_slots),
                             _p(free_slots), _p(top), _p(st))
     return out_len, int(top[0]), st
+
+
+def accept_stochastic(parent, draft, p, q, u_acc, u_res, without_replacement=False, lib=None):
+    """Rejection sampling over the draft tree (``oracle_accept_stochastic``): p and q are
+    [B, T, V] float32 target and draft distributions, u_acc and u_res [B, T] float64 uniforms.
+    Returns (accept_path [B,T], accept_len [B], bonus_tok [B], status [B])."""
+    lib = lib or load()
+    parent, draft = _i32(parent), _i32(draft)
+    B, T = parent.shape
+    p = np.ascontiguousarray(p, dtype=np.float32)
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    V = p.shape[-1]
+    assert p.shape == (B, T, V) and q.shape == (B, T, V)
+    u_acc = np.ascontiguousarray(u_acc, dtype=np.float64).reshape(B, T)
+    u_res = np.ascontiguousarray(u_res, dtype=np.float64).reshape(B, T)
+    path = np.empty((B, T), np.int32)
+    alen = np.empty(B, np.int32)
+    bonus = np.empty(B, np.int32)
+    status = np.zeros(B, np.int32)
+    lib.oracle_accept_stochastic(_p(parent), _p(draft), _p(p), _p(q), _p(u_acc), _p(u_res), B, T,
+                                 V, int(bool(without_replacement)), _p(path), _p(alen), _p(bonus),
+                                 _p(status))
+    return path, alen, bonus, status

@@ -31,6 +31,11 @@
  *                  Committing the accepted path by pointer swap makes the table's entries for
  *                  positions L_b .. L_b+n-1 name the accepted nodes' slots, in path order, and
  *                  returns the rejected nodes' slots to a free list; no row is copied.
+ *   stochastic     (lesty.tech section 4, rejection sampling) a drafted token x is accepted with
+ *   acceptance     probability min(1, p(x)/q(x)); after a rejection the residual
+ *                  max(0, p - q), normalised, is what the next sibling is tested against, and
+ *                  what the bonus token is drawn from when no child is accepted.  The random
+ *                  numbers are inputs (one uniform per tested child, one per sampling node).
  *
  * Floating inputs are either float32 (elem_bits = 32) or raw bfloat16 bit patterns
  * (elem_bits = 16), which are widened exactly.
@@ -435,4 +440,101 @@ void oracle_commit_paged(int32_t* table, int max_pages, const int32_t* cache_len
     cache_len_out[b] = L + n;
   }
   free(on_path);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* stochastic acceptance                                                                       */
+/* ------------------------------------------------------------------------------------------ */
+
+#define ORC_BAD_TOKEN 0x20
+
+/* Inverse-CDF draw from the (unnormalised) distribution r[0..V-1]: the smallest y whose running
+ * sum exceeds u times the total; the largest y with r[y] > 0 if none does; -1 if r has no mass. */
+static int draw_token(const double* r, int V, double u) {
+  double total = 0.0;
+  for (int y = 0; y < V; ++y) total += r[y];
+  const double thr = u * total;
+  double run = 0.0;
+  int last = -1;
+  for (int y = 0; y < V; ++y) {
+    if (r[y] > 0.0) last = y;
+    run += r[y];
+    if (run > thr && r[y] > 0.0) return y;
+  }
+  return last;
+}
+
+/* Rejection sampling over a draft tree (lesty.tech "EAGLE-2 vs. Medusa", section 4).
+ *
+ * p[b,u,:] is the target model's next-token distribution after node u and q[b,u,:] the draft
+ * model's, from which u's children were drawn; the uniforms u_acc and u_res are fp64.  Starting
+ * at the root (always kept), the walk
+ * tries the children of the current node in index order.  A child with token x is accepted iff
+ * u_acc[b,c] * q_j(x) < p_j(x), i.e. with probability min(1, p_j(x) / q_j(x)).  p_1 = p[b,u],
+ * q_1 = q[b,u]; a rejection replaces p_j by the residual max(0, p_j - q_j) / sum(max(0, p_j - q_j))
+ * for the next child, and with without_replacement != 0 also removes x from q_j and renormalises
+ * it (q_{j+1} = q_j with q_j(x) set to zero, divided by 1 - q_j(x); all zero if that is not
+ * positive).  An accepted child becomes the current node.  When no child is accepted, the bonus
+ * token is drawn from the current p_j with u_res[b,u] (draw_token).  If a residual has no mass,
+ * no further child is tried and the bonus is drawn from the p_j the rejected child faced.  A child
+ * whose token lies outside [0, V) is skipped and ORC_BAD_TOKEN is OR-ed into status[b].
+ * Outputs as oracle_accept. */
+void oracle_accept_stochastic(const int32_t* parent, const int32_t* draft, const float* p,
+                              const float* q, const double* u_acc, const double* u_res, int B,
+                              int T, int V, int without_replacement, int32_t* accept_path,
+                              int32_t* accept_len, int32_t* bonus_tok, int32_t* status) {
+  double* pj = (double*)malloc(sizeof(double) * (size_t)V);
+  double* qj = (double*)malloc(sizeof(double) * (size_t)V);
+  double* res = (double*)malloc(sizeof(double) * (size_t)V);
+  for (int b = 0; b < B; ++b) {
+    const int32_t* pb = parent + (size_t)b * T;
+    const int valid = tree_is_valid(pb, T);
+    int32_t* out = accept_path + (size_t)b * T;
+    for (int k = 0; k < T; ++k) out[k] = -1;
+    int n = 0, u = 0;
+    out[n++] = 0;
+    for (;;) {
+      const float* pu = p + ((size_t)b * T + u) * V;
+      const float* qu = q + ((size_t)b * T + u) * V;
+      for (int y = 0; y < V; ++y) {
+        pj[y] = pu[y];
+        qj[y] = qu[y];
+      }
+      int next = -1;
+      for (int c = u + 1; c < T && valid; ++c) {
+        if (pb[c] != u) continue;
+        const int x = draft[(size_t)b * T + c];
+        if (x < 0 || x >= V) {
+          status[b] |= ORC_BAD_TOKEN;
+          continue;
+        }
+        if (u_acc[(size_t)b * T + c] * qj[x] < pj[x]) {
+          next = c;
+          break;
+        }
+        double z = 0.0;
+        for (int y = 0; y < V; ++y) {
+          res[y] = pj[y] - qj[y] > 0.0 ? pj[y] - qj[y] : 0.0;
+          z += res[y];
+        }
+        if (!(z > 0.0)) break; /* nothing left to resample from: draw from pj */
+        for (int y = 0; y < V; ++y) pj[y] = res[y] / z;
+        if (without_replacement) {
+          const double keep = 1.0 - qj[x];
+          qj[x] = 0.0;
+          for (int y = 0; y < V; ++y) qj[y] = keep > 0.0 ? qj[y] / keep : 0.0;
+        }
+      }
+      if (next < 0) {
+        bonus_tok[b] = draw_token(pj, V, u_res[(size_t)b * T + u]);
+        break;
+      }
+      out[n++] = next;
+      u = next;
+    }
+    accept_len[b] = n;
+  }
+  free(pj);
+  free(qj);
+  free(res);
 }

@@ -11,7 +11,13 @@ oracle disagrees with something the pages or the mathematics fix:
   chain trees and single-node trees, and an explicit dense-mask softmax on random trees;
 * hand-derived acceptance cases (tests/golden/accept_hand_cases.txt), the chain extremes and a
   brute-force enumeration of root-to-node paths;
-* compaction against direct row selection, including tree rows that live inside the cache.
+* compaction against direct row selection, including tree rows that live inside the cache;
+* paged gather and the pointer-swap commit against the pinned dense attention and copy;
+* stochastic acceptance: hand-derived cases (tests/golden/stochastic_hand_cases.txt and a
+  duplicate-sibling case), the page's losslessness claim checked exactly by enumerating every
+  draft and integrating the uniforms out (one and two levels, both sibling modes), the reduction
+  to the greedy rule for one-hot targets, and to a plain inverse-CDF draw (numpy.searchsorted)
+  when q = p.
 
 ``test_oracle_pins.py`` runs every pin against the oracle; ``test_oracle_mutants.py`` runs them
 against deliberately broken copies of the oracle source to show that each plausible mistake is
@@ -635,6 +641,311 @@ def pin_commit_paged_matches_copy(lib):
     assert (tbl2[[0, 1, 2, 5]] == t0[[0, 1, 2, 5]]).all()
 
 
+# ----------------------------------------------------------------------------------------------
+# stochastic acceptance (lesty.tech "EAGLE-2 vs. Medusa", section 4: rejection sampling)
+# ----------------------------------------------------------------------------------------------
+def _frac(tok: str) -> float:
+    from fractions import Fraction
+
+    return float(Fraction(tok.strip()))
+
+
+def read_stochastic_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "stochastic_hand_cases.txt"), encoding="utf-8") as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            f_ = [x.strip() for x in line.split("|")]
+            name, mode = f_[0], int(f_[1])
+            draft = [int(x) for x in f_[2].split()]
+            rows = []
+            for field in (f_[3], f_[4]):
+                r = np.full((8, 4), 0.25)
+                for ent in filter(None, (e.strip() for e in field.split(";"))):
+                    node, vals = ent.split(":")
+                    r[int(node)] = [_frac(v) for v in vals.split(",")]
+                rows.append(r)
+            u_acc = [_frac(x) for x in f_[5].split()]
+            u_res = [_frac(x) for x in f_[6].split()]
+            path = [int(x) for x in f_[7].split(",")]
+            cases.append((name, mode, draft, rows[0], rows[1], u_acc, u_res, path, int(f_[8])))
+    return cases
+
+
+def pin_stochastic_hand_cases(lib):
+    parent = worked_tree_parent()
+    for name, mode, draft, p, q, u_acc, u_res, want_path, want_bonus in read_stochastic_cases():
+        path, n, bonus, st = O.accept_stochastic(parent[None], np.array([draft]), p[None], q[None],
+                                                 np.array([u_acc]), np.array([u_res]),
+                                                 without_replacement=mode, lib=lib)
+        assert list(path[0, : n[0]]) == want_path, (name, path[0, : n[0]])
+        assert (path[0, n[0]:] == -1).all(), name
+        assert bonus[0] == want_bonus, (name, bonus[0])
+        assert st[0] == 0, name
+
+
+def pin_stochastic_duplicate_siblings(lib):
+    """Hand-derived (no program computed the expected values): a root with three children whose
+    tokens are 0, 0 and 1; V = 4; p = [1/4, 1/4, 3/8, 1/8], q = [1/2, 1/8, 1/8, 1/4];
+    u_acc = 3/4, 1/2, 0.9 for children 1..3; u_res = 1/2 everywhere; leaves' p uniform.
+
+    Both modes: child 1 (token 0): 3/4 * 1/2 = 3/8 >= 1/4, rejected; residual
+    max(0, p - q) = [0, 1/8, 1/4, 0] -> p_2 = [0, 1/3, 2/3, 0].
+    Mode 0: child 2 (token 0) has p_2(0) = 0, rejected; residual max(0, p_2 - q) =
+    [0, 5/24, 13/24, 0] -> p_3 = [0, 5/18, 13/18, 0]; child 3 (token 1): ratio (5/18)/(1/8) > 1,
+    kept; node 3 is a leaf, uniform p, u_res 1/2 -> running sums 1/4, 1/2, 3/4 -> token 2.
+    Path 0,3; bonus 2.
+    Mode 1: q loses token 0: q_2 = [0, 1/4, 1/4, 1/2].  Child 2 (token 0 again): p_2(0) = 0,
+    rejected; residual max(0, p_2 - q_2) = [0, 1/12, 5/12, 0] -> p_3 = [0, 1/6, 5/6, 0]; token 0
+    is already out of q, so q_3 = q_2.  Child 3 (token 1): 0.9 * 1/4 = 0.225 >= 1/6, rejected;
+    residual [0, 0, 7/12, 0] -> token 2.  Path 0; bonus 2."""
+    parent = np.array([[-1, 0, 0, 0]], np.int32)
+    draft = np.array([[0, 0, 0, 1]], np.int32)
+    p = np.full((1, 4, 4), 0.25, np.float32)
+    q = p.copy()
+    p[0, 0] = [0.25, 0.25, 0.375, 0.125]
+    q[0, 0] = [0.5, 0.125, 0.125, 0.25]
+    u_acc = np.array([[0.5, 0.75, 0.5, 0.9]])
+    u_res = np.full((1, 4), 0.5)
+    for mode, want_path in ((0, [0, 3]), (1, [0])):
+        path, n, bonus, st = O.accept_stochastic(parent, draft, p, q, u_acc, u_res,
+                                                 without_replacement=mode, lib=lib)
+        assert list(path[0, : n[0]]) == want_path and bonus[0] == 2 and st[0] == 0, (mode, path, bonus)
+
+
+def walk_distribution(lib, parent, draft, p, q, mode):
+    """Exact probability of every emitted token sequence (accepted tokens, then the bonus) of the
+    stochastic walk, with the uniforms integrated out.  The oracle is used as a black box: every
+    acceptance is monotone in its uniform (accepted below a threshold) and every draw is monotone
+    in its uniform (inverse CDF), so each branch's probability is the length of a uniform interval
+    found by bisection (to 2^-50)."""
+    from collections import defaultdict
+
+    T, V = len(parent), p.shape[-1]
+    kids = {u: [c for c in range(u + 1, T) if parent[c] == u] for u in range(T)}
+    u_acc, u_res = np.full(T, 0.5), np.full(T, 0.5)
+
+    def run():
+        path, n, bonus, _ = O.accept_stochastic(parent[None], draft[None], p[None], q[None],
+                                                u_acc[None], u_res[None],
+                                                without_replacement=mode, lib=lib)
+        return list(path[0, : n[0]]), int(bonus[0])
+
+    def edge(pred):  # sup{x in [0, 1): pred(x)} for pred true on a lower interval
+        if not pred(0.0):
+            return 0.0
+        top = 1.0 - 2.0 ** -40
+        if pred(top):
+            return 1.0
+        lo, hi = 0.0, top
+        for _ in range(50):
+            mid = 0.5 * (lo + hi)
+            lo, hi = (mid, hi) if pred(mid) else (lo, mid)
+        return lo
+
+    out = defaultdict(float)
+
+    def visit(u, prob, emitted):
+        for c in kids[u]:
+            if not 0 <= draft[c] < V:
+                continue
+
+            def accepted(x, c=c):
+                u_acc[c] = x
+                return c in run()[0]
+
+            thr = edge(accepted)
+            if thr > 0.0:
+                u_acc[c] = 0.5 * thr
+                visit(c, prob * thr, emitted + (int(draft[c]),))
+            if thr >= 1.0:
+                return
+            u_acc[c] = 0.5 * (thr + 1.0)
+            prob *= 1.0 - thr
+        # no child accepted: the bonus draw at u
+        lo = [0.0]
+        for y in range(1, V):
+            def below(x, y=y):
+                u_res[u] = x
+                return run()[1] < y
+            lo.append(edge(below))
+        lo.append(1.0)
+        for y in range(V):
+            if lo[y + 1] > lo[y]:
+                out[emitted + (y,)] += prob * (lo[y + 1] - lo[y])
+
+    visit(0, 1.0, ())
+    return out
+
+
+def _draft_tuples(q_row, k, mode):
+    """Every ordered k-tuple of drafted tokens with its probability: independent draws from q
+    (mode 0) or draws without replacement (mode 1)."""
+    V = len(q_row)
+    for tup in itertools.product(range(V), repeat=k):
+        if mode and len(set(tup)) < k:
+            continue
+        w, used = 1.0, 0.0
+        for x in tup:
+            w *= q_row[x] / (1.0 - used) if mode else q_row[x]
+            used += q_row[x]
+        if w > 0.0:
+            yield tup, w
+
+
+def _rand_dist(rng, V, zeros=()):
+    """A random distribution with the given zero entries whose values are multiples of 1/256
+    summing to exactly one (exact in float32), so that losslessness can be checked to 1e-9."""
+    live = [y for y in range(V) if y not in zeros]
+    c = np.zeros(V, np.int64)
+    for y in live[:-1]:
+        c[y] = rng.integers(1, 256 // len(live) + 1)
+    c[live[-1]] = 256 - c.sum()
+    return (c / 256.0).astype(np.float32)
+
+
+def pin_stochastic_lossless_one_level(lib):
+    """The page's claim, checked exactly: with the children of a node drafted from q
+    (independently for mode 0, without replacement for mode 1), the first emitted token is
+    distributed exactly as p, whatever p and q are (zeros included)."""
+    rng = np.random.default_rng(51)
+    V = 4
+    for mode in (0, 1):
+        for k in (1, 2, 3):
+            for trial in range(2):
+                p0 = _rand_dist(rng, V, zeros=(trial,))
+                q0 = _rand_dist(rng, V, zeros=((trial + 2) % V,))
+                parent = np.array([-1] + [0] * k, np.int32)
+                p = np.tile(p0, (k + 1, 1))
+                q = np.tile(q0, (k + 1, 1))
+                first = np.zeros(V)
+                for tup, w in _draft_tuples(q0.astype(np.float64), k, mode):
+                    draft = np.array([0, *tup], np.int32)
+                    for seq, pr in walk_distribution(lib, parent, draft, p, q, mode).items():
+                        first[seq[0]] += w * pr
+                want = p0.astype(np.float64) / p0.astype(np.float64).sum()
+                assert np.abs(first - want).max() < 1e-9, (mode, k, first, want)
+
+
+def pin_stochastic_lossless_two_levels(lib):
+    """Two levels: the root's two children are drafted from q_root, each child's own child from
+    the draft distribution after that child's token.  The first emitted token follows p_root and,
+    after a kept first token y, the second follows the target distribution after y."""
+    rng = np.random.default_rng(52)
+    V = 3
+    P1, Q1 = _rand_dist(rng, V, zeros=(1,)), _rand_dist(rng, V)
+    P2 = [_rand_dist(rng, V, zeros=((y + 1) % V,)) for y in range(V)]
+    Q2 = [_rand_dist(rng, V, zeros=(y,)) for y in range(V)]
+    parent = np.array([-1, 0, 0, 1, 2], np.int32)
+    for mode in (0, 1):
+        joint = np.zeros((V, V))
+        first = np.zeros(V)
+        for top, w in _draft_tuples(Q1.astype(np.float64), 2, mode):
+            for g1, w1 in _draft_tuples(Q2[top[0]].astype(np.float64), 1, mode):
+                for g2, w2 in _draft_tuples(Q2[top[1]].astype(np.float64), 1, mode):
+                    draft = np.array([0, top[0], top[1], g1[0], g2[0]], np.int32)
+                    p = np.stack([P1, P2[top[0]], P2[top[1]], P1, P1])
+                    q = np.stack([Q1, Q2[top[0]], Q2[top[1]], Q1, Q1])
+                    for seq, pr in walk_distribution(lib, parent, draft, p, q, mode).items():
+                        first[seq[0]] += w * w1 * w2 * pr
+                        if len(seq) >= 2:
+                            joint[seq[0], seq[1]] += w * w1 * w2 * pr
+        want1 = P1.astype(np.float64) / P1.astype(np.float64).sum()
+        assert np.abs(first - want1).max() < 1e-9, (mode, first, want1)
+        for y in range(V):
+            if joint[y].sum() > 1e-12:
+                cond = joint[y] / joint[y].sum()
+                want2 = P2[y].astype(np.float64) / P2[y].astype(np.float64).sum()
+                assert np.abs(cond - want2).max() < 1e-9, (mode, y, cond, want2)
+
+
+def _distinct_sibling_tokens(rng, parent, V):
+    T = len(parent)
+    draft = np.zeros(T, np.int32)
+    for u in range(T):
+        kids = [c for c in range(u + 1, T) if parent[c] == u]
+        draft[kids] = rng.choice(V, size=len(kids), replace=False)
+    return draft
+
+
+def pin_stochastic_onehot_is_greedy(lib):
+    """A one-hot target distribution (temperature 0) turns rejection sampling into the greedy
+    rule: with distinct sibling tokens the walk equals the pinned greedy acceptance, and the bonus
+    is the target's token at the last kept node, whatever the uniforms and q."""
+    rng = np.random.default_rng(53)
+    V = 40
+    for mode in (0, 1):
+        for T in (1, 2, 9, 40, 100):
+            B = 4
+            parents = np.stack([random_parent(rng, T) for _ in range(B)]).astype(np.int32)
+            draft = np.stack([_distinct_sibling_tokens(rng, parents[b], V) for b in range(B)])
+            target = rng.integers(0, V, size=(B, T)).astype(np.int32)
+            # make acceptances likely: a node's target is often one of its children's tokens
+            for b in range(B):
+                for u in range(T):
+                    kids = [c for c in range(u + 1, T) if parents[b, c] == u]
+                    if kids and rng.random() < 0.7:
+                        target[b, u] = draft[b, rng.choice(kids)]
+            p = np.zeros((B, T, V), np.float32)
+            np.put_along_axis(p, target[..., None], 1.0, axis=2)
+            q = rng.random((B, T, V)).astype(np.float32) + 0.01
+            q /= q.sum(-1, keepdims=True)
+            u_acc = rng.random((B, T)).astype(np.float32)
+            u_res = rng.random((B, T)).astype(np.float32)
+            path, n, bonus, st = O.accept_stochastic(parents, draft, p, q, u_acc, u_res,
+                                                     without_replacement=mode, lib=lib)
+            g_path, g_n, g_bonus = O.accept(parents, draft, target, lib=lib)
+            assert np.array_equal(n, g_n) and np.array_equal(path, g_path), (mode, T)
+            assert np.array_equal(bonus, g_bonus) and (st == 0).all(), (mode, T)
+
+
+def pin_stochastic_q_equals_p(lib):
+    """q = p: every tested child has ratio 1 and is kept, so the walk follows first children to a
+    leaf, and the bonus is an ordinary inverse-CDF draw from the leaf's p
+    (numpy.searchsorted over the running sums)."""
+    rng = np.random.default_rng(54)
+    V = 50
+    for mode in (0, 1):
+        for T in (1, 7, 60, 128):
+            B = 3
+            parents = np.stack([random_parent(rng, T) for _ in range(B)]).astype(np.int32)
+            draft = rng.integers(3, V, size=(B, T)).astype(np.int32)  # tokens with mass
+            p = rng.random((B, T, V)) ** 4
+            p[..., :3] = 0.0
+            p = (p / p.sum(-1, keepdims=True)).astype(np.float32)
+            u_acc = rng.random((B, T)).astype(np.float32)
+            u_res = rng.random((B, T)).astype(np.float32)
+            path, n, bonus, st = O.accept_stochastic(parents, draft, p, p.copy(), u_acc, u_res,
+                                                     without_replacement=mode, lib=lib)
+            for b in range(B):
+                want = [0]
+                while True:
+                    kids = [c for c in range(T) if parents[b, c] == want[-1]]
+                    if not kids:
+                        break
+                    want.append(kids[0])
+                assert list(path[b, : n[b]]) == want, (mode, T, b)
+                leaf = p[b, want[-1]].astype(np.float64)
+                cdf = np.cumsum(leaf)
+                y = int(np.searchsorted(cdf, u_res[b, want[-1]] * cdf[-1], side="right"))
+                assert bonus[b] == y, (mode, T, b, bonus[b], y)
+
+
+def pin_stochastic_bad_tokens(lib):
+    """A child whose token is outside the vocabulary is skipped and flagged; the walk goes on as
+    if it were absent (compared with the same tree without that child's token being tested)."""
+    parent = worked_tree_parent()
+    V = 4
+    p = np.full((1, 8, V), 0.25, np.float32)
+    q = p.copy()
+    u = np.full((1, 8), 0.5, np.float32)
+    draft = np.array([[0, 7, 2, 0, 0, -1, 0, 0]], np.int32)  # node 1 and node 5 are out of range
+    path, n, bonus, st = O.accept_stochastic(parent[None], draft, p, q, u, u, lib=lib)
+    assert list(path[0, : n[0]]) == [0, 2] and st[0] == O.ORC_BAD_TOKEN
+    assert bonus[0] == 2  # uniform p at node 2, u_res 0.5: running sums 0.25, 0.5, 0.75 -> 2
+
+
 ALL_PINS = [
     pin_worked_tree_mask,
     pin_mask_closure_bruteforce,
@@ -656,4 +967,11 @@ ALL_PINS = [
     pin_paged_gather_and_attention,
     pin_commit_paged_hand_case,
     pin_commit_paged_matches_copy,
+    pin_stochastic_hand_cases,
+    pin_stochastic_duplicate_siblings,
+    pin_stochastic_bad_tokens,
+    pin_stochastic_q_equals_p,
+    pin_stochastic_onehot_is_greedy,
+    pin_stochastic_lossless_one_level,
+    pin_stochastic_lossless_two_levels,
 ]

@@ -78,6 +78,34 @@ MUTANTS = {
     # commit overflow check off by one
     "commit_overflow": ("if (!bits && (long)L + n > max_pages) bits |= ORC_OVERFLOW;",
                         "if (!bits && (long)L + n > max_pages + 1) bits |= ORC_OVERFLOW;"),
+    # stochastic: residual without the clamp at zero
+    "stoch_residual_no_max": ("res[y] = pj[y] - qj[y] > 0.0 ? pj[y] - qj[y] : 0.0;",
+                              "res[y] = pj[y] - qj[y];"),
+    # stochastic: residual not renormalised
+    "stoch_residual_unnormalised": ("for (int y = 0; y < V; ++y) pj[y] = res[y] / z;",
+                                    "for (int y = 0; y < V; ++y) pj[y] = res[y];"),
+    # stochastic: ratio upside down
+    "stoch_ratio_inverted": ("if (u_acc[(size_t)b * T + c] * qj[x] < pj[x]) {",
+                             "if (u_acc[(size_t)b * T + c] * pj[x] < qj[x]) {"),
+    # stochastic, without replacement: the rejected token stays in q
+    "stoch_q_keeps_rejected": ("          qj[x] = 0.0;\n", ""),
+    # stochastic, without replacement: q not renormalised after the removal
+    "stoch_q_unnormalised": ("qj[y] = keep > 0.0 ? qj[y] / keep : 0.0;", "qj[y] = qj[y];"),
+    # stochastic: bonus drawn from the target distribution instead of the residual
+    "stoch_bonus_from_p": ("bonus_tok[b] = draw_token(pj, V, u_res[(size_t)b * T + u]);",
+                           "for (int y = 0; y < V; ++y) res[y] = pu[y];\n"
+                           "        bonus_tok[b] = draw_token(res, V, u_res[(size_t)b * T + u]);"),
+    # stochastic: children tried from the last index down
+    "stoch_children_reversed": ("for (int c = u + 1; c < T && valid; ++c) {",
+                                "for (int c = T - 1; c > u && valid; --c) {"),
+    # stochastic: the bonus uses the parent's uniform
+    "stoch_uniform_of_parent": ("draw_token(pj, V, u_res[(size_t)b * T + u]);",
+                                "draw_token(pj, V, u_res[(size_t)b * T + (u ? pb[u] : 0)]);"),
+    # stochastic: no guard for a residual without mass
+    "stoch_no_zero_guard": ("if (!(z > 0.0)) break; /* nothing left to resample from: draw from pj */",
+                            ""),
+    # stochastic: an out-of-vocabulary child is tested (as token 0) instead of skipped
+    "stoch_bad_token_tested": ("          status[b] |= ORC_BAD_TOKEN;\n          continue;\n", ""),
 }
 
 
