@@ -55,6 +55,7 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_BAD_LEN 0x4  /* cache_len[b] < 0 or > Lmax */
 #define TV_BAD_PATH 0x8 /* accept_len[b] outside [0, T] or an accepted index outside [0, T) */
 #define TV_BAD_PAGE 0x10 /* paged K/V: a block-table entry or tree slot outside the pool */
+#define TV_BAD_TOKEN 0x20 /* stochastic acceptance: a tried child's token outside [0, V) */
 
 /* Human-readable name of a tv_status return value or of a single status bit. */
 const char* tv_status_string(int code);
@@ -142,6 +143,42 @@ int tv_profile_attn_main(void* ev_before, void* ev_after);
 int tree_accept(const uint64_t* anc_mask, const int32_t* draft_tok, const int32_t* target_tok,
                 int B, int T, int32_t* accept_path, int32_t* accept_len, int32_t* bonus_tok,
                 void* stream);
+
+/*
+ * tree_accept_stochastic — acceptance under sampling (temperature > 0) by rejection sampling,
+ * tried child by child (lesty.tech section 4: a drafted token x is kept with probability
+ * min(1, p(x)/q(x)); after a rejection the token comes from the residual max(0, p - q),
+ * normalised).  p[b,u,:] is the target model's next-token distribution after node u and
+ * q[b,u,:] the draft model's, from which u's children were drawn.  From the root (always kept)
+ * the walk tries the children of the current node in index order: child c with token x is kept
+ * iff u_acc[b,c] * q_j(x) < p_j(x); a rejection replaces p_j by the residual for the next child
+ * (and, with without_replacement = 1, removes x from q_j and renormalises it by 1 - q_j(x)).  The
+ * first kept child becomes the current node.  When none is kept, the bonus token is the smallest
+ * y whose running sum of p_j exceeds u_res[b,u] times its total (the last token with mass if
+ * none does; -1 if p_j has none).  If a residual has no mass left (possible only when p or q
+ * does not sum to one), no further child is tried and the bonus is drawn from the p_j the
+ * rejected child faced.  Results are exact up to fp64 rounding: each rejection sums the
+ * vocabulary once in fp64.
+ *
+ *   anc_mask     [B,T,W]  uint64  from tree_build_mask (a node's parent is its highest
+ *                                 ancestor bit below itself)
+ *   draft_tok    [B,T]    int32   drafted token of each node (entry 0 is not used)
+ *   p, q         [B,T,V]  float32 non-negative distributions; q rows of childless nodes and p
+ *                                 rows off the walk are not read
+ *   u_acc, u_res [B,T]    float64 uniforms in [0, 1): u_acc[b,c] is used when child c is tried,
+ *                                 u_res[b,u] when the bonus is drawn at u
+ *   without_replacement   0: siblings are independent draws from q; 1: drawn without
+ *                         replacement (q loses each rejected token)
+ *   accept_path, accept_len, bonus_tok   out, as for tree_accept
+ *   status       [B]      int32   optional (NULL): TV_BAD_TOKEN OR-ed in when a child tried
+ *                                 before the kept one (or any child, if none is kept) has a
+ *                                 token outside [0, V); that child is skipped
+ * Limits: 1 <= T <= 128, 1 <= V <= 1048576.
+ */
+int tree_accept_stochastic(const uint64_t* anc_mask, const int32_t* draft_tok, const float* p,
+                           const float* q, const double* u_acc, const double* u_res, int B, int T,
+                           int V, int without_replacement, int32_t* accept_path,
+                           int32_t* accept_len, int32_t* bonus_tok, int32_t* status, void* stream);
 
 /*
  * kv_compact_accepted — commit the accepted path's K/V to the cache.

@@ -4,16 +4,19 @@ This package only *draws inputs*: draft trees, draft/target tokens, prefix
 lengths and q/k/v tensors.  It holds none of the verification arithmetic
 (no masks, no attention, no acceptance walk, no compaction), so both the CPU
 oracle and the HIP path can be fed from it without sharing any of the method.
-``make_paged`` only places a workload's rows into a pool of token slots.
+``make_paged`` only places a workload's rows into a pool of token slots; ``make_stochastic``
+draws next-token distributions, drafted tokens and uniforms for sampling-mode acceptance.
 """
 from .workloads import (  # noqa: F401
     WORKLOADS,
     PagedLayout,
+    StochasticInputs,
     Workload,
     WorkloadSpec,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_paged,
+    make_stochastic,
     make_workload,
     random_parent,
     worked_tree_parent,

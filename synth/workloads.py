@@ -399,3 +399,64 @@ def make_paged(w: "Workload", page_size: int, seed: int = 0, headroom: int | Non
     k_pool[tree_slot.reshape(-1)] = w.k_tree.reshape(B * T, Hkv, D)
     v_pool[tree_slot.reshape(-1)] = w.v_tree.reshape(B * T, Hkv, D)
     return PagedLayout(P, k_pool, v_pool, table, tree_slot, num_slots, max_pages)
+
+
+STREAM_DIST = 5  # seed stream of the next-token distributions
+
+
+@dataclasses.dataclass
+class StochasticInputs:
+    """Inputs of sampling-mode acceptance for a workload's trees.
+
+    p / q [B, T, V] float32: the target and draft models' next-token distributions after every
+    node; draft [B, T] int32: each non-root node's token, drawn from its parent's q
+    (independently, or without replacement among siblings); u_acc / u_res [B, T] float64: the
+    uniforms the acceptance tests and the bonus draws consume."""
+    V: int
+    without_replacement: bool
+    p: np.ndarray
+    q: np.ndarray
+    draft: np.ndarray
+    u_acc: np.ndarray
+    u_res: np.ndarray
+
+
+def make_stochastic(w: "Workload", V: int | None = None, without_replacement: bool = False,
+                    seed: int = 0, spread: float = 2.0, draft_noise: float = 0.7,
+                    peak: tuple[float, float] = (-2.0, 4.0)) -> StochasticInputs:
+    """Next-token distributions and drafted tokens for w's tree shapes.  Pure input synthesis:
+    target logits are N(0, spread^2) plus one to three peaked tokens raised by
+    ln V + spread^2 / 2 + U(peak) (so the peak's share ranges from about 0.1 to 0.98, as in an
+    LLM's sampling distribution); draft logits add N(0, draft_noise^2) noise to the target's.
+    Both go through a softmax (float32 exponentials, float64 row sums) and are stored as
+    float32.  The children of every node
+    then draw their tokens from that node's draft distribution."""
+    V = int(V or w.spec.vocab)
+    B, T = w.B, w.T
+    p = np.empty((B, T, V), np.float32)
+    q = np.empty((B, T, V), np.float32)
+    draft = np.zeros((B, T), np.int32)
+    u_acc = np.empty((B, T), np.float64)
+    u_res = np.empty((B, T), np.float64)
+    lift = math.log(V) + 0.5 * spread * spread
+    for b in range(B):
+        rng = _rng(w.spec.wid, b, STREAM_DIST, seed)
+        z = rng.standard_normal((T, V), dtype=np.float32) * np.float32(spread)
+        for t in range(T):
+            k = int(rng.integers(1, 4))
+            z[t, rng.integers(0, V, size=k)] += np.float32(lift) + rng.uniform(*peak, size=k).astype(np.float32)
+        zd = z + rng.standard_normal((T, V), dtype=np.float32) * np.float32(draft_noise)
+        for src, dst in ((z, p), (zd, q)):
+            e = np.exp(src - src.max(axis=1, keepdims=True))
+            dst[b] = e / e.sum(axis=1, keepdims=True, dtype=np.float64)
+        par = w.parent[b]
+        for u in range(T):
+            kids = [c for c in range(u + 1, T) if par[c] == u]
+            if not kids:
+                continue
+            qu = q[b, u].astype(np.float64)
+            qu /= qu.sum()
+            draft[b, kids] = rng.choice(V, size=len(kids), replace=not without_replacement, p=qu)
+        u_acc[b] = rng.random(T)
+        u_res[b] = rng.random(T)
+    return StochasticInputs(V, bool(without_replacement), p, q, draft, u_acc, u_res)

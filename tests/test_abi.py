@@ -58,8 +58,9 @@ def test_status_strings(lib):
 
     for code in (tv.TV_OK, tv.TV_ERR_INVALID_ARG, tv.TV_ERR_UNSUPPORTED, tv.TV_ERR_WORKSPACE,
                  tv.TV_ERR_HIP, tv.TV_BAD_TREE, tv.TV_OVERFLOW, tv.TV_BAD_LEN, tv.TV_BAD_PATH,
-                 tv.TV_BAD_PAGE):
+                 tv.TV_BAD_PAGE, tv.TV_BAD_TOKEN):
         assert lib.tv_status_string(code)
+    assert b"TV_BAD_TOKEN" in lib.tv_status_string(tv.TV_BAD_TOKEN)
     assert b"unknown" in lib.tv_status_string(12345)
 
 
@@ -210,3 +211,16 @@ def test_product_path_does_not_import_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "oracle" not in text.lower(), f
+
+
+def test_stochastic_accept_argument_errors(lib):
+    # anc, draft, p, q, u_acc, u_res, B, T, V, mode, path, len, bonus, status, stream
+    base = [FAKE] * 6 + [1, 8, 1000, 0] + [FAKE] * 3 + [None, None]
+    for i in list(range(6)) + [10, 11, 12]:  # every pointer but status is required
+        bad = list(base)
+        bad[i] = None
+        assert lib.tree_accept_stochastic(*bad) == -1, i
+    for i, v in ((6, 0), (7, 0), (7, 129), (8, 0), (8, 1048577), (9, 2), (9, -1)):
+        bad = list(base)
+        bad[i] = v
+        assert lib.tree_accept_stochastic(*bad) == -1, (i, v)

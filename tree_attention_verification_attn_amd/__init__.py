@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     TV_BAD_LEN,
     TV_BAD_PAGE,
     TV_BAD_PATH,
+    TV_BAD_TOKEN,
     TV_BAD_TREE,
     TV_BF16,
     TV_ERR_HIP,
@@ -25,6 +26,7 @@ from .binding import (  # noqa: F401
     profile_attn_main,
     status_string,
     tree_accept,
+    tree_accept_stochastic,
     tree_build_mask,
     tree_verify_attn,
     tree_verify_attn_paged,

@@ -17,10 +17,12 @@ from . import build as _build
 TV_OK, TV_ERR_INVALID_ARG, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_HIP = 0, -1, -2, -3, -4
 TV_F32, TV_BF16 = 0, 1
 TV_BAD_TREE, TV_OVERFLOW, TV_BAD_LEN, TV_BAD_PATH, TV_BAD_PAGE = 0x1, 0x2, 0x4, 0x8, 0x10
+TV_BAD_TOKEN = 0x20
 
 EXPORTS = ("tv_status_string", "tree_build_mask", "tree_verify_attn_workspace_size",
            "tree_verify_attn", "tree_accept", "kv_compact_accepted", "tv_profile_attn_main",
-           "tree_verify_step", "tree_verify_attn_paged", "kv_commit_paged")
+           "tree_verify_step", "tree_verify_attn_paged", "kv_commit_paged",
+           "tree_accept_stochastic")
 
 
 class TreeVerifyError(RuntimeError):
@@ -79,6 +81,8 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_verify_attn_paged.restype = I
     lib.kv_commit_paged.argtypes = [P, I, I, P, P, P, P, P, P, P, I, I, I, P, P]
     lib.kv_commit_paged.restype = I
+    lib.tree_accept_stochastic.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, P, P, P]
+    lib.tree_accept_stochastic.restype = I
 
 
 def status_string(code: int) -> str:
@@ -209,6 +213,39 @@ def tree_accept(anc_mask, draft_tok, target_tok, accept_path=None, accept_len=No
     _check("tree_accept", load_library().tree_accept(
         _ptr(anc_mask), _ptr(draft_tok), _ptr(target_tok), B, T, _ptr(accept_path),
         _ptr(accept_len), _ptr(bonus_tok), _stream(stream)))
+    return accept_path, accept_len, bonus_tok
+
+
+def tree_accept_stochastic(anc_mask, draft_tok, p, q, u_acc, u_res, without_replacement=False,
+                           accept_path=None, accept_len=None, bonus_tok=None, status=None,
+                           stream=None):
+    """Rejection-sampling acceptance over the tree: p, q [B,T,V] float32, u_acc, u_res [B,T]
+    float64 -> (accept_path [B,T], accept_len [B], bonus_tok [B])."""
+    _need(anc_mask, "anc_mask", torch.int64, 3)
+    _need(draft_tok, "draft_tok", torch.int32, 2)
+    _need(p, "p", torch.float32, 3)
+    _need(q, "q", torch.float32, 3)
+    _need(u_acc, "u_acc", torch.float64, 2)
+    _need(u_res, "u_res", torch.float64, 2)
+    B, T = draft_tok.shape
+    V = p.shape[2]
+    if (tuple(anc_mask.shape) != (B, T, (T + 63) // 64) or tuple(p.shape) != (B, T, V)
+            or tuple(q.shape) != (B, T, V) or tuple(u_acc.shape) != (B, T)
+            or tuple(u_res.shape) != (B, T)):
+        raise ValueError("inconsistent tree_accept_stochastic shapes")
+    dev = draft_tok.device
+    accept_path = torch.empty((B, T), dtype=torch.int32, device=dev) if accept_path is None else accept_path
+    accept_len = torch.empty((B,), dtype=torch.int32, device=dev) if accept_len is None else accept_len
+    bonus_tok = torch.empty((B,), dtype=torch.int32, device=dev) if bonus_tok is None else bonus_tok
+    _need(accept_path, "accept_path", torch.int32, 2)
+    _need(accept_len, "accept_len", torch.int32, 1)
+    _need(bonus_tok, "bonus_tok", torch.int32, 1)
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    _check("tree_accept_stochastic", load_library().tree_accept_stochastic(
+        _ptr(anc_mask), _ptr(draft_tok), _ptr(p), _ptr(q), _ptr(u_acc), _ptr(u_res), B, T, V,
+        int(bool(without_replacement)), _ptr(accept_path), _ptr(accept_len), _ptr(bonus_tok),
+        _ptr(status), _stream(stream)))
     return accept_path, accept_len, bonus_tok
 
 
