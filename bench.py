@@ -62,6 +62,17 @@ def parse_args():
     p.add_argument("--page-size", type=int, default=1,
                    help="tokens per page for --kv paged (the commit needs 1; larger pages time "
                         "mask + attention + acceptance)")
+    p.add_argument("--accept", choices=("greedy", "stochastic"), default="greedy",
+                   help="greedy acceptance (the fused step), or rejection sampling over the tree "
+                        "(mask + attention + tree_accept_stochastic + compaction)")
+    p.add_argument("--sampling", choices=("independent", "without-replacement"),
+                   default="independent",
+                   help="how siblings were drafted, for --accept stochastic")
+    p.add_argument("--stoch-groups", type=int, default=0,
+                   help="workgroups sharing each vocabulary sweep of a sequence for --accept "
+                        "stochastic (0 = automatic)")
+    p.add_argument("--vocab", type=int, default=0,
+                   help="vocabulary of the next-token distributions (0 = the workload's, 128256)")
     p.add_argument("--rotate", type=int, default=0, help="input copies to rotate (0 = auto)")
     p.add_argument("--mode", choices=("graph", "eager"), default="graph",
                    help="replay each step as a captured HIP graph, or launch eagerly")
@@ -156,7 +167,8 @@ def kernel_source_hash() -> str:
 class StepSet:
     """Device buffers of one copy of the workload, plus pre-marshalled C-ABI argument tuples."""
 
-    def __init__(self, tv, torch, w, base=None, split_keys=0, workspace=None, paged=None):
+    def __init__(self, tv, torch, w, base=None, split_keys=0, workspace=None, paged=None,
+                 stoch=None, stoch_ws=None, stoch_groups=0):
         dev = torch.device("cuda:0")
 
         def up(a):
@@ -222,6 +234,23 @@ class StepSet:
                                 P(t["alen"]), P(t["free"]), P(t["free_top"]), paged.num_slots,
                                 B, T, P(t["status"]))
             self.api = "paged"
+        self.stoch = stoch
+        if stoch is not None:  # next-token distributions and uniforms (synth.make_stochastic)
+            if base is None:
+                t["p"], t["q"] = up(stoch.p), up(stoch.q)
+                t["sdraft"] = up(stoch.draft)
+                t["u_acc"], t["u_res"] = up(stoch.u_acc), up(stoch.u_res)
+            sws = 0 if stoch_ws is None else stoch_ws.numel()
+            self.stoch_args = (P(t["anc"]), P(t["sdraft"]), P(t["p"]), P(t["q"]), P(t["u_acc"]),
+                               P(t["u_res"]), B, T, stoch.V, int(stoch.without_replacement),
+                               stoch_groups,
+                               None if stoch_ws is None else P(stoch_ws), ctypes.c_size_t(sws),
+                               P(t["path"]), P(t["alen"]), P(t["bonus"]), P(t["status"]))
+            self.api = "stochastic"
+
+    def accept_stochastic(self, stream):
+        rc = self.lib.tree_accept_stochastic(*self.stoch_args, stream)
+        assert rc == 0, rc
 
     def attn_paged(self, stream):
         rc = self.lib.tree_verify_attn_paged(*self.attn_paged_args, stream)
@@ -262,10 +291,38 @@ class StepSet:
             self.accept(stream)
             self.commit(stream)
             return
+        if self.api == "stochastic":
+            self.mask(stream)
+            self.attn(stream)
+            self.accept_stochastic(stream)
+            self.compact(stream)
+            return
         self.mask(stream)
         self.attn(stream)
         self.accept(stream)
         self.compact(stream)
+
+
+def stochastic_work(parent, draft, path, alen, V) -> tuple[float, int]:
+    """Vocabulary sweeps of tree_accept_stochastic's walks, read off its outputs, and their bytes.
+
+    At every kept node but the last, each in-vocabulary child before the kept one was rejected
+    (one sweep of p and q each); at the last node every such child was, and the bonus draw sweeps
+    p (and q once a child was rejected there).  Returns (mean sweeps per sequence, bytes)."""
+    B, T = parent.shape
+    sweeps, nbytes = 0, 0
+    for b in range(B):
+        for i in range(int(alen[b])):
+            u = int(path[b, i])
+            kids = [c for c in range(u + 1, T) if parent[b, c] == u and 0 <= draft[b, c] < V]
+            last = i + 1 == int(alen[b])
+            rej = len(kids) if last else int(sum(c < int(path[b, i + 1]) for c in kids))
+            sweeps += rej
+            nbytes += rej * 8 * V
+            if last:
+                sweeps += 1
+                nbytes += (8 if rej else 4) * V
+    return sweeps / B, int(nbytes)
 
 
 def cpu_baseline(w, kv_bytes: int, target_s: float) -> dict:
@@ -362,13 +419,31 @@ def main() -> int:
             w.B, w.T, w.Hq, w.Hkv, w.D, cap,
             torch.bfloat16 if w.dtype == "bf16" else torch.float32, args.split_keys))
         args.api = "paged"
+    stoch, stoch_ws = None, None
+    if args.accept == "stochastic":
+        if args.kv == "paged":
+            raise SystemExit("--accept stochastic times the dense path; drop --kv paged")
+        from synth import make_stochastic
+
+        print("[bench] drawing next-token distributions", file=sys.stderr, flush=True)
+        stoch = make_stochastic(w, V=args.vocab or None,
+                                without_replacement=args.sampling == "without-replacement")
+        set_bytes += stoch.p.nbytes + stoch.q.nbytes
+        n_sets = max(1, min(n_sets, int(0.5 * free / set_bytes)))
+        args.api = "stochastic"
+        # one exchange workspace for every set: the calls are ordered on one stream, and each
+        # leaves it all zeros for the next
+        sws_bytes = tv.tree_accept_stochastic_workspace_size(w.B, w.T, stoch.V, args.stoch_groups)
+        stoch_ws = torch.zeros((sws_bytes,), dtype=torch.uint8, device="cuda") if sws_bytes else None
     workspace = torch.zeros((max(ws_bytes, 1),), dtype=torch.uint8, device="cuda") if ws_bytes else None
     print(f"[bench] uploading {n_sets} input sets ({set_bytes / 2**20:.1f} MiB each), "
           f"workspace {ws_bytes / 2**20:.1f} MiB", file=sys.stderr, flush=True)
-    sets = [StepSet(tv, torch, w, split_keys=args.split_keys, workspace=workspace, paged=paged)]
+    sets = [StepSet(tv, torch, w, split_keys=args.split_keys, workspace=workspace, paged=paged,
+                    stoch=stoch, stoch_ws=stoch_ws, stoch_groups=args.stoch_groups)]
     for _ in range(n_sets - 1):
         sets.append(StepSet(tv, torch, w, base=sets[0], split_keys=args.split_keys,
-                            workspace=workspace, paged=paged))
+                            workspace=workspace, paged=paged, stoch=stoch, stoch_ws=stoch_ws,
+                            stoch_groups=args.stoch_groups))
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
@@ -428,7 +503,7 @@ def main() -> int:
             torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps, t_wall
 
-    other = {"fused": "separate", "separate": "fused", "paged": None}[args.api]
+    other = {"fused": "separate", "separate": "fused", "paged": None, "stochastic": None}[args.api]
     ms_other = time_api(other)[0] if other else None
     ms_per_step, t_wall = time_api(args.api)
     t_step = ms_per_step * 1e-3
@@ -529,6 +604,51 @@ def main() -> int:
                      "attn_main_paged_us from the kernel's own timestamps"),
         }
 
+    # stochastic acceptance: the same calls with tree_accept_stochastic in place of tree_accept;
+    # the kernel's own duration comes from its profiling hook
+    stoch_breakdown = None
+    if stoch is not None:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_prof)]
+        for row in evs:
+            for e in row:
+                e.record(stream)
+        stream.synchronize()
+        with torch.cuda.stream(stream):
+            for i in range(n_prof):
+                s = sets[i % n_sets]
+                ei = evs[i]
+                s.mask(sptr)
+                s.attn(sptr)
+                tv.profile_accept_stochastic(ei[1], ei[2])
+                ei[0].record(stream)
+                s.accept_stochastic(sptr)
+                ei[3].record(stream)
+                s.compact(sptr)
+            tv.profile_accept_stochastic(None, None)
+            stream.synchronize()
+        t_sk = float(np.mean([evs[i][1].elapsed_time(evs[i][2]) for i in range(n_prof)])) * 1e-3
+        t_sc = float(np.mean([evs[i][0].elapsed_time(evs[i][3]) for i in range(n_prof)])) * 1e-3
+        spath = sets[0].t["path"].cpu().numpy()
+        slen = sets[0].t["alen"].cpu().numpy()
+        sweeps, sbytes = stochastic_work(w.parent, stoch.draft, spath, slen, stoch.V)
+        stoch_breakdown = {
+            "vocab": stoch.V, "sampling": args.sampling,
+            "workgroups_per_seq": (stoch_ws.numel() - 4 * w.B) // (16 * w.B * w.T)
+            if stoch_ws is not None else 1,
+            "mean_accept_len": float(slen.mean()),
+            "vocab_sweeps_per_call": sweeps,
+            "algorithmic_bytes_per_call": sbytes,
+            "kernel_us": t_sk * 1e6,
+            "call_us": t_sc * 1e6,
+            "tree_accept_greedy_us": t_accept * 1e6,
+            "achieved_gbps": sbytes / t_sk / 1e9,
+            "hbm_frac": sbytes / t_sk / 1e9 / HBM_PEAK_GBS,
+            "note": ("kernel_us from the kernel's own timestamps; call_us from events between "
+                     "eager calls (launch latency included); bytes: p and q rows of every "
+                     "vocabulary sweep the walk makes (one per rejected child, one for the bonus "
+                     "draw)"),
+        }
+
     alen = sets[0].t["alen"].cpu().numpy()
     status = sets[0].t["status"].cpu().numpy()
     if (status & ~0).any():
@@ -556,7 +676,8 @@ def main() -> int:
     roof["kernel"] = {"fused": "attn_main (tree_verify_step's instantiation, which also builds "
                                "the masks)",
                       "separate": "attn_main",
-                      "paged": "attn_main (tree_verify_attn_paged's instantiation)"}[args.api]
+                      "paged": "attn_main (tree_verify_attn_paged's instantiation)",
+                      "stochastic": "attn_main"}[args.api]
     roof["kernel_us"] = t_main * 1e6
     roof["algorithmic_bytes"] = kv_bytes
     roof["algorithmic_flops"] = flops
@@ -579,10 +700,12 @@ def main() -> int:
                    "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "prefix_tokens": int(L.sum()),
                    "Lmax": w.Lmax, "layers": 1, "mode": args.mode, "rotated_sets": n_sets,
                    "split_keys": args.split_keys, "step_api": args.api, "kv": args.kv,
+                   "accept": args.accept,
                    "graph_steps": graph_steps if args.mode == "graph" else None},
         "ms_per_step_by_api": ({args.api: ms_per_step, other: ms_other} if other
                                else {args.api: ms_per_step}),
         "paged": paged_breakdown,
+        "stochastic": stoch_breakdown,
         "hbm_frac": value / HBM_PEAK_GBS,
         "attn_kv_gbps": kv_bytes / t_attn / 1e9,
         "attn_hbm_frac": kv_bytes / t_attn / 1e9 / HBM_PEAK_GBS,

@@ -56,6 +56,8 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_BAD_PATH 0x8 /* accept_len[b] outside [0, T] or an accepted index outside [0, T) */
 #define TV_BAD_PAGE 0x10 /* paged K/V: a block-table entry or tree slot outside the pool */
 #define TV_BAD_TOKEN 0x20 /* stochastic acceptance: a tried child's token outside [0, V) */
+#define TV_SYNC_TIMEOUT 0x40 /* stochastic acceptance: its workgroups did not all meet (they were
+                                not resident together); results invalid, re-zero the workspace */
 
 /* Human-readable name of a tv_status return value or of a single status bit. */
 const char* tv_status_string(int code);
@@ -169,16 +171,39 @@ int tree_accept(const uint64_t* anc_mask, const int32_t* draft_tok, const int32_
  *                                 u_res[b,u] when the bonus is drawn at u
  *   without_replacement   0: siblings are independent draws from q; 1: drawn without
  *                         replacement (q loses each rejected token)
+ *   workgroups_per_seq    workgroups that share each vocabulary sweep of a sequence (0 =
+ *                         automatic: as many as keep B * G within the compute units, at most
+ *                         32, at least 2048 tokens each).  With G > 1 the workgroups of a
+ *                         sequence exchange partial sums and must all be resident together:
+ *                         B * G may not exceed the device's compute units (TV_ERR_INVALID_ARG).
+ *   workspace    device buffer of tree_accept_stochastic_workspace_size(...) bytes (NULL
+ *                allowed when that is 0), 16-byte aligned, zero-filled by the caller once
+ *                before its first use and not written by the caller afterwards: every call
+ *                leaves it all zeros again.  Calls that share a workspace must be ordered on
+ *                one stream.
  *   accept_path, accept_len, bonus_tok   out, as for tree_accept
  *   status       [B]      int32   optional (NULL): TV_BAD_TOKEN OR-ed in when a child tried
  *                                 before the kept one (or any child, if none is kept) has a
- *                                 token outside [0, V); that child is skipped
- * Limits: 1 <= T <= 128, 1 <= V <= 1048576.
+ *                                 token outside [0, V); that child is skipped.
+ *                                 TV_SYNC_TIMEOUT if the workgroups of a sequence did not all
+ *                                 meet within about 0.1 s (another kernel held compute units)
+ * Limits: 1 <= T <= 128, 1 <= V <= 1048576, 0 <= workgroups_per_seq <= 64.
  */
+size_t tree_accept_stochastic_workspace_size(int B, int T, int V, int workgroups_per_seq);
 int tree_accept_stochastic(const uint64_t* anc_mask, const int32_t* draft_tok, const float* p,
                            const float* q, const double* u_acc, const double* u_res, int B, int T,
-                           int V, int without_replacement, int32_t* accept_path,
+                           int V, int without_replacement, int workgroups_per_seq,
+                           void* workspace, size_t workspace_bytes, int32_t* accept_path,
                            int32_t* accept_len, int32_t* bonus_tok, int32_t* status, void* stream);
+
+/*
+ * tv_profile_accept_stochastic — profiling hook for tree_accept_stochastic's kernel, as
+ * tv_profile_attn_main is for the attention: while set, the kernel is launched with
+ * hipExtLaunchKernel so that the two hipEvent_t take its own start and end timestamps.  NULL,
+ * NULL turns it off.  Process-wide, not synchronised.  TV_ERR_INVALID_ARG if exactly one event
+ * is NULL.
+ */
+int tv_profile_accept_stochastic(void* ev_before, void* ev_after);
 
 /*
  * kv_compact_accepted — commit the accepted path's K/V to the cache.

@@ -214,13 +214,31 @@ def test_product_path_does_not_import_the_oracle():
 
 
 def test_stochastic_accept_argument_errors(lib):
-    # anc, draft, p, q, u_acc, u_res, B, T, V, mode, path, len, bonus, status, stream
-    base = [FAKE] * 6 + [1, 8, 1000, 0] + [FAKE] * 3 + [None, None]
-    for i in list(range(6)) + [10, 11, 12]:  # every pointer but status is required
+    # anc, draft, p, q, u_acc, u_res, B, T, V, mode, G, workspace, bytes, path, len, bonus,
+    # status, stream
+    base = [FAKE] * 6 + [1, 8, 1000, 0, 1, None, 0] + [FAKE] * 3 + [None, None]
+    for i in list(range(6)) + [13, 14, 15]:  # every pointer but workspace and status is required
         bad = list(base)
         bad[i] = None
         assert lib.tree_accept_stochastic(*bad) == -1, i
-    for i, v in ((6, 0), (7, 0), (7, 129), (8, 0), (8, 1048577), (9, 2), (9, -1)):
+    for i, v in ((6, 0), (7, 0), (7, 129), (8, 0), (8, 1048577), (9, 2), (9, -1), (10, -1),
+                 (10, 65)):
         bad = list(base)
         bad[i] = v
         assert lib.tree_accept_stochastic(*bad) == -1, (i, v)
+    # two workgroups per sequence exchange sums through a workspace
+    need = lib.tree_accept_stochastic_workspace_size(1, 8, 1000, 2)
+    assert need == 8 * 2 * 16 + 4
+    bad = list(base)
+    bad[10] = 2
+    assert lib.tree_accept_stochastic(*bad) == -3
+    bad[11], bad[12] = FAKE, need - 1
+    assert lib.tree_accept_stochastic(*bad) == -3
+
+
+def test_stochastic_workspace_size_rules(lib):
+    ws = lib.tree_accept_stochastic_workspace_size
+    assert ws(4, 60, 1000, 1) == 0        # one workgroup per sequence: no exchange
+    assert ws(4, 60, 1000, 0) == 0        # a 1000-token vocabulary is too small to split
+    assert ws(2, 60, 128256, 3) == 2 * 60 * 3 * 16 + 2 * 4
+    assert ws(0, 60, 1000, 0) == 0 and ws(1, 60, 1000, 65) == 0

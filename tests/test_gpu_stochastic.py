@@ -26,19 +26,21 @@ def _gpu():
     tv.load_library()
 
 
-def _check(parent, draft, p, q, u_acc, u_res, mode, label, p_dev=None, q_dev=None):
+def _check(parent, draft, p, q, u_acc, u_res, mode, label, p_dev=None, q_dev=None, G=0,
+           workspace=None):
     import tree_attention_verification_attn_amd as tv
     from oracle import oracle as O
 
     B, T = draft.shape
     V = p.shape[-1]
-    print(f"[case] stochastic {label} B={B} T={T} V={V} mode={mode}", flush=True)
+    print(f"[case] stochastic {label} B={B} T={T} V={V} mode={mode} G={G}", flush=True)
     anc, st = tv.tree_build_mask(to_dev(np.asarray(parent, np.int32)))
     status = torch.zeros(B, dtype=torch.int32, device="cuda")
     path, n, bonus = tv.tree_accept_stochastic(
         anc, to_dev(np.asarray(draft, np.int32)), to_dev(p) if p_dev is None else p_dev,
         to_dev(q) if q_dev is None else q_dev, to_dev(np.asarray(u_acc, np.float64)),
-        to_dev(np.asarray(u_res, np.float64)), without_replacement=mode, status=status)
+        to_dev(np.asarray(u_res, np.float64)), without_replacement=mode, workgroups_per_seq=G,
+        workspace=workspace, status=status)
     torch.cuda.synchronize()
     o_path, o_n, o_bonus, o_st = O.accept_stochastic(parent, draft, p, q, u_acc, u_res, mode)
     g_path, g_n, g_bonus, g_st = to_host(path), to_host(n), to_host(bonus), to_host(status)
@@ -85,13 +87,14 @@ CASES = [  # label, B, T, V, parent kind, draft noise
 
 @pytest.mark.parametrize("label,B,T,V,kind,noise", CASES, ids=[c[0] for c in CASES])
 @pytest.mark.parametrize("mode", [0, 1])
-def test_random_trees(label, B, T, V, kind, noise, mode):
+@pytest.mark.parametrize("G", [0, 3])
+def test_random_trees(label, B, T, V, kind, noise, mode, G):
     w = make_workload("batch32_L512-4096_T60", B=B, T=T, L=(0, 8), Hq=2, Hkv=1, D=64,
                       dtype="f32", parent_kind=kind, extra_seed=31, with_kv=False)
     if mode and max(np.bincount(w.parent[w.parent >= 0], minlength=1).max(), 0) > V:
         pytest.skip("more siblings than tokens to draw without replacement")
     s = make_stochastic(w, V=V, without_replacement=mode, seed=7, draft_noise=noise)
-    _check(w.parent, s.draft, s.p, s.q, s.u_acc, s.u_res, mode, label)
+    _check(w.parent, s.draft, s.p, s.q, s.u_acc, s.u_res, mode, label, G=G)
 
 
 def test_edge_distributions():
@@ -114,7 +117,8 @@ def test_edge_distributions():
         u_res[4] = 1.0 - 2.0 ** -30
         draft[5, 1::3] = 300                  # sequence 5: some tokens outside the vocabulary
         draft[5, 2::5] = -3
-        _check(w.parent, draft, p, q, u_acc, u_res, mode, "edge distributions")
+        for G in (1, 4):
+            _check(w.parent, draft, p, q, u_acc, u_res, mode, "edge distributions", G=G)
 
 
 def test_unaligned_rows_use_the_scalar_path():
@@ -133,10 +137,33 @@ def test_unaligned_rows_use_the_scalar_path():
     _check(w.parent, s.draft, s.p, s.q, s.u_acc, s.u_res, 0, "unaligned", p_dev=p_dev, q_dev=q_dev)
 
 
-@pytest.mark.parametrize("name,mode", [("llama8b_b1_L4096_T60", 0), ("llama8b_b1_L4096_T60", 1),
-                                       ("batch32_L512-4096_T60", 0)])
-def test_full_size(name, mode):
-    """The workloads' own trees with a Llama-3-sized vocabulary (128256), as the bench runs."""
+@pytest.mark.parametrize("name,mode,G", [("llama8b_b1_L4096_T60", 0, 0), ("llama8b_b1_L4096_T60", 1, 0),
+                                         ("llama8b_b1_L4096_T60", 0, 1),
+                                         ("batch32_L512-4096_T60", 0, 0)])
+def test_full_size(name, mode, G):
+    """The workloads' own trees with a Llama-3-sized vocabulary (128256), as the bench runs
+    (automatic split: 32 workgroups per sequence at batch 1, 8 at batch 32)."""
     w = make_workload(name, with_kv=False)
     s = make_stochastic(w, without_replacement=mode)
-    _check(w.parent, s.draft, s.p, s.q, s.u_acc, s.u_res, mode, name)
+    _check(w.parent, s.draft, s.p, s.q, s.u_acc, s.u_res, mode, name, G=G)
+
+
+def test_workspace_is_left_zero_and_reusable():
+    """Calls that share a workspace: each leaves it all zeros, and repeated calls agree."""
+    import tree_attention_verification_attn_amd as tv
+
+    w = make_workload("batch32_L512-4096_T60", B=5, T=60, L=(0, 8), Hq=2, Hkv=1, D=64,
+                      dtype="f32", parent_kind="random", extra_seed=34, with_kv=False)
+    s = make_stochastic(w, V=40000, seed=10, draft_noise=2.5)
+    G = 6
+    need = tv.tree_accept_stochastic_workspace_size(w.B, w.T, s.V, G)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    first = None
+    for rep in range(3):
+        out = _check(w.parent, s.draft, s.p, s.q, s.u_acc, s.u_res, 0, f"reuse {rep}", G=G,
+                     workspace=ws)
+        assert int(torch.count_nonzero(ws)) == 0
+        if first is None:
+            first = out
+        assert all(np.array_equal(x, y) for x, y in zip(out, first))

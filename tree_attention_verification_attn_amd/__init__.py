@@ -18,15 +18,18 @@ from .binding import (  # noqa: F401
     TV_F32,
     TV_OK,
     TV_OVERFLOW,
+    TV_SYNC_TIMEOUT,
     TreeVerifyError,
     kv_commit_paged,
     kv_compact_accepted,
     lib_path,
     load_library,
+    profile_accept_stochastic,
     profile_attn_main,
     status_string,
     tree_accept,
     tree_accept_stochastic,
+    tree_accept_stochastic_workspace_size,
     tree_build_mask,
     tree_verify_attn,
     tree_verify_attn_paged,

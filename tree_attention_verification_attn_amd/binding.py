@@ -17,12 +17,13 @@ from . import build as _build
 TV_OK, TV_ERR_INVALID_ARG, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_HIP = 0, -1, -2, -3, -4
 TV_F32, TV_BF16 = 0, 1
 TV_BAD_TREE, TV_OVERFLOW, TV_BAD_LEN, TV_BAD_PATH, TV_BAD_PAGE = 0x1, 0x2, 0x4, 0x8, 0x10
-TV_BAD_TOKEN = 0x20
+TV_BAD_TOKEN, TV_SYNC_TIMEOUT = 0x20, 0x40
 
 EXPORTS = ("tv_status_string", "tree_build_mask", "tree_verify_attn_workspace_size",
            "tree_verify_attn", "tree_accept", "kv_compact_accepted", "tv_profile_attn_main",
            "tree_verify_step", "tree_verify_attn_paged", "kv_commit_paged",
-           "tree_accept_stochastic")
+           "tree_accept_stochastic", "tree_accept_stochastic_workspace_size",
+           "tv_profile_accept_stochastic")
 
 
 class TreeVerifyError(RuntimeError):
@@ -81,8 +82,13 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_verify_attn_paged.restype = I
     lib.kv_commit_paged.argtypes = [P, I, I, P, P, P, P, P, P, P, I, I, I, P, P]
     lib.kv_commit_paged.restype = I
-    lib.tree_accept_stochastic.argtypes = [P, P, P, P, P, P, I, I, I, I, P, P, P, P, P]
+    lib.tree_accept_stochastic.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, ctypes.c_size_t,
+                                           P, P, P, P, P]
+    lib.tree_accept_stochastic_workspace_size.argtypes = [I, I, I, I]
+    lib.tree_accept_stochastic_workspace_size.restype = ctypes.c_size_t
     lib.tree_accept_stochastic.restype = I
+    lib.tv_profile_accept_stochastic.argtypes = [P, P]
+    lib.tv_profile_accept_stochastic.restype = I
 
 
 def status_string(code: int) -> str:
@@ -130,6 +136,14 @@ def profile_attn_main(before: torch.cuda.Event | None, after: torch.cuda.Event |
     The events must have been recorded once (torch creates them lazily)."""
     ptr = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)  # noqa: E731
     _check("tv_profile_attn_main", load_library().tv_profile_attn_main(ptr(before), ptr(after)))
+
+
+def profile_accept_stochastic(before: torch.cuda.Event | None,
+                              after: torch.cuda.Event | None) -> None:
+    """Record `before`/`after` around every later tree_accept_stochastic kernel (None: off)."""
+    ptr = lambda e: None if e is None else ctypes.c_void_p(e.cuda_event)  # noqa: E731
+    _check("tv_profile_accept_stochastic",
+           load_library().tv_profile_accept_stochastic(ptr(before), ptr(after)))
 
 
 def tree_build_mask(parent: torch.Tensor, anc_mask: torch.Tensor | None = None,
@@ -216,11 +230,16 @@ def tree_accept(anc_mask, draft_tok, target_tok, accept_path=None, accept_len=No
     return accept_path, accept_len, bonus_tok
 
 
+def tree_accept_stochastic_workspace_size(B: int, T: int, V: int, workgroups_per_seq: int = 0) -> int:
+    return int(load_library().tree_accept_stochastic_workspace_size(B, T, V, workgroups_per_seq))
+
+
 def tree_accept_stochastic(anc_mask, draft_tok, p, q, u_acc, u_res, without_replacement=False,
-                           accept_path=None, accept_len=None, bonus_tok=None, status=None,
-                           stream=None):
+                           workgroups_per_seq=0, workspace=None, accept_path=None, accept_len=None,
+                           bonus_tok=None, status=None, stream=None):
     """Rejection-sampling acceptance over the tree: p, q [B,T,V] float32, u_acc, u_res [B,T]
-    float64 -> (accept_path [B,T], accept_len [B], bonus_tok [B])."""
+    float64 -> (accept_path [B,T], accept_len [B], bonus_tok [B]).  `workspace` (uint8, zeroed
+    once, then reused untouched) is allocated here when not given."""
     _need(anc_mask, "anc_mask", torch.int64, 3)
     _need(draft_tok, "draft_tok", torch.int32, 2)
     _need(p, "p", torch.float32, 3)
@@ -242,9 +261,14 @@ def tree_accept_stochastic(anc_mask, draft_tok, p, q, u_acc, u_res, without_repl
     _need(bonus_tok, "bonus_tok", torch.int32, 1)
     if status is not None:
         _need(status, "status", torch.int32, 1)
+    need = tree_accept_stochastic_workspace_size(B, T, V, workgroups_per_seq)
+    if workspace is None and need:
+        workspace = torch.zeros((need,), dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("tree_accept_stochastic", load_library().tree_accept_stochastic(
         _ptr(anc_mask), _ptr(draft_tok), _ptr(p), _ptr(q), _ptr(u_acc), _ptr(u_res), B, T, V,
-        int(bool(without_replacement)), _ptr(accept_path), _ptr(accept_len), _ptr(bonus_tok),
+        int(bool(without_replacement)), int(workgroups_per_seq), _ptr(workspace),
+        ctypes.c_size_t(ws_bytes), _ptr(accept_path), _ptr(accept_len), _ptr(bonus_tok),
         _ptr(status), _stream(stream)))
     return accept_path, accept_len, bonus_tok
 

@@ -262,6 +262,8 @@ extern "C" const char* tv_status_string(int code) {
     case TV_BAD_PATH: return "TV_BAD_PATH: accept_len or an accepted index out of range";
     case TV_BAD_PAGE: return "TV_BAD_PAGE: a block-table entry or tree slot outside the pool";
     case TV_BAD_TOKEN: return "TV_BAD_TOKEN: a tried child's token is outside the vocabulary";
+    case TV_SYNC_TIMEOUT:
+      return "TV_SYNC_TIMEOUT: the workgroups of a sequence did not all meet; re-zero the workspace";
     default: return "unknown tree_verify status";
   }
 }
