@@ -155,10 +155,15 @@ def pmc_summary(d: str, workload: str) -> int:
     return 0
 
 
+# the sources attn_main is compiled from: the counters in COUNTERS_FILE hold while these are
+# unchanged
+ATTN_SOURCES = ("attn.hip", "tree_device.h", "tv_internal.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tree_attention_verification_attn_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ATTN_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
