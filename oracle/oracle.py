@@ -17,6 +17,7 @@ ORC_OVERFLOW = 0x2
 ORC_BAD_LEN = 0x4
 ORC_BAD_PATH = 0x8
 ORC_BAD_TOKEN = 0x20
+ORC_BAD_CONF = 0x80
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tree_oracle.c")
@@ -71,6 +72,10 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_compact.restype = None
     lib.oracle_accept_stochastic.argtypes = [P, P, P, P, P, P, i, i, i, i, P, P, P, P]
     lib.oracle_accept_stochastic.restype = None
+    lib.oracle_eagle2_rerank.argtypes = [P, P, P, i, i, i, i, P, P, P, P, P]
+    lib.oracle_eagle2_rerank.restype = None
+    lib.oracle_eagle2_build.argtypes = [P, P, P, i, i, i, i, i, P, P, P, i, P, P, P, P, P, P]
+    lib.oracle_eagle2_build.restype = i
     return lib
 
 
@@ -260,3 +265,59 @@ def accept_stochastic(parent, draft, p, q, u_acc, u_res, without_replacement=Fal
                                  V, int(bool(without_replacement)), _p(path), _p(alen), _p(bonus),
                                  _p(status))
     return path, alen, bonus, status
+
+
+def eagle2_node_count(depth: int, k: int, branch: int) -> int:
+    """Nodes of an EAGLE-2 expansion: the root, then branch children for each frontier node of
+    every level, the frontier of level l being min(k, children of level l)."""
+    n, F = 1, 1
+    for _ in range(depth):
+        n += F * branch
+        F = min(k, F * branch)
+    return n
+
+
+def eagle2_build(root_tok, child_tok, child_conf, T, lib=None) -> dict:
+    """EAGLE-2 tree construction (``oracle_eagle2_build``).  root_tok [B] int32; child_tok and
+    child_conf [depth, B, k, branch] (int32, float32).  Returns a dict of numpy arrays:
+    node_tok, node_parent, node_value [B, N]; frontier [depth, B, k]; parent, tok, depth,
+    node [B, T]; status [B]."""
+    lib = lib or load()
+    root_tok = _i32(root_tok)
+    child_tok = _i32(child_tok)
+    child_conf = np.ascontiguousarray(child_conf, dtype=np.float32)
+    depth, B, k, branch = child_tok.shape
+    assert child_conf.shape == child_tok.shape and root_tok.shape == (B,)
+    N = eagle2_node_count(depth, k, branch)
+    if not 1 <= T <= N:
+        raise ValueError(f"tree budget {T} outside [1, {N}]")
+    r = {name: np.empty((B, N), dt) for name, dt in
+         (("node_tok", np.int32), ("node_parent", np.int32), ("node_value", np.float32))}
+    r["frontier"] = np.empty((depth, B, k), np.int32)
+    for name in ("parent", "tok", "depth", "node"):
+        r[name] = np.empty((B, T), np.int32)
+    r["status"] = np.zeros(B, np.int32)
+    n = lib.oracle_eagle2_build(_p(root_tok), _p(child_tok), _p(child_conf), B, depth, k, branch,
+                                T, _p(r["node_tok"]), _p(r["node_parent"]), _p(r["node_value"]), N,
+                                _p(r["frontier"]), _p(r["parent"]), _p(r["tok"]), _p(r["depth"]),
+                                _p(r["node"]), _p(r["status"]))
+    if n != N:
+        raise AssertionError(f"oracle built {n} nodes, expected {N}")
+    return r
+
+
+def eagle2_rerank(node_tok, node_parent, node_value, T, lib=None) -> dict:
+    """Reranking and flattening of given node tables [B, N] (``oracle_eagle2_rerank``).
+    Returns parent, tok, depth, node [B, T] and status [B]."""
+    lib = lib or load()
+    node_tok, node_parent = _i32(node_tok), _i32(node_parent)
+    node_value = np.ascontiguousarray(node_value, dtype=np.float32)
+    B, N = node_tok.shape
+    if not 1 <= T <= N:
+        raise ValueError(f"tree budget {T} outside [1, {N}]")
+    r = {name: np.empty((B, T), np.int32) for name in ("parent", "tok", "depth", "node")}
+    r["status"] = np.zeros(B, np.int32)
+    lib.oracle_eagle2_rerank(_p(node_tok), _p(node_parent), _p(node_value), N, N, B, T,
+                             _p(r["parent"]), _p(r["tok"]), _p(r["depth"]), _p(r["node"]),
+                             _p(r["status"]))
+    return r

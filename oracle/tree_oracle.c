@@ -36,6 +36,12 @@
  *                  max(0, p - q), normalised, is what the next sibling is tested against, and
  *                  what the bonus token is drawn from when no child is accepted.  The random
  *                  numbers are inputs (one uniform per tested child, one per sampling node).
+ *   draft tree     (rainlin.net "EAGLE 系列", section 7) EAGLE-2's dynamic tree: each level
+ *   construction   expands the top-k nodes of the deepest layer by global acceptance value (the
+ *                  product of the drafter's confidences on the root path), then all nodes are
+ *                  reranked and the best T kept and flattened in level order.  Which node
+ *                  outranks which is decided on float32 products, the precision of the GPU
+ *                  kernels, since these decisions choose integers (node ids).
  *
  * Floating inputs are either float32 (elem_bits = 32) or raw bfloat16 bit patterns
  * (elem_bits = 16), which are widened exactly.
@@ -537,4 +543,192 @@ void oracle_accept_stochastic(const int32_t* parent, const int32_t* draft, const
   free(pj);
   free(qj);
   free(res);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* EAGLE-2 dynamic draft tree: expansion, reranking, flattening                                */
+/* ------------------------------------------------------------------------------------------ */
+
+#define ORC_BAD_CONF 0x80
+
+/* A drafter confidence used as a probability: NaN and negative values count as 0, values
+ * above 1 as 1; anything outside [0, 1] is reported. */
+static float conf_as_prob(float c, int32_t* st) {
+  if (!(c >= 0.0f && c <= 1.0f)) *st |= ORC_BAD_CONF;
+  return c > 0.0f ? (c < 1.0f ? c : 1.0f) : 0.0f;
+}
+
+/* A node value as it is ranked: NaN and negative values count as 0. */
+static float rank_value(float v) { return v > 0.0f ? v : 0.0f; }
+
+/* Node a outranks node b: a larger value, or the same value and a smaller id (created earlier,
+ * hence never deeper). */
+static int outranks(const float* value, int a, int b) {
+  const float va = rank_value(value[a]), vb = rank_value(value[b]);
+  return va > vb || (va == vb && a < b);
+}
+
+/* Reranking and flattening (rainlin.net "EAGLE 系列", section 7.2).
+ *
+ * The node table of sequence b holds n_nodes nodes (row stride n_max): node_parent[i] is the id
+ * of i's parent (-1 for the root, node 0) and node_value[i] its global acceptance value.  The T
+ * nodes that outrank all others are kept; when no child's value exceeds its parent's, the kept
+ * set is a connected tree (a parent outranks its children).  The kept tree is flattened in level
+ * order: by depth, then by the flattened index of the parent, then by node id (siblings are
+ * created in the drafter's order).  Outputs per flattened position f: parent_out (flattened
+ * index of the parent, -1 at the root), tok_out (node_tok), depth_out, node_out (node id).
+ * A table that is not such a tree (node 0 not a root, a parent id not below the node's, a child
+ * valued above its parent) sets ORC_BAD_TREE in status[b] (OR-ed) and gets parent -1, token -1,
+ * depth 0 and node -1 at every position.  Requires 1 <= T <= n_nodes. */
+void oracle_eagle2_rerank(const int32_t* node_tok, const int32_t* node_parent,
+                          const float* node_value, int n_nodes, int n_max, int B, int T,
+                          int32_t* parent_out, int32_t* tok_out, int32_t* depth_out,
+                          int32_t* node_out, int32_t* status) {
+  char* kept = (char*)malloc((size_t)n_nodes);
+  int32_t* flat_of = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_nodes);
+  int32_t* dep = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_nodes);
+  for (int b = 0; b < B; ++b) {
+    const int32_t* nt = node_tok + (size_t)b * n_max;
+    const int32_t* np = node_parent + (size_t)b * n_max;
+    const float* nv = node_value + (size_t)b * n_max;
+    int32_t* po = parent_out + (size_t)b * T;
+    int32_t* to = tok_out + (size_t)b * T;
+    int32_t* dout = depth_out + (size_t)b * T;
+    int32_t* no = node_out + (size_t)b * T;
+
+    int valid = np[0] == -1 && T >= 1 && T <= n_nodes;
+    for (int i = 1; i < n_nodes && valid; ++i) {
+      const int p = np[i];
+      if (p < 0 || p >= i || rank_value(nv[i]) > rank_value(nv[p])) valid = 0;
+    }
+    if (!valid) {
+      status[b] |= ORC_BAD_TREE;
+      for (int f = 0; f < T; ++f) {
+        po[f] = -1;
+        to[f] = -1;
+        dout[f] = 0;
+        no[f] = -1;
+      }
+      continue;
+    }
+
+    /* keep: T times, the best node not yet kept */
+    memset(kept, 0, (size_t)n_nodes);
+    for (int t = 0; t < T; ++t) {
+      int best = -1;
+      for (int i = 0; i < n_nodes; ++i)
+        if (!kept[i] && (best < 0 || outranks(nv, i, best))) best = i;
+      kept[best] = 1;
+    }
+
+    /* depth of every kept node: parent steps to the root */
+    int max_depth = 0;
+    for (int i = 0; i < n_nodes; ++i) {
+      flat_of[i] = -1;
+      if (!kept[i]) continue;
+      int d = 0;
+      for (int cur = i; np[cur] != -1; cur = np[cur]) ++d;
+      dep[i] = d;
+      if (d > max_depth) max_depth = d;
+    }
+
+    /* flatten level by level: within a level, smallest (parent's flattened index, id) first */
+    int f = 0;
+    for (int d = 0; d <= max_depth; ++d) {
+      for (;;) {
+        int best = -1;
+        for (int i = 0; i < n_nodes; ++i) {
+          if (!kept[i] || dep[i] != d || flat_of[i] >= 0) continue;
+          if (best < 0) {
+            best = i;
+            continue;
+          }
+          const int pf_i = d == 0 ? -1 : flat_of[np[i]];
+          const int pf_b = d == 0 ? -1 : flat_of[np[best]];
+          if (pf_i < pf_b || (pf_i == pf_b && i < best)) best = i;
+        }
+        if (best < 0) break;
+        flat_of[best] = f;
+        po[f] = d == 0 ? -1 : flat_of[np[best]];
+        to[f] = nt[best];
+        dout[f] = d;
+        no[f] = best;
+        ++f;
+      }
+    }
+  }
+  free(kept);
+  free(flat_of);
+  free(dep);
+}
+
+/* Expansion (rainlin.net "EAGLE 系列", section 7.1) followed by reranking.
+ *
+ * The root (node 0, token root_tok[b]) has value 1.  Level l = 1 .. depth expands the frontier
+ * of level l - 1 (the root alone for l = 1): the drafter gives frontier slot r the `branch`
+ * candidate children child_tok / child_conf [l-1][b][r][c] (layout [depth, B, k, branch]).
+ * Child c of slot r becomes node n_l + r * branch + c, where n_l counts the nodes of the levels
+ * before; its value is its parent's value times its confidence, a float32 product (the
+ * confidence taken as conf_as_prob; ORC_BAD_CONF is OR-ed in for one outside [0, 1]).  The
+ * global acceptance value of a node is thus the product of the confidences on its root path.
+ * The frontier of level l is the min(k, children of level l) children of that level that
+ * outrank the others, best first; frontier_out [depth, B, k] (optional) receives it, padded
+ * with -1.  The node table is written to node_tok / node_parent / node_value [B, n_max] and
+ * reranked as oracle_eagle2_rerank.  Returns the node count, or -1 if it exceeds n_max. */
+int oracle_eagle2_build(const int32_t* root_tok, const int32_t* child_tok,
+                        const float* child_conf, int B, int depth, int k, int branch, int T,
+                        int32_t* node_tok, int32_t* node_parent, float* node_value, int n_max,
+                        int32_t* frontier_out, int32_t* parent_out, int32_t* tok_out,
+                        int32_t* depth_out, int32_t* node_out, int32_t* status) {
+  int n_nodes = 1;
+  int32_t* front = (int32_t*)malloc(sizeof(int32_t) * (size_t)k);
+  char* picked = (char*)malloc((size_t)k * branch + 1);
+  for (int b = 0; b < B; ++b) {
+    int32_t* nt = node_tok + (size_t)b * n_max;
+    int32_t* np = node_parent + (size_t)b * n_max;
+    float* nv = node_value + (size_t)b * n_max;
+    int32_t st = 0;
+    nt[0] = root_tok[b];
+    np[0] = -1;
+    nv[0] = 1.0f;
+    int n = 1, F = 1;
+    front[0] = 0;
+    for (int l = 1; l <= depth; ++l) {
+      if (n + F * branch > n_max) {
+        free(front);
+        free(picked);
+        return -1;
+      }
+      const int base = n;
+      for (int r = 0; r < F; ++r)
+        for (int c = 0; c < branch; ++c) {
+          const size_t src = (((size_t)(l - 1) * B + b) * k + r) * branch + c;
+          const int id = n++;
+          const float prob = conf_as_prob(child_conf[src], &st);
+          nt[id] = child_tok[src];
+          np[id] = front[r];
+          nv[id] = nv[front[r]] * prob;
+        }
+      const int Fn = n - base < k ? n - base : k;
+      memset(picked, 0, (size_t)(n - base));
+      for (int i = 0; i < Fn; ++i) {
+        int best = -1;
+        for (int j = base; j < n; ++j)
+          if (!picked[j - base] && (best < 0 || outranks(nv, j, best))) best = j;
+        picked[best - base] = 1;
+        front[i] = best;
+      }
+      F = Fn;
+      if (frontier_out)
+        for (int i = 0; i < k; ++i)
+          frontier_out[((size_t)(l - 1) * B + b) * k + i] = i < F ? front[i] : -1;
+    }
+    status[b] |= st;
+    n_nodes = n;
+  }
+  free(front);
+  free(picked);
+  oracle_eagle2_rerank(node_tok, node_parent, node_value, n_nodes, n_max, B, T, parent_out,
+                       tok_out, depth_out, node_out, status);
+  return n_nodes;
 }

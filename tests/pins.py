@@ -26,6 +26,7 @@ caught by at least one pin.
 from __future__ import annotations
 
 import itertools
+import math
 import os
 
 import numpy as np
@@ -946,6 +947,306 @@ def pin_stochastic_bad_tokens(lib):
     assert bonus[0] == 2  # uniform p at node 2, u_res 0.5: running sums 0.25, 0.5, 0.75 -> 2
 
 
+
+# ----------------------------------------------------------------------------------------------
+# EAGLE-2 draft tree construction (rainlin.net "EAGLE 系列", section 7)
+# ----------------------------------------------------------------------------------------------
+def read_eagle2_case():
+    levels, frontiers, cases = {}, {}, []
+    with open(os.path.join(GOLDEN, "eagle2_hand_case.txt"), encoding="utf-8") as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            f_ = [x.strip() for x in line.split("|")]
+            if f_[0] == "shape":
+                k, branch, depth, root = (int(x) for x in f_[1:5])
+            elif f_[0] == "level":
+                levels[(int(f_[1]), int(f_[2]))] = ([int(x) for x in f_[3].split()],
+                                                    [_frac(x) for x in f_[4].split()])
+            elif f_[0] == "values":
+                values = [int(x) / 64 for x in f_[1].split()]
+            elif f_[0] == "parents":
+                parents = [int(x) for x in f_[1].split()]
+            elif f_[0] == "frontier":
+                frontiers[int(f_[1])] = [int(x) for x in f_[2].split()]
+            elif f_[0] == "case":
+                cases.append((int(f_[1]), *([int(x) for x in fld.split()] for fld in f_[2:6])))
+    tok = np.zeros((depth, 1, k, branch), np.int32)
+    conf = np.zeros((depth, 1, k, branch), np.float32)
+    for (lvl, slot), (t, c) in levels.items():
+        tok[lvl - 1, 0, slot] = t
+        conf[lvl - 1, 0, slot] = c
+    return dict(k=k, branch=branch, depth=depth, root=root, tok=tok, conf=conf, values=values,
+                parents=parents, frontiers=frontiers, cases=cases)
+
+
+def pin_eagle2_hand_case(lib):
+    g = read_eagle2_case()
+    for T, nodes, parents, depths, toks in g["cases"]:
+        r = O.eagle2_build(np.array([g["root"]]), g["tok"], g["conf"], T, lib=lib)
+        assert r["status"][0] == 0, f"T={T}: status {r['status'][0]}"
+        assert list(r["node_parent"][0]) == g["parents"]
+        assert list(r["node_value"][0].astype(np.float64)) == g["values"]
+        for lvl, want in g["frontiers"].items():
+            assert list(r["frontier"][lvl - 1, 0, : len(want)]) == want, f"frontier {lvl}"
+        assert list(r["node"][0]) == nodes, f"T={T}: nodes {list(r['node'][0])}"
+        assert list(r["parent"][0]) == parents, f"T={T}: parents {list(r['parent'][0])}"
+        assert list(r["depth"][0]) == depths and list(r["tok"][0]) == toks, f"T={T}"
+
+
+def _e2_inputs(rng, B, depth, k, branch, ties=False, vocab=50):
+    """Drafter outputs for a small expansion: confidences are a softmax of normal logits, sorted
+    best first as a top-`branch` returns them (``ties``: rounded to a few dyadic values)."""
+    logits = rng.normal(0.0, 1.4, size=(depth, B, k, branch))
+    e = np.exp(logits - logits.max(axis=-1, keepdims=True))
+    conf = -np.sort(-(e / e.sum(axis=-1, keepdims=True)), axis=-1)
+    if ties:
+        conf = np.clip(np.round(conf * 4) / 4, 0.25, 1.0)
+    tok = rng.integers(0, vocab, size=(depth, B, k, branch)).astype(np.int32)
+    root = rng.integers(0, vocab, size=B).astype(np.int32)
+    return root, tok, conf.astype(np.float32)
+
+
+def _outranks(values, a, b):
+    return values[a] > values[b] or (values[a] == values[b] and a < b)
+
+
+def _check_e2_structure(r, root, tok, conf, depth, k, branch, T, brute=True):
+    """Independent checks of one construction: node table against the drafter outputs, path
+    products taken by walking each root path, the top-set properties of every frontier and of
+    the kept set (and, on tiny tables, the maximum-sum subset by enumeration), and the flattened
+    order against a breadth-first traversal with children visited in id order."""
+    B = root.shape[0]
+    for b in range(B):
+        par, val, ntok = r["node_parent"][b], r["node_value"][b], r["node_tok"][b]
+        N = len(par)
+        # table layout: child c of frontier slot r at level l is node base + r*branch + c
+        front, base = [0], 1
+        for lvl in range(1, depth + 1):
+            for slot, u in enumerate(front):
+                for c in range(branch):
+                    nid = base + slot * branch + c
+                    assert par[nid] == u and ntok[nid] == tok[lvl - 1, b, slot, c]
+            n_lvl = len(front) * branch
+            level_ids = list(range(base, base + n_lvl))
+            F = min(k, n_lvl)
+            got = [int(x) for x in r["frontier"][lvl - 1, b, :F]]
+            assert all(x == -1 for x in r["frontier"][lvl - 1, b, F:])
+            vals = {i: float(val[i]) for i in level_ids}
+            for pos, x in enumerate(got):  # best first, and every member beats every non-member
+                assert x in vals
+                for y in level_ids:
+                    if y not in got:
+                        assert _outranks(vals, x, y), f"level {lvl}: {x} does not beat {y}"
+                if pos:
+                    assert _outranks(vals, got[pos - 1], x)
+            front, base = got, base + n_lvl
+        assert base == N
+        # values: float32 products along the root path, root first
+        for i in range(N):
+            path = []
+            cur = i
+            while cur != -1:
+                path.append(cur)
+                cur = int(par[cur])
+            v = np.float32(1.0)
+            for nd in path[::-1][1:]:  # root first, the root itself excluded
+                v = np.float32(v * _conf_of(r, tok, conf, b, nd, depth, k, branch))
+            assert val[i] == v, f"node {i}: value {val[i]} != path product {v}"
+        # kept set: the T best nodes
+        kept = [int(x) for x in r["node"][b]]
+        assert len(set(kept)) == T
+        vals = {i: float(val[i]) for i in range(N)}
+        kept_set = set(kept)
+        for x in kept:
+            for y in range(N):
+                if y not in kept_set:
+                    assert _outranks(vals, x, y), f"kept {x} does not beat dropped {y}"
+        if brute and len(set(vals.values())) == N and math.comb(N, T) <= 20000:
+            best = max(itertools.combinations(range(N), T),
+                       key=lambda S: sum(vals[i] for i in S))
+            assert set(best) == kept_set
+        # flattened order: breadth-first from the root, children in id order
+        order, queue = [], [0]
+        kids = {i: [] for i in range(N)}
+        for i in range(1, N):
+            kids[int(par[i])].append(i)
+        while queue:
+            u = queue.pop(0)
+            order.append(u)
+            queue.extend(c for c in kids[u] if c in kept_set)
+        assert order == kept, f"flattened {kept} != breadth-first {order}"
+        pos = {u: f for f, u in enumerate(order)}
+        assert list(r["parent"][b]) == [-1] + [pos[int(par[u])] for u in order[1:]]
+        assert list(r["tok"][b]) == [int(ntok[u]) for u in order]
+        assert r["tok"][b][0] == root[b]
+        dep = [0] * T
+        for f in range(1, T):
+            dep[f] = dep[r["parent"][b][f]] + 1
+        assert list(r["depth"][b]) == dep
+
+
+def _conf_of(r, tok, conf, b, nd, depth, k, branch):
+    """The drafter confidence that created node nd (found from the frontier records)."""
+    front, base = [0], 1
+    for lvl in range(1, depth + 1):
+        n_lvl = len(front) * branch
+        if nd < base + n_lvl:
+            slot, c = divmod(nd - base, branch)
+            return np.float32(min(max(float(conf[lvl - 1, b, slot, c]), 0.0), 1.0))
+        F = min(k, n_lvl)
+        front = [int(x) for x in r["frontier"][lvl - 1, b, :F]]
+        base += n_lvl
+    raise AssertionError("node id past the table")
+
+
+def pin_eagle2_bruteforce(lib):
+    rng = np.random.default_rng(7)
+    for trial in range(60):
+        depth, k, branch = int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        N = O.eagle2_node_count(depth, k, branch)
+        T = int(rng.integers(1, N + 1))
+        root, tok, conf = _e2_inputs(rng, 2, depth, k, branch, ties=trial % 3 == 0)
+        r = O.eagle2_build(root, tok, conf, T, lib=lib)
+        assert (r["status"] == 0).all()
+        _check_e2_structure(r, root, tok, conf, depth, k, branch, T)
+    # a larger expansion (the top-set and breadth-first checks only)
+    root, tok, conf = _e2_inputs(rng, 2, 5, 4, 4)
+    r = O.eagle2_build(root, tok, conf, 40, lib=lib)
+    _check_e2_structure(r, root, tok, conf, 5, 4, 4, 40, brute=False)
+
+
+def pin_eagle2_batch_independent(lib):
+    rng = np.random.default_rng(8)
+    root, tok, conf = _e2_inputs(rng, 4, 4, 3, 3)
+    r = O.eagle2_build(root, tok, conf, 17, lib=lib)
+    for b in range(4):
+        rb = O.eagle2_build(root[b : b + 1], tok[:, b : b + 1], conf[:, b : b + 1], 17, lib=lib)
+        for name in ("node_tok", "node_parent", "node_value", "parent", "tok", "depth", "node"):
+            assert (rb[name][0] == r[name][b]).all(), name
+        assert (rb["frontier"][:, 0] == r["frontier"][:, b]).all()
+
+
+def pin_eagle2_chain(lib):
+    """One child per node: the tree is a chain, and the kept prefix is the first T levels."""
+    rng = np.random.default_rng(9)
+    depth = 7
+    root, tok, conf = _e2_inputs(rng, 1, depth, 3, 1)
+    conf[:] = rng.uniform(0.05, 0.95, size=conf.shape).astype(np.float32)
+    for T in (1, 4, depth + 1):
+        r = O.eagle2_build(root, tok, conf, T, lib=lib)
+        assert list(r["node"][0]) == list(range(T))
+        assert list(r["parent"][0]) == list(range(-1, T - 1))
+        assert list(r["depth"][0]) == list(range(T))
+        assert list(r["tok"][0]) == [int(root[0])] + [int(tok[i, 0, 0, 0]) for i in range(T - 1)]
+        v = np.float32(1.0)
+        for i in range(1, depth + 1):
+            v = np.float32(v * conf[i - 1, 0, 0, 0])
+            assert r["node_value"][0, i] == v
+
+
+def pin_eagle2_keep_everything(lib):
+    """No pruning (k at least the widest level) and T = all nodes: the flattened tree is the
+    complete branch-ary tree in breadth-first order, parent of position f = (f - 1) // branch,
+    whatever the confidences."""
+    rng = np.random.default_rng(10)
+    for depth, branch in ((3, 2), (2, 4), (4, 3)):
+        k = branch ** depth
+        root, tok, conf = _e2_inputs(rng, 2, depth, k, branch)
+        N = O.eagle2_node_count(depth, k, branch)
+        assert N == sum(branch ** i for i in range(depth + 1))
+        r = O.eagle2_build(root, tok, conf, N, lib=lib)
+        for b in range(2):
+            assert list(r["parent"][b]) == [-1] + [(f - 1) // branch for f in range(1, N)]
+            # every drafted token appears once (level l uses the first branch**(l-1) slots)
+            exp = []
+            F = 1
+            for lvl in range(depth):
+                exp += [int(x) for x in tok[lvl, b, :F].ravel()]
+                F *= branch
+            assert sorted(int(x) for x in r["tok"][b][1:]) == sorted(exp)
+            assert r["tok"][b][0] == root[b]
+
+
+def pin_eagle2_equal_confidences(lib):
+    """Every confidence 1/2: a level's values all tie, so every frontier is its first k
+    children, and the kept set is the T smallest ids, already in flattened order."""
+    rng = np.random.default_rng(11)
+    for depth, k, branch, T in ((3, 2, 3, 12), (4, 3, 2, 18), (2, 5, 5, 9)):
+        root, tok, conf = _e2_inputs(rng, 1, depth, k, branch)
+        conf[:] = 0.5
+        r = O.eagle2_build(root, tok, conf, T, lib=lib)
+        assert list(r["node"][0]) == list(range(T))
+        assert list(r["parent"][0]) == [int(x) for x in r["node_parent"][0, :T]]
+        base, F = 1, 1
+        for lvl in range(depth):
+            n_lvl = F * branch
+            F = min(k, n_lvl)
+            assert list(r["frontier"][lvl, 0, :F]) == list(range(base, base + F))
+            base += n_lvl
+
+
+def pin_eagle2_bad_confidences(lib):
+    """Confidences outside [0, 1] are flagged and used clamped: NaN and negatives as 0, values
+    above one as 1 (-0.0 is a valid 0)."""
+    rng = np.random.default_rng(12)
+    root, tok, conf = _e2_inputs(rng, 2, 3, 3, 3)
+    bad = conf.copy()
+    bad[0, 0, 0, 1] = np.nan
+    bad[1, 0, 1, 0] = -0.5
+    bad[2, 0, 0, 2] = 1.5
+    bad[1, 0, 0, 0] = np.inf
+    bad[0, 1, 0, 2] = -0.0
+    clamped = bad.copy()
+    clamped[np.isnan(clamped)] = 0.0
+    clamped = np.clip(clamped, 0.0, 1.0)
+    clamped[0, 1, 0, 2] = 0.0
+    rb = O.eagle2_build(root, tok, bad, 20, lib=lib)
+    rc = O.eagle2_build(root, tok, clamped, 20, lib=lib)
+    assert list(rb["status"]) == [O.ORC_BAD_CONF, 0] and list(rc["status"]) == [0, 0]
+    for name in ("node_parent", "node_value", "frontier", "parent", "tok", "depth", "node"):
+        assert np.array_equal(rb[name], rc[name]), name
+    assert not np.signbit(rb["node_value"]).any()
+
+
+def pin_eagle2_rerank_tables(lib):
+    """Reranking of caller-built tables: a valid one (values never grow from parent to child)
+    gives the top-set and breadth-first order; a table that is not such a tree is flagged and
+    gets parent -1, token -1, depth 0, node -1 everywhere."""
+    rng = np.random.default_rng(13)
+    N, T = 30, 12
+    par = np.array([-1] + [int(rng.integers(0, i)) for i in range(1, N)], np.int32)
+    val = np.ones(N, np.float32)
+    for i in range(1, N):
+        val[i] = np.float32(val[par[i]] * np.float32(rng.choice([0.25, 0.5, 0.75, 1.0])))
+    ntok = rng.integers(0, 100, size=N).astype(np.int32)
+    r = O.eagle2_rerank(ntok[None], par[None], val[None], T, lib=lib)
+    assert r["status"][0] == 0
+    kept = [int(x) for x in r["node"][0]]
+    vals = {i: float(val[i]) for i in range(N)}
+    for x in kept:
+        for y in set(range(N)) - set(kept):
+            assert _outranks(vals, x, y)
+    order, queue = [], [0]
+    while queue:
+        u = queue.pop(0)
+        order.append(u)
+        queue.extend(c for c in range(1, N) if par[c] == u and c in kept)
+    assert order == kept
+    bads = []
+    p1 = par.copy(); p1[0] = 0; bads.append((p1, val))                      # root not a root
+    p2 = par.copy(); p2[7] = 7; bads.append((p2, val))                      # parent not below
+    p3 = par.copy(); p3[9] = -1; bads.append((p3, val))                     # second root
+    v4 = val.copy(); c = int(np.argmax(par > 0)); v4[c] = val[par[c]] * 2   # child above parent
+    bads.append((par, v4))
+    for pb, vb in bads:
+        rb = O.eagle2_rerank(np.stack([ntok, ntok]), np.stack([pb, par]), np.stack([vb, val]), T,
+                             lib=lib)
+        assert list(rb["status"]) == [O.ORC_BAD_TREE, 0]
+        assert (rb["parent"][0] == -1).all() and (rb["tok"][0] == -1).all()
+        assert (rb["depth"][0] == 0).all() and (rb["node"][0] == -1).all()
+        assert list(rb["node"][1]) == kept
+
 ALL_PINS = [
     pin_worked_tree_mask,
     pin_mask_closure_bruteforce,
@@ -974,4 +1275,12 @@ ALL_PINS = [
     pin_stochastic_onehot_is_greedy,
     pin_stochastic_lossless_one_level,
     pin_stochastic_lossless_two_levels,
+    pin_eagle2_hand_case,
+    pin_eagle2_chain,
+    pin_eagle2_equal_confidences,
+    pin_eagle2_keep_everything,
+    pin_eagle2_bad_confidences,
+    pin_eagle2_rerank_tables,
+    pin_eagle2_batch_independent,
+    pin_eagle2_bruteforce,
 ]

@@ -106,6 +106,34 @@ MUTANTS = {
                             ""),
     # stochastic: an out-of-vocabulary child is tested (as token 0) instead of skipped
     "stoch_bad_token_tested": ("          status[b] |= ORC_BAD_TOKEN;\n          continue;\n", ""),
+    # draft tree: a node's value is its own confidence, not the path product
+    "e2_value_not_product": ("nv[id] = nv[front[r]] * prob;", "nv[id] = prob;"),
+    # draft tree: every child hung under the best frontier node
+    "e2_parent_first_slot": ("np[id] = front[r];", "np[id] = front[0];"),
+    # draft tree: equal values go to the larger id
+    "e2_tie_larger_id": ("return va > vb || (va == vb && a < b);",
+                         "return va > vb || (va == vb && a > b);"),
+    # draft tree: the frontier keeps the worst children
+    "e2_frontier_worst": ("if (!picked[j - base] && (best < 0 || outranks(nv, j, best))) best = j;",
+                          "if (!picked[j - base] && (best < 0 || outranks(nv, best, j))) best = j;"),
+    # draft tree: the rerank keeps the T earliest nodes whatever their values
+    "e2_rerank_by_id": ("if (!kept[i] && (best < 0 || outranks(nv, i, best))) best = i;",
+                        "if (!kept[i] && (best < 0 || i < best)) best = i;"),
+    # draft tree: a level flattened by node id, ignoring the parents' flattened order
+    "e2_flatten_by_id": ("if (pf_i < pf_b || (pf_i == pf_b && i < best)) best = i;",
+                         "if (i < best) best = i;"),
+    # draft tree: siblings flattened in reverse
+    "e2_siblings_reversed": ("if (pf_i < pf_b || (pf_i == pf_b && i < best)) best = i;",
+                             "if (pf_i < pf_b || (pf_i == pf_b && i > best)) best = i;"),
+    # draft tree: confidences used unclamped
+    "e2_conf_unclamped": ("return c > 0.0f ? (c < 1.0f ? c : 1.0f) : 0.0f;", "return c;"),
+    # draft tree: bad confidences not reported
+    "e2_conf_not_flagged": ("if (!(c >= 0.0f && c <= 1.0f)) *st |= ORC_BAD_CONF;", ""),
+    # draft tree: a child valued above its parent accepted as a tree
+    "e2_table_allows_growth": ("if (p < 0 || p >= i || rank_value(nv[i]) > rank_value(nv[p])) valid = 0;",
+                               "if (p < 0 || p >= i) valid = 0;"),
+    # draft tree: flattened depth counted from one
+    "e2_depth_from_one": ("        dout[f] = d;\n", "        dout[f] = d + 1;\n"),
 }
 
 
