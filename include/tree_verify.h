@@ -58,6 +58,7 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_BAD_TOKEN 0x20 /* stochastic acceptance: a tried child's token outside [0, V) */
 #define TV_SYNC_TIMEOUT 0x40 /* stochastic acceptance: its workgroups did not all meet (they were
                                 not resident together); results invalid, re-zero the workspace */
+#define TV_BAD_CONF 0x80 /* draft tree: a drafter confidence outside [0, 1] (used clamped) */
 
 /* Human-readable name of a tv_status return value or of a single status bit. */
 const char* tv_status_string(int code);
@@ -309,6 +310,75 @@ int tree_verify_step(const int32_t* parent, const int32_t* draft_tok, const int3
                      int32_t* accept_len, int32_t* bonus_tok, int32_t* status, int B, int T,
                      int Hq, int Hkv, int D, int Lmax, int dtype, float scale, int split_keys,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Dynamic draft tree of EAGLE-2 (rainlin.net "EAGLE 系列", section 7), built on the device.
+ *
+ * Expansion (section 7.1): from the deepest level of the tree, the k nodes with the largest
+ * global acceptance value go to the drafter for the next level, a node's value being the
+ * product of the drafter's confidences on its root path.  Reranking (section 7.2): after the
+ * last level, the T nodes of largest value are kept (a child never outranks its parent, so they
+ * form a tree) and flattened into one sequence for verification.
+ *
+ * Node table of a sequence (caller-owned, row stride n_max): node_tok, node_parent (id of the
+ * parent, -1 at the root) and node_value (float32).  The root is node 0 with value 1; child c of
+ * frontier slot r of level l is node n_l + r * branch + c, where n_l = eagle2_node_count(l - 1,
+ * k, branch) counts the nodes of the levels before.  Node A outranks node B iff A's value is
+ * larger, or equal and A's id smaller (created earlier, so never deeper).  Values are float32
+ * products parent value * confidence, rounded to nearest even; every decision compares them
+ * exactly, so results are bit-exact.
+ */
+
+/* Nodes in the table after `depth` levels (the root, then branch children of every frontier
+ * node of each level, a frontier holding min(k, children of its level) nodes); -1 for bad
+ * arguments.  Host function, no device work. */
+int eagle2_node_count(int depth, int k, int branch);
+
+/*
+ * eagle2_expand — level `level` (1, 2, ...) of the expansion, for every sequence.
+ *
+ *   root_tok    [B]              int32  token of the root (the token the target model emitted
+ *                                       last); read at level 1 only (may be NULL otherwise)
+ *   child_tok   [B,k,branch]     int32  the drafter's candidate tokens for each frontier slot
+ *                                       (slot 0 only at level 1, whose parent is the root)
+ *   child_conf  [B,k,branch]     fp32   their confidences; one outside [0, 1] (or NaN) is used
+ *                                       clamped into it (NaN as 0) and TV_BAD_CONF is OR-ed in
+ *   node_tok, node_parent, node_value  [B,n_max]  the node table: level 1 writes the root and
+ *                                       its children, level l > 1 appends level l's nodes;
+ *                                       n_max >= eagle2_node_count(level, k, branch)
+ *   frontier    [B,k]            int32  in (level > 1): the previous level's frontier, as the
+ *                                       previous call left it; out: this level's frontier, its
+ *                                       min(k, children) best children, best first, then -1
+ *   status      [B]              int32  OR-ed: TV_BAD_CONF; TV_BAD_TREE if a frontier entry is
+ *                                       not a node of the previous level (that slot's children
+ *                                       get parent -1 and value 0, and eagle2_rerank rejects
+ *                                       the table)
+ * Limits: B >= 1, level >= 1, k >= 1, branch >= 1, k * branch <= 1024.
+ */
+int eagle2_expand(const int32_t* root_tok, const int32_t* child_tok, const float* child_conf,
+                  int B, int level, int k, int branch, int32_t* node_tok, int32_t* node_parent,
+                  float* node_value, int n_max, int32_t* frontier, int32_t* status, void* stream);
+
+/*
+ * eagle2_rerank — keep the T best nodes of each table and flatten them in level order: by
+ * depth, then by the flattened index of the parent, then by node id (siblings in the drafter's
+ * order).  The output is a level-ordered tree with its root at 0, ready for tree_build_mask.
+ *
+ *   node_tok, node_parent, node_value  [B,n_max]  tables of n_nodes nodes (any source: they
+ *                                       must form a tree with node 0 the root, parent ids below
+ *                                       the node's own, no value above its parent's; NaN and
+ *                                       negative values count as 0)
+ *   parent_out  [B,T]  int32  out: flattened index of each position's parent (-1 at 0)
+ *   tok_out     [B,T]  int32  out: its token (the draft tokens of the verification step)
+ *   depth_out   [B,T]  int32  out: its depth (the root is 0; position offsets for the target)
+ *   node_out    [B,T]  int32  out: its node id in the table
+ *   status      [B]    int32  OR-ed: TV_BAD_TREE for a table that is not such a tree; its
+ *                             outputs are parent -1, token -1, depth 0, node -1 everywhere
+ * Limits: B >= 1, 1 <= T <= min(128, n_nodes), n_nodes <= min(n_max, 16384).
+ */
+int eagle2_rerank(const int32_t* node_tok, const int32_t* node_parent, const float* node_value,
+                  int n_nodes, int n_max, int B, int T, int32_t* parent_out, int32_t* tok_out,
+                  int32_t* depth_out, int32_t* node_out, int32_t* status, void* stream);
 
 #ifdef __cplusplus
 }

@@ -5,7 +5,12 @@ lengths and q/k/v tensors.  It holds none of the verification arithmetic
 (no masks, no attention, no acceptance walk, no compaction), so both the CPU
 oracle and the HIP path can be fed from it without sharing any of the method.
 ``make_paged`` only places a workload's rows into a pool of token slots; ``make_stochastic``
-draws next-token distributions, drafted tokens and uniforms for sampling-mode acceptance.
+draws next-token distributions, drafted tokens and uniforms for sampling-mode acceptance;
+``make_draft_levels`` draws the drafter's per-level candidates (tokens and confidences) that
+EAGLE-2 tree construction consumes.  The workload trees themselves are inputs of the
+verification step, drawn by a float64 expand-and-rerank recipe in ``eagle2_tree``; the
+device-side tree construction is checked against the oracle on ``make_draft_levels`` inputs,
+never against these trees.
 """
 from .workloads import (  # noqa: F401
     WORKLOADS,
@@ -13,6 +18,8 @@ from .workloads import (  # noqa: F401
     StochasticInputs,
     Workload,
     WorkloadSpec,
+    DraftLevels,
+    make_draft_levels,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_paged,

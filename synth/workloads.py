@@ -460,3 +460,59 @@ def make_stochastic(w: "Workload", V: int | None = None, without_replacement: bo
         u_acc[b] = rng.random(T)
         u_res[b] = rng.random(T)
     return StochasticInputs(V, bool(without_replacement), p, q, draft, u_acc, u_res)
+
+
+STREAM_DRAFTER = 6  # seed stream of the drafter outputs for device-side tree construction
+
+
+@dataclasses.dataclass
+class DraftLevels:
+    """Drafter outputs consumed by EAGLE-2 tree construction, level by level.
+
+    root_tok [B] int32: the root token of each sequence.  child_tok / child_conf
+    [depth, B, k, branch] (int32, float32): at level l, the candidate children the drafter
+    proposes for frontier slot r of sequence b (the root alone is slot 0 of level 1), with
+    their confidences, best first as a top-`branch` returns them.  Sibling tokens are distinct.
+    The drafter is synthetic, so its output for a slot does not depend on which node sits in
+    that slot."""
+    depth: int
+    k: int
+    branch: int
+    root_tok: np.ndarray
+    child_tok: np.ndarray
+    child_conf: np.ndarray
+
+
+def make_draft_levels(spec: WorkloadSpec | str, B: int | None = None, depth: int | None = None,
+                      k: int | None = None, branch: int | None = None, seed: int = 0,
+                      vocab: int | None = None, variance: float = 2.0) -> DraftLevels:
+    """Seeded drafter outputs with a workload's expansion shape (overridable).  Each slot's
+    confidences are the softmax (float64, stored float32) of `branch` N(0, variance) logits,
+    the recipe of the workload trees; tokens are distinct draws from the vocabulary."""
+    if isinstance(spec, str):
+        spec = WORKLOADS[spec]
+    B = spec.B if B is None else B
+    depth = spec.depth_max if depth is None else depth
+    k = spec.topk if k is None else k
+    branch = spec.branch if branch is None else branch
+    vocab = spec.vocab if vocab is None else vocab
+    if min(depth, k, branch) < 1 or branch > vocab:
+        raise ValueError("expansion shape needs depth, k, branch >= 1 and branch <= vocab")
+    root = np.empty(B, np.int32)
+    tok = np.empty((depth, B, k, branch), np.int32)
+    conf = np.empty((depth, B, k, branch), np.float32)
+    sd = math.sqrt(variance)
+    for b in range(B):
+        rng = _rng(spec.wid, b, STREAM_DRAFTER, seed)
+        root[b] = rng.integers(0, vocab)
+        logits = rng.normal(0.0, sd, size=(depth, k, branch))
+        e = np.exp(logits - logits.max(axis=-1, keepdims=True))
+        conf[:, b] = -np.sort(-(e / e.sum(axis=-1, keepdims=True)), axis=-1)
+        for l in range(depth):
+            for r in range(k):
+                while True:
+                    t = rng.integers(0, vocab, size=branch)
+                    if len(np.unique(t)) == branch:
+                        break
+                tok[l, b, r] = t
+    return DraftLevels(depth, k, branch, root, tok, conf)

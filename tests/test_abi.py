@@ -242,3 +242,49 @@ def test_stochastic_workspace_size_rules(lib):
     assert ws(4, 60, 1000, 0) == 0        # a 1000-token vocabulary is too small to split
     assert ws(2, 60, 128256, 3) == 2 * 60 * 3 * 16 + 2 * 4
     assert ws(0, 60, 1000, 0) == 0 and ws(1, 60, 1000, 65) == 0
+
+
+def test_eagle2_node_count(lib):
+    from oracle import oracle as O
+
+    for depth, k, branch in ((0, 3, 3), (1, 10, 10), (6, 10, 10), (8, 10, 10), (10, 16, 16),
+                             (5, 1, 4), (4, 7, 1)):
+        assert lib.eagle2_node_count(depth, k, branch) == O.eagle2_node_count(depth, k, branch)
+    assert lib.eagle2_node_count(-1, 3, 3) == -1 and lib.eagle2_node_count(2, 0, 3) == -1
+    assert lib.eagle2_node_count(2000, 1024, 1024) == -1  # too many nodes
+
+
+def test_eagle2_expand_argument_errors(lib):
+    # root, tok, conf, B, level, k, branch, node_tok, node_parent, node_value, n_max, frontier,
+    # status, stream
+    base = [FAKE] * 3 + [2, 1, 10, 10] + [FAKE] * 3 + [111, FAKE, FAKE, None]
+    for i in (1, 2, 7, 8, 9, 11, 12):
+        bad = list(base)
+        bad[i] = None
+        assert lib.eagle2_expand(*bad) == -1, i
+    bad = list(base)
+    bad[0] = None  # the root token is needed at level 1 only
+    assert lib.eagle2_expand(*bad) == -1
+    for i, v in ((3, 0), (4, 0), (5, 0), (6, 0), (5, 103), (10, 10)):  # 103 * 10 > 1024
+        bad = list(base)
+        bad[i] = v
+        assert lib.eagle2_expand(*bad) == -1, (i, v)
+    bad = list(base)
+    bad[4], bad[10] = 2, 110  # level 2 needs 1 + 10 + 100 = 111 nodes
+    assert lib.eagle2_expand(*bad) == -1
+
+
+def test_eagle2_rerank_argument_errors(lib):
+    # tok, parent, value, n_nodes, n_max, B, T, parent_out, tok_out, depth_out, node_out,
+    # status, stream
+    base = [FAKE] * 3 + [511, 511, 1, 60] + [FAKE] * 5 + [None]
+    for i in (0, 1, 2, 7, 8, 9, 10, 11):
+        bad = list(base)
+        bad[i] = None
+        assert lib.eagle2_rerank(*bad) == -1, i
+    for i, v in ((5, 0), (6, 0), (6, 129), (3, 59), (4, 510), (3, 16385)):
+        bad = list(base)
+        bad[i] = v
+        if i == 3 and v > 511:
+            bad[4] = v
+        assert lib.eagle2_rerank(*bad) == -1, (i, v)

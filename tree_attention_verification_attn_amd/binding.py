@@ -17,13 +17,14 @@ from . import build as _build
 TV_OK, TV_ERR_INVALID_ARG, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_HIP = 0, -1, -2, -3, -4
 TV_F32, TV_BF16 = 0, 1
 TV_BAD_TREE, TV_OVERFLOW, TV_BAD_LEN, TV_BAD_PATH, TV_BAD_PAGE = 0x1, 0x2, 0x4, 0x8, 0x10
-TV_BAD_TOKEN, TV_SYNC_TIMEOUT = 0x20, 0x40
+TV_BAD_TOKEN, TV_SYNC_TIMEOUT, TV_BAD_CONF = 0x20, 0x40, 0x80
 
 EXPORTS = ("tv_status_string", "tree_build_mask", "tree_verify_attn_workspace_size",
            "tree_verify_attn", "tree_accept", "kv_compact_accepted", "tv_profile_attn_main",
            "tree_verify_step", "tree_verify_attn_paged", "kv_commit_paged",
            "tree_accept_stochastic", "tree_accept_stochastic_workspace_size",
-           "tv_profile_accept_stochastic")
+           "tv_profile_accept_stochastic", "eagle2_node_count", "eagle2_expand",
+           "eagle2_rerank")
 
 
 class TreeVerifyError(RuntimeError):
@@ -89,6 +90,12 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_accept_stochastic.restype = I
     lib.tv_profile_accept_stochastic.argtypes = [P, P]
     lib.tv_profile_accept_stochastic.restype = I
+    lib.eagle2_node_count.argtypes = [I, I, I]
+    lib.eagle2_node_count.restype = I
+    lib.eagle2_expand.argtypes = [P, P, P, I, I, I, I, P, P, P, I, P, P, P]
+    lib.eagle2_expand.restype = I
+    lib.eagle2_rerank.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P, P]
+    lib.eagle2_rerank.restype = I
 
 
 def status_string(code: int) -> str:
@@ -433,3 +440,68 @@ def kv_commit_paged(block_table, cache_len, tree_slot, accept_path, accept_len, 
         _ptr(tree_slot), _ptr(accept_path), _ptr(accept_len), _ptr(free_slots), _ptr(free_top),
         int(num_slots), B, T, _ptr(status), _stream(stream)))
     return cache_len_out
+
+
+def eagle2_node_count(depth: int, k: int, branch: int) -> int:
+    """Nodes of the table after `depth` expansion levels (host arithmetic of the library)."""
+    n = int(load_library().eagle2_node_count(depth, k, branch))
+    if n < 0:
+        raise ValueError(f"bad expansion shape depth={depth} k={k} branch={branch}")
+    return n
+
+
+def eagle2_new_table(B: int, n_max: int, k: int, device) -> dict:
+    """Device buffers of the EAGLE-2 node table of B sequences: node_tok, node_parent,
+    node_value [B, n_max], frontier [B, k] and status [B] (zeroed)."""
+    return {
+        "node_tok": torch.empty((B, n_max), dtype=torch.int32, device=device),
+        "node_parent": torch.empty((B, n_max), dtype=torch.int32, device=device),
+        "node_value": torch.empty((B, n_max), dtype=torch.float32, device=device),
+        "frontier": torch.empty((B, k), dtype=torch.int32, device=device),
+        "status": torch.zeros((B,), dtype=torch.int32, device=device),
+    }
+
+
+def eagle2_expand(table: dict, level: int, child_tok, child_conf, root_tok=None, stream=None):
+    """Expansion level `level` (1, 2, ...) into `table` (from eagle2_new_table): child_tok
+    [B,k,branch] int32 and child_conf [B,k,branch] float32 are the drafter's candidates for the
+    frontier slots; root_tok [B] int32 at level 1.  Updates the table and its frontier."""
+    _need(child_tok, "child_tok", torch.int32, 3)
+    _need(child_conf, "child_conf", torch.float32, 3)
+    B, k, branch = child_tok.shape
+    if tuple(child_conf.shape) != (B, k, branch):
+        raise ValueError("child_tok and child_conf shapes differ")
+    for name in ("node_tok", "node_parent", "node_value", "frontier", "status"):
+        _need(table[name], name)
+    n_max = table["node_tok"].shape[1]
+    if (tuple(table["frontier"].shape) != (B, k) or table["node_tok"].shape[0] != B
+            or tuple(table["node_parent"].shape) != (B, n_max)
+            or tuple(table["node_value"].shape) != (B, n_max)):
+        raise ValueError("node table shapes do not match the drafter outputs")
+    if root_tok is not None:
+        _need(root_tok, "root_tok", torch.int32, 1)
+    _check("eagle2_expand", load_library().eagle2_expand(
+        _ptr(root_tok), _ptr(child_tok), _ptr(child_conf), B, int(level), k, branch,
+        _ptr(table["node_tok"]), _ptr(table["node_parent"]), _ptr(table["node_value"]), n_max,
+        _ptr(table["frontier"]), _ptr(table["status"]), _stream(stream)))
+
+
+def eagle2_rerank(table: dict, n_nodes: int, T: int, out: dict | None = None, stream=None) -> dict:
+    """Keep the T best of the table's first n_nodes nodes and flatten them -> dict of parent,
+    tok, depth, node [B,T] int32 (the table's status is OR-ed)."""
+    for name in ("node_tok", "node_parent", "node_value", "status"):
+        _need(table[name], name)
+    B, n_max = table["node_tok"].shape
+    dev = table["node_tok"].device
+    if out is None:
+        out = {name: torch.empty((B, T), dtype=torch.int32, device=dev)
+               for name in ("parent", "tok", "depth", "node")}
+    for name in ("parent", "tok", "depth", "node"):
+        _need(out[name], name, torch.int32, 2)
+        if tuple(out[name].shape) != (B, T):
+            raise ValueError(f"{name} must be [{B}, {T}]")
+    _check("eagle2_rerank", load_library().eagle2_rerank(
+        _ptr(table["node_tok"]), _ptr(table["node_parent"]), _ptr(table["node_value"]),
+        int(n_nodes), n_max, B, int(T), _ptr(out["parent"]), _ptr(out["tok"]), _ptr(out["depth"]),
+        _ptr(out["node"]), _ptr(table["status"]), _stream(stream)))
+    return out

@@ -1,0 +1,313 @@
+// EAGLE-2 dynamic draft tree built on the device (rainlin.net "EAGLE 系列", section 7).
+//
+//   * Expansion (section 7.1), one launch per level, between the drafter's forward passes:
+//     every frontier node of the previous level receives the `branch` candidate children the
+//     drafter proposed for it.  A child's global acceptance value is its parent's value times
+//     its confidence (the product of the confidences on its root path, in float32), and the
+//     frontier of the new level is its k best children, best first.  One workgroup per
+//     sequence, one thread per child; a child's rank is the number of this level's children
+//     that outrank it (larger value, or equal value and smaller node id), counted over LDS.
+//   * Reranking and flattening (section 7.2), one launch after the last level: the T best nodes
+//     of the whole table are kept, and the kept tree is flattened in level order (depth, then
+//     the parent's flattened index, then node id), ready for tree_build_mask.  One workgroup
+//     of 1024 threads per sequence: a radix select over the 48-bit keys
+//     (value bits << 16 | 0xFFFF - id), six 8-bit passes with an LDS histogram and a wavefront
+//     suffix scan, finds the T-th best key; the kept nodes are sorted by id, their depths come
+//     from pointer jumping over the kept list, and the levels are flattened one after another.
+//
+// Node ids: the root is node 0; child c of frontier slot r of level l is node
+// n_l + r * branch + c, with n_l the nodes of the levels before l, so ids grow with depth and
+// equal values resolve towards the shallower node.
+#include <hip/hip_runtime.h>
+
+#include "tree_device.h"
+
+namespace tv {
+namespace {
+
+constexpr int kExpandMax = 1024;        // children of one level (k * branch)
+constexpr int kRerankThreads = 1024;
+constexpr int kRerankMaxNodes = 16384;  // node values staged in LDS (64 KB); ids fit 16 bits
+
+// A drafter confidence used as a probability: NaN and negatives count as 0, values above 1 as 1.
+__device__ inline float as_prob(float c) { return c > 0.f ? (c < 1.f ? c : 1.f) : 0.f; }
+// A node value as it is ranked: NaN and negatives count as 0 (so its bits order as an integer).
+__device__ inline float rank_value(float v) { return v > 0.f ? v : 0.f; }
+
+// One expansion level of sequence blockIdx.x.  F parents: the root at level 1, otherwise
+// frontier[b, 0..F) (ids of the previous level, [prev_lo, base)).  Children go to ids
+// base .. base + F*branch - 1; the new frontier (min(k, F*branch) ids, best first, padded with
+// -1 to k) overwrites frontier[b] after every parent entry has been read.
+__global__ __launch_bounds__(kExpandMax) void expand_kernel(
+    int level, const int32_t* __restrict__ root_tok, const int32_t* __restrict__ child_tok,
+    const float* __restrict__ child_conf, int k, int branch, int F, int prev_lo, int base,
+    int n_max, int32_t* __restrict__ node_tok, int32_t* __restrict__ node_parent,
+    float* __restrict__ node_value, int32_t* __restrict__ frontier, int32_t* __restrict__ status) {
+  __shared__ float s_val[kExpandMax];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int n = F * branch;
+  const int n_front = min(k, n);
+  const size_t row = (size_t)b * n_max;
+  int bits = 0;
+  float v = 0.f;
+  if (tid < n) {
+    const int r = tid / branch, c = tid - r * branch;
+    int pid = 0;
+    float pv = 1.f;
+    bool ok = true;
+    if (level > 1) {
+      pid = frontier[(size_t)b * k + r];
+      ok = pid >= prev_lo && pid < base;
+      pv = ok ? node_value[row + pid] : 0.f;
+      if (!ok) bits |= TV_BAD_TREE;
+    }
+    const size_t src = ((size_t)b * k + r) * branch + c;
+    const float conf = child_conf[src];
+    if (!(conf >= 0.f && conf <= 1.f)) bits |= TV_BAD_CONF;
+    v = rank_value(pv * as_prob(conf));
+    node_tok[row + base + tid] = child_tok[src];
+    node_parent[row + base + tid] = ok ? pid : -1;
+    node_value[row + base + tid] = v;
+    s_val[tid] = v;
+  }
+  if (level == 1 && tid == 0) {
+    node_tok[row] = root_tok[b];
+    node_parent[row] = -1;
+    node_value[row] = 1.f;
+  }
+  __syncthreads();  // every parent entry of the frontier has been read
+  if (tid < n) {
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const float w = s_val[j];
+      rank += (w > v) || (w == v && j < tid);
+    }
+    if (rank < n_front) frontier[(size_t)b * k + rank] = base + tid;
+  }
+  if (tid >= n_front && tid < k) frontier[(size_t)b * k + tid] = -1;
+  if (bits) atomicOr(status + b, bits);
+}
+
+// Reranking and flattening of sequence blockIdx.x's table of n nodes (row stride n_max).
+__global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
+    const int32_t* __restrict__ node_tok, const int32_t* __restrict__ node_parent,
+    const float* __restrict__ node_value, int n, int n_max, int T, int32_t* __restrict__ parent_out,
+    int32_t* __restrict__ tok_out, int32_t* __restrict__ depth_out, int32_t* __restrict__ node_out,
+    int32_t* __restrict__ status) {
+  __shared__ uint32_t s_key[kRerankMaxNodes];  // rank_value bits of every node
+  __shared__ int s_hist[256];
+  __shared__ int s_sel[2];  // digit of the pass, count still to take at or below it
+  __shared__ int s_cnt, s_dmax;
+  __shared__ int s_kept[kMaxT], s_id[kMaxT], s_lp[kMaxT], s_ptr[kMaxT], s_dep[kMaxT],
+      s_flat[kMaxT];
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t row = (size_t)b * n_max;
+  const size_t orow = (size_t)b * T;
+
+  for (int i = tid; i < n; i += kRerankThreads)
+    s_key[i] = __float_as_uint(rank_value(node_value[row + i]));
+  if (tid == 0) {
+    s_cnt = 0;
+    s_dmax = 0;
+  }
+  __syncthreads();
+  // a tree whose values never grow from parent to child: then a parent outranks its children
+  // and the kept set is closed under parents
+  int bad = 0;
+  for (int i = tid; i < n; i += kRerankThreads) {
+    const int p = node_parent[row + i];
+    bad |= i == 0 ? p != -1 : (p < 0 || p >= i || s_key[i] > s_key[p]);
+  }
+  if (__syncthreads_or(bad)) {
+    for (int f = tid; f < T; f += kRerankThreads) {
+      parent_out[orow + f] = -1;
+      tok_out[orow + f] = -1;
+      depth_out[orow + f] = 0;
+      node_out[orow + f] = -1;
+    }
+    if (tid == 0) atomicOr(status + b, TV_BAD_TREE);
+    return;
+  }
+
+  // ---- radix select of the T-th best key, 8 bits per pass from the top -------------------
+  auto key48 = [&](int i) -> uint64_t {
+    return ((uint64_t)s_key[i] << 16) | (uint32_t)(0xFFFF - i);
+  };
+  uint64_t prefix = 0;
+  int need = T;
+  for (int pass = 0; pass < 6; ++pass) {
+    const int shift = 40 - 8 * pass;
+    if (tid < 256) s_hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kRerankThreads) {
+      const uint64_t key = key48(i);
+      if ((key >> (shift + 8)) == (prefix >> (shift + 8)))
+        atomicAdd(&s_hist[(int)(key >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane l holds bins 4l .. 4l+3; S = keys in bins of lanes >= l (a suffix scan)
+      int h[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h[j] = s_hist[4 * lane + j];
+      const int mine = h[0] + h[1] + h[2] + h[3];
+      int S = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_down(S, off, 64);
+        if (lane + off < 64) S += o;
+      }
+      const int above = S - mine;
+      if (above < need && need <= S) {  // exactly one lane
+        int acc = above, d = 4 * lane;
+        for (int j = 3; j >= 0; --j) {
+          if (acc + h[j] >= need) {
+            d = 4 * lane + j;
+            break;
+          }
+          acc += h[j];
+        }
+        s_sel[0] = d;
+        s_sel[1] = need - acc;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint64_t)s_sel[0] << shift;
+    need = s_sel[1];
+  }
+  // keys are distinct, so exactly T nodes have a key at or above the T-th best
+
+  // ---- kept nodes in id order, parents, depths ---------------------------------------------
+  for (int i = tid; i < n; i += kRerankThreads)
+    if (key48(i) >= prefix) {
+      const int slot = atomicAdd(&s_cnt, 1);
+      if (slot < kMaxT) s_kept[slot] = i;
+    }
+  __syncthreads();
+  if (tid < T) {
+    const int u = s_kept[tid];
+    int r = 0;
+    for (int j = 0; j < T; ++j) r += s_kept[j] < u;
+    s_id[r] = u;
+  }
+  __syncthreads();
+  if (tid < T) {
+    // position of the parent in the id-ordered list (node 0, the best node, is at position 0)
+    int pos = -1;
+    if (tid > 0) {
+      const int pu = node_parent[row + s_id[tid]];
+      int lo = 0, hi = tid - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s_id[mid] < pu) lo = mid + 1;
+        else hi = mid;
+      }
+      pos = lo;
+    }
+    s_lp[tid] = pos;
+    s_ptr[tid] = pos;
+    s_dep[tid] = pos < 0 ? 0 : 1;
+    s_flat[tid] = -1;
+  }
+  // pointer jumping: s_dep is the distance to s_ptr, which doubles every round
+  for (int span = 1; span < T; span <<= 1) {
+    __syncthreads();
+    int nd = 0, np = -1;
+    if (tid < T) {
+      const int p = s_ptr[tid];
+      nd = s_dep[tid] + (p >= 0 ? s_dep[p] : 0);
+      np = p >= 0 ? s_ptr[p] : -1;
+    }
+    __syncthreads();
+    if (tid < T) {
+      s_dep[tid] = nd;
+      s_ptr[tid] = np;
+    }
+  }
+  __syncthreads();
+  int dep = 0, off = 0;
+  if (tid < T) {
+    dep = s_dep[tid];
+    atomicMax(&s_dmax, dep);
+    for (int j = 0; j < T; ++j) off += s_dep[j] < dep;
+  }
+  __syncthreads();
+  const int dmax = s_dmax;
+
+  // ---- flatten one level at a time: by the parent's flattened index, then by id --------------
+  for (int d = 0; d <= dmax; ++d) {
+    if (tid < T && dep == d) {
+      const int pf = d == 0 ? -1 : s_flat[s_lp[tid]];
+      int r = 0;
+      for (int j = 0; j < T; ++j) {
+        if (j == tid || s_dep[j] != d) continue;
+        const int pfj = d == 0 ? -1 : s_flat[s_lp[j]];
+        r += pfj < pf || (pfj == pf && j < tid);
+      }
+      s_flat[tid] = off + r;
+    }
+    __syncthreads();
+  }
+  if (tid < T) {
+    const int f = s_flat[tid], u = s_id[tid];
+    parent_out[orow + f] = s_lp[tid] < 0 ? -1 : s_flat[s_lp[tid]];
+    tok_out[orow + f] = node_tok[row + u];
+    depth_out[orow + f] = dep;
+    node_out[orow + f] = u;
+  }
+}
+
+// Nodes after `levels` expansion levels and the frontier size after the last one (host).
+long long node_count(int levels, int k, int branch, int* front) {
+  long long n = 1, F = 1;
+  for (int l = 0; l < levels; ++l) {
+    n += F * branch;
+    F = F * branch < k ? F * branch : k;
+    if (n > (1LL << 30)) return -1;
+  }
+  if (front) *front = (int)F;
+  return n;
+}
+
+}  // namespace
+}  // namespace tv
+
+using namespace tv;
+
+extern "C" int eagle2_node_count(int depth, int k, int branch) {
+  if (depth < 0 || k < 1 || branch < 1) return -1;
+  return (int)node_count(depth, k, branch, nullptr);
+}
+
+extern "C" int eagle2_expand(const int32_t* root_tok, const int32_t* child_tok,
+                             const float* child_conf, int B, int level, int k, int branch,
+                             int32_t* node_tok, int32_t* node_parent, float* node_value,
+                             int n_max, int32_t* frontier, int32_t* status, void* stream) {
+  if (!child_tok || !child_conf || !node_tok || !node_parent || !node_value || !frontier ||
+      !status || B < 1 || level < 1 || k < 1 || branch < 1 || (long long)k * branch > kExpandMax)
+    return TV_ERR_INVALID_ARG;
+  if (level == 1 && !root_tok) return TV_ERR_INVALID_ARG;
+  int F = 1;  // parents of this level: the frontier after level - 1
+  const long long base = node_count(level - 1, k, branch, &F);
+  const long long prev_lo = level == 1 ? 0 : node_count(level - 2, k, branch, nullptr);
+  if (base < 0 || base + (long long)F * branch > n_max) return TV_ERR_INVALID_ARG;
+  const int threads = ceil_div(max(F * branch, k), 64) * 64;
+  hipLaunchKernelGGL(expand_kernel, dim3(B), dim3(threads), 0, (hipStream_t)stream, level,
+                     root_tok, child_tok, child_conf, k, branch, F, (int)prev_lo, (int)base, n_max,
+                     node_tok, node_parent, node_value, frontier, status);
+  return launch_status();
+}
+
+extern "C" int eagle2_rerank(const int32_t* node_tok, const int32_t* node_parent,
+                             const float* node_value, int n_nodes, int n_max, int B, int T,
+                             int32_t* parent_out, int32_t* tok_out, int32_t* depth_out,
+                             int32_t* node_out, int32_t* status, void* stream) {
+  if (!node_tok || !node_parent || !node_value || !parent_out || !tok_out || !depth_out ||
+      !node_out || !status || B < 1 || T < 1 || T > kMaxT || n_nodes < T ||
+      n_nodes > kRerankMaxNodes || n_max < n_nodes)
+    return TV_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(rerank_kernel, dim3(B), dim3(kRerankThreads), 0, (hipStream_t)stream,
+                     node_tok, node_parent, node_value, n_nodes, n_max, T, parent_out, tok_out,
+                     depth_out, node_out, status);
+  return launch_status();
+}

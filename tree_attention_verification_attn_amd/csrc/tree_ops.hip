@@ -264,6 +264,7 @@ extern "C" const char* tv_status_string(int code) {
     case TV_BAD_TOKEN: return "TV_BAD_TOKEN: a tried child's token is outside the vocabulary";
     case TV_SYNC_TIMEOUT:
       return "TV_SYNC_TIMEOUT: the workgroups of a sequence did not all meet; re-zero the workspace";
+    case TV_BAD_CONF: return "TV_BAD_CONF: a drafter confidence outside [0, 1] (used clamped)";
     default: return "unknown tree_verify status";
   }
 }
