@@ -73,6 +73,10 @@ def parse_args():
                         "stochastic (0 = automatic)")
     p.add_argument("--vocab", type=int, default=0,
                    help="vocabulary of the next-token distributions (0 = the workload's, 128256)")
+    p.add_argument("--construct", action="store_true",
+                   help="also time device-side EAGLE-2 tree construction (every eagle2_expand "
+                        "level, then eagle2_rerank) on the workload's expansion shape, and the "
+                        "oracle's construction on the host; reported under \"construction\"")
     p.add_argument("--rotate", type=int, default=0, help="input copies to rotate (0 = auto)")
     p.add_argument("--mode", choices=("graph", "eager"), default="graph",
                    help="replay each step as a captured HIP graph, or launch eagerly")
@@ -328,6 +332,106 @@ def stochastic_work(parent, draft, path, alen, V) -> tuple[float, int]:
                 sweeps += 1
                 nbytes += (8 if rej else 4) * V
     return sweeps / B, int(nbytes)
+
+
+def construction_bench(tv, torch, w, stream, steps: int, warmup: int) -> dict:
+    """Device-side EAGLE-2 tree construction on the workload's expansion shape: every
+    eagle2_expand level, then eagle2_rerank, for the whole batch.  Timed as HIP graphs of
+    constructions (whole job, inputs resident), per kernel by events between eager calls, and
+    the oracle's construction of the same inputs on the host."""
+    from synth import make_draft_levels
+
+    d = make_draft_levels(w.spec.name)
+    depth, B, k, branch = d.child_tok.shape
+    N = tv.eagle2_node_count(depth, k, branch)
+    T = w.T
+    table = tv.eagle2_new_table(B, N, k, "cuda")
+    tok = torch.from_numpy(d.child_tok).cuda()
+    conf = torch.from_numpy(d.child_conf).cuda()
+    root = torch.from_numpy(d.root_tok).cuda()
+    out = {name: torch.empty((B, T), dtype=torch.int32, device="cuda")
+           for name in ("parent", "tok", "depth", "node")}
+
+    def expand(lvl, st):
+        tv.eagle2_expand(table, lvl, tok[lvl - 1], conf[lvl - 1],
+                         root_tok=root if lvl == 1 else None, stream=st)
+
+    def build(st):
+        for lvl in range(1, depth + 1):
+            expand(lvl, st)
+        tv.eagle2_rerank(table, N, T, out=out, stream=st)
+
+    reps = 8
+    with torch.cuda.stream(stream):
+        build(stream)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for _ in range(reps):
+                build(torch.cuda.current_stream())
+        for _ in range(max(1, warmup // reps)):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_graphs = max(1, steps // reps)
+        stream.synchronize()
+        e0.record(stream)
+        for _ in range(n_graphs):
+            g.replay()
+        e1.record(stream)
+        e1.synchronize()
+    t_build = e0.elapsed_time(e1) * 1e-3 / (n_graphs * reps)
+
+    n_prof = 100
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(depth + 2)] for _ in range(n_prof)]
+    for row in ev:
+        for e in row:
+            e.record(stream)
+    stream.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(n_prof):
+            ev[i][0].record(stream)
+            for lvl in range(1, depth + 1):
+                expand(lvl, stream)
+                ev[i][lvl].record(stream)
+            tv.eagle2_rerank(table, N, T, out=out, stream=stream)
+            ev[i][depth + 1].record(stream)
+        stream.synchronize()
+    lv = [float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n_prof)])) * 1e3
+          for j in range(depth + 1)]
+    status = table["status"].cpu().numpy()
+
+    # algorithmic bytes of one construction (the whole batch)
+    byts, F = 0, 1
+    for _ in range(depth):
+        byts += B * (F * branch * (4 + 4 + 12) + 2 * F * 4 + k * 4)
+        F = min(k, F * branch)
+    byts += B * (N * 8 + T * 8 + T * 16)
+
+    from oracle import oracle as O  # the CPU baseline leg
+
+    O.eagle2_build(d.root_tok, d.child_tok, d.child_conf, T)
+    n_cpu, t0 = 0, time.perf_counter()
+    while n_cpu < 3 or time.perf_counter() - t0 < 2.0:
+        O.eagle2_build(d.root_tok, d.child_tok, d.child_conf, T)
+        n_cpu += 1
+    t_cpu = (time.perf_counter() - t0) / n_cpu
+    return {
+        "levels": depth, "topk": k, "branch": branch, "nodes": N, "T": T, "B": B,
+        "construction_us": t_build * 1e6,
+        "trees_per_s": B / t_build,
+        "expand_us_by_level": lv[:depth],
+        "rerank_us": lv[depth],
+        "algorithmic_bytes": byts,
+        "achieved_gbps": byts / t_build / 1e9,
+        "status_nonzero": int((status != 0).sum()),
+        "cpu_baseline": {"construction_us": t_cpu * 1e6, "trees_per_s": B / t_cpu, "cores": 1,
+                         "kind": "oracle",
+                         "sample": f"the whole batch's construction, {n_cpu} runs"},
+        "note": ("construction_us: graphs of 8 constructions replayed back to back (one "
+                 "construction = every expand level and the rerank for the whole batch); the "
+                 "per-kernel times come from events between eager calls, launch latency "
+                 "included; latency-bound (a few KB per sequence per level)"),
+    }
 
 
 def cpu_baseline(w, kv_bytes: int, target_s: float) -> dict:
@@ -654,6 +758,11 @@ def main() -> int:
                      "draw)"),
         }
 
+    construction = None
+    if args.construct:
+        print("[bench] timing EAGLE-2 tree construction", file=sys.stderr, flush=True)
+        construction = construction_bench(tv, torch, w, stream, args.steps, args.warmup)
+
     alen = sets[0].t["alen"].cpu().numpy()
     status = sets[0].t["status"].cpu().numpy()
     if (status & ~0).any():
@@ -711,6 +820,7 @@ def main() -> int:
                                else {args.api: ms_per_step}),
         "paged": paged_breakdown,
         "stochastic": stoch_breakdown,
+        "construction": construction,
         "hbm_frac": value / HBM_PEAK_GBS,
         "attn_kv_gbps": kv_bytes / t_attn / 1e9,
         "attn_hbm_frac": kv_bytes / t_attn / 1e9 / HBM_PEAK_GBS,

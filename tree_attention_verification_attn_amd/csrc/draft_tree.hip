@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kExpandMax) void expand_kernel(
     const float* __restrict__ child_conf, int k, int branch, int F, int prev_lo, int base,
     int n_max, int32_t* __restrict__ node_tok, int32_t* __restrict__ node_parent,
     float* __restrict__ node_value, int32_t* __restrict__ frontier, int32_t* __restrict__ status) {
-  __shared__ float s_val[kExpandMax];
+  __shared__ __attribute__((aligned(16))) float s_val[kExpandMax];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int n = F * branch;
   const int n_front = min(k, n);
@@ -70,6 +70,7 @@ __global__ __launch_bounds__(kExpandMax) void expand_kernel(
     node_value[row + base + tid] = v;
     s_val[tid] = v;
   }
+  if (tid >= n && tid < ((n + 3) & ~3)) s_val[tid] = -1.f;  // padding: below every value
   if (level == 1 && tid == 0) {
     node_tok[row] = root_tok[b];
     node_parent[row] = -1;
@@ -77,10 +78,17 @@ __global__ __launch_bounds__(kExpandMax) void expand_kernel(
   }
   __syncthreads();  // every parent entry of the frontier has been read
   if (tid < n) {
+    // four values per LDS read (every lane reads the same address), several reads in flight
+    const float4* sv = reinterpret_cast<const float4*>(s_val);
     int rank = 0;
-    for (int j = 0; j < n; ++j) {
-      const float w = s_val[j];
-      rank += (w > v) || (w == v && j < tid);
+#pragma unroll 4
+    for (int q = 0; q < (n + 3) >> 2; ++q) {
+      const float4 w = sv[q];
+      const int j = 4 * q;
+      rank += (w.x > v) || (w.x == v && j < tid);
+      rank += (w.y > v) || (w.y == v && j + 1 < tid);
+      rank += (w.z > v) || (w.z == v && j + 2 < tid);
+      rank += (w.w > v) || (w.w == v && j + 3 < tid);
     }
     if (rank < n_front) frontier[(size_t)b * k + rank] = base + tid;
   }
@@ -98,11 +106,14 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
   __shared__ int s_hist[256];
   __shared__ int s_sel[2];  // digit of the pass, count still to take at or below it
   __shared__ int s_cnt, s_dmax;
-  __shared__ int s_kept[kMaxT], s_id[kMaxT], s_lp[kMaxT], s_ptr[kMaxT], s_dep[kMaxT],
-      s_flat[kMaxT];
+  __shared__ __attribute__((aligned(16))) int s_kept[kMaxT];
+  __shared__ __attribute__((aligned(16))) int s_dep[kMaxT];
+  __shared__ __attribute__((aligned(16))) uint32_t s_k[kMaxT];  // sort keys of one level
+  __shared__ int s_id[kMaxT], s_lp[kMaxT], s_ptr[kMaxT], s_flat[kMaxT];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t row = (size_t)b * n_max;
   const size_t orow = (size_t)b * T;
+  const int T4 = (T + 3) & ~3;  // lists padded to whole 16-byte reads
 
   for (int i = tid; i < n; i += kRerankThreads)
     s_key[i] = __float_as_uint(rank_value(node_value[row + i]));
@@ -183,11 +194,20 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
       const int slot = atomicAdd(&s_cnt, 1);
       if (slot < kMaxT) s_kept[slot] = i;
     }
+  if (tid >= T && tid < T4) {
+    s_kept[tid] = 0x7fffffff;  // padding: after every id, deeper than every node
+    s_dep[tid] = 0x7fffffff;
+  }
   __syncthreads();
   if (tid < T) {
     const int u = s_kept[tid];
+    const int4* sk = reinterpret_cast<const int4*>(s_kept);
     int r = 0;
-    for (int j = 0; j < T; ++j) r += s_kept[j] < u;
+#pragma unroll 4
+    for (int q = 0; q < T4 >> 2; ++q) {
+      const int4 w = sk[q];
+      r += (w.x < u) + (w.y < u) + (w.z < u) + (w.w < u);
+    }
     s_id[r] = u;
   }
   __syncthreads();
@@ -225,24 +245,38 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
     }
   }
   __syncthreads();
-  int dep = 0, off = 0;
+  int dep = 0, off = 0;  // off: kept nodes shallower than this one
   if (tid < T) {
     dep = s_dep[tid];
     atomicMax(&s_dmax, dep);
-    for (int j = 0; j < T; ++j) off += s_dep[j] < dep;
+    const int4* sd = reinterpret_cast<const int4*>(s_dep);
+#pragma unroll 4
+    for (int q = 0; q < T4 >> 2; ++q) {
+      const int4 w = sd[q];
+      off += (w.x < dep) + (w.y < dep) + (w.z < dep) + (w.w < dep);
+    }
   }
   __syncthreads();
   const int dmax = s_dmax;
 
   // ---- flatten one level at a time: by the parent's flattened index, then by id --------------
+  // A node of level d sorts by the key (parent's flattened index << 16 | position in id order);
+  // the other levels' entries hold the largest key.
   for (int d = 0; d <= dmax; ++d) {
+    if (tid < T4) {
+      uint32_t key = 0xffffffffu;
+      if (tid < T && dep == d) key = ((uint32_t)(d == 0 ? 0 : s_flat[s_lp[tid]]) << 16) | tid;
+      s_k[tid] = key;
+    }
+    __syncthreads();
     if (tid < T && dep == d) {
-      const int pf = d == 0 ? -1 : s_flat[s_lp[tid]];
+      const uint32_t mine = s_k[tid];
+      const uint4* sk = reinterpret_cast<const uint4*>(s_k);
       int r = 0;
-      for (int j = 0; j < T; ++j) {
-        if (j == tid || s_dep[j] != d) continue;
-        const int pfj = d == 0 ? -1 : s_flat[s_lp[j]];
-        r += pfj < pf || (pfj == pf && j < tid);
+#pragma unroll 4
+      for (int q = 0; q < T4 >> 2; ++q) {
+        const uint4 w = sk[q];
+        r += (w.x < mine) + (w.y < mine) + (w.z < mine) + (w.w < mine);
       }
       s_flat[tid] = off + r;
     }
