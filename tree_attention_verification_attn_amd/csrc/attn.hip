@@ -78,6 +78,7 @@ struct AttnArgs {
   const int32_t* tree_slot;
   int max_pages, log2P, num_slots;
   int B, T, Hq, Hkv, G, Lmax, W, GT, RB, S, chunk_tiles;
+  int lpt;         // dispatch the (sequence, chunk) pairs longest first (see lpt_item)
   float c;         // scale * log2(e)
 };
 
@@ -181,6 +182,58 @@ __device__ inline int xcd_remap(int bid, int n) {
   const int per = n / 8, rem = n % 8;
   const int xcd = bid % 8, slot = bid / 8;
   return xcd * per + min(xcd, rem) + slot;
+}
+
+// Work order for sequences of different lengths, longest processing time first.  Every
+// workgroup ranks the B*S (sequence, chunk) pairs by their tile count, largest first (ties by
+// index), from cache_len, in LDS scratch (P <= kLptMaxPairs).  Unit U = rank * Hkv + kvh.
+// Hardware ids are dealt to the 8 XCDs in turn and dispatched in order, so units go out in
+// groups of 8, one per XCD, and the RB row blocks of a unit (which read the same K/V tiles)
+// follow each other on the same XCD: every XCD gets a longest-first share of the work.
+constexpr int kLptMaxPairs = 256;
+
+__device__ inline void lpt_item(const AttnArgs& a, int* scratch, int& b, int& s, int& kvh,
+                                int& rb) {
+  const int P = a.B * a.S;
+  const int P4 = (P + 3) & ~3;
+  const int tid = threadIdx.x;
+  const int tree_tiles = ceil_div(a.T, kKT);
+  int* sz = scratch;        // [P4] tiles of each pair; padding -1 ranks after every pair
+  int* ord = scratch + P4;  // [P] pair of each rank
+  for (int i = tid; i < P4; i += kThreads) {
+    int v = -1;
+    if (i < P) {
+      const int bi = i / a.S, si = i - bi * a.S;
+      const int L = min(max(a.cache_len[bi], 0), a.Lmax);
+      v = min(max(tree_tiles + ceil_div(L, kKT) - si * a.chunk_tiles, 0), a.chunk_tiles);
+    }
+    sz[i] = v;
+  }
+  __syncthreads();
+  for (int i = tid; i < P; i += kThreads) {
+    const int me = sz[i];
+    const int4* s4 = reinterpret_cast<const int4*>(sz);
+    int r = 0;
+    for (int q = 0; q < P4 >> 2; ++q) {
+      const int4 o = s4[q];
+      const int j = 4 * q;
+      r += (o.x > me || (o.x == me && j < i)) + (o.y > me || (o.y == me && j + 1 < i)) +
+           (o.z > me || (o.z == me && j + 2 < i)) + (o.w > me || (o.w == me && j + 3 < i));
+    }
+    ord[r] = i;
+  }
+  __syncthreads();
+  const int n_units = P * a.Hkv;
+  const int per = 8 * a.RB;
+  const int h = blockIdx.x, g = h / per, w = h - g * per;
+  const int m = min(8, n_units - g * 8);  // units in this group (fewer in the last one)
+  const int U = g * 8 + w % m;
+  rb = w / m;
+  kvh = U % a.Hkv;
+  const int pair = ord[U / a.Hkv];
+  b = pair / a.S;
+  s = pair - b * a.S;
+  __syncthreads();  // the scratch is the K/V ring, which the first tile loads overwrite
 }
 
 // Score block j = 32 keys: tile j/2, half j%2.  P of a block: bf16 operands or fp32 values.
@@ -289,12 +342,17 @@ void attn_main(AttnArgs a) {
   constexpr int kDPW = Lay::kDmaPerWave;
   __shared__ __attribute__((aligned(1024))) char smem[kNS * Lay::kStage];
 
-  const int n_items = a.B * a.Hkv * a.S * a.RB;
-  const int item = xcd_remap(blockIdx.x, n_items);
-  const int rb = item % a.RB;
-  const int s = (item / a.RB) % a.S;
-  const int kvh = (item / (a.RB * a.S)) % a.Hkv;
-  const int b = item / (a.RB * a.S * a.Hkv);
+  int rb, s, kvh, b;
+  if (a.lpt) {
+    lpt_item(a, reinterpret_cast<int*>(smem), b, s, kvh, rb);
+  } else {
+    const int n_items = a.B * a.Hkv * a.S * a.RB;
+    const int item = xcd_remap(blockIdx.x, n_items);
+    rb = item % a.RB;
+    s = (item / a.RB) % a.S;
+    kvh = (item / (a.RB * a.S)) % a.Hkv;
+    b = item / (a.RB * a.S * a.Hkv);
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1158,6 +1216,8 @@ static int prepare_attn(AttnArgs& a, Plan& p, const void* q, const void* k_cache
   a.RB = p.RB;
   a.S = p.S;
   a.chunk_tiles = p.chunk_tiles;
+  // lengths differ between sequences only when there are several
+  a.lpt = B > 1 && (long long)B * p.S <= kLptMaxPairs;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
   a.c = sc * kLog2e;
   const int elem = dtype == TV_BF16 ? 2 : 4;
