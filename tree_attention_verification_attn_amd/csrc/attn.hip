@@ -1079,11 +1079,13 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int elem_bytes, i
   if (split_keys > 0) {
     chunk_tiles = ceil_div(split_keys, kKT);
   } else {
-    // One workgroup per compute unit: aim for two rounds, with chunks of at least 4 tiles.
+    // One workgroup per compute unit: aim for two rounds, with chunks of at least 3 tiles
+    // (shorter chunks spend more on filling the load pipeline and writing partials than they
+    // gain in parallelism).
     const long long units = (long long)B * Hkv * p.RB;
     const long long want = 2LL * device_cu_count();
     const int S = (int)std::min<long long>(std::max<long long>(1, ceil_div_ll(want, units)),
-                                           std::max(1, ceil_div(tiles, 4)));
+                                           std::max(1, ceil_div(tiles, 3)));
     chunk_tiles = ceil_div(tiles, S);
   }
   p.chunk_tiles = chunk_tiles;
