@@ -76,6 +76,14 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_eagle2_rerank.restype = None
     lib.oracle_eagle2_build.argtypes = [P, P, P, i, i, i, i, i, P, P, P, i, P, P, P, P, P, P]
     lib.oracle_eagle2_build.restype = i
+    lib.oracle_lm_project.argtypes = [P, P, i, i, i, P]
+    lib.oracle_lm_project.restype = None
+    lib.oracle_lm_screen.argtypes = [P, P, P, i, i, i, i, i, P, P]
+    lib.oracle_lm_screen.restype = None
+    lib.oracle_lm_rescore.argtypes = [P, P, P, i, i, i, i, P, P]
+    lib.oracle_lm_rescore.restype = None
+    lib.oracle_lm_topk.argtypes = [P, P, i, i, i, i, P, P]
+    lib.oracle_lm_topk.restype = None
     return lib
 
 
@@ -321,3 +329,75 @@ def eagle2_rerank(node_tok, node_parent, node_value, T, lib=None) -> dict:
                              _p(r["parent"]), _p(r["tok"]), _p(r["depth"]), _p(r["node"]),
                              _p(r["status"]))
     return r
+
+
+def _bf16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError(f"expected bfloat16 bit patterns (uint16), got {a.dtype}")
+    return a
+
+
+def lm_project(h, Bm, lib=None) -> np.ndarray:
+    """u [M, r] float32 = B h, each entry by the fixed-order float32 dot product (dot_seg64).
+    h [M, d] and B [r, d] are bfloat16 bit patterns; d a multiple of 64."""
+    lib = lib or load()
+    h, Bm = _bf16(h), _bf16(Bm)
+    M, d = h.shape
+    r = Bm.shape[0]
+    assert Bm.shape[1] == d and d % 64 == 0
+    u = np.empty((M, r), np.float32)
+    lib.oracle_lm_project(_p(h), _p(Bm), M, r, d, _p(u))
+    return u
+
+
+def lm_screen(A, u, row_token, tile, k_tile, lib=None) -> tuple[np.ndarray, np.ndarray]:
+    """Local top-k screening: (cand [M, n_tiles*k_tile] int32 tokens, cand_score float32)."""
+    lib = lib or load()
+    A = _bf16(A)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    row_token = _i32(row_token)
+    n, r = A.shape
+    M = u.shape[0]
+    assert u.shape[1] == r and row_token.shape == (n,)
+    C = (n + tile - 1) // tile * k_tile
+    cand = np.empty((M, C), np.int32)
+    score = np.empty((M, C), np.float32)
+    lib.oracle_lm_screen(_p(A), _p(u), _p(row_token), M, r, n, int(tile), int(k_tile), _p(cand),
+                         _p(score))
+    return cand, score
+
+
+def lm_rescore(W, h, cand, lib=None) -> tuple[np.ndarray, np.ndarray]:
+    """Exact candidate logits [M, C] float32 (dot_seg64 of W's rows and h) and status [M]."""
+    lib = lib or load()
+    W, h = _bf16(W), _bf16(h)
+    cand = _i32(cand)
+    V, d = W.shape
+    M, C = cand.shape
+    logits = np.empty((M, C), np.float32)
+    status = np.zeros(M, np.int32)
+    lib.oracle_lm_rescore(_p(W), _p(h), _p(cand), M, C, d, V, _p(logits), _p(status))
+    return logits, status
+
+
+def lm_topk(logits, cand, K, V, lib=None) -> tuple[np.ndarray, np.ndarray]:
+    """The K best valid candidates per hidden state (tokens [M, K] int32) and their softmax
+    confidences over the candidates ([M, K] float64)."""
+    lib = lib or load()
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    cand = _i32(cand)
+    M, C = cand.shape
+    tok = np.empty((M, K), np.int32)
+    conf = np.empty((M, K), np.float64)
+    lib.oracle_lm_topk(_p(logits), _p(cand), M, C, int(K), int(V), _p(tok), _p(conf))
+    return tok, conf
+
+
+def lm_head_two_stage(h, A, Bm, W, row_token, tile, k_tile, K, lib=None) -> dict:
+    """Both stages and the children: dict of u, cand, cand_score, logits, status, tok, conf."""
+    u = lm_project(h, Bm, lib=lib)
+    cand, score = lm_screen(A, u, row_token, tile, k_tile, lib=lib)
+    logits, status = lm_rescore(W, h, cand, lib=lib)
+    tok, conf = lm_topk(logits, cand, K, W.shape[0], lib=lib)
+    return dict(u=u, cand=cand, cand_score=score, logits=logits, status=status, tok=tok, conf=conf)

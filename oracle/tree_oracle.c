@@ -42,6 +42,11 @@
  *                  reranked and the best T kept and flattened in level order.  Which node
  *                  outranks which is decided on float32 products, the precision of the GPU
  *                  kernels, since these decisions choose integers (node ids).
+ *   drafter LM     (jialefu.github.io, EAGLE-4 efficient LM head) two stages: a low-rank head
+ *   head           scores the vocabulary and a local top-k per tile of shuffled rows keeps
+ *                  candidates; the full head's rows recompute their logits exactly; the
+ *                  drafter's children are the best of them.  Float32 in the kernels' stated
+ *                  summation order, since the values choose integers (candidate tokens).
  *
  * Floating inputs are either float32 (elem_bits = 32) or raw bfloat16 bit patterns
  * (elem_bits = 16), which are widened exactly.
@@ -731,4 +736,161 @@ int oracle_eagle2_build(const int32_t* root_tok, const int32_t* child_tok,
   oracle_eagle2_rerank(node_tok, node_parent, node_value, n_nodes, n_max, B, T, parent_out,
                        tok_out, depth_out, node_out, status);
   return n_nodes;
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* Two-stage drafter LM head (jialefu.github.io, "EAGLE-4: Notes on the Efficient LM Head")    */
+/* ------------------------------------------------------------------------------------------ */
+/*
+ * Stage one scores the whole vocabulary with a low-rank head: u = B h, then A u, and keeps
+ * candidates by a local top-k inside each tile of vocabulary rows (rows shuffled beforehand,
+ * row_token[row] naming the token of each row).  Stage two recomputes the candidates' logits
+ * exactly from the full head's rows, W[token] . h.  The drafter then takes its top children
+ * and their confidences (a softmax over the candidates).  Which candidates are kept and which
+ * children chosen is decided by float32 values, so these are computed in the float32
+ * arithmetic, and the summation order, that the kernels use:
+ *   dot_seg64   64 segments of d/64 consecutive elements, each a chain of fused multiply-adds in
+ *               index order from 0; then the segment sums are combined pairwise, sum j with sum
+ *               j ^ 32, then j ^ 16, ..., j ^ 1; the result is that of segment 0.
+ *   screening   one chain of fused multiply-adds over the rank index, in order, from 0.
+ * Values are ranked by the float's order with -0 taken as +0 (an unsigned key of the bits);
+ * equal values go to the smaller row (screening) or the smaller token (final selection).
+ */
+
+static float bf16f(uint16_t b) {
+  union {
+    uint32_t u;
+    float f;
+  } x;
+  x.u = (uint32_t)b << 16;
+  return x.f;
+}
+
+/* Unsigned key in the order of the float value (-0 as +0; NaN above +inf or below -inf). */
+static uint32_t float_key(float v) {
+  union {
+    float f;
+    uint32_t u;
+  } x;
+  x.f = v + 0.0f;
+  return (x.u & 0x80000000u) ? ~x.u : (x.u | 0x80000000u);
+}
+
+static float dot_seg64(const uint16_t* x, const uint16_t* y, int d) {
+  float v[64], w[64];
+  const int seg = d / 64;
+  for (int j = 0; j < 64; ++j) {
+    float acc = 0.0f;
+    for (int i = 0; i < seg; ++i) acc = fmaf(bf16f(x[j * seg + i]), bf16f(y[j * seg + i]), acc);
+    v[j] = acc;
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    for (int j = 0; j < 64; ++j) w[j] = v[j] + v[j ^ off];
+    for (int j = 0; j < 64; ++j) v[j] = w[j];
+  }
+  return v[0];
+}
+
+/* u[m, i] = B[i, :] . h[m, :] (dot_seg64); h [M, d], B [r, d] bfloat16 bits; d % 64 == 0. */
+void oracle_lm_project(const uint16_t* h, const uint16_t* Bm, int M, int r, int d, float* u) {
+  for (int m = 0; m < M; ++m)
+    for (int i = 0; i < r; ++i)
+      u[(size_t)m * r + i] = dot_seg64(Bm + (size_t)i * d, h + (size_t)m * d, d);
+}
+
+/* Screening: for hidden state m and tile t of `tile` consecutive rows of A [n, r] (bfloat16),
+ * score(row) = the fused multiply-add chain of A[row, i] * u[m, i] over i = 0 .. r-1; the
+ * k_tile best rows of the tile (by score, then smaller row) become candidates
+ * cand[m, t * k_tile + j] = row_token[row], best first, with their scores in cand_score; a
+ * tile with fewer rows pads with token -1 and score -inf. */
+void oracle_lm_screen(const uint16_t* A, const float* u, const int32_t* row_token, int M, int r,
+                      int n, int tile, int k_tile, int32_t* cand, float* cand_score) {
+  const int n_tiles = (n + tile - 1) / tile;
+  const int C = n_tiles * k_tile;
+  float* s = (float*)malloc(sizeof(float) * (size_t)tile);
+  char* taken = (char*)malloc((size_t)tile);
+  for (int m = 0; m < M; ++m) {
+    const float* um = u + (size_t)m * r;
+    for (int t = 0; t < n_tiles; ++t) {
+      const int r0 = t * tile, rows = n - r0 < tile ? n - r0 : tile;
+      for (int q = 0; q < rows; ++q) {
+        const uint16_t* a = A + (size_t)(r0 + q) * r;
+        float acc = 0.0f;
+        for (int i = 0; i < r; ++i) acc = fmaf(bf16f(a[i]), um[i], acc);
+        s[q] = acc;
+        taken[q] = 0;
+      }
+      for (int j = 0; j < k_tile; ++j) {
+        int best = -1;
+        for (int q = 0; q < rows; ++q)
+          if (!taken[q] && (best < 0 || float_key(s[q]) > float_key(s[best]))) best = q;
+        const size_t o = (size_t)m * C + (size_t)t * k_tile + j;
+        if (best < 0) {
+          cand[o] = -1;
+          cand_score[o] = -INFINITY;
+        } else {
+          taken[best] = 1;
+          cand[o] = row_token[r0 + best];
+          cand_score[o] = s[best];
+        }
+      }
+    }
+  }
+  free(s);
+  free(taken);
+}
+
+/* Exact logits of the candidates: logits[m, c] = W[cand[m, c], :] . h[m, :] (dot_seg64), W
+ * [V, d] bfloat16 in token order.  A candidate outside [0, V) gets -inf and sets
+ * ORC_BAD_TOKEN in status[m]. */
+void oracle_lm_rescore(const uint16_t* W, const uint16_t* h, const int32_t* cand, int M, int C,
+                       int d, int V, float* logits, int32_t* status) {
+  for (int m = 0; m < M; ++m)
+    for (int c = 0; c < C; ++c) {
+      const int tok = cand[(size_t)m * C + c];
+      if (tok < 0 || tok >= V) {
+        logits[(size_t)m * C + c] = -INFINITY;
+        if (tok != -1) status[m] |= ORC_BAD_TOKEN;
+        continue;
+      }
+      logits[(size_t)m * C + c] = dot_seg64(W + (size_t)tok * d, h + (size_t)m * d, d);
+    }
+}
+
+/* The drafter's children: the K best valid candidates of hidden state m (by exact logit, then
+ * smaller token), best first, and their confidences, the softmax of the logits over all valid
+ * candidates of m (fp64).  Fewer than K valid candidates pad with token -1, confidence 0. */
+void oracle_lm_topk(const float* logits, const int32_t* cand, int M, int C, int K, int V,
+                    int32_t* out_tok, double* out_conf) {
+  char* taken = (char*)malloc((size_t)C);
+  for (int m = 0; m < M; ++m) {
+    const float* l = logits + (size_t)m * C;
+    const int32_t* cm = cand + (size_t)m * C;
+    double mx = -INFINITY;
+    for (int c = 0; c < C; ++c) {
+      taken[c] = !(cm[c] >= 0 && cm[c] < V);
+      if (!taken[c] && (double)l[c] > mx) mx = (double)l[c];
+    }
+    double z = 0.0;
+    for (int c = 0; c < C; ++c)
+      if (!taken[c]) z += exp((double)l[c] - mx);
+    for (int j = 0; j < K; ++j) {
+      int best = -1;
+      for (int c = 0; c < C; ++c) {
+        if (taken[c]) continue;
+        if (best < 0 || float_key(l[c]) > float_key(l[best]) ||
+            (float_key(l[c]) == float_key(l[best]) && cm[c] < cm[best]))
+          best = c;
+      }
+      if (best < 0) {
+        out_tok[(size_t)m * K + j] = -1;
+        out_conf[(size_t)m * K + j] = 0.0;
+      } else {
+        taken[best] = 1;
+        out_tok[(size_t)m * K + j] = cm[best];
+        out_conf[(size_t)m * K + j] = exp((double)l[best] - mx) / z;
+      }
+    }
+  }
+  free(taken);
 }

@@ -32,7 +32,7 @@ import os
 import numpy as np
 
 from oracle import oracle as O
-from synth import f32_to_bf16_bits, random_parent, worked_tree_parent
+from synth import bf16_bits_to_f32, f32_to_bf16_bits, random_parent, worked_tree_parent
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -1247,6 +1247,164 @@ def pin_eagle2_rerank_tables(lib):
         assert (rb["depth"][0] == 0).all() and (rb["node"][0] == -1).all()
         assert list(rb["node"][1]) == kept
 
+
+# ----------------------------------------------------------------------------------------------
+# two-stage drafter LM head (jialefu.github.io, "EAGLE-4: Notes on the Efficient LM Head")
+# ----------------------------------------------------------------------------------------------
+def _bits(x) -> np.ndarray:
+    return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def pin_lm_summation_order(lib):
+    """Hand-derived float32 results (tests/golden/lm_head_order.txt) that change under any
+    other summation order."""
+    with open(os.path.join(GOLDEN, "lm_head_order.txt"), encoding="utf-8") as f:
+        for line in f:
+            if not line.strip() or line.startswith("#"):
+                continue
+            f_ = [x.strip() for x in line.split("|")]
+            if f_[0] == "dot":
+                d = int(f_[1])
+                x = np.zeros(d, np.float32)
+                y = np.zeros(d, np.float32)
+                for ent in f_[2].split():
+                    i, a, b_ = ent.split(":")
+                    x[int(i)], y[int(i)] = float(a), float(b_)
+                u = O.lm_project(_bits(y)[None], _bits(x)[None], lib=lib)
+                assert u[0, 0] == np.float32(f_[3]), (u[0, 0], f_[3])
+                # the same order in stage two: W row x, hidden state y
+                logits, st = O.lm_rescore(_bits(x)[None], _bits(y)[None], np.zeros((1, 1), np.int32),
+                                          lib=lib)
+                assert logits[0, 0] == np.float32(f_[3]) and st[0] == 0
+            elif f_[0] == "screen":
+                a = np.array([float(v) for v in f_[2].split()], np.float32)
+                uu = np.array([[float(v) for v in f_[3].split()]], np.float32)
+                cand, score = O.lm_screen(_bits(a)[None], uu, np.array([7], np.int32), 1, 1, lib=lib)
+                assert cand[0, 0] == 7 and score[0, 0] == np.float32(f_[4]), score
+
+
+def _int_lm_case(rng, M, d, r, n, lo=-3, hi=4):
+    """Small-integer bfloat16 inputs: every product and partial sum is an integer below 2^24,
+    so float32 arithmetic in any order is exact and equals numpy's int64 results."""
+    h = rng.integers(lo, hi, size=(M, d))
+    Bm = rng.integers(lo, hi, size=(r, d))
+    A = rng.integers(lo, hi, size=(n, r))
+    W = rng.integers(lo, hi, size=(n, d))
+    perm = rng.permutation(n).astype(np.int32)
+    return h, Bm, A, W, perm
+
+
+def _lexsort_best(vals, keys2, k):
+    """Indices of the k largest vals, ties to the smaller keys2 (numpy lexsort)."""
+    order = np.lexsort((keys2, -np.asarray(vals, dtype=np.float64)))
+    return order[:k]
+
+
+def pin_lm_integer_bruteforce(lib):
+    """Exact small-integer cases against numpy: u = B h, per-tile screening (top k_tile rows of
+    each tile, ties to the smaller row, mapped through the row permutation), exact logits of the
+    candidates, the K best (ties to the smaller token) and softmax confidences over the
+    candidates."""
+    from scipy.special import softmax
+
+    rng = np.random.default_rng(31)
+    for trial in range(25):
+        M, d, r = int(rng.integers(1, 4)), 64 * int(rng.integers(1, 3)), int(rng.integers(1, 9))
+        n, tile, k_tile = int(rng.integers(5, 60)), int(rng.integers(2, 12)), int(rng.integers(1, 4))
+        h, Bm, A, W, perm = _int_lm_case(rng, M, d, r, n)
+        K = int(rng.integers(1, 6))
+        res = O.lm_head_two_stage(_bits(h), _bits(A[perm]), _bits(Bm), _bits(W), perm, tile, k_tile,
+                                  K, lib=lib)
+        u = h @ Bm.T  # [M, r], exact
+        assert np.array_equal(res["u"], u.astype(np.float32))
+        As = A[perm]  # row q of the shuffled head is token perm[q]
+        scores = u @ As.T  # [M, n], exact
+        n_tiles = -(-n // tile)
+        for m in range(M):
+            want = []
+            for t in range(n_tiles):
+                rows = np.arange(t * tile, min(n, (t + 1) * tile))
+                best = rows[_lexsort_best(scores[m, rows], rows, k_tile)]
+                want += [int(perm[q]) for q in best] + [-1] * (k_tile - len(best))
+            assert list(res["cand"][m]) == want, (trial, m)
+            valid = res["cand"][m] >= 0
+            exact = (W[np.maximum(res["cand"][m], 0)] @ h[m]).astype(np.float64)
+            assert np.array_equal(res["logits"][m][valid], exact[valid].astype(np.float32))
+            assert np.isneginf(res["logits"][m][~valid]).all()
+            vc = res["cand"][m][valid]
+            top = vc[_lexsort_best(exact[valid], vc, K)]
+            assert list(res["tok"][m][: len(top)]) == [int(x) for x in top]
+            assert (res["tok"][m][len(top):] == -1).all()
+            p = softmax(exact[valid])
+            conf = {int(t): float(p[i]) for i, t in enumerate(vc)}
+            for j, t in enumerate(res["tok"][m][: len(top)]):
+                assert abs(res["conf"][m, j] - conf[int(t)]) <= 1e-12
+
+
+def pin_lm_error_bound(lib):
+    """Normal-valued inputs: every float32 dot product lies within the rounding bound of its
+    exact value, (terms + 6) * 2^-24 * sum |x_i y_i| for the segmented dot products and
+    r * 2^-24 * sum |a_i u_i| for the screening chain."""
+    rng = np.random.default_rng(32)
+    M, d, r, n = 3, 256, 48, 40
+    h = _bits(rng.standard_normal((M, d)))
+    Bm = _bits(rng.standard_normal((r, d)))
+    A = _bits(rng.standard_normal((n, r)))
+    W = _bits(rng.standard_normal((n, d)))
+    f = lambda b: bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
+    u = O.lm_project(h, Bm, lib=lib)
+    ex, mag = f(h) @ f(Bm).T, np.abs(f(h)) @ np.abs(f(Bm)).T
+    assert (np.abs(u - ex) <= (d // 64 + 7) * 2.0 ** -24 * mag + 1e-30).all()
+    perm = np.arange(n, dtype=np.int32)
+    cand, score = O.lm_screen(A, u, perm, n, n, lib=lib)  # one tile keeps every row
+    ex_s = u.astype(np.float64) @ f(A).T
+    mag_s = np.abs(u.astype(np.float64)) @ np.abs(f(A)).T
+    for m in range(M):
+        got = score[m, np.argsort(cand[m])]
+        assert (np.abs(got - ex_s[m]) <= (r + 1) * 2.0 ** -24 * mag_s[m] + 1e-30).all()
+    logits, _ = O.lm_rescore(W, h, np.tile(np.arange(n, dtype=np.int32), (M, 1)), lib=lib)
+    ex_l, mag_l = f(h) @ f(W).T, np.abs(f(h)) @ np.abs(f(W)).T
+    assert (np.abs(logits - ex_l) <= (d // 64 + 7) * 2.0 ** -24 * mag_l + 1e-30).all()
+
+
+def pin_lm_exact_screen_keeps_global_best(lib):
+    """A screening head equal to the full head (A = W, B = identity) with k_tile >= K keeps
+    every token of the global top K, so the children equal the full vocabulary's best K
+    (numpy over all of W h, ties to the smaller token), whatever the row shuffle."""
+    rng = np.random.default_rng(33)
+    for trial in range(10):
+        M, d, n, K = 2, 64, int(rng.integers(20, 90)), int(rng.integers(1, 5))
+        tile, k_tile = int(rng.integers(3, 10)), K + int(rng.integers(0, 3))
+        h, _, _, W, perm = _int_lm_case(rng, M, d, 1, n, lo=-6, hi=7)
+        eye = np.eye(d, dtype=np.int64)
+        res = O.lm_head_two_stage(_bits(h), _bits(W[perm]), _bits(eye), _bits(W), perm, tile,
+                                  k_tile, K, lib=lib)
+        full = W @ h.T  # [n, M]
+        for m in range(M):
+            best = _lexsort_best(full[:, m], np.arange(n), K)
+            assert list(res["tok"][m]) == [int(x) for x in best], (trial, m)
+
+
+def pin_lm_padding_and_bad_tokens(lib):
+    """A last tile shorter than k_tile pads with token -1 (score -inf); -1 candidates get -inf
+    logits without a flag, out-of-range ones get -inf and ORC_BAD_TOKEN; the children skip them
+    and pad with -1 / 0 when fewer than K valid candidates remain."""
+    rng = np.random.default_rng(34)
+    h, Bm, A, W, perm = _int_lm_case(rng, 2, 64, 4, 7)
+    u = O.lm_project(_bits(h), _bits(Bm), lib=lib)
+    cand, score = O.lm_screen(_bits(A), u, perm, 3, 2, lib=lib)  # tiles of 3, 3, 1 rows
+    assert cand.shape == (2, 6) and (cand[:, 5] == -1).all() and np.isneginf(score[:, 5]).all()
+    bad = cand.copy()
+    bad[0, 0] = 7      # outside the vocabulary
+    bad[1, 1] = -5
+    logits, st = O.lm_rescore(_bits(W), _bits(h), bad, lib=lib)
+    assert list(st) == [O.ORC_BAD_TOKEN, O.ORC_BAD_TOKEN]
+    assert np.isneginf(logits[0, [0, 5]]).all() and np.isneginf(logits[1, [1, 5]]).all()
+    tok, conf = O.lm_topk(logits, bad, 6, 7, lib=lib)
+    assert list(tok[0, 4:]) == [-1, -1] and list(conf[0, 4:]) == [0.0, 0.0]
+    assert set(tok[0, :4]) == set(int(x) for x in bad[0, 1:5])
+    assert abs(conf[0].sum() - 1.0) < 1e-12
+
 ALL_PINS = [
     pin_worked_tree_mask,
     pin_mask_closure_bruteforce,
@@ -1283,4 +1441,9 @@ ALL_PINS = [
     pin_eagle2_rerank_tables,
     pin_eagle2_batch_independent,
     pin_eagle2_bruteforce,
+    pin_lm_summation_order,
+    pin_lm_integer_bruteforce,
+    pin_lm_error_bound,
+    pin_lm_exact_screen_keeps_global_best,
+    pin_lm_padding_and_bad_tokens,
 ]

@@ -134,6 +134,31 @@ MUTANTS = {
                                "if (p < 0 || p >= i) valid = 0;"),
     # draft tree: flattened depth counted from one
     "e2_depth_from_one": ("        dout[f] = d;\n", "        dout[f] = d + 1;\n"),
+    # LM head: segment sums combined from the nearest pairs up instead of from j ^ 32 down
+    "lm_butterfly_reversed": ("for (int off = 32; off >= 1; off >>= 1) {\n    for (int j = 0; j < 64; ++j) w[j]",
+                              "for (int off = 1; off <= 32; off <<= 1) {\n    for (int j = 0; j < 64; ++j) w[j]"),
+    # LM head: each segment's chain run from its last element
+    "lm_segment_reversed": ("acc = fmaf(bf16f(x[j * seg + i]), bf16f(y[j * seg + i]), acc);",
+                            "acc = fmaf(bf16f(x[j * seg + seg - 1 - i]), bf16f(y[j * seg + seg - 1 - i]), acc);"),
+    # LM head: screening chain over the rank index in reverse
+    "lm_screen_reversed": ("for (int i = 0; i < r; ++i) acc = fmaf(bf16f(a[i]), um[i], acc);",
+                           "for (int i = r - 1; i >= 0; --i) acc = fmaf(bf16f(a[i]), um[i], acc);"),
+    # LM head: equal scores go to the larger row
+    "lm_screen_tie_larger": ("if (!taken[q] && (best < 0 || float_key(s[q]) > float_key(s[best]))) best = q;",
+                             "if (!taken[q] && (best < 0 || float_key(s[q]) >= float_key(s[best]))) best = q;"),
+    # LM head: candidates reported by row instead of token
+    "lm_cand_is_row": ("cand[o] = row_token[r0 + best];", "cand[o] = r0 + best;"),
+    # LM head: equal logits go to the larger token
+    "lm_topk_tie_larger": ("(float_key(l[c]) == float_key(l[best]) && cm[c] < cm[best]))",
+                           "(float_key(l[c]) == float_key(l[best]) && cm[c] > cm[best]))"),
+    # LM head: confidences normalised over the chosen children only
+    "lm_conf_over_chosen": ("out_conf[(size_t)m * K + j] = exp((double)l[best] - mx) / z;",
+                            "out_conf[(size_t)m * K + j] = exp((double)l[best] - mx) / (z > 0 ? 1.0 : z);"),
+    # LM head: the projection uses h's row for B's index
+    "lm_project_swapped": ("u[(size_t)m * r + i] = dot_seg64(Bm + (size_t)i * d, h + (size_t)m * d, d);",
+                           "u[(size_t)m * r + i] = dot_seg64(Bm + (size_t)(i % r) * d, h + (size_t)(i % M) * d, d);"),
+    # LM head: out-of-vocabulary candidates not reported
+    "lm_bad_token_silent": ("if (tok != -1) status[m] |= ORC_BAD_TOKEN;", ""),
 }
 
 
