@@ -380,6 +380,57 @@ int eagle2_rerank(const int32_t* node_tok, const int32_t* node_parent, const flo
                   int n_nodes, int n_max, int B, int T, int32_t* parent_out, int32_t* tok_out,
                   int32_t* depth_out, int32_t* node_out, int32_t* status, void* stream);
 
+/*
+ * Two-stage drafter LM head (jialefu.github.io, "EAGLE-4: Notes on the Efficient LM Head").
+ *
+ * Stage one scores the whole vocabulary with low-rank factors of the head, u = B h then A u,
+ * and keeps candidates by a local top-k inside each tile of vocabulary rows (the rows of A were
+ * shuffled before tiling; row_token names each row's token), so the approximate scores never
+ * go to memory.  Stage two gathers the candidates' rows of the full head W and recomputes their
+ * logits exactly.  The drafter's children are the K best candidates (their tokens and
+ * confidences feed eagle2_expand).  h, A, B and W are bfloat16 (16-bit words); results are
+ * float32.  Which candidates and children are chosen is decided by float32 values computed in
+ * a fixed order, so the results are bit-exact:
+ *   - dot products over d (u = B h and the exact logits): 64 segments of d/64 consecutive
+ *     elements, each a chain of fused multiply-adds in index order from 0, then the 64 segment
+ *     sums combined pairwise, segment j with j^32, then j^16, ..., j^1;
+ *   - screening scores A[row] . u[m]: one chain of fused multiply-adds over the rank index in
+ *     order from 0.
+ * Values rank by their float order with -0 as +0; equal values go to the smaller row of A
+ * (screening) or the smaller token (children).
+ */
+
+/* lm_head_project — u [M, r] fp32 = B [r, d] h [M, d] (rows of h are hidden states).
+ * Limits: 1 <= M <= 64, r >= 1, d a positive multiple of 512. */
+int lm_head_project(const void* h, const void* B, int M, int r, int d, float* u, void* stream);
+
+/* lm_head_screen — local top-k screening.  A [n, r] bfloat16 (rows in shuffled order),
+ * u [M, r] fp32 from lm_head_project, row_token [n] int32.  Tile t holds rows t*tile ..
+ * t*tile + tile - 1 (the last one may be shorter); its k_tile best rows for hidden state m
+ * become cand[m, t*k_tile + j] = row_token[row] (best first) with cand_score = the row's
+ * score; a tile with fewer than k_tile rows pads with token -1 and score -inf.
+ * C = ceil(n / tile) * k_tile candidates per hidden state.
+ * Limits: 1 <= M <= 64, r a positive multiple of 8 with (M rounded up to the next of 2, 4, 6,
+ * 8, 10, 12, 16, 24, 32, 48, 64) * r * 4 <= 65536, 1 <= tile <= 256, 1 <= k_tile <= 16. */
+int lm_head_screen(const void* A, const float* u, const int32_t* row_token, int M, int r, int n,
+                   int tile, int k_tile, int32_t* cand, float* cand_score, void* stream);
+
+/* lm_head_rescore — exact logits of the candidates: logits [M, C] fp32 = W[cand[m, c]] . h[m]
+ * with W [V, d] bfloat16 in token order.  A candidate outside [0, V) gets -inf; one other than
+ * -1 also ORs TV_BAD_TOKEN into status[m] (status may be NULL).
+ * Limits: 1 <= M <= 64, C >= 1, V >= 1, d a positive multiple of 512. */
+int lm_head_rescore(const void* W, const void* h, const int32_t* cand, int M, int C, int d,
+                    int V, float* logits, int32_t* status, void* stream);
+
+/* lm_head_topk — the drafter's children: the K best valid candidates (tokens in [0, V)) of
+ * each hidden state by exact logit, best first, out_tok [M, K] int32, and their confidences
+ * out_conf [M, K] fp32, the softmax of the logits over all valid candidates of that hidden
+ * state (fp32 sums; confidences agree with an fp64 evaluation to about 1e-6 relative).  With
+ * fewer than K valid candidates the rest are token -1, confidence 0.
+ * Limits: M >= 1, 1 <= C <= 8192, 1 <= K <= 64, V >= 1. */
+int lm_head_topk(const float* logits, const int32_t* cand, int M, int C, int K, int V,
+                 int32_t* out_tok, float* out_conf, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

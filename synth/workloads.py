@@ -516,3 +516,78 @@ def make_draft_levels(spec: WorkloadSpec | str, B: int | None = None, depth: int
                         break
                 tok[l, b, r] = t
     return DraftLevels(depth, k, branch, root, tok, conf)
+
+
+STREAM_LM = 7  # seed stream of the drafter LM head's weights and hidden states
+
+
+@dataclasses.dataclass
+class LmHeadInputs:
+    """Synthetic drafter LM head (bfloat16 bit patterns).
+
+    h [M, d]: hidden states.  A [n, r]: the low-rank head's rows in shuffled order, row q
+    belonging to token row_token[q] ([n] int32, a permutation).  B [r, d].  W [n, d]: the full
+    head in token order, W = A_tok B plus full-rank noise, so the low-rank screening scores
+    approximate the logits.  tile, k_tile, K: screening tile, candidates per tile, children."""
+    name: str
+    M: int
+    d: int
+    n: int
+    r: int
+    tile: int
+    k_tile: int
+    K: int
+    h: np.ndarray
+    A: np.ndarray
+    B: np.ndarray
+    W: np.ndarray
+    row_token: np.ndarray
+
+
+LM_HEADS = {
+    # one EAGLE-2 expansion level at batch 1: the 10 frontier nodes' hidden states through a
+    # Llama-3-8B-sized head (hidden 4096, vocabulary 128256), rank 256, tiles of 256 rows with
+    # 4 candidates each (2004 candidates), 10 children per node
+    "llama8b_head_M10": dict(wid=20, M=10, d=4096, n=LLAMA3_VOCAB, r=256, tile=256, k_tile=4,
+                             K=10),
+    # the same head for 64 hidden states at once (e.g. 64 sequences drafting one token each)
+    "llama8b_head_M64": dict(wid=21, M=64, d=4096, n=LLAMA3_VOCAB, r=256, tile=256, k_tile=4,
+                             K=10),
+}
+
+
+def make_lm_head(name: str = "llama8b_head_M10", seed: int = 0, noise: float = 1.0,
+                 **override) -> LmHeadInputs:
+    """Seeded drafter head.  h ~ N(0, 1); B ~ N(0, 1/d) so u = B h is about N(0, 1); the
+    token-order factor A_tok ~ N(0, 9/r) so screening scores are about N(0, 9); W = A_tok B + E
+    with E uniform of variance noise^2/d, so an exact logit is the screening score plus
+    noise of variance about noise^2.  Rows of A are shuffled by a seeded permutation.
+    `override` changes M, d, n, r, tile, k_tile or K (tests use small heads)."""
+    cfg = dict(LM_HEADS[name])
+    cfg.update(override)
+    M, d, n, r = cfg["M"], cfg["d"], cfg["n"], cfg["r"]
+    rng = _rng(cfg["wid"], 0, STREAM_LM, seed)
+    h = rng.standard_normal((M, d), dtype=np.float32)
+    Bf = rng.standard_normal((r, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(d))
+    A_tok = rng.standard_normal((n, r), dtype=np.float32) * np.float32(3.0 / math.sqrt(r))
+    perm = rng.permutation(n).astype(np.int32)
+    W = np.empty((n, d), np.uint16)
+    step = 8192
+    for i0 in range(0, n, step):
+        blk = A_tok[i0:i0 + step] @ Bf
+        e = rng.random(blk.shape, dtype=np.float32)
+        e -= np.float32(0.5)
+        e *= np.float32(noise * math.sqrt(12.0 / d))
+        blk += e
+        # round to nearest even bfloat16 in place (the values are finite): as f32_to_bf16_bits
+        u = blk.view(np.uint32)
+        t = e.view(np.uint32)
+        np.right_shift(u, np.uint32(16), out=t)
+        t &= np.uint32(1)
+        t += np.uint32(0x7FFF)
+        t += u
+        t >>= np.uint32(16)
+        W[i0:i0 + step] = t
+    return LmHeadInputs(name, M, d, n, r, cfg["tile"], cfg["k_tile"], cfg["K"],
+                        f32_to_bf16_bits(h), f32_to_bf16_bits(A_tok[perm]), f32_to_bf16_bits(Bf),
+                        W, perm)

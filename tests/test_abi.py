@@ -288,3 +288,49 @@ def test_eagle2_rerank_argument_errors(lib):
         if i == 3 and v > 511:
             bad[4] = v
         assert lib.eagle2_rerank(*bad) == -1, (i, v)
+
+
+def test_lm_head_argument_errors(lib):
+    # project: h, B, M, r, d, u, stream
+    base = [FAKE, FAKE, 10, 256, 4096, FAKE, None]
+    for i in (0, 1, 5):
+        bad = list(base)
+        bad[i] = None
+        assert lib.lm_head_project(*bad) == -1, i
+    for i, v in ((2, 0), (2, 65), (3, 0), (4, 0), (4, 4000), (4, 256)):
+        bad = list(base)
+        bad[i] = v
+        assert lib.lm_head_project(*bad) == -1, (i, v)
+    # screen: A, u, row_token, M, r, n, tile, k_tile, cand, score, stream
+    base = [FAKE, FAKE, FAKE, 10, 256, 128256, 256, 4, FAKE, FAKE, None]
+    for i in (0, 1, 2, 8, 9):
+        bad = list(base)
+        bad[i] = None
+        assert lib.lm_head_screen(*bad) == -1, i
+    for i, v in ((3, 0), (3, 65), (4, 0), (4, 12), (5, 0), (6, 0), (6, 257), (7, 0), (7, 17)):
+        bad = list(base)
+        bad[i] = v
+        assert lib.lm_head_screen(*bad) == -1, (i, v)
+    bad = list(base)
+    bad[3], bad[4] = 64, 512  # 64 chains x 512 ranks x 4 B of u exceeds 64 KB of LDS
+    assert lib.lm_head_screen(*bad) == -1
+    # rescore: W, h, cand, M, C, d, V, logits, status, stream
+    base = [FAKE, FAKE, FAKE, 10, 2004, 4096, 128256, FAKE, None, None]
+    for i in (0, 1, 2, 7):
+        bad = list(base)
+        bad[i] = None
+        assert lib.lm_head_rescore(*bad) == -1, i
+    for i, v in ((3, 0), (3, 65), (4, 0), (5, 100), (6, 0)):
+        bad = list(base)
+        bad[i] = v
+        assert lib.lm_head_rescore(*bad) == -1, (i, v)
+    # topk: logits, cand, M, C, K, V, tok, conf, stream
+    base = [FAKE, FAKE, 10, 2004, 10, 128256, FAKE, FAKE, None]
+    for i in (0, 1, 6, 7):
+        bad = list(base)
+        bad[i] = None
+        assert lib.lm_head_topk(*bad) == -1, i
+    for i, v in ((2, 0), (3, 0), (3, 8193), (4, 0), (4, 65), (5, 0)):
+        bad = list(base)
+        bad[i] = v
+        assert lib.lm_head_topk(*bad) == -1, (i, v)

@@ -24,7 +24,8 @@ EXPORTS = ("tv_status_string", "tree_build_mask", "tree_verify_attn_workspace_si
            "tree_verify_step", "tree_verify_attn_paged", "kv_commit_paged",
            "tree_accept_stochastic", "tree_accept_stochastic_workspace_size",
            "tv_profile_accept_stochastic", "eagle2_node_count", "eagle2_expand",
-           "eagle2_rerank")
+           "eagle2_rerank", "lm_head_project", "lm_head_screen", "lm_head_rescore",
+           "lm_head_topk")
 
 
 class TreeVerifyError(RuntimeError):
@@ -96,6 +97,14 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.eagle2_expand.restype = I
     lib.eagle2_rerank.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P, P]
     lib.eagle2_rerank.restype = I
+    lib.lm_head_project.argtypes = [P, P, I, I, I, P, P]
+    lib.lm_head_project.restype = I
+    lib.lm_head_screen.argtypes = [P, P, P, I, I, I, I, I, P, P, P]
+    lib.lm_head_screen.restype = I
+    lib.lm_head_rescore.argtypes = [P, P, P, I, I, I, I, P, P, P]
+    lib.lm_head_rescore.restype = I
+    lib.lm_head_topk.argtypes = [P, P, I, I, I, I, P, P, P]
+    lib.lm_head_topk.restype = I
 
 
 def status_string(code: int) -> str:
@@ -505,3 +514,85 @@ def eagle2_rerank(table: dict, n_nodes: int, T: int, out: dict | None = None, st
         int(n_nodes), n_max, B, int(T), _ptr(out["parent"]), _ptr(out["tok"]), _ptr(out["depth"]),
         _ptr(out["node"]), _ptr(table["status"]), _stream(stream)))
     return out
+
+
+def _bf16_2d(t: torch.Tensor, name: str) -> None:
+    _need(t, name, torch.bfloat16, 2)
+
+
+def lm_head_project(h, B, u=None, stream=None):
+    """u [M, r] float32 = B [r, d] h [M, d] (bfloat16 inputs)."""
+    _bf16_2d(h, "h")
+    _bf16_2d(B, "B")
+    M, d = h.shape
+    r = B.shape[0]
+    if B.shape[1] != d:
+        raise ValueError("h and B disagree on d")
+    u = torch.empty((M, r), dtype=torch.float32, device=h.device) if u is None else u
+    _need(u, "u", torch.float32, 2)
+    _check("lm_head_project", load_library().lm_head_project(_ptr(h), _ptr(B), M, r, d, _ptr(u),
+                                                            _stream(stream)))
+    return u
+
+
+def lm_head_screen(A, u, row_token, tile: int, k_tile: int, cand=None, cand_score=None,
+                   stream=None):
+    """Local top-k screening -> (cand [M, C] int32 tokens, cand_score [M, C] float32)."""
+    _bf16_2d(A, "A")
+    _need(u, "u", torch.float32, 2)
+    _need(row_token, "row_token", torch.int32, 1)
+    n, r = A.shape
+    M = u.shape[0]
+    if u.shape[1] != r or row_token.shape[0] != n:
+        raise ValueError("inconsistent lm_head_screen shapes")
+    C = -(-n // tile) * k_tile
+    dev = A.device
+    cand = torch.empty((M, C), dtype=torch.int32, device=dev) if cand is None else cand
+    cand_score = (torch.empty((M, C), dtype=torch.float32, device=dev) if cand_score is None
+                  else cand_score)
+    _check("lm_head_screen", load_library().lm_head_screen(
+        _ptr(A), _ptr(u), _ptr(row_token), M, r, n, int(tile), int(k_tile), _ptr(cand),
+        _ptr(cand_score), _stream(stream)))
+    return cand, cand_score
+
+
+def lm_head_rescore(W, h, cand, logits=None, status=None, stream=None):
+    """Exact candidate logits [M, C] float32 = W[cand] . h."""
+    _bf16_2d(W, "W")
+    _bf16_2d(h, "h")
+    _need(cand, "cand", torch.int32, 2)
+    V, d = W.shape
+    M, C = cand.shape
+    if h.shape != (M, d):
+        raise ValueError("inconsistent lm_head_rescore shapes")
+    logits = torch.empty((M, C), dtype=torch.float32, device=W.device) if logits is None else logits
+    if status is not None:
+        _need(status, "status", torch.int32, 1)
+    _check("lm_head_rescore", load_library().lm_head_rescore(
+        _ptr(W), _ptr(h), _ptr(cand), M, C, d, V, _ptr(logits), _ptr(status), _stream(stream)))
+    return logits
+
+
+def lm_head_topk(logits, cand, K: int, V: int, out_tok=None, out_conf=None, stream=None):
+    """The drafter's children -> (tokens [M, K] int32, confidences [M, K] float32)."""
+    _need(logits, "logits", torch.float32, 2)
+    _need(cand, "cand", torch.int32, 2)
+    M, C = cand.shape
+    dev = cand.device
+    out_tok = torch.empty((M, K), dtype=torch.int32, device=dev) if out_tok is None else out_tok
+    out_conf = torch.empty((M, K), dtype=torch.float32, device=dev) if out_conf is None else out_conf
+    _check("lm_head_topk", load_library().lm_head_topk(
+        _ptr(logits), _ptr(cand), M, C, int(K), int(V), _ptr(out_tok), _ptr(out_conf),
+        _stream(stream)))
+    return out_tok, out_conf
+
+
+def lm_head_two_stage(h, A, B, W, row_token, tile: int, k_tile: int, K: int, status=None,
+                      stream=None) -> dict:
+    """Both stages and the children, in four launches on one stream: dict of u, cand,
+    cand_score, logits, tok, conf."""
+    u = lm_head_project(h, B, stream=stream)
+    cand, score = lm_head_screen(A, u, row_token, tile, k_tile, stream=stream)
+    logits = lm_head_rescore(W, h, cand, status=status, stream=stream)
+    tok, conf = lm_head_topk(logits, cand, K, W.shape[0], stream=stream)
+    return dict(u=u, cand=cand, cand_score=score, logits=logits, tok=tok, conf=conf)
