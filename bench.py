@@ -77,6 +77,10 @@ def parse_args():
                    help="also time device-side EAGLE-2 tree construction (every eagle2_expand "
                         "level, then eagle2_rerank) on the workload's expansion shape, and the "
                         "oracle's construction on the host; reported under \"construction\"")
+    p.add_argument("--lm-head", metavar="HEAD", default=None,
+                   help="also time the two-stage drafter LM head (lm_head_project, _screen, "
+                        "_rescore, _topk) on a synthetic head (synth.LM_HEADS: llama8b_head_M10, "
+                        "llama8b_head_M64); reported under \"lm_head\"")
     p.add_argument("--rotate", type=int, default=0, help="input copies to rotate (0 = auto)")
     p.add_argument("--mode", choices=("graph", "eager"), default="graph",
                    help="replay each step as a captured HIP graph, or launch eagerly")
@@ -434,6 +438,107 @@ def construction_bench(tv, torch, w, stream, steps: int, warmup: int) -> dict:
     }
 
 
+def lm_head_bench(tv, torch, name: str, stream, steps: int, warmup: int) -> dict:
+    """The two-stage drafter LM head on a synthetic head: the four launches replayed as HIP
+    graphs (inputs resident), per-kernel durations from events between eager calls, the
+    roofline of the whole head against HBM, and the oracle on the host for a sample of hidden
+    states."""
+    from synth import make_lm_head
+
+    x = make_lm_head(name)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)  # noqa: E731
+    h, A, Bm, W = bf(x.h), bf(x.A), bf(x.B), bf(x.W)
+    perm = torch.from_numpy(x.row_token).cuda()
+    M, C = x.M, -(-x.n // x.tile) * x.k_tile
+    u = torch.empty((M, x.r), dtype=torch.float32, device="cuda")
+    cand = torch.empty((M, C), dtype=torch.int32, device="cuda")
+    score = torch.empty((M, C), dtype=torch.float32, device="cuda")
+    logits = torch.empty((M, C), dtype=torch.float32, device="cuda")
+    tok = torch.empty((M, x.K), dtype=torch.int32, device="cuda")
+    conf = torch.empty((M, x.K), dtype=torch.float32, device="cuda")
+
+    calls = [
+        lambda st: tv.lm_head_project(h, Bm, u=u, stream=st),
+        lambda st: tv.lm_head_screen(A, u, perm, x.tile, x.k_tile, cand=cand, cand_score=score,
+                                     stream=st),
+        lambda st: tv.lm_head_rescore(W, h, cand, logits=logits, stream=st),
+        lambda st: tv.lm_head_topk(logits, cand, x.K, x.n, out_tok=tok, out_conf=conf, stream=st),
+    ]
+
+    reps = 8
+    with torch.cuda.stream(stream):
+        for c in calls:
+            c(stream)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            cs = torch.cuda.current_stream()
+            for _ in range(reps):
+                for c in calls:
+                    c(cs)
+        for _ in range(max(1, warmup // reps)):
+            g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_graphs = max(1, steps // reps)
+        stream.synchronize()
+        e0.record(stream)
+        for _ in range(n_graphs):
+            g.replay()
+        e1.record(stream)
+        e1.synchronize()
+    t_head = e0.elapsed_time(e1) * 1e-3 / (n_graphs * reps)
+
+    n_prof = 50
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_prof)]
+    for row in ev:
+        for e in row:
+            e.record(stream)
+    stream.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(n_prof):
+            ev[i][0].record(stream)
+            for j, c in enumerate(calls):
+                c(stream)
+                ev[i][j + 1].record(stream)
+        stream.synchronize()
+    per = [float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n_prof)])) * 1e3
+           for j in range(4)]
+
+    # algorithmic bytes: A, B and h once, the candidates' rows of W, the small outputs
+    a_bytes = x.n * x.r * 2 + x.r * x.d * 2 + M * x.d * 2
+    w_bytes = M * C * x.d * 2
+    out_bytes = M * x.r * 4 * 2 + M * C * 4 * 5 + M * x.K * 8
+    byts = a_bytes + w_bytes + out_bytes
+    full_head_bytes = x.n * x.d * 2
+
+    from oracle import oracle as O  # the CPU baseline leg
+
+    rows = min(M, 2)
+    t0 = time.perf_counter()
+    O.lm_head_two_stage(x.h[:rows], x.A, x.B, x.W, x.row_token, x.tile, x.k_tile, x.K)
+    t_cpu = (time.perf_counter() - t0) * M / rows
+    return {
+        "head": name, "M": M, "d": x.d, "vocab": x.n, "rank": x.r, "tile": x.tile,
+        "k_tile": x.k_tile, "candidates": C, "children": x.K,
+        "head_us": t_head * 1e6,
+        "hidden_states_per_s": M / t_head,
+        "kernel_us": {"lm_head_project": per[0], "lm_head_screen": per[1],
+                      "lm_head_rescore": per[2], "lm_head_topk": per[3]},
+        "algorithmic_bytes": byts,
+        "roofline": {"bound": "hbm", "achieved": byts / t_head / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": byts / t_head / 1e9 / HBM_PEAK_GBS},
+        "full_head_bytes": full_head_bytes,
+        "full_head_us_at_hbm_peak": full_head_bytes / (HBM_PEAK_GBS * 1e9) * 1e6,
+        "cpu_baseline": {"head_us": t_cpu * 1e6, "cores": 1, "kind": "oracle",
+                         "sample": f"{rows} of {M} hidden states through both stages, scaled "
+                                   f"to {M}"},
+        "note": ("head_us: graphs of 8 heads (four launches each) replayed back to back; "
+                 "kernel_us from events between eager calls (launch latency included); bytes: "
+                 "A, B and h once plus the candidates' rows of W; full_head_* is what reading "
+                 "the whole head once would take at the HBM peak, for context"),
+    }
+
+
 def cpu_baseline(w, kv_bytes: int, target_s: float) -> dict:
     """The oracle (never tuned) on a bounded random sample of attention rows."""
     from oracle import oracle as O
@@ -763,6 +868,12 @@ def main() -> int:
         print("[bench] timing EAGLE-2 tree construction", file=sys.stderr, flush=True)
         construction = construction_bench(tv, torch, w, stream, args.steps, args.warmup)
 
+    lm_head = None
+    if args.lm_head:
+        print(f"[bench] timing the two-stage drafter LM head {args.lm_head}", file=sys.stderr,
+              flush=True)
+        lm_head = lm_head_bench(tv, torch, args.lm_head, stream, args.steps, args.warmup)
+
     alen = sets[0].t["alen"].cpu().numpy()
     status = sets[0].t["status"].cpu().numpy()
     if (status & ~0).any():
@@ -821,6 +932,7 @@ def main() -> int:
         "paged": paged_breakdown,
         "stochastic": stoch_breakdown,
         "construction": construction,
+        "lm_head": lm_head,
         "hbm_frac": value / HBM_PEAK_GBS,
         "attn_kv_gbps": kv_bytes / t_attn / 1e9,
         "attn_hbm_frac": kv_bytes / t_attn / 1e9 / HBM_PEAK_GBS,

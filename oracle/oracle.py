@@ -340,12 +340,12 @@ def _bf16(a) -> np.ndarray:
 
 def lm_project(h, Bm, lib=None) -> np.ndarray:
     """u [M, r] float32 = B h, each entry by the fixed-order float32 dot product (dot_seg64).
-    h [M, d] and B [r, d] are bfloat16 bit patterns; d a multiple of 64."""
+    h [M, d] and B [r, d] are bfloat16 bit patterns; d a multiple of 512."""
     lib = lib or load()
     h, Bm = _bf16(h), _bf16(Bm)
     M, d = h.shape
     r = Bm.shape[0]
-    assert Bm.shape[1] == d and d % 64 == 0
+    assert Bm.shape[1] == d and d % 512 == 0
     u = np.empty((M, r), np.float32)
     lib.oracle_lm_project(_p(h), _p(Bm), M, r, d, _p(u))
     return u
@@ -375,6 +375,7 @@ def lm_rescore(W, h, cand, lib=None) -> tuple[np.ndarray, np.ndarray]:
     cand = _i32(cand)
     V, d = W.shape
     M, C = cand.shape
+    assert d % 512 == 0
     logits = np.empty((M, C), np.float32)
     status = np.zeros(M, np.int32)
     lib.oracle_lm_rescore(_p(W), _p(h), _p(cand), M, C, d, V, _p(logits), _p(status))

@@ -749,9 +749,10 @@ int oracle_eagle2_build(const int32_t* root_tok, const int32_t* child_tok,
  * and their confidences (a softmax over the candidates).  Which candidates are kept and which
  * children chosen is decided by float32 values, so these are computed in the float32
  * arithmetic, and the summation order, that the kernels use:
- *   dot_seg64   64 segments of d/64 consecutive elements, each a chain of fused multiply-adds in
- *               index order from 0; then the segment sums are combined pairwise, sum j with sum
- *               j ^ 32, then j ^ 16, ..., j ^ 1; the result is that of segment 0.
+ *   dot_seg64   d is a multiple of 512.  Chain j (j = 0 .. 63) runs fused multiply-adds from 0
+ *               over elements 512 p + 8 j + e, for p = 0 .. d/512 - 1 and e = 0 .. 7 in that
+ *               order (p outer); then the 64 chain sums are combined pairwise, sum j with sum
+ *               j ^ 32, then j ^ 16, ..., j ^ 1; the result is that of chain 0.
  *   screening   one chain of fused multiply-adds over the rank index, in order, from 0.
  * Values are ranked by the float's order with -0 taken as +0 (an unsigned key of the bits);
  * equal values go to the smaller row (screening) or the smaller token (final selection).
@@ -778,10 +779,13 @@ static uint32_t float_key(float v) {
 
 static float dot_seg64(const uint16_t* x, const uint16_t* y, int d) {
   float v[64], w[64];
-  const int seg = d / 64;
   for (int j = 0; j < 64; ++j) {
     float acc = 0.0f;
-    for (int i = 0; i < seg; ++i) acc = fmaf(bf16f(x[j * seg + i]), bf16f(y[j * seg + i]), acc);
+    for (int p = 0; p < d / 512; ++p)
+      for (int e = 0; e < 8; ++e) {
+        const int i = 512 * p + 8 * j + e;
+        acc = fmaf(bf16f(x[i]), bf16f(y[i]), acc);
+      }
     v[j] = acc;
   }
   for (int off = 32; off >= 1; off >>= 1) {
@@ -791,7 +795,7 @@ static float dot_seg64(const uint16_t* x, const uint16_t* y, int d) {
   return v[0];
 }
 
-/* u[m, i] = B[i, :] . h[m, :] (dot_seg64); h [M, d], B [r, d] bfloat16 bits; d % 64 == 0. */
+/* u[m, i] = B[i, :] . h[m, :] (dot_seg64); h [M, d], B [r, d] bfloat16 bits; d % 512 == 0. */
 void oracle_lm_project(const uint16_t* h, const uint16_t* Bm, int M, int r, int d, float* u) {
   for (int m = 0; m < M; ++m)
     for (int i = 0; i < r; ++i)

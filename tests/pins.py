@@ -1309,7 +1309,7 @@ def pin_lm_integer_bruteforce(lib):
 
     rng = np.random.default_rng(31)
     for trial in range(25):
-        M, d, r = int(rng.integers(1, 4)), 64 * int(rng.integers(1, 3)), int(rng.integers(1, 9))
+        M, d, r = int(rng.integers(1, 4)), 512 * int(rng.integers(1, 3)), int(rng.integers(1, 9))
         n, tile, k_tile = int(rng.integers(5, 60)), int(rng.integers(2, 12)), int(rng.integers(1, 4))
         h, Bm, A, W, perm = _int_lm_case(rng, M, d, r, n)
         K = int(rng.integers(1, 6))
@@ -1346,7 +1346,7 @@ def pin_lm_error_bound(lib):
     exact value, (terms + 6) * 2^-24 * sum |x_i y_i| for the segmented dot products and
     r * 2^-24 * sum |a_i u_i| for the screening chain."""
     rng = np.random.default_rng(32)
-    M, d, r, n = 3, 256, 48, 40
+    M, d, r, n = 3, 1024, 48, 40
     h = _bits(rng.standard_normal((M, d)))
     Bm = _bits(rng.standard_normal((r, d)))
     A = _bits(rng.standard_normal((n, r)))
@@ -1354,7 +1354,7 @@ def pin_lm_error_bound(lib):
     f = lambda b: bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
     u = O.lm_project(h, Bm, lib=lib)
     ex, mag = f(h) @ f(Bm).T, np.abs(f(h)) @ np.abs(f(Bm)).T
-    assert (np.abs(u - ex) <= (d // 64 + 7) * 2.0 ** -24 * mag + 1e-30).all()
+    assert (np.abs(u - ex) <= (d // 64 + 7) * 2.0 ** -24 * mag + 1e-30).all()  # d/64 per chain
     perm = np.arange(n, dtype=np.int32)
     cand, score = O.lm_screen(A, u, perm, n, n, lib=lib)  # one tile keeps every row
     ex_s = u.astype(np.float64) @ f(A).T
@@ -1373,7 +1373,7 @@ def pin_lm_exact_screen_keeps_global_best(lib):
     (numpy over all of W h, ties to the smaller token), whatever the row shuffle."""
     rng = np.random.default_rng(33)
     for trial in range(10):
-        M, d, n, K = 2, 64, int(rng.integers(20, 90)), int(rng.integers(1, 5))
+        M, d, n, K = 2, 512, int(rng.integers(20, 90)), int(rng.integers(1, 5))
         tile, k_tile = int(rng.integers(3, 10)), K + int(rng.integers(0, 3))
         h, _, _, W, perm = _int_lm_case(rng, M, d, 1, n, lo=-6, hi=7)
         eye = np.eye(d, dtype=np.int64)
@@ -1390,7 +1390,7 @@ def pin_lm_padding_and_bad_tokens(lib):
     logits without a flag, out-of-range ones get -inf and ORC_BAD_TOKEN; the children skip them
     and pad with -1 / 0 when fewer than K valid candidates remain."""
     rng = np.random.default_rng(34)
-    h, Bm, A, W, perm = _int_lm_case(rng, 2, 64, 4, 7)
+    h, Bm, A, W, perm = _int_lm_case(rng, 2, 512, 4, 7)
     u = O.lm_project(_bits(h), _bits(Bm), lib=lib)
     cand, score = O.lm_screen(_bits(A), u, perm, 3, 2, lib=lib)  # tiles of 3, 3, 1 rows
     assert cand.shape == (2, 6) and (cand[:, 5] == -1).all() and np.isneginf(score[:, 5]).all()

@@ -137,9 +137,12 @@ MUTANTS = {
     # LM head: segment sums combined from the nearest pairs up instead of from j ^ 32 down
     "lm_butterfly_reversed": ("for (int off = 32; off >= 1; off >>= 1) {\n    for (int j = 0; j < 64; ++j) w[j]",
                               "for (int off = 1; off <= 32; off <<= 1) {\n    for (int j = 0; j < 64; ++j) w[j]"),
-    # LM head: each segment's chain run from its last element
-    "lm_segment_reversed": ("acc = fmaf(bf16f(x[j * seg + i]), bf16f(y[j * seg + i]), acc);",
-                            "acc = fmaf(bf16f(x[j * seg + seg - 1 - i]), bf16f(y[j * seg + seg - 1 - i]), acc);"),
+    # LM head: each chain runs over its pieces' elements in reverse
+    "lm_segment_reversed": ("const int i = 512 * p + 8 * j + e;",
+                            "const int i = 512 * (d / 512 - 1 - p) + 8 * j + 7 - e;"),
+    # LM head: chains over d/64 consecutive elements instead of interleaved 8-element pieces
+    "lm_segment_contiguous": ("const int i = 512 * p + 8 * j + e;",
+                              "const int i = j * (d / 64) + 8 * p + e;"),
     # LM head: screening chain over the rank index in reverse
     "lm_screen_reversed": ("for (int i = 0; i < r; ++i) acc = fmaf(bf16f(a[i]), um[i], acc);",
                            "for (int i = r - 1; i >= 0; --i) acc = fmaf(bf16f(a[i]), um[i], acc);"),

@@ -8,10 +8,11 @@
 //
 // The candidates and children are chosen by float32 values, so every dot product has a stated
 // order, part of the definition of the result:
-//   * lm_dot (u = B h, logits = W[token] h): lane j of a wavefront owns the d/64 consecutive
-//     elements of segment j and runs a chain of fused multiply-adds over them in index order
-//     from 0; the 64 segment sums are then combined by a butterfly, j with j^32, then j^16, ...,
-//     j^1, which leaves the same value in every lane;
+//   * lm_dot (u = B h, logits = W[token] h; d a multiple of 512): lane j of a wavefront runs a
+//     chain of fused multiply-adds from 0 over elements 512 p + 8 j + e (p = 0, 1, ... outer,
+//     e = 0 .. 7 inner), so every 16-byte load of the wavefront covers 1 KB contiguously; the
+//     64 chain sums are then combined by a butterfly, j with j^32, then j^16, ..., j^1, which
+//     leaves the same value in every lane;
 //   * screening (A u): one chain of fused multiply-adds over the rank index, in order, from 0.
 // Ranking uses an unsigned key of the float (-0 as +0); equal values go to the smaller row
 // (screening) or the smaller token (children).
@@ -24,8 +25,9 @@
 //                      runs the M chains, then each wavefront picks its k best rows per hidden
 //                      state by wavefront maxima and the four wavefronts' picks are merged
 //   lm_rescore_kernel  one wavefront per (m, c): W[cand] . h[m]                  (8 KB per row)
-//   lm_topk_kernel     one workgroup per hidden state: K rounds of block-wide maxima over the
-//                      candidates, and the softmax denominator over all valid candidates
+//   lm_topk_kernel     one workgroup per hidden state: each wavefront takes K rounds of
+//                      wavefront maxima over its share of the candidates, the 4K picks are
+//                      merged by rank, and the softmax denominator covers all valid candidates
 #include <hip/hip_runtime.h>
 
 #include "tree_device.h"
@@ -61,16 +63,15 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
 }
 
 // The fixed-order dot product of two bfloat16 rows of length d (d % 512 == 0), by the calling
-// wavefront: lane j reads its segment as 16-byte pieces (seg / 8 of them).
+// wavefront: lane j's pieces are the 16 bytes at element 512 p + 8 j.
 __device__ inline float lm_dot(const uint16_t* __restrict__ x, const uint16_t* __restrict__ y,
                                int d) {
   const int lane = threadIdx.x & 63;
-  const int seg = d >> 6;
-  const uint4* xs = reinterpret_cast<const uint4*>(x + (size_t)lane * seg);
-  const uint4* ys = reinterpret_cast<const uint4*>(y + (size_t)lane * seg);
+  const uint4* xs = reinterpret_cast<const uint4*>(x) + lane;  // 64 pieces per 512 elements
+  const uint4* ys = reinterpret_cast<const uint4*>(y) + lane;
   float acc = 0.f;
-  for (int p = 0; p < (seg >> 3); ++p) {
-    const uint4 a = xs[p], b = ys[p];
+  for (int p = 0; p < (d >> 9); ++p) {
+    const uint4 a = xs[64 * p], b = ys[64 * p];
     acc = __builtin_fmaf(bf16_lo(a.x), bf16_lo(b.x), acc);
     acc = __builtin_fmaf(bf16_hi(a.x), bf16_hi(b.x), acc);
     acc = __builtin_fmaf(bf16_lo(a.y), bf16_lo(b.y), acc);
@@ -96,7 +97,8 @@ __global__ __launch_bounds__(256) void lm_project_kernel(const uint16_t* __restr
 }
 
 // Screening of tile blockIdx.x: rows r0 .. r0 + rows - 1 of A [n, r]; u [M, r] fp32 staged in
-// LDS (dynamic shared memory, kM * r floats, rows m >= M zero); k_tile candidates per hidden
+// LDS (dynamic shared memory, kM * r floats, rows m >= M zero) and read with 16-byte reads
+// that every lane of a wavefront takes from the same address; k_tile candidates per hidden
 // state.  kM >= M is the number of chains each thread runs (a compile-time count so the
 // accumulators stay in registers; the chains of m >= M are discarded).
 template <int kM>
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(256) void lm_screen_kernel(
     float* __restrict__ cand_score) {
   // two slices of the tile's rows: [row][128 B], piece v of row q at ((v ^ (q & 7)) * 16)
   __shared__ __attribute__((aligned(16))) char s_a[2][kLmMaxTile * 128];
-  extern __shared__ float s_u[];  // [M][r]
+  extern __shared__ __attribute__((aligned(16))) float s_u[];  // [kM][r]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x;
   const int r0 = t * tile;
@@ -147,14 +149,27 @@ __global__ __launch_bounds__(256) void lm_screen_kernel(
     const int q = tid;
     const int i_end = min(kLmSlice, r - sl * kLmSlice);
     const float* us = s_u + sl * kLmSlice;
+#pragma unroll 2
     for (int v = 0; v < (i_end >> 3); ++v) {
       const uint4 a = *reinterpret_cast<const uint4*>(&s_a[sl & 1][q * 128 + ((v ^ (q & 7)) << 4)]);
       const float av[8] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
                            bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w)};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-#pragma unroll
-        for (int m = 0; m < kM; ++m) acc[m] = __builtin_fmaf(av[e], us[m * r + v * 8 + e], acc[m]);
+      for (int m = 0; m < kM; ++m) {
+        // u[m][8v .. 8v+7], the same for every lane
+        const float* um = us + m * r + v * 8;
+        const float4 u0 = *reinterpret_cast<const float4*>(um);
+        const float4 u1 = *reinterpret_cast<const float4*>(um + 4);
+        float a_m = acc[m];
+        a_m = __builtin_fmaf(av[0], u0.x, a_m);
+        a_m = __builtin_fmaf(av[1], u0.y, a_m);
+        a_m = __builtin_fmaf(av[2], u0.z, a_m);
+        a_m = __builtin_fmaf(av[3], u0.w, a_m);
+        a_m = __builtin_fmaf(av[4], u1.x, a_m);
+        a_m = __builtin_fmaf(av[5], u1.y, a_m);
+        a_m = __builtin_fmaf(av[6], u1.z, a_m);
+        a_m = __builtin_fmaf(av[7], u1.w, a_m);
+        acc[m] = a_m;
       }
     }
     if (sl + 1 < n_slices) store((sl + 1) & 1);
@@ -217,18 +232,19 @@ __global__ __launch_bounds__(256) void lm_rescore_kernel(const uint16_t* __restr
   }
 }
 
-// Children of hidden state blockIdx.x: K rounds of block-wide maxima of the 64-bit key
-// (logit key << 32 | ~token) over the valid candidates; confidences exp(l - max) / sum.
+// Children of hidden state blockIdx.x.  The 64-bit key (logit key << 32 | ~token) of every
+// valid candidate; each wavefront takes K rounds of wavefront maxima over its candidates, the
+// 4K picks (0 = none) are merged by rank; confidences exp(l - max) / sum over valid ones.
+template <int kPer>  // candidates per thread: C <= 256 * kPer
 __global__ __launch_bounds__(256) void lm_topk_kernel(const float* __restrict__ logits,
                                                       const int32_t* __restrict__ cand, int C,
                                                       int K, int V, int32_t* __restrict__ out_tok,
                                                       float* __restrict__ out_conf) {
-  __shared__ uint64_t s_w[4];
+  __shared__ uint64_t s_pick[4 * kLmMaxK];
   __shared__ float s_f[4];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* l = logits + (size_t)m * C;
   const int32_t* cm = cand + (size_t)m * C;
-  constexpr int kPer = 32;  // candidates per thread: C <= 256 * kPer
   uint64_t key[kPer];
   float mx = -INFINITY;
 #pragma unroll
@@ -257,32 +273,31 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const float* __restrict__ 
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
   if (lane == 0) s_f[wave] = z;
-  __syncthreads();
-  z = (s_f[0] + s_f[1]) + (s_f[2] + s_f[3]);
 
+  // this wavefront's K best
   for (int j = 0; j < K; ++j) {
     uint64_t best = 0;
 #pragma unroll
     for (int k = 0; k < kPer; ++k) best = key[k] > best ? key[k] : best;
     best = wave_max_u64(best);
-    if (lane == 0) s_w[wave] = best;
-    __syncthreads();
-    best = s_w[0];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) best = s_w[w] > best ? s_w[w] : best;
-    __syncthreads();  // s_w is rewritten next round
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-      if (key[k] == best) key[k] = 0;
-    if (tid == 0) {
-      const size_t o = (size_t)m * K + j;
-      if (best == 0) {
-        out_tok[o] = -1;
-        out_conf[o] = 0.f;
-      } else {
-        out_tok[o] = (int)(0xffffffffu - (uint32_t)best);
-        out_conf[o] = expf(fkey_value((uint32_t)(best >> 32)) - mx) / z;
-      }
+    for (int k = 0; k < kPer; ++k) key[k] = key[k] == best ? 0 : key[k];
+    if (lane == 0) s_pick[wave * K + j] = best;
+  }
+  __syncthreads();
+  z = (s_f[0] + s_f[1]) + (s_f[2] + s_f[3]);
+  for (int e = tid; e < 4 * K; e += 256) {
+    const uint64_t me = s_pick[e];
+    int rank = 0;  // picks are distinct except 0 (none), which ranks by entry
+    for (int o = 0; o < 4 * K; ++o) rank += s_pick[o] > me || (s_pick[o] == me && o < e);
+    if (rank >= K) continue;
+    const size_t o = (size_t)m * K + rank;
+    if (me == 0) {
+      out_tok[o] = -1;
+      out_conf[o] = 0.f;
+    } else {
+      out_tok[o] = (int)(0xffffffffu - (uint32_t)me);
+      out_conf[o] = expf(fkey_value((uint32_t)(me >> 32)) - mx) / z;
     }
   }
 }
@@ -364,7 +379,15 @@ extern "C" int lm_head_topk(const float* logits, const int32_t* cand, int M, int
   if (!logits || !cand || !out_tok || !out_conf || M < 1 || C < 1 || C > 256 * 32 || K < 1 ||
       K > kLmMaxK || V < 1)
     return TV_ERR_INVALID_ARG;
-  hipLaunchKernelGGL(lm_topk_kernel, dim3(M), dim3(256), 0, (hipStream_t)stream, logits, cand, C,
-                     K, V, out_tok, out_conf);
+  hipStream_t st = (hipStream_t)stream;
+  if (C <= 256 * 8)
+    hipLaunchKernelGGL(lm_topk_kernel<8>, dim3(M), dim3(256), 0, st, logits, cand, C, K, V, out_tok,
+                       out_conf);
+  else if (C <= 256 * 16)
+    hipLaunchKernelGGL(lm_topk_kernel<16>, dim3(M), dim3(256), 0, st, logits, cand, C, K, V,
+                       out_tok, out_conf);
+  else
+    hipLaunchKernelGGL(lm_topk_kernel<32>, dim3(M), dim3(256), 0, st, logits, cand, C, K, V,
+                       out_tok, out_conf);
   return launch_status();
 }
