@@ -593,9 +593,9 @@ def main() -> int:
     if args.copy_calibration:
         return copy_calibration()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the verification step has no multi-GPU path in "
-              "this build (sequences and KV heads would shard with no exchange; see DESIGN.md)",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the verification step has no multi-GPU path "
+              "(sequences and KV heads would shard across GPUs with no exchange, and one long "
+              "prefix as split-K with one exchange of partials)", file=sys.stderr)
         return 2
     import torch
 
