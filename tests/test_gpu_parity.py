@@ -71,6 +71,27 @@ def test_split_results_agree():
         assert np.abs(a - b).max() <= TOL_OUT["bf16"]
 
 
+# ---- every shape of the split-K merge ------------------------------------------------------
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+@pytest.mark.parametrize("target", [2, 4, 8, 20, 64])
+def test_merge_shapes(dtype, D, target):
+    """The merge loads 2, 4 or 8 chunks per round per thread, and beyond 8 chunks the four
+    wavefronts of a workgroup share a piece and meet in LDS (beyond 32, in several rounds).
+    Every such shape in both input types and head sizes.  G * T = 61 rows, so the second row of
+    the last bf16 pair is padding.  A zero-length prefix (one chunk, written directly) sits next
+    to sequences with many chunks."""
+    L = (1200, 2500) if target == 64 else (600, 1200)
+    w = make_workload("batch32_L512-4096_T60", B=3, T=61, L=L, Hq=3, Hkv=3, D=D, dtype=dtype,
+                      parent_kind="random", extra_seed=70 + target)
+    w.cache_len[1] = 0
+    tiles = 1 + -(-w.Lmax // 64)
+    chunk_tiles = -(-tiles // target)
+    S = -(-tiles // chunk_tiles)
+    lo = {2: 2, 4: 3, 8: 5, 20: 9, 64: 33}[target]
+    assert lo <= S <= max(target, 16) or (target == 64 and S > 32), (tiles, S)
+    _run_and_check(w, split_keys=64 * chunk_tiles, label=f"merge {dtype} D={D} S={S}")
+
+
 # ---- ragged shapes and edge cases ------------------------------------------------------------
 EDGE = [
     # (label, overrides)

@@ -909,106 +909,213 @@ void attn_main(AttnArgs a) {
 
 // Merge the per-chunk partials of sequences with more than one non-empty chunk:
 //   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  lse = (M + log2 den) ln 2.
-// One thread per group of four consecutive d of one row (the partials' register order), so a
-// row block of 256 rows is D / 4 workgroups' work.  Chunks are taken eight at a time with all
-// their loads in flight, and M is raised per batch (online, as in the main kernel).  Workgroups
-// are dealt to XCDs in the same (b, kvh) order as attn_main's, so a merge reads partials from
-// the L2 they were written to.
+// A thread owns 16 bytes of a slot's partial, in the partials' register order: in bf16 two
+// adjacent groups (rows r, r + 1 of one wavefront, four consecutive d), in fp32 one group (one
+// row, four d).  Chunks are taken kBatch at a time, exactly as many as the sequence has, with
+// all their loads in flight, and M is raised per batch (online, as in the main kernel).  With
+// few chunks (S <= 8) every thread of a workgroup owns different bytes and merges all chunks.
+// With more, the four wavefronts of a workgroup own the same 64 pieces and take every fourth
+// chunk each, then combine their (M, den, O) through LDS: four times the workgroups and a
+// quarter of the round trips, for the long splits of short batches.  Workgroups are dealt to
+// XCDs in the same (b, kvh) order as attn_main's, so a merge reads partials from the L2 they
+// were written to.
+template <typename E>
+constexpr int combine_rows_per_thread() {
+  return std::is_same<E, __bf16>::value ? 2 : 1;
+}
+
+// the merge's compile-time shape for a plan with S chunks per (b, kvh, rb)
+struct CombineShape {
+  int batch;  // chunks loaded per round by one thread
+  int sw;     // wavefronts sharing one piece (1 or 4)
+};
+inline CombineShape combine_shape(int S) {
+  if (S <= 2) return {2, 1};
+  if (S <= 4) return {4, 1};
+  if (S <= 8) return {8, 1};
+  return {8, 4};
+}
+
+template <typename E, int D, int kSW>
+constexpr int combine_wgs_per_item() {  // workgroups per (b, kvh, rb)
+  return kRows * D / 4 / combine_rows_per_thread<E>() * kSW / 256;
+}
+
 template <typename E, int D>
-constexpr int combine_wgs_per_item() {
-  return kRows * D / 4 / 256;  // workgroups of 256 threads per (b, kvh, rb)
+int combine_grid(int items, int S) {
+  return items * (combine_shape(S).sw == 1 ? combine_wgs_per_item<E, D, 1>()
+                                           : combine_wgs_per_item<E, D, 4>());
 }
 
 // Logical merge workgroup c (of B * Hkv * RB * combine_wgs_per_item), 256 threads.  The chunk
 // count comes from the workspace (written by attn_main), not from cache_len, which a fused
 // compaction may be updating at the same time.
-template <typename E, int D>
+template <typename E, int D, int kBatch, int kSW>
 __device__ void combine_group(const AttnArgs& a, int c) {
   constexpr bool kBF16 = std::is_same<E, __bf16>::value;
   constexpr int kDB = D / 32;
-  constexpr int kWGs = combine_wgs_per_item<E, D>();
-  constexpr int kBatch = 8;
+  constexpr int kR = combine_rows_per_thread<E>();
+  constexpr int kWGs = combine_wgs_per_item<E, D, kSW>();
+  constexpr int kPer = 256 / kSW;              // pieces per workgroup
+  constexpr int kStride = kRows * D / 4 / kR;  // 16-byte units per slot
+  using ML = typename std::conditional<kR == 2, float4, float2>::type;
   const int item = c / kWGs;  // (b, kvh, rb)
-  const int g = (c % kWGs) * 256 + threadIdx.x;
+  const int tid = threadIdx.x;
+  const int pl = tid % kPer, sg = tid / kPer;  // piece within the workgroup, chunk group
+  const int g = ((c % kWGs) * kPer + pl) * kR;  // first register-order group of the piece
   const int rb = item % a.RB;
   const int kvh = (item / a.RB) % a.Hkv;
   const int b = item / (a.RB * a.Hkv);
   const int n_split = a.nsplit[b];
-  if (n_split <= 1) return;  // written directly by attn_main
+  if (n_split <= 1) return;  // written directly by attn_main (uniform: the whole workgroup)
   // g = ((wave*kDB + db)*4 + j)*64 + lane  ->  row wave*32 + lane%32, d = db*32 + 8j + 4*(lane/32)
   const int lane = g & 63, j = (g >> 6) & 3, db = (g >> 8) % kDB, wave = (g >> 8) / kDB;
-  const int rloc = wave * 32 + (lane & 31);
-  const int r = rb * kRows + rloc;
-  if (r >= a.GT) return;
+  const int rloc = wave * 32 + (lane & 31);  // rows rloc .. rloc + kR - 1 (lane is even for kR 2)
+  const int r0 = rb * kRows + rloc;
+  const bool live = r0 < a.GT;  // padding rows were never written
   const int d = db * 32 + 8 * j + 4 * (lane >> 5);
   const size_t slot0 = (((size_t)b * a.Hkv + kvh) * a.RB + rb) * a.S;
-  const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + slot0 * kRows + rloc;
+  const uint4* po = reinterpret_cast<const uint4*>(a.part_o) + slot0 * kStride + g / kR;
+  const ML* pml =
+      reinterpret_cast<const ML*>(reinterpret_cast<const float2*>(a.part_ml) + slot0 * kRows + rloc);
 
-  float M = -INFINITY, den = 0.f;
-  float4 acc = float4{0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < n_split; s0 += kBatch) {
-    float2 ml[kBatch];
-    float4 v[kBatch];
+  float M[kR], den[kR];
+  float4 acc[kR];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      // past the last chunk: load the last one again (no branch, so all loads stay in flight)
-      // and give it weight 0
-      const int s = min(s0 + u, n_split - 1);
-      ml[u] = pml[(size_t)s * kRows];
-      if (s0 + u >= n_split) ml[u].x = -INFINITY;
-      const size_t gi = (slot0 + s) * (kRows * D / 4) + g;
-      if constexpr (kBF16) {
-        const uint2 w = reinterpret_cast<const uint2*>(a.part_o)[gi];
-        v[u] = float4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                      __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
-      } else {
-        v[u] = reinterpret_cast<const float4*>(a.part_o)[gi];
+  for (int i = 0; i < kR; ++i) {
+    M[i] = -INFINITY;
+    den[i] = 0.f;
+    acc[i] = float4{0.f, 0.f, 0.f, 0.f};
+  }
+  // chunk group sg takes chunks sg, sg + kSW, sg + 2 kSW, ...
+  const int n_mine = live && sg < n_split ? (n_split - sg + kSW - 1) / kSW : 0;
+  for (int k0 = 0; k0 < n_mine; k0 += kBatch) {
+    const int nb = min(kBatch, n_mine - k0);  // uniform across the wavefront
+    uint4 v[kBatch];
+    ML ml[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (u < nb) {
+        const size_t sidx = (size_t)(k0 + u) * kSW + sg;
+        v[u] = po[sidx * kStride];
+        ml[u] = pml[sidx * (kRows / kR)];
       }
-    }
-    // every non-empty chunk has a finite m (each row sees a key in it), so Mb is finite
-    float Mb = M;
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) Mb = fmaxf(Mb, ml[u].x);
-    const float sc = fast_exp2(M - Mb);  // 0 on the first batch
-    den *= sc;
-    acc.x *= sc;
-    acc.y *= sc;
-    acc.z *= sc;
-    acc.w *= sc;
+    for (int i = 0; i < kR; ++i) {
+      // (m, l) of row i and its four values in chunk u
+      auto m_of = [&](int u) -> float {
+        if constexpr (kR == 2) return i == 0 ? ml[u].x : ml[u].z;
+        else return ml[u].x;
+      };
+      auto l_of = [&](int u) -> float {
+        if constexpr (kR == 2) return i == 0 ? ml[u].y : ml[u].w;
+        else return ml[u].y;
+      };
+      auto val_of = [&](int u) {
+        if constexpr (kBF16) {
+          const uint32_t lo = i == 0 ? v[u].x : v[u].z, hi = i == 0 ? v[u].y : v[u].w;
+          return float4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
+                        __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
+        } else {
+          return float4{__uint_as_float(v[u].x), __uint_as_float(v[u].y),
+                        __uint_as_float(v[u].z), __uint_as_float(v[u].w)};
+        }
+      };
+      // every non-empty chunk has a finite m (each row sees a key in it), so Mb is finite
+      float Mb = M[i];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const float w = fast_exp2(ml[u].x - Mb);
-      den += w * ml[u].y;
-      acc.x += w * v[u].x;
-      acc.y += w * v[u].y;
-      acc.z += w * v[u].z;
-      acc.w += w * v[u].w;
+      for (int u = 0; u < kBatch; ++u)
+        if (u < nb) Mb = fmaxf(Mb, m_of(u));
+      const float sc = fast_exp2(M[i] - Mb);  // 0 on the first batch
+      den[i] *= sc;
+      acc[i].x *= sc;
+      acc[i].y *= sc;
+      acc[i].z *= sc;
+      acc[i].w *= sc;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (u < nb) {
+          const float w = fast_exp2(m_of(u) - Mb);
+          const float4 x = val_of(u);
+          den[i] += w * l_of(u);
+          acc[i].x += w * x.x;
+          acc[i].y += w * x.y;
+          acc[i].z += w * x.z;
+          acc[i].w += w * x.w;
+        }
+      M[i] = Mb;
     }
-    M = Mb;
   }
-  const float inv = 1.f / den;
-  const int t = r / a.G, head = kvh * a.G + r % a.G;
-  const size_t orow = ((size_t)b * a.T + t) * a.Hq + head;
-  E* o = reinterpret_cast<E*>(a.out) + orow * D;
-  if constexpr (kBF16) {
-    *reinterpret_cast<uint2*>(o + d) =
-        uint2{pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv)};
-  } else {
-    *reinterpret_cast<float4*>(o + d) = float4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+  if constexpr (kSW > 1) {
+    // the chunk groups' partial merges meet in LDS; group 0 combines them in group order
+    __shared__ float4 s_acc[kSW][kPer][kR];
+    __shared__ float2 s_mden[kSW][kPer][kR];
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      s_acc[sg][pl][i] = acc[i];
+      s_mden[sg][pl][i] = float2{M[i], den[i]};
+    }
+    __syncthreads();
+    if (sg != 0) return;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      float Mt = M[i];
+#pragma unroll
+      for (int q = 1; q < kSW; ++q) Mt = fmaxf(Mt, s_mden[q][pl][i].x);
+      // group 0 always holds chunk 0, so Mt is finite for live rows; an empty group has
+      // M = -inf, den = 0 and O = 0, and weight 0
+      const float sc = fast_exp2(M[i] - Mt);
+      den[i] *= sc;
+      acc[i].x *= sc;
+      acc[i].y *= sc;
+      acc[i].z *= sc;
+      acc[i].w *= sc;
+#pragma unroll
+      for (int q = 1; q < kSW; ++q) {
+        const float2 md = s_mden[q][pl][i];
+        const float4 x = s_acc[q][pl][i];
+        const float w = fast_exp2(md.x - Mt);
+        den[i] += w * md.y;
+        acc[i].x += w * x.x;
+        acc[i].y += w * x.y;
+        acc[i].z += w * x.z;
+        acc[i].w += w * x.w;
+      }
+      M[i] = Mt;
+    }
   }
-  if (a.lse && d == 0) a.lse[orow] = (M + __log2f(den)) * kLn2;
+  if (!live) return;
+#pragma unroll
+  for (int i = 0; i < kR; ++i) {
+    const int r = r0 + i;
+    if (r >= a.GT) break;  // the second row of a pair may be padding (never written)
+    const float inv = 1.f / den[i];
+    const int t = r / a.G, head = kvh * a.G + r % a.G;
+    const size_t orow = ((size_t)b * a.T + t) * a.Hq + head;
+    E* o = reinterpret_cast<E*>(a.out) + orow * D;
+    if constexpr (kBF16) {
+      *reinterpret_cast<uint2*>(o + d) = uint2{pack_bf16x2(acc[i].x * inv, acc[i].y * inv),
+                                               pack_bf16x2(acc[i].z * inv, acc[i].w * inv)};
+    } else {
+      *reinterpret_cast<float4*>(o + d) =
+          float4{acc[i].x * inv, acc[i].y * inv, acc[i].z * inv, acc[i].w * inv};
+    }
+    if (a.lse && d == 0) a.lse[orow] = (M[i] + __log2f(den[i])) * kLn2;
+  }
 }
 
-template <typename E, int D>
+template <typename E, int D, int kBatch, int kSW>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
-  combine_group<E, D>(a, xcd_remap(blockIdx.x, a.B * a.Hkv * a.RB * combine_wgs_per_item<E, D>()));
+  combine_group<E, D, kBatch, kSW>(
+      a, xcd_remap(blockIdx.x, a.B * a.Hkv * a.RB * combine_wgs_per_item<E, D, kSW>()));
 }
 
 // ---- fused tail of a verification step -----------------------------------------------------
-// Workgroups [0, n_comb) merge split-K partials (as attn_combine); workgroup n_comb + b runs
-// the acceptance walk of sequence b on its first wavefront, then all four wavefronts copy the
-// accepted K/V rows of every KV head into the cache.  Used only when the tree K/V does not
-// overlap the cache, so rows are copied directly, without staging.
+// Workgroup b < B runs the acceptance walk of sequence b on its first wavefront, then all four
+// wavefronts copy the accepted K/V rows of every KV head into the cache; they come first so
+// they run under the merge.  Workgroups from n_acc (B rounded up to a multiple of the 8 XCDs,
+// so the merge keeps attn_combine's XCD order) merge split-K partials.  Used only when the
+// tree K/V does not overlap the cache, so rows are copied directly, without staging.
 struct TailArgs {
   const uint64_t* anc;
   const int32_t* draft;
@@ -1020,18 +1127,19 @@ struct TailArgs {
   char* vc;
   int32_t* cache_len_out;
   int32_t* status;
-  int n_comb, W, row_bytes;
+  int n_comb, n_acc, W, row_bytes;
 };
 
-template <typename E, int D>
+template <typename E, int D, int kBatch, int kSW>
 __global__ __launch_bounds__(256) void step_tail(AttnArgs a, TailArgs t) {
-  if ((int)blockIdx.x < t.n_comb) {
-    combine_group<E, D>(a, xcd_remap(blockIdx.x, t.n_comb));
+  if ((int)blockIdx.x >= t.n_acc) {
+    combine_group<E, D, kBatch, kSW>(a, xcd_remap(blockIdx.x - t.n_acc, t.n_comb));
     return;
   }
+  if ((int)blockIdx.x >= a.B) return;  // XCD alignment padding
   __shared__ int s_path[kMaxT];
   __shared__ int s_n;
-  const int b = blockIdx.x - t.n_comb, tid = threadIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x;
   const int L = a.cache_len[b];  // read before this workgroup writes cache_len_out[b]
   if (tid < 64) {
     const int n = accept_walk(b, a.T, t.W, t.anc, t.draft, t.target, t.accept_path, t.accept_len,
@@ -1120,10 +1228,15 @@ template <typename E, int D, bool kPaged = false>
 int launch_attn(const AttnArgs& a, hipStream_t stream) {
   const int rc = launch_main<E, D, false, kPaged>(a, stream);
   if (rc != TV_OK) return rc;
-  if (a.S > 1)
-    hipLaunchKernelGGL((attn_combine<E, D>),
-                       dim3(a.B * a.Hkv * a.RB * combine_wgs_per_item<E, D>()), dim3(256), 0,
-                       stream, a);
+  if (a.S > 1) {
+    const dim3 grid(combine_grid<E, D>(a.B * a.Hkv * a.RB, a.S)), block(256);
+    switch (combine_shape(a.S).batch * combine_shape(a.S).sw) {
+      case 2: hipLaunchKernelGGL((attn_combine<E, D, 2, 1>), grid, block, 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((attn_combine<E, D, 4, 1>), grid, block, 0, stream, a); break;
+      case 8: hipLaunchKernelGGL((attn_combine<E, D, 8, 1>), grid, block, 0, stream, a); break;
+      default: hipLaunchKernelGGL((attn_combine<E, D, 8, 4>), grid, block, 0, stream, a);
+    }
+  }
   return launch_status();
 }
 
@@ -1131,8 +1244,15 @@ template <typename E, int D>
 int launch_step(const AttnArgs& a, TailArgs t, hipStream_t stream) {
   const int rc = launch_main<E, D, true>(a, stream);
   if (rc != TV_OK) return rc;
-  t.n_comb = a.S > 1 ? a.B * a.Hkv * a.RB * combine_wgs_per_item<E, D>() : 0;
-  hipLaunchKernelGGL((step_tail<E, D>), dim3(t.n_comb + a.B), dim3(256), 0, stream, a, t);
+  t.n_comb = a.S > 1 ? combine_grid<E, D>(a.B * a.Hkv * a.RB, a.S) : 0;
+  t.n_acc = (a.B + 7) / 8 * 8;
+  const dim3 grid(t.n_acc + t.n_comb), block(256);
+  switch (combine_shape(a.S).batch * combine_shape(a.S).sw) {
+    case 2: hipLaunchKernelGGL((step_tail<E, D, 2, 1>), grid, block, 0, stream, a, t); break;
+    case 4: hipLaunchKernelGGL((step_tail<E, D, 4, 1>), grid, block, 0, stream, a, t); break;
+    case 8: hipLaunchKernelGGL((step_tail<E, D, 8, 1>), grid, block, 0, stream, a, t); break;
+    default: hipLaunchKernelGGL((step_tail<E, D, 8, 4>), grid, block, 0, stream, a, t);
+  }
   return launch_status();
 }
 
