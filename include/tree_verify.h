@@ -391,13 +391,16 @@ int eagle2_rerank(const int32_t* node_tok, const int32_t* node_parent, const flo
  * confidences feed eagle2_expand).  h, A, B and W are bfloat16 (16-bit words); results are
  * float32.  Which candidates and children are chosen is decided by float32 values computed in
  * a fixed order, so the results are bit-exact:
- *   - dot products over d (u = B h and the exact logits): 64 segments of d/64 consecutive
- *     elements, each a chain of fused multiply-adds in index order from 0, then the 64 segment
- *     sums combined pairwise, segment j with j^32, then j^16, ..., j^1;
+ *   - dot products over d (u = B h and the exact logits): 64 chains of fused multiply-adds
+ *     from 0, chain j over the elements 512 p + 8 j + e for p = 0 .. d/512 - 1 (outer) and
+ *     e = 0 .. 7 (inner), then the 64 chain sums combined pairwise, chain j with j^32, then
+ *     j^16, ..., j^1;
  *   - screening scores A[row] . u[m]: one chain of fused multiply-adds over the rank index in
  *     order from 0.
  * Values rank by their float order with -0 as +0; equal values go to the smaller row of A
  * (screening) or the smaller token (children).
+ * h, B, A, W and u are read 16 bytes at a time: each must be 16-byte aligned (as any device
+ * allocation is), else the call returns TV_ERR_INVALID_ARG.
  */
 
 /* lm_head_project — u [M, r] fp32 = B [r, d] h [M, d] (rows of h are hidden states).
@@ -426,7 +429,9 @@ int lm_head_rescore(const void* W, const void* h, const int32_t* cand, int M, in
  * each hidden state by exact logit, best first, out_tok [M, K] int32, and their confidences
  * out_conf [M, K] fp32, the softmax of the logits over all valid candidates of that hidden
  * state (fp32 sums; confidences agree with an fp64 evaluation to about 1e-6 relative).  With
- * fewer than K valid candidates the rest are token -1, confidence 0.
+ * fewer than K valid candidates the rest are token -1, confidence 0.  Every entry of cand is
+ * a candidate of its own: a token listed twice (lm_head_screen never does) can be chosen twice
+ * and counts twice in the softmax.
  * Limits: M >= 1, 1 <= C <= 8192, 1 <= K <= 64, V >= 1. */
 int lm_head_topk(const float* logits, const int32_t* cand, int M, int C, int K, int V,
                  int32_t* out_tok, float* out_conf, void* stream);

@@ -314,6 +314,19 @@ def test_lm_head_argument_errors(lib):
     bad = list(base)
     bad[3], bad[4] = 64, 512  # 64 chains x 512 ranks x 4 B of u exceeds 64 KB of LDS
     assert lib.lm_head_screen(*bad) == -1
+    # pointers read 16 bytes at a time must be 16-byte aligned
+    odd = ctypes.c_void_p(0x1004)
+    for i in (0, 1):
+        bad = list(base)
+        bad[i] = odd
+        assert lib.lm_head_screen(*bad) == -1, i
+    for i in (0, 1):
+        bad = [FAKE, FAKE, 10, 256, 4096, FAKE, None]
+        bad[i] = odd
+        assert lib.lm_head_project(*bad) == -1, i
+        bad = [FAKE, FAKE, FAKE, 10, 2004, 4096, 128256, FAKE, None, None]
+        bad[i] = odd
+        assert lib.lm_head_rescore(*bad) == -1, i
     # rescore: W, h, cand, M, C, d, V, logits, status, stream
     base = [FAKE, FAKE, FAKE, 10, 2004, 4096, 128256, FAKE, None, None]
     for i in (0, 1, 2, 7):

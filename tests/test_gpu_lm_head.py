@@ -162,3 +162,37 @@ def test_children_feed_the_expansion():
     tv.eagle2_expand(table, 2, tok, conf)
     torch.cuda.synchronize()
     assert to_host(table["status"])[0] == 0
+
+
+@pytest.mark.parametrize("C,K", [(40, 10), (700, 16), (2004, 10), (8192, 64)])
+def test_topk_repeated_tokens_and_ties(C, K):
+    """lm_head_topk alone, on candidate lists that repeat tokens (a token's copies carry the
+    same logit, as lm_head_rescore gives them) and hold many equal logits and invalid tokens.
+    Each copy is a candidate of its own, as in the oracle: a repeated token can be chosen once
+    per copy, and every copy counts in the softmax denominator."""
+    import tree_attention_verification_attn_amd as tv
+    from oracle import oracle as O
+
+    rng = np.random.default_rng(C + K)
+    M, V = 5, 3000
+    cand = rng.integers(0, V, (M, C)).astype(np.int32)
+    # repeated tokens: copy some entries onto others
+    src = rng.integers(0, C, (M, C // 4))
+    dst = rng.integers(0, C, (M, C // 4))
+    for m in range(M):
+        cand[m, dst[m]] = cand[m, src[m]]
+    cand[rng.random((M, C)) < 0.05] = -1
+    cand[0, :3] = [V, V + 5, -7]  # out of range: invalid, not flagged here
+    # logits on a coarse grid (many ties), one value per token
+    table = (rng.integers(-20, 20, (M, V + 10)) * 0.25).astype(np.float32)
+    logits = np.take_along_axis(table, np.clip(cand, 0, V + 9), axis=1).astype(np.float32)
+    print(f"[case] lm topk repeated tokens M={M} C={C} K={K}", flush=True)
+    tok, conf = tv.lm_head_topk(to_dev(logits), to_dev(cand), K, V)
+    torch.cuda.synchronize()
+    o_tok, o_conf = O.lm_topk(logits, cand, K, V)
+    g_tok, g_conf = to_host(tok), to_host(conf).astype(np.float64)
+    assert np.array_equal(g_tok, o_tok)
+    err = np.abs(g_conf - o_conf) / np.maximum(o_conf, 1e-30)
+    assert (err[o_conf > 0] <= TOL_CONF).all() and (g_conf[o_conf == 0] == 0).all(), err.max()
+    # repeated tokens do come out more than once
+    assert any(len(set(r[r >= 0].tolist())) < (r >= 0).sum() for r in g_tok)

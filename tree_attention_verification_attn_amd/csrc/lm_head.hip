@@ -21,9 +21,10 @@
 //   lm_project_kernel  one wavefront per (i, m), u[m, i] = B[i] . h[m]          (2 MB of B)
 //   lm_screen_kernel   one workgroup per tile of rows: the tile's A rows stream through LDS in
 //                      64-element slices (each row's 128 B XOR-swizzled by 16-byte piece so a
-//                      thread reading its row is free of bank conflicts), one thread per row
-//                      runs the M chains, then each wavefront picks its k best rows per hidden
-//                      state by wavefront maxima and the four wavefronts' picks are merged
+//                      thread reading its row is free of bank conflicts), a thread runs half of
+//                      the M chains for two rows (one LDS read of u serves both), then each
+//                      wavefront picks its k best rows per hidden state by wavefront maxima and
+//                      the two wavefronts' picks of each hidden state are merged
 //   lm_rescore_kernel  one wavefront per (m, c): W[cand] . h[m]                  (8 KB per row)
 //   lm_topk_kernel     one workgroup per hidden state: each wavefront takes K rounds of
 //                      wavefront maxima over its share of the candidates, the 4K picks are
@@ -53,13 +54,68 @@ __device__ inline float fkey_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
+// A 64-bit value moved by one DPP control, both halves alike; lanes without a source (or in
+// rows outside kRowMask) keep their own value.
+template <int kCtrl, int kRowMask>
+__device__ inline uint64_t dpp_u64(uint64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const int lo2 = __builtin_amdgcn_update_dpp(lo, lo, kCtrl, kRowMask, 0xf, false);
+  const int hi2 = __builtin_amdgcn_update_dpp(hi, hi, kCtrl, kRowMask, 0xf, false);
+  return ((uint64_t)(uint32_t)hi2 << 32) | (uint32_t)lo2;
+}
+
+// A 32-bit value moved by one DPP control (lanes without a source keep their own value).
+template <int kCtrl, int kRowMask>
+__device__ inline uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtrl, kRowMask, 0xf, false);
+}
+
+// Maximum of a 32-bit value over the wavefront, in every lane (the scan of wave_max_u64 below).
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0x111, 0xf>(v));  // row_shr:1
+  v = max(v, dpp_u32<0x112, 0xf>(v));  // row_shr:2
+  v = max(v, dpp_u32<0x114, 0xf>(v));  // row_shr:4
+  v = max(v, dpp_u32<0x118, 0xf>(v));  // row_shr:8
+  v = max(v, dpp_u32<0x142, 0xa>(v));  // row_bcast:15 into rows 1 and 3
+  v = max(v, dpp_u32<0x143, 0xc>(v));  // row_bcast:31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Maximum of a float over the wavefront, in every lane (by the order-preserving key).
+__device__ inline float wave_max_f32(float v) { return fkey_value(wave_max_u32(fkey(v))); }
+
+// Sum of a float over the wavefront, in every lane: the scan of wave_max_u32 with addition,
+// lanes without a source adding 0.
+template <int kCtrl, int kRowMask>
+__device__ inline float dpp_f32_or0(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xf,
+                                                    false));
+}
+__device__ inline float wave_sum_f32(float v) {
+  v += dpp_f32_or0<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_f32_or0<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_f32_or0<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_f32_or0<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_f32_or0<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f32_or0<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Maximum over the wavefront, returned to every lane.  An inclusive max scan runs within each
+// row of 16 lanes (row shifts by 1, 2, 4, 8), then across rows (lane 15 of a row broadcast to
+// the next row, then lane 31 to rows 2 and 3), so lane 63 ends with the maximum, which is read
+// out as a uniform value.  All steps stay in the vector ALU; no LDS round trips.
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint64_t o = shfl64(v, (int)(threadIdx.x & 63) ^ off);
-    v = o > v ? o : v;
-  }
-  return v;
+  auto mx = [](uint64_t a, uint64_t b) { return a > b ? a : b; };
+  v = mx(v, dpp_u64<0x111, 0xf>(v));  // row_shr:1
+  v = mx(v, dpp_u64<0x112, 0xf>(v));  // row_shr:2
+  v = mx(v, dpp_u64<0x114, 0xf>(v));  // row_shr:4
+  v = mx(v, dpp_u64<0x118, 0xf>(v));  // row_shr:8
+  v = mx(v, dpp_u64<0x142, 0xa>(v));  // row_bcast:15 into rows 1 and 3
+  v = mx(v, dpp_u64<0x143, 0xc>(v));  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // The fixed-order dot product of two bfloat16 rows of length d (d % 512 == 0), by the calling
@@ -99,8 +155,9 @@ __global__ __launch_bounds__(256) void lm_project_kernel(const uint16_t* __restr
 // Screening of tile blockIdx.x: rows r0 .. r0 + rows - 1 of A [n, r]; u [M, r] fp32 staged in
 // LDS (dynamic shared memory, kM * r floats, rows m >= M zero) and read with 16-byte reads
 // that every lane of a wavefront takes from the same address; k_tile candidates per hidden
-// state.  kM >= M is the number of chains each thread runs (a compile-time count so the
-// accumulators stay in registers; the chains of m >= M are discarded).
+// state.  kM >= M (even) is the number of chains a row runs, half of them in each half of the
+// workgroup (a compile-time count so the accumulators stay in registers; the chains of m >= M
+// are discarded).
 template <int kM>
 __global__ __launch_bounds__(256) void lm_screen_kernel(
     const uint16_t* __restrict__ A, const float* __restrict__ u, const int32_t* __restrict__ row_token,
@@ -114,8 +171,6 @@ __global__ __launch_bounds__(256) void lm_screen_kernel(
   const int r0 = t * tile;
   const int rows = min(tile, n - r0);
   const int n_slices = ceil_div(r, kLmSlice);
-
-  for (int x = tid; x < kM * r; x += 256) s_u[x] = x < M * r ? u[x] : 0.f;
 
   // slice loads: piece L = k * 256 + tid of the slice is (row L / 8, 16-byte piece L % 8);
   // pieces past the row's rank or past the tile read as zero and are never used
@@ -137,63 +192,109 @@ __global__ __launch_bounds__(256) void lm_screen_kernel(
     }
   };
 
-  float acc[kM];
+  // Thread (half, p) runs the chains of hidden states half * kH .. half * kH + kH - 1 for rows p
+  // and p + 128 of the tile: each u value read from LDS serves two rows.
+  constexpr int kH = kM / 2;
+  const int half = tid >> 7, p = tid & 127;
+  float acc[2][kH];
 #pragma unroll
-  for (int m = 0; m < kM; ++m) acc[m] = 0.f;
+  for (int i = 0; i < kH; ++i) acc[0][i] = acc[1][i] = 0.f;
 
   fetch(0);
+  // u into LDS while the first slice is in flight: float4 pieces (r % 8 == 0), every load of a
+  // pass issued before its stores
+  {
+    constexpr int kPass = 4;
+    const int n4 = kM * r / 4, m4 = M * r / 4;
+    for (int base = 0; base < n4; base += kPass * 256) {
+      float4 v[kPass];
+#pragma unroll
+      for (int i = 0; i < kPass; ++i) {
+        const int x = base + i * 256 + tid;
+        v[i] = x < m4 ? reinterpret_cast<const float4*>(u)[x] : float4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < kPass; ++i) {
+        const int x = base + i * 256 + tid;
+        if (x < n4) reinterpret_cast<float4*>(s_u)[x] = v[i];
+      }
+    }
+  }
   store(0);
   for (int sl = 0; sl < n_slices; ++sl) {
     if (sl + 1 < n_slices) fetch(sl + 1);
     __syncthreads();  // slice sl (and, the first time, u) is in LDS
-    const int q = tid;
     const int i_end = min(kLmSlice, r - sl * kLmSlice);
-    const float* us = s_u + sl * kLmSlice;
+    const float* us = s_u + (size_t)half * kH * r + sl * kLmSlice;
+    const char* sa = &s_a[sl & 1][0];
 #pragma unroll 2
     for (int v = 0; v < (i_end >> 3); ++v) {
-      const uint4 a = *reinterpret_cast<const uint4*>(&s_a[sl & 1][q * 128 + ((v ^ (q & 7)) << 4)]);
-      const float av[8] = {bf16_lo(a.x), bf16_hi(a.x), bf16_lo(a.y), bf16_hi(a.y),
-                           bf16_lo(a.z), bf16_hi(a.z), bf16_lo(a.w), bf16_hi(a.w)};
+      // rows p and p + 128 (same swizzle: (p + 128) & 7 == p & 7)
+      const int off = p * 128 + ((v ^ (p & 7)) << 4);
+      const uint4 a0 = *reinterpret_cast<const uint4*>(sa + off);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(sa + off + 128 * 128);
+      const float x0[8] = {bf16_lo(a0.x), bf16_hi(a0.x), bf16_lo(a0.y), bf16_hi(a0.y),
+                           bf16_lo(a0.z), bf16_hi(a0.z), bf16_lo(a0.w), bf16_hi(a0.w)};
+      const float x1[8] = {bf16_lo(a1.x), bf16_hi(a1.x), bf16_lo(a1.y), bf16_hi(a1.y),
+                           bf16_lo(a1.z), bf16_hi(a1.z), bf16_lo(a1.w), bf16_hi(a1.w)};
 #pragma unroll
-      for (int m = 0; m < kM; ++m) {
+      for (int i = 0; i < kH; ++i) {
         // u[m][8v .. 8v+7], the same for every lane
-        const float* um = us + m * r + v * 8;
+        const float* um = us + i * r + v * 8;
         const float4 u0 = *reinterpret_cast<const float4*>(um);
         const float4 u1 = *reinterpret_cast<const float4*>(um + 4);
-        float a_m = acc[m];
-        a_m = __builtin_fmaf(av[0], u0.x, a_m);
-        a_m = __builtin_fmaf(av[1], u0.y, a_m);
-        a_m = __builtin_fmaf(av[2], u0.z, a_m);
-        a_m = __builtin_fmaf(av[3], u0.w, a_m);
-        a_m = __builtin_fmaf(av[4], u1.x, a_m);
-        a_m = __builtin_fmaf(av[5], u1.y, a_m);
-        a_m = __builtin_fmaf(av[6], u1.z, a_m);
-        a_m = __builtin_fmaf(av[7], u1.w, a_m);
-        acc[m] = a_m;
+        const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        float c0 = acc[0][i], c1 = acc[1][i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          c0 = __builtin_fmaf(x0[e], uv[e], c0);
+          c1 = __builtin_fmaf(x1[e], uv[e], c1);
+        }
+        acc[0][i] = c0;
+        acc[1][i] = c1;
       }
     }
     if (sl + 1 < n_slices) store((sl + 1) & 1);
   }
   __syncthreads();  // every thread is done with the slices: their LDS holds the picks now
 
-  // each wavefront's k best rows per hidden state, then the merge of the four wavefronts
-  uint64_t* s_pick = reinterpret_cast<uint64_t*>(&s_a[0][0]);  // [M][4][k_tile]
-  const bool real = tid < rows;
+  // Each wavefront's k best rows per hidden state, then the merge of the two wavefronts of the
+  // half.  A wavefront holds rows q0 = 64 (wave & 1) + lane and q0 + 128, so among its rows
+  // with the best score the smallest row is the lowest lane holding it in its first row, else
+  // in its second: a 32-bit maximum and ballots replace a 64-bit (score, row) maximum.  The
+  // hidden states' reductions of one round are independent, so they interleave.
+  uint64_t* s_pick = reinterpret_cast<uint64_t*>(&s_a[0][0]);  // [M][2][k_tile]
+  const int wh = wave & 1;
+  const bool real0 = p < rows, real1 = p + 128 < rows;
+  uint64_t taken0 = 0, taken1 = 0;  // bit i: the row was picked for hidden state half*kH + i
+  for (int j = 0; j < k_tile; ++j) {
 #pragma unroll
-  for (int m = 0; m < kM; ++m) {
-    if (m < M) {
-      uint64_t key =
-          real ? ((uint64_t)fkey(acc[m]) << 32) | (0xffffffffu - (uint32_t)(r0 + tid)) : 0;
-      for (int j = 0; j < k_tile; ++j) {
-        const uint64_t best = wave_max_u64(key);
-        if (key == best) key = 0;  // keys of real rows are distinct
-        if (lane == 0) s_pick[(m * 4 + wave) * k_tile + j] = best;
+    for (int i = 0; i < kH; ++i) {
+      const int m = half * kH + i;
+      if (m < M) {
+        const bool open0 = real0 && !((taken0 >> i) & 1);
+        const bool open1 = real1 && !((taken1 >> i) & 1);
+        const uint32_t k0 = open0 ? fkey(acc[0][i]) : 0u, k1 = open1 ? fkey(acc[1][i]) : 0u;
+        const uint32_t best = wave_max_u32(max(k0, k1));
+        const uint64_t h0 = __ballot(open0 && k0 == best);
+        const uint64_t h1 = __ballot(open1 && k1 == best);
+        uint64_t pick = 0;  // none left: fewer real rows than picks
+        if (h0 | h1) {
+          const int w = __builtin_ctzll(h0 ? h0 : h1);
+          const int q = (h0 ? 0 : 128) + wh * 64 + w;
+          if (lane == w) {
+            if (h0) taken0 |= 1ull << i;
+            else taken1 |= 1ull << i;
+          }
+          pick = ((uint64_t)best << 32) | (0xffffffffu - (uint32_t)(r0 + q));
+        }
+        if (lane == 0) s_pick[(m * 2 + wh) * k_tile + j] = pick;
       }
     }
   }
   __syncthreads();
   const int C = ceil_div(n, tile) * k_tile;
-  const int per_m = 4 * k_tile;
+  const int per_m = 2 * k_tile;
   for (int x = tid; x < M * per_m; x += 256) {
     const int m = x / per_m, e = x - m * per_m;
     const uint64_t* pm = s_pick + m * per_m;
@@ -249,19 +350,18 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const float* __restrict__ 
   float mx = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
+    // token and logit loaded together (no load waits for the other)
     const int c = k * 256 + tid;
+    const int tok = c < C ? cm[c] : -1;
+    const float lv = c < C ? l[c] : 0.f;
     key[k] = 0;
-    if (c < C) {
-      const int tok = cm[c];
-      if (tok >= 0 && tok < V) {
-        key[k] = ((uint64_t)fkey(l[c]) << 32) | (0xffffffffu - (uint32_t)tok);
-        mx = fmaxf(mx, l[c]);
-      }
+    if (tok >= 0 && tok < V) {
+      key[k] = ((uint64_t)fkey(lv) << 32) | (0xffffffffu - (uint32_t)tok);
+      mx = fmaxf(mx, lv);
     }
   }
   // max and sum of exponentials over the valid candidates
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  mx = wave_max_f32(mx);
   if (lane == 0) s_f[wave] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(s_f[0], s_f[1]), fmaxf(s_f[2], s_f[3]));
@@ -270,25 +370,46 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const float* __restrict__ 
 #pragma unroll
   for (int k = 0; k < kPer; ++k)
     if (key[k]) z += expf(fkey_value((uint32_t)(key[k] >> 32)) - mx);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+  z = wave_sum_f32(z);
   if (lane == 0) s_f[wave] = z;
 
-  // this wavefront's K best
+  // this wavefront's K best: the best score by a 32-bit maximum; the token decides only
+  // between lanes holding equal scores (a 64-bit maximum over those lanes, rarely needed).
+  // Each round removes one copy of the best key (candidates may repeat a token): the first
+  // slot holding it in the lowest lane holding it.
   for (int j = 0; j < K; ++j) {
+    uint64_t mine = 0;  // this lane's best key (0: none)
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) mine = key[k] > mine ? key[k] : mine;
+    const uint32_t top = wave_max_u32((uint32_t)(mine >> 32));
+    const uint64_t holders = __ballot(mine != 0 && (uint32_t)(mine >> 32) == top);
     uint64_t best = 0;
+    if (holders) {
+      if ((holders & (holders - 1)) == 0) {
+        const int w = __builtin_ctzll(holders);
+        best = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), w) << 32) |
+               (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, w);
+      } else {
+        best = wave_max_u64((uint32_t)(mine >> 32) == top ? mine : 0);
+      }
+      const int owner = __builtin_ctzll(__ballot(mine == best));
+      if (lane == owner) {
+        bool done = false;
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) best = key[k] > best ? key[k] : best;
-    best = wave_max_u64(best);
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) key[k] = key[k] == best ? 0 : key[k];
+        for (int k = 0; k < kPer; ++k)
+          if (!done && key[k] == best) {
+            key[k] = 0;
+            done = true;
+          }
+      }
+    }
     if (lane == 0) s_pick[wave * K + j] = best;
   }
   __syncthreads();
   z = (s_f[0] + s_f[1]) + (s_f[2] + s_f[3]);
   for (int e = tid; e < 4 * K; e += 256) {
     const uint64_t me = s_pick[e];
-    int rank = 0;  // picks are distinct except 0 (none), which ranks by entry
+    int rank = 0;  // equal picks (a repeated token's copies, or 0 for none) rank by entry
     for (int o = 0; o < 4 * K; ++o) rank += s_pick[o] > me || (s_pick[o] == me && o < e);
     if (rank >= K) continue;
     const size_t o = (size_t)m * K + rank;
@@ -307,10 +428,12 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const float* __restrict__ 
 
 using namespace tv;
 
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 extern "C" int lm_head_project(const void* h, const void* B, int M, int r, int d, float* u,
                                void* stream) {
-  if (!h || !B || !u || M < 1 || M > kLmMaxM || r < 1 || d < 512 || d % 512 != 0 ||
-      (long long)M * r > (1 << 24))
+  if (!h || !B || !u || !aligned16(h) || !aligned16(B) || M < 1 || M > kLmMaxM || r < 1 ||
+      d < 512 || d % 512 != 0 || (long long)M * r > (1 << 24))
     return TV_ERR_INVALID_ARG;
   hipLaunchKernelGGL(lm_project_kernel, dim3(ceil_div(M * r, 4)), dim3(256), 0,
                      (hipStream_t)stream, (const uint16_t*)h, (const uint16_t*)B, M, r, d, u);
@@ -335,9 +458,9 @@ void launch_screen(const void* A, const float* u, const int32_t* row_token, int 
 extern "C" int lm_head_screen(const void* A, const float* u, const int32_t* row_token, int M,
                               int r, int n, int tile, int k_tile, int32_t* cand, float* cand_score,
                               void* stream) {
-  if (!A || !u || !row_token || !cand || !cand_score || M < 1 || M > kLmMaxM || r < 8 ||
-      r % 8 != 0 || n < 1 || tile < 1 || tile > kLmMaxTile || k_tile < 1 ||
-      k_tile > kLmMaxKTile || (long long)ceil_div(n, tile) * k_tile * M >= (1LL << 31))
+  if (!A || !u || !row_token || !cand || !cand_score || !aligned16(A) || !aligned16(u) || M < 1 ||
+      M > kLmMaxM || r < 8 || r % 8 != 0 || n < 1 || tile < 1 || tile > kLmMaxTile ||
+      k_tile < 1 || k_tile > kLmMaxKTile || (long long)ceil_div(n, tile) * k_tile * M >= (1LL << 31))
     return TV_ERR_INVALID_ARG;
   int kM = kLmMaxM;
   for (int c : kScreenM)
@@ -365,8 +488,8 @@ extern "C" int lm_head_screen(const void* A, const float* u, const int32_t* row_
 
 extern "C" int lm_head_rescore(const void* W, const void* h, const int32_t* cand, int M, int C,
                                int d, int V, float* logits, int32_t* status, void* stream) {
-  if (!W || !h || !cand || !logits || M < 1 || M > kLmMaxM || C < 1 || V < 1 || d < 512 ||
-      d % 512 != 0 || (long long)M * C >= (1LL << 31))
+  if (!W || !h || !cand || !logits || !aligned16(W) || !aligned16(h) || M < 1 || M > kLmMaxM ||
+      C < 1 || V < 1 || d < 512 || d % 512 != 0 || (long long)M * C >= (1LL << 31))
     return TV_ERR_INVALID_ARG;
   hipLaunchKernelGGL(lm_rescore_kernel, dim3(ceil_div(M * C, 4)), dim3(256), 0,
                      (hipStream_t)stream, (const uint16_t*)W, (const uint16_t*)h, cand, M, C, d, V,
