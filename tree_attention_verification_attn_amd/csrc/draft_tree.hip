@@ -12,8 +12,9 @@
 //     the parent's flattened index, then node id), ready for tree_build_mask.  One workgroup
 //     of 1024 threads per sequence: a radix select over the 48-bit keys
 //     (value bits << 16 | 0xFFFF - id), six 8-bit passes with an LDS histogram and a wavefront
-//     suffix scan, finds the T-th best key; the kept nodes are sorted by id, their depths come
-//     from pointer jumping over the kept list, and the levels are flattened one after another.
+//     suffix scan, finds the T-th best key; then wavefront 0 alone sorts the kept nodes by id,
+//     finds their depths by pointer jumping over the kept list and flattens the levels one
+//     after another, without workgroup barriers.
 //
 // Node ids: the root is node 0; child c of frontier slot r of level l is node
 // n_l + r * branch + c, with n_l the nodes of the levels before l, so ids grow with depth and
@@ -96,16 +97,43 @@ __global__ __launch_bounds__(kExpandMax) void expand_kernel(
   if (bits) atomicOr(status + b, bits);
 }
 
-// Reranking and flattening of sequence blockIdx.x's table of n nodes (row stride n_max).
+// Inclusive prefix sum over the wavefront (DPP row shifts, then row broadcasts; lanes without a
+// source add 0), in every lane.
+template <int kCtrl, int kRowMask>
+__device__ inline int dpp_i32_or0(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, kCtrl, kRowMask, 0xf, false);
+}
+__device__ inline int wave_prefix_sum(int v) {
+  v += dpp_i32_or0<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_i32_or0<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_i32_or0<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_i32_or0<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_i32_or0<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_i32_or0<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Orders the LDS accesses of one wavefront around it: a wavefront's LDS operations complete in
+// issue order, so after this its lanes see each other's earlier writes.
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Reranking and flattening of sequence blockIdx.x's table of n nodes (row stride n_max).  All
+// 1024 threads stage the table and run the radix select; the kept nodes (at most 128) are then
+// sorted, linked and flattened by wavefront 0 alone, two nodes per lane, with no workgroup
+// barrier.
 __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
     const int32_t* __restrict__ node_tok, const int32_t* __restrict__ node_parent,
     const float* __restrict__ node_value, int n, int n_max, int T, int32_t* __restrict__ parent_out,
     int32_t* __restrict__ tok_out, int32_t* __restrict__ depth_out, int32_t* __restrict__ node_out,
     int32_t* __restrict__ status) {
   __shared__ uint32_t s_key[kRerankMaxNodes];  // rank_value bits of every node
-  __shared__ int s_hist[256];
+  __shared__ int32_t s_par[kRerankMaxNodes];   // every node's parent
+  __shared__ int s_hist[2][256];               // one pass counts while the other is cleared
   __shared__ int s_sel[2];  // digit of the pass, count still to take at or below it
-  __shared__ int s_cnt, s_dmax;
+  __shared__ int s_cnt;
   __shared__ __attribute__((aligned(16))) int s_kept[kMaxT];
   __shared__ __attribute__((aligned(16))) int s_dep[kMaxT];
   __shared__ __attribute__((aligned(16))) uint32_t s_k[kMaxT];  // sort keys of one level
@@ -115,18 +143,18 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
   const size_t orow = (size_t)b * T;
   const int T4 = (T + 3) & ~3;  // lists padded to whole 16-byte reads
 
-  for (int i = tid; i < n; i += kRerankThreads)
+  for (int i = tid; i < n; i += kRerankThreads) {
     s_key[i] = __float_as_uint(rank_value(node_value[row + i]));
-  if (tid == 0) {
-    s_cnt = 0;
-    s_dmax = 0;
+    s_par[i] = node_parent[row + i];
   }
+  if (tid < 512) (&s_hist[0][0])[tid] = 0;
+  if (tid == 0) s_cnt = 0;
   __syncthreads();
   // a tree whose values never grow from parent to child: then a parent outranks its children
   // and the kept set is closed under parents
   int bad = 0;
   for (int i = tid; i < n; i += kRerankThreads) {
-    const int p = node_parent[row + i];
+    const int p = s_par[i];
     bad |= i == 0 ? p != -1 : (p < 0 || p >= i || s_key[i] > s_key[p]);
   }
   if (__syncthreads_or(bad)) {
@@ -148,26 +176,21 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
   int need = T;
   for (int pass = 0; pass < 6; ++pass) {
     const int shift = 40 - 8 * pass;
-    if (tid < 256) s_hist[tid] = 0;
-    __syncthreads();
+    int* hist = s_hist[pass & 1];
     for (int i = tid; i < n; i += kRerankThreads) {
       const uint64_t key = key48(i);
       if ((key >> (shift + 8)) == (prefix >> (shift + 8)))
-        atomicAdd(&s_hist[(int)(key >> shift) & 255], 1);
+        atomicAdd(&hist[(int)(key >> shift) & 255], 1);
     }
     __syncthreads();
     if (wave == 0) {
-      // lane l holds bins 4l .. 4l+3; S = keys in bins of lanes >= l (a suffix scan)
+      // lane l holds bins 4l .. 4l+3; S = keys in bins of lanes >= l (a suffix sum)
       int h[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) h[j] = s_hist[4 * lane + j];
+      for (int j = 0; j < 4; ++j) h[j] = hist[4 * lane + j];
       const int mine = h[0] + h[1] + h[2] + h[3];
-      int S = mine;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_down(S, off, 64);
-        if (lane + off < 64) S += o;
-      }
+      const int P = wave_prefix_sum(mine);
+      const int S = __builtin_amdgcn_readlane(P, 63) - P + mine;
       const int above = S - mine;
       if (above < need && need <= S) {  // exactly one lane
         int acc = above, d = 4 * lane;
@@ -181,6 +204,8 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
         s_sel[0] = d;
         s_sel[1] = need - acc;
       }
+    } else if (wave >= 4 && wave < 8) {
+      s_hist[(pass + 1) & 1][tid - 256] = 0;  // the next pass's histogram (read last pass)
     }
     __syncthreads();
     prefix |= (uint64_t)s_sel[0] << shift;
@@ -188,106 +213,145 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
   }
   // keys are distinct, so exactly T nodes have a key at or above the T-th best
 
-  // ---- kept nodes in id order, parents, depths ---------------------------------------------
   for (int i = tid; i < n; i += kRerankThreads)
     if (key48(i) >= prefix) {
       const int slot = atomicAdd(&s_cnt, 1);
       if (slot < kMaxT) s_kept[slot] = i;
     }
-  if (tid >= T && tid < T4) {
-    s_kept[tid] = 0x7fffffff;  // padding: after every id, deeper than every node
-    s_dep[tid] = 0x7fffffff;
-  }
   __syncthreads();
-  if (tid < T) {
-    const int u = s_kept[tid];
-    const int4* sk = reinterpret_cast<const int4*>(s_kept);
-    int r = 0;
+  if (wave != 0) return;
+
+  // ---- wavefront 0: kept nodes in id order, parents, depths, level order --------------------
+  // lane l handles list positions l and l + 64
+  if (lane < T4 - T) {
+    s_kept[T + lane] = 0x7fffffff;  // padding: after every id, deeper than every node
+    s_dep[T + lane] = 0x7fffffff;
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = lane + 64 * h;
+    if (t < T) {
+      const int u = s_kept[t];
+      const int4* sk = reinterpret_cast<const int4*>(s_kept);
+      int r = 0;
 #pragma unroll 4
-    for (int q = 0; q < T4 >> 2; ++q) {
-      const int4 w = sk[q];
-      r += (w.x < u) + (w.y < u) + (w.z < u) + (w.w < u);
-    }
-    s_id[r] = u;
-  }
-  __syncthreads();
-  if (tid < T) {
-    // position of the parent in the id-ordered list (node 0, the best node, is at position 0)
-    int pos = -1;
-    if (tid > 0) {
-      const int pu = node_parent[row + s_id[tid]];
-      int lo = 0, hi = tid - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (s_id[mid] < pu) lo = mid + 1;
-        else hi = mid;
+      for (int q = 0; q < T4 >> 2; ++q) {
+        const int4 w = sk[q];
+        r += (w.x < u) + (w.y < u) + (w.z < u) + (w.w < u);
       }
-      pos = lo;
+      s_id[r] = u;
     }
-    s_lp[tid] = pos;
-    s_ptr[tid] = pos;
-    s_dep[tid] = pos < 0 ? 0 : 1;
-    s_flat[tid] = -1;
+  }
+  wave_lds_sync();
+  int tok[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = lane + 64 * h;
+    tok[h] = 0;
+    if (t < T) {
+      const int u = s_id[t];
+      tok[h] = node_tok[row + u];  // used at the end; the load runs under the work below
+      // position of the parent in the id-ordered list (node 0, the best node, is at position 0)
+      int pos = -1;
+      if (t > 0) {
+        const int pu = s_par[u];
+        int lo = 0, hi = t - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_id[mid] < pu) lo = mid + 1;
+          else hi = mid;
+        }
+        pos = lo;
+      }
+      s_lp[t] = pos;
+      s_ptr[t] = pos;
+      s_dep[t] = pos < 0 ? 0 : 1;
+    }
   }
   // pointer jumping: s_dep is the distance to s_ptr, which doubles every round
   for (int span = 1; span < T; span <<= 1) {
-    __syncthreads();
-    int nd = 0, np = -1;
-    if (tid < T) {
-      const int p = s_ptr[tid];
-      nd = s_dep[tid] + (p >= 0 ? s_dep[p] : 0);
-      np = p >= 0 ? s_ptr[p] : -1;
+    wave_lds_sync();
+    int nd[2] = {0, 0}, np[2] = {-1, -1};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = lane + 64 * h;
+      if (t < T) {
+        const int p = s_ptr[t];
+        nd[h] = s_dep[t] + (p >= 0 ? s_dep[p] : 0);
+        np[h] = p >= 0 ? s_ptr[p] : -1;
+      }
     }
-    __syncthreads();
-    if (tid < T) {
-      s_dep[tid] = nd;
-      s_ptr[tid] = np;
+    wave_lds_sync();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = lane + 64 * h;
+      if (t < T) {
+        s_dep[t] = nd[h];
+        s_ptr[t] = np[h];
+      }
     }
   }
-  __syncthreads();
-  int dep = 0, off = 0;  // off: kept nodes shallower than this one
-  if (tid < T) {
-    dep = s_dep[tid];
-    atomicMax(&s_dmax, dep);
-    const int4* sd = reinterpret_cast<const int4*>(s_dep);
+  wave_lds_sync();
+  int dep[2] = {0, 0}, off[2] = {0, 0};  // off: kept nodes shallower than this one
+  int dmax = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = lane + 64 * h;
+    if (t < T) {
+      dep[h] = s_dep[t];
+      dmax = max(dmax, dep[h]);
+      const int4* sd = reinterpret_cast<const int4*>(s_dep);
 #pragma unroll 4
-    for (int q = 0; q < T4 >> 2; ++q) {
-      const int4 w = sd[q];
-      off += (w.x < dep) + (w.y < dep) + (w.z < dep) + (w.w < dep);
+      for (int q = 0; q < T4 >> 2; ++q) {
+        const int4 w = sd[q];
+        off[h] += (w.x < dep[h]) + (w.y < dep[h]) + (w.z < dep[h]) + (w.w < dep[h]);
+      }
     }
   }
-  __syncthreads();
-  const int dmax = s_dmax;
+  dmax = __reduce_max_sync(~0ull, dmax);
 
   // ---- flatten one level at a time: by the parent's flattened index, then by id --------------
   // A node of level d sorts by the key (parent's flattened index << 16 | position in id order);
   // the other levels' entries hold the largest key.
   for (int d = 0; d <= dmax; ++d) {
-    if (tid < T4) {
-      uint32_t key = 0xffffffffu;
-      if (tid < T && dep == d) key = ((uint32_t)(d == 0 ? 0 : s_flat[s_lp[tid]]) << 16) | tid;
-      s_k[tid] = key;
-    }
-    __syncthreads();
-    if (tid < T && dep == d) {
-      const uint32_t mine = s_k[tid];
-      const uint4* sk = reinterpret_cast<const uint4*>(s_k);
-      int r = 0;
-#pragma unroll 4
-      for (int q = 0; q < T4 >> 2; ++q) {
-        const uint4 w = sk[q];
-        r += (w.x < mine) + (w.y < mine) + (w.z < mine) + (w.w < mine);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = lane + 64 * h;
+      if (t < T4) {
+        uint32_t key = 0xffffffffu;
+        if (t < T && dep[h] == d) key = ((uint32_t)(d == 0 ? 0 : s_flat[s_lp[t]]) << 16) | t;
+        s_k[t] = key;
       }
-      s_flat[tid] = off + r;
     }
-    __syncthreads();
+    wave_lds_sync();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int t = lane + 64 * h;
+      if (t < T && dep[h] == d) {
+        const uint32_t mine = s_k[t];
+        const uint4* sk = reinterpret_cast<const uint4*>(s_k);
+        int r = 0;
+#pragma unroll 4
+        for (int q = 0; q < T4 >> 2; ++q) {
+          const uint4 w = sk[q];
+          r += (w.x < mine) + (w.y < mine) + (w.z < mine) + (w.w < mine);
+        }
+        s_flat[t] = off[h] + r;
+      }
+    }
+    wave_lds_sync();
   }
-  if (tid < T) {
-    const int f = s_flat[tid], u = s_id[tid];
-    parent_out[orow + f] = s_lp[tid] < 0 ? -1 : s_flat[s_lp[tid]];
-    tok_out[orow + f] = node_tok[row + u];
-    depth_out[orow + f] = dep;
-    node_out[orow + f] = u;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int t = lane + 64 * h;
+    if (t < T) {
+      const int f = s_flat[t];
+      parent_out[orow + f] = s_lp[t] < 0 ? -1 : s_flat[s_lp[t]];
+      tok_out[orow + f] = tok[h];
+      depth_out[orow + f] = dep[h];
+      node_out[orow + f] = s_id[t];
+    }
   }
 }
 
