@@ -136,8 +136,10 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
   __shared__ int s_cnt;
   __shared__ __attribute__((aligned(16))) int s_kept[kMaxT];
   __shared__ __attribute__((aligned(16))) int s_dep[kMaxT];
-  __shared__ __attribute__((aligned(16))) uint32_t s_k[kMaxT];  // sort keys of one level
-  __shared__ int s_id[kMaxT], s_lp[kMaxT], s_ptr[kMaxT], s_flat[kMaxT];
+  __shared__ __attribute__((aligned(16))) int s_lp[kMaxT];
+  __shared__ int s_id[kMaxT], s_ptr[kMaxT], s_flat[kMaxT];
+  __shared__ int s_cc[kMaxT];                         // children of list position t
+  __shared__ __attribute__((aligned(8))) int s_A[kMaxT], s_E[kMaxT];  // by level-order index
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t row = (size_t)b * n_max;
   const size_t orow = (size_t)b * T;
@@ -224,8 +226,8 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
   // ---- wavefront 0: kept nodes in id order, parents, depths, level order --------------------
   // lane l handles list positions l and l + 64
   if (lane < T4 - T) {
-    s_kept[T + lane] = 0x7fffffff;  // padding: after every id, deeper than every node
-    s_dep[T + lane] = 0x7fffffff;
+    s_kept[T + lane] = 0x7fffffff;  // padding: after every id
+    s_lp[T + lane] = -2;            // padding: nobody's sibling
   }
   wave_lds_sync();
 #pragma unroll
@@ -267,6 +269,7 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
       s_lp[t] = pos;
       s_ptr[t] = pos;
       s_dep[t] = pos < 0 ? 0 : 1;
+      s_cc[t] = 0;
     }
   }
   // pointer jumping: s_dep is the distance to s_ptr, which doubles every round
@@ -293,7 +296,8 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
     }
   }
   wave_lds_sync();
-  int dep[2] = {0, 0}, off[2] = {0, 0};  // off: kept nodes shallower than this one
+  // depths, children counts, and each node's rank among its siblings in id order
+  int dep[2] = {0, 0}, lp[2] = {-1, -1}, sib[2] = {0, 0};
   int dmax = 0;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -301,53 +305,54 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
     if (t < T) {
       dep[h] = s_dep[t];
       dmax = max(dmax, dep[h]);
-      const int4* sd = reinterpret_cast<const int4*>(s_dep);
+      lp[h] = s_lp[t];
+      if (lp[h] >= 0) atomicAdd(&s_cc[lp[h]], 1);
+      const int4* sl = reinterpret_cast<const int4*>(s_lp);
 #pragma unroll 4
       for (int q = 0; q < T4 >> 2; ++q) {
-        const int4 w = sd[q];
-        off[h] += (w.x < dep[h]) + (w.y < dep[h]) + (w.z < dep[h]) + (w.w < dep[h]);
+        const int4 w = sl[q];
+        sib[h] += (w.x == lp[h] && 4 * q < t) + (w.y == lp[h] && 4 * q + 1 < t) +
+                  (w.z == lp[h] && 4 * q + 2 < t) + (w.w == lp[h] && 4 * q + 3 < t);
       }
     }
   }
   dmax = __reduce_max_sync(~0ull, dmax);
 
-  // ---- flatten one level at a time: by the parent's flattened index, then by id --------------
-  // A node of level d sorts by the key (parent's flattened index << 16 | position in id order);
-  // the other levels' entries hold the largest key.
-  for (int d = 0; d <= dmax; ++d) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = lane + 64 * h;
-      if (t < T4) {
-        uint32_t key = 0xffffffffu;
-        if (t < T && dep[h] == d) key = ((uint32_t)(d == 0 ? 0 : s_flat[s_lp[t]]) << 16) | t;
-        s_k[t] = key;
-      }
-    }
+  // ---- level order (depth, then the parent's index in it, then id) ---------------------------
+  // In that order a node's children follow every child of the nodes placed before it, so a
+  // child at depth d takes index 1 + (children of the nodes before its parent) + (its rank
+  // among its siblings).  Level by level: s_A holds each placed node's children count at its
+  // index, s_E the exclusive prefix sums of s_A (a wavefront scan over index pairs).
+  wave_lds_sync();
+  *reinterpret_cast<int2*>(&s_A[2 * lane]) = int2{0, 0};
+  wave_lds_sync();
+  if (lane == 0) {
+    s_flat[0] = 0;  // the root
+    s_A[0] = s_cc[0];
+  }
+  for (int d = 1; d <= dmax; ++d) {
+    wave_lds_sync();
+    const int2 a = *reinterpret_cast<const int2*>(&s_A[2 * lane]);
+    const int e0 = wave_prefix_sum(a.x + a.y) - (a.x + a.y);
+    *reinterpret_cast<int2*>(&s_E[2 * lane]) = int2{e0, e0 + a.x};
     wave_lds_sync();
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int t = lane + 64 * h;
       if (t < T && dep[h] == d) {
-        const uint32_t mine = s_k[t];
-        const uint4* sk = reinterpret_cast<const uint4*>(s_k);
-        int r = 0;
-#pragma unroll 4
-        for (int q = 0; q < T4 >> 2; ++q) {
-          const uint4 w = sk[q];
-          r += (w.x < mine) + (w.y < mine) + (w.z < mine) + (w.w < mine);
-        }
-        s_flat[t] = off[h] + r;
+        const int f = 1 + s_E[s_flat[lp[h]]] + sib[h];
+        s_flat[t] = f;
+        s_A[f] = s_cc[t];
       }
     }
-    wave_lds_sync();
   }
+  wave_lds_sync();
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int t = lane + 64 * h;
     if (t < T) {
       const int f = s_flat[t];
-      parent_out[orow + f] = s_lp[t] < 0 ? -1 : s_flat[s_lp[t]];
+      parent_out[orow + f] = lp[h] < 0 ? -1 : s_flat[lp[h]];
       tok_out[orow + f] = tok[h];
       depth_out[orow + f] = dep[h];
       node_out[orow + f] = s_id[t];
