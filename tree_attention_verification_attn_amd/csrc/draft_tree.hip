@@ -5,8 +5,9 @@
 //     drafter proposed for it.  A child's global acceptance value is its parent's value times
 //     its confidence (the product of the confidences on its root path, in float32), and the
 //     frontier of the new level is its k best children, best first.  One workgroup per
-//     sequence, one thread per child; a child's rank is the number of this level's children
-//     that outrank it (larger value, or equal value and smaller node id), counted over LDS.
+//     sequence; a child's rank is the number of this level's children that outrank it (larger
+//     value, or equal value and smaller node id), counted over LDS by up to four threads, each
+//     over a quarter of the values.
 //   * Reranking and flattening (section 7.2), one launch after the last level: the T best nodes
 //     of the whole table are kept, and the kept tree is flattened in level order (depth, then
 //     the parent's flattened index, then node id), ready for tree_build_mask.  One workgroup
@@ -45,14 +46,19 @@ __global__ __launch_bounds__(kExpandMax) void expand_kernel(
     int n_max, int32_t* __restrict__ node_tok, int32_t* __restrict__ node_parent,
     float* __restrict__ node_value, int32_t* __restrict__ frontier, int32_t* __restrict__ status) {
   __shared__ __attribute__((aligned(16))) float s_val[kExpandMax];
+  __shared__ int s_part[kExpandMax];  // partial ranks, [group][child]
   const int b = blockIdx.x, tid = threadIdx.x;
   const int n = F * branch;
   const int n_front = min(k, n);
+  // npad threads per group (one per child); G groups split each child's rank count
+  const int npad = (max(n, k) + 63) & ~63;
+  const int G = blockDim.x / npad;
+  const int g = tid / npad, c = tid - g * npad;
   const size_t row = (size_t)b * n_max;
   int bits = 0;
   float v = 0.f;
-  if (tid < n) {
-    const int r = tid / branch, c = tid - r * branch;
+  if (g == 0 && c < n) {
+    const int r = c / branch, cc = c - r * branch;
     int pid = 0;
     float pv = 1.f;
     bool ok = true;
@@ -62,39 +68,51 @@ __global__ __launch_bounds__(kExpandMax) void expand_kernel(
       pv = ok ? node_value[row + pid] : 0.f;
       if (!ok) bits |= TV_BAD_TREE;
     }
-    const size_t src = ((size_t)b * k + r) * branch + c;
+    const size_t src = ((size_t)b * k + r) * branch + cc;
     const float conf = child_conf[src];
     if (!(conf >= 0.f && conf <= 1.f)) bits |= TV_BAD_CONF;
     v = rank_value(pv * as_prob(conf));
-    node_tok[row + base + tid] = child_tok[src];
-    node_parent[row + base + tid] = ok ? pid : -1;
-    node_value[row + base + tid] = v;
-    s_val[tid] = v;
+    node_tok[row + base + c] = child_tok[src];
+    node_parent[row + base + c] = ok ? pid : -1;
+    node_value[row + base + c] = v;
+    s_val[c] = v;
   }
-  if (tid >= n && tid < ((n + 3) & ~3)) s_val[tid] = -1.f;  // padding: below every value
+  if (g == 0 && c >= n && c < ((n + 3) & ~3)) s_val[c] = -1.f;  // padding: below every value
   if (level == 1 && tid == 0) {
     node_tok[row] = root_tok[b];
     node_parent[row] = -1;
     node_value[row] = 1.f;
   }
   __syncthreads();  // every parent entry of the frontier has been read
-  if (tid < n) {
+  // group g counts, for child c, the outranking children among words [q0, q1) of the values
+  int rank = 0;
+  if (c < n) {
+    if (g > 0) v = s_val[c];
+    const int Q = (n + 3) >> 2, Qg = (Q + G - 1) / G;
+    const int q0 = g * Qg, q1 = min(Q, q0 + Qg);
     // four values per LDS read (every lane reads the same address), several reads in flight
     const float4* sv = reinterpret_cast<const float4*>(s_val);
-    int rank = 0;
 #pragma unroll 4
-    for (int q = 0; q < (n + 3) >> 2; ++q) {
+    for (int q = q0; q < q1; ++q) {
       const float4 w = sv[q];
       const int j = 4 * q;
-      rank += (w.x > v) || (w.x == v && j < tid);
-      rank += (w.y > v) || (w.y == v && j + 1 < tid);
-      rank += (w.z > v) || (w.z == v && j + 2 < tid);
-      rank += (w.w > v) || (w.w == v && j + 3 < tid);
+      rank += (w.x > v) || (w.x == v && j < c);
+      rank += (w.y > v) || (w.y == v && j + 1 < c);
+      rank += (w.z > v) || (w.z == v && j + 2 < c);
+      rank += (w.w > v) || (w.w == v && j + 3 < c);
     }
-    if (rank < n_front) frontier[(size_t)b * k + rank] = base + tid;
   }
-  if (tid >= n_front && tid < k) frontier[(size_t)b * k + tid] = -1;
-  if (bits) atomicOr(status + b, bits);
+  if (G > 1) {
+    s_part[tid] = rank;
+    __syncthreads();
+    if (g == 0 && c < n)
+      for (int q = 1; q < G; ++q) rank += s_part[q * npad + c];
+  }
+  if (g == 0) {
+    if (c < n && rank < n_front) frontier[(size_t)b * k + rank] = base + c;
+    if (c >= n_front && c < k) frontier[(size_t)b * k + c] = -1;
+    if (bits) atomicOr(status + b, bits);
+  }
 }
 
 // Inclusive prefix sum over the wavefront (DPP row shifts, then row broadcasts; lanes without a
@@ -394,7 +412,9 @@ extern "C" int eagle2_expand(const int32_t* root_tok, const int32_t* child_tok,
   const long long base = node_count(level - 1, k, branch, &F);
   const long long prev_lo = level == 1 ? 0 : node_count(level - 2, k, branch, nullptr);
   if (base < 0 || base + (long long)F * branch > n_max) return TV_ERR_INVALID_ARG;
-  const int threads = ceil_div(max(F * branch, k), 64) * 64;
+  // one thread per child, in up to four groups that split the rank counts
+  const int npad = ceil_div(max(F * branch, k), 64) * 64;
+  const int threads = npad * (npad <= kExpandMax / 4 ? 4 : npad <= kExpandMax / 2 ? 2 : 1);
   hipLaunchKernelGGL(expand_kernel, dim3(B), dim3(threads), 0, (hipStream_t)stream, level,
                      root_tok, child_tok, child_conf, k, branch, F, (int)prev_lo, (int)base, n_max,
                      node_tok, node_parent, node_value, frontier, status);
