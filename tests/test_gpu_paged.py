@@ -99,6 +99,53 @@ def test_paged_equals_dense_bitwise():
         assert torch.equal(lse, lse_d)
 
 
+def test_paged_pool_over_4gb():
+    """A bf16 pool larger than 4 GB per cache is addressed with 64-bit pointers (smaller pools
+    take 32-bit offsets from the pool's base).  The workload's rows sit past the first 4 GB of
+    an otherwise untouched pool; the result must equal the oracle's on the compact layout and,
+    bit for bit, the same rows in a small pool."""
+    import tree_attention_verification_attn_amd as tv
+    from oracle import oracle as O
+
+    w = make_workload("batch32_L512-4096_T60", B=3, T=40, L=(20, 700), Hq=8, Hkv=2, D=128,
+                      parent_kind="random", extra_seed=29)
+    P = 16
+    pl = make_paged(w, P, seed=13)
+    slot_bytes = w.Hkv * w.D * 2
+    shift_pages = -(-(1 << 32) // (slot_bytes * P))  # rows start past 4 GB
+    shift = shift_pages * P
+    big_slots = shift + pl.num_slots
+    assert big_slots * slot_bytes > (1 << 32)
+    print(f"[case] paged pool over 4 GB: {big_slots} slots, {2 * big_slots * slot_bytes / 2**30:.1f} GiB",
+          flush=True)
+    g = upload(w)
+    kb = torch.empty((big_slots, w.Hkv, w.D), dtype=torch.bfloat16, device="cuda")
+    vb = torch.empty_like(kb)
+    kb[shift:] = to_dev(pl.k_pool)
+    vb[shift:] = to_dev(pl.v_pool)
+    table = np.where(pl.block_table >= 0, pl.block_table + shift_pages, -1).astype(np.int32)
+    tslot = (pl.tree_slot + shift).astype(np.int32)
+    anc, status = tv.tree_build_mask(g["parent"])
+    out, lse = tv.tree_verify_attn_paged(g["q"], kb, vb, to_dev(table), P, g["cache_len"],
+                                         to_dev(tslot), anc, status=status, split_keys=128)
+    # the same rows in a compact pool (32-bit offsets)
+    p = _paged_dev(pl)
+    out_s, lse_s = tv.tree_verify_attn_paged(g["q"], p["k_pool"], p["v_pool"], p["table"], P,
+                                             g["cache_len"], p["tree_slot"], anc, split_keys=128)
+    torch.cuda.synchronize()
+    assert (to_host(status) == 0).all(), to_host(status)
+    assert torch.equal(out.view(torch.int16), out_s.view(torch.int16))
+    assert torch.equal(lse, lse_s)
+    o_out, o_lse = O.paged_attention(w.q, pl.k_pool, pl.v_pool, pl.block_table, P, w.cache_len,
+                                     pl.tree_slot, w.parent)
+    err = float(np.abs(as_f64(to_host(out)) - o_out).max())
+    lerr = float(np.abs(to_host(lse).astype(np.float64) - o_lse).max())
+    print(f"       max-abs err {err:.3e}  lse err {lerr:.3e}", flush=True)
+    assert err <= TOL_OUT["bf16"] and lerr <= TOL_LSE["bf16"], (err, lerr)
+    del kb, vb
+    torch.cuda.empty_cache()
+
+
 def test_paged_bad_entries_flagged_not_read():
     import tree_attention_verification_attn_amd as tv
 

@@ -345,7 +345,9 @@ __device__ inline bool build_masks_wave(const int (&par)[2], int b, int T,
   return bad;
 }
 
-template <typename E, int D, bool kSplit, bool kMasks, bool kPaged>
+// kPaged: 0 dense caches; 1 paged, rows addressed by 64-bit pointers; 2 paged, by 32-bit offsets
+// from the pool's base (pools under 4 GB: no 64-bit address arithmetic per load)
+template <typename E, int D, bool kSplit, bool kMasks, int kPaged>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
                           amdgpu_waves_per_eu(2, 2)))
 void attn_main(AttnArgs a) {
@@ -462,13 +464,19 @@ void attn_main(AttnArgs a) {
       const long long slot =
           tile < n_tree_tiles
               ? (long long)e
-              : (e < 0 ? -1LL : (long long)e * (pmask + 1) + (row_key(tile, i) & pmask));
+              : (e < 0 ? -1LL : ((long long)e << a.log2P) + (row_key(tile, i) & pmask));
       const bool out = slot < 0 || slot >= a.num_slots;
       bad_slot = bad_slot || out;
       const int mine = out ? (slot < 0 ? 0 : a.num_slots - 1) : (int)slot;
-      const size_t off = (size_t)mine * hstride + dma_chunk[i];
-      lds_dma16_addr(kl + i * 1024, kpool + off);
-      lds_dma16_addr(vl + i * 1024, vpool + off);
+      if constexpr (kPaged == 2) {
+        const uint32_t off = (uint32_t)mine * (uint32_t)hstride + dma_chunk[i];
+        lds_dma16(kl + i * 1024, kpool, off);
+        lds_dma16(vl + i * 1024, vpool, off);
+      } else {
+        const size_t off = (size_t)mine * hstride + dma_chunk[i];
+        lds_dma16_addr(kl + i * 1024, kpool + off);
+        lds_dma16_addr(vl + i * 1024, vpool + off);
+      }
     }
   };
 
@@ -1225,7 +1233,7 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int elem_bytes, i
 // Profiling events recorded around the main kernel (tv_profile_attn_main).
 hipEvent_t g_prof_before = nullptr, g_prof_after = nullptr;
 
-template <typename E, int D, bool kMasks = false, bool kPaged = false>
+template <typename E, int D, bool kMasks = false, int kPaged = 0>
 int launch_main(const AttnArgs& a, hipStream_t stream) {
   const int n_items = a.B * a.Hkv * a.S * a.RB;
   auto kernel = a.S > 1 ? attn_main<E, D, true, kMasks, kPaged>
@@ -1240,7 +1248,7 @@ int launch_main(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? TV_OK : TV_ERR_HIP;
 }
 
-template <typename E, int D, bool kPaged = false>
+template <typename E, int D, int kPaged = 0>
 int launch_attn(const AttnArgs& a, hipStream_t stream) {
   const int rc = launch_main<E, D, false, kPaged>(a, stream);
   if (rc != TV_OK) return rc;
@@ -1410,9 +1418,15 @@ extern "C" int tree_verify_attn_paged(const void* q, const void* k_pool, const v
   a.log2P = 31 - __builtin_clz((unsigned)page_size);
   a.num_slots = num_slots;
   hipStream_t st = (hipStream_t)stream;
-  if (dtype == TV_BF16)
-    return D == 128 ? launch_attn<__bf16, 128, true>(a, st) : launch_attn<__bf16, 64, true>(a, st);
-  return D == 128 ? launch_attn<float, 128, true>(a, st) : launch_attn<float, 64, true>(a, st);
+  // a pool of at most 4 GB per cache is addressed by 32-bit offsets from its base
+  const bool off32 =
+      (unsigned long long)num_slots * Hkv * D * (dtype == TV_BF16 ? 2 : 4) <= 0xffffffffull;
+  if (dtype == TV_BF16) {
+    if (off32)
+      return D == 128 ? launch_attn<__bf16, 128, 2>(a, st) : launch_attn<__bf16, 64, 2>(a, st);
+    return D == 128 ? launch_attn<__bf16, 128, 1>(a, st) : launch_attn<__bf16, 64, 1>(a, st);
+  }
+  return D == 128 ? launch_attn<float, 128, 1>(a, st) : launch_attn<float, 64, 1>(a, st);
 }
 
 // True when byte ranges [a, a + na) and [b, b + nb) intersect.
