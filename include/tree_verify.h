@@ -288,8 +288,8 @@ int kv_commit_paged(int32_t* block_table, int max_pages, int page_size, const in
 /*
  * tree_verify_step — one whole verification step: tree_build_mask, tree_verify_attn,
  * tree_accept and kv_compact_accepted, in that order and with the same results and status
- * bits, fused into three kernel launches (ancestor masks; the attention main kernel; the
- * split-K merge together with the acceptance walk and the compaction).  The step is the one
+ * bits, fused into two kernel launches (the attention main kernel, which also builds the
+ * ancestor masks; the split-K merge together with the acceptance walk and the compaction).  The step is the one
  * the pages describe: attention of the flattened tree (lesty.tech section 5), greedy
  * acceptance of the longest path (section 4; rainlin.net section 3.2), commit of its K/V
  * (lesty.tech section 8).
