@@ -69,21 +69,35 @@ struct StochArgs {
   int T, W, V, mode, G;
 };
 
-__device__ inline double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;  // identical in every lane: each butterfly step adds the same pair
+// DPP move of a double (both halves alike); a lane without a source takes 0.
+template <int kCtrl, int kRowMask = 0xf>
+__device__ inline double dpp_f64_or0(double v) {
+  const long long x = __double_as_longlong(v);
+  const int lo = dpp_mov<kCtrl, kRowMask>((int)(uint32_t)x, 0);
+  const int hi = dpp_mov<kCtrl, kRowMask>((int)(x >> 32), 0);
+  return __longlong_as_double(((long long)hi << 32) | (uint32_t)lo);
 }
 
-// Inclusive prefix sum over the lanes of a wavefront.
-__device__ inline double wave_scan_f64(double v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double t = __shfl_up(v, off, 64);
-    if (lane >= off) v += t;
-  }
+__device__ inline double readlane_f64(double v, int l) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)x, l);
+  const int hi = __builtin_amdgcn_readlane((int)(x >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (uint32_t)lo);
+}
+
+// Inclusive prefix sum over the lanes of a wavefront (row shifts, then row broadcasts).
+__device__ inline double wave_scan_f64(double v) {
+  v += dpp_f64_or0<0x111>(v);
+  v += dpp_f64_or0<0x112>(v);
+  v += dpp_f64_or0<0x114>(v);
+  v += dpp_f64_or0<0x118>(v);
+  v += dpp_f64_or0<0x142, 0xa>(v);
+  v += dpp_f64_or0<0x143, 0xc>(v);
   return v;
 }
+
+// Sum over the wavefront, the same in every lane (lane 63's prefix, read out as uniform).
+__device__ inline double wave_sum_f64(double v) { return readlane_f64(wave_scan_f64(v), 63); }
 
 // Highest ancestor bit below c in a mask row: c's parent, or -1.
 __device__ inline int parent_from_row(int c, uint64_t lo, uint64_t hi) {
@@ -293,10 +307,11 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
       const int l = __builtin_ctzll(k ? m1 : m0);
       if (k) m1 &= m1 - 1; else m0 &= m0 - 1;
       const int c = l + 64 * k;
-      const int x = __shfl(k ? tok[1] : tok[0], l, 64);
-      const double pxd = (double)__shfl(k ? px[1] : px[0], l, 64);
-      const double qxd = (double)__shfl(k ? qx[1] : qx[0], l, 64);
-      const double uac = __shfl(k ? ua[1] : ua[0], l, 64);
+      // the child's token, probabilities and uniform from its lane (l is uniform)
+      const int x = __builtin_amdgcn_readlane(k ? tok[1] : tok[0], l);
+      const double pxd = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(k ? px[1] : px[0]), l));
+      const double qxd = (double)__int_as_float(__builtin_amdgcn_readlane(__float_as_int(k ? qx[1] : qx[0]), l));
+      const double uac = readlane_f64(k ? ua[1] : ua[0], l);
       bool excl = false;
       if (a.mode) {
         const bool same = ((rj0 >> lane) & 1 && tok[0] == x) || ((rj1 >> lane) & 1 && tok[1] == x);
@@ -360,12 +375,11 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
       const int kk = lane * per + j;
       if (kk < nloc) local += s_chunk[kk];
     }
-    const double incl = wave_scan_f64(local, lane);
-    double excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.0;
+    const double incl = wave_scan_f64(local);
+    const double excl = dpp_f64_or0<0x138>(incl);  // wave_shr:1: the previous lane's (0 in lane 0)
     // the slice where the running sum first exceeds u * total (owner), the running sum before
     // it (base), and the last token with mass over the whole vocabulary (gnz)
-    double total = __shfl(incl, 63, 64), base = 0.0;
+    double total = readlane_f64(incl, 63), base = 0.0;
     int owner = 0, gnz = last_nz;
     if (G > 1) {
       exchange(a, b, g, rounds, total, last_nz, tid, s_xval, s_xnz, &s_timeout);
@@ -398,7 +412,7 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
     const uint64_t over = __ballot(base + (excl + local) > thr);
     if (over) {
       const int L = __builtin_ctzll(over);
-      const double excl_L = base + __shfl(excl, L, 64);
+      const double excl_L = base + readlane_f64(excl, L);
       // chunk of lane L where the running sum first exceeds thr (walked by every lane alike)
       int kc = -1;
       double before = excl_L, run = 0.0;
@@ -424,7 +438,7 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
           uv[e] = resid(pv[e], qv[e], C);
           ls += uv[e];
         }
-        const double inc2 = wave_scan_f64(ls, lane);
+        const double inc2 = wave_scan_f64(ls);
         double r = before + (inc2 - ls);
         int hit = -1, lastpos = -1;
 #pragma unroll
@@ -436,7 +450,7 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
           }
         }
         const uint64_t hits = __ballot(hit >= 0);
-        bonus = hits ? __shfl(hit, __builtin_ctzll(hits), 64)
+        bonus = hits ? __builtin_amdgcn_readlane(hit, __builtin_ctzll(hits))
                      : wave_max(lastpos);  // rounding tie at the chunk's end
       }
     }

@@ -14,15 +14,37 @@ __device__ inline void low_bits(int n, uint64_t& lo, uint64_t& hi) {
   hi = n >= 128 ? ~0ull : (n <= 64 ? 0ull : bit64(n - 64) - 1);
 }
 
+// One DPP move of a 32-bit value across the lanes of a wavefront (controls: row_shr:n is
+// 0x110 + n, wave_shr:1 is 0x138, row_bcast:15 is 0x142, row_bcast:31 is 0x143); a lane
+// without a source, or in a row outside kRowMask, takes `fill`.
+template <int kCtrl, int kRowMask = 0xf>
+__device__ inline int dpp_mov(int v, int fill) {
+  return __builtin_amdgcn_update_dpp(fill, v, kCtrl, kRowMask, 0xf, false);
+}
+
+// Maximum over the wavefront, the same in every lane: an inclusive max scan (row shifts by 1,
+// 2, 4, 8, then lane 15 of a row into the next row and lane 31 into rows 2 and 3) leaves it in
+// lane 63, read out as a uniform value.  All in the vector ALU, no LDS round trips.
 __device__ inline int wave_max(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-  return v;
+  v = max(v, dpp_mov<0x111>(v, v));
+  v = max(v, dpp_mov<0x112>(v, v));
+  v = max(v, dpp_mov<0x114>(v, v));
+  v = max(v, dpp_mov<0x118>(v, v));
+  v = max(v, dpp_mov<0x142, 0xa>(v, v));
+  v = max(v, dpp_mov<0x143, 0xc>(v, v));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ inline uint64_t shfl64(uint64_t v, int src) {
   const int lo = __shfl((int)(uint32_t)v, src, 64);
   const int hi = __shfl((int)(uint32_t)(v >> 32), src, 64);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Lane src's value of v in every lane; src must be the same in all lanes.
+__device__ inline uint64_t readlane64(uint64_t v, int src) {
+  const int lo = __builtin_amdgcn_readlane((int)(uint32_t)v, src);
+  const int hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), src);
   return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
@@ -34,8 +56,8 @@ __device__ inline uint64_t shfl64(uint64_t v, int src) {
 // goes there.  Returns accept_len.
 //
 // All global loads (mask rows, draft and target tokens of the lane's two nodes) are issued
-// together; the parent's target token and the winner's mask row then come from other lanes by
-// shuffles, so the walk makes one round trip to memory before its writes.
+// together; the parent's target token then comes from another lane by a shuffle and the winner's
+// mask row by lane reads, so the walk makes one round trip to memory before its writes.
 __device__ inline int accept_walk(int b, int T, int W, const uint64_t* __restrict__ anc,
                                   const int32_t* __restrict__ draft,
                                   const int32_t* __restrict__ target,
@@ -94,9 +116,9 @@ __device__ inline int accept_walk(int b, int T, int W, const uint64_t* __restric
   // the winner's mask row and target token, from lane best % 64, slot best / 64
   const int src = best & 63;
   const bool hi_slot = best >= 64;
-  const uint64_t b0 = hi_slot ? shfl64(a0[1], src) : shfl64(a0[0], src);
-  const uint64_t b1 = hi_slot ? shfl64(a1[1], src) : shfl64(a1[0], src);
-  const int bonus = hi_slot ? __shfl(tg[1], src, 64) : __shfl(tg[0], src, 64);
+  const uint64_t b0 = readlane64(hi_slot ? a0[1] : a0[0], src);
+  const uint64_t b1 = readlane64(hi_slot ? a1[1] : a1[0], src);
+  const int bonus = __builtin_amdgcn_readlane(hi_slot ? tg[1] : tg[0], src);
   const int n = __popcll(b0) + __popcll(b1);
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
