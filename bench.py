@@ -246,7 +246,16 @@ class StepSet:
                                 P(t["cache_len_out"]), P(t["tree_slot"]), P(t["path"]),
                                 P(t["alen"]), P(t["free"]), P(t["free_top"]), paged.num_slots,
                                 B, T, P(t["status"]))
-            self.api = "paged"
+            # the fused paged step (one-token pages): the same four calls in two launches
+            self.step_paged_args = (P(t["parent"]), P(t["draft"]), P(t["target"]), P(t["q"]),
+                                    P(t["k_pool"]), P(t["v_pool"]), paged.num_slots,
+                                    P(t["table"]), mp, paged.page_size, P(t["cache_len"]),
+                                    P(t["cache_len_out"]), P(t["tree_slot"]), P(t["anc"]),
+                                    P(t["out"]), P(t["lse"]), P(t["path"]), P(t["alen"]),
+                                    P(t["bonus"]), P(t["free"]), P(t["free_top"]),
+                                    P(t["status"]), B, T, Hq, w.Hkv, D, dt, ctypes.c_float(0.0),
+                                    split_keys, ws_ptr, ctypes.c_size_t(ws_bytes))
+            self.api = "paged_fused" if paged.page_size == 1 else "paged"
         self.stoch = stoch
         if stoch is not None:  # next-token distributions and uniforms (synth.make_stochastic)
             if base is None:
@@ -267,6 +276,10 @@ class StepSet:
 
     def attn_paged(self, stream):
         rc = self.lib.tree_verify_attn_paged(*self.attn_paged_args, stream)
+        assert rc == 0, rc
+
+    def fused_paged(self, stream):
+        rc = self.lib.tree_verify_step_paged(*self.step_paged_args, stream)
         assert rc == 0, rc
 
     def commit(self, stream):
@@ -297,6 +310,9 @@ class StepSet:
     def step(self, stream):
         if self.api == "fused":
             self.fused(stream)
+            return
+        if self.api == "paged_fused":
+            self.fused_paged(stream)
             return
         if self.api == "paged":
             self.mask(stream)
@@ -632,7 +648,7 @@ def main() -> int:
         ws_bytes = max(ws_bytes, tv.tree_verify_attn_workspace_size(
             w.B, w.T, w.Hq, w.Hkv, w.D, cap,
             torch.bfloat16 if w.dtype == "bf16" else torch.float32, args.split_keys))
-        args.api = "paged"
+        args.api = "paged_fused" if args.page_size == 1 else "paged"
     stoch, stoch_ws = None, None
     if args.accept == "stochastic":
         if args.kv == "paged":
@@ -717,7 +733,8 @@ def main() -> int:
             torch.cuda.synchronize()
         return e0.elapsed_time(e1) / args.steps, t_wall
 
-    other = {"fused": "separate", "separate": "fused", "paged": None, "stochastic": None}[args.api]
+    other = {"fused": "separate", "separate": "fused", "paged_fused": "paged", "paged": None,
+             "stochastic": None}[args.api]
     ms_other = time_api(other)[0] if other else None
     ms_per_step, t_wall = time_api(args.api)
     t_step = ms_per_step * 1e-3
@@ -808,14 +825,38 @@ def main() -> int:
             return float(np.mean([evp[i][a].elapsed_time(evp[i][b]) for i in range(n_prof)])) * 1e-3
 
         t_main = pavg(2, 3)
+        # the fused paged step, its main kernel by the same hook
+        step_paged_us = main_step_paged_us = None
+        if paged.page_size == 1:
+            evq = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                   for _ in range(n_prof)]
+            for row in evq:
+                for e in row:
+                    e.record(stream)
+            stream.synchronize()
+            with torch.cuda.stream(stream):
+                for i in range(n_prof):
+                    ei = evq[i]
+                    tv.profile_attn_main(ei[1], ei[2])
+                    ei[0].record(stream)
+                    sets[i % n_sets].fused_paged(sptr)
+                    ei[3].record(stream)
+                tv.profile_attn_main(None, None)
+                stream.synchronize()
+            step_paged_us = float(np.mean([evq[i][0].elapsed_time(evq[i][3])
+                                           for i in range(n_prof)])) * 1e3
+            main_step_paged_us = float(np.mean([evq[i][1].elapsed_time(evq[i][2])
+                                                for i in range(n_prof)])) * 1e3
         paged_breakdown = {
             "page_size": paged.page_size, "num_slots": paged.num_slots,
             "max_pages": int(paged.block_table.shape[1]),
             "tree_verify_attn_paged_us": pavg(1, 4) * 1e6, "attn_main_paged_us": t_main * 1e6,
             "kv_commit_paged_us": pavg(5, 6) * 1e6 if paged.page_size == 1 else None,
             "kv_compact_accepted_copy_us": t_compact * 1e6,
+            "tree_verify_step_paged_us": step_paged_us,
+            "attn_main_step_paged_us": main_step_paged_us,
             "note": ("per-call times from events between eager calls (launch latency included); "
-                     "attn_main_paged_us from the kernel's own timestamps"),
+                     "attn_main_* from the kernel's own timestamps"),
         }
 
     # stochastic acceptance: the same calls with tree_accept_stochastic in place of tree_accept;
@@ -884,7 +925,7 @@ def main() -> int:
     peak_tf = MFMA_PEAK_TFLOPS[w.dtype]
     ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
     traffic = None
-    if os.path.exists(COUNTERS_FILE):
+    if os.path.exists(COUNTERS_FILE) and args.kv == "dense":  # counters of the dense kernel
         with open(COUNTERS_FILE, encoding="utf-8") as f:
             cnt = json.load(f)
         rec = cnt.get(args.workload)
@@ -902,6 +943,7 @@ def main() -> int:
                                "the masks)",
                       "separate": "attn_main",
                       "paged": "attn_main (tree_verify_attn_paged's instantiation)",
+                      "paged_fused": "attn_main (tree_verify_attn_paged's instantiation)",
                       "stochastic": "attn_main"}[args.api]
     roof["kernel_us"] = t_main * 1e6
     roof["algorithmic_bytes"] = kv_bytes

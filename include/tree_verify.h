@@ -312,6 +312,36 @@ int tree_verify_step(const int32_t* parent, const int32_t* draft_tok, const int3
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * tree_verify_step_paged — the verification step over a paged cache: tree_build_mask,
+ * tree_verify_attn_paged, tree_accept and kv_commit_paged, in that order and with the same
+ * results and status bits, fused into two kernel launches (the paged attention main kernel,
+ * which also builds the ancestor masks; the split-K merge together with the acceptance walk and
+ * the pointer-swap commit).  The serving layout of lesty.tech section 8: the prefix in the
+ * sequence's pages, the tree nodes in scratch slots of the same pool, the accepted nodes'
+ * slots adopted by the block table and the rest returned to the free list.
+ *
+ * Arguments are those of the four calls: parent, draft_tok, target_tok as for tree_build_mask
+ * and tree_accept; q, k_pool, v_pool, num_slots, block_table, max_pages, cache_len, tree_slot,
+ * out, lse, scale, split_keys, workspace as for tree_verify_attn_paged (the same workspace
+ * size); anc_mask is an output here; accept_path, accept_len, bonus_tok as for tree_accept;
+ * block_table (in/out), cache_len_out, free_slots, free_top as for kv_commit_paged
+ * (cache_len_out may be the same pointer as cache_len, not partly overlapping).  page_size
+ * must be 1 (TV_ERR_UNSUPPORTED otherwise), as for kv_commit_paged.  status [B] is required;
+ * it is written by the mask stage and OR-ed by the others.  The block table's entries that the
+ * attention reads (positions below cache_len) and those the commit writes (from cache_len on)
+ * do not meet, and the commit runs after every attention read.
+ */
+int tree_verify_step_paged(const int32_t* parent, const int32_t* draft_tok,
+                           const int32_t* target_tok, const void* q, const void* k_pool,
+                           const void* v_pool, int num_slots, int32_t* block_table, int max_pages,
+                           int page_size, const int32_t* cache_len, int32_t* cache_len_out,
+                           const int32_t* tree_slot, uint64_t* anc_mask, void* out, float* lse,
+                           int32_t* accept_path, int32_t* accept_len, int32_t* bonus_tok,
+                           int32_t* free_slots, int32_t* free_top, int32_t* status, int B, int T,
+                           int Hq, int Hkv, int D, int dtype, float scale, int split_keys,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Dynamic draft tree of EAGLE-2 (rainlin.net "EAGLE 系列", section 7), built on the device.
  *
  * Expansion (section 7.1): from the deepest level of the tree, the k nodes with the largest

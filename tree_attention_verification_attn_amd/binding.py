@@ -22,6 +22,7 @@ TV_BAD_TOKEN, TV_SYNC_TIMEOUT, TV_BAD_CONF = 0x20, 0x40, 0x80
 EXPORTS = ("tv_status_string", "tree_build_mask", "tree_verify_attn_workspace_size",
            "tree_verify_attn", "tree_accept", "kv_compact_accepted", "tv_profile_attn_main",
            "tree_verify_step", "tree_verify_attn_paged", "kv_commit_paged",
+           "tree_verify_step_paged",
            "tree_accept_stochastic", "tree_accept_stochastic_workspace_size",
            "tv_profile_accept_stochastic", "eagle2_node_count", "eagle2_expand",
            "eagle2_rerank", "lm_head_project", "lm_head_screen", "lm_head_rescore",
@@ -84,6 +85,10 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_verify_attn_paged.restype = I
     lib.kv_commit_paged.argtypes = [P, I, I, P, P, P, P, P, P, P, I, I, I, P, P]
     lib.kv_commit_paged.restype = I
+    lib.tree_verify_step_paged.argtypes = [P, P, P, P, P, P, I, P, I, I, P, P, P, P, P, P, P, P,
+                                           P, P, P, P, I, I, I, I, I, I, F, I, P,
+                                           ctypes.c_size_t, P]
+    lib.tree_verify_step_paged.restype = I
     lib.tree_accept_stochastic.argtypes = [P, P, P, P, P, P, I, I, I, I, I, P, ctypes.c_size_t,
                                            P, P, P, P, P]
     lib.tree_accept_stochastic_workspace_size.argtypes = [I, I, I, I]
@@ -449,6 +454,73 @@ def kv_commit_paged(block_table, cache_len, tree_slot, accept_path, accept_len, 
         _ptr(tree_slot), _ptr(accept_path), _ptr(accept_len), _ptr(free_slots), _ptr(free_top),
         int(num_slots), B, T, _ptr(status), _stream(stream)))
     return cache_len_out
+
+
+def tree_verify_step_paged(parent, draft_tok, target_tok, q, k_pool, v_pool, block_table,
+                           cache_len, tree_slot, free_slots, free_top, page_size: int = 1,
+                           cache_len_out=None, out=None, lse=None, anc_mask=None,
+                           accept_path=None, accept_len=None, bonus_tok=None, status=None,
+                           scale: float = 0.0, split_keys: int = 0,
+                           workspace: torch.Tensor | None = None, with_lse: bool = True,
+                           stream=None):
+    """One fused verification step over a paged cache (masks, paged attention, acceptance,
+    pointer-swap commit); updates block_table, free_slots and free_top in place.
+
+    Returns a dict with anc_mask, out, lse, accept_path, accept_len, bonus_tok, cache_len_out
+    and status."""
+    for name, t, nd in (("parent", parent, 2), ("draft_tok", draft_tok, 2),
+                        ("target_tok", target_tok, 2), ("block_table", block_table, 2),
+                        ("cache_len", cache_len, 1), ("tree_slot", tree_slot, 2),
+                        ("free_slots", free_slots, 1), ("free_top", free_top, 1)):
+        _need(t, name, torch.int32, nd)
+    _need(q, "q", None, 4)
+    B, T, Hq, D = q.shape
+    dt = _dtype_code(q)
+    _need(k_pool, "k_pool", q.dtype, 3)
+    _need(v_pool, "v_pool", q.dtype, 3)
+    num_slots, Hkv = k_pool.shape[0], k_pool.shape[1]
+    max_pages = block_table.shape[1]
+    W = (T + 63) // 64
+    if (tuple(k_pool.shape) != (num_slots, Hkv, D) or tuple(v_pool.shape) != tuple(k_pool.shape)
+            or block_table.shape[0] != B or tuple(tree_slot.shape) != (B, T)
+            or tuple(cache_len.shape) != (B,) or tuple(parent.shape) != (B, T)
+            or tuple(draft_tok.shape) != (B, T) or tuple(target_tok.shape) != (B, T)
+            or free_slots.numel() < num_slots or free_top.numel() != 1):
+        raise ValueError("inconsistent tree_verify_step_paged shapes")
+    dev = q.device
+    new = lambda shape, dtype: torch.empty(shape, dtype=dtype, device=dev)  # noqa: E731
+    anc_mask = new((B, T, W), torch.int64) if anc_mask is None else anc_mask
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and with_lse:
+        lse = new((B, T, Hq), torch.float32)
+    accept_path = new((B, T), torch.int32) if accept_path is None else accept_path
+    accept_len = new((B,), torch.int32) if accept_len is None else accept_len
+    bonus_tok = new((B,), torch.int32) if bonus_tok is None else bonus_tok
+    cache_len_out = torch.empty_like(cache_len) if cache_len_out is None else cache_len_out
+    status = new((B,), torch.int32) if status is None else status
+    _need(anc_mask, "anc_mask", torch.int64, 3)
+    _need(out, "out", q.dtype, 4)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, 3)
+    for name, t in (("accept_len", accept_len), ("bonus_tok", bonus_tok),
+                    ("cache_len_out", cache_len_out), ("status", status)):
+        _need(t, name, torch.int32, 1)
+    _need(accept_path, "accept_path", torch.int32, 2)
+    ws_bytes = tree_verify_attn_workspace_size(B, T, Hq, Hkv, D, max_pages * page_size, q.dtype,
+                                               split_keys)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("tree_verify_step_paged", load_library().tree_verify_step_paged(
+        _ptr(parent), _ptr(draft_tok), _ptr(target_tok), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+        num_slots, _ptr(block_table), max_pages, int(page_size), _ptr(cache_len),
+        _ptr(cache_len_out), _ptr(tree_slot), _ptr(anc_mask), _ptr(out), _ptr(lse),
+        _ptr(accept_path), _ptr(accept_len), _ptr(bonus_tok), _ptr(free_slots), _ptr(free_top),
+        _ptr(status), B, T, Hq, Hkv, D, dt, float(scale), int(split_keys), _ptr(workspace),
+        ws_have, _stream(stream)))
+    return dict(anc_mask=anc_mask, out=out, lse=lse, accept_path=accept_path,
+                accept_len=accept_len, bonus_tok=bonus_tok, cache_len_out=cache_len_out,
+                status=status)
 
 
 def eagle2_node_count(depth: int, k: int, branch: int) -> int:

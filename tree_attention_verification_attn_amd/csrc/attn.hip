@@ -877,7 +877,10 @@ void attn_main(AttnArgs a) {
   }
 
   // ---- epilogue ----------------------------------------------------------------------------
-  if (kPaged && __ballot(bad_slot) && lane == 0 && a.status) atomicOr(a.status + b, TV_BAD_PAGE);
+  // (when the kernel builds the masks, its mask writer stores status[b] with a plain write, so
+  // the fused step's second kernel reports bad pages instead)
+  if (kPaged && !kMasks && __ballot(bad_slot) && lane == 0 && a.status)
+    atomicOr(a.status + b, TV_BAD_PAGE);
   l_run += partner(l_run);
 
   if (direct) {
@@ -1152,7 +1155,50 @@ struct TailArgs {
   int32_t* cache_len_out;
   int32_t* status;
   int n_comb, n_acc, W, row_bytes;
+  // paged step (table not null): pointer-swap commit into the block table and free list
+  int32_t* table;
+  int32_t* free_slots;
+  int32_t* free_top;
 };
+
+// Acceptance workgroup of the paged step (one-token pages): wavefront 0 walks the tree and then
+// commits the path by pointer swap, while the whole workgroup checks the block-table entries of
+// positions [0, L) and the tree slots, the entries the attention read, and reports TV_BAD_PAGE
+// as tree_verify_attn_paged does.
+__device__ inline void tail_commit_paged(const AttnArgs& a, const TailArgs& t, int b, int L,
+                                         int* s_path) {
+  __shared__ int s_on[kMaxT];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  const int Lc = min(max(L, 0), a.Lmax);  // the attention's clamp of the length
+  bool bad = false;
+  for (int p = tid; p < Lc; p += 256) {
+    const int e = a.table[(size_t)b * a.max_pages + p];
+    bad = bad || e < 0 || e >= a.num_slots;
+  }
+  for (int c = tid; c < a.T; c += 256) {
+    const int e = a.tree_slot[(size_t)b * a.T + c];
+    bad = bad || e < 0 || e >= a.num_slots;
+  }
+  if (bad) atomicOr(&s_bad, 1);
+  if (tid < 64) {
+    const int n = accept_walk(b, a.T, t.W, t.anc, t.draft, t.target, t.accept_path, t.accept_len,
+                              t.bonus_tok, s_path);
+    wave_lds_sync();
+    int pe[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = tid + 64 * k;
+      pe[k] = c < n ? s_path[c] : -1;
+    }
+    commit_paged_wave(b, L, n, pe, t.table, a.max_pages, a.tree_slot, a.T, a.num_slots,
+                      t.free_slots, t.free_top, t.status, t.cache_len_out, s_on);
+  }
+  __syncthreads();
+  if (tid == 0 && s_bad && t.status) atomicOr(t.status + b, TV_BAD_PAGE);
+}
 
 template <typename E, int D, int kBatch, int kSW>
 __global__ __launch_bounds__(256) void step_tail(AttnArgs a, TailArgs t) {
@@ -1165,6 +1211,10 @@ __global__ __launch_bounds__(256) void step_tail(AttnArgs a, TailArgs t) {
   __shared__ int s_n;
   const int b = blockIdx.x, tid = threadIdx.x;
   const int L = a.cache_len[b];  // read before this workgroup writes cache_len_out[b]
+  if (t.table) {
+    tail_commit_paged(a, t, b, L, s_path);
+    return;
+  }
   if (tid < 64) {
     const int n = accept_walk(b, a.T, t.W, t.anc, t.draft, t.target, t.accept_path, t.accept_len,
                               t.bonus_tok, s_path);
@@ -1264,9 +1314,9 @@ int launch_attn(const AttnArgs& a, hipStream_t stream) {
   return launch_status();
 }
 
-template <typename E, int D>
+template <typename E, int D, int kPaged = 0>
 int launch_step(const AttnArgs& a, TailArgs t, hipStream_t stream) {
-  const int rc = launch_main<E, D, true>(a, stream);
+  const int rc = launch_main<E, D, true, kPaged>(a, stream);
   if (rc != TV_OK) return rc;
   t.n_comb = a.S > 1 ? combine_grid<E, D>(a.B * a.Hkv * a.RB, a.S) : 0;
   t.n_acc = (a.B + 7) / 8 * 8;
@@ -1493,8 +1543,66 @@ extern "C" int tree_verify_step(const int32_t* parent, const int32_t* draft_tok,
   t.n_comb = 0;
   t.W = ceil_div(T, 64);
   t.row_bytes = D * (int)elem;
+  t.table = t.free_slots = t.free_top = nullptr;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == TV_BF16)
     return D == 128 ? launch_step<__bf16, 128>(a, t, st) : launch_step<__bf16, 64>(a, t, st);
   return D == 128 ? launch_step<float, 128>(a, t, st) : launch_step<float, 64>(a, t, st);
+}
+
+extern "C" int tree_verify_step_paged(
+    const int32_t* parent, const int32_t* draft_tok, const int32_t* target_tok, const void* q,
+    const void* k_pool, const void* v_pool, int num_slots, int32_t* block_table, int max_pages,
+    int page_size, const int32_t* cache_len, int32_t* cache_len_out, const int32_t* tree_slot,
+    uint64_t* anc_mask, void* out, float* lse, int32_t* accept_path, int32_t* accept_len,
+    int32_t* bonus_tok, int32_t* free_slots, int32_t* free_top, int32_t* status, int B, int T,
+    int Hq, int Hkv, int D, int dtype, float scale, int split_keys, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (!parent || !draft_tok || !target_tok || !cache_len_out || !accept_path || !accept_len ||
+      !bonus_tok || !status || !block_table || !tree_slot || !free_slots || !free_top ||
+      num_slots < 1 || max_pages < 1 || page_size < 1 || (page_size & (page_size - 1)) ||
+      max_pages >= (1 << 30))
+    return TV_ERR_INVALID_ARG;
+  if (page_size != 1) return TV_ERR_UNSUPPORTED;  // the pointer-swap commit needs token pages
+  if (cache_len_out != cache_len &&
+      overlaps(cache_len_out, (size_t)B * 4, cache_len, (size_t)B * 4))
+    return TV_ERR_INVALID_ARG;
+  AttnArgs a;
+  Plan p;
+  // the dense argument checks, with the pools standing in for the caches and the tree K/V
+  const int rc = prepare_attn(a, p, q, k_pool, v_pool, cache_len, k_pool, v_pool, anc_mask, out,
+                              lse, status, B, T, Hq, Hkv, D, max_pages, dtype, scale, split_keys,
+                              workspace, workspace_bytes);
+  if (rc != TV_OK) return rc;
+  a.table = block_table;
+  a.tree_slot = tree_slot;
+  a.max_pages = max_pages;
+  a.log2P = 0;
+  a.num_slots = num_slots;
+  a.parent = parent;
+  TailArgs t;
+  t.anc = anc_mask;
+  t.draft = draft_tok;
+  t.target = target_tok;
+  t.accept_path = accept_path;
+  t.accept_len = accept_len;
+  t.bonus_tok = bonus_tok;
+  t.kc = t.vc = nullptr;  // nothing is copied
+  t.cache_len_out = cache_len_out;
+  t.status = status;
+  t.n_comb = 0;
+  t.W = ceil_div(T, 64);
+  t.row_bytes = 0;
+  t.table = block_table;
+  t.free_slots = free_slots;
+  t.free_top = free_top;
+  hipStream_t st = (hipStream_t)stream;
+  const bool off32 =
+      (unsigned long long)num_slots * Hkv * D * (dtype == TV_BF16 ? 2 : 4) <= 0xffffffffull;
+  if (dtype == TV_BF16) {
+    if (off32)
+      return D == 128 ? launch_step<__bf16, 128, 2>(a, t, st) : launch_step<__bf16, 64, 2>(a, t, st);
+    return D == 128 ? launch_step<__bf16, 128, 1>(a, t, st) : launch_step<__bf16, 64, 1>(a, t, st);
+  }
+  return D == 128 ? launch_step<float, 128, 1>(a, t, st) : launch_step<float, 64, 1>(a, t, st);
 }

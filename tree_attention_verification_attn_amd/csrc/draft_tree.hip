@@ -131,13 +131,6 @@ __device__ inline int wave_prefix_sum(int v) {
   return v;
 }
 
-// Orders the LDS accesses of one wavefront around it: a wavefront's LDS operations complete in
-// issue order, so after this its lanes see each other's earlier writes.
-__device__ inline void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
 // Reranking and flattening of sequence blockIdx.x's table of n nodes (row stride n_max).  All
 // 1024 threads stage the table and run the radix select; the kept nodes (at most 128) are then
 // sorted, linked and flattened by wavefront 0 alone, two nodes per lane, with no workgroup

@@ -41,6 +41,13 @@ __device__ inline uint64_t shfl64(uint64_t v, int src) {
   return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
 }
 
+// Orders the LDS accesses of one wavefront around it: a wavefront's LDS operations complete in
+// issue order, so after this its lanes see each other's earlier writes.
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // Lane src's value of v in every lane; src must be the same in all lanes.
 __device__ inline uint64_t readlane64(uint64_t v, int src) {
   const int lo = __builtin_amdgcn_readlane((int)(uint32_t)v, src);
@@ -140,6 +147,83 @@ __device__ inline int accept_walk(int b, int T, int W, const uint64_t* __restric
     bonus_tok[b] = bonus;
   }
   return n;
+}
+
+// Pointer-swap commit of sequence b ("EAGLE-2 vs. Medusa" section 8, pages of one token) by the
+// calling wavefront (all 64 lanes): block_table[b][L + i] = tree_slot[b][path[i]] for i < n, and
+// the slots of the nodes not on the path go back to the free list, reserved with one atomic add
+// on free_top and written in node order.  Nothing is copied.  pe[k] is path entry lane + 64k
+// (only entries below n are used), L the sequence's length before the step.  A bad length, path
+// or tree slot, or a table too short for L + n, commits and frees nothing, keeps the length and
+// OR-s the reason into status[b] (if status is not null).  s_on is LDS scratch of kMaxT ints
+// used by this wavefront alone.
+__device__ inline void commit_paged_wave(int b, int L, int n, const int pe[2],
+                                         int32_t* __restrict__ table, int max_pages,
+                                         const int32_t* __restrict__ tree_slot, int T,
+                                         int num_slots, int32_t* __restrict__ free_slots,
+                                         int32_t* __restrict__ free_top, int32_t* status,
+                                         int32_t* cache_len_out, int* s_on) {
+  const int lane = threadIdx.x & 63;
+  int ts[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    ts[k] = c < T ? tree_slot[(size_t)b * T + c] : 0;
+    if (c < kMaxT) s_on[c] = 0;
+  }
+  wave_lds_sync();
+  int bits = 0;
+  if (L < 0 || L > max_pages) bits |= TV_BAD_LEN;
+  bool bad = n < 0 || n > T;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    if (c < T && (ts[k] < 0 || ts[k] >= num_slots)) bad = true;
+    if (!(n < 0 || n > T) && c < n) {
+      if (pe[k] < 0 || pe[k] >= T) bad = true;
+      else atomicAdd(&s_on[pe[k]], 1);
+    }
+  }
+  wave_lds_sync();
+  bool rej[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    const int cnt = c < T ? s_on[c] : 0;
+    if (cnt > 1) bad = true;  // a node twice on the path
+    rej[k] = c < T && cnt == 0;
+  }
+  if (__ballot(bad)) bits |= TV_BAD_PATH;
+  if (!bits && (long long)L + n > max_pages) bits |= TV_OVERFLOW;
+  if (bits) {
+    if (lane == 0) {
+      if (status) atomicOr(status + b, bits);
+      cache_len_out[b] = L;
+    }
+    return;
+  }
+  // the table takes the accepted nodes' slots, in path order (slot of node p from its lane)
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = lane + 64 * k;
+    const int p = max(pe[k], 0);
+    const int t0 = __shfl(ts[0], p & 63, 64), t1 = __shfl(ts[1], p & 63, 64);
+    if (i < n) table[(size_t)b * max_pages + L + i] = p >= 64 ? t1 : t0;
+  }
+  // the rejected nodes' slots return to the free list
+  const uint64_t m0 = __ballot(rej[0]), m1 = __ballot(rej[1]);
+  const int cnt = __popcll(m0) + __popcll(m1);
+  int at = 0;
+  if (lane == 0 && cnt) at = atomicAdd(free_top, cnt);
+  at = __builtin_amdgcn_readfirstlane(at);
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    if (!rej[k]) continue;
+    const int r = k == 0 ? __popcll(m0 & below) : __popcll(m0) + __popcll(m1 & below);
+    if (at + r < num_slots) free_slots[at + r] = ts[k];
+  }
+  if (lane == 0) cache_len_out[b] = L + n;
 }
 
 }  // namespace tv

@@ -167,10 +167,7 @@ __global__ __launch_bounds__(256) void compact_kernel(
 }
 
 // ------------------------------------------------------------------------------------------
-// kv_commit_paged: commit by pointer swap ("EAGLE-2 vs. Medusa" section 8), pages of one token.
-// One wavefront per sequence: block_table[b][L + i] = tree_slot[b][path[i]] for i < n, and the
-// slots of the nodes not on the path go back to the free list, reserved with one atomic add on
-// free_top and written in node order.  Nothing is copied.
+// kv_commit_paged: one wavefront per sequence runs commit_paged_wave on the path in memory.
 // ------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void commit_paged_kernel(
     int32_t* __restrict__ table, int max_pages, const int32_t* cache_len, int32_t* cache_len_out,
@@ -181,67 +178,14 @@ __global__ __launch_bounds__(64) void commit_paged_kernel(
   const int b = blockIdx.x, lane = threadIdx.x;
   const int L = cache_len[b];  // read before cache_len_out[b] is written (they may alias)
   const int n = alen[b];
-  int pe[2], ts[2];
+  int pe[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int c = lane + 64 * k;
     pe[k] = c < T ? path[(size_t)b * T + c] : -1;
-    ts[k] = c < T ? tree_slot[(size_t)b * T + c] : 0;
-    if (c < kMaxT) s_on[c] = 0;
   }
-  __syncthreads();
-  int bits = 0;
-  if (L < 0 || L > max_pages) bits |= TV_BAD_LEN;
-  bool bad = n < 0 || n > T;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int c = lane + 64 * k;
-    if (c < T && (ts[k] < 0 || ts[k] >= num_slots)) bad = true;
-    if (!(n < 0 || n > T) && c < n) {
-      if (pe[k] < 0 || pe[k] >= T) bad = true;
-      else atomicAdd(&s_on[pe[k]], 1);
-    }
-  }
-  __syncthreads();
-  bool rej[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int c = lane + 64 * k;
-    const int cnt = c < T ? s_on[c] : 0;
-    if (cnt > 1) bad = true;  // a node twice on the path
-    rej[k] = c < T && cnt == 0;
-  }
-  if (__ballot(bad)) bits |= TV_BAD_PATH;
-  if (!bits && (long long)L + n > max_pages) bits |= TV_OVERFLOW;
-  if (bits) {
-    if (lane == 0) {
-      if (status) atomicOr(status + b, bits);
-      cache_len_out[b] = L;
-    }
-    return;
-  }
-  // the table takes the accepted nodes' slots, in path order (slot of node p from its lane)
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int i = lane + 64 * k;
-    const int p = max(pe[k], 0);
-    const int t0 = __shfl(ts[0], p & 63, 64), t1 = __shfl(ts[1], p & 63, 64);
-    if (i < n) table[(size_t)b * max_pages + L + i] = p >= 64 ? t1 : t0;
-  }
-  // the rejected nodes' slots return to the free list
-  const uint64_t m0 = __ballot(rej[0]), m1 = __ballot(rej[1]);
-  const int cnt = __popcll(m0) + __popcll(m1);
-  int at = 0;
-  if (lane == 0 && cnt) at = atomicAdd(free_top, cnt);
-  at = __shfl(at, 0, 64);
-  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    if (!rej[k]) continue;
-    const int r = k == 0 ? __popcll(m0 & below) : __popcll(m0) + __popcll(m1 & below);
-    if (at + r < num_slots) free_slots[at + r] = ts[k];
-  }
-  if (lane == 0) cache_len_out[b] = L + n;
+  commit_paged_wave(b, L, n, pe, table, max_pages, tree_slot, T, num_slots, free_slots, free_top,
+                    status, cache_len_out, s_on);
 }
 
 }  // namespace
