@@ -1155,49 +1155,70 @@ struct TailArgs {
   int32_t* cache_len_out;
   int32_t* status;
   int n_comb, n_acc, W, row_bytes;
-  // paged step (table not null): pointer-swap commit into the block table and free list
+  // paged step (table not null): pointer-swap commit into the block table and free list, and
+  // n_scan workgroups (scan_per_seq per sequence) checking the entries the attention read
   int32_t* table;
   int32_t* free_slots;
   int32_t* free_top;
+  int n_scan, scan_per_seq;
 };
 
+constexpr int kScanPerThread = 16;                  // table entries per thread of a scan
+constexpr int kScanSlice = 256 * kScanPerThread;    // table entries per scan workgroup
+
 // Acceptance workgroup of the paged step (one-token pages): wavefront 0 walks the tree and then
-// commits the path by pointer swap, while the whole workgroup checks the block-table entries of
-// positions [0, L) and the tree slots, the entries the attention read, and reports TV_BAD_PAGE
-// as tree_verify_attn_paged does.
+// commits the path by pointer swap.
 __device__ inline void tail_commit_paged(const AttnArgs& a, const TailArgs& t, int b, int L,
                                          int* s_path) {
   __shared__ int s_on[kMaxT];
-  __shared__ int s_bad;
   const int tid = threadIdx.x;
-  if (tid == 0) s_bad = 0;
-  __syncthreads();
-  const int Lc = min(max(L, 0), a.Lmax);  // the attention's clamp of the length
-  bool bad = false;
-  for (int p = tid; p < Lc; p += 256) {
-    const int e = a.table[(size_t)b * a.max_pages + p];
-    bad = bad || e < 0 || e >= a.num_slots;
-  }
-  for (int c = tid; c < a.T; c += 256) {
-    const int e = a.tree_slot[(size_t)b * a.T + c];
-    bad = bad || e < 0 || e >= a.num_slots;
-  }
-  if (bad) atomicOr(&s_bad, 1);
-  if (tid < 64) {
-    const int n = accept_walk(b, a.T, t.W, t.anc, t.draft, t.target, t.accept_path, t.accept_len,
-                              t.bonus_tok, s_path);
-    wave_lds_sync();
-    int pe[2];
+  if (tid >= 64) return;
+  const int n = accept_walk(b, a.T, t.W, t.anc, t.draft, t.target, t.accept_path, t.accept_len,
+                            t.bonus_tok, s_path);
+  wave_lds_sync();
+  int pe[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int c = tid + 64 * k;
-      pe[k] = c < n ? s_path[c] : -1;
-    }
-    commit_paged_wave(b, L, n, pe, t.table, a.max_pages, a.tree_slot, a.T, a.num_slots,
-                      t.free_slots, t.free_top, t.status, t.cache_len_out, s_on);
+  for (int k = 0; k < 2; ++k) {
+    const int c = tid + 64 * k;
+    pe[k] = c < n ? s_path[c] : -1;
   }
-  __syncthreads();
-  if (tid == 0 && s_bad && t.status) atomicOr(t.status + b, TV_BAD_PAGE);
+  commit_paged_wave(b, L, n, pe, t.table, a.max_pages, a.tree_slot, a.T, a.num_slots,
+                    t.free_slots, t.free_top, t.status, t.cache_len_out, s_on);
+}
+
+// Scan workgroup k of the paged step: checks the block-table entries of positions
+// [slice * kScanSlice, +kScanSlice) below the attention's clamped length of its sequence, and
+// (slice 0) every tree slot, and ORs TV_BAD_PAGE as tree_verify_attn_paged does.  The mask
+// writer of the step's main kernel stores status[b] with a plain write, so that kernel leaves
+// bad pages to these workgroups, which run after it.  All loads of a thread are in flight at
+// once.
+__device__ inline void tail_scan_pages(const AttnArgs& a, const TailArgs& t, int k) {
+  const int b = k / t.scan_per_seq, slice = k - b * t.scan_per_seq;
+  const int tid = threadIdx.x;
+  // With cache_len_out aliasing cache_len, the acceptance workgroup of b may already have
+  // committed L + n.  Read with acquire against the commit's release, the new length comes with
+  // the n new entries, which are tree slots the commit found inside the pool, so the verdict
+  // is the same as over the L entries the attention read.
+  const int L = __hip_atomic_load(const_cast<int32_t*>(a.cache_len) + b, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int Lc = min(max(L, 0), a.Lmax);
+  const int lo = slice * kScanSlice;
+  if (lo >= Lc && slice > 0) return;  // uniform
+  const int32_t* row = a.table + (size_t)b * a.max_pages;
+  const int last = max(Lc - 1, 0);  // row[0] exists (max_pages >= 1)
+  int e[kScanPerThread];
+#pragma unroll
+  for (int j = 0; j < kScanPerThread; ++j) e[j] = row[min(lo + j * 256 + tid, last)];
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < kScanPerThread; ++j)
+    bad = bad || (lo + j * 256 + tid < Lc && (e[j] < 0 || e[j] >= a.num_slots));
+  if (slice == 0 && tid < a.T) {
+    const int ts = a.tree_slot[(size_t)b * a.T + tid];
+    bad = bad || ts < 0 || ts >= a.num_slots;
+  }
+  if (__syncthreads_or(bad) && tid == 0 && t.status) atomicOr(t.status + b, TV_BAD_PAGE);
 }
 
 template <typename E, int D, int kBatch, int kSW>
@@ -1206,7 +1227,10 @@ __global__ __launch_bounds__(256) void step_tail(AttnArgs a, TailArgs t) {
     combine_group<E, D, kBatch, kSW>(a, xcd_remap(blockIdx.x - t.n_acc, t.n_comb));
     return;
   }
-  if ((int)blockIdx.x >= a.B) return;  // XCD alignment padding
+  if ((int)blockIdx.x >= a.B) {  // bad-page scans, then XCD alignment padding
+    if ((int)blockIdx.x - a.B < t.n_scan) tail_scan_pages(a, t, blockIdx.x - a.B);
+    return;
+  }
   __shared__ int s_path[kMaxT];
   __shared__ int s_n;
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -1319,7 +1343,7 @@ int launch_step(const AttnArgs& a, TailArgs t, hipStream_t stream) {
   const int rc = launch_main<E, D, true, kPaged>(a, stream);
   if (rc != TV_OK) return rc;
   t.n_comb = a.S > 1 ? combine_grid<E, D>(a.B * a.Hkv * a.RB, a.S) : 0;
-  t.n_acc = (a.B + 7) / 8 * 8;
+  t.n_acc = (a.B + t.n_scan + 7) / 8 * 8;
   const dim3 grid(t.n_acc + t.n_comb), block(256);
   switch (combine_shape(a.S).batch * combine_shape(a.S).sw) {
     case 2: hipLaunchKernelGGL((step_tail<E, D, 2, 1>), grid, block, 0, stream, a, t); break;
@@ -1544,6 +1568,7 @@ extern "C" int tree_verify_step(const int32_t* parent, const int32_t* draft_tok,
   t.W = ceil_div(T, 64);
   t.row_bytes = D * (int)elem;
   t.table = t.free_slots = t.free_top = nullptr;
+  t.n_scan = t.scan_per_seq = 0;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == TV_BF16)
     return D == 128 ? launch_step<__bf16, 128>(a, t, st) : launch_step<__bf16, 64>(a, t, st);
@@ -1596,6 +1621,9 @@ extern "C" int tree_verify_step_paged(
   t.table = block_table;
   t.free_slots = free_slots;
   t.free_top = free_top;
+  t.scan_per_seq = ceil_div(max_pages, kScanSlice);
+  if ((long long)B * t.scan_per_seq > (1 << 24)) return TV_ERR_INVALID_ARG;
+  t.n_scan = B * t.scan_per_seq;
   hipStream_t st = (hipStream_t)stream;
   const bool off32 =
       (unsigned long long)num_slots * Hkv * D * (dtype == TV_BF16 ? 2 : 4) <= 0xffffffffull;

@@ -223,7 +223,11 @@ __device__ inline void commit_paged_wave(int b, int L, int n, const int pe[2],
     const int r = k == 0 ? __popcll(m0 & below) : __popcll(m0) + __popcll(m1 & below);
     if (at + r < num_slots) free_slots[at + r] = ts[k];
   }
-  if (lane == 0) cache_len_out[b] = L + n;
+  // release: a workgroup that reads the new length (cache_len_out may be cache_len) with an
+  // acquire also sees the table entries written above
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  if (lane == 0) __hip_atomic_store(cache_len_out + b, L + n, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace tv
