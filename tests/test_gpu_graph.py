@@ -313,3 +313,71 @@ def test_lm_head_replays():
     _replays_match_eager("lm head", lambda: head(d1, b1), b1, lambda: head(d2, b2),
                          poison=poison, clear=[b1["status"], b2["status"]])
     assert int(b1["status"].abs().sum()) == 0
+
+
+def test_fused_paged_step_replays():
+    """tree_verify_step_paged with split-K partials and ragged prefixes: each replay, from the
+    same block table and an empty free list, commits the same path into the same entries."""
+    import tree_attention_verification_attn_amd as tv
+
+    w = make_workload("batch32_L512-4096_T60", B=6, T=60, L=(0, 700), Hq=8, Hkv=2, D=128,
+                      extra_seed=46)
+    w.target[:, :-1] = np.where(np.arange(w.T - 1) % 2 == 0, w.draft[:, 1:], w.target[:, :-1])
+    w2 = make_workload("batch32_L512-4096_T60", B=6, T=60, L=(0, 700), Hq=8, Hkv=2, D=128,
+                       extra_seed=47)
+    pl, pl2 = make_paged(w, 1, seed=17), make_paged(w2, 1, seed=18)
+    g, g2 = upload(w), upload(w2)
+    split = 128
+
+    def dev(p):
+        return dict(k_pool=to_dev(p.k_pool), v_pool=to_dev(p.v_pool),
+                    table=to_dev(p.block_table), slots=to_dev(p.tree_slot),
+                    free=torch.full((p.num_slots,), -1, dtype=torch.int32, device="cuda"),
+                    top=torch.zeros(1, dtype=torch.int32, device="cuda"))
+
+    p, p2 = dev(pl), dev(pl2)
+    table0 = p["table"].clone()
+    ws = torch.empty((max(1, tv.tree_verify_attn_workspace_size(
+        w.B, w.T, w.Hq, w.Hkv, w.D, max(pl.block_table.shape[1], pl2.block_table.shape[1]),
+        torch.bfloat16, split)),), dtype=torch.uint8, device="cuda")
+    bufs, bufs2 = _step_buffers(g, w), _step_buffers(g2, w2)
+
+    def step(x, q, b):
+        tv.tree_verify_step_paged(x["parent"], x["draft"], x["target"], x["q"], q["k_pool"],
+                                  q["v_pool"], q["table"], x["cache_len"], q["slots"], q["free"],
+                                  q["top"], split_keys=split, workspace=ws, **b)
+
+    def reset():
+        p["table"].copy_(table0)
+        p["free"].fill_(-1)
+        p["top"].zero_()
+
+    print("[case] graph tree_verify_step_paged: eager run", flush=True)
+    step(g, p, bufs)
+    torch.cuda.synchronize()
+    ref = {k: _bits(v).clone() for k, v in bufs.items()}
+    ref_table, ref_top = p["table"].clone(), int(p["top"].item())
+    ref_free = sorted(p["free"][:ref_top].tolist())
+    assert int(bufs["status"].abs().sum()) == 0
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    print("[case] graph tree_verify_step_paged: capture", flush=True)
+    with torch.cuda.graph(graph, stream=stream):
+        step(g, p, bufs)
+    torch.cuda.synchronize()
+    for rep in range(REPLAYS):
+        for v in bufs.values():
+            _poison(v)
+        reset()
+        step(g2, p2, bufs2)  # another step eagerly in between: same workspace
+        torch.cuda.synchronize()
+        print(f"[case] graph tree_verify_step_paged: replay {rep}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in bufs.items():
+            assert torch.equal(_bits(v), ref[k]), f"replay {rep} differs in {k}"
+        assert torch.equal(p["table"], ref_table), f"replay {rep}: block table differs"
+        assert int(p["top"].item()) == ref_top
+        assert sorted(p["free"][:ref_top].tolist()) == ref_free
