@@ -1198,11 +1198,16 @@ __device__ inline void tail_scan_pages(const AttnArgs& a, const TailArgs& t, int
   // With cache_len_out aliasing cache_len, the acceptance workgroup of b may already have
   // committed L + n.  Read with acquire against the commit's release, the new length comes with
   // the n new entries, which are tree slots the commit found inside the pool, so the verdict
-  // is the same as over the L entries the attention read.
-  const int L = __hip_atomic_load(const_cast<int32_t*>(a.cache_len) + b, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int Lc = min(max(L, 0), a.Lmax);
+  // is the same as over the L entries the attention read.  One thread reads it, so the whole
+  // workgroup uses one value.
+  __shared__ int s_len;
+  if (tid == 0) {
+    s_len = __hip_atomic_load(const_cast<int32_t*>(a.cache_len) + b, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  const int Lc = min(max(s_len, 0), a.Lmax);
   const int lo = slice * kScanSlice;
   if (lo >= Lc && slice > 0) return;  // uniform
   const int32_t* row = a.table + (size_t)b * a.max_pages;
