@@ -171,6 +171,32 @@ def test_paged_argument_errors(lib):
     assert lib.kv_commit_paged(*bad) == -2
 
 
+def test_step_paged_argument_errors(lib):
+    # parent, draft, target, q, k_pool, v_pool, num_slots, block_table, max_pages, page_size,
+    # cache_len, cache_len_out, tree_slot, anc, out, lse, path, alen, bonus, free_slots,
+    # free_top, status, B, T, Hq, Hkv, D, dtype, scale, split_keys, ws, ws_bytes, stream
+    base = ([FAKE] * 6 + [100, FAKE, 16, 1] + [FAKE] * 12 +
+            [1, 8, 2, 1, 64, 0, 0.0, 0, None, 0, None])
+    ptrs = [0, 1, 2, 3, 4, 5, 7, 10, 11, 12, 13, 14, 16, 17, 18, 19, 20, 21]
+    for i in ptrs:  # every pointer but lse is required
+        bad = list(base)
+        bad[i] = None
+        assert lib.tree_verify_step_paged(*bad) == -1, i
+    for i, v, code in ((9, 4, -2),   # the pointer-swap commit needs one-token pages
+                       (9, 3, -1),   # page size: a power of two
+                       (6, 0, -1),   # empty pool
+                       (8, 0, -1),   # empty table
+                       (26, 96, -2)):  # head_dim
+        bad = list(base)
+        bad[i] = v
+        assert lib.tree_verify_step_paged(*bad) == code, (i, v)
+    bad = list(base)  # partly overlapping cache_len / cache_len_out
+    bad[10] = ctypes.c_void_p(0x2000)
+    bad[11] = ctypes.c_void_p(0x2002)
+    bad[22] = 4
+    assert lib.tree_verify_step_paged(*bad) == -1
+
+
 def test_accept_argument_errors(lib):
     assert lib.tree_accept(None, FAKE, FAKE, 1, 8, FAKE, FAKE, FAKE, None) == -1
     assert lib.tree_accept(FAKE, FAKE, FAKE, 1, 8, FAKE, None, FAKE, None) == -1
