@@ -59,6 +59,7 @@ typedef enum { TV_F32 = 0, TV_BF16 = 1 } tv_dtype;
 #define TV_SYNC_TIMEOUT 0x40 /* stochastic acceptance: its workgroups did not all meet (they were
                                 not resident together); results invalid, re-zero the workspace */
 #define TV_BAD_CONF 0x80 /* draft tree: a drafter confidence outside [0, 1] (used clamped) */
+#define TV_FREE_FULL 0x100 /* paged commit: the free list had no room for some rejected slots */
 
 /* Human-readable name of a tv_status return value or of a single status bit. */
 const char* tv_status_string(int code);
@@ -110,6 +111,9 @@ size_t tree_verify_attn_workspace_size(int B, int T, int Hq, int Hkv, int D, int
  *   workspace  device buffer of at least tree_verify_attn_workspace_size(...) bytes (may be
  *              NULL when that size is 0); holds per-split partial results, no state across
  *              calls.
+ * Row offsets are 32-bit within one (b, kvh) cache slab and within one sequence's tree rows:
+ * Lmax * D * elem and T * Hkv * D * elem may not exceed 4 GiB (TV_ERR_INVALID_ARG otherwise;
+ * also for tree_verify_step).
  */
 int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* cache_len, const void* k_tree, const void* v_tree,
@@ -271,14 +275,18 @@ int tree_verify_attn_paged(const void* q, const void* k_pool, const void* v_pool
  *   free_slots  [num_slots]    int32  out: rejected slots are written at free_top, free_top+1, ..
  *                                     in node order per sequence (the order between sequences
  *                                     follows the atomics); entries at or past num_slots are not
- *                                     written
+ *                                     written, and a sequence whose rejected slots do not all fit
+ *                                     gets TV_FREE_FULL (which sequence that is, when several
+ *                                     commit into a full list, follows the atomics)
  *   free_top    [1]            int32  in/out: advanced by the number of rejected nodes
  *   status      [B]            int32  optional (NULL): TV_BAD_LEN (cache_len outside
  *                                     [0, max_pages]), TV_BAD_PATH (bad accept_len, an accepted
  *                                     index outside [0, T) or repeated, a tree slot outside the
  *                                     pool) or TV_OVERFLOW (L_b + accept_len[b] > max_pages)
  *                                     OR-ed in; such a sequence commits nothing, frees nothing
- *                                     and keeps cache_len_out[b] = cache_len[b]
+ *                                     and keeps cache_len_out[b] = cache_len[b].  TV_FREE_FULL
+ *                                     is OR-ed in as well by a sequence that committed but
+ *                                     could not write every rejected slot
  */
 int kv_commit_paged(int32_t* block_table, int max_pages, int page_size, const int32_t* cache_len,
                     int32_t* cache_len_out, const int32_t* tree_slot, const int32_t* accept_path,

@@ -16,6 +16,7 @@ ORC_BAD_TREE = 0x1
 ORC_OVERFLOW = 0x2
 ORC_BAD_LEN = 0x4
 ORC_BAD_PATH = 0x8
+ORC_FREE_FULL = 0x100
 ORC_BAD_TOKEN = 0x20
 ORC_BAD_CONF = 0x80
 

@@ -61,6 +61,7 @@
 #define ORC_OVERFLOW 0x2
 #define ORC_BAD_LEN 0x4
 #define ORC_BAD_PATH 0x8
+#define ORC_FREE_FULL 0x100 /* pointer-swap commit: the free list had no room for a rejected slot */
 
 /* ------------------------------------------------------------------------------------------ */
 /* tree paths                                                                                  */
@@ -410,7 +411,8 @@ int oracle_paged_gather(int elem_bytes, const void* k_pool, const void* v_pool, 
  * order: the length, path and slots are checked (a failing sequence commits nothing and keeps
  * its length, as oracle_compact); then table[b][L + k] = tree_slot[b][path[k]] for k < n, and
  * the slots of the nodes not on the path are appended to free_slots in node order at
- * *free_top, which advances by their number (entries at or past num_slots are not written). */
+ * *free_top, which advances by their number; entries at or past num_slots are not written,
+ * and a sequence with such an entry is flagged as having found the free list full. */
 void oracle_commit_paged(int32_t* table, int max_pages, const int32_t* cache_len,
                          int32_t* cache_len_out, const int32_t* tree_slot,
                          const int32_t* accept_path, const int32_t* accept_len, int B, int T,
@@ -447,6 +449,7 @@ void oracle_commit_paged(int32_t* table, int max_pages, const int32_t* cache_len
       if (on_path[j]) continue;
       int at = (*free_top)++;
       if (at < num_slots) free_slots[at] = tree_slot[(size_t)b * T + j];
+      else status[b] |= ORC_FREE_FULL;
     }
     cache_len_out[b] = L + n;
   }

@@ -93,9 +93,42 @@ def sample_rows(w, n_random: int, seed: int = 0) -> np.ndarray:
     return np.array(sorted(rows), np.int32)
 
 
-def check_step(w, res: dict, rows: np.ndarray | None = None, label: str = "") -> dict:
+# Sharp softmax (a large explicit scale, peaked rows): an output row approaches one V row, whose
+# entries reach 4..5 for N(0,1) values.  A bf16 output of that size carries up to 2^-8 of its
+# value from its own rounding, and the bf16 rounding of P before P.V adds up to 2^-8 of
+# sum p|v| / l, which is then about |o|.  Those cases are held to 2e-2 + 2^-7 |o|, elementwise.
+RTOL_SHARP = {"f32": 0.0, "bf16": 2.0 ** -7}
+
+
+def score_error_bound(w, scale: float | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """Float32 rounding bound of the scores, per row (b, node, query head): a score
+    scale * sum_d q_d k_d accumulated in float32 errs by at most (D + 3) 2^-24 scale
+    sum_d |q_d k_d| (D products and sums, the scale, the log2(e) factor, the exponent).  Taken
+    over every prefix and tree key of the row's KV head (a superset of the visible keys).
+    Perturbing the scores by at most ds moves the softmax output by at most 2 ds max|v| and lse
+    by at most ds.  Returns (ds [B, T, Hq], max|v| [B, T, Hq])."""
+    scale = w.scale if scale is None else scale
+    G = w.Hq // w.Hkv
+    ds = np.zeros((w.B, w.T, w.Hq))
+    vmax = np.zeros((w.B, w.T, w.Hq))
+    for b in range(w.B):
+        L = int(np.clip(w.cache_len[b], 0, w.Lmax))
+        for kvh in range(w.Hkv):
+            K = np.abs(np.concatenate([as_f64(w.k_cache[b, kvh, :L]), as_f64(w.k_tree[b, :, kvh])]))
+            V = np.abs(np.concatenate([as_f64(w.v_cache[b, kvh, :L]), as_f64(w.v_tree[b, :, kvh])]))
+            Q = np.abs(as_f64(w.q[b, :, kvh * G:(kvh + 1) * G]))  # [T, G, D]
+            mag = (Q.reshape(-1, w.D) @ K.T).max(axis=1).reshape(w.T, G)
+            ds[b, :, kvh * G:(kvh + 1) * G] = (w.D + 3) * 2.0 ** -24 * scale * mag
+            vmax[b, :, kvh * G:(kvh + 1) * G] = V.max()
+    return ds, vmax
+
+
+def check_step(w, res: dict, rows: np.ndarray | None = None, label: str = "",
+               rtol: float = 0.0, score_err: tuple | None = None) -> dict:
     """Compare a device step with the oracle.  Integer results and the cache bytes must match
-    exactly; attention within the dtype's tolerance (all rows, or the sampled ones)."""
+    exactly; attention within the dtype's tolerance (all rows, or the sampled ones), plus
+    `rtol` times the exact value's magnitude, plus (with `score_err` from score_error_bound)
+    what the float32 rounding of the scores can move the output and lse by."""
     o_anc, o_st = O.build_mask(w.parent)
     assert np.array_equal(res["anc"], o_anc), f"{label}: ancestor mask differs"
     o_path, o_len, o_bonus = O.accept(w.parent, w.draft, w.target)
@@ -128,6 +161,14 @@ def check_step(w, res: dict, rows: np.ndarray | None = None, label: str = "") ->
     err = float(np.abs(got - o_out).max())
     lerr = float(np.abs(got_lse - o_lse).max())
     assert np.isfinite(got).all(), f"{label}: non-finite attention output"
-    assert err <= TOL_OUT[w.dtype], f"{label}: attention max-abs error {err}"
-    assert lerr <= TOL_LSE[w.dtype], f"{label}: lse max-abs error {lerr}"
+    tol_o, tol_l = TOL_OUT[w.dtype] + rtol * np.abs(o_out), np.full(o_lse.shape, TOL_LSE[w.dtype])
+    if score_err is not None:
+        ds, vmax = score_err
+        if rows is not None:
+            ds, vmax = ds[rows[:, 0], rows[:, 2], rows[:, 1]], vmax[rows[:, 0], rows[:, 2], rows[:, 1]]
+        tol_o = tol_o + (2 * ds * vmax)[..., None]
+        tol_l = tol_l + ds
+    excess = float((np.abs(got - o_out) - tol_o).max())
+    assert excess <= 0, f"{label}: attention max-abs error {err} (rtol {rtol})"
+    assert (np.abs(got_lse - o_lse) <= tol_l).all(), f"{label}: lse max-abs error {lerr}"
     return dict(err=err, lse_err=lerr)

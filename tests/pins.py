@@ -581,6 +581,21 @@ def pin_commit_paged_hand_case(lib):
     assert list(table[0]) == [40, 41, 42, 50, 52, 55] + [-1] * 6
     assert out_len[0] == 6 and top == 15 and st[0] == 0
     assert list(free[10:15]) == [51, 53, 54, 56, 57] and (free[:10] == -7).all()
+    # a free list with room for three of the five rejected slots: the table is still committed,
+    # the first three slots are written, nothing at or past num_slots, and the sequence is told
+    table[0, 3:] = -1
+    free[:] = -7
+    out_len, top, st = O.commit_paged(table, np.array([3], np.int32), tree_slot, path,
+                                      np.array([3], np.int32), 60, free, 57, lib=lib)
+    assert list(table[0]) == [40, 41, 42, 50, 52, 55] + [-1] * 6 and out_len[0] == 6
+    assert top == 62 and st[0] == O.ORC_FREE_FULL
+    assert list(free[57:60]) == [51, 53, 54] and (free[60:] == -7).all()
+    # exactly full: no flag
+    free[:] = -7
+    table[0, 3:] = -1
+    out_len, top, st = O.commit_paged(table, np.array([3], np.int32), tree_slot, path,
+                                      np.array([3], np.int32), 60, free, 55, lib=lib)
+    assert top == 60 and st[0] == 0 and list(free[55:60]) == [51, 53, 54, 56, 57]
 
 
 def pin_commit_paged_matches_copy(lib):

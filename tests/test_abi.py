@@ -58,9 +58,11 @@ def test_status_strings(lib):
 
     for code in (tv.TV_OK, tv.TV_ERR_INVALID_ARG, tv.TV_ERR_UNSUPPORTED, tv.TV_ERR_WORKSPACE,
                  tv.TV_ERR_HIP, tv.TV_BAD_TREE, tv.TV_OVERFLOW, tv.TV_BAD_LEN, tv.TV_BAD_PATH,
-                 tv.TV_BAD_PAGE, tv.TV_BAD_TOKEN):
+                 tv.TV_BAD_PAGE, tv.TV_BAD_TOKEN, tv.TV_SYNC_TIMEOUT, tv.TV_BAD_CONF,
+                 tv.TV_FREE_FULL):
         assert lib.tv_status_string(code)
     assert b"TV_BAD_TOKEN" in lib.tv_status_string(tv.TV_BAD_TOKEN)
+    assert b"TV_FREE_FULL" in lib.tv_status_string(tv.TV_FREE_FULL)
     assert b"unknown" in lib.tv_status_string(12345)
 
 
@@ -105,6 +107,11 @@ def test_attention_argument_errors(lib):
     assert need > 0
     assert _attn(lib, Lmax=4096, split=256) == -3
     assert _attn(lib, Lmax=4096, split=256, ws=FAKE, wsb=need - 1) == -3
+    # row offsets are 32-bit within a (b, kvh) cache slab and a sequence's tree rows
+    big = 1 << 62
+    assert _attn(lib, Lmax=(1 << 24) + 1, D=128, dt=1, ws=FAKE, wsb=big) == -1
+    assert _attn(lib, Lmax=(1 << 23) + 1, D=128, dt=0, ws=FAKE, wsb=big) == -1
+    assert _attn(lib, T=128, Hq=131073, Hkv=131073, D=128, dt=1, ws=FAKE, wsb=big) == -1
 
 
 def test_workspace_size_rules(lib):
@@ -138,6 +145,11 @@ def test_step_argument_errors(lib):
     bad = list(base)
     bad[21] = 96    # head_dim
     assert lib.tree_verify_step(*bad) == -2
+    # a (b, kvh) cache slab past 4 GiB (32-bit row offsets)
+    bad = list(base)
+    bad[21], bad[22], bad[23] = 128, (1 << 24) + 1, 1
+    bad[26], bad[27] = FAKE, 1 << 62
+    assert lib.tree_verify_step(*bad) == -1
     # partly overlapping cache_len / cache_len_out
     bad = list(base)
     bad[6] = ctypes.c_void_p(0x2000)

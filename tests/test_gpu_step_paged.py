@@ -109,7 +109,10 @@ def _oracle_check(w, pl, res, rows=None, spare_top=0):
     ("batch32_L512-4096_T60", dict(B=5, T=33, L=(0, 300)), 64, False),
     ("wide_b64_L1024-8192_T128", dict(B=3, L=(10, 400)), 0, False),
     ("batch32_L512-4096_T60", {}, 0, True),
-], ids=["llama8b_b1", "batch6", "ragged_split64", "wide_T128", "batch32_full_sampled"])
+    ("llama70b_b8_L32768_T64", {}, 0, True),
+    ("wide_b64_L1024-8192_T128", {}, 0, True),
+], ids=["llama8b_b1", "batch6", "ragged_split64", "wide_T128", "batch32_full_sampled",
+        "llama70b_full_sampled", "wide_full_sampled"])
 def test_step_paged_matches_oracle(name, kw, split_keys, sampled):
     w = make_workload(name, **kw, extra_seed=41)
     # accept a few levels: some drafts equal their parent's target token
@@ -178,3 +181,22 @@ def test_step_paged_rejects_larger_pages():
                                   to_dev(pl.k_pool), to_dev(pl.v_pool), to_dev(pl.block_table),
                                   g["cache_len"], to_dev(pl.tree_slot), free, top, page_size=4)
     assert e.value.code == tv.TV_ERR_UNSUPPORTED
+
+
+def test_step_paged_free_list_full():
+    """A free list with room for only two of the rejected slots: the path is still committed,
+    two slots are written, nothing past the list's end, and the sequence gets TV_FREE_FULL
+    (batch 1, so which sequence found the list full is unique)."""
+    import tree_attention_verification_attn_amd as tv
+
+    w = make_workload("llama8b_b1_L4096_T60", L=(300, 300), extra_seed=46)
+    w.target[:, :-1] = np.where(np.arange(w.T - 1) % 3 == 0, w.draft[:, 1:], w.target[:, :-1])
+    pl = make_paged(w, 1, seed=18)
+    spare_top = pl.num_slots - 2
+    print(f"[case] step_paged free list full (top {spare_top} of {pl.num_slots})", flush=True)
+    res = _fused(w, pl, spare_top=spare_top)
+    assert res["status"][0] & tv.TV_FREE_FULL
+    _oracle_check(w, pl, res, spare_top=spare_top)
+    assert (res["free"][:spare_top] == -1).all()
+    sep = _separate(w, pl, spare_top=spare_top)
+    _same(res, sep, spare_top=spare_top)

@@ -162,6 +162,8 @@ MUTANTS = {
                            "u[(size_t)m * r + i] = dot_seg64(Bm + (size_t)(i % r) * d, h + (size_t)(i % M) * d, d);"),
     # LM head: out-of-vocabulary candidates not reported
     "lm_bad_token_silent": ("if (tok != -1) status[m] |= ORC_BAD_TOKEN;", ""),
+    # paged commit: a full free list not reported
+    "commit_free_full_silent": ("else status[b] |= ORC_FREE_FULL;", ""),
 }
 
 

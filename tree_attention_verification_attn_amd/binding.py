@@ -17,7 +17,7 @@ from . import build as _build
 TV_OK, TV_ERR_INVALID_ARG, TV_ERR_UNSUPPORTED, TV_ERR_WORKSPACE, TV_ERR_HIP = 0, -1, -2, -3, -4
 TV_F32, TV_BF16 = 0, 1
 TV_BAD_TREE, TV_OVERFLOW, TV_BAD_LEN, TV_BAD_PATH, TV_BAD_PAGE = 0x1, 0x2, 0x4, 0x8, 0x10
-TV_BAD_TOKEN, TV_SYNC_TIMEOUT, TV_BAD_CONF = 0x20, 0x40, 0x80
+TV_BAD_TOKEN, TV_SYNC_TIMEOUT, TV_BAD_CONF, TV_FREE_FULL = 0x20, 0x40, 0x80, 0x100
 
 EXPORTS = ("tv_status_string", "tree_build_mask", "tree_verify_attn_workspace_size",
            "tree_verify_attn", "tree_accept", "kv_compact_accepted", "tv_profile_attn_main",

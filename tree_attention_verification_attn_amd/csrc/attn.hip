@@ -208,14 +208,14 @@ __device__ inline int xcd_remap(int bid, int n) {
 // follow each other on the same XCD: every XCD gets a longest-first share of the work.
 constexpr int kLptMaxPairs = 256;
 
-__device__ inline void lpt_item(const AttnArgs& a, int* scratch, int& b, int& s, int& kvh,
+__device__ inline void lpt_item(const AttnArgs& a, int* lds, int& b, int& s, int& kvh,
                                 int& rb) {
   const int P = a.B * a.S;
   const int P4 = (P + 3) & ~3;
   const int tid = threadIdx.x;
   const int tree_tiles = ceil_div(a.T, kKT);
-  int* sz = scratch;        // [P4] tiles of each pair; padding -1 ranks after every pair
-  int* ord = scratch + P4;  // [P] pair of each rank
+  int* sz = lds;        // [P4] tiles of each pair; padding -1 ranks after every pair
+  int* ord = lds + P4;  // [P] pair of each rank
   for (int i = tid; i < P4; i += kThreads) {
     int v = -1;
     if (i < P) {
@@ -249,7 +249,7 @@ __device__ inline void lpt_item(const AttnArgs& a, int* scratch, int& b, int& s,
   const int pair = ord[U / a.Hkv];
   b = pair / a.S;
   s = pair - b * a.S;
-  __syncthreads();  // the scratch is the K/V ring, which the first tile loads overwrite
+  __syncthreads();  // this LDS is the K/V ring, which the first tile loads overwrite
 }
 
 // Score block j = 32 keys: tile j/2, half j%2.  P of a block: bf16 operands or fp32 values.
@@ -1048,12 +1048,16 @@ __device__ void combine_group(const AttnArgs& a, int c) {
                         __uint_as_float(v[u].z), __uint_as_float(v[u].w)};
         }
       };
-      // every non-empty chunk has a finite m (each row sees a key in it), so Mb is finite
+      // A chunk in which a row sees no key (a second tree tile that holds none of the row's
+      // ancestors, cut into a chunk of its own) carries m = -inf, l = 0, O = 0.  When every
+      // chunk so far is such a chunk, Mb is -inf too; the exponents are then taken against 0,
+      // so those chunks weigh 0 instead of 2^(-inf - -inf) = NaN.
       float Mb = M[i];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
         if (u < nb) Mb = fmaxf(Mb, m_of(u));
-      const float sc = fast_exp2(M[i] - Mb);  // 0 on the first batch
+      const float Me = Mb == -INFINITY ? 0.f : Mb;
+      const float sc = fast_exp2(M[i] - Me);  // 0 on the first batch
       den[i] *= sc;
       acc[i].x *= sc;
       acc[i].y *= sc;
@@ -1062,7 +1066,7 @@ __device__ void combine_group(const AttnArgs& a, int c) {
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
         if (u < nb) {
-          const float w = fast_exp2(m_of(u) - Mb);
+          const float w = fast_exp2(m_of(u) - Me);
           const float4 x = val_of(u);
           den[i] += w * l_of(u);
           acc[i].x += w * x.x;
@@ -1089,8 +1093,9 @@ __device__ void combine_group(const AttnArgs& a, int c) {
       float Mt = M[i];
 #pragma unroll
       for (int q = 1; q < kSW; ++q) Mt = fmaxf(Mt, s_mden[q][pl][i].x);
-      // group 0 always holds chunk 0, so Mt is finite for live rows; an empty group has
-      // M = -inf, den = 0 and O = 0, and weight 0
+      // group 0 always holds chunk 0, whose first tile holds the root (visible to every row),
+      // so Mt is finite for live rows; a group that saw no key has M = -inf, den = 0, O = 0
+      // and weight 0
       const float sc = fast_exp2(M[i] - Mt);
       den[i] *= sc;
       acc[i].x *= sc;
@@ -1454,6 +1459,13 @@ static int prepare_attn(AttnArgs& a, Plan& p, const void* q, const void* k_cache
   return TV_OK;
 }
 
+// The dense main kernel forms each K/V row's byte offset in 32 bits, within one (b, kvh) cache
+// slab and within the sequence's tree rows; larger slabs are refused rather than wrapped.
+static bool dense_offsets_ok(int T, int Hkv, int D, int Lmax, int dtype) {
+  const long long row = (long long)D * (dtype == TV_BF16 ? 2 : 4);
+  return (long long)Lmax * row <= (1LL << 32) && (long long)T * Hkv * row <= (1LL << 32);
+}
+
 extern "C" int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                                 const int32_t* cache_len, const void* k_tree, const void* v_tree,
                                 const uint64_t* anc_mask, void* out, float* lse, int32_t* status,
@@ -1466,6 +1478,7 @@ extern "C" int tree_verify_attn(const void* q, const void* k_cache, const void* 
                               out, lse, status, B, T, Hq, Hkv, D, Lmax, dtype, scale, split_keys,
                               workspace, workspace_bytes);
   if (rc != TV_OK) return rc;
+  if (!dense_offsets_ok(T, Hkv, D, Lmax, dtype)) return TV_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == TV_BF16)
     return D == 128 ? launch_attn<__bf16, 128>(a, st) : launch_attn<__bf16, 64>(a, st);
@@ -1532,6 +1545,7 @@ extern "C" int tree_verify_step(const int32_t* parent, const int32_t* draft_tok,
                         status, B, T, Hq, Hkv, D, Lmax, dtype, scale, split_keys, workspace,
                         workspace_bytes);
   if (rc != TV_OK) return rc;
+  if (!dense_offsets_ok(T, Hkv, D, Lmax, dtype)) return TV_ERR_INVALID_ARG;
   if (cache_len_out != cache_len &&
       overlaps(cache_len_out, (size_t)B * 4, cache_len, (size_t)B * 4))
     return TV_ERR_INVALID_ARG;
@@ -1639,3 +1653,4 @@ extern "C" int tree_verify_step_paged(
   }
   return D == 128 ? launch_step<float, 128, 1>(a, t, st) : launch_step<float, 64, 1>(a, t, st);
 }
+

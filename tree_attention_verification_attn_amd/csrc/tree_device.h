@@ -155,8 +155,9 @@ __device__ inline int accept_walk(int b, int T, int W, const uint64_t* __restric
 // on free_top and written in node order.  Nothing is copied.  pe[k] is path entry lane + 64k
 // (only entries below n are used), L the sequence's length before the step.  A bad length, path
 // or tree slot, or a table too short for L + n, commits and frees nothing, keeps the length and
-// OR-s the reason into status[b] (if status is not null).  s_on is LDS scratch of kMaxT ints
-// used by this wavefront alone.
+// OR-s the reason into status[b] (if status is not null).  Rejected slots that find no room in
+// the free list (past num_slots) are not written, and TV_FREE_FULL is OR-ed in.  s_on is LDS
+// scratch of kMaxT ints used by this wavefront alone.
 __device__ inline void commit_paged_wave(int b, int L, int n, const int pe[2],
                                          int32_t* __restrict__ table, int max_pages,
                                          const int32_t* __restrict__ tree_slot, int T,
@@ -223,6 +224,9 @@ __device__ inline void commit_paged_wave(int b, int L, int n, const int pe[2],
     const int r = k == 0 ? __popcll(m0 & below) : __popcll(m0) + __popcll(m1 & below);
     if (at + r < num_slots) free_slots[at + r] = ts[k];
   }
+  // slots that found no room in the free list are lost to it: report that
+  if (lane == 0 && status && cnt && (long long)at + cnt > num_slots)
+    atomicOr(status + b, TV_FREE_FULL);
   // release: a workgroup that reads the new length (cache_len_out may be cache_len) with an
   // acquire also sees the table entries written above
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");

@@ -209,6 +209,7 @@ extern "C" const char* tv_status_string(int code) {
     case TV_SYNC_TIMEOUT:
       return "TV_SYNC_TIMEOUT: the workgroups of a sequence did not all meet; re-zero the workspace";
     case TV_BAD_CONF: return "TV_BAD_CONF: a drafter confidence outside [0, 1] (used clamped)";
+    case TV_FREE_FULL: return "TV_FREE_FULL: the free list had no room for some rejected slots";
     default: return "unknown tree_verify status";
   }
 }
