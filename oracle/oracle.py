@@ -79,10 +79,14 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_eagle2_build.restype = i
     lib.oracle_lm_project.argtypes = [P, P, i, i, i, P]
     lib.oracle_lm_project.restype = None
-    lib.oracle_lm_screen.argtypes = [P, P, P, i, i, i, i, i, P, P]
+    lib.oracle_lm_scores.argtypes = [P, P, i, i, i, P]
+    lib.oracle_lm_scores.restype = None
+    lib.oracle_lm_screen.argtypes = [P, P, i, i, i, i, P, P]
     lib.oracle_lm_screen.restype = None
     lib.oracle_lm_rescore.argtypes = [P, P, P, i, i, i, i, P, P]
     lib.oracle_lm_rescore.restype = None
+    lib.oracle_lm_logits_all.argtypes = [P, P, i, i, i, P, i]
+    lib.oracle_lm_logits_all.restype = None
     lib.oracle_lm_topk.argtypes = [P, P, i, i, i, i, P, P]
     lib.oracle_lm_topk.restype = None
     return lib
@@ -340,54 +344,78 @@ def _bf16(a) -> np.ndarray:
 
 
 def lm_project(h, Bm, lib=None) -> np.ndarray:
-    """u [M, r] float32 = B h, each entry by the fixed-order float32 dot product (dot_seg64).
-    h [M, d] and B [r, d] are bfloat16 bit patterns; d a multiple of 512."""
+    """u [M, r] float64 = B h (exact products, fp64 sum).  h [M, d] and B [r, d] are bfloat16
+    bit patterns."""
     lib = lib or load()
     h, Bm = _bf16(h), _bf16(Bm)
     M, d = h.shape
     r = Bm.shape[0]
-    assert Bm.shape[1] == d and d % 512 == 0
-    u = np.empty((M, r), np.float32)
+    assert Bm.shape[1] == d
+    u = np.empty((M, r), np.float64)
     lib.oracle_lm_project(_p(h), _p(Bm), M, r, d, _p(u))
     return u
 
 
-def lm_screen(A, u, row_token, tile, k_tile, lib=None) -> tuple[np.ndarray, np.ndarray]:
-    """Local top-k screening: (cand [M, n_tiles*k_tile] int32 tokens, cand_score float32)."""
+def lm_scores(A, u, lib=None) -> np.ndarray:
+    """Approximate score of every stored row of A for every hidden state: [M, n] float64."""
     lib = lib or load()
     A = _bf16(A)
-    u = np.ascontiguousarray(u, dtype=np.float32)
-    row_token = _i32(row_token)
+    u = np.ascontiguousarray(u, dtype=np.float64)
     n, r = A.shape
     M = u.shape[0]
-    assert u.shape[1] == r and row_token.shape == (n,)
+    assert u.shape[1] == r
+    s = np.empty((M, n), np.float64)
+    lib.oracle_lm_scores(_p(A), _p(u), M, r, n, _p(s))
+    return s
+
+
+def lm_screen(A, u, row_token, tile, k_tile, lib=None) -> tuple[np.ndarray, np.ndarray]:
+    """Local top-k screening: (cand [M, n_tiles*k_tile] int32 tokens, cand_score float64)."""
+    lib = lib or load()
+    s = lm_scores(A, u, lib=lib)
+    row_token = _i32(row_token)
+    M, n = s.shape
+    assert row_token.shape == (n,)
     C = (n + tile - 1) // tile * k_tile
     cand = np.empty((M, C), np.int32)
-    score = np.empty((M, C), np.float32)
-    lib.oracle_lm_screen(_p(A), _p(u), _p(row_token), M, r, n, int(tile), int(k_tile), _p(cand),
+    score = np.empty((M, C), np.float64)
+    lib.oracle_lm_screen(_p(s), _p(row_token), M, n, int(tile), int(k_tile), _p(cand),
                          _p(score))
     return cand, score
 
 
 def lm_rescore(W, h, cand, lib=None) -> tuple[np.ndarray, np.ndarray]:
-    """Exact candidate logits [M, C] float32 (dot_seg64 of W's rows and h) and status [M]."""
+    """Exact candidate logits [M, C] float64 (W's rows dotted with h) and status [M]."""
     lib = lib or load()
     W, h = _bf16(W), _bf16(h)
     cand = _i32(cand)
     V, d = W.shape
     M, C = cand.shape
-    assert d % 512 == 0
-    logits = np.empty((M, C), np.float32)
+    logits = np.empty((M, C), np.float64)
     status = np.zeros(M, np.int32)
     lib.oracle_lm_rescore(_p(W), _p(h), _p(cand), M, C, d, V, _p(logits), _p(status))
     return logits, status
+
+
+def lm_logits_all(W, h, n_threads=None, lib=None) -> np.ndarray:
+    """Exact logit of every vocabulary token for every hidden state: [M, V] float64."""
+    lib = lib or load()
+    W, h = _bf16(W), _bf16(h)
+    V, d = W.shape
+    M = h.shape[0]
+    assert h.shape[1] == d
+    if n_threads is None:
+        n_threads = len(os.sched_getaffinity(0))
+    logits = np.empty((M, V), np.float64)
+    lib.oracle_lm_logits_all(_p(W), _p(h), M, d, V, _p(logits), int(n_threads))
+    return logits
 
 
 def lm_topk(logits, cand, K, V, lib=None) -> tuple[np.ndarray, np.ndarray]:
     """The K best valid candidates per hidden state (tokens [M, K] int32) and their softmax
     confidences over the candidates ([M, K] float64)."""
     lib = lib or load()
-    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    logits = np.ascontiguousarray(logits, dtype=np.float64)
     cand = _i32(cand)
     M, C = cand.shape
     tok = np.empty((M, K), np.int32)

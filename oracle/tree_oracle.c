@@ -45,8 +45,9 @@
  *   drafter LM     (jialefu.github.io, EAGLE-4 efficient LM head) two stages: a low-rank head
  *   head           scores the vocabulary and a local top-k per tile of shuffled rows keeps
  *                  candidates; the full head's rows recompute their logits exactly; the
- *                  drafter's children are the best of them.  Float32 in the kernels' stated
- *                  summation order, since the values choose integers (candidate tokens).
+ *                  drafter's children are the best of them.  All in fp64 (plain dot
+ *                  products); the float32 kernels are checked for validity against these
+ *                  exact values within the float32 rounding bound.
  *
  * Floating inputs are either float32 (elem_bits = 32) or raw bfloat16 bit patterns
  * (elem_bits = 16), which are widened exactly.
@@ -746,91 +747,69 @@ int oracle_eagle2_build(const int32_t* root_tok, const int32_t* child_tok,
 /* ------------------------------------------------------------------------------------------ */
 /*
  * Stage one scores the whole vocabulary with a low-rank head: u = B h, then A u, and keeps
- * candidates by a local top-k inside each tile of vocabulary rows (rows shuffled beforehand,
- * row_token[row] naming the token of each row).  Stage two recomputes the candidates' logits
- * exactly from the full head's rows, W[token] . h.  The drafter then takes its top children
- * and their confidences (a softmax over the candidates).  Which candidates are kept and which
- * children chosen is decided by float32 values, so these are computed in the float32
- * arithmetic, and the summation order, that the kernels use:
- *   dot_seg64   d is a multiple of 512.  Chain j (j = 0 .. 63) runs fused multiply-adds from 0
- *               over elements 512 p + 8 j + e, for p = 0 .. d/512 - 1 and e = 0 .. 7 in that
- *               order (p outer); then the 64 chain sums are combined pairwise, sum j with sum
- *               j ^ 32, then j ^ 16, ..., j ^ 1; the result is that of chain 0.
- *   screening   one chain of fused multiply-adds over the rank index, in order, from 0.
- * Values are ranked by the float's order with -0 taken as +0 (an unsigned key of the bits);
- * equal values go to the smaller row (screening) or the smaller token (final selection).
+ * candidates by a local top-k inside each tile of consecutive rows of A, whose rows were
+ * shuffled beforehand (row_token[row] names the token of each row).  Stage two recomputes the
+ * candidates' logits exactly from the full head's rows, W[token] . h.  The drafter's children
+ * are the best of those candidates, with a softmax over the candidates as confidence.
+ *
+ * Everything here is the plain definition in fp64: each dot product is one loop in index order,
+ * bfloat16 inputs widened exactly.  Ties at equal value go to the smaller row (screening) or
+ * the smaller token (children).  The GPU kernels compute in float32; their choices are checked
+ * for validity against these exact values and the float32 rounding bound, not bit for bit.
  */
 
-static float bf16f(uint16_t b) {
+static double bf16d(uint16_t b) {
   union {
     uint32_t u;
     float f;
   } x;
   x.u = (uint32_t)b << 16;
-  return x.f;
+  return (double)x.f;
 }
 
-/* Unsigned key in the order of the float value (-0 as +0; NaN above +inf or below -inf). */
-static uint32_t float_key(float v) {
-  union {
-    float f;
-    uint32_t u;
-  } x;
-  x.f = v + 0.0f;
-  return (x.u & 0x80000000u) ? ~x.u : (x.u | 0x80000000u);
+static double dot_bf16(const uint16_t* x, const uint16_t* y, int d) {
+  double acc = 0.0;
+  for (int i = 0; i < d; ++i) acc += bf16d(x[i]) * bf16d(y[i]);
+  return acc;
 }
 
-static float dot_seg64(const uint16_t* x, const uint16_t* y, int d) {
-  float v[64], w[64];
-  for (int j = 0; j < 64; ++j) {
-    float acc = 0.0f;
-    for (int p = 0; p < d / 512; ++p)
-      for (int e = 0; e < 8; ++e) {
-        const int i = 512 * p + 8 * j + e;
-        acc = fmaf(bf16f(x[i]), bf16f(y[i]), acc);
-      }
-    v[j] = acc;
-  }
-  for (int off = 32; off >= 1; off >>= 1) {
-    for (int j = 0; j < 64; ++j) w[j] = v[j] + v[j ^ off];
-    for (int j = 0; j < 64; ++j) v[j] = w[j];
-  }
-  return v[0];
-}
-
-/* u[m, i] = B[i, :] . h[m, :] (dot_seg64); h [M, d], B [r, d] bfloat16 bits; d % 512 == 0. */
-void oracle_lm_project(const uint16_t* h, const uint16_t* Bm, int M, int r, int d, float* u) {
+/* u[m, i] = B[i, :] . h[m, :]; h [M, d], B [r, d] bfloat16 bits. */
+void oracle_lm_project(const uint16_t* h, const uint16_t* Bm, int M, int r, int d, double* u) {
   for (int m = 0; m < M; ++m)
     for (int i = 0; i < r; ++i)
-      u[(size_t)m * r + i] = dot_seg64(Bm + (size_t)i * d, h + (size_t)m * d, d);
+      u[(size_t)m * r + i] = dot_bf16(Bm + (size_t)i * d, h + (size_t)m * d, d);
 }
 
-/* Screening: for hidden state m and tile t of `tile` consecutive rows of A [n, r] (bfloat16),
- * score(row) = the fused multiply-add chain of A[row, i] * u[m, i] over i = 0 .. r-1; the
- * k_tile best rows of the tile (by score, then smaller row) become candidates
- * cand[m, t * k_tile + j] = row_token[row], best first, with their scores in cand_score; a
- * tile with fewer rows pads with token -1 and score -inf. */
-void oracle_lm_screen(const uint16_t* A, const float* u, const int32_t* row_token, int M, int r,
-                      int n, int tile, int k_tile, int32_t* cand, float* cand_score) {
+/* Approximate score of every stored row of A [n, r] (bfloat16) for every hidden state:
+ * s[m, row] = A[row, :] . u[m, :]. */
+void oracle_lm_scores(const uint16_t* A, const double* u, int M, int r, int n, double* s) {
+  for (int m = 0; m < M; ++m)
+    for (int row = 0; row < n; ++row) {
+      const uint16_t* a = A + (size_t)row * r;
+      double acc = 0.0;
+      for (int i = 0; i < r; ++i) acc += bf16d(a[i]) * u[(size_t)m * r + i];
+      s[(size_t)m * n + row] = acc;
+    }
+}
+
+/* Local top-k: tile t holds rows t*tile .. t*tile + tile - 1 (the last one may be shorter).
+ * Its k_tile best rows by score (ties to the smaller row), best first, become candidates
+ * cand[m, t * k_tile + j] = row_token[row] with score cand_score[m, t * k_tile + j]; a tile of
+ * fewer rows pads with token -1 and score -inf.  s is oracle_lm_scores' output. */
+void oracle_lm_screen(const double* s, const int32_t* row_token, int M, int n, int tile,
+                      int k_tile, int32_t* cand, double* cand_score) {
   const int n_tiles = (n + tile - 1) / tile;
   const int C = n_tiles * k_tile;
-  float* s = (float*)malloc(sizeof(float) * (size_t)tile);
   char* taken = (char*)malloc((size_t)tile);
   for (int m = 0; m < M; ++m) {
-    const float* um = u + (size_t)m * r;
+    const double* sm = s + (size_t)m * n;
     for (int t = 0; t < n_tiles; ++t) {
       const int r0 = t * tile, rows = n - r0 < tile ? n - r0 : tile;
-      for (int q = 0; q < rows; ++q) {
-        const uint16_t* a = A + (size_t)(r0 + q) * r;
-        float acc = 0.0f;
-        for (int i = 0; i < r; ++i) acc = fmaf(bf16f(a[i]), um[i], acc);
-        s[q] = acc;
-        taken[q] = 0;
-      }
+      memset(taken, 0, (size_t)tile);
       for (int j = 0; j < k_tile; ++j) {
         int best = -1;
         for (int q = 0; q < rows; ++q)
-          if (!taken[q] && (best < 0 || float_key(s[q]) > float_key(s[best]))) best = q;
+          if (!taken[q] && (best < 0 || sm[r0 + q] > sm[r0 + best])) best = q;
         const size_t o = (size_t)m * C + (size_t)t * k_tile + j;
         if (best < 0) {
           cand[o] = -1;
@@ -838,20 +817,19 @@ void oracle_lm_screen(const uint16_t* A, const float* u, const int32_t* row_toke
         } else {
           taken[best] = 1;
           cand[o] = row_token[r0 + best];
-          cand_score[o] = s[best];
+          cand_score[o] = sm[r0 + best];
         }
       }
     }
   }
-  free(s);
   free(taken);
 }
 
-/* Exact logits of the candidates: logits[m, c] = W[cand[m, c], :] . h[m, :] (dot_seg64), W
- * [V, d] bfloat16 in token order.  A candidate outside [0, V) gets -inf and sets
- * ORC_BAD_TOKEN in status[m]. */
+/* Exact logits of the candidates: logits[m, c] = W[cand[m, c], :] . h[m, :], W [V, d]
+ * bfloat16 in token order.  A candidate outside [0, V) gets -inf, and one other than -1 (the
+ * padding of a short tile) sets ORC_BAD_TOKEN in status[m]. */
 void oracle_lm_rescore(const uint16_t* W, const uint16_t* h, const int32_t* cand, int M, int C,
-                       int d, int V, float* logits, int32_t* status) {
+                       int d, int V, double* logits, int32_t* status) {
   for (int m = 0; m < M; ++m)
     for (int c = 0; c < C; ++c) {
       const int tok = cand[(size_t)m * C + c];
@@ -860,34 +838,74 @@ void oracle_lm_rescore(const uint16_t* W, const uint16_t* h, const int32_t* cand
         if (tok != -1) status[m] |= ORC_BAD_TOKEN;
         continue;
       }
-      logits[(size_t)m * C + c] = dot_seg64(W + (size_t)tok * d, h + (size_t)m * d, d);
+      logits[(size_t)m * C + c] = dot_bf16(W + (size_t)tok * d, h + (size_t)m * d, d);
     }
 }
 
-/* The drafter's children: the K best valid candidates of hidden state m (by exact logit, then
+/* Exact logit of every vocabulary token: logits[m, v] = W[v, :] . h[m, :] (the full head;
+ * what stage two evaluates at the candidates).  Rows are split over n_threads threads. */
+struct lm_all_job {
+  const uint16_t *W, *h;
+  int M, d, V, v0, v1;
+  double* logits;
+};
+
+static void* lm_all_worker(void* arg) {
+  const struct lm_all_job* J = (const struct lm_all_job*)arg;
+  for (int m = 0; m < J->M; ++m)
+    for (int v = J->v0; v < J->v1; ++v)
+      J->logits[(size_t)m * J->V + v] =
+          dot_bf16(J->W + (size_t)v * J->d, J->h + (size_t)m * J->d, J->d);
+  return NULL;
+}
+
+void oracle_lm_logits_all(const uint16_t* W, const uint16_t* h, int M, int d, int V,
+                          double* logits, int n_threads) {
+  if (n_threads < 1) n_threads = 1;
+  if (n_threads > 64) n_threads = 64;
+  pthread_t th[64];
+  struct lm_all_job jobs[64];
+  for (int k = 0; k < n_threads; ++k) {
+    jobs[k].W = W;
+    jobs[k].h = h;
+    jobs[k].M = M;
+    jobs[k].d = d;
+    jobs[k].V = V;
+    jobs[k].v0 = (int)((long)V * k / n_threads);
+    jobs[k].v1 = (int)((long)V * (k + 1) / n_threads);
+    jobs[k].logits = logits;
+  }
+  int started = 0;
+  for (int k = 1; k < n_threads; ++k)
+    if (pthread_create(&th[k], NULL, lm_all_worker, &jobs[k]) == 0) ++started;
+    else lm_all_worker(&jobs[k]);
+  lm_all_worker(&jobs[0]);
+  for (int k = 1; k <= started; ++k) pthread_join(th[k], NULL);
+}
+
+/* The drafter's children: the K best valid candidates of hidden state m (by logit, ties to the
  * smaller token), best first, and their confidences, the softmax of the logits over all valid
- * candidates of m (fp64).  Fewer than K valid candidates pad with token -1, confidence 0. */
-void oracle_lm_topk(const float* logits, const int32_t* cand, int M, int C, int K, int V,
+ * candidates of m.  Fewer than K valid candidates pad with token -1, confidence 0.  A token
+ * listed twice among the candidates counts twice, as two candidates. */
+void oracle_lm_topk(const double* logits, const int32_t* cand, int M, int C, int K, int V,
                     int32_t* out_tok, double* out_conf) {
   char* taken = (char*)malloc((size_t)C);
   for (int m = 0; m < M; ++m) {
-    const float* l = logits + (size_t)m * C;
+    const double* l = logits + (size_t)m * C;
     const int32_t* cm = cand + (size_t)m * C;
     double mx = -INFINITY;
     for (int c = 0; c < C; ++c) {
       taken[c] = !(cm[c] >= 0 && cm[c] < V);
-      if (!taken[c] && (double)l[c] > mx) mx = (double)l[c];
+      if (!taken[c] && l[c] > mx) mx = l[c];
     }
     double z = 0.0;
     for (int c = 0; c < C; ++c)
-      if (!taken[c]) z += exp((double)l[c] - mx);
+      if (!taken[c]) z += exp(l[c] - mx);
     for (int j = 0; j < K; ++j) {
       int best = -1;
       for (int c = 0; c < C; ++c) {
         if (taken[c]) continue;
-        if (best < 0 || float_key(l[c]) > float_key(l[best]) ||
-            (float_key(l[c]) == float_key(l[best]) && cm[c] < cm[best]))
-          best = c;
+        if (best < 0 || l[c] > l[best] || (l[c] == l[best] && cm[c] < cm[best])) best = c;
       }
       if (best < 0) {
         out_tok[(size_t)m * K + j] = -1;
@@ -895,7 +913,7 @@ void oracle_lm_topk(const float* logits, const int32_t* cand, int M, int C, int 
       } else {
         taken[best] = 1;
         out_tok[(size_t)m * K + j] = cm[best];
-        out_conf[(size_t)m * K + j] = exp((double)l[best] - mx) / z;
+        out_conf[(size_t)m * K + j] = exp(l[best] - mx) / z;
       }
     }
   }

@@ -1270,32 +1270,48 @@ def _bits(x) -> np.ndarray:
     return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
 
 
-def pin_lm_summation_order(lib):
-    """Hand-derived float32 results (tests/golden/lm_head_order.txt) that change under any
-    other summation order."""
-    with open(os.path.join(GOLDEN, "lm_head_order.txt"), encoding="utf-8") as f:
+def _read_lm_hand_case():
+    rec = {}
+    with open(os.path.join(GOLDEN, "lm_head_hand_case.txt"), encoding="utf-8") as f:
         for line in f:
             if not line.strip() or line.startswith("#"):
                 continue
-            f_ = [x.strip() for x in line.split("|")]
-            if f_[0] == "dot":
-                d = int(f_[1])
-                x = np.zeros(d, np.float32)
-                y = np.zeros(d, np.float32)
-                for ent in f_[2].split():
-                    i, a, b_ = ent.split(":")
-                    x[int(i)], y[int(i)] = float(a), float(b_)
-                u = O.lm_project(_bits(y)[None], _bits(x)[None], lib=lib)
-                assert u[0, 0] == np.float32(f_[3]), (u[0, 0], f_[3])
-                # the same order in stage two: W row x, hidden state y
-                logits, st = O.lm_rescore(_bits(x)[None], _bits(y)[None], np.zeros((1, 1), np.int32),
-                                          lib=lib)
-                assert logits[0, 0] == np.float32(f_[3]) and st[0] == 0
-            elif f_[0] == "screen":
-                a = np.array([float(v) for v in f_[2].split()], np.float32)
-                uu = np.array([[float(v) for v in f_[3].split()]], np.float32)
-                cand, score = O.lm_screen(_bits(a)[None], uu, np.array([7], np.int32), 1, 1, lib=lib)
-                assert cand[0, 0] == 7 and score[0, 0] == np.float32(f_[4]), score
+            k, v = (x.strip() for x in line.split("|"))
+            rec[k] = v
+    return rec
+
+
+def pin_lm_hand_case(lib):
+    """The hand-derived case (tests/golden/lm_head_hand_case.txt): projection, the score of
+    every stored row, tile boundaries and padding, ties to the smaller row, candidates mapped
+    through the row shuffle, exact logits, children with ties to the smaller token, and
+    confidences normalised over every valid candidate."""
+    g = _read_lm_hand_case()
+    num = lambda k: [float(x) for x in g[k].split()]  # noqa: E731
+    d = int(g["d"])
+    h = np.zeros((1, d), np.float32)
+    h[0, 0] = float(g["h0"])
+    b0 = num("B_col0")
+    Bm = np.full((len(b0), d), 100.0, np.float32)
+    Bm[:, 0] = b0
+    A = np.array([[float(x) for x in row.split()] for row in g["A"].split(";")], np.float32)
+    perm = np.array([int(x) for x in g["row_token"].split()], np.int32)
+    w0 = num("W_col0")
+    W = np.full((len(w0), d), 100.0, np.float32)
+    W[:, 0] = w0
+    tile, k_tile, K = int(g["tile"]), int(g["k_tile"]), int(g["K"])
+    u = O.lm_project(_bits(h), _bits(Bm), lib=lib)
+    assert list(u[0]) == num("u")
+    assert list(O.lm_scores(_bits(A), u, lib=lib)[0]) == num("scores")
+    res = O.lm_head_two_stage(_bits(h), _bits(A), _bits(Bm), _bits(W), perm, tile, k_tile, K,
+                              lib=lib)
+    assert list(res["cand"][0]) == [int(x) for x in g["cand"].split()]
+    assert list(res["cand_score"][0]) == num("cand_score")
+    assert list(res["logits"][0]) == num("logits") and res["status"][0] == 0
+    assert list(res["tok"][0]) == [int(x) for x in g["children"].split()]
+    Z = sum(math.exp(x) for x in num("Z_logits"))
+    for j, lg in enumerate(num("children_logits")):
+        assert abs(res["conf"][0, j] - math.exp(lg) / Z) <= 1e-15
 
 
 def _int_lm_case(rng, M, d, r, n, lo=-3, hi=4):
@@ -1331,7 +1347,7 @@ def pin_lm_integer_bruteforce(lib):
         res = O.lm_head_two_stage(_bits(h), _bits(A[perm]), _bits(Bm), _bits(W), perm, tile, k_tile,
                                   K, lib=lib)
         u = h @ Bm.T  # [M, r], exact
-        assert np.array_equal(res["u"], u.astype(np.float32))
+        assert np.array_equal(res["u"], u.astype(np.float64))
         As = A[perm]  # row q of the shuffled head is token perm[q]
         scores = u @ As.T  # [M, n], exact
         n_tiles = -(-n // tile)
@@ -1344,7 +1360,10 @@ def pin_lm_integer_bruteforce(lib):
             assert list(res["cand"][m]) == want, (trial, m)
             valid = res["cand"][m] >= 0
             exact = (W[np.maximum(res["cand"][m], 0)] @ h[m]).astype(np.float64)
-            assert np.array_equal(res["logits"][m][valid], exact[valid].astype(np.float32))
+            assert np.array_equal(res["logits"][m][valid], exact[valid])
+            want_s = [scores[m, perm.tolist().index(t)] if t >= 0 else -np.inf
+                      for t in res["cand"][m]]
+            assert np.array_equal(res["cand_score"][m], np.array(want_s, np.float64))
             assert np.isneginf(res["logits"][m][~valid]).all()
             vc = res["cand"][m][valid]
             top = vc[_lexsort_best(exact[valid], vc, K)]
@@ -1356,30 +1375,44 @@ def pin_lm_integer_bruteforce(lib):
                 assert abs(res["conf"][m, j] - conf[int(t)]) <= 1e-12
 
 
-def pin_lm_error_bound(lib):
-    """Normal-valued inputs: every float32 dot product lies within the rounding bound of its
-    exact value, (terms + 6) * 2^-24 * sum |x_i y_i| for the segmented dot products and
-    r * 2^-24 * sum |a_i u_i| for the screening chain."""
+def pin_lm_fp64_near_exact(lib):
+    """Normal-valued bfloat16 inputs: u, the scores of every row and the logits of every token
+    lie within n * 2^-53 * sum |x_i y_i| (plus the propagated error of u) of the exact rational
+    values, computed with fractions.Fraction on a sample of entries."""
+    from fractions import Fraction
+
     rng = np.random.default_rng(32)
-    M, d, r, n = 3, 1024, 48, 40
+    M, d, r, n = 2, 1024, 24, 30
     h = _bits(rng.standard_normal((M, d)))
     Bm = _bits(rng.standard_normal((r, d)))
     A = _bits(rng.standard_normal((n, r)))
     W = _bits(rng.standard_normal((n, d)))
+    fr = lambda b: [Fraction(float(x)) for x in bf16_bits_to_f32(b).reshape(-1)]  # noqa: E731
+    hq, Bq, Aq, Wq = fr(h), fr(Bm), fr(A), fr(W)
     f = lambda b: bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
     u = O.lm_project(h, Bm, lib=lib)
-    ex, mag = f(h) @ f(Bm).T, np.abs(f(h)) @ np.abs(f(Bm)).T
-    assert (np.abs(u - ex) <= (d // 64 + 7) * 2.0 ** -24 * mag + 1e-30).all()  # d/64 per chain
-    perm = np.arange(n, dtype=np.int32)
-    cand, score = O.lm_screen(A, u, perm, n, n, lib=lib)  # one tile keeps every row
-    ex_s = u.astype(np.float64) @ f(A).T
-    mag_s = np.abs(u.astype(np.float64)) @ np.abs(f(A)).T
+    s = O.lm_scores(A, u, lib=lib)
+    L = O.lm_logits_all(W, h, n_threads=2, lib=lib)
+    eps = 2.0 ** -53
     for m in range(M):
-        got = score[m, np.argsort(cand[m])]
-        assert (np.abs(got - ex_s[m]) <= (r + 1) * 2.0 ** -24 * mag_s[m] + 1e-30).all()
-    logits, _ = O.lm_rescore(W, h, np.tile(np.arange(n, dtype=np.int32), (M, 1)), lib=lib)
-    ex_l, mag_l = f(h) @ f(W).T, np.abs(f(h)) @ np.abs(f(W)).T
-    assert (np.abs(logits - ex_l) <= (d // 64 + 7) * 2.0 ** -24 * mag_l + 1e-30).all()
+        hm = hq[m * d:(m + 1) * d]
+        ue = [sum(Bq[i * d + k] * hm[k] for k in range(d)) for i in range(r)]
+        mag_u = np.abs(f(Bm)) @ np.abs(f(h[m]))
+        assert all(abs(Fraction(float(u[m, i])) - ue[i]) <= Fraction(d * eps * mag_u[i])
+                   for i in range(r))
+        for row in range(0, n, 7):
+            se = sum(Aq[row * r + i] * ue[i] for i in range(r))
+            bound = r * eps * float(np.abs(f(A[row])) @ np.abs(u[m])) + \
+                float(np.abs(f(A[row])) @ (d * eps * mag_u)) * 1.01
+            assert abs(Fraction(float(s[m, row])) - se) <= Fraction(bound)
+        for v in range(0, n, 5):
+            le = sum(Wq[v * d + k] * hm[k] for k in range(d))
+            bound = d * eps * float(np.abs(f(W[v])) @ np.abs(f(h[m])))
+            assert abs(Fraction(float(L[m, v])) - le) <= Fraction(bound)
+    # the candidates' logits are the full head's logits at those tokens
+    cand = rng.integers(0, n, size=(M, 9)).astype(np.int32)
+    lg, st = O.lm_rescore(W, h, cand, lib=lib)
+    assert (st == 0).all() and np.array_equal(lg, np.take_along_axis(L, cand, axis=1))
 
 
 def pin_lm_exact_screen_keeps_global_best(lib):
@@ -1456,9 +1489,9 @@ ALL_PINS = [
     pin_eagle2_rerank_tables,
     pin_eagle2_batch_independent,
     pin_eagle2_bruteforce,
-    pin_lm_summation_order,
+    pin_lm_hand_case,
     pin_lm_integer_bruteforce,
-    pin_lm_error_bound,
+    pin_lm_fp64_near_exact,
     pin_lm_exact_screen_keeps_global_best,
     pin_lm_padding_and_bad_tokens,
 ]

@@ -1,10 +1,29 @@
 """GPU parity of the two-stage drafter LM head (lm_head_project, lm_head_screen,
 lm_head_rescore, lm_head_topk) against the CPU oracle, through the C ABI.
 
-Both sides compute every value that chooses a candidate or a child in float32 in the same
-stated order (fused multiply-add chains; 64 segments combined by a fixed butterfly), so u,
-the candidate tokens, their scores, the exact logits and the children must agree exactly.  The
-confidences come from fp32 sums on the GPU and fp64 in the oracle: relative error <= 1e-5.
+The oracle computes the page's definition exactly (fp64 dot products of the bfloat16 inputs):
+u = B h, the score A u of every row, the local top-k of every tile of shuffled rows, the exact
+logits W h, the children and their softmax confidences.  The kernels compute in float32, so
+where two rows score within rounding of each other either choice is correct.  Parity is
+therefore a validity check against the exact values, with the float32 rounding bound of the
+kernels' arithmetic:
+
+* every float32 value the GPU reports (u, candidate scores, logits) lies within its bound of
+  the exact value.  A kernel dot product passes each term through at most n roundings
+  (n = d/64 + 6 for u and the logits: 64-term chains of fused multiply-adds over d/64 pieces,
+  then a six-level pairwise combination; n = r for a screening score: one chain over the rank
+  index, on the float32 u), so it errs by at most gamma_n sum |x_i y_i|, gamma_n =
+  n u / (1 - n u), u = 2^-24; a screening score also carries A times u's own error;
+* every tile's candidates are distinct rows of that tile, as many as it has up to k_tile, named
+  by their tokens through the row shuffle, best first by the GPU's scores; and no unchosen row
+  of the tile beats a chosen one by more than both bounds: min over chosen (s + e) >=
+  max over unchosen (s - e).  Where the tile's k_tile-th and next exact scores are further apart
+  than that, the set is forced, and it must equal the oracle's;
+* the children are the K best of the GPU's candidates by the same rule on the exact logits; the
+  confidences are within the softmax's sensitivity to those bounds (relative exp(2E) - 1, E the
+  largest logit bound of the hidden state, plus 1e-5 for float32 exponentials and sums) of the
+  exact softmax over the GPU's candidates;
+* out-of-vocabulary candidates get -inf and set TV_BAD_TOKEN.
 """
 import numpy as np
 import pytest
@@ -16,7 +35,12 @@ from synth import bf16_bits_to_f32, make_lm_head
 
 pytestmark = pytest.mark.gpu
 
+UNIT = 2.0 ** -24
 TOL_CONF = 1e-5
+
+
+def gamma(n: int) -> float:
+    return n * UNIT / (1 - n * UNIT)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -28,19 +52,15 @@ def _gpu():
     tv.load_library()
 
 
-def run_both(h, A, Bm, W, perm, tile, k_tile, K, label, rows=None, cand_override=None):
-    """Device and oracle two-stage heads on the same bits; `rows` limits the oracle (and the
-    comparison) to some hidden states."""
+def _f(b):
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+def run_gpu(h, A, Bm, W, perm, tile, k_tile, K, cand_override=None):
     import tree_attention_verification_attn_amd as tv
-    from oracle import oracle as O
 
     M = h.shape[0]
-    print(f"[case] lm head {label} M={M} d={h.shape[1]} n={A.shape[0]} r={A.shape[1]} "
-          f"tile={tile} k_tile={k_tile} K={K}", flush=True)
-    hd, Ad, Bd, Wd = (to_dev(x).view(torch.bfloat16) for x in (h.view(np.int16),
-                                                                 A.view(np.int16),
-                                                                 Bm.view(np.int16),
-                                                                 W.view(np.int16)))
+    hd, Ad, Bd, Wd = (to_dev(x.view(np.int16)).view(torch.bfloat16) for x in (h, A, Bm, W))
     status = torch.zeros(M, dtype=torch.int32, device="cuda")
     u = tv.lm_head_project(hd, Bd)
     cand, score = tv.lm_head_screen(Ad, u, to_dev(perm), tile, k_tile)
@@ -49,26 +69,135 @@ def run_both(h, A, Bm, W, perm, tile, k_tile, K, label, rows=None, cand_override
     logits = tv.lm_head_rescore(Wd, hd, cand, status=status)
     tok, conf = tv.lm_head_topk(logits, cand, K, W.shape[0])
     torch.cuda.synchronize()
-    g = dict(u=to_host(u), cand=to_host(cand), cand_score=to_host(score), logits=to_host(logits),
-             tok=to_host(tok), conf=to_host(conf), status=to_host(status))
+    return dict(u=to_host(u), cand=to_host(cand), cand_score=to_host(score),
+                logits=to_host(logits), tok=to_host(tok), conf=to_host(conf),
+                status=to_host(status))
+
+
+def check_screen(g, A, o_u, eps_u, perm, tile, k_tile, sel, o_cand):
+    """Candidates of every tile of every selected hidden state; returns how many tiles had a
+    forced set (and matched the oracle's)."""
+    from oracle import oracle as O
+
+    n, r = A.shape
+    Ms = len(sel)
+    s_ex = O.lm_scores(A, o_u)  # [Ms, n] exact
+    absA = np.abs(_f(A))
+    eps_s = gamma(r) * (np.abs(o_u) + eps_u) @ absA.T + eps_u @ absA.T
+    n_tiles = -(-n // tile)
+    pad = n_tiles * tile - n
+    S = np.pad(s_ex, ((0, 0), (0, pad)), constant_values=-np.inf).reshape(Ms, n_tiles, tile)
+    E = np.pad(eps_s, ((0, 0), (0, pad))).reshape(Ms, n_tiles, tile)
+    cand = g["cand"][sel].reshape(Ms, n_tiles, k_tile)
+    score = g["cand_score"][sel].astype(np.float64).reshape(Ms, n_tiles, k_tile)
+    inv = np.empty(n, np.int64)
+    inv[perm] = np.arange(n)
+    rows_in = np.minimum(tile, n - np.arange(n_tiles) * tile)  # rows of each tile
+    n_valid = np.minimum(k_tile, rows_in)
+    slot = np.arange(k_tile)
+    want_valid = slot[None, None, :] < n_valid[None, :, None]
+    assert np.array_equal(cand >= 0, np.broadcast_to(want_valid, cand.shape)), "candidate count"
+    assert np.isneginf(score[~want_valid.repeat(Ms, 0)]).all()
+    assert (cand < n).all()
+    row = np.where(cand >= 0, inv[np.maximum(cand, 0)], -1)
+    loc = row - np.arange(n_tiles)[None, :, None] * tile
+    assert ((loc >= 0) & (loc < tile))[cand >= 0].all(), "candidate outside its tile"
+    # distinct rows, best first by the GPU's own scores
+    srt = np.sort(np.where(cand >= 0, loc, -1 - slot[None, None, :]), axis=2)
+    assert (np.diff(srt, axis=2) != 0).all(), "a row chosen twice"
+    assert (np.diff(np.where(want_valid, score, -1e300), axis=2) <= 0).all(), "not best first"
+    m_i, t_i, j_i = np.nonzero(cand >= 0)
+    l_i = loc[m_i, t_i, j_i]
+    ex = S[m_i, t_i, l_i]
+    assert (np.abs(score[m_i, t_i, j_i] - ex) <= E[m_i, t_i, l_i]).all(), "candidate score"
+    chosen = np.zeros(S.shape, bool)
+    chosen[m_i, t_i, l_i] = True
+    lo = np.where(chosen, S + E, np.inf).min(axis=2)
+    real = np.isfinite(S)
+    hi = np.where(~chosen & real, S - E, -np.inf).max(axis=2)
+    assert (lo >= hi).all(), f"a tile's candidates are not its best rows ({(lo < hi).sum()})"
+    # forced tiles (the exact top set beats every other row by more than both bounds) must
+    # equal the oracle's candidates
+    rank = np.argsort(np.argsort(-S, axis=2, kind="stable"), axis=2)
+    top = rank < n_valid[None, :, None]
+    fmin = np.where(top, S - E, np.inf).min(axis=2)
+    fmax = np.where(~top & real, S + E, -np.inf).max(axis=2)
+    forced = fmin > fmax
+    oc = o_cand.reshape(Ms, n_tiles, k_tile)
+    same = (np.sort(oc, axis=2) == np.sort(cand, axis=2)).all(axis=2)
+    assert same[forced].all(), "a forced tile differs from the oracle's candidates"
+    return int(forced.sum()), int(forced.size)
+
+
+def check_children(g, L_all, eps_l, sel, K, V):
+    """Logits of the GPU's candidates, the children and their confidences."""
+    import tree_attention_verification_attn_amd as tv
+
+    for i, m in enumerate(sel):
+        cand = g["cand"][m]
+        valid = (cand >= 0) & (cand < V)
+        lg = g["logits"][m].astype(np.float64)
+        assert np.isneginf(lg[~valid]).all()
+        ex = L_all[i, cand[valid]]
+        ec = eps_l[i, cand[valid]]
+        assert (np.abs(lg[valid] - ex) <= ec).all(), "logit"
+        bad = ((cand < -1) | (cand >= V)).any()
+        assert (g["status"][m] & tv.TV_BAD_TOKEN) == (tv.TV_BAD_TOKEN if bad else 0)
+        tok = g["tok"][m]
+        nk = min(K, int(valid.sum()))
+        assert (tok[nk:] == -1).all() and (g["conf"][m][nk:] == 0).all()
+        kids = tok[:nk]
+        assert (kids >= 0).all() and (kids < V).all()
+        # each child is one copy of a valid candidate
+        vals, cnt = np.unique(cand[valid], return_counts=True)
+        kv, kc = np.unique(kids, return_counts=True)
+        have = dict(zip(vals.tolist(), cnt.tolist()))
+        assert all(have.get(t, 0) >= c for t, c in zip(kv.tolist(), kc.tolist())), "child copies"
+        left = dict(have)
+        for t in kids.tolist():
+            left[t] -= 1
+        k_ex, k_eps = L_all[i, kids], eps_l[i, kids]
+        un = [t for t, c in left.items() for _ in range(c)]
+        if un:
+            assert (k_ex + k_eps).min() >= (L_all[i, un] - eps_l[i, un]).max(), "children"
+        # best first by the GPU's own logits (every copy of a token has the same logit)
+        glog = {int(t): float(v) for t, v in zip(cand[valid], lg[valid])}
+        kl = np.array([glog[int(t)] for t in kids])
+        assert (np.diff(kl) <= 0).all(), "children not best first"
+        # confidences: softmax over every valid candidate copy, within its sensitivity
+        mx = ex.max()
+        z = np.exp(ex - mx).sum()
+        want = np.exp(k_ex - mx) / z
+        rel = np.expm1(2 * ec.max()) + TOL_CONF
+        err = np.abs(g["conf"][m][:nk].astype(np.float64) - want)
+        assert (err <= rel * want + 1e-30).all(), (err / want).max()
+
+
+def run_both(h, A, Bm, W, perm, tile, k_tile, K, label, rows=None, cand_override=None):
+    """Device head against the oracle's exact values; `rows` limits the check to some hidden
+    states."""
+    from oracle import oracle as O
+
+    M, d = h.shape
+    n, r = A.shape
+    V = W.shape[0]
+    print(f"[case] lm head {label} M={M} d={d} n={n} r={r} tile={tile} k_tile={k_tile} K={K}",
+          flush=True)
+    g = run_gpu(h, A, Bm, W, perm, tile, k_tile, K, cand_override)
     sel = np.arange(M) if rows is None else np.asarray(rows)
+    depth = d // 64 + 6
     o_u = O.lm_project(h[sel], Bm)
-    assert np.array_equal(g["u"][sel].view(np.uint32), o_u.view(np.uint32)), label
-    o_cand, o_score = O.lm_screen(A, o_u, perm, tile, k_tile)
+    eps_u = gamma(depth) * (np.abs(_f(h[sel])) @ np.abs(_f(Bm)).T)
+    assert (np.abs(g["u"][sel].astype(np.float64) - o_u) <= eps_u).all(), f"{label}: u"
+    o_cand, _ = O.lm_screen(A, o_u, perm, tile, k_tile)
+    forced = None
     if cand_override is None:
-        assert np.array_equal(g["cand"][sel], o_cand), label
-        assert np.array_equal(g["cand_score"][sel], o_score), label
-        c_use = o_cand
-    else:
-        c_use = cand_override[sel]
-    o_logits, o_st = O.lm_rescore(W, h[sel], c_use)
-    assert np.array_equal(g["logits"][sel].view(np.uint32), o_logits.view(np.uint32)), label
-    assert np.array_equal(g["status"][sel], o_st), label
-    o_tok, o_conf = O.lm_topk(o_logits, c_use, K, W.shape[0])
-    assert np.array_equal(g["tok"][sel], o_tok), label
-    err = np.abs(g["conf"][sel].astype(np.float64) - o_conf) / np.maximum(o_conf, 1e-30)
-    assert (err[o_conf > 0] <= TOL_CONF).all() and (g["conf"][sel][o_conf == 0] == 0).all(), \
-        (label, err.max())
+        forced = check_screen(g, A, o_u, eps_u, perm, tile, k_tile, sel, o_cand)
+    L_all = O.lm_logits_all(W, h[sel])
+    eps_l = gamma(depth) * (np.abs(_f(h[sel])) @ np.abs(_f(W)).T)
+    check_children(g, L_all, eps_l, sel, K, V)
+    if forced is not None:
+        print(f"       forced tiles {forced[0]} of {forced[1]} equal the oracle's", flush=True)
     return g
 
 
@@ -93,13 +222,16 @@ def test_random_small():
 
 
 def test_small_integers_ties():
-    """Integer-valued inputs: scores and logits tie often, exercising both tie rules."""
+    """Integer-valued inputs: every float32 sum is exact (the bounds still hold), and scores and
+    logits tie often; tied rows may go either way, but the GPU's choice must be a best set."""
     rng = np.random.default_rng(42)
     for trial in range(6):
         M, d, r, n = 5, 512, 16, 700
         h, Bm, A, W, perm = pins._int_lm_case(rng, M, d, r, n, lo=-2, hi=3)
-        run_both(pins._bits(h), pins._bits(A[perm]), pins._bits(Bm), pins._bits(W), perm, 64, 5,
-                 12, f"integers {trial}")
+        g = run_both(pins._bits(h), pins._bits(A[perm]), pins._bits(Bm), pins._bits(W), perm,
+                     64, 5, 12, f"integers {trial}")
+        # exact arithmetic: the GPU's values equal the exact ones
+        assert np.array_equal(g["u"].astype(np.float64), (h @ Bm.T).astype(np.float64))
 
 
 def test_every_hidden_state_count():
@@ -168,8 +300,9 @@ def test_children_feed_the_expansion():
 def test_topk_repeated_tokens_and_ties(C, K):
     """lm_head_topk alone, on candidate lists that repeat tokens (a token's copies carry the
     same logit, as lm_head_rescore gives them) and hold many equal logits and invalid tokens.
-    Each copy is a candidate of its own, as in the oracle: a repeated token can be chosen once
-    per copy, and every copy counts in the softmax denominator."""
+    The logits are exact multiples of 1/4, so the children are unique up to the tie rule
+    (larger logit, then smaller token; each copy a candidate of its own): they must equal the
+    oracle's.  Confidences within 1e-5 relative of the oracle's fp64 softmax."""
     import tree_attention_verification_attn_amd as tv
     from oracle import oracle as O
 
@@ -189,7 +322,7 @@ def test_topk_repeated_tokens_and_ties(C, K):
     print(f"[case] lm topk repeated tokens M={M} C={C} K={K}", flush=True)
     tok, conf = tv.lm_head_topk(to_dev(logits), to_dev(cand), K, V)
     torch.cuda.synchronize()
-    o_tok, o_conf = O.lm_topk(logits, cand, K, V)
+    o_tok, o_conf = O.lm_topk(logits.astype(np.float64), cand, K, V)
     g_tok, g_conf = to_host(tok), to_host(conf).astype(np.float64)
     assert np.array_equal(g_tok, o_tok)
     err = np.abs(g_conf - o_conf) / np.maximum(o_conf, 1e-30)

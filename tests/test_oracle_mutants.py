@@ -134,32 +134,35 @@ MUTANTS = {
                                "if (p < 0 || p >= i) valid = 0;"),
     # draft tree: flattened depth counted from one
     "e2_depth_from_one": ("        dout[f] = d;\n", "        dout[f] = d + 1;\n"),
-    # LM head: segment sums combined from the nearest pairs up instead of from j ^ 32 down
-    "lm_butterfly_reversed": ("for (int off = 32; off >= 1; off >>= 1) {\n    for (int j = 0; j < 64; ++j) w[j]",
-                              "for (int off = 1; off <= 32; off <<= 1) {\n    for (int j = 0; j < 64; ++j) w[j]"),
-    # LM head: each chain runs over its pieces' elements in reverse
-    "lm_segment_reversed": ("const int i = 512 * p + 8 * j + e;",
-                            "const int i = 512 * (d / 512 - 1 - p) + 8 * j + 7 - e;"),
-    # LM head: chains over d/64 consecutive elements instead of interleaved 8-element pieces
-    "lm_segment_contiguous": ("const int i = 512 * p + 8 * j + e;",
-                              "const int i = j * (d / 64) + 8 * p + e;"),
-    # LM head: screening chain over the rank index in reverse
-    "lm_screen_reversed": ("for (int i = 0; i < r; ++i) acc = fmaf(bf16f(a[i]), um[i], acc);",
-                           "for (int i = r - 1; i >= 0; --i) acc = fmaf(bf16f(a[i]), um[i], acc);"),
+    # LM head: the projection uses h's row for B's index
+    "lm_project_swapped": ("u[(size_t)m * r + i] = dot_bf16(Bm + (size_t)i * d, h + (size_t)m * d, d);",
+                           "u[(size_t)m * r + i] = dot_bf16(Bm + (size_t)(i % r) * d, h + (size_t)(i % M) * d, d);"),
+    # LM head: a dot product that skips its first element
+    "lm_dot_skips_first": ("for (int i = 0; i < d; ++i) acc += bf16d(x[i]) * bf16d(y[i]);",
+                           "for (int i = 1; i < d; ++i) acc += bf16d(x[i]) * bf16d(y[i]);"),
+    # LM head: screening scores from the hidden state's first r elements instead of u = B h
+    "lm_scores_skip_projection": ("for (int i = 0; i < r; ++i) acc += bf16d(a[i]) * u[(size_t)m * r + i];",
+                                  "for (int i = 0; i < r; ++i) acc += bf16d(a[i]) * (double)(i == 0);"),
     # LM head: equal scores go to the larger row
-    "lm_screen_tie_larger": ("if (!taken[q] && (best < 0 || float_key(s[q]) > float_key(s[best]))) best = q;",
-                             "if (!taken[q] && (best < 0 || float_key(s[q]) >= float_key(s[best]))) best = q;"),
+    "lm_screen_tie_larger": ("if (!taken[q] && (best < 0 || sm[r0 + q] > sm[r0 + best])) best = q;",
+                             "if (!taken[q] && (best < 0 || sm[r0 + q] >= sm[r0 + best])) best = q;"),
+    # LM head: the last row of every tile never considered
+    "lm_tile_drops_last_row": ("const int r0 = t * tile, rows = n - r0 < tile ? n - r0 : tile;",
+                               "const int r0 = t * tile, rows = n - r0 < tile - 1 ? n - r0 : tile - 1;"),
     # LM head: candidates reported by row instead of token
     "lm_cand_is_row": ("cand[o] = row_token[r0 + best];", "cand[o] = r0 + best;"),
+    # LM head: the exact logits read W's row by candidate slot instead of token
+    "lm_rescore_by_slot": ("logits[(size_t)m * C + c] = dot_bf16(W + (size_t)tok * d, h + (size_t)m * d, d);",
+                           "logits[(size_t)m * C + c] = dot_bf16(W + (size_t)(c % V) * d, h + (size_t)m * d, d);"),
+    # LM head: the full head's logits one row off
+    "lm_logits_all_shifted": ("dot_bf16(J->W + (size_t)v * J->d, J->h + (size_t)m * J->d, J->d);",
+                              "dot_bf16(J->W + (size_t)((v + 1) % J->V) * J->d, J->h + (size_t)m * J->d, J->d);"),
     # LM head: equal logits go to the larger token
-    "lm_topk_tie_larger": ("(float_key(l[c]) == float_key(l[best]) && cm[c] < cm[best]))",
-                           "(float_key(l[c]) == float_key(l[best]) && cm[c] > cm[best]))"),
+    "lm_topk_tie_larger": ("if (best < 0 || l[c] > l[best] || (l[c] == l[best] && cm[c] < cm[best])) best = c;",
+                           "if (best < 0 || l[c] > l[best] || (l[c] == l[best] && cm[c] > cm[best])) best = c;"),
     # LM head: confidences normalised over the chosen children only
-    "lm_conf_over_chosen": ("out_conf[(size_t)m * K + j] = exp((double)l[best] - mx) / z;",
-                            "out_conf[(size_t)m * K + j] = exp((double)l[best] - mx) / (z > 0 ? 1.0 : z);"),
-    # LM head: the projection uses h's row for B's index
-    "lm_project_swapped": ("u[(size_t)m * r + i] = dot_seg64(Bm + (size_t)i * d, h + (size_t)m * d, d);",
-                           "u[(size_t)m * r + i] = dot_seg64(Bm + (size_t)(i % r) * d, h + (size_t)(i % M) * d, d);"),
+    "lm_conf_over_chosen": ("out_conf[(size_t)m * K + j] = exp(l[best] - mx) / z;",
+                            "out_conf[(size_t)m * K + j] = exp(l[best] - mx) / (z > 0 ? 1.0 : z);"),
     # LM head: out-of-vocabulary candidates not reported
     "lm_bad_token_silent": ("if (tok != -1) status[m] |= ORC_BAD_TOKEN;", ""),
     # paged commit: a full free list not reported
