@@ -22,6 +22,8 @@ The worked 8-node tree It/is/has/a/the/to/good/be (rainlin.net section 4) is
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 import math
 
 import numpy as np
@@ -328,22 +330,33 @@ def make_workload(spec: WorkloadSpec | str, extra_seed: int = 0, B: int | None =
     store = np.float32 if dtype == "f32" else np.uint16
     nan = np.float32(np.nan) if dtype == "f32" else BF16_NAN_BITS
     q = np.empty((B, T, Hq, D), store)
-    if with_kv:
-        k_cache = np.full((B, Hkv, Lmax, D), nan, store)
-        v_cache = np.full((B, Hkv, Lmax, D), nan, store)
+    if with_kv:  # rows at and past each prefix are NaN (filled per sequence below)
+        k_cache = np.empty((B, Hkv, Lmax, D), store)
+        v_cache = np.empty((B, Hkv, Lmax, D), store)
     else:
         k_cache = v_cache = np.empty((0,), store)
     k_tree = np.empty((B, T, Hkv, D), store)
     v_tree = np.empty((B, T, Hkv, D), store)
-    for b in range(B):
+
+    def draw(b):  # every sequence has its own generators, so the draws may run in any order
         q[b] = _normal(_rng(wid, b, STREAM_Q, extra_seed), (T, Hq, D), dtype)
         rkv = _rng(wid, b, STREAM_KV, extra_seed)
         Lb = int(cache_len[b])
         if with_kv:
             k_cache[b, :, :Lb] = _normal(rkv, (Hkv, Lb, D), dtype)
             v_cache[b, :, :Lb] = _normal(rkv, (Hkv, Lb, D), dtype)
+            k_cache[b, :, Lb:] = nan
+            v_cache[b, :, Lb:] = nan
         k_tree[b] = _normal(rkv, (T, Hkv, D), dtype)
         v_tree[b] = _normal(rkv, (T, Hkv, D), dtype)
+
+    workers = min(B, 16, len(os.sched_getaffinity(0)))
+    if workers > 1 and with_kv:
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            list(pool.map(draw, range(B)))
+    else:
+        for b in range(B):
+            draw(b)
     return Workload(spec=spec, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, Lmax=Lmax, dtype=dtype,
                     parent=parent, draft=draft, target=target, cache_len=cache_len, q=q,
                     k_cache=k_cache, v_cache=v_cache, k_tree=k_tree, v_tree=v_tree)
