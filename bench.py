@@ -4,7 +4,9 @@
 One step = tree_build_mask + tree_verify_attn + tree_accept + kv_compact_accepted (one layer)
 over one batch of the chosen synthetic workload, all on one stream with the inputs resident in
 HBM.  Copies of the input set are rotated so the bytes touched per sweep exceed twice the
-256 MB Infinity Cache.  Prints one JSON line:
+256 MB Infinity Cache.  The default workload is the largest that fits one GPU: the wide-tree
+batch (64 sequences, prefixes of 1024..8192 tokens, 128-node trees).  The timed region (K
+steps) runs several times and the median is reported.  Prints one JSON line:
 
   value            KV-prefix bytes of the step / step time (GB/s), i.e. the prefix K/V read rate
                    of the whole verification step
@@ -12,6 +14,7 @@ HBM.  Copies of the input set are rotated so the bytes touched per sweep exceed 
   tree_tokens_per_s, accepted_tokens_per_s   B*T and sum(accept_len) per second of step time
   roofline         the attention main kernel against MI355X's HBM (8 TB/s) or bf16 MFMA peak
   cpu_baseline     the CPU oracle on a bounded sample of the same workload
+  other_workloads  the same fused step timed on the other multi-token workloads (--also)
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -34,7 +37,8 @@ if ROOT not in sys.path:
 
 from synth import WORKLOADS, make_workload  # noqa: E402
 
-DEFAULT_WORKLOAD = "llama8b_b1_L4096_T60"
+DEFAULT_WORKLOAD = "wide_b64_L1024-8192_T128"
+ALSO_WORKLOADS = "llama8b_b1_L4096_T60,batch32_L512-4096_T60,llama70b_b8_L32768_T64"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 MALL_BYTES = 256 << 20
@@ -46,6 +50,11 @@ def parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=400)
     p.add_argument("--warmup", type=int, default=40)
+    p.add_argument("--repeats", type=int, default=5,
+                   help="times the K-step timed region is run; the median is reported")
+    p.add_argument("--also", default=ALSO_WORKLOADS,
+                   help="comma-separated workloads whose fused step is also timed and reported "
+                        "under \"other_workloads\" ('' for none)")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     p.add_argument("--split-keys", type=int, default=0, help="prefix keys per split (0 = auto)")
     p.add_argument("--graph-steps", type=int, default=0,
@@ -53,7 +62,7 @@ def parse_args():
                         "as the layers of a model would (0 = auto: the smallest multiple of the "
                         "set count that is >= 8)")
     p.add_argument("--api", choices=("fused", "separate"), default="fused",
-                   help="time the step through tree_verify_step (three launches) or through the "
+                   help="time the step through tree_verify_step (two launches) or through the "
                         "four separate entry points; the other is timed too and reported")
     p.add_argument("--kv", choices=("dense", "paged"), default="dense",
                    help="dense caches, or a paged pool read through a block table with the path "
@@ -555,6 +564,113 @@ def lm_head_bench(tv, torch, name: str, stream, steps: int, warmup: int) -> dict
     }
 
 
+def other_workload_bench(tv, torch, name: str, args, stream) -> dict:
+    """The fused step (tree_verify_step) on another workload, measured as the headline is:
+    input sets rotated past twice the Infinity Cache, HIP graphs of consecutive steps, W warmup
+    steps, `repeats` timed regions of K steps continuing the rotation (median reported), and
+    the main kernel's own duration from its profiling hook over an eager pass."""
+    print(f"[bench] also timing {name}", file=sys.stderr, flush=True)
+    w = make_workload(name)
+    kv_bytes = w.kv_prefix_bytes()
+    L = np.clip(w.cache_len, 0, w.Lmax).astype(np.int64)
+    flops = 4 * int(L.sum()) * w.Hq * w.T * w.D
+    set_bytes = w.k_cache.nbytes + w.v_cache.nbytes + w.q.nbytes * 2 + w.k_tree.nbytes * 2
+    free, _ = torch.cuda.mem_get_info()
+    n_sets = max(1, min(math.ceil(2 * MALL_BYTES / max(kv_bytes, 1)), int(0.5 * free / set_bytes)))
+    ws_bytes = tv.tree_verify_attn_workspace_size(w.B, w.T, w.Hq, w.Hkv, w.D, w.Lmax,
+                                                  torch.bfloat16 if w.dtype == "bf16"
+                                                  else torch.float32, 0)
+    workspace = torch.zeros((ws_bytes,), dtype=torch.uint8, device="cuda") if ws_bytes else None
+    sets = [StepSet(tv, torch, w, workspace=workspace)]
+    for _ in range(n_sets - 1):
+        sets.append(StepSet(tv, torch, w, base=sets[0], workspace=workspace))
+    del w.k_cache, w.v_cache  # host copies are no longer needed
+    gs = n_sets * math.ceil(8 / n_sets)
+    graphs = {}
+
+    def graph(n, start):
+        key = (n, start % n_sets)
+        if key not in graphs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                for i in range(n):
+                    sets[(start + i) % n_sets].fused(cs)
+            graphs[key] = g
+        return graphs[key]
+
+    def plan(k, start):
+        return [graph(gs, start)] * (k // gs) + ([graph(k % gs, start)] if k % gs else [])
+
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    with torch.cuda.stream(stream):
+        for st in sets:
+            st.fused(sptr)
+    stream.synchronize()
+    warm = plan(args.warmup, 0)
+    plans = [plan(args.steps, args.warmup + r * args.steps) for r in range(args.repeats)]
+    torch.cuda.synchronize()
+    per = []
+    with torch.cuda.stream(stream):
+        for g in warm:
+            g.replay()
+        for pl in plans:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            stream.synchronize()
+            e0.record(stream)
+            for g in pl:
+                g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            per.append(e0.elapsed_time(e1) / args.steps)
+        # the main kernel's own duration, by its start and end timestamps
+        n_prof = 50
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_prof)]
+        for a, b in ev:
+            a.record(stream)
+            b.record(stream)
+        stream.synchronize()
+        for i, (a, b) in enumerate(ev):
+            tv.profile_attn_main(a, b)
+            sets[i % n_sets].fused(sptr)
+        tv.profile_attn_main(None, None)
+        stream.synchronize()
+    t_main = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    ms = float(np.median(per))
+    t_step = ms * 1e-3
+    peak_tf = MFMA_PEAK_TFLOPS[w.dtype]
+    hbm_bound = flops / kv_bytes < peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
+    res = {
+        "workload": name, "desc": w.spec.desc, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv,
+        "D": w.D, "prefix_tokens": int(L.sum()), "rotated_sets": n_sets, "graph_steps": gs,
+        "ms_per_step": ms, "ms_per_step_repeats": per,
+        "value_gbps": kv_bytes / t_step / 1e9,
+        "hbm_frac": kv_bytes / t_step / 1e9 / HBM_PEAK_GBS,
+        "tree_tokens_per_s": w.B * w.T / t_step,
+        "attn_main_us": t_main * 1e6,
+        "attn_main_bound": "hbm" if hbm_bound else "mfma",
+        "attn_main_hbm_frac": kv_bytes / t_main / 1e9 / HBM_PEAK_GBS,
+        "attn_main_mfma_frac": flops / t_main / 1e12 / peak_tf,
+        "algorithmic_bytes": kv_bytes, "algorithmic_flops": flops,
+    }
+    del sets, graphs, workspace
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, kv_bytes: int, target_s: float) -> dict:
     """The oracle (never tuned) on a bounded random sample of attention rows."""
     from oracle import oracle as O
@@ -593,6 +709,7 @@ def cpu_baseline(w, kv_bytes: int, target_s: float) -> dict:
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"{n} of {total} (b, query head, node) attention rows drawn uniformly "
                    f"(seed 0), fp64, {reps} pass(es) of {dt:.2f} s wall each; rate = KV-prefix "
                    f"bytes of the whole step x {frac:.4f} / wall time per pass; mask, acceptance "
@@ -679,64 +796,81 @@ def main() -> int:
     stream = torch.cuda.Stream()
     sptr = ctypes.c_void_p(stream.cuda_stream)
 
-    graph_steps = args.graph_steps or n_sets * math.ceil(8 / n_sets)
+    # whole graphs hold a multiple of the set count, so consecutive replays keep the rotation
+    graph_steps = n_sets * math.ceil((args.graph_steps or 8) / n_sets)
 
     def time_api(api):
-        """W untimed steps, then exactly K timed steps through `api`; (ms per step, wall s).
+        """W untimed steps, then `repeats` timed regions of exactly K steps through `api`;
+        returns (median ms per step, every region's ms per step, wall s of the median region).
 
-        In graph mode a graph holds `graph_steps` consecutive steps on input sets 0, 1, ...
-        (cycling); a run of k steps replays whole graphs, then one graph of the remainder."""
+        In graph mode a graph holds `graph_steps` consecutive steps on input sets s, s+1, ...
+        (cycling, from a start set s); a run of k steps replays whole graphs, then one graph of
+        the remainder.  Every run starts on the set after the last one the previous run used, so
+        a timed region never begins on sets the warmup just touched."""
         for s in sets:
             s.api = api
         graphs = {}
 
-        def graph_of(n):
-            if n not in graphs:
+        def graph_of(n, start):
+            key = (n, start % n_sets)
+            if key not in graphs:
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=stream):
                     cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
                     for i in range(n):
-                        sets[i % n_sets].step(cs)
-                graphs[n] = g
-            return graphs[n]
+                        sets[(start + i) % n_sets].step(cs)
+                graphs[key] = g
+            return graphs[key]
 
         if args.mode == "graph":
             with torch.cuda.stream(stream):
                 for s in sets:  # one eager step first so lazy initialisation is outside capture
                     s.step(sptr)
             stream.synchronize()
-            for n in {graph_steps, args.warmup % graph_steps, args.steps % graph_steps} - {0}:
-                graph_of(n)
-            torch.cuda.synchronize()
 
-        def run_steps(k):
+        def run_steps(k, start):
+            """k steps from set `start`; graphs are captured before the first replay."""
             if args.mode == "graph":
-                for _ in range(k // graph_steps):
-                    graphs[graph_steps].replay()
-                if k % graph_steps:
-                    graphs[k % graph_steps].replay()
-            else:
-                for i in range(k):
-                    sets[i % n_sets].step(sptr)
+                plan = [graph_of(graph_steps, start)] * (k // graph_steps)
+                if k % graph_steps:  # whole graphs hold a multiple of the set count
+                    plan.append(graph_of(k % graph_steps, start))
+                return plan
+            return [lambda i=i: sets[(start + i) % n_sets].step(sptr) for i in range(k)]
 
+        def replay(plan):
+            for g in plan:
+                g.replay() if args.mode == "graph" else g()
+
+        start = 0
+        warm = run_steps(args.warmup, start)
+        start += args.warmup
+        plans = []
+        for _ in range(args.repeats):
+            plans.append(run_steps(args.steps, start))
+            start += args.steps
+        torch.cuda.synchronize()
+        per, walls = [], []
         with torch.cuda.stream(stream):
-            run_steps(args.warmup)
+            replay(warm)
             stream.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            t_wall = time.perf_counter()
-            e0.record(stream)
-            run_steps(args.steps)
-            e1.record(stream)
-            e1.synchronize()
-            t_wall = time.perf_counter() - t_wall
-            torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps, t_wall
+            for plan in plans:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                t_wall = time.perf_counter()
+                e0.record(stream)
+                replay(plan)
+                e1.record(stream)
+                e1.synchronize()
+                walls.append(time.perf_counter() - t_wall)
+                torch.cuda.synchronize()
+                per.append(e0.elapsed_time(e1) / args.steps)
+        mid = int(np.argsort(per)[len(per) // 2])
+        return per[mid], per, walls[mid]
 
     other = {"fused": "separate", "separate": "fused", "paged_fused": "paged", "paged": None,
              "stochastic": None}[args.api]
     ms_other = time_api(other)[0] if other else None
-    ms_per_step, t_wall = time_api(args.api)
+    ms_per_step, ms_repeats, t_wall = time_api(args.api)
     t_step = ms_per_step * 1e-3
 
     # ---- per-call durations: a separate eager pass with events between the calls -------------
@@ -961,6 +1095,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_repeats": ms_repeats,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -997,6 +1132,13 @@ def main() -> int:
         result["cpu_baseline"] = cpu_baseline(w, kv_bytes, args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
+    others = [x for x in args.also.split(",") if x and x != args.workload]
+    if others:
+        del sets
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        result["other_workloads"] = {x: other_workload_bench(tv, torch, x, args, stream)
+                                     for x in others}
     print(json.dumps(result))
     return 0
 
