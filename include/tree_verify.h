@@ -320,6 +320,35 @@ int tree_verify_step(const int32_t* parent, const int32_t* draft_tok, const int3
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * tree_verify_step_noalloc — tree_verify_step for callers that cannot allocate device memory:
+ * code under HIP graph capture that may not call hipMalloc, tight serving loops, harnesses that
+ * forbid allocation.  It calls no allocating routine.  The split-K partials go to a device array
+ * owned by the library, TV_NOALLOC_SCRATCH_BYTES on each GPU the library runs on, held until
+ * the process ends; its device address is looked up once per device, on the first call with
+ * that device current.
+ *
+ * Arguments, results and status bits as for tree_verify_step, without workspace and
+ * workspace_bytes.  Returns TV_ERR_WORKSPACE, launching nothing, when
+ * tree_verify_attn_workspace_size(B, T, Hq, Hkv, D, Lmax, dtype, split_keys) exceeds
+ * TV_NOALLOC_SCRATCH_BYTES.  The automatic split (split_keys = 0) always fits on a 256-CU
+ * device: a plan splits only while there are fewer than 512 (sequence, KV head, row block)
+ * units, so it holds fewer than 1024 partial slots of 256 rows x (D + 2) floats, at most
+ * 136.2 MB.  An explicit split_keys may need more; a larger one needs less.
+ * Every call on one GPU uses that GPU's one array, and each call rewrites what it reads, so no
+ * state carries over between calls; calls that overlap in time on one GPU (on different
+ * streams or from different host threads) race on the array and give wrong results.
+ */
+#define TV_NOALLOC_SCRATCH_BYTES (144u << 20)
+int tree_verify_step_noalloc(const int32_t* parent, const int32_t* draft_tok,
+                             const int32_t* target_tok, const void* q, void* k_cache,
+                             void* v_cache, const int32_t* cache_len, int32_t* cache_len_out,
+                             const void* k_tree, const void* v_tree, uint64_t* anc_mask,
+                             void* out, float* lse, int32_t* accept_path, int32_t* accept_len,
+                             int32_t* bonus_tok, int32_t* status, int B, int T, int Hq, int Hkv,
+                             int D, int Lmax, int dtype, float scale, int split_keys,
+                             void* stream);
+
+/*
  * tree_verify_step_paged — the verification step over a paged cache: tree_build_mask,
  * tree_verify_attn_paged, tree_accept and kv_commit_paged, in that order and with the same
  * results and status bits, fused into two kernel launches (the paged attention main kernel,

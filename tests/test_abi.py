@@ -385,3 +385,22 @@ def test_lm_head_argument_errors(lib):
         bad = list(base)
         bad[i] = v
         assert lib.lm_head_topk(*bad) == -1, (i, v)
+
+
+def test_noalloc_rejects_plans_beyond_its_array(lib):
+    """tree_verify_step_noalloc refuses, before any device call, a plan whose split-K partials
+    exceed its fixed device array; the automatic plan of the largest workloads fits."""
+    import re
+
+    hdr = open(HEADER, encoding="utf-8").read()
+    m = re.search(r"#define TV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    limit = int(m.group(1)) << int(m.group(2))
+    ws = lib.tree_verify_attn_workspace_size
+    # 64-key chunks over a 65536-token cache at batch 64: far more partials than the array holds
+    assert ws(64, 128, 32, 8, 128, 65536, 1, 64) > limit
+    args = [FAKE] * 17 + [64, 128, 32, 8, 128, 65536, 1, ctypes.c_float(0.0), 64, None]
+    assert lib.tree_verify_step_noalloc(*args) == -3
+    # automatic plans: the worst case (511 units of two chunks each, fp32, D = 128) and the
+    # 70B-like workload fit
+    assert 0 < ws(511, 64, 1, 1, 128, 4096, 0, 0) <= limit
+    assert 0 < ws(8, 64, 64, 8, 128, 32832, 1, 0) <= limit

@@ -21,7 +21,8 @@ TV_BAD_TOKEN, TV_SYNC_TIMEOUT, TV_BAD_CONF, TV_FREE_FULL = 0x20, 0x40, 0x80, 0x1
 
 EXPORTS = ("tv_status_string", "tree_build_mask", "tree_verify_attn_workspace_size",
            "tree_verify_attn", "tree_accept", "kv_compact_accepted", "tv_profile_attn_main",
-           "tree_verify_step", "tree_verify_attn_paged", "kv_commit_paged",
+           "tree_verify_step", "tree_verify_step_noalloc", "tree_verify_attn_paged",
+           "kv_commit_paged",
            "tree_verify_step_paged",
            "tree_accept_stochastic", "tree_accept_stochastic_workspace_size",
            "tv_profile_accept_stochastic", "eagle2_node_count", "eagle2_expand",
@@ -80,6 +81,9 @@ def _declare(lib: ctypes.CDLL) -> None:
     lib.tree_verify_step.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                      I, I, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
     lib.tree_verify_step.restype = I
+    lib.tree_verify_step_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                             I, I, I, I, I, I, I, F, I, P]
+    lib.tree_verify_step_noalloc.restype = I
     lib.tree_verify_attn_paged.argtypes = [P, P, P, I, P, I, I, P, P, P, P, P, P,
                                            I, I, I, I, I, I, F, I, P, ctypes.c_size_t, P]
     lib.tree_verify_attn_paged.restype = I
@@ -337,6 +341,26 @@ def tree_verify_step(parent, draft_tok, target_tok, q, k_cache, v_cache, cache_l
 
     Returns a dict with anc_mask, out, lse, accept_path, accept_len, bonus_tok, cache_len_out
     and status."""
+    return _step(False, parent, draft_tok, target_tok, q, k_cache, v_cache, cache_len, k_tree,
+                 v_tree, cache_len_out, out, lse, anc_mask, accept_path, accept_len, bonus_tok,
+                 status, scale, split_keys, workspace, with_lse, stream)
+
+
+def tree_verify_step_noalloc(parent, draft_tok, target_tok, q, k_cache, v_cache, cache_len,
+                             k_tree, v_tree, cache_len_out=None, out=None, lse=None,
+                             anc_mask=None, accept_path=None, accept_len=None, bonus_tok=None,
+                             status=None, scale: float = 0.0, split_keys: int = 0,
+                             with_lse: bool = True, stream=None):
+    """tree_verify_step whose split-K workspace is the library's own device array: the library
+    allocates nothing (outputs the caller does not pass are still allocated here, by torch)."""
+    return _step(True, parent, draft_tok, target_tok, q, k_cache, v_cache, cache_len, k_tree,
+                 v_tree, cache_len_out, out, lse, anc_mask, accept_path, accept_len, bonus_tok,
+                 status, scale, split_keys, None, with_lse, stream)
+
+
+def _step(noalloc, parent, draft_tok, target_tok, q, k_cache, v_cache, cache_len, k_tree,
+          v_tree, cache_len_out, out, lse, anc_mask, accept_path, accept_len, bonus_tok, status,
+          scale, split_keys, workspace, with_lse, stream):
     _need(parent, "parent", torch.int32, 2)
     _need(draft_tok, "draft_tok", torch.int32, 2)
     _need(target_tok, "target_tok", torch.int32, 2)
@@ -373,16 +397,21 @@ def tree_verify_step(parent, draft_tok, target_tok, q, k_cache, v_cache, cache_l
                     ("cache_len_out", cache_len_out), ("status", status)):
         _need(t, name, torch.int32, 1)
     _need(accept_path, "accept_path", torch.int32, 2)
-    ws_bytes = tree_verify_attn_workspace_size(B, T, Hq, Hkv, D, Lmax, q.dtype, split_keys)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
-    ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check("tree_verify_step", load_library().tree_verify_step(
-        _ptr(parent), _ptr(draft_tok), _ptr(target_tok), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-        _ptr(cache_len), _ptr(cache_len_out), _ptr(k_tree), _ptr(v_tree), _ptr(anc_mask),
-        _ptr(out), _ptr(lse), _ptr(accept_path), _ptr(accept_len), _ptr(bonus_tok),
-        _ptr(status), B, T, Hq, Hkv, D, Lmax, dt, float(scale), int(split_keys),
-        _ptr(workspace), ws_have, _stream(stream)))
+    args = (_ptr(parent), _ptr(draft_tok), _ptr(target_tok), _ptr(q), _ptr(k_cache),
+            _ptr(v_cache), _ptr(cache_len), _ptr(cache_len_out), _ptr(k_tree), _ptr(v_tree),
+            _ptr(anc_mask), _ptr(out), _ptr(lse), _ptr(accept_path), _ptr(accept_len),
+            _ptr(bonus_tok), _ptr(status), B, T, Hq, Hkv, D, Lmax, dt, float(scale),
+            int(split_keys))
+    if noalloc:
+        _check("tree_verify_step_noalloc",
+               load_library().tree_verify_step_noalloc(*args, _stream(stream)))
+    else:
+        ws_bytes = tree_verify_attn_workspace_size(B, T, Hq, Hkv, D, Lmax, q.dtype, split_keys)
+        if workspace is None and ws_bytes > 0:
+            workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+        ws_have = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _check("tree_verify_step", load_library().tree_verify_step(
+            *args, _ptr(workspace), ws_have, _stream(stream)))
     return dict(anc_mask=anc_mask, out=out, lse=lse, accept_path=accept_path,
                 accept_len=accept_len, bonus_tok=bonus_tok, cache_len_out=cache_len_out,
                 status=status)

@@ -36,6 +36,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "tree_device.h"
@@ -1654,3 +1655,55 @@ extern "C" int tree_verify_step_paged(
   return D == 128 ? launch_step<float, 128, 1>(a, t, st) : launch_step<float, 64, 1>(a, t, st);
 }
 
+// ---- tree_verify_step_noalloc: the step with a library-owned workspace ----------------------
+// The split-K partials live in this array instead of a caller's workspace.  Every GPU the
+// library runs on holds its own copy for the life of the process.  In host code the name is
+// only a host-side handle: the device address is looked up once per device (scratch_on_device)
+// and only that address is ever passed to a kernel.
+static __device__ __align__(256) char scratch[TV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on the first call on that device (with
+// that device current).
+int scratch_on_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return TV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return TV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TV_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return TV_OK;
+}
+}  // namespace
+
+extern "C" int tree_verify_step_noalloc(const int32_t* parent, const int32_t* draft_tok,
+                                        const int32_t* target_tok, const void* q, void* k_cache,
+                                        void* v_cache, const int32_t* cache_len,
+                                        int32_t* cache_len_out, const void* k_tree,
+                                        const void* v_tree, uint64_t* anc_mask, void* out,
+                                        float* lse, int32_t* accept_path, int32_t* accept_len,
+                                        int32_t* bonus_tok, int32_t* status, int B, int T,
+                                        int Hq, int Hkv, int D, int Lmax, int dtype, float scale,
+                                        int split_keys, void* stream) {
+  // the size check comes first: a plan beyond the array is refused before any device call
+  const size_t need =
+      tree_verify_attn_workspace_size(B, T, Hq, Hkv, D, Lmax, dtype, split_keys);
+  if (need > (size_t)TV_NOALLOC_SCRATCH_BYTES) return TV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int rc = scratch_on_device(&ws);
+    if (rc != TV_OK) return rc;
+  }
+  return tree_verify_step(parent, draft_tok, target_tok, q, k_cache, v_cache, cache_len,
+                          cache_len_out, k_tree, v_tree, anc_mask, out, lse, accept_path,
+                          accept_len, bonus_tok, status, B, T, Hq, Hkv, D, Lmax, dtype, scale,
+                          split_keys, ws, need, stream);
+}
