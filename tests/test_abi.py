@@ -123,8 +123,8 @@ def test_workspace_size_rules(lib):
     # sequence
     assert ws(1, 8, 2, 1, 64, 4096, 0, 256) == 17 * 256 * (64 * 4 + 8) + 1 * 4
     # G*T = 8*60 = 480 rows -> 2 row blocks of 256; 65 tiles in chunks of 32 -> 3 chunks;
-    # bf16 inputs keep the partial O in bf16
-    assert ws(2, 60, 64, 8, 128, 4096, 1, 2048) == 2 * 8 * 2 * 3 * 256 * (128 * 2 + 8) + 2 * 4
+    # the partial O is fp32 for bf16 inputs too
+    assert ws(2, 60, 64, 8, 128, 4096, 1, 2048) == 2 * 8 * 2 * 3 * 256 * (128 * 4 + 8) + 2 * 4
     # bad arguments report 0
     assert ws(1, 8, 3, 2, 64, 4096, 0, 0) == 0
     assert ws(1, 8, 2, 1, 80, 4096, 0, 0) == 0

@@ -90,8 +90,12 @@ struct Layout {
   static constexpr int kRowBytes = D * kElem;          // 128, 256 or 512
   static constexpr int kCPR = kRowBytes / 16;          // 16-byte chunks per row
   static constexpr int kTile = kKT * kRowBytes;        // bytes of one K (or V) tile
-  static constexpr int kStage = 2 * kTile;             // K tile then V tile
+  static constexpr int kStage = 2 * kTile;             // one K tile and one V tile
   static constexpr int kStages = kStage <= 32768 ? 4 : 2;
+  // K stage s at s * kTile, V stage s at kVBase + s * kTile: every K stage lies within the first
+  // 64 KB and every V stage within 64 KB of kVBase, so (bf16) a fragment read takes its stage as
+  // an immediate offset from one fixed per-lane address
+  static constexpr int kVBase = kStages * kTile;
   // bf16 pipelines blocks across tile barriers: four stages hold the tile read for S, the tile
   // read for O and two in flight.  fp32 (the small exact path) runs its blocks one after the
   // other, with every stage but the current one in flight.
@@ -111,11 +115,10 @@ struct Layout {
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value of lane l ^ 32.
-__device__ inline float partner(float x) {
-  const int lane = __lane_id();
+// Value of lane l ^ 32 (hi: the calling lane is one of lanes 32..63).
+__device__ inline float partner(float x, int hi) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-  return __int_as_float(lane < 32 ? r[1] : r[0]);
+  return __int_as_float(hi ? r[0] : r[1]);
 }
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
@@ -483,8 +486,8 @@ void attn_main(AttnArgs a) {
 
   auto issue_tile = [&](int tile) __attribute__((always_inline)) {
     const int stage = tile % kNS;
-    const uint32_t kl = smem_base + stage * Lay::kStage + wave * kDPW * 1024;
-    const uint32_t vl = kl + Lay::kTile;
+    const uint32_t kl = smem_base + stage * Lay::kTile + wave * kDPW * 1024;
+    const uint32_t vl = kl + Lay::kVBase;
     if constexpr (kPaged) {
       if constexpr (!Lay::kCrossTile) {
         // fp32 (the small exact path): entries fetched at issue, waiting for everything
@@ -580,8 +583,11 @@ void attn_main(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
         const int row = 8 * sec + tr_key;
-        voff[sec * kDB + db] =
-            row * kRB + (((4 * db + (tr_d >> 3)) ^ Lay::swz(row)) << 4) + (tr_d & 7) * 2;
+        // V tiles sit at kVBase and above: the base is held here, so the stage and block
+        // offsets (under 64 KB) fit the reads' immediate field
+        voff[sec * kDB + db] = Lay::kVBase + row * kRB +
+                               (((4 * db + (tr_d >> 3)) ^ Lay::swz(row)) << 4) + (tr_d & 7) * 2;
+        asm volatile("" : "+v"(voff[sec * kDB + db]));
       }
   }
 
@@ -642,47 +648,41 @@ void attn_main(AttnArgs a) {
     if (t + Lay::kAhead < n_tiles) issue_tile(t + Lay::kAhead);
   };
 
-  // LDS offsets of the lane's fragments in the tile whose K (V) is being read.
-  uint32_t kaddr[kBF16 ? kKS : 1], vaddr[kBF16 ? 2 * kDB : 1];
-  auto set_k = [&](int tile) __attribute__((always_inline)) {
-    if constexpr (kBF16) {
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) kaddr[ks] = koff[ks] + (tile % kNS) * Lay::kStage;
-    } else {
-      kaddr[0] = (tile % kNS) * Lay::kStage;
-    }
+  // LDS byte offset of the K (V) tile of ring stage st.  In the bf16 pipeline the stage is a
+  // compile-time constant, so the fragment reads below take it as an immediate offset from the
+  // fixed per-lane koff / voff.
+  auto kbase = [&](int st) __attribute__((always_inline)) -> uint32_t { return st * Lay::kTile; };
+  auto vbase = [&](int st) __attribute__((always_inline)) -> uint32_t {
+    return Lay::kVBase + st * Lay::kTile;
   };
-  auto set_v = [&](int tile) __attribute__((always_inline)) {
-    if constexpr (kBF16) {
-#pragma unroll
-      for (int i = 0; i < 2 * kDB; ++i)
-        vaddr[i] = voff[i] + (tile % kNS) * Lay::kStage + Lay::kTile;
-    } else {
-      vaddr[0] = (tile % kNS) * Lay::kStage + Lay::kTile;
-    }
+  // bf16 V reads: voff already holds kVBase
+  auto vbase_rel = [&](int st) __attribute__((always_inline)) -> uint32_t {
+    return st * Lay::kTile;
   };
 
-  // S^T = K Q^T for block j (its tile set by set_k)
-  auto qk = [&](int j, f32x16& S) __attribute__((always_inline)) {
+  // S^T = K Q^T for block j, its K tile at LDS offset kb0
+  auto qk = [&](int j, f32x16& S, uint32_t kb0) __attribute__((always_inline)) {
     const int kb = j & 1;
     S = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       if constexpr (kBF16) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(smem + kaddr[ks] + kb * 32 * kRB);
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(smem + koff[ks] + (kb0 + kb * 32 * kRB));
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S, 0, 0, 0);
       } else {
         const int key = kb * 32 + n;
         const int d = 2 * ks + h;
         const float kf = *reinterpret_cast<const float*>(
-            smem + kaddr[0] + key * kRB + ((((d >> 2) ^ Lay::swz(key))) << 4) + (d & 3) * 4);
+            smem + kb0 + key * kRB + ((((d >> 2) ^ Lay::swz(key))) << 4) + (d & 3) * 4);
         S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf, qf[ks], S, 0, 0, 0);
       }
     }
   };
 
-  // O^T += V^T P^T for block j (its tile set by set_v)
-  auto pv = [&](int j, const PBlock<kBF16>& P) __attribute__((always_inline)) {
+  // O^T += V^T P^T for block j, its V tile at LDS offset vb0 (bf16: relative to kVBase, which
+  // voff holds; fp32: absolute)
+  auto pv = [&](int j, const PBlock<kBF16>& P, uint32_t vb0) __attribute__((always_inline)) {
     const int kb = j & 1;
     if constexpr (kBF16) {
       // 16-key step st: keys kb*32 + 16st + {4h..4h+3} (elements 0-3) and kb*32 + 16st + 8 +
@@ -690,13 +690,13 @@ void attn_main(AttnArgs a) {
       // consecutive keys at d = D0 + i.
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const char* vl = smem + (kb * 32 + 16 * st) * kRB;
+        const uint32_t vo = vb0 + (kb * 32 + 16 * st) * kRB;  // stage offset of V, relative
 #pragma unroll
         for (int db = 0; db < kDB; ++db) {
           const i16x4 x0 =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vl + vaddr[db]));
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + voff[db] + vo));
           const i16x4 x1 =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vl + vaddr[kDB + db]));
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + voff[kDB + db] + vo));
           const i16x8 v = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v),
                                                             P.v[st], oacc[db], 0, 0, 0);
@@ -710,7 +710,7 @@ void attn_main(AttnArgs a) {
         for (int db = 0; db < kDB; ++db) {
           const int d = db * 32 + n;
           const float vf = *reinterpret_cast<const float*>(
-              smem + vaddr[0] + key * kRB + ((((d >> 2) ^ Lay::swz(key))) << 4) + (d & 3) * 4);
+              smem + vb0 + key * kRB + ((((d >> 2) ^ Lay::swz(key))) << 4) + (d & 3) * 4);
           oacc[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vf, P.v[e], oacc[db], 0, 0, 0);
         }
       }
@@ -775,7 +775,7 @@ void attn_main(AttnArgs a) {
       float mx = S[0];
 #pragma unroll
       for (int e = 1; e < 16; ++e) mx = fmaxf(mx, S[e]);
-      mx = fmaxf(mx, partner(mx));
+      mx = fmaxf(mx, partner(mx, h));
       const float m_new = fmaxf(m_run, mx * a.c);
       alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);  // 0 while m_run is unset
       m_run = m_new;
@@ -823,56 +823,69 @@ void attn_main(AttnArgs a) {
     }
   };
   if constexpr (Lay::kCrossTile) {
+    static_assert(kNS == 4, "the bf16 pipeline unrolls its tile loop over four ring stages");
     barrier_tile(0);
     masks_from_lds();
-    set_k(0);
-    qk(0, Se);
+    qk(0, Se, kbase(0));
     mask_block(0, Se);
     // R(0)
-    qk(1, So);
+    qk(1, So, kbase(0));
     softmax(Se, Pe);
     end_region(Pe);
     mask_block(1, So);
     rescale();
-    for (int t = 1; t < n_tiles; ++t) {
+    // Tile t (stage t % 4) reads K of tile t and V of tile t - 1.  The stage is a template
+    // constant of each unrolled copy, so every fragment address is fixed per lane.
+    auto tile_step = [&](int t, auto stage) __attribute__((always_inline)) {
+      constexpr int SK = decltype(stage)::value, SV = (SK + kNS - 1) % kNS;
       barrier_tile(t);
       // R(2t-1): S of block 2t, O of block 2t-2, softmax of block 2t-1
-      set_k(t);
-      set_v(t - 1);
-      qk(2 * t, Se);
-      pv(2 * t - 2, Pe);
+      qk(2 * t, Se, kbase(SK));
+      pv(2 * t - 2, Pe, vbase_rel(SV));
       softmax(So, Po);
       end_region(Po);
       mask_block(2 * t, Se);
       rescale();
       // R(2t): S of block 2t+1, O of block 2t-1, softmax of block 2t
-      qk(2 * t + 1, So);
-      pv(2 * t - 1, Po);
+      qk(2 * t + 1, So, kbase(SK));
+      pv(2 * t - 1, Po, vbase_rel(SV));
       softmax(Se, Pe);
       end_region(Pe);
       mask_block(2 * t + 1, So);
       rescale();
+    };
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    using S0 = std::integral_constant<int, 0>;
+    for (int t = 1; t < n_tiles; t += 4) {  // t % 4 == 1 at the top of every pass
+      tile_step(t, S1{});
+      if (t + 1 >= n_tiles) break;
+      tile_step(t + 1, S2{});
+      if (t + 2 >= n_tiles) break;
+      tile_step(t + 2, S3{});
+      if (t + 3 >= n_tiles) break;
+      tile_step(t + 3, S0{});
     }
     // R(2n-1): O of block 2n-2, softmax of block 2n-1; then O of block 2n-1
-    set_v(n_tiles - 1);
-    pv(2 * n_tiles - 2, Pe);
+    const uint32_t vlast = vbase_rel((n_tiles - 1) % kNS);
+    pv(2 * n_tiles - 2, Pe, vlast);
     softmax(So, Po);
     end_region(Po);
     rescale();
-    pv(2 * n_tiles - 1, Po);
+    pv(2 * n_tiles - 1, Po, vlast);
   } else {
     for (int t = 0; t < n_tiles; ++t) {
       barrier_tile(t);
       if (t == 0) masks_from_lds();
-      set_k(t);
-      set_v(t);
+      const uint32_t kb0 = kbase(t % kNS), vb0 = vbase(t % kNS);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        qk(2 * t + kb, Se);
+        qk(2 * t + kb, Se, kb0);
         mask_block(2 * t + kb, Se);
         softmax(Se, Pe);
         rescale();
-        pv(2 * t + kb, Pe);
+        pv(2 * t + kb, Pe, vb0);
       }
     }
   }
@@ -882,7 +895,7 @@ void attn_main(AttnArgs a) {
   // the fused step's second kernel reports bad pages instead)
   if (kPaged && !kMasks && __ballot(bad_slot) && lane == 0 && a.status)
     atomicOr(a.status + b, TV_BAD_PAGE);
-  l_run += partner(l_run);
+  l_run += partner(l_run, h);
 
   if (direct) {
     if (row_ok) {
@@ -909,24 +922,18 @@ void attn_main(AttnArgs a) {
       if (a.lse && h == 0) a.lse[orow] = (m_run + __log2f(l_run)) * kLn2;
     }
   } else if (row_ok) {  // padding rows are never merged
-    // unnormalised O in the input type (bf16 partials carry the rounding the output gets
-    // anyway), four consecutive d per lane and group: group index ((wave*kDB + db)*4 + j)*64 + lane
+    // unnormalised O in fp32 whatever the input type (the fp32 accumulation is never rounded
+    // before the merge), four consecutive d per lane and group: group index
+    // ((wave*kDB + db)*4 + j)*64 + lane, so a wavefront's store is one 1 KB run
     const size_t slot = (((size_t)b * a.Hkv + kvh) * a.RB + rb) * a.S + s;
-    using PO = typename std::conditional<kBF16, uint2, float4>::type;
-    PO* po = reinterpret_cast<PO*>(a.part_o + slot * (size_t)kRows * D * sizeof(E));
+    float4* po = reinterpret_cast<float4*>(a.part_o + slot * (size_t)kRows * D * sizeof(float));
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x16& acc = oacc[db];
-        if constexpr (kBF16) {
-          store_stream(&po[(((wave * kDB + db) * 4 + j) << 6) + lane],
-                       uint2{pack_bf16x2(acc[4 * j], acc[4 * j + 1]),
-                             pack_bf16x2(acc[4 * j + 2], acc[4 * j + 3])});
-        } else {
-          store_stream(&po[(((wave * kDB + db) * 4 + j) << 6) + lane],
-                       float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]});
-        }
+        store_stream(&po[(((wave * kDB + db) * 4 + j) << 6) + lane],
+                     float4{acc[4 * j], acc[4 * j + 1], acc[4 * j + 2], acc[4 * j + 3]});
       }
     if (h == 0) {
       float2* pml = reinterpret_cast<float2*>(a.part_ml + slot * (size_t)kRows * 2);
@@ -937,9 +944,8 @@ void attn_main(AttnArgs a) {
 
 // Merge the per-chunk partials of sequences with more than one non-empty chunk:
 //   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  lse = (M + log2 den) ln 2.
-// A thread owns 16 bytes of a slot's partial, in the partials' register order: in bf16 two
-// adjacent groups (rows r, r + 1 of one wavefront, four consecutive d), in fp32 one group (one
-// row, four d).  Chunks are taken kBatch at a time, exactly as many as the sequence has, with
+// A thread owns 16 bytes of a slot's partial, in the partials' register order: one group (one
+// row, four consecutive d, fp32).  Chunks are taken kBatch at a time, exactly as many as the sequence has, with
 // all their loads in flight, and M is raised per batch (online, as in the main kernel).  With
 // few chunks (S <= 8) every thread of a workgroup owns different bytes and merges all chunks.
 // With more, the four wavefronts of a workgroup own the same 64 pieces and take every fourth
@@ -949,7 +955,7 @@ void attn_main(AttnArgs a) {
 // were written to.
 template <typename E>
 constexpr int combine_rows_per_thread() {
-  return std::is_same<E, __bf16>::value ? 2 : 1;
+  return 1;  // the partials are fp32 for every input type
 }
 
 // the merge's compile-time shape for a plan with S chunks per (b, kvh, rb)
@@ -1040,14 +1046,8 @@ __device__ void combine_group(const AttnArgs& a, int c) {
         else return ml[u].y;
       };
       auto val_of = [&](int u) {
-        if constexpr (kBF16) {
-          const uint32_t lo = i == 0 ? v[u].x : v[u].z, hi = i == 0 ? v[u].y : v[u].w;
-          return float4{__uint_as_float(lo << 16), __uint_as_float(lo & 0xffff0000u),
-                        __uint_as_float(hi << 16), __uint_as_float(hi & 0xffff0000u)};
-        } else {
-          return float4{__uint_as_float(v[u].x), __uint_as_float(v[u].y),
-                        __uint_as_float(v[u].z), __uint_as_float(v[u].w)};
-        }
+        return float4{__uint_as_float(v[u].x), __uint_as_float(v[u].y),
+                      __uint_as_float(v[u].z), __uint_as_float(v[u].w)};
       };
       // A chunk in which a row sees no key (a second tree tile that holds none of the row's
       // ancestors, cut into a chunk of its own) carries m = -inf, l = 0, O = 0.  When every
@@ -1286,7 +1286,7 @@ struct Plan {
   size_t ws_bytes;
 };
 
-Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int elem_bytes, int split_keys) {
+Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int split_keys) {
   Plan p;
   const int G = Hq / Hkv;
   p.RB = ceil_div(G * T, kRows);
@@ -1296,20 +1296,34 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int elem_bytes, i
   if (split_keys > 0) {
     chunk_tiles = ceil_div(split_keys, kKT);
   } else {
-    // One workgroup per compute unit: aim for two rounds, with chunks of at least 3 tiles
-    // (shorter chunks spend more on filling the load pipeline and writing partials than they
-    // gain in parallelism).
+    // One workgroup per compute unit.  A chunk costs a prologue (Q and the first tiles), a
+    // 128 KB fp32 partial (256 rows x D = 128) written and merged, so splitting pays only where
+    // CUs would otherwise idle:
+    //  * fewer (sequence, KV head, row block) units than CUs: aim for two rounds, with chunks
+    //    of at least 4 tiles (3-tile chunks write a larger partial than the 96 KB of K/V they
+    //    read: 20.8 against 19.9 us at batch 1, prefix 4096);
+    //  * at least as many units as CUs, but fewer than twice: only sequences longer than 3/4
+    //    of the longest split, into a 3/4 chunk and the rest, which the longest-first dispatch
+    //    places in the second round (126 us against 143 us for halves at batch 32, prefixes of
+    //    512..4096: most sequences then need no merge at all);
+    //  * twice the CUs or more: no split; the longest-first dispatch balances the rounds.
     const long long units = (long long)B * Hkv * p.RB;
-    const long long want = 2LL * device_cu_count();
-    const int S = (int)std::min<long long>(std::max<long long>(1, ceil_div_ll(want, units)),
-                                           std::max(1, ceil_div(tiles, 3)));
-    chunk_tiles = ceil_div(tiles, S);
+    const long long cus = device_cu_count();
+    if (units >= 2 * cus) {
+      chunk_tiles = tiles;
+    } else if (units >= cus) {
+      chunk_tiles = std::max(1, ceil_div(3 * tiles, 4));
+    } else {
+      const int S = (int)std::min<long long>(std::max<long long>(1, ceil_div_ll(2 * cus, units)),
+                                             std::max(1, ceil_div(tiles, 4)));
+      chunk_tiles = ceil_div(tiles, S);
+    }
   }
   p.chunk_tiles = chunk_tiles;
   p.S = ceil_div(tiles, chunk_tiles);
-  // per slot: kRows x D partial O in the input type, then kRows x (m, l) in fp32; then the
-  // chunk count of every sequence
-  p.ws_bytes = p.S > 1 ? (size_t)B * Hkv * p.RB * p.S * kRows * ((size_t)D * elem_bytes + 8) +
+  // per slot: kRows x D partial O in fp32, then kRows x (m, l) in fp32; then the chunk count
+  // of every sequence
+  p.ws_bytes = p.S > 1 ? (size_t)B * Hkv * p.RB * p.S * kRows * ((size_t)D * 4 + 8) +
                              (size_t)B * sizeof(int32_t)
                        : 0;
   return p;
@@ -1402,7 +1416,7 @@ extern "C" size_t tree_verify_attn_workspace_size(int B, int T, int Hq, int Hkv,
   if (!attn_shapes_ok(B, T, Hq, Hkv, Lmax) || (D != 64 && D != 128) ||
       (dtype != TV_F32 && dtype != TV_BF16))
     return 0;
-  return make_plan(B, T, Hq, Hkv, D, Lmax, dtype == TV_BF16 ? 2 : 4, split_keys).ws_bytes;
+  return make_plan(B, T, Hq, Hkv, D, Lmax, split_keys).ws_bytes;
 }
 
 // Checks the attention arguments and fills `a`; returns TV_OK or the error to report.
@@ -1416,7 +1430,7 @@ static int prepare_attn(AttnArgs& a, Plan& p, const void* q, const void* k_cache
       !attn_shapes_ok(B, T, Hq, Hkv, Lmax) || split_keys < 0)
     return TV_ERR_INVALID_ARG;
   if ((dtype != TV_F32 && dtype != TV_BF16) || (D != 64 && D != 128)) return TV_ERR_UNSUPPORTED;
-  p = make_plan(B, T, Hq, Hkv, D, Lmax, dtype == TV_BF16 ? 2 : 4, split_keys);
+  p = make_plan(B, T, Hq, Hkv, D, Lmax, split_keys);
   if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes)) return TV_ERR_WORKSPACE;
   if ((long long)B * Hkv * p.RB * p.S >= (1LL << 31)) return TV_ERR_INVALID_ARG;
 
@@ -1451,12 +1465,11 @@ static int prepare_attn(AttnArgs& a, Plan& p, const void* q, const void* k_cache
   a.lpt = B > 1 && (long long)B * p.S <= kLptMaxPairs;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
   a.c = sc * kLog2e;
-  const int elem = dtype == TV_BF16 ? 2 : 4;
   char* ws = (char*)workspace;
   const size_t slots = (size_t)B * Hkv * p.RB * p.S;
   a.part_o = ws;
-  a.part_ml = p.ws_bytes ? (float*)(ws + slots * kRows * D * elem) : nullptr;
-  a.nsplit = p.ws_bytes ? (int32_t*)(ws + slots * kRows * ((size_t)D * elem + 8)) : nullptr;
+  a.part_ml = p.ws_bytes ? (float*)(ws + slots * kRows * D * sizeof(float)) : nullptr;
+  a.nsplit = p.ws_bytes ? (int32_t*)(ws + slots * kRows * ((size_t)D * sizeof(float) + 8)) : nullptr;
   return TV_OK;
 }
 
