@@ -687,7 +687,7 @@ def cpu_baseline(w, kv_bytes: int, target_s: float) -> dict:
         return np.stack([b, h, i], axis=1).astype(np.int32)
 
     L = np.clip(w.cache_len, 0, w.Lmax).astype(np.int32)
-    n0 = min(total, cores)
+    n0 = min(total, 32 * cores)  # a probe long enough that thread start-up does not dominate
     t0 = time.perf_counter()
     O.attention(w.q, w.k_cache, w.v_cache, L, w.k_tree, w.v_tree, w.parent, rows=rows_of(n0),
                 n_threads=cores)

@@ -456,16 +456,14 @@ int eagle2_rerank(const int32_t* node_tok, const int32_t* node_parent, const flo
  * go to memory.  Stage two gathers the candidates' rows of the full head W and recomputes their
  * logits exactly.  The drafter's children are the K best candidates (their tokens and
  * confidences feed eagle2_expand).  h, A, B and W are bfloat16 (16-bit words); results are
- * float32.  Which candidates and children are chosen is decided by float32 values computed in
- * a fixed order, so the results are bit-exact:
- *   - dot products over d (u = B h and the exact logits): 64 chains of fused multiply-adds
- *     from 0, chain j over the elements 512 p + 8 j + e for p = 0 .. d/512 - 1 (outer) and
- *     e = 0 .. 7 (inner), then the 64 chain sums combined pairwise, chain j with j^32, then
- *     j^16, ..., j^1;
- *   - screening scores A[row] . u[m]: one chain of fused multiply-adds over the rank index in
- *     order from 0.
- * Values rank by their float order with -0 as +0; equal values go to the smaller row of A
- * (screening) or the smaller token (children).
+ * float32.  The sums are float32 in an order of the kernels' own (fixed, so a call repeats
+ * bit for bit); each value is therefore the exact dot product of its bfloat16 operands within
+ * float32 rounding: d/64 + 6 roundings per term for u = B h and for the exact logits (each of
+ * 64 lanes sums d/64 products, then six pairwise combining steps), r per term for a screening
+ * score A[row] . u[m].  Choices made on such values (which candidates a tile keeps, which
+ * children win) are those of the exact values except where two of them lie within that
+ * rounding of each other.  Values rank by their float order with -0 as +0; equal values go to
+ * the smaller row of A (screening) or the smaller token (children).
  * h, B, A, W and u are read 16 bytes at a time: each must be 16-byte aligned (as any device
  * allocation is), else the call returns TV_ERR_INVALID_ARG.
  */

@@ -96,3 +96,41 @@ def lib_limit():
                        "tree_verify.h")
     m = re.search(r"#define TV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(hdr).read())
     return int(m.group(1)) << int(m.group(2))
+
+
+def test_noalloc_step_replays_in_a_graph():
+    """The use the entry point is for: the step captured in a HIP graph with no allocation in
+    it (every output passed in).  Replays, with eager calls on other inputs in between that use
+    the same device array, equal the eager result bit for bit."""
+    import tree_attention_verification_attn_amd as tv
+    from test_gpu_graph import _poison, _replays_match_eager, _step_buffers
+
+    w = make_workload("batch32_L512-4096_T60", B=5, T=60, L=(0, 900), Hq=8, Hkv=2, D=128,
+                      extra_seed=96)
+    w2 = make_workload("batch32_L512-4096_T60", B=5, T=60, L=(0, 900), Hq=8, Hkv=2, D=128,
+                       extra_seed=97)
+    g, g2 = upload(w), upload(w2)
+    bufs, bufs2 = _step_buffers(g, w), _step_buffers(g2, w2)
+    split = 128
+
+    def step(x, b):
+        tv.tree_verify_step_noalloc(x["parent"], x["draft"], x["target"], x["q"], x["k_cache"],
+                                    x["v_cache"], x["cache_len"], x["k_tree"], x["v_tree"],
+                                    split_keys=split, **b)
+
+    L = np.clip(w.cache_len, 0, w.Lmax)
+    ends = []
+
+    def poison():
+        if not ends:
+            ends.extend(np.minimum(L + bufs["accept_len"].cpu().numpy(), w.Lmax))
+        for v in bufs.values():
+            _poison(v)
+        for b in range(w.B):
+            g["k_cache"][b, :, int(L[b]):int(ends[b])].fill_(float("nan"))
+            g["v_cache"][b, :, int(L[b]):int(ends[b])].fill_(float("nan"))
+
+    outs = dict(bufs, k_cache=g["k_cache"], v_cache=g["v_cache"])
+    _replays_match_eager("tree_verify_step_noalloc", lambda: step(g, bufs), outs,
+                         lambda: step(g2, bufs2), poison=poison)
+    assert int(bufs["status"].abs().sum()) == 0

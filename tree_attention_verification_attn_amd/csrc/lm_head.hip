@@ -6,14 +6,16 @@
 // head W and recomputes their logits exactly.  The drafter's children are the K best candidates,
 // with confidences from a softmax over the candidates.
 //
-// The candidates and children are chosen by float32 values, so every dot product has a stated
-// order, part of the definition of the result:
+// The arithmetic is float32 in a fixed order of the kernels' choosing (the page defines the
+// stages, not a summation order; results are valid wherever two values lie within float32
+// rounding of each other, and each term passes through a bounded number of roundings):
 //   * lm_dot (u = B h, logits = W[token] h; d a multiple of 512): lane j of a wavefront runs a
 //     chain of fused multiply-adds from 0 over elements 512 p + 8 j + e (p = 0, 1, ... outer,
 //     e = 0 .. 7 inner), so every 16-byte load of the wavefront covers 1 KB contiguously; the
 //     64 chain sums are then combined by a butterfly, j with j^32, then j^16, ..., j^1, which
-//     leaves the same value in every lane;
-//   * screening (A u): one chain of fused multiply-adds over the rank index, in order, from 0.
+//     leaves the same value in every lane (d/64 + 6 roundings per term);
+//   * screening (A u): one chain of fused multiply-adds over the rank index, in order, from 0
+//     (r roundings per term).
 // Ranking uses an unsigned key of the float (-0 as +0); equal values go to the smaller row
 // (screening) or the smaller token (children).
 //
