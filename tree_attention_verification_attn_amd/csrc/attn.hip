@@ -401,6 +401,7 @@ void attn_main(AttnArgs a) {
   const int k1 = min(max(v1 - tree_tiles, 0) * kKT, L);
   const int n_prefix_tiles = k1 > k0 ? ceil_div(k1 - k0, kKT) : 0;
   const int n_tiles = n_tree_tiles + n_prefix_tiles;  // >= 1 for every non-empty chunk
+  const int mask_from = n_prefix_tiles > 0 && (k1 - k0) % kKT != 0 ? n_tiles - 1 : n_tiles;
 
   // ---- the lane's query row: r = rb*256 + wave*32 + n -------------------------------------
   const int r = rb * kRows + wave * 32 + n;
@@ -484,8 +485,11 @@ void attn_main(AttnArgs a) {
     }
   };
 
-  auto issue_tile = [&](int tile) __attribute__((always_inline)) {
-    const int stage = tile % kNS;
+  // `part`: 1 the K rows, 2 the V rows, 3 both.  The dense bf16 pipeline issues a tile's K rows
+  // at one tile barrier and its V rows half a tile later, so each wavefront's tile loads leave
+  // in two groups.
+  constexpr bool kSplitIssue = !kPaged && Lay::kCrossTile;
+  auto issue_tile = [&](int tile, int stage, int part) __attribute__((always_inline)) {
     const uint32_t kl = smem_base + stage * Lay::kTile + wave * kDPW * 1024;
     const uint32_t vl = kl + Lay::kVBase;
     if constexpr (kPaged) {
@@ -503,8 +507,8 @@ void attn_main(AttnArgs a) {
       for (int i = 0; i < kDPW; ++i) {
         // keys past the tree load the last node's row: masked to -inf, they add exactly 0
         const uint32_t off = (uint32_t)min(base + dma_row[i], a.T - 1) * tree_stride + dma_chunk[i];
-        lds_dma16(kl + i * 1024, kt_head, off);
-        lds_dma16(vl + i * 1024, vt_head, off);
+        if (part & 1) lds_dma16(kl + i * 1024, kt_head, off);
+        if (part & 2) lds_dma16(vl + i * 1024, vt_head, off);
       }
     } else {
       const int base = k0 + (tile - n_tree_tiles) * kKT;
@@ -512,8 +516,8 @@ void attn_main(AttnArgs a) {
       for (int i = 0; i < kDPW; ++i) {
         // keys past the chunk load its last row (never a row at or past cache_len)
         const uint32_t off = (uint32_t)min(base + dma_row[i], k1 - 1) * kRB + dma_chunk[i];
-        lds_dma16(kl + i * 1024, kc_head, off);
-        lds_dma16(vl + i * 1024, vc_head, off);
+        if (part & 1) lds_dma16(kl + i * 1024, kc_head, off);
+        if (part & 2) lds_dma16(vl + i * 1024, vc_head, off);
       }
     }
   };
@@ -530,7 +534,7 @@ void attn_main(AttnArgs a) {
   }
 #pragma unroll
   for (int t = 0; t < Lay::kAhead; ++t)
-    if (t < n_tiles) issue_tile(t);
+    if (t < n_tiles) issue_tile(t, t, 3);
   if constexpr (kPaged && Lay::kCrossTile) {
     if (n_tiles > 2) load_entries(2);
   }
@@ -614,7 +618,7 @@ void attn_main(AttnArgs a) {
   // done with the tile whose stage tile t + kAhead takes (across tiles, tile t-2, whose last
   // reader is the O^T step of block 2t-3; one block after another, tile t-1), so that tile is
   // loaded now.
-  auto barrier_tile = [&](int t) __attribute__((always_inline)) {
+  auto barrier_tile = [&](int t, int next_stage) __attribute__((always_inline)) {
     if constexpr (kPaged && Lay::kCrossTile) {
       // Issue order per barrier t: entries of tile t+3, then data of tile t+2.  Loads newer
       // than tile t's data: entries of t+2 and data of t+1 (issued at barrier t-1).
@@ -632,20 +636,19 @@ void attn_main(AttnArgs a) {
         if (t + 3 < n_tiles) vm_wait<Dd + En>();
         else vm_wait<Dd>();
         asm volatile("" ::: "memory");
-        issue_tile(t + 2);
+        issue_tile(t + 2, next_stage, 3);
       }
       return;
     }
     // newer tiles may stay in flight
-    const int newer = min(Lay::kAhead - 1, n_tiles - 1 - t);
-    if (Lay::kAhead >= 3 && newer >= 2) vm_wait<(Lay::kAhead >= 3 ? 4 * kDPW : 0)>();
-    else if (Lay::kAhead >= 2 && newer == 1) vm_wait<(Lay::kAhead >= 2 ? 2 * kDPW : 0)>();
+    if (Lay::kAhead >= 3 && t + 2 < n_tiles) vm_wait<(Lay::kAhead >= 3 ? 4 * kDPW : 0)>();
+    else if (Lay::kAhead >= 2 && t + 1 < n_tiles) vm_wait<(Lay::kAhead >= 2 ? 2 * kDPW : 0)>();
     else vm_wait<0>();
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): earlier LDS reads are done
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (t + Lay::kAhead < n_tiles) issue_tile(t + Lay::kAhead);
+    if (t + Lay::kAhead < n_tiles) issue_tile(t + Lay::kAhead, next_stage, kSplitIssue ? 1 : 3);
   };
 
   // LDS byte offset of the K (V) tile of ring stage st.  In the bf16 pipeline the stage is a
@@ -722,6 +725,7 @@ void attn_main(AttnArgs a) {
   // tile; a tree tile covers nodes 64*tile .. 64*tile+63, so one mask word per row.
   auto mask_block = [&](int j, f32x16& S) __attribute__((always_inline)) {
     const int tile = j >> 1, kb = j & 1;
+    if (tile >= n_tree_tiles && tile < mask_from) return;
     const bool is_tree = tile < n_tree_tiles;
     const int base = is_tree ? (v0 + tile) * kKT : k0 + (tile - n_tree_tiles) * kKT;
     const int lim = (is_tree ? a.T : k1) - base - kb * 32;  // keys of this block that exist
@@ -844,7 +848,7 @@ void attn_main(AttnArgs a) {
   };
   if constexpr (Lay::kCrossTile) {
     static_assert(kNS == 4, "the bf16 pipeline unrolls its tile loop over four ring stages");
-    barrier_tile(0);
+    barrier_tile(0, Lay::kAhead % kNS);
     masks_from_lds();
     qk(0, Se, kbase(0));
     mask_block(0, Se);
@@ -854,11 +858,13 @@ void attn_main(AttnArgs a) {
     end_region(Pe);
     mask_block(1, So);
     rescale();
+    if (kSplitIssue && Lay::kAhead < n_tiles)
+      issue_tile(Lay::kAhead, Lay::kAhead % kNS, 2);  // V rows of tile 2
     // Tile t (stage t % 4) reads K of tile t and V of tile t - 1.  The stage is a template
     // constant of each unrolled copy, so every fragment address is fixed per lane.
     auto tile_step = [&](int t, auto stage) __attribute__((always_inline)) {
       constexpr int SK = decltype(stage)::value, SV = (SK + kNS - 1) % kNS;
-      barrier_tile(t);
+      barrier_tile(t, (SK + Lay::kAhead) % kNS);
       // R(2t-1): S of block 2t, O of block 2t-2, softmax of block 2t-1
       qk(2 * t, Se, kbase(SK));
       pv(2 * t - 2, Pe, vbase_rel(SV));
@@ -866,6 +872,8 @@ void attn_main(AttnArgs a) {
       end_region(Po);
       mask_block(2 * t, Se);
       rescale();
+      if (kSplitIssue && t + Lay::kAhead < n_tiles)
+        issue_tile(t + Lay::kAhead, (SK + Lay::kAhead) % kNS, 2);  // V rows of tile t + 2
       // R(2t): S of block 2t+1, O of block 2t-1, softmax of block 2t
       qk(2 * t + 1, So, kbase(SK));
       pv(2 * t - 1, Po, vbase_rel(SV));
@@ -896,7 +904,7 @@ void attn_main(AttnArgs a) {
     pv(2 * n_tiles - 1, Po, vlast);
   } else {
     for (int t = 0; t < n_tiles; ++t) {
-      barrier_tile(t);
+      barrier_tile(t, (t + Lay::kAhead) % kNS);
       if (t == 0) masks_from_lds();
       const uint32_t kb0 = kbase(t % kNS), vb0 = vbase(t % kNS);
 #pragma unroll
