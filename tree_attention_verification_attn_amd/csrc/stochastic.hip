@@ -23,7 +23,8 @@
 // per-slice sums are exchanged.  With G > 1 the partial sums of a sweep meet in a workspace: each
 // workgroup stores its value with a device-coherent atomic, in a form that is never zero, and
 // waits (bounded) until every value of that sweep is there; all workgroups then add the G values
-// in the same order, so they take the same decisions.  The last workgroup to leave clears the slots the
+// in the same order, so they take the same decisions.  Each workgroup counts itself out after its
+// last exchange, and the last one to do so clears the slots the
 // call used, so the workspace is all zeros between calls.  The host keeps B * G within the
 // compute units, so all workgroups of a sequence are resident together.
 #include <hip/hip_ext.h>
@@ -277,6 +278,7 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
   }
 
   int u = 0, n = 1, buf = 0, bad = 0, rounds = 0;
+  uint32_t exit_prev = 0;  // the sequence's exit count before this workgroup's (thread 0)
   int bonus = -1;
   bool writer = false;  // this workgroup writes bonus_tok[b]
   if (tid == 0) {
@@ -318,13 +320,14 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
         excl = __ballot(same) != 0;
       }
       const double Ux = fmax(fma(-C, qxd, pxd), 0.0);  // U_j(x) = p_j(x) * S_j
-      const double qj = (excl || !(N > 0.0)) ? 0.0 : qxd / N;
+      // (x / 1 is x exactly: independent siblings skip the divisions)
+      const double qj = (excl || !(N > 0.0)) ? 0.0 : (N == 1.0 ? qxd : qxd / N);
       if (uac * qj * S < Ux) {
         next = c;
         break;
       }
       // rejected: the residual for the next sibling
-      const double Cn = C + (N > 0.0 ? S / N : 0.0);
+      const double Cn = C + (N > 0.0 ? (N == 1.0 ? S : S / N) : 0.0);
       int unused = -1;
       const double part =
           wave_sum_f64(sweep<kVec, false>(pu, qu, Cn, V, k_lo, k_hi, wave, lane, nullptr, unused));
@@ -383,6 +386,11 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
     int owner = 0, gnz = last_nz;
     if (G > 1) {
       exchange(a, b, g, rounds, total, last_nz, tid, s_xval, s_xnz, &s_timeout);
+      // every walk ends with this exchange, its last use of the slots: count this workgroup
+      // out now, so the atomic's round trip overlaps the rest of the draw
+      if (tid == 0)
+        exit_prev = __hip_atomic_fetch_add(a.exitc + b, 1u, __ATOMIC_ACQ_REL,
+                                           __HIP_MEMORY_SCOPE_AGENT);
       total = 0.0;
       for (int h = 0; h < G; ++h) total += s_xval[h];
       const double thr_all = a.u_res[(size_t)b * T + u] * total;
@@ -466,12 +474,8 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
   if (g == 0)
     for (int t = tid; t < T; t += kSThreads) a.path[(size_t)b * T + t] = t < n ? s_path[t] : -1;
   if (G > 1) {
-    // the last workgroup of the sequence to get here clears the slots this call used
-    if (tid == 0) {
-      const uint32_t prev =
-          __hip_atomic_fetch_add(a.exitc + b, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = prev == (uint32_t)(G - 1);
-    }
+    // the last workgroup of the sequence to count out clears the slots this call used
+    if (tid == 0) s_last = exit_prev == (uint32_t)(G - 1);
     __syncthreads();
     if (s_last) {
       XSlot* rows = a.xch + (size_t)b * T * G;
