@@ -249,20 +249,23 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
   const int per_wg = ceil_div(nchunks, G);
   const int k_lo = min(nchunks, g * per_wg), k_hi = min(nchunks, k_lo + per_wg);
 
-  // the lane's two nodes: parent, token, acceptance uniform
+  // the lane's two nodes: parent, token, acceptance and residual uniforms (the residual one is
+  // read only by the bonus draw, but fetched here so its load is long done by then)
   int par[2], tok[2];
-  double ua[2];
+  double ua[2], ur[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int c = lane + 64 * k;
     par[k] = -2;
     tok[k] = -1;
     ua[k] = 0.0;
+    ur[k] = 0.0;
     if (c < T) {
       const uint64_t* row = a.anc + ((size_t)b * T + c) * a.W;
       par[k] = parent_from_row(c, row[0], a.W > 1 ? row[1] : 0ull);
       tok[k] = a.draft[(size_t)b * T + c];
       ua[k] = a.u_acc[(size_t)b * T + c];
+      ur[k] = a.u_res[(size_t)b * T + c];
     }
   }
 
@@ -363,6 +366,7 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
     }
 
     // ---- bonus draw at u from U = max(0, p - C q) ----
+    const double u_draw = readlane_f64(u < 64 ? ur[0] : ur[1], u & 63);
     // chunk sums of this workgroup's slice into LDS, and its last token with mass
     int last_nz = -1;
     sweep<kVec, true>(pu, qu, C, V, k_lo, k_hi, wave, lane, s_chunk, last_nz);
@@ -393,7 +397,7 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
                                            __HIP_MEMORY_SCOPE_AGENT);
       total = 0.0;
       for (int h = 0; h < G; ++h) total += s_xval[h];
-      const double thr_all = a.u_res[(size_t)b * T + u] * total;
+      const double thr_all = u_draw * total;
       double pre = 0.0;
       owner = -1;
       gnz = -1;
@@ -407,7 +411,7 @@ __global__ __launch_bounds__(kSThreads) void accept_stochastic_kernel(StochArgs 
       }
     }
     ++rounds;
-    const double thr = a.u_res[(size_t)b * T + u] * total;
+    const double thr = u_draw * total;
     if (owner < 0) {  // no running sum exceeds the threshold (u >= 1, rounding)
       writer = g == 0;
       bonus = gnz;
