@@ -213,19 +213,22 @@ __device__ inline int xcd_remap(int bid, int n) {
 constexpr int kLptMaxPairs = 256;
 
 __device__ inline void lpt_item(const AttnArgs& a, int* lds, int& b, int& s, int& kvh,
-                                int& rb) {
+                                int& rb, int& L_raw) {
   const int P = a.B * a.S;
   const int P4 = (P + 3) & ~3;
   const int tid = threadIdx.x;
   const int tree_tiles = ceil_div(a.T, kKT);
   int* sz = lds;        // [P4] tiles of each pair; padding -1 ranks after every pair
   int* ord = lds + P4;  // [P] pair of each rank
+  int* len = ord + P;   // [P] cache_len of each pair's sequence, as given
   for (int i = tid; i < P4; i += kThreads) {
     int v = -1;
     if (i < P) {
       const int bi = i / a.S, si = i - bi * a.S;
-      const int L = min(max(a.cache_len[bi], 0), a.Lmax);
+      const int Lr = a.cache_len[bi];
+      const int L = min(max(Lr, 0), a.Lmax);
       v = min(max(tree_tiles + ceil_div(L, kKT) - si * a.chunk_tiles, 0), a.chunk_tiles);
+      len[i] = Lr;
     }
     sz[i] = v;
   }
@@ -253,6 +256,7 @@ __device__ inline void lpt_item(const AttnArgs& a, int* lds, int& b, int& s, int
   const int pair = ord[U / a.Hkv];
   b = pair / a.S;
   s = pair - b * a.S;
+  L_raw = len[pair];  // (no second global read of cache_len[b])
   __syncthreads();  // this LDS is the K/V ring, which the first tile loads overwrite
 }
 
@@ -268,15 +272,18 @@ struct PBlock<false> {
   float v[16];  // element e of the S^T accumulator
 };
 
-// Ancestor masks of sequence b built by wavefront 0 from the parent array (pointer jumping over
-// wavefront shuffles): node c = lane + 64*k lives in lane c % 64, slot k.  Each node keeps the
-// set of its ancestors closer than 2^r and a pointer to the ancestor at distance 2^r; one round
-// merges the pointed-to node's set and doubles the pointer, every lane reading the others' old
-// values.  A tree that is not level-ordered with one root gets only each node's own bit (as
+// Ancestor masks of sequence b built by wavefront 0 from the parent array, by pointer jumping
+// through LDS: node c = lane + 64*k lives in lane c % 64, slot k.  Each node keeps the set of
+// its ancestors closer than 2^r and a pointer to the ancestor at distance 2^r; one round reads
+// the pointed-to node's set and pointer, then merges the set and takes over the pointer.  A
+// round's reads all come before its writes (the wavefront's LDS instructions execute in order;
+// compiler barriers keep them in place), and its writes have completed (lgkmcnt) before the next
+// round reads.  Rounds stop once no pointer is left (after ceil(log2(depth + 1)) rounds).  A
+// tree that is not level-ordered with one root gets only each node's own bit (as
 // tree_build_mask).  par[k] is parent[b, lane + 64*k].  Writes the masks to s_anc (and to
-// anc_out when not null); returns whether the tree was bad.
+// anc_out when not null); s_ptr is LDS for T pointers.  Returns whether the tree was bad.
 __device__ inline bool build_masks_wave(const int (&par)[2], int b, int T,
-                                        uint64_t (*s_anc)[2], uint64_t* anc_out) {
+                                        uint64_t (*s_anc)[2], int* s_ptr, uint64_t* anc_out) {
   const int lane = threadIdx.x & 63;
   const int W = T > 64 ? 2 : 1;
   uint64_t lo[2], hi[2];
@@ -294,41 +301,40 @@ __device__ inline bool build_masks_wave(const int (&par)[2], int b, int T,
       ptr[k] = (c > 0 && ok) ? p : -1;
       lo[k] = k == 0 ? bit64(c) : 0;
       hi[k] = k == 1 ? bit64(c) : 0;
+      s_anc[c][0] = lo[k];
+      s_anc[c][1] = hi[k];
+      s_ptr[c] = ptr[k];
     }
   }
   bad = __ballot(bad) != 0;
-  for (int span = 1; span < T; span <<= 1) {
-    uint64_t nlo[2], nhi[2];
-    int nptr[2];
+  // a pointer only ever moves to a smaller node, so every path ends within T - 1 steps
+  for (int span = 1; span < T && __ballot(ptr[0] >= 0 || ptr[1] >= 0); span <<= 1) {
+    uint64_t plo[2], phi[2];
+    int pp[2];
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the previous round's writes are done
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      // every lane takes part in every shuffle; the result is kept only where ptr >= 0
-      const int src = max(ptr[k], 0);
-      const int sl = src & 63;
-      const bool s1 = src >= 64;
-      const uint64_t l0 = shfl64(lo[0], sl);
-      const int p0 = __shfl(ptr[0], sl, 64);
-      uint64_t plo = l0, phi = 0;
-      int pp = p0;
-      if (W == 2) {
-        const uint64_t l1 = shfl64(lo[1], sl), h0 = shfl64(hi[0], sl), h1 = shfl64(hi[1], sl);
-        const int p1 = __shfl(ptr[1], sl, 64);
-        plo = s1 ? l1 : l0;
-        phi = s1 ? h1 : h0;
-        pp = s1 ? p1 : p0;
-      }
-      const bool follow = ptr[k] >= 0;
-      nlo[k] = follow ? (lo[k] | plo) : lo[k];
-      nhi[k] = follow ? (hi[k] | phi) : hi[k];
-      nptr[k] = follow ? pp : ptr[k];
+      const int src = max(ptr[k], 0);  // lanes without a pointer read node 0 and drop it
+      plo[k] = s_anc[src][0];
+      phi[k] = s_anc[src][1];
+      pp[k] = s_ptr[src];
     }
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      lo[k] = nlo[k];
-      hi[k] = nhi[k];
-      ptr[k] = nptr[k];
+      const int c = lane + 64 * k;
+      if (ptr[k] >= 0) {  // (only nodes c < T have one)
+        lo[k] |= plo[k];
+        hi[k] |= phi[k];
+        ptr[k] = pp[k];
+        s_anc[c][0] = lo[k];
+        s_anc[c][1] = hi[k];
+        s_ptr[c] = ptr[k];
+      }
     }
   }
+  asm volatile("" ::: "memory");
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int c = lane + 64 * k;
@@ -336,9 +342,9 @@ __device__ inline bool build_masks_wave(const int (&par)[2], int b, int T,
       if (bad) {
         lo[k] = k == 0 ? bit64(c) : 0;
         hi[k] = k == 1 ? bit64(c) : 0;
+        s_anc[c][0] = lo[k];
+        s_anc[c][1] = hi[k];
       }
-      s_anc[c][0] = lo[k];
-      s_anc[c][1] = hi[k];
       if (anc_out) {
         uint64_t* row = anc_out + ((size_t)b * T + c) * W;
         row[0] = lo[k];
@@ -364,9 +370,9 @@ void attn_main(AttnArgs a) {
   constexpr int kDPW = Lay::kDmaPerWave;
   __shared__ __attribute__((aligned(1024))) char smem[kNS * Lay::kStage];
 
-  int rb, s, kvh, b;
+  int rb, s, kvh, b, L_lpt = 0;
   if (a.lpt) {
-    lpt_item(a, reinterpret_cast<int*>(smem), b, s, kvh, rb);
+    lpt_item(a, reinterpret_cast<int*>(smem), b, s, kvh, rb, L_lpt);
   } else {
     const int n_items = a.B * a.Hkv * a.S * a.RB;
     const int item = xcd_remap(blockIdx.x, n_items);
@@ -380,7 +386,7 @@ void attn_main(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;
 
-  const int L_raw = a.cache_len[b];
+  const int L_raw = a.lpt ? L_lpt : a.cache_len[b];
   const int L = min(max(L_raw, 0), a.Lmax);
   // one workgroup per sequence reports its status (and, building masks, writes them)
   const bool writer = kvh == 0 && s == 0 && rb == 0;
@@ -564,7 +570,8 @@ void attn_main(AttnArgs a) {
   // Masks built here: wavefront 0 of every workgroup that reads tree keys, and of the
   // sequence's writer, runs the pointer jumping once its tile loads have landed; the other
   // wavefronts read their rows' masks after the first tile barrier.
-  __shared__ uint64_t s_anc[kMasks ? kMaxT : 1][2];
+  __shared__ __attribute__((aligned(16))) uint64_t s_anc[kMasks ? kMaxT : 1][2];
+  __shared__ int s_ptr[kMasks ? kMaxT : 1];
   const bool need_masks = kMasks && (n_tree_tiles > 0 || writer);
   int par[2] = {-1, -1};
   if (need_masks && wave == 0) {
@@ -598,7 +605,7 @@ void attn_main(AttnArgs a) {
   vm_wait<0>();
   if constexpr (kMasks) {
     if (need_masks && wave == 0) {
-      const bool bad = build_masks_wave(par, b, a.T, s_anc,
+      const bool bad = build_masks_wave(par, b, a.T, s_anc, s_ptr,
                                         writer ? const_cast<uint64_t*>(a.anc) : nullptr);
       if (writer && lane == 0 && a.status)
         a.status[b] = (bad ? TV_BAD_TREE : 0) | ((L_raw < 0 || L_raw > a.Lmax) ? TV_BAD_LEN : 0);
