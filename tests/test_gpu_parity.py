@@ -100,6 +100,9 @@ EDGE = [
                                  parent_kind="random")),
     ("T65_partial_second_tile", dict(B=2, T=65, L=(1, 130), Hq=4, Hkv=1, D=128, dtype="bf16",
                                      parent_kind="deep")),
+    # depth 127: every pointer-jumping round of a mask build, pointers crossing mask words
+    ("T128_chain", dict(B=2, T=128, L=(3, 200), Hq=4, Hkv=2, D=128, dtype="bf16",
+                        parent_kind="chain")),
     ("row_blocks_4", dict(B=2, T=100, L=(63, 65), Hq=16, Hkv=2, D=128, dtype="bf16",
                           parent_kind="random")),
     ("d64_bf16", dict(B=3, T=20, L=(1, 300), Hq=12, Hkv=3, D=64, dtype="bf16",
