@@ -307,7 +307,7 @@ __device__ inline bool build_masks_wave(const int (&par)[2], int b, int T,
     }
   }
   bad = __ballot(bad) != 0;
-  // a pointer only ever moves to a smaller node, so every path ends within T - 1 steps
+  // a pointer's distance doubles every round, so ceil(log2 T) rounds reach past every root
   for (int span = 1; span < T && __ballot(ptr[0] >= 0 || ptr[1] >= 0); span <<= 1) {
     uint64_t plo[2], phi[2];
     int pp[2];
