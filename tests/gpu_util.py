@@ -81,18 +81,23 @@ def run_step_fused(g: dict, split_keys: int = 0, in_place_len: bool = False, tv=
 
 
 def sample_rows(w, n_random: int, seed: int = 0) -> np.ndarray:
-    """(b, h, i) rows: corners of every axis, one row of every (sequence, KV head) unit (a random
-    query head of its group and a random node), so every work item the kernel's longest-first
-    and XCD-aware dispatch reorders is checked, plus uniform random ones."""
+    """(b, h, i) rows: corners of every axis; one row of every 32-row group of every (sequence,
+    KV head) unit, where a unit's rows are node * G + g over its G query heads (one wavefront of
+    the main kernel owns such a group, eight of them a workgroup), so every wavefront of every
+    work item that the kernel's longest-first and XCD-aware dispatch reorders is checked; plus
+    uniform random ones."""
     rng = np.random.default_rng(seed)
     rows = set()
     for b in {0, w.B - 1}:
         for h in {0, w.Hq - 1, w.G - 1, w.G % w.Hq}:
             for i in {0, w.T - 1, w.T // 2}:
                 rows.add((b, h, i))
+    GT = w.G * w.T
     for b in range(w.B):
         for kvh in range(w.Hkv):
-            rows.add((b, kvh * w.G + int(rng.integers(w.G)), int(rng.integers(w.T))))
+            for r0 in range(0, GT, 32):
+                r = int(rng.integers(r0, min(r0 + 32, GT)))
+                rows.add((b, kvh * w.G + r % w.G, r // w.G))
     target = len(rows) + n_random
     while len(rows) < target:
         rows.add((int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.T))))
