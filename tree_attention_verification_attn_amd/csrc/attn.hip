@@ -233,17 +233,28 @@ __device__ inline void lpt_item(const AttnArgs& a, int* lds, int& b, int& s, int
     sz[i] = v;
   }
   __syncthreads();
-  for (int i = tid; i < P; i += kThreads) {
-    const int me = sz[i];
+  // The rank of pair i counts the pairs ahead of it.  tpp consecutive lanes (a power of two, at
+  // most a wavefront) share a pair: each counts every tpp-th int4 of sz, and the counts meet by
+  // butterfly shuffles, so all wavefronts rank and each lane waits on few LDS reads.
+  {
+    const int lg = P > 1 ? 32 - __clz(P - 1) : 0;  // ceil(log2 P); P <= kLptMaxPairs
+    const int lt = min(6, __builtin_ctz(kThreads) - lg);
+    const int tpp = 1 << lt;
+    const int i = tid >> lt, j = tid & (tpp - 1);
     const int4* s4 = reinterpret_cast<const int4*>(sz);
     int r = 0;
-    for (int q = 0; q < P4 >> 2; ++q) {
-      const int4 o = s4[q];
-      const int j = 4 * q;
-      r += (o.x > me || (o.x == me && j < i)) + (o.y > me || (o.y == me && j + 1 < i)) +
-           (o.z > me || (o.z == me && j + 2 < i)) + (o.w > me || (o.w == me && j + 3 < i));
+    if (i < P) {
+      const int me = sz[i];
+#pragma unroll 4
+      for (int q = j; q < P4 >> 2; q += tpp) {
+        const int4 o = s4[q];
+        const int c = 4 * q;
+        r += (o.x > me || (o.x == me && c < i)) + (o.y > me || (o.y == me && c + 1 < i)) +
+             (o.z > me || (o.z == me && c + 2 < i)) + (o.w > me || (o.w == me && c + 3 < i));
+      }
     }
-    ord[r] = i;
+    for (int off = tpp >> 1; off > 0; off >>= 1) r += __shfl_xor(r, off, 64);
+    if (i < P && j == 0) ord[r] = i;
   }
   __syncthreads();
   const int n_units = P * a.Hkv;
