@@ -41,6 +41,23 @@ def _draw(i: int, paged: bool = False) -> dict:
 N_CONTIG, N_PAGED = 96, 32
 
 
+def _draw_groups(i: int) -> tuple[dict, int]:
+    """Large query-head groups (multi-query shapes among them): G * T spans one to 16 row
+    blocks of 256 rows, with a ragged last block."""
+    r = np.random.default_rng(np.random.SeedSequence([2024, 2, i]))
+    G = int(r.choice([6, 7, 12, 16, 24, 32, 48, 64]))
+    T = int(r.integers(1, min(128, 4096 // G) + 1))
+    lo, hi = sorted(int(x) for x in r.choice(L_CHOICES, 2))
+    Hkv = int(r.choice([1, 1, 2]))
+    return dict(B=int(r.integers(1, 4)), T=T, L=(lo, hi), Hkv=Hkv, Hq=Hkv * G,
+                D=int(r.choice([64, 128])), dtype="f32" if r.random() < 0.25 else "bf16",
+                parent_kind=str(r.choice(["random", "deep", "chain", "star"]))), \
+        int(r.choice(SPLITS))
+
+
+N_GROUPS = 16
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     if not torch.cuda.is_available():
@@ -63,6 +80,21 @@ def test_sweep_contiguous(i):
         x, y = np.ascontiguousarray(a[k]), np.ascontiguousarray(b[k])
         assert x.shape == y.shape and np.array_equal(x.view(np.uint8), y.view(np.uint8)), \
             f"sweep {i}: fused {k}"
+
+
+@pytest.mark.parametrize("i", range(N_GROUPS))
+def test_sweep_large_groups(i):
+    kw, split_keys = _draw_groups(i)
+    w = make_workload("batch32_L512-4096_T60", extra_seed=900 + i, **kw)
+    print(f"[case] sweep groups {i}: {kw} split_keys={split_keys}", flush=True)
+    a = run_step(upload(w), split_keys=split_keys)
+    stats = check_step(w, a, label=f"sweep groups {i}", rtol=RTOL_SHARP[w.dtype])
+    print(f"       max-abs err {stats['err']:.3e}  lse err {stats['lse_err']:.3e}", flush=True)
+    b = run_step_fused(upload(w), split_keys=split_keys)
+    for k in a:
+        x, y = np.ascontiguousarray(a[k]), np.ascontiguousarray(b[k])
+        assert x.shape == y.shape and np.array_equal(x.view(np.uint8), y.view(np.uint8)), \
+            f"sweep groups {i}: fused {k}"
 
 
 @pytest.mark.parametrize("i", range(N_PAGED))
