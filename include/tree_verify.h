@@ -114,6 +114,10 @@ size_t tree_verify_attn_workspace_size(int B, int T, int Hq, int Hkv, int D, int
  * Row offsets are 32-bit within one (b, kvh) cache slab and within one sequence's tree rows:
  * Lmax * D * elem and T * Hkv * D * elem may not exceed 4 GiB (TV_ERR_INVALID_ARG otherwise;
  * also for tree_verify_step).
+ * q, k_cache, v_cache, k_tree and v_tree are read 16 bytes at a time, and out is written in
+ * pieces of up to 16 bytes: each must be 16-byte aligned, as any device allocation is
+ * (TV_ERR_INVALID_ARG otherwise; also for tree_verify_step and, with the pools in place of the
+ * caches, the paged entry points).
  */
 int tree_verify_attn(const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* cache_len, const void* k_tree, const void* v_tree,

@@ -112,6 +112,9 @@ def test_attention_argument_errors(lib):
     assert _attn(lib, Lmax=(1 << 24) + 1, D=128, dt=1, ws=FAKE, wsb=big) == -1
     assert _attn(lib, Lmax=(1 << 23) + 1, D=128, dt=0, ws=FAKE, wsb=big) == -1
     assert _attn(lib, T=128, Hq=131073, Hkv=131073, D=128, dt=1, ws=FAKE, wsb=big) == -1
+    # rows are read and written 16 bytes at a time
+    for name in ("q", "kc", "vc", "kt", "vt", "out"):
+        assert _attn(lib, **{name: ctypes.c_void_p(0x1008)}) == -1, name
 
 
 def test_workspace_size_rules(lib):
@@ -145,6 +148,9 @@ def test_step_argument_errors(lib):
     bad = list(base)
     bad[21] = 96    # head_dim
     assert lib.tree_verify_step(*bad) == -2
+    bad = list(base)
+    bad[3] = ctypes.c_void_p(0x1008)  # q not 16-byte aligned
+    assert lib.tree_verify_step(*bad) == -1
     # a (b, kvh) cache slab past 4 GiB (32-bit row offsets)
     bad = list(base)
     bad[21], bad[22], bad[23] = 128, (1 << 24) + 1, 1

@@ -1465,6 +1465,8 @@ extern "C" size_t tree_verify_attn_workspace_size(int B, int T, int Hq, int Hkv,
   return make_plan(B, T, Hq, Hkv, D, Lmax, split_keys).ws_bytes;
 }
 
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 // Checks the attention arguments and fills `a`; returns TV_OK or the error to report.
 static int prepare_attn(AttnArgs& a, Plan& p, const void* q, const void* k_cache,
                         const void* v_cache, const int32_t* cache_len, const void* k_tree,
@@ -1474,6 +1476,10 @@ static int prepare_attn(AttnArgs& a, Plan& p, const void* q, const void* k_cache
                         size_t workspace_bytes) {
   if (!q || !k_cache || !v_cache || !cache_len || !k_tree || !v_tree || !anc_mask || !out ||
       !attn_shapes_ok(B, T, Hq, Hkv, Lmax) || split_keys < 0)
+    return TV_ERR_INVALID_ARG;
+  // q, K and V rows are read 16 bytes at a time (fp32 output rows are written so too)
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_tree) ||
+      !aligned16(v_tree) || !aligned16(out))
     return TV_ERR_INVALID_ARG;
   if ((dtype != TV_F32 && dtype != TV_BF16) || (D != 64 && D != 128)) return TV_ERR_UNSUPPORTED;
   p = make_plan(B, T, Hq, Hkv, D, Lmax, split_keys);
