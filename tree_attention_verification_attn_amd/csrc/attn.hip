@@ -990,19 +990,20 @@ void attn_main(AttnArgs a) {
 
 // Merge the per-chunk partials of sequences with more than one non-empty chunk:
 //   M = max_s m_s,  O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s,  lse = (M + log2 den) ln 2.
-// A thread owns 16 bytes of a slot's partial, in the partials' register order: one group (one
-// row, four consecutive d, fp32).  Chunks are taken kBatch at a time, exactly as many as the sequence has, with
-// all their loads in flight, and M is raised per batch (online, as in the main kernel).  With
-// few chunks (S <= 8) every thread of a workgroup owns different bytes and merges all chunks.
-// With more, the four wavefronts of a workgroup own the same 64 pieces and take every fourth
-// chunk each, then combine their (M, den, O) through LDS: four times the workgroups and a
-// quarter of the round trips, for the long splits of short batches.  Workgroups are dealt to
-// XCDs in the same (b, kvh) order as attn_main's, so a merge reads partials from the L2 they
-// were written to.
-template <typename E>
-constexpr int combine_rows_per_thread() {
-  return 1;  // the partials are fp32 for every input type
-}
+// The unit of work is a piece: 16 bytes of a slot's partial in the partials' register order,
+// that is one row and four consecutive d in fp32.  Chunks are taken kBatch at a time, exactly as
+// many as the sequence has, with all their loads in flight, and M is raised per batch (online,
+// as in the main kernel).
+//  * Few chunks (S <= 8): every thread owns kP pieces of one (b, kvh, rb) and merges all its
+//    chunks in one batch, the loads of all kP pieces in flight together (kP * kBatch = 8
+//    loads of 16 bytes).  Sequences that were not split leave their workgroups with nothing
+//    to do but one read of the chunk count, so fewer, fuller workgroups keep the merge from
+//    being bound by dispatch and that read's latency (batch 32: 2048 workgroups, not 8192).
+//  * More chunks: the four wavefronts of a workgroup own the same 64 pieces and take every
+//    fourth chunk each, then combine their (M, den, O) through LDS: four times the workgroups
+//    and a quarter of the round trips, for the long splits of short batches.
+// Workgroups are dealt to XCDs in the same (b, kvh) order as attn_main's, so a merge reads
+// partials from the L2 they were written to.
 
 // the merge's compile-time shape for a plan with S chunks per (b, kvh, rb)
 struct CombineShape {
@@ -1016,15 +1017,22 @@ inline CombineShape combine_shape(int S) {
   return {8, 4};
 }
 
-template <typename E, int D, int kSW>
+// pieces per thread: eight 16-byte partial loads in flight per thread
+constexpr int combine_pieces(int batch, int sw) { return sw == 1 ? 8 / batch : 1; }
+
+template <int D, int kBatch, int kSW>
 constexpr int combine_wgs_per_item() {  // workgroups per (b, kvh, rb)
-  return kRows * D / 4 / combine_rows_per_thread<E>() * kSW / 256;
+  return kRows * D / 4 * kSW / combine_pieces(kBatch, kSW) / 256;
 }
 
-template <typename E, int D>
+template <int D>
 int combine_grid(int items, int S) {
-  return items * (combine_shape(S).sw == 1 ? combine_wgs_per_item<E, D, 1>()
-                                           : combine_wgs_per_item<E, D, 4>());
+  const CombineShape c = combine_shape(S);
+  const int per = c.sw == 4 ? combine_wgs_per_item<D, 8, 4>()
+                  : c.batch == 2 ? combine_wgs_per_item<D, 2, 1>()
+                  : c.batch == 4 ? combine_wgs_per_item<D, 4, 1>()
+                                 : combine_wgs_per_item<D, 8, 1>();
+  return items * per;
 }
 
 // Logical merge workgroup c (of B * Hkv * RB * combine_wgs_per_item), 256 threads.  The chunk
@@ -1034,159 +1042,238 @@ template <typename E, int D, int kBatch, int kSW>
 __device__ void combine_group(const AttnArgs& a, int c) {
   constexpr bool kBF16 = std::is_same<E, __bf16>::value;
   constexpr int kDB = D / 32;
-  constexpr int kR = combine_rows_per_thread<E>();
-  constexpr int kWGs = combine_wgs_per_item<E, D, kSW>();
-  constexpr int kPer = 256 / kSW;              // pieces per workgroup
-  constexpr int kStride = kRows * D / 4 / kR;  // 16-byte units per slot
-  using ML = typename std::conditional<kR == 2, float4, float2>::type;
-  const int item = c / kWGs;  // (b, kvh, rb)
+  constexpr int kP = combine_pieces(kBatch, kSW);
+  constexpr int kWGs = combine_wgs_per_item<D, kBatch, kSW>();
+  constexpr int kPer = 256 / kSW;          // pieces per workgroup and per-thread piece index
+  constexpr int kStride = kRows * D / 4;   // pieces per slot
+  static_assert(kSW == 1 || kP == 1, "shared pieces are merged one per thread");
   const int tid = threadIdx.x;
   const int pl = tid % kPer, sg = tid / kPer;  // piece within the workgroup, chunk group
-  const int g = ((c % kWGs) * kPer + pl) * kR;  // first register-order group of the piece
+  int b, item;
+  if constexpr (kSW == 1) {
+    // Logical workgroups go to split sequences only, in sequence order: logical workgroup c
+    // serves the (c / per_seq)-th sequence with more than one chunk, so all the merge's work
+    // sits in the first workgroups (the hardware deals them to the XCDs in turn) and the rest,
+    // up to the grid's bound for a plan that splits every sequence, leave at once.  Wavefront
+    // 0 ranks the sequences by ballots over their chunk counts.
+    __shared__ int s_b;
+    const int per_seq = a.Hkv * a.RB * kWGs;
+    const int rank = c / per_seq;
+    if (tid < 64) {
+      int found = -1, before = 0;
+      for (int base = 0; base < a.B && found < 0; base += 256) {
+        bool sp[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int bi = base + 64 * k + tid;
+          sp[k] = bi < a.B && a.nsplit[bi] > 1;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint64_t m = __ballot(sp[k]);
+          const int cnt = __popcll(m);
+          if (found < 0 && rank < before + cnt) {
+            uint64_t mm = m;  // the (rank - before)-th set lane
+            for (int i = rank - before; i > 0; --i) mm &= mm - 1;
+            found = base + 64 * k + __builtin_ctzll(mm);
+          }
+          before += cnt;
+        }
+      }
+      if (tid == 0) s_b = found;
+    }
+    __syncthreads();
+    b = s_b;
+    if (b < 0) return;  // more logical workgroups than the split sequences need (uniform)
+    item = b * a.Hkv * a.RB + (c % per_seq) / kWGs;
+  } else {
+    item = c / kWGs;
+    b = item / (a.RB * a.Hkv);
+  }
   const int rb = item % a.RB;
   const int kvh = (item / a.RB) % a.Hkv;
-  const int b = item / (a.RB * a.Hkv);
   const int n_split = a.nsplit[b];
   if (n_split <= 1) return;  // written directly by attn_main (uniform: the whole workgroup)
-  // g = ((wave*kDB + db)*4 + j)*64 + lane  ->  row wave*32 + lane%32, d = db*32 + 8j + 4*(lane/32)
-  const int lane = g & 63, j = (g >> 6) & 3, db = (g >> 8) % kDB, wave = (g >> 8) / kDB;
-  const int rloc = wave * 32 + (lane & 31);  // rows rloc .. rloc + kR - 1 (lane is even for kR 2)
-  const int r0 = rb * kRows + rloc;
-  const bool live = r0 < a.GT;  // padding rows were never written
-  const int d = db * 32 + 8 * j + 4 * (lane >> 5);
   const size_t slot0 = (((size_t)b * a.Hkv + kvh) * a.RB + rb) * a.S;
-  const uint4* po = reinterpret_cast<const uint4*>(a.part_o) + slot0 * kStride + g / kR;
-  const ML* pml =
-      reinterpret_cast<const ML*>(reinterpret_cast<const float2*>(a.part_ml) + slot0 * kRows + rloc);
+  const float4* po = reinterpret_cast<const float4*>(a.part_o) + slot0 * kStride;
+  const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + slot0 * kRows;
 
-  float M[kR], den[kR];
-  float4 acc[kR];
+  // piece q of this thread: register-order group g = ((wave*kDB + db)*4 + j)*64 + lane, that is
+  // row wave*32 + lane%32 and d = db*32 + 8j + 4*(lane/32); consecutive threads own consecutive
+  // groups, so each of the thread's loads is part of one 4 KB run per workgroup
+  int g[kP], rloc[kP], dq[kP];
+  bool live[kP];
 #pragma unroll
-  for (int i = 0; i < kR; ++i) {
-    M[i] = -INFINITY;
-    den[i] = 0.f;
-    acc[i] = float4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < kP; ++q) {
+    g[q] = ((c % kWGs) * kP + q) * kPer + pl;
+    const int lane = g[q] & 63, j = (g[q] >> 6) & 3, db = (g[q] >> 8) % kDB;
+    const int wave = (g[q] >> 8) / kDB;
+    rloc[q] = wave * 32 + (lane & 31);
+    live[q] = rb * kRows + rloc[q] < a.GT;  // padding rows were never written
+    dq[q] = db * 32 + 8 * j + 4 * (lane >> 5);
+  }
+
+  float M[kP], den[kP];
+  float4 acc[kP];
+#pragma unroll
+  for (int q = 0; q < kP; ++q) {
+    M[q] = -INFINITY;
+    den[q] = 0.f;
+    acc[q] = float4{0.f, 0.f, 0.f, 0.f};
   }
   // chunk group sg takes chunks sg, sg + kSW, sg + 2 kSW, ...
-  const int n_mine = live && sg < n_split ? (n_split - sg + kSW - 1) / kSW : 0;
+  const int n_mine = sg < n_split ? (n_split - sg + kSW - 1) / kSW : 0;
   for (int k0 = 0; k0 < n_mine; k0 += kBatch) {
-    const int nb = min(kBatch, n_mine - k0);  // uniform across the wavefront
-    uint4 v[kBatch];
-    ML ml[kBatch];
+    const int nb = min(kBatch, n_mine - k0);  // uniform across the workgroup
+    float4 v[kP][kBatch];
+    float2 ml[kP][kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u)
-      if (u < nb) {
-        const size_t sidx = (size_t)(k0 + u) * kSW + sg;
-        v[u] = po[sidx * kStride];
-        ml[u] = pml[sidx * (kRows / kR)];
-      }
+    for (int q = 0; q < kP; ++q)
 #pragma unroll
-    for (int i = 0; i < kR; ++i) {
-      // (m, l) of row i and its four values in chunk u
-      auto m_of = [&](int u) -> float {
-        if constexpr (kR == 2) return i == 0 ? ml[u].x : ml[u].z;
-        else return ml[u].x;
-      };
-      auto l_of = [&](int u) -> float {
-        if constexpr (kR == 2) return i == 0 ? ml[u].y : ml[u].w;
-        else return ml[u].y;
-      };
-      auto val_of = [&](int u) {
-        return float4{__uint_as_float(v[u].x), __uint_as_float(v[u].y),
-                      __uint_as_float(v[u].z), __uint_as_float(v[u].w)};
-      };
+      for (int u = 0; u < kBatch; ++u)
+        if (u < nb && live[q]) {
+          const size_t sidx = (size_t)(k0 + u) * kSW + sg;
+          v[q][u] = po[sidx * kStride + g[q]];
+          ml[q][u] = pml[sidx * kRows + rloc[q]];
+        } else {
+          v[q][u] = float4{0.f, 0.f, 0.f, 0.f};
+          ml[q][u] = float2{-INFINITY, 0.f};
+        }
+#pragma unroll
+    for (int q = 0; q < kP; ++q) {
       // A chunk in which a row sees no key (a second tree tile that holds none of the row's
       // ancestors, cut into a chunk of its own) carries m = -inf, l = 0, O = 0.  When every
       // chunk so far is such a chunk, Mb is -inf too; the exponents are then taken against 0,
       // so those chunks weigh 0 instead of 2^(-inf - -inf) = NaN.
-      float Mb = M[i];
+      float Mb = M[q];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
-        if (u < nb) Mb = fmaxf(Mb, m_of(u));
+        if (u < nb) Mb = fmaxf(Mb, ml[q][u].x);
       const float Me = Mb == -INFINITY ? 0.f : Mb;
-      const float sc = fast_exp2(M[i] - Me);  // 0 on the first batch
-      den[i] *= sc;
-      acc[i].x *= sc;
-      acc[i].y *= sc;
-      acc[i].z *= sc;
-      acc[i].w *= sc;
+      const float sc = fast_exp2(M[q] - Me);  // 0 on the first batch
+      den[q] *= sc;
+      acc[q].x *= sc;
+      acc[q].y *= sc;
+      acc[q].z *= sc;
+      acc[q].w *= sc;
 #pragma unroll
       for (int u = 0; u < kBatch; ++u)
         if (u < nb) {
-          const float w = fast_exp2(m_of(u) - Me);
-          const float4 x = val_of(u);
-          den[i] += w * l_of(u);
-          acc[i].x += w * x.x;
-          acc[i].y += w * x.y;
-          acc[i].z += w * x.z;
-          acc[i].w += w * x.w;
+          const float w = fast_exp2(ml[q][u].x - Me);
+          const float4 x = v[q][u];
+          den[q] += w * ml[q][u].y;
+          acc[q].x += w * x.x;
+          acc[q].y += w * x.y;
+          acc[q].z += w * x.z;
+          acc[q].w += w * x.w;
         }
-      M[i] = Mb;
+      M[q] = Mb;
     }
   }
   if constexpr (kSW > 1) {
     // the chunk groups' partial merges meet in LDS; group 0 combines them in group order
-    __shared__ float4 s_acc[kSW][kPer][kR];
-    __shared__ float2 s_mden[kSW][kPer][kR];
-#pragma unroll
-    for (int i = 0; i < kR; ++i) {
-      s_acc[sg][pl][i] = acc[i];
-      s_mden[sg][pl][i] = float2{M[i], den[i]};
-    }
+    __shared__ float4 s_acc[kSW][kPer];
+    __shared__ float2 s_mden[kSW][kPer];
+    s_acc[sg][pl] = acc[0];
+    s_mden[sg][pl] = float2{M[0], den[0]};
     __syncthreads();
     if (sg != 0) return;
+    float Mt = M[0];
 #pragma unroll
-    for (int i = 0; i < kR; ++i) {
-      float Mt = M[i];
+    for (int w = 1; w < kSW; ++w) Mt = fmaxf(Mt, s_mden[w][pl].x);
+    // group 0 always holds chunk 0, whose first tile holds the root (visible to every row),
+    // so Mt is finite for live rows; a group that saw no key has M = -inf, den = 0, O = 0
+    // and weight 0
+    const float sc = fast_exp2(M[0] - Mt);
+    den[0] *= sc;
+    acc[0].x *= sc;
+    acc[0].y *= sc;
+    acc[0].z *= sc;
+    acc[0].w *= sc;
 #pragma unroll
-      for (int q = 1; q < kSW; ++q) Mt = fmaxf(Mt, s_mden[q][pl][i].x);
-      // group 0 always holds chunk 0, whose first tile holds the root (visible to every row),
-      // so Mt is finite for live rows; a group that saw no key has M = -inf, den = 0, O = 0
-      // and weight 0
-      const float sc = fast_exp2(M[i] - Mt);
-      den[i] *= sc;
-      acc[i].x *= sc;
-      acc[i].y *= sc;
-      acc[i].z *= sc;
-      acc[i].w *= sc;
-#pragma unroll
-      for (int q = 1; q < kSW; ++q) {
-        const float2 md = s_mden[q][pl][i];
-        const float4 x = s_acc[q][pl][i];
-        const float w = fast_exp2(md.x - Mt);
-        den[i] += w * md.y;
-        acc[i].x += w * x.x;
-        acc[i].y += w * x.y;
-        acc[i].z += w * x.z;
-        acc[i].w += w * x.w;
-      }
-      M[i] = Mt;
+    for (int w = 1; w < kSW; ++w) {
+      const float2 md = s_mden[w][pl];
+      const float4 x = s_acc[w][pl];
+      const float wt = fast_exp2(md.x - Mt);
+      den[0] += wt * md.y;
+      acc[0].x += wt * x.x;
+      acc[0].y += wt * x.y;
+      acc[0].z += wt * x.z;
+      acc[0].w += wt * x.w;
     }
+    M[0] = Mt;
   }
-  if (!live) return;
-#pragma unroll
-  for (int i = 0; i < kR; ++i) {
-    const int r = r0 + i;
-    if (r >= a.GT) break;  // the second row of a pair may be padding (never written)
-    const float inv = 1.f / den[i];
+  // output row of a (live) row index of this item
+  auto out_row = [&](int r) -> size_t {
     const int t = r / a.G, head = kvh * a.G + r % a.G;
-    const size_t orow = ((size_t)b * a.T + t) * a.Hq + head;
+    return ((size_t)b * a.T + t) * a.Hq + head;
+  };
+  if constexpr (kSW == 1) {
+    // The workgroup's pieces cover a block of whole row segments: kRowsWG rows (32 consecutive
+    // per 8 D pieces) by kDSpan consecutive d.  Stored piece by piece, every store instruction
+    // would write 16 bytes into each of 32 rows; staged through LDS (rows padded by 16 bytes,
+    // so the 32 rows of a staging write fall in different banks), every row segment leaves in
+    // contiguous 16-byte stores.
+    constexpr int kWGPieces = 256 * kP;
+    constexpr int kGroupPieces = 8 * D;  // pieces of 32 whole rows
+    constexpr int kRowsWG = kWGPieces >= kGroupPieces ? 32 * (kWGPieces / kGroupPieces) : 32;
+    constexpr int kDSpan = kWGPieces >= kGroupPieces ? D : D * kWGPieces / kGroupPieces;
+    constexpr int kSegBytes = kDSpan * (int)sizeof(E);
+    constexpr int kLdsRow = kSegBytes + 16;
+    constexpr int kChunks = kRowsWG * kSegBytes / 16;  // 16-byte stores of the block
+    __shared__ __attribute__((aligned(16))) char s_out[kRowsWG * kLdsRow];
+    const int gb = (c % kWGs) * kWGPieces >> 8;  // (wave * kDB + db) of the block's first piece
+    const int row0 = (gb / kDB) * 32;              // first row of the block within the item
+    const int d0 = kDSpan == D ? 0 : (gb % kDB) * 32;
+#pragma unroll
+    for (int q = 0; q < kP; ++q) {
+      if (!live[q]) continue;
+      const float inv = 1.f / den[q];
+      char* dst = s_out + (rloc[q] - row0) * kLdsRow + (dq[q] - d0) * (int)sizeof(E);
+      if constexpr (kBF16) {
+        *reinterpret_cast<uint2*>(dst) = uint2{pack_bf16x2(acc[q].x * inv, acc[q].y * inv),
+                                               pack_bf16x2(acc[q].z * inv, acc[q].w * inv)};
+      } else {
+        *reinterpret_cast<float4*>(dst) =
+            float4{acc[q].x * inv, acc[q].y * inv, acc[q].z * inv, acc[q].w * inv};
+      }
+      if (a.lse && dq[q] == 0)
+        a.lse[out_row(rb * kRows + rloc[q])] = (M[q] + __log2f(den[q])) * kLn2;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = tid; k < kChunks; k += 256) {
+      const int rr = k / (kSegBytes / 16), off = (k % (kSegBytes / 16)) * 16;
+      const int r = rb * kRows + row0 + rr;
+      if (r >= a.GT) continue;  // padding rows are never written
+      char* o = a.out + (out_row(r) * D + d0) * sizeof(E) + off;
+      *reinterpret_cast<uint4*>(o) = *reinterpret_cast<const uint4*>(s_out + rr * kLdsRow + off);
+    }
+  } else {
+    if (!live[0]) return;
+    const int r = rb * kRows + rloc[0];
+    const float inv = 1.f / den[0];
+    const size_t orow = out_row(r);
     E* o = reinterpret_cast<E*>(a.out) + orow * D;
+    const int d = dq[0];
     if constexpr (kBF16) {
-      *reinterpret_cast<uint2*>(o + d) = uint2{pack_bf16x2(acc[i].x * inv, acc[i].y * inv),
-                                               pack_bf16x2(acc[i].z * inv, acc[i].w * inv)};
+      *reinterpret_cast<uint2*>(o + d) = uint2{pack_bf16x2(acc[0].x * inv, acc[0].y * inv),
+                                               pack_bf16x2(acc[0].z * inv, acc[0].w * inv)};
     } else {
       *reinterpret_cast<float4*>(o + d) =
-          float4{acc[i].x * inv, acc[i].y * inv, acc[i].z * inv, acc[i].w * inv};
+          float4{acc[0].x * inv, acc[0].y * inv, acc[0].z * inv, acc[0].w * inv};
     }
-    if (a.lse && d == 0) a.lse[orow] = (M[i] + __log2f(den[i])) * kLn2;
+    if (a.lse && d == 0) a.lse[orow] = (M[0] + __log2f(den[0])) * kLn2;
   }
 }
 
 template <typename E, int D, int kBatch, int kSW>
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+  // (few chunks: split sequences first, in hardware order; many: XCD-aligned with attn_main)
   combine_group<E, D, kBatch, kSW>(
-      a, xcd_remap(blockIdx.x, a.B * a.Hkv * a.RB * combine_wgs_per_item<E, D, kSW>()));
+      a, kSW == 1 ? (int)blockIdx.x
+                  : xcd_remap(blockIdx.x, a.B * a.Hkv * a.RB *
+                                              combine_wgs_per_item<D, kBatch, kSW>()));
 }
 
 // ---- fused tail of a verification step -----------------------------------------------------
@@ -1281,7 +1368,8 @@ __device__ inline void tail_scan_pages(const AttnArgs& a, const TailArgs& t, int
 template <typename E, int D, int kBatch, int kSW>
 __global__ __launch_bounds__(256) void step_tail(AttnArgs a, TailArgs t) {
   if ((int)blockIdx.x >= t.n_acc) {
-    combine_group<E, D, kBatch, kSW>(a, xcd_remap(blockIdx.x - t.n_acc, t.n_comb));
+    const int c = blockIdx.x - t.n_acc;
+    combine_group<E, D, kBatch, kSW>(a, kSW == 1 ? c : xcd_remap(c, t.n_comb));
     return;
   }
   if ((int)blockIdx.x >= a.B) {  // bad-page scans, then XCD alignment padding
@@ -1398,7 +1486,7 @@ int launch_attn(const AttnArgs& a, hipStream_t stream) {
   const int rc = launch_main<E, D, false, kPaged>(a, stream);
   if (rc != TV_OK) return rc;
   if (a.S > 1) {
-    const dim3 grid(combine_grid<E, D>(a.B * a.Hkv * a.RB, a.S)), block(256);
+    const dim3 grid(combine_grid<D>(a.B * a.Hkv * a.RB, a.S)), block(256);
     switch (combine_shape(a.S).batch * combine_shape(a.S).sw) {
       case 2: hipLaunchKernelGGL((attn_combine<E, D, 2, 1>), grid, block, 0, stream, a); break;
       case 4: hipLaunchKernelGGL((attn_combine<E, D, 4, 1>), grid, block, 0, stream, a); break;
@@ -1413,7 +1501,7 @@ template <typename E, int D, int kPaged = 0>
 int launch_step(const AttnArgs& a, TailArgs t, hipStream_t stream) {
   const int rc = launch_main<E, D, true, kPaged>(a, stream);
   if (rc != TV_OK) return rc;
-  t.n_comb = a.S > 1 ? combine_grid<E, D>(a.B * a.Hkv * a.RB, a.S) : 0;
+  t.n_comb = a.S > 1 ? combine_grid<D>(a.B * a.Hkv * a.RB, a.S) : 0;
   t.n_acc = (a.B + t.n_scan + 7) / 8 * 8;
   const dim3 grid(t.n_acc + t.n_comb), block(256);
   switch (combine_shape(a.S).batch * combine_shape(a.S).sw) {
