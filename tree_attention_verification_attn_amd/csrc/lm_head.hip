@@ -14,19 +14,28 @@
 //     e = 0 .. 7 inner), so every 16-byte load of the wavefront covers 1 KB contiguously; the
 //     64 chain sums are then combined by a butterfly, j with j^32, then j^16, ..., j^1, which
 //     leaves the same value in every lane (d/64 + 6 roundings per term);
-//   * screening (A u): one chain of fused multiply-adds over the rank index, in order, from 0
-//     (r roundings per term).
+//   * screening (A u), ranks up to 256: on v_mfma_f32_32x32x16_bf16 with u split exactly into
+//     three bfloat16 parts (u = hi + mid + lo), so every product with A is exact in float32 and
+//     a term passes through at most 16 + 3 ceil(r / 16) roundings (16 inside its MFMA, one per
+//     later MFMA of the chain); larger ranks: one chain of fused multiply-adds over the rank
+//     index, in order, from 0 (r roundings per term).
 // Ranking uses an unsigned key of the float (-0 as +0); equal values go to the smaller row
 // (screening) or the smaller token (children).
 //
 // Kernels:
 //   lm_project_kernel  one wavefront per (i, m), u[m, i] = B[i] . h[m]          (2 MB of B)
-//   lm_screen_kernel   one workgroup per tile of rows: the tile's A rows stream through LDS in
-//                      64-element slices (each row's 128 B XOR-swizzled by 16-byte piece so a
-//                      thread reading its row is free of bank conflicts), a thread runs half of
-//                      the M chains for two rows (one LDS read of u serves both), then each
-//                      wavefront picks its k best rows per hidden state by wavefront maxima and
-//                      the two wavefronts' picks of each hidden state are merged
+//   lm_screen_mfma_kernel  one workgroup per tile of rows (ranks up to 256): each wavefront
+//                      loads 64 rows of A straight into MFMA operands, u's three bfloat16 parts
+//                      sit in LDS one block of 32 hidden states at a time, each lane picks the
+//                      k best of the 32 rows its accumulators hold for one hidden state, and the
+//                      eight lists of a hidden state merge by rank
+//   lm_screen_kernel   (larger ranks) one workgroup per tile of rows: the tile's A rows stream
+//                      through LDS in 64-element slices (each row's 128 B XOR-swizzled by
+//                      16-byte piece so a thread reading its row is free of bank conflicts), a
+//                      thread runs half of the M chains for two rows (one LDS read of u serves
+//                      both), then each wavefront picks its k best rows per hidden state by
+//                      wavefront maxima and the two wavefronts' picks of each hidden state are
+//                      merged
 //   lm_rescore_kernel  one wavefront per (m, c): W[cand] . h[m]                  (8 KB per row)
 //   lm_topk_kernel     one workgroup per hidden state: each wavefront takes K rounds of
 //                      wavefront maxima over its share of the candidates, the 4K picks are
@@ -154,12 +163,82 @@ __global__ __launch_bounds__(256) void lm_project_kernel(const uint16_t* __restr
   if ((threadIdx.x & 63) == 0) u[(size_t)m * r + i] = v;
 }
 
-// Screening of tile blockIdx.x: rows r0 .. r0 + rows - 1 of A [n, r]; u [M, r] fp32 staged in
-// LDS (dynamic shared memory, kM * r floats, rows m >= M zero) and read with 16-byte reads
-// that every lane of a wavefront takes from the same address; k_tile candidates per hidden
-// state.  kM >= M (even) is the number of chains a row runs, half of them in each half of the
-// workgroup (a compile-time count so the accumulators stay in registers; the chains of m >= M
-// are discarded).
+// The tile's k_tile best rows per hidden state from its scores (thread (half, p) of the 256
+// holds rows p and p + 128 for hidden states half * kM/2 + i), written as candidates best first.
+// s_pick is LDS for M * 2 * k_tile 64-bit picks that no thread still reads.
+template <int kM>
+__device__ inline void screen_picks(const float (&acc)[2][kM / 2], uint64_t* s_pick,
+                                    const int32_t* __restrict__ row_token, int M, int n, int tile,
+                                    int k_tile, int32_t* __restrict__ cand,
+                                    float* __restrict__ cand_score) {
+  constexpr int kH = kM / 2;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = tid >> 7, p = tid & 127;
+  const int t = blockIdx.x;
+  const int r0 = t * tile;
+  const int rows = min(tile, n - r0);
+  // Each wavefront's k best rows per hidden state, then the merge of the two wavefronts of the
+  // half.  A wavefront holds rows q0 = 64 (wave & 1) + lane and q0 + 128, so among its rows
+  // with the best score the smallest row is the lowest lane holding it in its first row, else
+  // in its second: a 32-bit maximum and ballots replace a 64-bit (score, row) maximum.  The
+  // hidden states' reductions of one round are independent, so they interleave.
+  const int wh = wave & 1;
+  const bool real0 = p < rows, real1 = p + 128 < rows;
+  uint64_t taken0 = 0, taken1 = 0;  // bit i: the row was picked for hidden state half*kH + i
+  for (int j = 0; j < k_tile; ++j) {
+#pragma unroll
+    for (int i = 0; i < kH; ++i) {
+      const int m = half * kH + i;
+      if (m < M) {
+        const bool open0 = real0 && !((taken0 >> i) & 1);
+        const bool open1 = real1 && !((taken1 >> i) & 1);
+        const uint32_t k0 = open0 ? fkey(acc[0][i]) : 0u, k1 = open1 ? fkey(acc[1][i]) : 0u;
+        const uint32_t best = wave_max_u32(max(k0, k1));
+        const uint64_t h0 = __ballot(open0 && k0 == best);
+        const uint64_t h1 = __ballot(open1 && k1 == best);
+        uint64_t pick = 0;  // none left: fewer real rows than picks
+        if (h0 | h1) {
+          const int w = __builtin_ctzll(h0 ? h0 : h1);
+          const int q = (h0 ? 0 : 128) + wh * 64 + w;
+          if (lane == w) {
+            if (h0) taken0 |= 1ull << i;
+            else taken1 |= 1ull << i;
+          }
+          pick = ((uint64_t)best << 32) | (0xffffffffu - (uint32_t)(r0 + q));
+        }
+        if (lane == 0) s_pick[(m * 2 + wh) * k_tile + j] = pick;
+      }
+    }
+  }
+  __syncthreads();
+  const int C = ceil_div(n, tile) * k_tile;
+  const int per_m = 2 * k_tile;
+  for (int x = tid; x < M * per_m; x += 256) {
+    const int m = x / per_m, e = x - m * per_m;
+    const uint64_t* pm = s_pick + m * per_m;
+    const uint64_t me = pm[e];
+    int rank = 0;  // picks are distinct except padding (0), which ranks by entry
+    for (int o = 0; o < per_m; ++o) rank += pm[o] > me || (pm[o] == me && o < e);
+    if (rank >= k_tile) continue;
+    const size_t out = (size_t)m * C + (size_t)t * k_tile + rank;
+    if (me == 0) {  // the tile has fewer real rows than k_tile: padding picks rank last
+      cand[out] = -1;
+      cand_score[out] = -INFINITY;
+    } else {
+      const int row = (int)(0xffffffffu - (uint32_t)me);
+      cand[out] = row_token[row];
+      cand_score[out] = fkey_value((uint32_t)(me >> 32));
+    }
+  }
+}
+
+// Screening of tile blockIdx.x by float32 chains on the vector ALU (ranks beyond the MFMA
+// kernel's reach): rows r0 .. r0 + rows - 1 of A [n, r]; u [M, r] fp32 staged in LDS (dynamic
+// shared memory, kM * r floats, rows m >= M zero) and read with 16-byte reads that every lane
+// of a wavefront takes from the same address; k_tile candidates per hidden state.  kM >= M
+// (even) is the number of chains a row runs, half of them in each half of the workgroup (a
+// compile-time count so the accumulators stay in registers; the chains of m >= M are
+// discarded).
 template <int kM>
 __global__ __launch_bounds__(256) void lm_screen_kernel(
     const uint16_t* __restrict__ A, const float* __restrict__ u, const int32_t* __restrict__ row_token,
@@ -259,59 +338,176 @@ __global__ __launch_bounds__(256) void lm_screen_kernel(
     if (sl + 1 < n_slices) store((sl + 1) & 1);
   }
   __syncthreads();  // every thread is done with the slices: their LDS holds the picks now
+  screen_picks<kM>(acc, reinterpret_cast<uint64_t*>(&s_a[0][0]), row_token, M, n, tile, k_tile,
+                   cand, cand_score);
+}
 
-  // Each wavefront's k best rows per hidden state, then the merge of the two wavefronts of the
-  // half.  A wavefront holds rows q0 = 64 (wave & 1) + lane and q0 + 128, so among its rows
-  // with the best score the smallest row is the lowest lane holding it in its first row, else
-  // in its second: a 32-bit maximum and ballots replace a 64-bit (score, row) maximum.  The
-  // hidden states' reductions of one round are independent, so they interleave.
-  uint64_t* s_pick = reinterpret_cast<uint64_t*>(&s_a[0][0]);  // [M][2][k_tile]
-  const int wh = wave & 1;
-  const bool real0 = p < rows, real1 = p + 128 < rows;
-  uint64_t taken0 = 0, taken1 = 0;  // bit i: the row was picked for hidden state half*kH + i
-  for (int j = 0; j < k_tile; ++j) {
+// u = hi + mid + lo with three bfloat16 parts: hi = bf16(x), mid = bf16(x - hi), lo = the rest.
+// Each subtraction is exact (the operands are within a factor of two), and the rest has at most
+// eight significant bits, so the parts sum to x exactly (for |x| well above 2^-110).
+__device__ inline void split3(float x, __bf16& hi, __bf16& mid, __bf16& lo) {
+  hi = (__bf16)x;
+  const float r1 = x - (float)hi;
+  mid = (__bf16)r1;
+  lo = (__bf16)(r1 - (float)mid);
+}
+
+constexpr int kMfmaMaxR = 256;  // ranks the MFMA screening kernel holds in registers
+
+// Screening of tile blockIdx.x on v_mfma_f32_32x32x16_bf16: scores S = A_tile u^T with u split
+// into three bfloat16 parts, so every product A_i * part is exact in float32 and a term passes
+// through at most 16 + 3 ceil(r / 16) roundings (16 inside its MFMA, one per later MFMA of the
+// chain), within the vector kernel's r for the workload's rank.
+//  * Wavefront w owns rows 64 w .. 64 w + 63 as two 32-row blocks; lane (q, h) = (lane % 32,
+//    lane / 32) holds, for every 16-element k-step s, elements 16 s + 8 h .. + 7 of row q of
+//    each block: the MFMA's A operand, loaded straight from memory (16 bytes per lane, zero
+//    past r or past the tile).
+//  * The three parts of u sit in LDS (rows padded by 16 bytes so the 32 rows of a B-operand
+//    read fall in different banks); a hidden-state block of 32 reads its
+//    B operand there, and every B operand serves both row blocks.
+//  * Each lane picks from the 32 rows of one hidden state its accumulators hold; the eight
+//    lists of a hidden state then merge by rank.
+template <int kM>
+__global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
+    const uint16_t* __restrict__ A, const float* __restrict__ u,
+    const int32_t* __restrict__ row_token, int M, int r, int n, int tile, int k_tile,
+    int32_t* __restrict__ cand, float* __restrict__ cand_score) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x16 __attribute__((ext_vector_type(16)));
+  constexpr int kMpad = kM <= 32 ? 32 : 64;
+  constexpr int kNMB = kMpad / 32;  // hidden-state blocks
+  constexpr int kKS = kMfmaMaxR / 16;
+  // u's parts for one block of 32 hidden states (r <= kMfmaMaxR), then the picks
+  // (M * 8 * k_tile 64-bit words); two workgroups fit a compute unit
+  constexpr int kPartsLds = 3 * 32 * (2 * kMfmaMaxR + 16);
+  constexpr int kPickLds = kMpad * 8 * kLmMaxKTile * 8;
+  constexpr int kLds = kPartsLds > kPickLds ? kPartsLds : kPickLds;
+  __shared__ __attribute__((aligned(16))) char s_dyn[kLds];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane & 31, h = lane >> 5;
+  const int t = blockIdx.x;
+  const int r0 = t * tile;
+  const int rows = min(tile, n - r0);
+  // every row of a part holds kMfmaMaxR elements (zero from r on) and 16 bytes of padding, so
+  // the k-step loop below runs all kMfmaMaxR / 16 steps without a branch: a step past r adds
+  // exact zeros
+  constexpr int u_row = 2 * kMfmaMaxR + 16;  // bytes per row of a part
+  constexpr int u_part = 32 * u_row;
+
+  // the wavefront's A operands, every load issued before u is staged
+  bf16x8 a[2][kKS];
 #pragma unroll
-    for (int i = 0; i < kH; ++i) {
-      const int m = half * kH + i;
-      if (m < M) {
-        const bool open0 = real0 && !((taken0 >> i) & 1);
-        const bool open1 = real1 && !((taken1 >> i) & 1);
-        const uint32_t k0 = open0 ? fkey(acc[0][i]) : 0u, k1 = open1 ? fkey(acc[1][i]) : 0u;
-        const uint32_t best = wave_max_u32(max(k0, k1));
-        const uint64_t h0 = __ballot(open0 && k0 == best);
-        const uint64_t h1 = __ballot(open1 && k1 == best);
-        uint64_t pick = 0;  // none left: fewer real rows than picks
-        if (h0 | h1) {
-          const int w = __builtin_ctzll(h0 ? h0 : h1);
-          const int q = (h0 ? 0 : 128) + wh * 64 + w;
-          if (lane == w) {
-            if (h0) taken0 |= 1ull << i;
-            else taken1 |= 1ull << i;
-          }
-          pick = ((uint64_t)best << 32) | (0xffffffffu - (uint32_t)(r0 + q));
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+      const int row = 64 * wave + 32 * rb + q, i0 = 16 * s + 8 * h;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row < rows && i0 < r)  // r % 8 == 0: a piece is all in or all out
+        v = *reinterpret_cast<const uint4*>(A + (size_t)(r0 + row) * r + i0);
+      a[rb][s] = __builtin_bit_cast(bf16x8, v);
+    }
+
+  f32x16 acc[2][kNMB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < kNMB; ++mb) acc[rb][mb] = f32x16{};
+  constexpr int per_row = kMfmaMaxR / 8;
+#pragma unroll
+  for (int mb = 0; mb < kNMB; ++mb) {
+    if (mb > 0) __syncthreads();  // the previous block's parts are no longer read
+    // u's three parts of hidden states 32 mb .. 32 mb + 31 into LDS: part p, hidden state
+    // 32 mb + j, element i at p*u_part + j*u_row + 2 i (zero for hidden states >= M or i >= r)
+    for (int x = tid; x < 32 * per_row; x += 256) {
+      const int j = x / per_row, i0 = (x - j * per_row) * 8, m = 32 * mb + j;
+      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (m < M && i0 < r) {
+        const float4 v0 = *reinterpret_cast<const float4*>(u + (size_t)m * r + i0);
+        const float4 v1 = *reinterpret_cast<const float4*>(u + (size_t)m * r + i0 + 4);
+        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+      }
+      uint32_t w[3][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        __bf16 h0, m0, l0, h1, m1, l1;
+        split3(v[2 * e], h0, m0, l0);
+        split3(v[2 * e + 1], h1, m1, l1);
+        w[0][e] = __builtin_bit_cast(uint32_t, bf16x2{h0, h1});
+        w[1][e] = __builtin_bit_cast(uint32_t, bf16x2{m0, m1});
+        w[2][e] = __builtin_bit_cast(uint32_t, bf16x2{l0, l1});
+      }
+#pragma unroll
+      for (int pt = 0; pt < 3; ++pt)
+        *reinterpret_cast<uint4*>(s_dyn + pt * u_part + j * u_row + 2 * i0) =
+            make_uint4(w[pt][0], w[pt][1], w[pt][2], w[pt][3]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < kKS; ++s)
+#pragma unroll
+      for (int pt = 0; pt < 3; ++pt) {
+        const bf16x8 bq = *reinterpret_cast<const bf16x8*>(s_dyn + pt * u_part + q * u_row +
+                                                           2 * (16 * s + 8 * h));
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+          acc[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb][s], bq, acc[rb][mb], 0, 0, 0);
+      }
+  }
+  __syncthreads();  // every wavefront is done with u's parts: their LDS takes the picks
+
+  // Picks straight from the accumulators.  Element e of acc[rb][mb] is row
+  // 64 w + 32 rb + 8 (e / 4) + 4 h + e % 4 of the tile for hidden state 32 mb + q, so each lane
+  // holds 32 rows of one hidden state.  A row's key is (fkey(score) << 32) | ~row: the larger
+  // key is the better row, ties going to the smaller row; rows past the tile have key 0.  Each
+  // lane takes its k_tile best keys, best first, by rounds of a maximum and its removal (keys
+  // of real rows are distinct), into s_pick[m][2 w + h][j]; then the 8 lists of a hidden state
+  // merge by rank.
+  uint64_t* s_pick = reinterpret_cast<uint64_t*>(s_dyn);  // [M][8][k_tile]
+#pragma unroll
+  for (int mb = 0; mb < kNMB; ++mb) {
+    const int m = 32 * mb + q;
+    if (m < M) {
+      uint64_t key[32];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = 64 * wave + 32 * rb + 8 * (e >> 2) + 4 * h + (e & 3);
+          key[rb * 16 + e] = row < rows ? ((uint64_t)fkey(acc[rb][mb][e]) << 32) |
+                                              (0xffffffffu - (uint32_t)(r0 + row))
+                                        : 0ull;
         }
-        if (lane == 0) s_pick[(m * 2 + wh) * k_tile + j] = pick;
+      uint64_t* out = s_pick + ((size_t)m * 8 + 2 * wave + h) * k_tile;
+      for (int j = 0; j < k_tile; ++j) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int x = 1; x < 32; ++x) best = key[x] > best ? key[x] : best;
+#pragma unroll
+        for (int x = 0; x < 32; ++x) key[x] = key[x] == best ? 0ull : key[x];
+        out[j] = best;  // 0: no real row left
       }
     }
   }
   __syncthreads();
   const int C = ceil_div(n, tile) * k_tile;
-  const int per_m = 2 * k_tile;
+  const int per_m = 8 * k_tile;
   for (int x = tid; x < M * per_m; x += 256) {
     const int m = x / per_m, e = x - m * per_m;
-    const uint64_t* pm = s_pick + m * per_m;
+    const uint64_t* pm = s_pick + (size_t)m * per_m;
     const uint64_t me = pm[e];
     int rank = 0;  // picks are distinct except padding (0), which ranks by entry
     for (int o = 0; o < per_m; ++o) rank += pm[o] > me || (pm[o] == me && o < e);
     if (rank >= k_tile) continue;
-    const size_t out = (size_t)m * C + (size_t)t * k_tile + rank;
+    const size_t o_at = (size_t)m * C + (size_t)t * k_tile + rank;
     if (me == 0) {  // the tile has fewer real rows than k_tile: padding picks rank last
-      cand[out] = -1;
-      cand_score[out] = -INFINITY;
+      cand[o_at] = -1;
+      cand_score[o_at] = -INFINITY;
     } else {
       const int row = (int)(0xffffffffu - (uint32_t)me);
-      cand[out] = row_token[row];
-      cand_score[out] = fkey_value((uint32_t)(me >> 32));
+      cand[o_at] = row_token[row];
+      cand_score[o_at] = fkey_value((uint32_t)(me >> 32));
     }
   }
 }
@@ -450,9 +646,13 @@ constexpr int kScreenM[] = {2, 4, 6, 8, 10, 12, 16, 24, 32, 48, 64};
 template <int kM>
 void launch_screen(const void* A, const float* u, const int32_t* row_token, int M, int r, int n,
                    int tile, int k_tile, int32_t* cand, float* cand_score, hipStream_t stream) {
-  hipLaunchKernelGGL(lm_screen_kernel<kM>, dim3(ceil_div(n, tile)), dim3(256),
-                     (size_t)kM * r * sizeof(float), stream, (const uint16_t*)A, u, row_token, M, r,
-                     n, tile, k_tile, cand, cand_score);
+  if (r <= kMfmaMaxR)  // matrix cores; larger ranks run the float32 chains
+    hipLaunchKernelGGL(lm_screen_mfma_kernel<kM>, dim3(ceil_div(n, tile)), dim3(256), 0, stream,
+                       (const uint16_t*)A, u, row_token, M, r, n, tile, k_tile, cand, cand_score);
+  else
+    hipLaunchKernelGGL(lm_screen_kernel<kM>, dim3(ceil_div(n, tile)), dim3(256),
+                       (size_t)kM * r * sizeof(float), stream, (const uint16_t*)A, u, row_token, M,
+                       r, n, tile, k_tile, cand, cand_score);
 }
 }  // namespace
 }  // namespace tv
