@@ -251,6 +251,19 @@ def test_every_hidden_state_count():
         run_both(_rand(rng, (M, d)), A, Bm, W, perm, 128, 3, 8, f"M={M}")
 
 
+def test_screen_kernel_boundary_and_largest_picks():
+    """Ranks at and just past the matrix-core screening kernel's limit (256, then 272 on the
+    float32 chains), the most hidden states and candidates per tile (64 and 16: the largest
+    pick area), a short last tile, and ranks that are not multiples of 16."""
+    rng = np.random.default_rng(46)
+    d, n = 512, 1300
+    for M, r, k_tile in ((64, 256, 16), (48, 272, 16), (33, 248, 16), (40, 200, 5)):
+        h, Bm = _rand(rng, (M, d)), _rand(rng, (r, d), 1 / np.sqrt(d))
+        A, W = _rand(rng, (n, r)), _rand(rng, (n, d), 0.05)
+        perm = rng.permutation(n).astype(np.int32)
+        run_both(h, A, Bm, W, perm, 256, k_tile, 12, f"M={M} r={r} k_tile={k_tile}")
+
+
 def test_padding_bad_tokens_and_short_lists():
     import tree_attention_verification_attn_amd as tv
 

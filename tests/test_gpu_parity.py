@@ -71,6 +71,23 @@ def test_split_results_agree():
         assert np.abs(a - b).max() <= TOL_OUT["bf16"]
 
 
+# ---- merge ranking over more than 256 sequences ---------------------------------------------
+def test_merge_ranks_more_than_256_sequences():
+    """With few chunks per sequence the merge ranks the split sequences by ballots, 256 per pass:
+    300 sequences, most split in two and some not split, so the ranking takes two passes and
+    skips sequences in both.  The separate calls and the fused step agree bit for bit and match
+    the oracle."""
+    from gpu_util import run_step_fused
+
+    w = make_workload("batch32_L512-4096_T60", B=300, T=8, L=(0, 120), Hq=2, Hkv=1, D=64,
+                      parent_kind="random", extra_seed=91)
+    w.cache_len[::7] = 0  # the tree tile alone: one chunk, written directly, never merged
+    res, _ = _run_and_check(w, split_keys=64, label="300 sequences, split_keys 64")
+    fused = run_step_fused(upload(w), split_keys=64)
+    assert np.array_equal(res["out"].view(np.uint16), fused["out"].view(np.uint16))
+    assert np.array_equal(res["lse"].view(np.uint32), fused["lse"].view(np.uint32))
+
+
 # ---- every shape of the split-K merge ------------------------------------------------------
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
 @pytest.mark.parametrize("target", [2, 4, 8, 20, 64])
