@@ -1049,51 +1049,59 @@ __device__ void combine_group(const AttnArgs& a, int c) {
   static_assert(kSW == 1 || kP == 1, "shared pieces are merged one per thread");
   const int tid = threadIdx.x;
   const int pl = tid % kPer, sg = tid / kPer;  // piece within the workgroup, chunk group
-  int b, item;
+  int b, item, n_split;
   if constexpr (kSW == 1) {
     // Logical workgroups go to split sequences only, in sequence order: logical workgroup c
     // serves the (c / per_seq)-th sequence with more than one chunk, so all the merge's work
     // sits in the first workgroups (the hardware deals them to the XCDs in turn) and the rest,
     // up to the grid's bound for a plan that splits every sequence, leave at once.  Wavefront
     // 0 ranks the sequences by ballots over their chunk counts.
-    __shared__ int s_b;
+    // The chunk count of the sequence found goes along with it, so the partials' loads wait
+    // for one read of the counts, not two.
+    __shared__ int s_b, s_n;
     const int per_seq = a.Hkv * a.RB * kWGs;
     const int rank = c / per_seq;
     if (tid < 64) {
-      int found = -1, before = 0;
+      int found = -1, found_n = 0, before = 0;
       for (int base = 0; base < a.B && found < 0; base += 256) {
-        bool sp[4];
+        int ns[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int bi = base + 64 * k + tid;
-          sp[k] = bi < a.B && a.nsplit[bi] > 1;
+          ns[k] = bi < a.B ? a.nsplit[bi] : 0;
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const uint64_t m = __ballot(sp[k]);
+          const uint64_t m = __ballot(ns[k] > 1);
           const int cnt = __popcll(m);
           if (found < 0 && rank < before + cnt) {
             uint64_t mm = m;  // the (rank - before)-th set lane
             for (int i = rank - before; i > 0; --i) mm &= mm - 1;
-            found = base + 64 * k + __builtin_ctzll(mm);
+            const int lane = __builtin_ctzll(mm);
+            found = base + 64 * k + lane;
+            found_n = __shfl(ns[k], lane, 64);
           }
           before += cnt;
         }
       }
-      if (tid == 0) s_b = found;
+      if (tid == 0) {
+        s_b = found;
+        s_n = found_n;
+      }
     }
     __syncthreads();
     b = s_b;
     if (b < 0) return;  // more logical workgroups than the split sequences need (uniform)
+    n_split = s_n;
     item = b * a.Hkv * a.RB + (c % per_seq) / kWGs;
   } else {
+    // the chunk count is read here but first needed after the first batch's loads are issued
     item = c / kWGs;
     b = item / (a.RB * a.Hkv);
+    n_split = a.nsplit[b];
   }
   const int rb = item % a.RB;
   const int kvh = (item / a.RB) % a.Hkv;
-  const int n_split = a.nsplit[b];
-  if (n_split <= 1) return;  // written directly by attn_main (uniform: the whole workgroup)
   const size_t slot0 = (((size_t)b * a.Hkv + kvh) * a.RB + rb) * a.S;
   const float4* po = reinterpret_cast<const float4*>(a.part_o) + slot0 * kStride;
   const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + slot0 * kRows;
@@ -1122,11 +1130,9 @@ __device__ void combine_group(const AttnArgs& a, int c) {
     acc[q] = float4{0.f, 0.f, 0.f, 0.f};
   }
   // chunk group sg takes chunks sg, sg + kSW, sg + 2 kSW, ...
-  const int n_mine = sg < n_split ? (n_split - sg + kSW - 1) / kSW : 0;
-  for (int k0 = 0; k0 < n_mine; k0 += kBatch) {
-    const int nb = min(kBatch, n_mine - k0);  // uniform across the workgroup
-    float4 v[kP][kBatch];
-    float2 ml[kP][kBatch];
+  float4 v[kP][kBatch];
+  float2 ml[kP][kBatch];
+  auto load_batch = [&](int k0, int nb) {
 #pragma unroll
     for (int q = 0; q < kP; ++q)
 #pragma unroll
@@ -1139,6 +1145,16 @@ __device__ void combine_group(const AttnArgs& a, int c) {
           v[q][u] = float4{0.f, 0.f, 0.f, 0.f};
           ml[q][u] = float2{-INFINITY, 0.f};
         }
+  };
+  // The first batch is loaded as far as the plan's chunk count, which bounds the sequence's
+  // own and whose slots all exist, so with shared pieces these loads need not wait for the
+  // count.  Slots past the sequence's count hold stale values; they only ever pass the u < nb
+  // selects below, never the arithmetic.
+  const int n_plan = kSW == 1 ? n_split : a.S;
+  load_batch(0, min(kBatch, sg < n_plan ? (n_plan - sg + kSW - 1) / kSW : 0));
+  const int n_mine = sg < n_split ? (n_split - sg + kSW - 1) / kSW : 0;
+  for (int k0 = 0;;) {
+    const int nb = min(kBatch, n_mine - k0);  // uniform across the workgroup; 0 if none
 #pragma unroll
     for (int q = 0; q < kP; ++q) {
       // A chunk in which a row sees no key (a second tree tile that holds none of the row's
@@ -1169,7 +1185,11 @@ __device__ void combine_group(const AttnArgs& a, int c) {
         }
       M[q] = Mb;
     }
+    k0 += kBatch;
+    if (k0 >= n_mine) break;
+    load_batch(k0, min(kBatch, n_mine - k0));
   }
+  if (n_split <= 1) return;  // written directly by attn_main (uniform: the whole workgroup)
   if constexpr (kSW > 1) {
     // the chunk groups' partial merges meet in LDS; group 0 combines them in group order
     __shared__ float4 s_acc[kSW][kPer];
