@@ -27,8 +27,9 @@
 //   lm_screen_mfma_kernel  one workgroup per tile of rows (ranks up to 256): each wavefront
 //                      loads 64 rows of A straight into MFMA operands, u's three bfloat16 parts
 //                      sit in LDS one block of 32 hidden states at a time, each lane picks the
-//                      k best of the 32 rows its accumulators hold for one hidden state, and the
-//                      eight lists of a hidden state merge by rank
+//                      k best of the 32 rows its accumulators hold for one hidden state (a
+//                      sorting network on float64 stand-ins of the keys for k <= 4), and the
+//                      eight lists of a hidden state merge
 //   lm_screen_kernel   (larger ranks) one workgroup per tile of rows: the tile's A rows stream
 //                      through LDS in 64-element slices (each row's 128 B XOR-swizzled by
 //                      16-byte piece so a thread reading its row is free of bank conflicts), a
@@ -59,7 +60,8 @@ __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0
 // Unsigned key in the float's order, -0 taken as +0.
 __device__ inline uint32_t fkey(float v) {
   const uint32_t u = __float_as_uint(v + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // negative: all bits flipped; otherwise the sign bit set
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ inline float fkey_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
@@ -354,6 +356,13 @@ __device__ inline void split3(float x, __bf16& hi, __bf16& mid, __bf16& lo) {
 
 constexpr int kMfmaMaxR = 256;  // ranks the MFMA screening kernel holds in registers
 
+// a >= b afterwards (neither is NaN)
+__device__ inline void cmp_swap_desc(double& a, double& b) {
+  const double hi = __builtin_fmax(a, b), lo = __builtin_fmin(a, b);
+  a = hi;
+  b = lo;
+}
+
 // The k_tile best of kL sorted lists of picks (64-bit keys, best first, 0 for no row) of one
 // hidden state, written as candidates out[0 .. k_tile) of cand / cand_score from index `at`:
 // the lists' heads sit in registers, and k_tile rounds take the best head and refill that list's
@@ -441,45 +450,39 @@ __global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
   constexpr int u_row = 2 * kMfmaMaxR + 16;  // bytes per row of a part
   constexpr int u_part = 32 * u_row;
 
-  // the wavefront's A operands, every load issued before u is staged
-  bf16x8 a[2][kKS];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int s = 0; s < kKS; ++s) {
-      const int row = 64 * wave + 32 * rb + q, i0 = 16 * s + 8 * h;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row < rows && i0 < r)  // r % 8 == 0: a piece is all in or all out
-        v = *reinterpret_cast<const uint4*>(A + (size_t)(r0 + row) * r + i0);
-      a[rb][s] = __builtin_bit_cast(bf16x8, v);
-    }
-
-  f32x16 acc[2][kNMB];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int mb = 0; mb < kNMB; ++mb) acc[rb][mb] = f32x16{};
   constexpr int per_row = kMfmaMaxR / 8;
+  constexpr int kUIt = 32 * per_row / 256;  // 8-element pieces of a u block per thread
+  // u's raw values of hidden states 32 mb .. 32 mb + 31: thread piece k covers hidden state
+  // j = x / per_row, elements i0 .. i0 + 7, x = tid + 256 k (zero for hidden states >= M or
+  // i >= r)
+  auto load_u = [&](int mb, float (&v)[kUIt][8]) {
 #pragma unroll
-  for (int mb = 0; mb < kNMB; ++mb) {
-    if (mb > 0) __syncthreads();  // the previous block's parts are no longer read
-    // u's three parts of hidden states 32 mb .. 32 mb + 31 into LDS: part p, hidden state
-    // 32 mb + j, element i at p*u_part + j*u_row + 2 i (zero for hidden states >= M or i >= r)
-    for (int x = tid; x < 32 * per_row; x += 256) {
+    for (int k = 0; k < kUIt; ++k) {
+      const int x = tid + 256 * k;
       const int j = x / per_row, i0 = (x - j * per_row) * 8, m = 32 * mb + j;
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (m < M && i0 < r) {
-        const float4 v0 = *reinterpret_cast<const float4*>(u + (size_t)m * r + i0);
-        const float4 v1 = *reinterpret_cast<const float4*>(u + (size_t)m * r + i0 + 4);
-        v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-        v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-      }
+      // clamped, not branched, so that every load is issued and the waits count exactly
+      const float* src = u + (size_t)min(m, M - 1) * r + min(i0, r - 8);
+      const float4 v0 = *reinterpret_cast<const float4*>(src);
+      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+      const bool in = m < M && i0 < r;
+      v[k][0] = in ? v0.x : 0.f; v[k][1] = in ? v0.y : 0.f;
+      v[k][2] = in ? v0.z : 0.f; v[k][3] = in ? v0.w : 0.f;
+      v[k][4] = in ? v1.x : 0.f; v[k][5] = in ? v1.y : 0.f;
+      v[k][6] = in ? v1.z : 0.f; v[k][7] = in ? v1.w : 0.f;
+    }
+  };
+  // their three parts into LDS: part p, hidden state j, element i at p*u_part + j*u_row + 2 i
+  auto stage_u = [&](const float (&v)[kUIt][8]) {
+#pragma unroll
+    for (int k = 0; k < kUIt; ++k) {
+      const int x = tid + 256 * k;
+      const int j = x / per_row, i0 = (x - j * per_row) * 8;
       uint32_t w[3][4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         __bf16 h0, m0, l0, h1, m1, l1;
-        split3(v[2 * e], h0, m0, l0);
-        split3(v[2 * e + 1], h1, m1, l1);
+        split3(v[k][2 * e], h0, m0, l0);
+        split3(v[k][2 * e + 1], h1, m1, l1);
         w[0][e] = __builtin_bit_cast(uint32_t, bf16x2{h0, h1});
         w[1][e] = __builtin_bit_cast(uint32_t, bf16x2{m0, m1});
         w[2][e] = __builtin_bit_cast(uint32_t, bf16x2{l0, l1});
@@ -489,6 +492,49 @@ __global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
         *reinterpret_cast<uint4*>(s_dyn + pt * u_part + j * u_row + 2 * i0) =
             make_uint4(w[pt][0], w[pt][1], w[pt][2], w[pt][3]);
     }
+  };
+
+  // The first block of u is read before the tile, and the tile's A operands are issued k-step
+  // by k-step, so the MFMA chain below starts on the first steps while the later ones are
+  // still in flight (loads complete in issue order).
+  float uv[kUIt][8];
+  load_u(0, uv);
+  bf16x8 a[2][kKS];
+#pragma unroll
+  for (int s = 0; s < kKS; ++s)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      // Clamped, not branched, so that every load is issued and the MFMAs wait for exactly
+      // the steps they use: rows past the tile repeat its last row (their keys are 0 below),
+      // and pieces past r (r % 8 == 0: a piece is all in or all out) repeat the row's last
+      // piece until zeroed below.
+      const int row = 64 * wave + 32 * rb + q, i0 = 16 * s + 8 * h;
+      a[rb][s] = *reinterpret_cast<const bf16x8*>(A + (size_t)(r0 + min(row, rows - 1)) * r +
+                                                  min(i0, r - 8));
+    }
+  if (r < kMfmaMaxR) {
+    // The k-step loop runs all kMfmaMaxR / 16 steps without a branch, so a step past r must
+    // add exact zeros: u's parts are zero there, and the repeated pieces, which may hold an
+    // infinity, are zeroed (uniform branch: at the full rank no wait is spent here).
+#pragma unroll
+    for (int s = 0; s < kKS; ++s)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        if (16 * s + 8 * h >= r) a[rb][s] = bf16x8{};
+  }
+
+  f32x16 acc[2][kNMB];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int mb = 0; mb < kNMB; ++mb) acc[rb][mb] = f32x16{};
+#pragma unroll
+  for (int mb = 0; mb < kNMB; ++mb) {
+    if (mb > 0) {
+      load_u(mb, uv);
+      __syncthreads();  // the previous block's parts are no longer read
+    }
+    stage_u(uv);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < kKS; ++s)
@@ -507,8 +553,9 @@ __global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
   // 64 w + 32 rb + 8 (e / 4) + 4 h + e % 4 of the tile for hidden state 32 mb + q, so each lane
   // holds 32 rows of one hidden state.  A row's key is (fkey(score) << 32) | ~row: the larger
   // key is the better row, ties going to the smaller row; rows past the tile have key 0.  Each
-  // lane takes its k_tile best keys, best first, by rounds of a maximum and its removal (keys
-  // of real rows are distinct), into s_pick[m][2 w + h][j]; then the 8 sorted lists of each
+  // lane takes its k_tile best keys, best first (keys of real rows are distinct: a sorting
+  // network for k_tile <= 4, else rounds of a maximum and its removal), into
+  // s_pick[m][2 w + h][j]; then the 8 sorted lists of each
   // hidden state merge: by counting ranks when the picks are few (M * 8 * k_tile <= 512), by one
   // thread per hidden state otherwise (at M = 64 the ranks took 44.8 us against 38.3 us, at
   // M = 10 24.0 us against 25.8 us).
@@ -517,24 +564,77 @@ __global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
   for (int mb = 0; mb < kNMB; ++mb) {
     const int m = 32 * mb + q;
     if (m < M) {
-      uint64_t key[32];
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = 64 * wave + 32 * rb + 8 * (e >> 2) + 4 * h + (e & 3);
-          key[rb * 16 + e] = row < rows ? ((uint64_t)fkey(acc[rb][mb][e]) << 32) |
-                                              (0xffffffffu - (uint32_t)(r0 + row))
-                                        : 0ull;
-        }
       uint64_t* out = s_pick + ((size_t)m * 8 + 2 * wave + h) * k_tile;
-      for (int j = 0; j < k_tile; ++j) {
-        uint64_t best = key[0];
+      // the row in the tile of element x = 16 rb + e of this lane
+      auto tile_row = [&](int x) { return 64 * wave + 32 * (x >> 4) + 8 * ((x & 15) >> 2) + 4 * h + (x & 3); };
+      if (k_tile <= 4) {
+        // Sorting network: eight sorted groups of four, then seven bitonic merges that keep
+        // the best four of two groups (68 compare-exchanges and 28 maxima, where four rounds
+        // take 124 maxima and 128 compares for the removals).  It runs on float64 stand-ins
+        // of the keys: the bits (fkey << 31) | (2^31 - 1 - row in the tile) are a non-negative
+        // double, and below the NaN patterns once fkey is capped under them (which only moves
+        // NaN scores, all to one place above +inf, ties by row), so the doubles order as the
+        // keys do and a compare-exchange is one v_max_f64 and one v_min_f64.  Rows past the
+        // tile are +0.0, below every real row.
+        double g[8][4];
 #pragma unroll
-        for (int x = 1; x < 32; ++x) best = key[x] > best ? key[x] : best;
+        for (int x = 0; x < 32; ++x) {
+          const uint32_t fk = min(fkey(acc[x >> 4][mb][x & 15]), 0xffdfffffu);
+          const uint32_t lo = (fk << 31) | (0x7fffffffu - (uint32_t)tile_row(x)), hi = fk >> 1;
+          g[x >> 2][x & 3] = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+        }
+        if (__builtin_expect(rows < 256, 0)) {  // uniform: only the vocabulary's last tile
 #pragma unroll
-        for (int x = 0; x < 32; ++x) key[x] = key[x] == best ? 0ull : key[x];
-        out[j] = best;  // 0: no real row left
+          for (int x = 0; x < 32; ++x)
+            if (tile_row(x) >= rows) g[x >> 2][x & 3] = 0.0;
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          cmp_swap_desc(g[x][0], g[x][1]);
+          cmp_swap_desc(g[x][2], g[x][3]);
+          cmp_swap_desc(g[x][0], g[x][2]);
+          cmp_swap_desc(g[x][1], g[x][3]);
+          cmp_swap_desc(g[x][1], g[x][2]);
+        }
+#pragma unroll
+        for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+          for (int x = 0; x < w; ++x) {
+            // g[x] descending, g[x + w] descending: the larger of g[x][e] and g[x + w][3 - e]
+            // are the best four, in bitonic order; two half-cleaners sort them
+            double c[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c[e] = __builtin_fmax(g[x][e], g[x + w][3 - e]);
+            cmp_swap_desc(c[0], c[2]);
+            cmp_swap_desc(c[1], c[3]);
+            cmp_swap_desc(c[0], c[1]);
+            cmp_swap_desc(c[2], c[3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) g[x][e] = c[e];
+          }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j < k_tile) {  // back to the key (0: no real row left)
+            const uint64_t d = (uint64_t)__double_as_longlong(g[0][j]);
+            const uint32_t row = 0x7fffffffu - (uint32_t)(d & 0x7fffffffu);
+            out[j] = d ? ((d >> 31) << 32) | (0xffffffffu - (uint32_t)r0 - row) : 0ull;
+          }
+      } else {
+        // rounds of a maximum and its removal
+        uint64_t key[32];
+#pragma unroll
+        for (int x = 0; x < 32; ++x)
+          key[x] = tile_row(x) < rows ? ((uint64_t)fkey(acc[x >> 4][mb][x & 15]) << 32) |
+                                            (0xffffffffu - (uint32_t)(r0 + tile_row(x)))
+                                      : 0ull;
+        for (int j = 0; j < k_tile; ++j) {
+          uint64_t best = key[0];
+#pragma unroll
+          for (int x = 1; x < 32; ++x) best = key[x] > best ? key[x] : best;
+#pragma unroll
+          for (int x = 0; x < 32; ++x) key[x] = key[x] == best ? 0ull : key[x];
+          out[j] = best;  // 0: no real row left
+        }
       }
     }
   }
