@@ -701,17 +701,25 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const float* __restrict__ 
   const int32_t* cm = cand + (size_t)m * C;
   uint64_t key[kPer];
   float mx = -INFINITY;
+  // every slot's token and logit are loaded before any is used: clamped to the last candidate
+  // rather than branched, so the 2 kPer loads are in flight together
+  int tok[kPer];
+  float lv[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
-    // token and logit loaded together (no load waits for the other)
-    const int c = k * 256 + tid;
-    const int tok = c < C ? cm[c] : -1;
-    const float lv = c < C ? l[c] : 0.f;
-    key[k] = 0;
-    if (tok >= 0 && tok < V) {
-      key[k] = ((uint64_t)fkey(lv) << 32) | (0xffffffffu - (uint32_t)tok);
-      mx = fmaxf(mx, lv);
-    }
+    const int c = min(k * 256 + tid, C - 1);
+    tok[k] = cm[c];
+    lv[k] = l[c];
+  }
+  // the values are taken here, so all the loads above are issued before the first wait
+  // rather than sunk into the conditional uses below
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) __asm__ volatile("" ::"v"(tok[k]), "v"(lv[k]));
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const bool ok = k * 256 + tid < C && tok[k] >= 0 && tok[k] < V;
+    key[k] = ok ? ((uint64_t)fkey(lv[k]) << 32) | (0xffffffffu - (uint32_t)tok[k]) : 0ull;
+    mx = ok ? fmaxf(mx, lv[k]) : mx;
   }
   // max and sum of exponentials over the valid candidates
   mx = wave_max_f32(mx);
@@ -763,7 +771,15 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const float* __restrict__ 
   for (int e = tid; e < 4 * K; e += 256) {
     const uint64_t me = s_pick[e];
     int rank = 0;  // equal picks (a repeated token's copies, or 0 for none) rank by entry
-    for (int o = 0; o < 4 * K; ++o) rank += s_pick[o] > me || (s_pick[o] == me && o < e);
+    // eight LDS reads in flight per step (4 K is a multiple of 4; entries past it read 0)
+    for (int o0 = 0; o0 < 4 * K; o0 += 8) {
+      uint64_t v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = o0 + i < 4 * K ? s_pick[o0 + i] : 0ull;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        rank += o0 + i < 4 * K && (v[i] > me || (v[i] == me && o0 + i < e));
+    }
     if (rank >= K) continue;
     const size_t o = (size_t)m * K + rank;
     if (me == 0) {
