@@ -415,8 +415,8 @@ __device__ inline void merge_pick_lists(const uint64_t* pm, int k_tile, size_t a
 // chain), within the vector kernel's r for the workload's rank.
 //  * Wavefront w owns rows 64 w .. 64 w + 63 as two 32-row blocks; lane (q, h) = (lane % 32,
 //    lane / 32) holds, for every 16-element k-step s, elements 16 s + 8 h .. + 7 of row q of
-//    each block: the MFMA's A operand, loaded straight from memory (16 bytes per lane, zero
-//    past r or past the tile).
+//    each block: the MFMA's A operand, loaded straight from memory (16 bytes per lane; pieces
+//    past r zeroed, rows past the tile computed from its last row and dropped at the picks).
 //  * The three parts of u sit in LDS (rows padded by 16 bytes so the 32 rows of a B-operand
 //    read fall in different banks); a hidden-state block of 32 reads its
 //    B operand there, and every B operand serves both row blocks.
