@@ -14,10 +14,11 @@ kernels' arithmetic:
   then a six-level pairwise combination), so it errs by at most gamma_n sum |x_i y_i|,
   gamma_n = n u / (1 - n u), u = 2^-24.  A screening score on the matrix cores splits the
   float32 u exactly into three bfloat16 parts (each product with A exact) and passes each term
-  through at most 16 + 3 ceil(r / 16) roundings (16 inside its MFMA, one per later MFMA), with
-  the parts' magnitudes summing to at most (1 + 2^-8) |u|; ranks the MFMA kernel does not take
-  run one chain over the rank index (r roundings).  So a screening score errs by at most
-  gamma_n (1 + 2^-8) sum |A_i u_i| with n = max(r, 16 + 3 ceil(r / 16)), plus A times u's own
+  through at most k + 3 ceil(r / k) roundings (k products inside its MFMA: 16 with blocks of 32
+  hidden states, 32 with blocks of 16; then one per later MFMA), with the parts' magnitudes
+  summing to at most (1 + 2^-8) |u|; ranks the MFMA kernel does not take run one chain over the
+  rank index (r roundings).  So a screening score errs by at most gamma_n (1 + 2^-8)
+  sum |A_i u_i| with n = max(r, 16 + 3 ceil(r / 16), 32 + 3 ceil(r / 32)), plus A times u's own
   error;
 * every tile's candidates are distinct rows of that tile, as many as it has up to k_tile, named
   by their tokens through the row shuffle, best first by the GPU's scores; and no unchosen row
@@ -88,7 +89,7 @@ def check_screen(g, A, o_u, eps_u, perm, tile, k_tile, sel, o_cand):
     Ms = len(sel)
     s_ex = O.lm_scores(A, o_u)  # [Ms, n] exact
     absA = np.abs(_f(A))
-    n_round = max(r, 16 + 3 * -(-r // 16))  # either screening kernel (module docstring)
+    n_round = max(r, 16 + 3 * -(-r // 16), 32 + 3 * -(-r // 32))  # any screening path (docstring)
     eps_s = gamma(n_round) * (1 + 2.0 ** -8) * (np.abs(o_u) + eps_u) @ absA.T + eps_u @ absA.T
     n_tiles = -(-n // tile)
     pad = n_tiles * tile - n

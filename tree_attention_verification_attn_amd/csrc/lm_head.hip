@@ -14,11 +14,12 @@
 //     e = 0 .. 7 inner), so every 16-byte load of the wavefront covers 1 KB contiguously; the
 //     64 chain sums are then combined by a butterfly, j with j^32, then j^16, ..., j^1, which
 //     leaves the same value in every lane (d/64 + 6 roundings per term);
-//   * screening (A u), ranks up to 256: on v_mfma_f32_32x32x16_bf16 with u split exactly into
-//     three bfloat16 parts (u = hi + mid + lo), so every product with A is exact in float32 and
-//     a term passes through at most 16 + 3 ceil(r / 16) roundings (16 inside its MFMA, one per
-//     later MFMA of the chain); larger ranks: one chain of fused multiply-adds over the rank
-//     index, in order, from 0 (r roundings per term).
+//   * screening (A u), ranks up to 256: on v_mfma_f32_32x32x16_bf16 (v_mfma_f32_16x16x32_bf16
+//     for at most 16 hidden states) with u split exactly into three bfloat16 parts
+//     (u = hi + mid + lo), so every product with A is exact in float32 and a term passes through
+//     at most k + 3 ceil(r / k) roundings (k = 16 or 32 products inside its MFMA, one per later
+//     MFMA of the chain); larger ranks: one chain of fused multiply-adds over the rank index, in
+//     order, from 0 (r roundings per term).
 // Ranking uses an unsigned key of the float (-0 as +0); equal values go to the smaller row
 // (screening) or the smaller token (children).
 //
@@ -26,10 +27,10 @@
 //   lm_project_kernel  one wavefront per (i, m), u[m, i] = B[i] . h[m]          (2 MB of B)
 //   lm_screen_mfma_kernel  one workgroup per tile of rows (ranks up to 256): each wavefront
 //                      loads 64 rows of A straight into MFMA operands, u's three bfloat16 parts
-//                      sit in LDS one block of 32 hidden states at a time, each lane picks the
-//                      k best of the 32 rows its accumulators hold for one hidden state (a
-//                      sorting network on float64 stand-ins of the keys for k <= 4), and the
-//                      eight lists of a hidden state merge
+//                      sit in LDS one block of 32 (or 16) hidden states at a time, each lane
+//                      picks the k best of the 32 (or 16) rows its accumulators hold for one
+//                      hidden state (a sorting network on float64 stand-ins of the keys for
+//                      k <= 4), and the 8 (or 16) lists of a hidden state merge
 //   lm_screen_kernel   (larger ranks) one workgroup per tile of rows: the tile's A rows stream
 //                      through LDS in 64-element slices (each row's 128 B XOR-swizzled by
 //                      16-byte piece so a thread reading its row is free of bank conflicts), a
@@ -409,19 +410,23 @@ __device__ inline void merge_pick_lists(const uint64_t* pm, int k_tile, size_t a
   }
 }
 
-// Screening of tile blockIdx.x on v_mfma_f32_32x32x16_bf16: scores S = A_tile u^T with u split
-// into three bfloat16 parts, so every product A_i * part is exact in float32 and a term passes
-// through at most 16 + 3 ceil(r / 16) roundings (16 inside its MFMA, one per later MFMA of the
-// chain), within the vector kernel's r for the workload's rank.
-//  * Wavefront w owns rows 64 w .. 64 w + 63 as two 32-row blocks; lane (q, h) = (lane % 32,
-//    lane / 32) holds, for every 16-element k-step s, elements 16 s + 8 h .. + 7 of row q of
-//    each block: the MFMA's A operand, loaded straight from memory (16 bytes per lane; pieces
-//    past r zeroed, rows past the tile computed from its last row and dropped at the picks).
-//  * The three parts of u sit in LDS (rows padded by 16 bytes so the 32 rows of a B-operand
-//    read fall in different banks); a hidden-state block of 32 reads its
-//    B operand there, and every B operand serves both row blocks.
-//  * Each lane picks from the 32 rows of one hidden state its accumulators hold; the eight
-//    sorted lists of a hidden state then merge.
+// Screening of tile blockIdx.x on the matrix cores: scores S = A_tile u^T with u split into
+// three bfloat16 parts, so every product A_i * part is exact in float32.  The hidden states go
+// in blocks of kN: v_mfma_f32_32x32x16_bf16 for kN = 32, and v_mfma_f32_16x16x32_bf16 for
+// kN = 16 (kM <= 16), which pads fewer hidden states and leaves each lane half as many rows to
+// pick from.  A term passes through at most kK + 3 ceil(r / kK) roundings (kK = 512 / kN
+// products inside its MFMA, then one per later MFMA of the chain).
+//  * Wavefront w owns rows 64 w .. 64 w + 63 as 64 / kN blocks of kN rows; lane (q, h) =
+//    (lane % kN, lane / kN) holds, for every kK-element k-step s, elements kK s + 8 h .. + 7 of
+//    row q of each block: the MFMA's A operand, loaded straight from memory (16 bytes per lane;
+//    pieces past r zeroed, rows past the tile computed from its last row and dropped at the
+//    picks).
+//  * The three parts of u sit in LDS (rows padded by 16 bytes so the rows of a B-operand read
+//    fall in different banks); a block of kN hidden states reads its B operand there (lane
+//    (q, h): hidden state q, the same elements), and every B operand serves all row blocks.
+//  * Element e of a row block's accumulator is row 4 kLG (e / 4) + 4 h + e % 4 of the block for
+//    hidden state q (kLG = 64 / kN lane groups), so each lane picks from 64 / kLG rows of one
+//    hidden state; the 4 kLG sorted lists of a hidden state then merge.
 template <int kM>
 __global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
     const uint16_t* __restrict__ A, const float* __restrict__ u,
@@ -429,37 +434,43 @@ __global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
     int32_t* __restrict__ cand, float* __restrict__ cand_score) {
   typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  typedef float f32x16 __attribute__((ext_vector_type(16)));
-  constexpr int kMpad = kM <= 32 ? 32 : 64;
-  constexpr int kNMB = kMpad / 32;  // hidden-state blocks
-  constexpr int kKS = kMfmaMaxR / 16;
-  // u's parts for one block of 32 hidden states (r <= kMfmaMaxR), then the picks
-  // (M * 8 * k_tile 64-bit words); two workgroups fit a compute unit
-  constexpr int kPartsLds = 3 * 32 * (2 * kMfmaMaxR + 16);
-  constexpr int kPickLds = kMpad * 8 * kLmMaxKTile * 8;
+  constexpr int kN = kM <= 16 ? 16 : 32;  // hidden states per MFMA block
+  constexpr int kLG = 64 / kN;             // lane groups along k (4 or 2)
+  constexpr int kK = 8 * kLG;              // products per MFMA output (32 or 16)
+  constexpr int kRB = 64 / kN;             // row blocks per wavefront (4 or 2)
+  constexpr int kE = kN * kN / 64;         // accumulator elements per lane (4 or 16)
+  constexpr int kKeys = kRB * kE;          // rows a lane picks from (16 or 32)
+  constexpr int kLists = 4 * kLG;          // sorted pick lists per hidden state (16 or 8)
+  constexpr int kNMB = (kM + kN - 1) / kN;  // hidden-state blocks
+  constexpr int kMpad = kNMB * kN;
+  constexpr int kKS = kMfmaMaxR / kK;      // k-steps
+  typedef float accv __attribute__((ext_vector_type(kE)));
+  // u's parts for one block of kN hidden states (r <= kMfmaMaxR), then the picks
+  // (M * kLists * k_tile 64-bit words); two workgroups fit a compute unit
+  constexpr int kPartsLds = 3 * kN * (2 * kMfmaMaxR + 16);
+  constexpr int kPickLds = kMpad * kLists * kLmMaxKTile * 8;
   constexpr int kLds = kPartsLds > kPickLds ? kPartsLds : kPickLds;
   __shared__ __attribute__((aligned(16))) char s_dyn[kLds];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = lane & 31, h = lane >> 5;
+  const int q = lane % kN, h = lane / kN;
   const int t = blockIdx.x;
   const int r0 = t * tile;
   const int rows = min(tile, n - r0);
   // every row of a part holds kMfmaMaxR elements (zero from r on) and 16 bytes of padding, so
-  // the k-step loop below runs all kMfmaMaxR / 16 steps without a branch: a step past r adds
-  // exact zeros
+  // the k-step loop below runs all kKS steps without a branch: a step past r adds exact zeros
   constexpr int u_row = 2 * kMfmaMaxR + 16;  // bytes per row of a part
-  constexpr int u_part = 32 * u_row;
+  constexpr int u_part = kN * u_row;
 
   constexpr int per_row = kMfmaMaxR / 8;
-  constexpr int kUIt = 32 * per_row / 256;  // 8-element pieces of a u block per thread
-  // u's raw values of hidden states 32 mb .. 32 mb + 31: thread piece k covers hidden state
+  constexpr int kUIt = kN * per_row / 256;  // 8-element pieces of a u block per thread
+  // u's raw values of hidden states kN mb .. kN mb + kN - 1: thread piece k covers hidden state
   // j = x / per_row, elements i0 .. i0 + 7, x = tid + 256 k (zero for hidden states >= M or
   // i >= r)
   auto load_u = [&](int mb, float (&v)[kUIt][8]) {
 #pragma unroll
     for (int k = 0; k < kUIt; ++k) {
       const int x = tid + 256 * k;
-      const int j = x / per_row, i0 = (x - j * per_row) * 8, m = 32 * mb + j;
+      const int j = x / per_row, i0 = (x - j * per_row) * 8, m = kN * mb + j;
       // clamped, not branched, so that every load is issued and the waits count exactly
       const float* src = u + (size_t)min(m, M - 1) * r + min(i0, r - 8);
       const float4 v0 = *reinterpret_cast<const float4*>(src);
@@ -499,35 +510,35 @@ __global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
   // still in flight (loads complete in issue order).
   float uv[kUIt][8];
   load_u(0, uv);
-  bf16x8 a[2][kKS];
+  bf16x8 a[kRB][kKS];
 #pragma unroll
   for (int s = 0; s < kKS; ++s)
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       // Clamped, not branched, so that every load is issued and the MFMAs wait for exactly
       // the steps they use: rows past the tile repeat its last row (their keys are 0 below),
       // and pieces past r (r % 8 == 0: a piece is all in or all out) repeat the row's last
       // piece until zeroed below.
-      const int row = 64 * wave + 32 * rb + q, i0 = 16 * s + 8 * h;
+      const int row = 64 * wave + kN * rb + q, i0 = kK * s + 8 * h;
       a[rb][s] = *reinterpret_cast<const bf16x8*>(A + (size_t)(r0 + min(row, rows - 1)) * r +
                                                   min(i0, r - 8));
     }
   if (r < kMfmaMaxR) {
-    // The k-step loop runs all kMfmaMaxR / 16 steps without a branch, so a step past r must
-    // add exact zeros: u's parts are zero there, and the repeated pieces, which may hold an
-    // infinity, are zeroed (uniform branch: at the full rank no wait is spent here).
+    // The k-step loop runs all kKS steps without a branch, so a step past r must add exact
+    // zeros: u's parts are zero there, and the repeated pieces, which may hold an infinity,
+    // are zeroed (uniform branch: at the full rank no wait is spent here).
 #pragma unroll
     for (int s = 0; s < kKS; ++s)
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        if (16 * s + 8 * h >= r) a[rb][s] = bf16x8{};
+      for (int rb = 0; rb < kRB; ++rb)
+        if (kK * s + 8 * h >= r) a[rb][s] = bf16x8{};
   }
 
-  f32x16 acc[2][kNMB];
+  accv acc[kRB][kNMB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < kRB; ++rb)
 #pragma unroll
-    for (int mb = 0; mb < kNMB; ++mb) acc[rb][mb] = f32x16{};
+    for (int mb = 0; mb < kNMB; ++mb) acc[rb][mb] = accv{};
 #pragma unroll
   for (int mb = 0; mb < kNMB; ++mb) {
     if (mb > 0) {
@@ -541,55 +552,61 @@ __global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
 #pragma unroll
       for (int pt = 0; pt < 3; ++pt) {
         const bf16x8 bq = *reinterpret_cast<const bf16x8*>(s_dyn + pt * u_part + q * u_row +
-                                                           2 * (16 * s + 8 * h));
+                                                           2 * (kK * s + 8 * h));
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-          acc[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb][s], bq, acc[rb][mb], 0, 0, 0);
+        for (int rb = 0; rb < kRB; ++rb) {
+          if constexpr (kN == 32)
+            acc[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb][s], bq, acc[rb][mb], 0, 0, 0);
+          else
+            acc[rb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb][s], bq, acc[rb][mb], 0, 0, 0);
+        }
       }
   }
   __syncthreads();  // every wavefront is done with u's parts: their LDS takes the picks
 
-  // Picks straight from the accumulators.  Element e of acc[rb][mb] is row
-  // 64 w + 32 rb + 8 (e / 4) + 4 h + e % 4 of the tile for hidden state 32 mb + q, so each lane
-  // holds 32 rows of one hidden state.  A row's key is (fkey(score) << 32) | ~row: the larger
-  // key is the better row, ties going to the smaller row; rows past the tile have key 0.  Each
-  // lane takes its k_tile best keys, best first (keys of real rows are distinct: a sorting
-  // network for k_tile <= 4, else rounds of a maximum and its removal), into
-  // s_pick[m][2 w + h][j]; then the 8 sorted lists of each
-  // hidden state merge: by counting ranks when the picks are few (M * 8 * k_tile <= 512), by one
-  // thread per hidden state otherwise (at M = 64 the ranks took 44.8 us against 38.3 us, at
-  // M = 10 24.0 us against 25.8 us).
-  uint64_t* s_pick = reinterpret_cast<uint64_t*>(s_dyn);  // [M][8][k_tile]
+  // Picks straight from the accumulators: each lane holds kKeys rows of hidden state
+  // kN mb + q.  A row's key is (fkey(score) << 32) | ~row: the larger key is the better row,
+  // ties going to the smaller row; rows past the tile have key 0.  Each lane takes its k_tile
+  // best keys, best first (keys of real rows are distinct: a sorting network for k_tile <= 4,
+  // else rounds of a maximum and its removal), into s_pick[m][kLG w + h][j]; then the kLists
+  // sorted lists of each hidden state merge: by counting ranks when the picks are few
+  // (M * kLists * k_tile <= 512), by one thread per hidden state otherwise (at M = 64 the ranks
+  // took 44.8 us against 38.3 us, at M = 10 24.0 us against 25.8 us).
+  uint64_t* s_pick = reinterpret_cast<uint64_t*>(s_dyn);  // [M][kLists][k_tile]
+  // the row in the tile of this lane's element x = kE rb + e (increasing with x)
+  auto tile_row = [&](int x) {
+    const int rb = x / kE, e = x % kE;
+    return 64 * wave + kN * rb + 4 * kLG * (e >> 2) + 4 * h + (e & 3);
+  };
 #pragma unroll
   for (int mb = 0; mb < kNMB; ++mb) {
-    const int m = 32 * mb + q;
+    const int m = kN * mb + q;
     if (m < M) {
-      uint64_t* out = s_pick + ((size_t)m * 8 + 2 * wave + h) * k_tile;
-      // the row in the tile of element x = 16 rb + e of this lane
-      auto tile_row = [&](int x) { return 64 * wave + 32 * (x >> 4) + 8 * ((x & 15) >> 2) + 4 * h + (x & 3); };
+      uint64_t* out = s_pick + ((size_t)m * kLists + kLG * wave + h) * k_tile;
       if (k_tile <= 4) {
-        // Sorting network: eight sorted groups of four, then seven bitonic merges that keep
-        // the best four of two groups (68 compare-exchanges and 28 maxima, where four rounds
+        // Sorting network: sorted groups of four, then bitonic merges that keep the best four
+        // of two groups (with 32 keys 68 compare-exchanges and 28 maxima, where four rounds
         // take 124 maxima and 128 compares for the removals).  It runs on float64 stand-ins
         // of the keys: the bits (fkey << 31) | (2^31 - 1 - row in the tile) are a non-negative
         // double, and below the NaN patterns once fkey is capped under them (which only moves
         // NaN scores, all to one place above +inf, ties by row), so the doubles order as the
         // keys do and a compare-exchange is one v_max_f64 and one v_min_f64.  Rows past the
         // tile are +0.0, below every real row.
-        double g[8][4];
+        constexpr int kG = kKeys / 4;  // groups
+        double g[kG][4];
 #pragma unroll
-        for (int x = 0; x < 32; ++x) {
-          const uint32_t fk = min(fkey(acc[x >> 4][mb][x & 15]), 0xffdfffffu);
+        for (int x = 0; x < kKeys; ++x) {
+          const uint32_t fk = min(fkey(acc[x / kE][mb][x % kE]), 0xffdfffffu);
           const uint32_t lo = (fk << 31) | (0x7fffffffu - (uint32_t)tile_row(x)), hi = fk >> 1;
           g[x >> 2][x & 3] = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
         }
         if (__builtin_expect(rows < 256, 0)) {  // uniform: only the vocabulary's last tile
 #pragma unroll
-          for (int x = 0; x < 32; ++x)
+          for (int x = 0; x < kKeys; ++x)
             if (tile_row(x) >= rows) g[x >> 2][x & 3] = 0.0;
         }
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
+        for (int x = 0; x < kG; ++x) {
           cmp_swap_desc(g[x][0], g[x][1]);
           cmp_swap_desc(g[x][2], g[x][3]);
           cmp_swap_desc(g[x][0], g[x][2]);
@@ -597,7 +614,7 @@ __global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
           cmp_swap_desc(g[x][1], g[x][2]);
         }
 #pragma unroll
-        for (int w = 4; w >= 1; w >>= 1)
+        for (int w = kG / 2; w >= 1; w >>= 1)
 #pragma unroll
           for (int x = 0; x < w; ++x) {
             // g[x] descending, g[x + w] descending: the larger of g[x][e] and g[x + w][3 - e]
@@ -621,18 +638,18 @@ __global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
           }
       } else {
         // rounds of a maximum and its removal
-        uint64_t key[32];
+        uint64_t key[kKeys];
 #pragma unroll
-        for (int x = 0; x < 32; ++x)
-          key[x] = tile_row(x) < rows ? ((uint64_t)fkey(acc[x >> 4][mb][x & 15]) << 32) |
+        for (int x = 0; x < kKeys; ++x)
+          key[x] = tile_row(x) < rows ? ((uint64_t)fkey(acc[x / kE][mb][x % kE]) << 32) |
                                             (0xffffffffu - (uint32_t)(r0 + tile_row(x)))
                                       : 0ull;
         for (int j = 0; j < k_tile; ++j) {
           uint64_t best = key[0];
 #pragma unroll
-          for (int x = 1; x < 32; ++x) best = key[x] > best ? key[x] : best;
+          for (int x = 1; x < kKeys; ++x) best = key[x] > best ? key[x] : best;
 #pragma unroll
-          for (int x = 0; x < 32; ++x) key[x] = key[x] == best ? 0ull : key[x];
+          for (int x = 0; x < kKeys; ++x) key[x] = key[x] == best ? 0ull : key[x];
           out[j] = best;  // 0: no real row left
         }
       }
@@ -640,7 +657,7 @@ __global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
   }
   __syncthreads();
   const int C = ceil_div(n, tile) * k_tile;
-  const int per_m = 8 * k_tile;
+  const int per_m = kLists * k_tile;
   if (M * per_m <= 512) {
     // few picks: every (hidden state, pick) pair counts the picks ahead of it, two pairs per
     // thread at most
@@ -661,9 +678,9 @@ __global__ __launch_bounds__(256) void lm_screen_mfma_kernel(
         cand_score[o_at] = fkey_value((uint32_t)(me >> 32));
       }
     }
-  } else if (tid < M) {  // many: one thread per hidden state merges its 8 sorted lists
-    merge_pick_lists<8>(s_pick + (size_t)tid * per_m, k_tile, (size_t)tid * C + (size_t)t * k_tile,
-                        row_token, cand, cand_score);
+  } else if (tid < M) {  // many: one thread per hidden state merges its sorted lists
+    merge_pick_lists<kLists>(s_pick + (size_t)tid * per_m, k_tile,
+                             (size_t)tid * C + (size_t)t * k_tile, row_token, cand, cand_score);
   }
 }
 
