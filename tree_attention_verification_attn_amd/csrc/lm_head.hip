@@ -140,8 +140,7 @@ __device__ inline float lm_dot(const uint16_t* __restrict__ x, const uint16_t* _
   const uint4* xs = reinterpret_cast<const uint4*>(x) + lane;  // 64 pieces per 512 elements
   const uint4* ys = reinterpret_cast<const uint4*>(y) + lane;
   float acc = 0.f;
-  for (int p = 0; p < (d >> 9); ++p) {
-    const uint4 a = xs[64 * p], b = ys[64 * p];
+  auto chain = [&](const uint4& a, const uint4& b) {
     acc = __builtin_fmaf(bf16_lo(a.x), bf16_lo(b.x), acc);
     acc = __builtin_fmaf(bf16_hi(a.x), bf16_hi(b.x), acc);
     acc = __builtin_fmaf(bf16_lo(a.y), bf16_lo(b.y), acc);
@@ -150,7 +149,22 @@ __device__ inline float lm_dot(const uint16_t* __restrict__ x, const uint16_t* _
     acc = __builtin_fmaf(bf16_hi(a.z), bf16_hi(b.z), acc);
     acc = __builtin_fmaf(bf16_lo(a.w), bf16_lo(b.w), acc);
     acc = __builtin_fmaf(bf16_hi(a.w), bf16_hi(b.w), acc);
+  };
+  // eight pieces of each vector in flight at a time (4096 elements: one memory round trip),
+  // then the chain over them in order
+  const int np = d >> 9;
+  int p = 0;
+  for (; p + 8 <= np; p += 8) {
+    uint4 a[8], b[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      a[k] = xs[64 * (p + k)];
+      b[k] = ys[64 * (p + k)];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) chain(a[k], b[k]);
   }
+  for (; p < np; ++p) chain(xs[64 * p], ys[64 * p]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc = acc + __shfl_xor(acc, off, 64);
   return acc;
