@@ -463,11 +463,15 @@ int eagle2_rerank(const int32_t* node_tok, const int32_t* node_parent, const flo
  * float32.  The sums are float32 in an order of the kernels' own (fixed, so a call repeats
  * bit for bit); each value is therefore the exact dot product of its bfloat16 operands within
  * float32 rounding: d/64 + 6 roundings per term for u = B h and for the exact logits (each of
- * 64 lanes sums d/64 products, then six pairwise combining steps), r per term for a screening
- * score A[row] . u[m].  Choices made on such values (which candidates a tile keeps, which
- * children win) are those of the exact values except where two of them lie within that
- * rounding of each other.  Values rank by their float order with -0 as +0; equal values go to
- * the smaller row of A (screening) or the smaller token (children).
+ * 64 lanes sums d/64 products, then six pairwise combining steps); for a screening score
+ * A[row] . u[m], at most max(r, 16 + 3 ceil(r/16), 32 + 3 ceil(r/32)) roundings per term, with
+ * u split exactly into three bfloat16 parts whose magnitudes add up to at most (1 + 2^-8) |u|
+ * (ranks up to 256 run on the matrix cores, 16 or 32 products per instruction, then one rounding
+ * per later instruction; larger ranks one chain over the rank index).  Choices made on such
+ * values (which candidates a tile keeps, which children win) are those of the exact values
+ * except where two of them lie within that rounding of each other.  Values rank by their float
+ * order with -0 as +0 (a NaN score ranks above +inf); equal values go to the smaller row of A
+ * (screening) or the smaller token (children).
  * h, B, A, W and u are read 16 bytes at a time: each must be 16-byte aligned (as any device
  * allocation is), else the call returns TV_ERR_INVALID_ARG.
  */
