@@ -470,8 +470,8 @@ int eagle2_rerank(const int32_t* node_tok, const int32_t* node_parent, const flo
  * per later instruction; larger ranks one chain over the rank index).  Choices made on such
  * values (which candidates a tile keeps, which children win) are those of the exact values
  * except where two of them lie within that rounding of each other.  Values rank by their float
- * order with -0 as +0 (a NaN score ranks above +inf); equal values go to the smaller row of A
- * (screening) or the smaller token (children).
+ * order with -0 as +0 (a NaN score ranks above +inf with its sign bit clear, below -inf with it
+ * set); equal values go to the smaller row of A (screening) or the smaller token (children).
  * h, B, A, W and u are read 16 bytes at a time: each must be 16-byte aligned (as any device
  * allocation is), else the call returns TV_ERR_INVALID_ARG.
  */
