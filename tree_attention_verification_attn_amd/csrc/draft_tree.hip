@@ -59,6 +59,11 @@ __global__ __launch_bounds__(kExpandMax) void expand_kernel(
   float v = 0.f;
   if (g == 0 && c < n) {
     const int r = c / branch, cc = c - r * branch;
+    // the child's own token and confidence first: they go out with the frontier read, not
+    // behind the parent's value, which waits for it
+    const size_t src = ((size_t)b * k + r) * branch + cc;
+    const float conf = child_conf[src];
+    const int32_t ctok = child_tok[src];
     int pid = 0;
     float pv = 1.f;
     bool ok = true;
@@ -68,11 +73,9 @@ __global__ __launch_bounds__(kExpandMax) void expand_kernel(
       pv = ok ? node_value[row + pid] : 0.f;
       if (!ok) bits |= TV_BAD_TREE;
     }
-    const size_t src = ((size_t)b * k + r) * branch + cc;
-    const float conf = child_conf[src];
     if (!(conf >= 0.f && conf <= 1.f)) bits |= TV_BAD_CONF;
     v = rank_value(pv * as_prob(conf));
-    node_tok[row + base + c] = child_tok[src];
+    node_tok[row + base + c] = ctok;
     node_parent[row + base + c] = ok ? pid : -1;
     node_value[row + base + c] = v;
     s_val[c] = v;
@@ -156,9 +159,25 @@ __global__ __launch_bounds__(kRerankThreads) void rerank_kernel(
   const size_t orow = (size_t)b * T;
   const int T4 = (T + 3) & ~3;  // lists padded to whole 16-byte reads
 
-  for (int i = tid; i < n; i += kRerankThreads) {
-    s_key[i] = __float_as_uint(rank_value(node_value[row + i]));
-    s_par[i] = node_parent[row + i];
+  // four nodes per thread in flight at a time: loads clamped to the last node rather than
+  // branched, so a batch costs one memory round trip (n >= 1)
+  for (int base = 0; base < n; base += 4 * kRerankThreads) {
+    float v[4];
+    int pp[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = min(base + k * kRerankThreads + tid, n - 1);
+      v[k] = node_value[row + i];
+      pp[k] = node_parent[row + i];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = base + k * kRerankThreads + tid;
+      if (i < n) {
+        s_key[i] = __float_as_uint(rank_value(v[k]));
+        s_par[i] = pp[k];
+      }
+    }
   }
   if (tid < 512) (&s_hist[0][0])[tid] = 0;
   if (tid == 0) s_cnt = 0;
