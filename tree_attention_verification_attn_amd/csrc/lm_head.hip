@@ -769,10 +769,27 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const float* __restrict__ 
   // between lanes holding equal scores (a 64-bit maximum over those lanes, rarely needed).
   // Each round removes one copy of the best key (candidates may repeat a token): the first
   // slot holding it in the lowest lane holding it.
+  // With eight slots a lane's keys are sorted once (a 19-exchange network), so its best is its
+  // first key and a removal shifts the rest up.
+  if constexpr (kPer == 8) {
+    auto cx = [&](int i, int k) {
+      const uint64_t hi = key[i] > key[k] ? key[i] : key[k], lo = key[i] > key[k] ? key[k] : key[i];
+      key[i] = hi;
+      key[k] = lo;
+    };
+    cx(0, 2); cx(1, 3); cx(4, 6); cx(5, 7);
+    cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
+    cx(0, 1); cx(2, 3); cx(4, 5); cx(6, 7);
+    cx(2, 4); cx(3, 5);
+    cx(1, 4); cx(3, 6);
+    cx(1, 2); cx(3, 4); cx(5, 6);
+  }
   for (int j = 0; j < K; ++j) {
-    uint64_t mine = 0;  // this lane's best key (0: none)
+    uint64_t mine = key[0];  // this lane's best key (0: none)
+    if constexpr (kPer != 8) {
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) mine = key[k] > mine ? key[k] : mine;
+      for (int k = 1; k < kPer; ++k) mine = key[k] > mine ? key[k] : mine;
+    }
     const uint32_t top = wave_max_u32((uint32_t)(mine >> 32));
     const uint64_t holders = __ballot(mine != 0 && (uint32_t)(mine >> 32) == top);
     uint64_t best = 0;
@@ -786,13 +803,19 @@ __global__ __launch_bounds__(256) void lm_topk_kernel(const float* __restrict__ 
       }
       const int owner = __builtin_ctzll(__ballot(mine == best));
       if (lane == owner) {
-        bool done = false;
+        if constexpr (kPer == 8) {  // the best is the first key: the rest move up
 #pragma unroll
-        for (int k = 0; k < kPer; ++k)
-          if (!done && key[k] == best) {
-            key[k] = 0;
-            done = true;
-          }
+          for (int k = 0; k < kPer - 1; ++k) key[k] = key[k + 1];
+          key[kPer - 1] = 0;
+        } else {
+          bool done = false;
+#pragma unroll
+          for (int k = 0; k < kPer; ++k)
+            if (!done && key[k] == best) {
+              key[k] = 0;
+              done = true;
+            }
+        }
       }
     }
     if (lane == 0) s_pick[wave * K + j] = best;
