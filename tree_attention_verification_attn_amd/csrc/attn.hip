@@ -1453,9 +1453,11 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int split_keys) {
     // One workgroup per compute unit.  A chunk costs a prologue (Q and the first tiles), a
     // 128 KB fp32 partial (256 rows x D = 128) written and merged, so splitting pays only where
     // CUs would otherwise idle:
-    //  * fewer (sequence, KV head, row block) units than CUs: aim for two rounds, with chunks
-    //    of at least 4 tiles (3-tile chunks write a larger partial than the 96 KB of K/V they
-    //    read: 20.8 against 19.9 us at batch 1, prefix 4096);
+    //  * fewer (sequence, KV head, row block) units than CUs: one round of workgroups, with
+    //    chunks of at least 4 tiles (3-tile chunks write a larger partial than the 96 KB of K/V
+    //    they read: 20.8 against 19.9 us at batch 1, prefix 4096).  Two rounds pay a second
+    //    prologue and twice the partials: 543.5 against 533.0 us for the step at batch 8,
+    //    prefix 32768;
     //  * at least as many units as CUs, but fewer than twice: only sequences longer than 3/4
     //    of the longest split, into a 3/4 chunk and the rest, which the longest-first dispatch
     //    places in the second round (126 us against 143 us for halves at batch 32, prefixes of
@@ -1468,7 +1470,7 @@ Plan make_plan(int B, int T, int Hq, int Hkv, int D, int Lmax, int split_keys) {
     } else if (units >= cus) {
       chunk_tiles = std::max(1, ceil_div(3 * tiles, 4));
     } else {
-      const int S = (int)std::min<long long>(std::max<long long>(1, ceil_div_ll(2 * cus, units)),
+      const int S = (int)std::min<long long>(std::max<long long>(1, ceil_div_ll(cus, units)),
                                              std::max(1, ceil_div(tiles, 4)));
       chunk_tiles = ceil_div(tiles, S);
     }
